@@ -1,0 +1,256 @@
+"""Python face of the f64 CPU oracle (``qd_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline use this package; the product path never imports it.  It shares no
+code with the HIP library; the only common module is ``synth`` (seeded input
+generation, no decode arithmetic).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+class _Q4(C.Structure):
+    _fields_ = [("d", C.c_void_p), ("qs", C.c_void_p), ("rows", C.c_int64), ("cols", C.c_int64)]
+
+
+class _Layer(C.Structure):
+    _fields_ = [("attn_norm", C.c_void_p), ("ffn_norm", C.c_void_p), ("q_norm", C.c_void_p),
+                ("k_norm", C.c_void_p)] + [(n, _Q4) for n in
+                                           ("wq", "wk", "wv", "wo", "wgate", "wup", "wdown")]
+
+
+class _Cfg(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("hidden", "layers", "n_heads", "n_kv", "head_dim",
+                                         "intermediate", "vocab", "rot_dim", "qk_norm",
+                                         "max_seq", "kv_round")] + \
+               [("eps", C.c_double), ("inv_freq", C.c_void_p)]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        # QD_ORACLE_LIB points the wrapper at another build of qd_oracle.c
+        # (the mutation test uses it to load deliberately broken copies)
+        path = os.environ.get("QD_ORACLE_LIB") or _build.LIB
+        if path == _build.LIB and not os.path.exists(path):
+            _build.build()
+        L = C.CDLL(path)
+        L.or_f16_to_f64.restype = C.c_double
+        L.or_f16_to_f64.argtypes = [C.c_uint16]
+        L.or_f64_to_f16.restype = C.c_uint16
+        L.or_f64_to_f16.argtypes = [C.c_double]
+        L.or_dequant_q4_0.argtypes = [C.POINTER(_Q4), C.c_void_p]
+        L.or_gemv_q4_0.argtypes = [C.POINTER(_Q4), C.c_void_p, C.c_void_p, C.c_int]
+        L.or_rmsnorm.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_double, C.c_void_p]
+        L.or_rope_neox.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_int64]
+        L.or_attn_decode.restype = C.c_int
+        L.or_attn_decode.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                                     C.c_int32, C.c_int32, C.c_void_p, C.c_int32, C.c_int32,
+                                     C.c_int32, C.c_int32, C.c_double, C.c_void_p, C.c_int]
+        L.or_model_create.restype = C.c_void_p
+        L.or_model_create.argtypes = [C.POINTER(_Cfg), C.POINTER(_Q4), C.c_void_p, C.c_void_p,
+                                      C.POINTER(_Q4), C.c_int]
+        L.or_model_step.restype = C.c_int
+        L.or_model_step.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]
+        L.or_model_kv.restype = C.c_int
+        L.or_model_kv.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                  C.c_void_p]
+        L.or_model_destroy.argtypes = [C.c_void_p]
+        _lib = L
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _p(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _q4(W) -> _Q4:
+    d = np.ascontiguousarray(W.d, dtype=np.uint16)
+    qs = np.ascontiguousarray(W.qs, dtype=np.uint8)
+    assert d.shape[0] == qs.shape[0] and d.shape[1] == qs.shape[1] and qs.shape[2] == 16
+    s = _Q4(_p(d), _p(qs), d.shape[0], d.shape[1] * 32)
+    s._keep = (d, qs)
+    return s
+
+
+# --------------------------------------------------------------------------- primitives
+
+def f16_to_f64(bits) -> np.ndarray:
+    L = lib()
+    b = np.asarray(bits, dtype=np.uint16)
+    return np.array([L.or_f16_to_f64(int(x)) for x in b.ravel()], dtype=np.float64).reshape(b.shape)
+
+
+def f64_to_f16(vals) -> np.ndarray:
+    L = lib()
+    v = np.asarray(vals, dtype=np.float64)
+    return np.array([L.or_f64_to_f16(float(x)) for x in v.ravel()], dtype=np.uint16).reshape(v.shape)
+
+
+def dequant(W) -> np.ndarray:
+    q = _q4(W)
+    out = np.empty((q.rows, q.cols), dtype=np.float64)
+    lib().or_dequant_q4_0(C.byref(q), _p(out))
+    return out
+
+
+def gemv(W, x, nthreads: int | None = None) -> np.ndarray:
+    """y = dequant(W) @ x in f64 (x is promoted exactly from its dtype)."""
+    q = _q4(W)
+    xx = np.ascontiguousarray(x, dtype=np.float64)
+    assert xx.shape == (q.cols,)
+    y = np.empty(q.rows, dtype=np.float64)
+    lib().or_gemv_q4_0(C.byref(q), _p(xx), _p(y), nthreads or default_threads())
+    return y
+
+
+def rmsnorm(x, w, eps: float) -> np.ndarray:
+    xx = np.ascontiguousarray(x, dtype=np.float64)
+    ww = np.ascontiguousarray(w, dtype=np.float32)
+    out = np.empty_like(xx)
+    lib().or_rmsnorm(_p(xx), _p(ww), xx.size, float(eps), _p(out))
+    return out
+
+
+def rope(v, rot: int, inv_freq, pos: int) -> np.ndarray:
+    vv = np.array(v, dtype=np.float64, copy=True)
+    f = np.ascontiguousarray(inv_freq, dtype=np.float32)
+    assert f.size >= rot // 2
+    lib().or_rope_neox(_p(vv), vv.size, int(rot), _p(f), int(pos))
+    return vv
+
+
+def attn_decode(q, k, v, kv_lens, nkv: int, scale: float, block_tables=None,
+                block_size: int = 16, contig_max_kv: int = 0,
+                nthreads: int | None = None) -> np.ndarray:
+    """Decode attention; see or_attn_decode.  q f32 [B, nq, hd]."""
+    qq = np.ascontiguousarray(q, dtype=np.float32)
+    B, nq, hd = qq.shape
+    kk = np.ascontiguousarray(k, dtype=np.uint16)
+    vv = np.ascontiguousarray(v, dtype=np.uint16)
+    lens = np.ascontiguousarray(kv_lens, dtype=np.int32)
+    out = np.empty((B, nq, hd), dtype=np.float64)
+    if block_tables is not None:
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        tp, mbps = _p(bt), bt.shape[1]
+    else:
+        bt, tp, mbps = None, None, 0
+    rc = lib().or_attn_decode(_p(qq), _p(kk), _p(vv), tp, mbps, block_size, contig_max_kv,
+                              _p(lens), B, nq, nkv, hd, float(scale), _p(out),
+                              nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("or_attn_decode rejected its arguments")
+    return out
+
+
+def attn_inputs(a, nthreads: int | None = None) -> np.ndarray:
+    """Oracle attention for a ``synth.AttnInputs`` (paged)."""
+    return attn_decode(a.q, a.k_pool, a.v_pool, a.kv_lens, a.nkv, 1.0 / np.sqrt(a.hd),
+                       block_tables=a.block_tables, block_size=a.block, nthreads=nthreads)
+
+
+# --------------------------------------------------------------------------- model
+
+class Model:
+    """The oracle decoder over a ``synth.ModelInputs``; KV cache kept inside."""
+
+    def __init__(self, mi, nthreads: int | None = None, kv_round: bool = True):
+        s = mi.shape
+        self.mi = mi
+        self.vocab = s.vocab
+        self._embed = _q4(mi.embed)
+        self._lm = _q4(mi.lm_head)
+        self._keep = []
+        layers = (_Layer * s.layers)()
+        for i, Lw in enumerate(mi.layers):
+            ns = [np.ascontiguousarray(a, dtype=np.float32) for a in
+                  (Lw.attn_norm, Lw.ffn_norm, Lw.q_norm, Lw.k_norm)]
+            qs = [_q4(m) for m in (Lw.wq, Lw.wk, Lw.wv, Lw.wo, Lw.wgate, Lw.wup, Lw.wdown)]
+            self._keep.append((ns, qs))
+            layers[i] = _Layer(_p(ns[0]), _p(ns[1]), _p(ns[2]), _p(ns[3]), *qs)
+        self._layers = layers
+        self._final = np.ascontiguousarray(mi.final_norm, dtype=np.float32)
+        self._inv = np.ascontiguousarray(mi.inv_freq, dtype=np.float32)
+        self._cfg = _Cfg(s.hidden, s.layers, s.n_heads, s.n_kv, s.head_dim, s.intermediate,
+                         s.vocab, s.rot_dim, int(s.qk_norm), s.max_seq, int(kv_round),
+                         float(s.eps), _p(self._inv))
+        self.nthreads = nthreads or default_threads()
+        h = lib().or_model_create(C.byref(self._cfg), C.byref(self._embed), self._layers,
+                                  _p(self._final), C.byref(self._lm), self.nthreads)
+        if not h:
+            raise ValueError("oracle rejected the model configuration")
+        self._h = h
+
+    def step(self, token: int, pos: int) -> np.ndarray:
+        out = np.empty(self.vocab, dtype=np.float64)
+        if lib().or_model_step(self._h, int(token), int(pos), _p(out)) != 0:
+            raise ValueError(f"oracle step rejected token={token} pos={pos}")
+        return out
+
+    def kv(self, layer: int, pos: int, kv_head: int, which_v: bool) -> np.ndarray:
+        out = np.empty(self.mi.shape.head_dim, dtype=np.float64)
+        if lib().or_model_kv(self._h, layer, pos, kv_head, int(which_v), _p(out)) != 0:
+            raise ValueError("bad kv index")
+        return out
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().or_model_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown
+            pass
+
+
+def greedy_pick(logits: np.ndarray):
+    """Greedy choice over logits rounded to f32 (the precision the device
+    compares in); lowest index wins ties.  Returns (token, top1 - top2 margin
+    of the f64 logits)."""
+    f32 = logits.astype(np.float32)
+    tok = int(np.argmax(f32))
+    top2 = np.partition(logits, -2)[-2:]
+    return tok, float(top2[1] - top2[0])
+
+
+def generate(model: Model, prompt, G: int, keep_logits_at=(), on_step=None):
+    """Sequential-decode prefill of ``prompt`` (positions 0..P-1) then G greedy
+    tokens: the logits at position P-1 give token 0, token i is fed at P+i-1.
+    Returns (tokens[G], margins[G], {greedy index: logits f64})."""
+    prompt = [int(t) for t in prompt]
+    P = len(prompt)
+    toks, margins, kept = [], [], {}
+    keep = set(keep_logits_at)
+    cur = prompt[0]
+    for pos in range(P + G - 1):
+        lg = model.step(cur, pos)
+        if on_step is not None:
+            on_step(pos)
+        if pos + 1 < P:
+            cur = prompt[pos + 1]
+            continue
+        gi = pos - (P - 1)
+        t, mg = greedy_pick(lg)
+        toks.append(t)
+        margins.append(mg)
+        if gi in keep:
+            kept[gi] = lg.copy()
+        cur = t
+    return np.array(toks, dtype=np.int32), np.array(margins), kept

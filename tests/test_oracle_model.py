@@ -1,0 +1,147 @@
+"""Pin of the oracle's whole decode step.
+
+The oracle runs the tiny config one token at a time (sequential decode with a
+KV cache).  The installed ``transformers`` Qwen3 implementation, loaded with
+the same dequantised weights and run in f64, computes the same logits for the
+whole prompt at once with a causal mask and no cache: a separate
+implementation and a separate algorithm (full causal attention, not
+incremental decode).  As shipped it computes RMSNorm statistics, the rotary
+tables and (eager path) the softmax in f32 even for an f64 model, so it agrees
+to f32 rounding; with the norm and rotary switched to the model's own dtype
+(same formulas, no down-cast) and torch's SDPA for the attention, it agrees
+to f64 rounding.
+"""
+import contextlib
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+
+def _hf_model(mi, oracle_lib, attn="eager"):
+    from transformers import Qwen3Config, Qwen3ForCausalLM
+    s = mi.shape
+    cfg = Qwen3Config(vocab_size=s.vocab, hidden_size=s.hidden, intermediate_size=s.intermediate,
+                      num_hidden_layers=s.layers, num_attention_heads=s.n_heads,
+                      num_key_value_heads=s.n_kv, head_dim=s.head_dim, rope_theta=s.rope_theta,
+                      rms_norm_eps=s.eps, tie_word_embeddings=s.tied,
+                      max_position_embeddings=max(64, s.max_seq), attention_bias=False)
+    cfg._attn_implementation = attn
+    torch.manual_seed(0)
+    m = Qwen3ForCausalLM(cfg).to(torch.float64).eval()
+    T = lambda a: torch.tensor(np.asarray(a, dtype=np.float64))
+    with torch.no_grad():
+        m.model.embed_tokens.weight.copy_(T(oracle_lib.dequant(mi.embed)))
+        for i, L in enumerate(mi.layers):
+            ml = m.model.layers[i]
+            ml.self_attn.q_proj.weight.copy_(T(oracle_lib.dequant(L.wq)))
+            ml.self_attn.k_proj.weight.copy_(T(oracle_lib.dequant(L.wk)))
+            ml.self_attn.v_proj.weight.copy_(T(oracle_lib.dequant(L.wv)))
+            ml.self_attn.o_proj.weight.copy_(T(oracle_lib.dequant(L.wo)))
+            ml.self_attn.q_norm.weight.copy_(T(L.q_norm))
+            ml.self_attn.k_norm.weight.copy_(T(L.k_norm))
+            ml.mlp.gate_proj.weight.copy_(T(oracle_lib.dequant(L.wgate)))
+            ml.mlp.up_proj.weight.copy_(T(oracle_lib.dequant(L.wup)))
+            ml.mlp.down_proj.weight.copy_(T(oracle_lib.dequant(L.wdown)))
+            ml.input_layernorm.weight.copy_(T(L.attn_norm))
+            ml.post_attention_layernorm.weight.copy_(T(L.ffn_norm))
+        m.model.norm.weight.copy_(T(mi.final_norm))
+        if not s.tied:
+            m.lm_head.weight.copy_(T(oracle_lib.dequant(mi.lm_head)))
+        # the same host-precomputed frequencies the oracle is given
+        m.model.rotary_emb.inv_freq.copy_(torch.tensor(mi.inv_freq.astype(np.float64)))
+    return m
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return synth.make_model("tiny")
+
+
+@contextlib.contextmanager
+def _hf_in_f64():
+    """Run transformers' Qwen3 RMSNorm and rotary tables in the input dtype."""
+    from transformers.models.qwen3 import modeling_qwen3 as mq
+    old_norm, old_rot = mq.Qwen3RMSNorm.forward, mq.Qwen3RotaryEmbedding.forward
+
+    def norm(self, h):
+        var = h.pow(2).mean(-1, keepdim=True)
+        return self.weight * (h * torch.rsqrt(var + self.variance_epsilon))
+
+    @torch.no_grad()
+    def rot(self, x, position_ids):
+        f = self.inv_freq.to(torch.float64)[None, :, None] * position_ids[:, None, :].to(torch.float64)
+        emb = torch.cat((f, f), dim=1).transpose(1, 2)
+        return emb.cos().to(x.dtype), emb.sin().to(x.dtype)
+
+    mq.Qwen3RMSNorm.forward, mq.Qwen3RotaryEmbedding.forward = norm, rot
+    try:
+        yield
+    finally:
+        mq.Qwen3RMSNorm.forward, mq.Qwen3RotaryEmbedding.forward = old_norm, old_rot
+
+
+def _hf_logits(mi, oracle_lib, attn="eager"):
+    hf = _hf_model(mi, oracle_lib, attn)
+    with torch.no_grad():
+        return hf(torch.tensor(mi.prompt[None, :].astype(np.int64))).logits[0].numpy()
+
+
+def test_sequential_decode_equals_full_causal_forward(oracle_lib, tiny):
+    mi = tiny
+    om = oracle_lib.Model(mi, kv_round=False)
+    ours = np.stack([om.step(int(t), p) for p, t in enumerate(mi.prompt)])
+    ref32 = _hf_logits(mi, oracle_lib)
+    with _hf_in_f64():
+        # torch's SDPA keeps the softmax in f64 (the eager path casts it to f32)
+        ref64 = _hf_logits(mi, oracle_lib, attn="sdpa")
+    scale = np.abs(ref64).max()
+    assert np.max(np.abs(ours - ref64)) <= 1e-12 * scale
+    assert np.max(np.abs(ours - ref32)) <= 1e-6 * scale
+    # a wrong step would be far outside either bound
+    assert np.abs(ref64[1:] - ref64[:-1]).max(axis=1).min() > 0.1 * scale
+
+
+def test_f16_kv_cache_rounding(oracle_lib, tiny):
+    """kv_round stores K/V as binary16 and changes logits only at the level of
+    that rounding."""
+    mi = tiny
+    a = oracle_lib.Model(mi, kv_round=True)
+    b = oracle_lib.Model(mi, kv_round=False)
+    la = [a.step(int(t), p) for p, t in enumerate(mi.prompt[:6])]
+    lb = [b.step(int(t), p) for p, t in enumerate(mi.prompt[:6])]
+    for L in range(mi.shape.layers):
+        for p in range(6):
+            for g in range(mi.shape.n_kv):
+                for which in (0, 1):
+                    kr = a.kv(L, p, g, which)
+                    assert np.array_equal(kr, kr.astype(np.float16).astype(np.float64))
+                    if L == 0:
+                        # layer 0's K/V depend only on the token: the rounded
+                        # model stores exactly the binary16 of the unrounded one
+                        kf = b.kv(L, p, g, which)
+                        assert np.array_equal(kr, kf.astype(np.float16).astype(np.float64))
+    d = max(np.abs(x - y).max() for x, y in zip(la, lb))
+    assert 0 < d < 1e-2
+
+
+def test_oracle_step_rejects_bad_inputs(oracle_lib, tiny):
+    om = oracle_lib.Model(tiny)
+    with pytest.raises(ValueError):
+        om.step(tiny.shape.vocab, 0)
+    with pytest.raises(ValueError):
+        om.step(0, tiny.shape.max_seq)
+    with pytest.raises(ValueError):
+        om.step(-1, 0)
+
+
+def test_generate_counts(oracle_lib, tiny):
+    om = oracle_lib.Model(tiny)
+    steps = []
+    toks, margins, kept = oracle_lib.generate(om, tiny.prompt, 5, keep_logits_at=(0, 4),
+                                              on_step=steps.append)
+    P = tiny.shape.prompt_len
+    assert len(toks) == 5 and len(margins) == 5 and set(kept) == {0, 4}
+    assert steps == list(range(P + 5 - 1))
+    assert toks[0] == int(np.argmax(kept[0].astype(np.float32)))
