@@ -1,0 +1,200 @@
+"""Benchmark: batch-1 greedy decode tok/s at the Qwen3-8B shape on one MI355X.
+
+One timed "step" is one decode step of the whole path (embedding, 36 layers of
+fused q4_0 GEMVs + split-KV GQA attention + fused norm/rotary/SwiGLU/residual,
+LM head + greedy argmax), replayed from a hipGraph with the token and position
+held on the device.  The 2048-token seeded prompt is prefilled by sequential
+decode first; warmup and timed steps are the greedy steps that follow
+(positions 2047 + ...), as in the 2048 + 512 workload.
+
+Also reported, on the same JSON line:
+  roofline      the q4_0 GEMV at the fused gate|up shape (24576 x 4096, the
+                step's dominant kernel) through qd_gemv_q4_0, timed with HIP
+                events on its own stream over >= 1 GiB of rotated weight copies
+                (no Infinity-Cache reuse); achieved = algorithmic bytes / mean
+                launch duration, against 8 TB/s.
+  step_roofline the whole step's algorithmic bytes / measured step time.
+  cpu_baseline  the f64 CPU oracle running decode steps of the same model on
+                the host cores (a bounded sample from position 0).
+
+Usage: python bench.py [--gpus 1] [--steps 448] [--warmup 16]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def q4_bytes(rows: int, cols: int) -> int:
+    return rows * cols * 18 // 32
+
+
+def step_bytes(s, kv_len: int) -> int:
+    """Algorithmic HBM bytes of one decode step at context kv_len (K/V read for
+    kv_len positions, one position written): q4_0 weights (+ the embedding row),
+    f32 norm vectors, the f16 KV traffic."""
+    H, I, hd, nq, nkv, V, L = s.hidden, s.intermediate, s.head_dim, s.n_heads, s.n_kv, s.vocab, s.layers
+    per_layer = (q4_bytes((nq + 2 * nkv) * hd, H) + q4_bytes(H, nq * hd) + q4_bytes(2 * I, H)
+                 + q4_bytes(H, I) + 4 * (2 * H + 2 * hd))
+    kv = L * (kv_len * nkv * hd * 2 * 2 + nkv * hd * 2 * 2)
+    return L * per_layer + q4_bytes(V, H) + q4_bytes(1, H) + 4 * H + kv
+
+
+def gemv_roofline(reps: int = 100, min_bytes: int = 1 << 30):
+    """Mean duration of qd_gemv_q4_0 at 24576 x 4096 over rotated weight copies."""
+    import torch
+    import synth
+    import token_decode_q4_amd as qd
+    N, K = 24576, 4096
+    (W,), x = synth.gemv_case(synth.GEMV_SHAPES.index((N, K)))
+    nbytes_w = W.d.nbytes + W.qs.nbytes
+    copies = max(1, -(-min_bytes // nbytes_w))
+    d0 = torch.from_numpy(W.d.view(np.int16)).cuda()
+    q0 = torch.from_numpy(W.qs).cuda()
+    ds = [d0] + [d0.clone() for _ in range(copies - 1)]
+    qs = [q0] + [q0.clone() for _ in range(copies - 1)]
+    xt = torch.from_numpy(x).cuda()
+    y = torch.empty(N, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(10):
+            qd.gemv_q4_0(ds[i % copies], qs[i % copies], xt, y, stream=stream)
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            qd.gemv_q4_0(ds[i % copies], qs[i % copies], xt, y, stream=stream)
+        e1.record(stream)
+        stream.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    algo = N * K * 18 // 32 + 4 * K + 4 * N
+    achieved = algo / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "k_gemv_plain (qd_gemv_q4_0) 24576x4096", "mean_us": round(us, 3),
+            "bytes_per_launch": algo, "weight_copies": copies}
+
+
+def cpu_baseline(mi, seconds: float = 15.0):
+    """The oracle as it stands, decode steps of the same model from position 0."""
+    import oracle
+    threads = oracle.default_threads()
+    om = oracle.Model(mi, nthreads=threads)
+    t0 = time.time()
+    n = 0
+    while True:
+        om.step(int(mi.prompt[n]), n)
+        n += 1
+        if time.time() - t0 >= seconds or n >= len(mi.prompt):
+            break
+    el = time.time() - t0
+    om.close()
+    return {"value": round(n / el, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} f64 oracle decode steps of the Qwen3-8B-shape model at positions "
+                      f"0..{n - 1} (prompt tokens), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=448)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--config", default="qwen3-8b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-roofline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): batch-1 decode of one "
+              "model copy uses a single device; see DESIGN.md for how it would shard.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import token_decode_q4_amd as qd
+
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    mi = synth.make_model(args.config)
+    s = mi.shape
+    log(f"inputs {s.name} ready in {time.time() - t0:.1f}s (sha256 {mi.digest[:16]})")
+    P = s.prompt_len
+    if P - 1 + args.warmup + args.steps > s.max_seq:
+        sys.exit(f"warmup + steps must be <= {s.max_seq - P + 1}")
+    t0 = time.time()
+    model = qd.Model(mi, use_graph=True)
+    log(f"qd_create {time.time() - t0:.1f}s")
+    stream = torch.cuda.current_stream()
+    toks = torch.empty(s.max_seq, dtype=torch.int32, device="cuda")
+    model.set_prompt(mi.prompt)
+    t0 = time.time()
+    model.generate(0, P - 1, tokens=toks[: P - 1])
+    torch.cuda.synchronize()
+    log(f"prefill {P - 1} steps in {time.time() - t0:.2f}s")
+    pos = P - 1
+    model.generate(pos, args.warmup, tokens=toks[pos:pos + args.warmup])
+    pos += args.warmup
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    model.generate(pos, args.steps, tokens=toks[pos:pos + args.steps])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    tok_s = args.steps / (ms * 1e-3)
+    kv_lens = np.arange(pos + 1, pos + args.steps + 1)
+    mean_bytes = float(np.mean([step_bytes(s, int(k)) for k in kv_lens]))
+    step_gbs = mean_bytes / (ms * 1e-3 / args.steps) / 1e9
+    log(f"decode {args.steps} steps: {ms:.2f} ms, {tok_s:.1f} tok/s, {step_gbs:.0f} GB/s")
+    model.close()
+    del model
+    torch.cuda.empty_cache()
+
+    roof = None
+    if not args.no_roofline:
+        roof = gemv_roofline()
+        log(f"gemv roofline: {roof['mean_us']} us, {roof['achieved']} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(mi)
+        log(f"cpu baseline: {cpu['value']} tok/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": "decode tok/s (batch 1) at Qwen3-8B shape; q4_0 GEMV GB/s as % of HBM peak",
+        "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "q4_0/f32",
+        "data": "synthetic (seeded N(0,0.02) weights quantised to q4_0, random prompt)",
+        "config": {"workload": f"{s.name} batch-1 greedy decode, positions {pos}..{pos + args.steps - 1} "
+                               f"after a {P}-token sequential-decode prefill",
+                   "layers": s.layers, "hidden": s.hidden, "heads": f"{s.n_heads}/{s.n_kv}",
+                   "head_dim": s.head_dim, "intermediate": s.intermediate, "vocab": s.vocab,
+                   "kv": "paged f16, block 16, shuffled table" if s.kv_paged else "contiguous f16",
+                   "batch": 1, "parallelism": "single GPU"},
+        "step_roofline": {"bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                          "bytes_per_step": round(mean_bytes)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

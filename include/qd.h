@@ -1,0 +1,193 @@
+/*
+ * qd.h -- C ABI of the MI355X (gfx950) batch-1 q4_0 decode library.
+ *
+ * The library computes the batch-1 greedy decode step of a dense Qwen3-style
+ * decoder whose matrices are q4_0 (inferencelayer cuda_llm.rs page, module
+ * doc and CudaQwen3::step; ferrum-kernels cuda_decode.rs page,
+ * CudaDecodeRunner::decode_step), and exposes its two hot kernels on their
+ * own: the q4_0 GEMV and the GQA decode attention.
+ *
+ * Conventions for every entry point:
+ *   - return QD_OK (0) or a negative QD_E* code; qd_last_error() then returns
+ *     a message (thread-local, valid until the next call on that thread);
+ *   - arguments are validated before any HIP call: on a validation error
+ *     nothing is enqueued and nothing is allocated;
+ *   - "stream" is a hipStream_t passed as void* (NULL = the null stream);
+ *     work is enqueued asynchronously on it unless stated otherwise;
+ *   - "host" pointers are read during the call only; "device" pointers must
+ *     stay valid until the enqueued work has finished;
+ *   - no C++ exception crosses this interface.
+ */
+#ifndef QD_H
+#define QD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QD_OK 0
+#define QD_EINVAL (-1)       /* null pointer, bad shape or inconsistent config */
+#define QD_ERANGE (-2)       /* token or position out of range */
+#define QD_ENOMEM (-3)       /* device allocation failed */
+#define QD_EUNSUPPORTED (-4) /* valid but not built: head_dim, GQA group, block size */
+#define QD_EHIP (-5)         /* HIP runtime error (message has hipGetErrorString) */
+
+typedef void* qd_stream; /* hipStream_t */
+
+/* ------------------------------------------------------------------ q4_0
+ * A q4_0 matrix [rows, cols], row-major, in blocks of 32 weights along a row
+ * (inferencelayer cuda_llm.rs page, Q4Dev and LayerDev: one f16 scale and 16
+ * bytes of nibbles per 32 weights; value = (nibble - 8) * scale):
+ *   d  [rows][cols/32]      binary16 bit patterns of the block scales
+ *   qs [rows][cols/32][16]  byte j of a block: element j in the low nibble,
+ *                           element j+16 in the high nibble
+ * cols must be a multiple of 32.                                           */
+typedef struct {
+    const uint16_t* d;
+    const uint8_t* qs;
+    int32_t rows, cols;
+} qd_q4_0;
+
+/* One decoder layer, host memory.  Norm vectors are f32: attn_norm and
+ * ffn_norm [hidden], q_norm and k_norm [head_dim] (ignored when qk_norm = 0).
+ * wq [n_heads*head_dim, hidden], wk and wv [n_kv*head_dim, hidden],
+ * wo [hidden, n_heads*head_dim], wgate and wup [intermediate, hidden],
+ * wdown [hidden, intermediate]. */
+typedef struct {
+    const float *attn_norm, *ffn_norm, *q_norm, *k_norm;
+    qd_q4_0 wq, wk, wv, wo, wgate, wup, wdown;
+} qd_layer_weights;
+
+/* embed [vocab, hidden] q4_0: a token's embedding is its dequantised row.
+ * lm_head [vocab, hidden] q4_0, ignored when the config says tied (the
+ * embedding table is then the head).  final_norm f32 [hidden].
+ * layers: [config.layers]. */
+typedef struct {
+    qd_q4_0 embed;
+    qd_q4_0 lm_head;
+    const float* final_norm;
+    const qd_layer_weights* layers;
+} qd_weights;
+
+/* Model configuration (inferencelayer cuda_llm.rs page, Cfg).
+ *   rot_dim: even, <= head_dim; the first rot_dim dims of every q and k head
+ *            turn NeoX split-half style (pairs i, i + rot_dim/2); the rest
+ *            pass through (partial rotary).
+ *   inv_freq: host f32 [rot_dim/2], the host-precomputed rotary frequencies
+ *            (Cfg::rope_inv_freq); angle of pair i at position p = p*inv_freq[i].
+ *   qk_norm: 1 = per-head RMSNorm of q and k (over head_dim) before rotary.
+ *   max_seq: positions 0 .. max_seq-1 exist in the KV cache.
+ *   kv_paged: 0 = contiguous f16 KV cache; 1 = paged (ferrum-kernels
+ *            cuda_decode.rs page, PagedSequenceKvState / attention_paged):
+ *            a pool of num_kv_blocks blocks of kv_block_size tokens per layer,
+ *            and block_table [ceil(max_seq/kv_block_size)] (host, int32) mapping
+ *            logical block -> physical block (distinct entries in
+ *            [0, num_kv_blocks)); NULL = identity.  The whole table is fixed
+ *            at create time, so a captured step never needs a table update.
+ *   use_graph: 1 = one decode step is captured in a hipGraph at create time
+ *            and replayed; 0 = the step's kernels are launched one by one.
+ * Supported: head_dim 64 or 128; n_heads / n_kv in {1, 2, 4, 8};
+ * kv_block_size 16; hidden, intermediate and n_heads*head_dim multiples of 32. */
+typedef struct {
+    int32_t hidden, layers, n_heads, n_kv, head_dim, intermediate, vocab;
+    float eps;
+    int32_t rot_dim;
+    const float* inv_freq;
+    int32_t tied;
+    int32_t qk_norm;
+    int32_t max_seq;
+    int32_t kv_paged, kv_block_size, num_kv_blocks;
+    const int32_t* block_table;
+    int32_t use_graph;
+} qd_config;
+
+typedef struct qd_model qd_model;
+
+/* Create a model on the current HIP device.  Copies every host array it is
+ * given (weights, inv_freq, block_table) into library-owned device memory
+ * (the layout there is the library's own); the caller's buffers may be freed
+ * on return.  Synchronous.  *out receives the handle. */
+int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream stream, qd_model** out);
+
+/* Free all device memory of the model (after synchronising its work). */
+int qd_destroy(qd_model* m);
+
+/* One decode step (inferencelayer cuda_llm.rs page, CudaQwen3::step): embed
+ * `token` at position `pos`, write its K/V at `pos`, attend over positions
+ * 0..pos, produce f32 logits [vocab].  Positions 0..pos-1 must have been
+ * written by earlier steps (prefill is sequential decode).  d_logits (device
+ * f32 [vocab]) and d_next (device int32, greedy argmax, lowest index on ties)
+ * may each be NULL.  Asynchronous on `stream`. */
+int qd_decode_step(qd_model* m, int32_t token, int32_t pos, float* d_logits, int32_t* d_next,
+                   qd_stream stream);
+
+/* Greedy generation driven on the device (inferencelayer cuda_llm.rs page,
+ * CudaQwen3::seed / capture / run_graph / tokens): the model keeps a token
+ * per position.  qd_set_prompt stores host tokens [n] at positions 0..n-1
+ * and marks them forced.  qd_generate runs n_steps steps at positions
+ * pos0 .. pos0+n_steps-1 with no host synchronisation: the step at p reads
+ * the token stored at p and computes the argmax of its logits; if p+1 is not
+ * a forced position that argmax becomes the token at p+1.  d_tokens (device
+ * int32 [n_steps] or NULL) receives the argmax of every step; d_logits_last
+ * (device f32 [vocab] or NULL) the logits of the last step.  Prompt prefill
+ * plus G greedy tokens is qd_set_prompt(prompt, P) then
+ * qd_generate(0, P+G-1, ...): entries P-1 .. P+G-2 of d_tokens are the
+ * greedy tokens.  Requires pos0 + n_steps <= max_seq. */
+int qd_set_prompt(qd_model* m, const int32_t* tokens, int32_t n, qd_stream stream);
+int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* d_tokens,
+                float* d_logits_last, qd_stream stream);
+
+/* Standalone q4_0 GEMV (inferencelayer cuda_llm.rs page, CudaQwen3::gemv):
+ * y[N] = W[N, K] x[K], W in the q4_0 layout above (device d_scales
+ * [N][K/32], d_qs [N][K/32][16]), x and y device f32.  K % 32 == 0.  No
+ * allocation; capturable. */
+int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x, float* d_y,
+                 int32_t N, int32_t K, qd_stream stream);
+
+/* Standalone GQA decode attention with split-KV partials and an
+ * online-softmax combine (inferencelayer cuda_llm.rs page, attn_partial /
+ * attn_reduce and the flash-decoding arm; ferrum-kernels cuda_decode.rs page,
+ * flash_decode_attention, paged_decode_attention, batched_decode_attention).
+ *   q        device f32 [B][nq][head_dim]
+ *   k, v     device f16 bits.  Paged (block_tables != NULL): pools
+ *            [num_blocks][nkv][block_size][head_dim]; block_tables device
+ *            int32 [B][max_blocks_per_seq], logical block -> physical block.
+ *            Contiguous (block_tables == NULL): [B][nkv][max_kv_len][head_dim].
+ *   kv_lens  device int32 [B]; each in [0, max_kv_len]; 0 -> output zeros
+ *   max_kv_len host bound on kv_lens (sizes the grid)
+ *   scale    softmax scale (usually 1/sqrt(head_dim))
+ *   out      device f32 [B][nq][head_dim]
+ * Query head h reads kv head h / (nq/nkv).  Supported: head_dim 64 or 128,
+ * nq/nkv in {1, 2, 4, 8}, block_size 16. */
+typedef struct {
+    const float* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* block_tables;
+    int32_t max_blocks_per_seq;
+    int32_t block_size;
+    const int32_t* kv_lens;
+    int32_t max_kv_len;
+    int32_t B, nq, nkv, head_dim;
+    float scale;
+    float* out;
+} qd_attn_args;
+
+/* Bytes of device workspace qd_attn_decode needs for these sizes.  The
+ * workspace must be zero-filled once before its first use; each call leaves
+ * it ready for the next (its completion counters return to zero). */
+size_t qd_attn_workspace_bytes(int32_t B, int32_t nq, int32_t nkv, int32_t head_dim,
+                               int32_t max_kv_len);
+int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t workspace_bytes,
+                   qd_stream stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* qd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QD_H */

@@ -1,0 +1,130 @@
+"""The C ABI library without a GPU: it loads, exports every function the
+header declares, and rejects bad arguments with an error code before any HIP
+call (so these run on a machine with no GPU)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def qd():
+    import token_decode_q4_amd as qd
+    qd.lib()
+    return qd
+
+
+def test_header_functions_exported(qd):
+    hdr = open(os.path.join(ROOT, "include", "qd.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    names = set(re.findall(r"\b(qd_[a-z0-9_]+)\s*\(", hdr))
+    assert names == set(qd.EXPORTS)
+    L = qd.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    # and the shared object's dynamic symbol table agrees
+    import subprocess
+    syms = subprocess.run(["nm", "-D", "--defined-only", qd.LIB_PATH], capture_output=True,
+                          text=True, check=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", syms, re.M), n
+
+
+def test_gemv_validation(qd):
+    L = qd.lib()
+    p = C.c_void_p(16)
+    assert L.qd_gemv_q4_0(None, p, p, p, 4, 32, None) == qd._native.QD_EINVAL
+    assert L.qd_gemv_q4_0(p, p, p, p, 4, 33, None) == qd._native.QD_EINVAL
+    assert L.qd_gemv_q4_0(p, p, p, p, -1, 32, None) == qd._native.QD_EINVAL
+    assert L.qd_gemv_q4_0(p, p, p, p, 4, 32 * 100000, None) == qd._native.QD_EUNSUPPORTED
+    assert L.qd_gemv_q4_0(p, C.c_void_p(17), p, p, 4, 32, None) == qd._native.QD_EINVAL
+    assert b"aligned" in L.qd_last_error()
+
+
+def test_attention_validation(qd):
+    L = qd.lib()
+    p = 16
+    A = qd._native.AttnArgs
+    good = dict(q=p, k=p, v=p, block_tables=p, max_blocks_per_seq=4, block_size=16, kv_lens=p,
+                max_kv_len=64, B=1, nq=32, nkv=8, head_dim=128, scale=0.1, out=p)
+    ws = qd.attn_workspace_bytes(1, 32, 8, 128, 64)
+    assert ws > 0
+
+    def call(**kw):
+        d = dict(good, **kw)
+        return L.qd_attn_decode(C.byref(A(**d)), C.c_void_p(16), ws, None)
+
+    assert call(nq=30) == qd._native.QD_EINVAL
+    assert call(nq=48, nkv=4) == qd._native.QD_EUNSUPPORTED   # group of 12
+    assert call(head_dim=96) == qd._native.QD_EUNSUPPORTED
+    assert call(block_size=32) == qd._native.QD_EUNSUPPORTED
+    assert call(max_blocks_per_seq=3) == qd._native.QD_EINVAL
+    assert call(q=None) == qd._native.QD_EINVAL
+    assert L.qd_attn_decode(C.byref(A(**good)), C.c_void_p(16), ws - 1, None) == qd._native.QD_EINVAL
+    assert L.qd_attn_decode(None, C.c_void_p(16), ws, None) == qd._native.QD_EINVAL
+    assert qd.attn_workspace_bytes(0, 32, 8, 128, 64) == 0
+
+
+def _cfg_weights(qd, mi, **over):
+    """Config/weights structs for `mi` with fields overridden (all host memory)."""
+    N = qd._native
+    s = mi.shape
+    keep = []
+    layers = (N.LayerWeights * s.layers)()
+    for i, Lw in enumerate(mi.layers):
+        ns = [np.ascontiguousarray(a, dtype=np.float32) for a in
+              (Lw.attn_norm, Lw.ffn_norm, Lw.q_norm, Lw.k_norm)]
+        keep.append(ns)
+        layers[i] = N.LayerWeights(*[a.ctypes.data for a in ns],
+                                   *[N._q4(m) for m in (Lw.wq, Lw.wk, Lw.wv, Lw.wo, Lw.wgate,
+                                                         Lw.wup, Lw.wdown)])
+    fn = np.ascontiguousarray(mi.final_norm, dtype=np.float32)
+    inv = np.ascontiguousarray(mi.inv_freq, dtype=np.float32)
+    keep += [fn, inv, layers]
+    w = N.Weights(N._q4(mi.embed), N._q4(mi.lm_head), fn.ctypes.data, layers)
+    f = dict(hidden=s.hidden, layers=s.layers, n_heads=s.n_heads, n_kv=s.n_kv,
+             head_dim=s.head_dim, intermediate=s.intermediate, vocab=s.vocab, eps=s.eps,
+             rot_dim=s.rot_dim, inv_freq=inv.ctypes.data, tied=int(s.tied),
+             qk_norm=int(s.qk_norm), max_seq=s.max_seq, kv_paged=0, kv_block_size=16,
+             num_kv_blocks=0, block_table=None, use_graph=1)
+    f.update(over)
+    return N.Config(**f), w, keep
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(n_kv=3), -1), (dict(head_dim=96), -4), (dict(rot_dim=63), -1), (dict(rot_dim=66), -1),
+    (dict(hidden=0), -1), (dict(n_heads=12, n_kv=1), -4), (dict(kv_paged=1, kv_block_size=32), -4),
+    (dict(kv_paged=1, num_kv_blocks=2), -1), (dict(inv_freq=None), -1), (dict(vocab=1000), -1),
+    (dict(intermediate=512), -1), (dict(eps=-1.0), -1),
+])
+def test_create_validation(qd, over, code):
+    mi = synth.make_model("tiny")
+    cfg, w, keep = _cfg_weights(qd, mi, **over)
+    h = C.c_void_p()
+    rc = qd.lib().qd_create(C.byref(cfg), C.byref(w), None, C.byref(h))
+    assert rc == code, qd.lib().qd_last_error()
+    assert not h.value
+
+
+def test_create_rejects_bad_block_table(qd):
+    mi = synth.make_model("tiny")
+    for tbl in ([0, 0, 1], [0, 1, 9], [-1, 1, 2]):
+        t = np.array(tbl, dtype=np.int32)
+        cfg, w, keep = _cfg_weights(qd, mi, kv_paged=1, num_kv_blocks=4, block_table=t.ctypes.data)
+        h = C.c_void_p()
+        assert qd.lib().qd_create(C.byref(cfg), C.byref(w), None, C.byref(h)) == qd._native.QD_EINVAL
+
+
+def test_create_rejects_null_weight(qd):
+    mi = synth.make_model("tiny")
+    cfg, w, keep = _cfg_weights(qd, mi)
+    w.layers[1].wdown.qs = None
+    h = C.c_void_p()
+    assert qd.lib().qd_create(C.byref(cfg), C.byref(w), None, C.byref(h)) == qd._native.QD_EINVAL
+    assert b"layer 1 wdown" in qd.lib().qd_last_error()

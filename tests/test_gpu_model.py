@@ -1,0 +1,180 @@
+"""Whole decode step through the C ABI (qd_create / qd_decode_step /
+qd_set_prompt / qd_generate) against the f64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import LOGITS_BAR, TIE_MARGIN, check_greedy, host, load_golden, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return synth.make_model("tiny")
+
+
+@pytest.fixture(scope="module")
+def tiny_ref(tiny):
+    om = oracle.Model(tiny)
+    toks, margins, _ = oracle.generate(om, tiny.prompt, tiny.shape.gen)
+    # teacher-forced logits of the oracle's own sequence, every position
+    seq = list(tiny.prompt) + list(toks[:-1])
+    om2 = oracle.Model(tiny)
+    logits = np.stack([om2.step(int(t), p) for p, t in enumerate(seq)])
+    return toks, margins, seq, logits
+
+
+def _gen(model, prompt, G):
+    """qd_set_prompt + qd_generate over P+G-1 steps; returns all step argmaxes."""
+    import torch
+    P = len(prompt)
+    out = torch.full((P + G - 1,), -1, dtype=torch.int32, device="cuda")
+    model.set_prompt(prompt)
+    model.generate(0, P + G - 1, tokens=out)
+    return host(out)
+
+
+def _teacher_forced_logits(model, seq, V):
+    import torch
+    lg = torch.empty((len(seq), V), dtype=torch.float32, device="cuda")
+    nxt = torch.empty((len(seq),), dtype=torch.int32, device="cuda")
+    for p, t in enumerate(seq):
+        model.decode_step(int(t), p, logits=lg[p], next_tok=nxt[p:p + 1])
+    return host(lg), host(nxt)
+
+
+@pytest.mark.parametrize("graph", [True, False])
+def test_tiny_teacher_forced_logits(tiny, tiny_ref, graph):
+    import token_decode_q4_amd as qd
+    say(f"tiny teacher-forced logits graph={graph}")
+    toks, margins, seq, ref = tiny_ref
+    m = qd.Model(tiny, use_graph=graph)
+    lg, nxt = _teacher_forced_logits(m, seq, tiny.shape.vocab)
+    err = float(np.max(np.abs(lg - ref)))
+    say(f"tiny logits max abs err {err:.3e} (scale {np.abs(ref).max():.2f})")
+    assert err <= LOGITS_BAR
+    assert err <= 1e-4
+    # teacher-forced greedy choices equal the oracle's (f32-rounded) argmax
+    P = tiny.shape.prompt_len
+    ref_arg = np.argmax(ref.astype(np.float32), axis=1)
+    assert np.array_equal(nxt[P - 1:], ref_arg[P - 1:])
+    m.close()
+
+
+def test_tiny_free_running_greedy(tiny, tiny_ref):
+    import token_decode_q4_amd as qd
+    toks, margins, _, _ = tiny_ref
+    P, G = tiny.shape.prompt_len, tiny.shape.gen
+    m = qd.Model(tiny, use_graph=True)
+    got = _gen(m, tiny.prompt, G)[P - 1:]
+    n = check_greedy(got, toks, margins, "tiny")
+    assert n == G
+    m.close()
+
+
+def test_tiny_graph_equals_eager_bitwise(tiny):
+    import torch
+    import token_decode_q4_amd as qd
+    P, G = tiny.shape.prompt_len, tiny.shape.gen
+    res = []
+    for graph in (True, False):
+        m = qd.Model(tiny, use_graph=graph)
+        toks = _gen(m, tiny.prompt, G)
+        lg = torch.empty(tiny.shape.vocab, dtype=torch.float32, device="cuda")
+        m.generate(P + G - 2, 1, logits_last=lg)   # recompute the last step
+        res.append((toks, host(lg)))
+        m.close()
+    assert np.array_equal(res[0][0], res[1][0])
+    assert np.array_equal(res[0][1], res[1][1])
+
+
+def test_tiny_paged_equals_contiguous_bitwise(tiny):
+    import token_decode_q4_amd as qd
+    G = tiny.shape.gen
+    a = _gen(qd.Model(tiny, paged=False), tiny.prompt, G)
+    # shuffled physical blocks, more blocks than needed
+    tbl = np.random.default_rng(3).permutation(8).astype(np.int32)
+    mi = synth.ModelInputs(tiny.shape, tiny.embed, tiny.layers, tiny.final_norm, tiny.lm_head,
+                           tiny.inv_freq, tiny.prompt, tbl)
+    b = _gen(qd.Model(mi, paged=True, num_kv_blocks=8), tiny.prompt, G)
+    assert np.array_equal(a, b)
+
+
+def test_tiny_decode_step_rejects_out_of_range(tiny):
+    import token_decode_q4_amd as qd
+    m = qd.Model(tiny)
+    for tok, pos, code in [(tiny.shape.vocab, 0, qd._native.QD_ERANGE), (-1, 0, qd._native.QD_ERANGE),
+                           (0, tiny.shape.max_seq, qd._native.QD_ERANGE), (0, -1, qd._native.QD_ERANGE)]:
+        with pytest.raises(qd.QdError) as ei:
+            m.decode_step(tok, pos)
+        assert ei.value.code == code
+    with pytest.raises(qd.QdError):
+        m.generate(tiny.shape.max_seq - 2, 3)
+    m.close()
+
+
+def _golden_run(name):
+    import torch
+    import token_decode_q4_amd as qd
+    g = load_golden(name)
+    if g is None:
+        pytest.skip(f"tests/golden/greedy_{name}.json not generated")
+    say(f"{name}: generating inputs")
+    mi = synth.make_model(name)
+    assert mi.digest == g["digest"], "inputs differ from the ones the golden file was made from"
+    s = mi.shape
+    P, G = s.prompt_len, s.gen
+    say(f"{name}: qd_create")
+    m = qd.Model(mi, use_graph=True)
+    V = s.vocab
+    # sample points: prefill positions and greedy steps (greedy step i is at position P-1+i)
+    points = {}
+    for tag in g["samples"]:
+        kind, k = tag.split(":")
+        pos = int(k) if kind == "prefill" else P - 1 + int(k)
+        points[pos] = tag
+    toks = torch.full((P + G - 1,), -1, dtype=torch.int32, device="cuda")
+    lg = torch.empty(V, dtype=torch.float32, device="cuda")
+    m.set_prompt(mi.prompt)
+    got_logits = {}
+    pos = 0
+    for stop in sorted(points) + [P + G - 1]:
+        if stop < pos:
+            continue
+        n = stop + 1 - pos if stop in points else stop - pos
+        if n > 0:
+            m.generate(pos, n, tokens=toks[pos:pos + n], logits_last=lg)
+            pos += n
+            if stop in points:
+                got_logits[points[stop]] = host(lg).copy()
+        say(f"{name}: reached position {pos}")
+    all_toks = host(toks)
+    m.close()
+    greedy = all_toks[P - 1:]
+    n_eq = check_greedy(greedy, g["tokens"], g["margins"], name)
+    worst = 0.0
+    for tag, lv in got_logits.items():
+        kind, k = tag.split(":")
+        if kind == "greedy" and int(k) > n_eq:
+            continue   # after a near-tie divergence the contexts differ
+        smp = g["samples"][tag]
+        idx = np.array(smp["idx"])
+        err = float(np.max(np.abs(lv[idx] - np.array(smp["val"]))))
+        tidx = np.array(smp["top_idx"])
+        err = max(err, float(np.max(np.abs(lv[tidx] - np.array(smp["top_val"])))))
+        worst = max(worst, err)
+        say(f"{name}: logits {tag} max abs err {err:.3e}")
+    assert worst <= LOGITS_BAR
+    return n_eq, worst
+
+
+def test_qwen3_06b_shape_vs_golden():
+    n_eq, worst = _golden_run("qwen3-0.6b")
+    assert worst <= 1e-3
+
+
+def test_qwen3_8b_shape_vs_golden():
+    n_eq, worst = _golden_run("qwen3-8b")
+    assert worst <= 1e-3

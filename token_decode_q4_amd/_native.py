@@ -1,0 +1,204 @@
+"""ctypes binding of ``libqd.so`` (the C ABI declared in ``include/qd.h``).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+library.  Device buffers are torch tensors on ``cuda`` (ROCm), streams are
+torch streams; host arrays are numpy arrays.  If the library has not been
+built this module raises on first use: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqd.so")
+
+QD_OK, QD_EINVAL, QD_ERANGE, QD_ENOMEM, QD_EUNSUPPORTED, QD_EHIP = 0, -1, -2, -3, -4, -5
+
+# every function declared in include/qd.h
+EXPORTS = ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate",
+           "qd_gemv_q4_0", "qd_attn_workspace_bytes", "qd_attn_decode", "qd_last_error")
+
+
+class QdError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"qd error {code}: {msg}")
+        self.code = code
+
+
+class Q4(C.Structure):
+    _fields_ = [("d", C.c_void_p), ("qs", C.c_void_p), ("rows", C.c_int32), ("cols", C.c_int32)]
+
+
+class LayerWeights(C.Structure):
+    _fields_ = [("attn_norm", C.c_void_p), ("ffn_norm", C.c_void_p), ("q_norm", C.c_void_p),
+                ("k_norm", C.c_void_p)] + [(n, Q4) for n in
+                                           ("wq", "wk", "wv", "wo", "wgate", "wup", "wdown")]
+
+
+class Weights(C.Structure):
+    _fields_ = [("embed", Q4), ("lm_head", Q4), ("final_norm", C.c_void_p),
+                ("layers", C.POINTER(LayerWeights))]
+
+
+class Config(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("layers", C.c_int32), ("n_heads", C.c_int32),
+                ("n_kv", C.c_int32), ("head_dim", C.c_int32), ("intermediate", C.c_int32),
+                ("vocab", C.c_int32), ("eps", C.c_float), ("rot_dim", C.c_int32),
+                ("inv_freq", C.c_void_p), ("tied", C.c_int32), ("qk_norm", C.c_int32),
+                ("max_seq", C.c_int32), ("kv_paged", C.c_int32), ("kv_block_size", C.c_int32),
+                ("num_kv_blocks", C.c_int32), ("block_table", C.c_void_p),
+                ("use_graph", C.c_int32)]
+
+
+class AttnArgs(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p),
+                ("block_tables", C.c_void_p), ("max_blocks_per_seq", C.c_int32),
+                ("block_size", C.c_int32), ("kv_lens", C.c_void_p), ("max_kv_len", C.c_int32),
+                ("B", C.c_int32), ("nq", C.c_int32), ("nkv", C.c_int32), ("head_dim", C.c_int32),
+                ("scale", C.c_float), ("out", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run python token_decode_q4_amd/build.py")
+        L = C.CDLL(LIB_PATH)
+        L.qd_create.argtypes = [C.POINTER(Config), C.POINTER(Weights), C.c_void_p,
+                                C.POINTER(C.c_void_p)]
+        L.qd_destroy.argtypes = [C.c_void_p]
+        L.qd_decode_step.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                     C.c_void_p]
+        L.qd_set_prompt.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p]
+        L.qd_generate.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                  C.c_void_p]
+        L.qd_gemv_q4_0.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                                   C.c_int32, C.c_void_p]
+        L.qd_attn_workspace_bytes.restype = C.c_size_t
+        L.qd_attn_workspace_bytes.argtypes = [C.c_int32] * 5
+        L.qd_attn_decode.argtypes = [C.POINTER(AttnArgs), C.c_void_p, C.c_size_t, C.c_void_p]
+        L.qd_last_error.restype = C.c_char_p
+        for n in ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate",
+                  "qd_gemv_q4_0", "qd_attn_decode"):
+            getattr(L, n).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def check(rc: int):
+    if rc != QD_OK:
+        raise QdError(rc, lib().qd_last_error().decode())
+    return rc
+
+
+def _ptr(t) -> int | None:
+    """Device pointer of a torch tensor (or None)."""
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+# ----------------------------------------------------------------- standalone ops
+
+def gemv_q4_0(d, qs, x, y, stream=None) -> int:
+    """y[N] = W x on the device; d uint16/int16 [N, K/32], qs uint8 [N, K/32, 16]."""
+    N = d.shape[0]
+    K = x.shape[0]
+    return check(lib().qd_gemv_q4_0(_ptr(d), _ptr(qs), _ptr(x), _ptr(y), N, K, _stream(stream)))
+
+
+def attn_workspace_bytes(B, nq, nkv, head_dim, max_kv_len) -> int:
+    return int(lib().qd_attn_workspace_bytes(B, nq, nkv, head_dim, max_kv_len))
+
+
+def attn_decode(q, k, v, kv_lens, max_kv_len, nkv, scale, out, workspace, block_tables=None,
+                block_size=16, stream=None) -> int:
+    B, nq, hd = q.shape
+    a = AttnArgs(_ptr(q), _ptr(k), _ptr(v), _ptr(block_tables),
+                 0 if block_tables is None else block_tables.shape[1], block_size, _ptr(kv_lens),
+                 int(max_kv_len), B, nq, nkv, hd, float(scale), _ptr(out))
+    return check(lib().qd_attn_decode(C.byref(a), _ptr(workspace), workspace.numel() *
+                                      workspace.element_size(), _stream(stream)))
+
+
+# ----------------------------------------------------------------- model
+
+def _q4(W) -> Q4:
+    return Q4(W.d.ctypes.data, W.qs.ctypes.data, W.rows, W.cols)
+
+
+class Model:
+    """A decode model built from host q4_0 weights (``synth.ModelInputs``-like)."""
+
+    def __init__(self, mi, use_graph: bool = True, stream=None, paged: bool | None = None,
+                 max_seq: int | None = None, num_kv_blocks: int | None = None):
+        s = mi.shape
+        self.shape = s
+        self.vocab = s.vocab
+        self.max_seq = max_seq or s.max_seq
+        paged = s.kv_paged if paged is None else paged
+        keep = []
+        layers = (LayerWeights * s.layers)()
+        for i, L in enumerate(mi.layers):
+            ns = [np.ascontiguousarray(a, dtype=np.float32) for a in
+                  (L.attn_norm, L.ffn_norm, L.q_norm, L.k_norm)]
+            keep.append(ns)
+            layers[i] = LayerWeights(*[a.ctypes.data for a in ns],
+                                     *[_q4(m) for m in (L.wq, L.wk, L.wv, L.wo, L.wgate, L.wup,
+                                                        L.wdown)])
+        fn = np.ascontiguousarray(mi.final_norm, dtype=np.float32)
+        inv = np.ascontiguousarray(mi.inv_freq, dtype=np.float32)
+        nblk_need = (self.max_seq + 15) // 16
+        table = None
+        if paged:
+            if len(mi.block_table) >= nblk_need:
+                table = np.ascontiguousarray(mi.block_table[:nblk_need], dtype=np.int32)
+            nblocks = num_kv_blocks or (max(int(table.max()) + 1, nblk_need) if table is not None
+                                        else nblk_need)
+        else:
+            nblocks = 0
+        w = Weights(_q4(mi.embed), _q4(mi.lm_head), fn.ctypes.data, layers)
+        cfg = Config(s.hidden, s.layers, s.n_heads, s.n_kv, s.head_dim, s.intermediate, s.vocab,
+                     float(s.eps), s.rot_dim, inv.ctypes.data, int(s.tied), int(s.qk_norm),
+                     self.max_seq, int(bool(paged)), 16, nblocks,
+                     None if table is None else table.ctypes.data, int(bool(use_graph)))
+        h = C.c_void_p()
+        check(lib().qd_create(C.byref(cfg), C.byref(w), _stream(stream), C.byref(h)))
+        self._h = h
+        del keep
+
+    def decode_step(self, token: int, pos: int, logits=None, next_tok=None, stream=None):
+        return check(lib().qd_decode_step(self._h, int(token), int(pos), _ptr(logits),
+                                          _ptr(next_tok), _stream(stream)))
+
+    def set_prompt(self, tokens, stream=None):
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        return check(lib().qd_set_prompt(self._h, t.ctypes.data, t.size, _stream(stream)))
+
+    def generate(self, pos0: int, n_steps: int, tokens=None, logits_last=None, stream=None):
+        return check(lib().qd_generate(self._h, int(pos0), int(n_steps), _ptr(tokens),
+                                       _ptr(logits_last), _stream(stream)))
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().qd_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

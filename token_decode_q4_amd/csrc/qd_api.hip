@@ -1,0 +1,807 @@
+// qd_api.hip -- C ABI and runtime of the batch-1 q4_0 decode library (gfx950).
+//
+// The runtime owns: device copies of the weights (q|k|v rows concatenated,
+// gate/up rows interleaved), the f16 KV cache (contiguous, or a paged pool
+// with a block table fixed at create time), every step buffer (allocated
+// once in qd_create: nothing is allocated per step), host-built rotary
+// cos/sin tables, the device-resident step state (position, stored token per
+// position, forced-prefix length) and an optional hipGraph of one step.
+// (inferencelayer cuda_llm.rs page, CudaQwen3 fields, step, seed, capture,
+// run_graph, tokens; ferrum-kernels cuda_decode.rs page, GpuPagedKvPool use
+// and init_kv_cache_paged.)
+#include "qd.h"
+
+#include "step_kernels.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace qd;
+
+// ------------------------------------------------------------------ errors
+
+static thread_local std::string g_err;
+
+static int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+#define HIP_TRY(expr)                                                                     \
+    do {                                                                                  \
+        hipError_t e_ = (expr);                                                           \
+        if (e_ != hipSuccess)                                                             \
+            return fail(QD_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));          \
+    } while (0)
+
+extern "C" const char* qd_last_error(void) { return g_err.c_str(); }
+
+// ------------------------------------------------------------------ GEMV launch
+
+static constexpr int GEMV_NWAVES = 4;
+static constexpr int GEMV_MAX_LDS = 64 * 1024;
+
+// lanes per row: the largest of 64/32/16/8 dividing the number of blocks
+static int pick_lpr(int nb)
+{
+    for (int l = 64; l >= 8; l >>= 1)
+        if (nb % l == 0)
+            return l;
+    return 8;
+}
+
+static int rows_per_tile(int lpr, int rps) { return GEMV_NWAVES * (WAVE / lpr) * rps; }
+
+static size_t gemv_lds_bytes(int nb) { return (size_t)gemv_lds_floats(nb) * sizeof(float); }
+
+static int gemv_grid(int ntiles, int cap) { return ntiles < cap ? (ntiles > 0 ? ntiles : 1) : cap; }
+
+#define QD_DISPATCH_LPR(lpr, RPS_, BODY)                                                  \
+    switch (lpr) {                                                                        \
+    case 64: { constexpr int LPR = 64, RPS = RPS_; BODY; } break;                         \
+    case 32: { constexpr int LPR = 32, RPS = RPS_; BODY; } break;                         \
+    case 16: { constexpr int LPR = 16, RPS = RPS_; BODY; } break;                         \
+    default: { constexpr int LPR = 8, RPS = RPS_; BODY; } break;                          \
+    }
+
+static hipError_t launch_gemv_plain(const uint16_t* d, const uint8_t* q, const float* x, float* y,
+                                    int N, int K, hipStream_t s)
+{
+    const int nb = K / 32, lpr = pick_lpr(nb);
+    const int ntiles = (N + rows_per_tile(lpr, 4) - 1) / rows_per_tile(lpr, 4);
+    const int grid = gemv_grid(ntiles, 2048);
+    QD_DISPATCH_LPR(lpr, 4, {
+        hipLaunchKernelGGL((k_gemv_plain<LPR, RPS, GEMV_NWAVES>), dim3(grid),
+                           dim3(GEMV_NWAVES * WAVE), gemv_lds_bytes(nb), s, d, q, x, y, N, nb);
+    });
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ model
+
+struct DevQ4 {
+    uint16_t* d = nullptr;
+    uint8_t* qs = nullptr;
+    int rows = 0, cols = 0, nb = 0;
+};
+
+struct DevLayer {
+    DevQ4 qkv, o, gu, down;
+    float *attn_norm = nullptr, *ffn_norm = nullptr, *q_norm = nullptr, *k_norm = nullptr;
+    uint16_t *kc = nullptr, *vc = nullptr;
+};
+
+struct qd_model {
+    int H, L, nq, nkv, hd, I, V, rot, qkv_rows, max_seq, qk_norm, paged, nblocks;
+    float eps;
+    std::vector<DevLayer> layers;
+    DevQ4 embed, lm;
+    float* final_norm = nullptr;
+    float *rope_cos = nullptr, *rope_sin = nullptr;
+    int32_t* table = nullptr;
+    // step buffers
+    float *x = nullptr, *u = nullptr, *ss_part = nullptr, *qkv_raw = nullptr, *qbuf = nullptr;
+    float *attn = nullptr, *act = nullptr, *logits = nullptr, *arg_val = nullptr;
+    int32_t* arg_idx = nullptr;
+    unsigned int* counters = nullptr;  // [qkv heads] [attention nkv] [lm head 1]
+    float* attn_part = nullptr;
+    int attn_chunk = 0, attn_nsplit = 0;
+    StepState* st = nullptr;
+    int32_t *ids = nullptr, *pred = nullptr;
+    // launch geometry
+    int lpr_qkv, rps_qkv, grid_qkv, lpr_o, grid_o, lpr_gu, grid_gu, lpr_down, grid_down;
+    int lpr_lm, grid_lm;
+    // graph
+    int use_graph = 0;
+    hipStream_t cap_stream = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    std::vector<void*> allocs;
+    StepState* h_state = nullptr;  // pinned host staging
+};
+
+static int dev_alloc(qd_model* m, void** p, size_t bytes)
+{
+    if (bytes == 0)
+        bytes = 16;
+    hipError_t e = hipMalloc(p, bytes);
+    if (e != hipSuccess) {
+        *p = nullptr;
+        return fail(e == hipErrorOutOfMemory ? QD_ENOMEM : QD_EHIP, "hipMalloc(%zu): %s", bytes,
+                    hipGetErrorString(e));
+    }
+    m->allocs.push_back(*p);
+    return QD_OK;
+}
+
+#define QD_TRY(expr)                  \
+    do {                              \
+        int r_ = (expr);              \
+        if (r_ != QD_OK)              \
+            return r_;                \
+    } while (0)
+
+template <class T>
+static int dev_alloc_t(qd_model* m, T** p, size_t count)
+{
+    return dev_alloc(m, reinterpret_cast<void**>(p), count * sizeof(T));
+}
+
+static int check_q4(const qd_q4_0& w, int rows, int cols, const char* name)
+{
+    if (!w.d || !w.qs)
+        return fail(QD_EINVAL, "%s: null pointer", name);
+    if (w.rows != rows || w.cols != cols)
+        return fail(QD_EINVAL, "%s: shape [%d, %d], expected [%d, %d]", name, w.rows, w.cols, rows,
+                    cols);
+    return QD_OK;
+}
+
+// Upload row blocks of several host q4_0 matrices into one device matrix.
+// `order` lists (source index, source row) for every destination row.
+struct RowSrc {
+    const qd_q4_0* w;
+    int row;
+};
+
+static int upload_rows(qd_model* m, DevQ4* dst, const std::vector<RowSrc>& rows, int cols,
+                       hipStream_t s)
+{
+    const int nb = cols / 32;
+    dst->rows = (int)rows.size();
+    dst->cols = cols;
+    dst->nb = nb;
+    QD_TRY(dev_alloc_t(m, &dst->d, (size_t)dst->rows * nb));
+    QD_TRY(dev_alloc_t(m, &dst->qs, (size_t)dst->rows * nb * 16));
+    std::vector<uint16_t> hd((size_t)dst->rows * nb);
+    std::vector<uint8_t> hq((size_t)dst->rows * nb * 16);
+    for (size_t r = 0; r < rows.size(); ++r) {
+        const qd_q4_0* w = rows[r].w;
+        const size_t sr = (size_t)rows[r].row;
+        memcpy(&hd[r * nb], w->d + sr * nb, sizeof(uint16_t) * nb);
+        memcpy(&hq[r * nb * 16], w->qs + sr * nb * 16, (size_t)nb * 16);
+    }
+    HIP_TRY(hipMemcpyAsync(dst->d, hd.data(), hd.size() * sizeof(uint16_t), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(dst->qs, hq.data(), hq.size(), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    return QD_OK;
+}
+
+static int upload_whole(qd_model* m, DevQ4* dst, const qd_q4_0& w, hipStream_t s)
+{
+    const int nb = w.cols / 32;
+    dst->rows = w.rows;
+    dst->cols = w.cols;
+    dst->nb = nb;
+    QD_TRY(dev_alloc_t(m, &dst->d, (size_t)w.rows * nb));
+    QD_TRY(dev_alloc_t(m, &dst->qs, (size_t)w.rows * nb * 16));
+    HIP_TRY(hipMemcpyAsync(dst->d, w.d, (size_t)w.rows * nb * sizeof(uint16_t), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(dst->qs, w.qs, (size_t)w.rows * nb * 16, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    return QD_OK;
+}
+
+static int upload_f32(qd_model* m, float** dst, const float* src, size_t n, hipStream_t s)
+{
+    QD_TRY(dev_alloc_t(m, dst, n));
+    HIP_TRY(hipMemcpyAsync(*dst, src, n * sizeof(float), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    return QD_OK;
+}
+
+static void free_model(qd_model* m)
+{
+    if (!m)
+        return;
+    if (m->exec)
+        (void)hipGraphExecDestroy(m->exec);
+    if (m->graph)
+        (void)hipGraphDestroy(m->graph);
+    if (m->cap_stream)
+        (void)hipStreamDestroy(m->cap_stream);
+    for (void* p : m->allocs)
+        (void)hipFree(p);
+    if (m->h_state)
+        (void)hipHostFree(m->h_state);
+    delete m;
+}
+
+static int validate_config(const qd_config* c, const qd_weights* w)
+{
+    if (!c || !w)
+        return fail(QD_EINVAL, "null config or weights");
+    if (c->hidden <= 0 || c->layers <= 0 || c->n_heads <= 0 || c->n_kv <= 0 || c->head_dim <= 0 ||
+        c->intermediate <= 0 || c->vocab <= 0 || c->max_seq <= 0)
+        return fail(QD_EINVAL, "sizes must be positive");
+    if (c->n_heads % c->n_kv)
+        return fail(QD_EINVAL, "n_heads %% n_kv != 0");
+    const int gq = c->n_heads / c->n_kv;
+    if (gq != 1 && gq != 2 && gq != 4 && gq != 8)
+        return fail(QD_EUNSUPPORTED, "GQA group %d not in {1,2,4,8}", gq);
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return fail(QD_EUNSUPPORTED, "head_dim %d not in {64,128}", c->head_dim);
+    if (c->hidden % 32 || c->intermediate % 32 || (c->n_heads * c->head_dim) % 32)
+        return fail(QD_EUNSUPPORTED, "hidden, intermediate and n_heads*head_dim must be multiples of 32");
+    if (c->rot_dim < 0 || c->rot_dim > c->head_dim || (c->rot_dim & 1))
+        return fail(QD_EINVAL, "rot_dim must be even and <= head_dim");
+    if (c->rot_dim > 0 && !c->inv_freq)
+        return fail(QD_EINVAL, "inv_freq is null");
+    if (!(c->eps >= 0.f))
+        return fail(QD_EINVAL, "eps must be >= 0");
+    const size_t kmax = (size_t)GEMV_MAX_LDS / (sizeof(float) * (XPAD + 1)) * 32;
+    if ((size_t)c->hidden > kmax || (size_t)c->intermediate > kmax ||
+        (size_t)c->n_heads * c->head_dim > kmax)
+        return fail(QD_EUNSUPPORTED, "GEMV input length above %zu", kmax);
+    if (c->kv_paged) {
+        if (c->kv_block_size != ATT_BS)
+            return fail(QD_EUNSUPPORTED, "kv_block_size %d (only %d)", c->kv_block_size, ATT_BS);
+        const int need = (c->max_seq + ATT_BS - 1) / ATT_BS;
+        if (c->num_kv_blocks < need)
+            return fail(QD_EINVAL, "num_kv_blocks %d < %d blocks for max_seq", c->num_kv_blocks, need);
+        if (c->block_table) {
+            std::vector<char> seen(c->num_kv_blocks, 0);
+            for (int i = 0; i < need; ++i) {
+                const int p = c->block_table[i];
+                if (p < 0 || p >= c->num_kv_blocks)
+                    return fail(QD_EINVAL, "block_table[%d] = %d out of range", i, p);
+                if (seen[p])
+                    return fail(QD_EINVAL, "block_table maps two logical blocks to physical %d", p);
+                seen[p] = 1;
+            }
+        }
+    }
+    const int H = c->hidden, hd = c->head_dim, nqd = c->n_heads * hd, nkd = c->n_kv * hd;
+    QD_TRY(check_q4(w->embed, c->vocab, H, "embed"));
+    if (!c->tied)
+        QD_TRY(check_q4(w->lm_head, c->vocab, H, "lm_head"));
+    if (!w->final_norm || !w->layers)
+        return fail(QD_EINVAL, "final_norm or layers is null");
+    for (int l = 0; l < c->layers; ++l) {
+        const qd_layer_weights& L = w->layers[l];
+        char nm[64];
+        if (!L.attn_norm || !L.ffn_norm || (c->qk_norm && (!L.q_norm || !L.k_norm)))
+            return fail(QD_EINVAL, "layer %d: null norm weight", l);
+        snprintf(nm, sizeof nm, "layer %d wq", l);
+        QD_TRY(check_q4(L.wq, nqd, H, nm));
+        snprintf(nm, sizeof nm, "layer %d wk", l);
+        QD_TRY(check_q4(L.wk, nkd, H, nm));
+        snprintf(nm, sizeof nm, "layer %d wv", l);
+        QD_TRY(check_q4(L.wv, nkd, H, nm));
+        snprintf(nm, sizeof nm, "layer %d wo", l);
+        QD_TRY(check_q4(L.wo, H, nqd, nm));
+        snprintf(nm, sizeof nm, "layer %d wgate", l);
+        QD_TRY(check_q4(L.wgate, c->intermediate, H, nm));
+        snprintf(nm, sizeof nm, "layer %d wup", l);
+        QD_TRY(check_q4(L.wup, c->intermediate, H, nm));
+        snprintf(nm, sizeof nm, "layer %d wdown", l);
+        QD_TRY(check_q4(L.wdown, H, c->intermediate, nm));
+    }
+    return QD_OK;
+}
+
+// Enqueue one decode step (position and token come from the device state).
+static int enqueue_step(qd_model* m, hipStream_t s)
+{
+    const int H = m->H;
+    hipLaunchKernelGGL(k_embed, dim3(1), dim3(256), 0, s, m->embed.d, m->embed.qs, H, m->V, m->st,
+                       m->ids, m->max_seq, m->layers[0].attn_norm, m->x, m->u, m->ss_part);
+    int n_part = 1;
+    for (int l = 0; l < m->L; ++l) {
+        DevLayer& Ly = m->layers[l];
+        // q | k | v, per-head norm + rotary + KV write
+        QkvEpi e;
+        e.raw = m->qkv_raw;
+        e.q_out = m->qbuf;
+        e.nq = m->nq;
+        e.nkv = m->nkv;
+        e.hd = m->hd;
+        e.rot = m->rot;
+        e.qk_norm = m->qk_norm;
+        e.eps = m->eps;
+        e.q_norm = Ly.q_norm;
+        e.k_norm = Ly.k_norm;
+        e.rope_cos = m->rope_cos;
+        e.rope_sin = m->rope_sin;
+        e.st = m->st;
+        e.max_seq = m->max_seq;
+        e.kc = Ly.kc;
+        e.vc = Ly.vc;
+        e.paged = m->paged;
+        e.table = m->table;
+        e.counters = m->counters;
+        {
+            const int nb = Ly.qkv.nb;
+            if (m->rps_qkv == 4) {
+                QD_DISPATCH_LPR(m->lpr_qkv, 4, {
+                    hipLaunchKernelGGL((k_gemv_qkv<LPR, RPS, GEMV_NWAVES>), dim3(m->grid_qkv),
+                                       dim3(GEMV_NWAVES * WAVE), gemv_lds_bytes(nb), s, Ly.qkv.d,
+                                       Ly.qkv.qs, m->u, Ly.qkv.rows, nb, m->ss_part, n_part, H,
+                                       m->eps, e);
+                });
+            } else if (m->rps_qkv == 2) {
+                QD_DISPATCH_LPR(m->lpr_qkv, 2, {
+                    hipLaunchKernelGGL((k_gemv_qkv<LPR, RPS, GEMV_NWAVES>), dim3(m->grid_qkv),
+                                       dim3(GEMV_NWAVES * WAVE), gemv_lds_bytes(nb), s, Ly.qkv.d,
+                                       Ly.qkv.qs, m->u, Ly.qkv.rows, nb, m->ss_part, n_part, H,
+                                       m->eps, e);
+                });
+            } else {
+                QD_DISPATCH_LPR(m->lpr_qkv, 1, {
+                    hipLaunchKernelGGL((k_gemv_qkv<LPR, RPS, GEMV_NWAVES>), dim3(m->grid_qkv),
+                                       dim3(GEMV_NWAVES * WAVE), gemv_lds_bytes(nb), s, Ly.qkv.d,
+                                       Ly.qkv.qs, m->u, Ly.qkv.rows, nb, m->ss_part, n_part, H,
+                                       m->eps, e);
+                });
+            }
+        }
+        // attention
+        {
+            AttnParams p;
+            p.q = m->qbuf;
+            p.k = Ly.kc;
+            p.v = Ly.vc;
+            p.tables = m->paged ? m->table : nullptr;
+            p.mbps = (m->max_seq + ATT_BS - 1) / ATT_BS;
+            p.kv_lens = nullptr;
+            p.pos = &m->st->pos;
+            p.max_kv = m->max_seq;
+            p.nq = m->nq;
+            p.nkv = m->nkv;
+            p.scale = 1.0f / sqrtf((float)m->hd);
+            p.chunk = m->attn_chunk;
+            p.nsplit = m->attn_nsplit;
+            p.part = m->attn_part;
+            p.counters = m->counters + (m->nq + 2 * m->nkv);
+            p.out = m->attn;
+            const dim3 grid(m->attn_nsplit, m->nkv, 1);
+            const int gq = m->nq / m->nkv;
+#define QD_ATT(HD_, GQ_)                                                                          \
+    if (m->paged)                                                                                 \
+        hipLaunchKernelGGL((k_attn_decode<HD_, GQ_, true>), grid, dim3(ATT_NT), 0, s, p);         \
+    else                                                                                          \
+        hipLaunchKernelGGL((k_attn_decode<HD_, GQ_, false>), grid, dim3(ATT_NT), 0, s, p);
+            if (m->hd == 128) {
+                if (gq == 1) { QD_ATT(128, 1) } else if (gq == 2) { QD_ATT(128, 2) }
+                else if (gq == 4) { QD_ATT(128, 4) } else { QD_ATT(128, 8) }
+            } else {
+                if (gq == 1) { QD_ATT(64, 1) } else if (gq == 2) { QD_ATT(64, 2) }
+                else if (gq == 4) { QD_ATT(64, 4) } else { QD_ATT(64, 8) }
+            }
+#undef QD_ATT
+        }
+        // o-proj + residual, u = x * ffn_norm
+        QD_DISPATCH_LPR(m->lpr_o, 4, {
+            hipLaunchKernelGGL((k_gemv_residual<LPR, RPS, GEMV_NWAVES>), dim3(m->grid_o),
+                               dim3(GEMV_NWAVES * WAVE), gemv_lds_bytes(Ly.o.nb), s, Ly.o.d, Ly.o.qs,
+                               m->attn, Ly.o.rows, Ly.o.nb, m->x, m->u, Ly.ffn_norm, m->ss_part);
+        });
+        n_part = m->grid_o;
+        // gate|up + SwiGLU
+        QD_DISPATCH_LPR(m->lpr_gu, 4, {
+            hipLaunchKernelGGL((k_gemv_swiglu<LPR, RPS, GEMV_NWAVES>), dim3(m->grid_gu),
+                               dim3(GEMV_NWAVES * WAVE), gemv_lds_bytes(Ly.gu.nb), s, Ly.gu.d,
+                               Ly.gu.qs, m->u, Ly.gu.rows, Ly.gu.nb, m->ss_part, n_part, H, m->eps,
+                               m->act);
+        });
+        // down + residual, u = x * (next attn_norm | final_norm)
+        const float* wn = (l + 1 < m->L) ? m->layers[l + 1].attn_norm : m->final_norm;
+        QD_DISPATCH_LPR(m->lpr_down, 4, {
+            hipLaunchKernelGGL((k_gemv_residual<LPR, RPS, GEMV_NWAVES>), dim3(m->grid_down),
+                               dim3(GEMV_NWAVES * WAVE), gemv_lds_bytes(Ly.down.nb), s, Ly.down.d,
+                               Ly.down.qs, m->act, Ly.down.rows, Ly.down.nb, m->x, m->u, wn,
+                               m->ss_part);
+        });
+        n_part = m->grid_down;
+    }
+    QD_DISPATCH_LPR(m->lpr_lm, 4, {
+        hipLaunchKernelGGL((k_gemv_lmhead<LPR, RPS, GEMV_NWAVES>), dim3(m->grid_lm),
+                           dim3(GEMV_NWAVES * WAVE), gemv_lds_bytes(m->lm.nb), s, m->lm.d, m->lm.qs,
+                           m->u, m->lm.rows, m->lm.nb, m->ss_part, n_part, H, m->eps, m->logits,
+                           m->arg_val, m->arg_idx, m->counters + (m->nq + 2 * m->nkv) + m->nkv,
+                           m->st, m->ids, m->pred, m->max_seq);
+    });
+    HIP_TRY(hipGetLastError());
+    return QD_OK;
+}
+
+static int run_steps(qd_model* m, int n, hipStream_t s)
+{
+    for (int i = 0; i < n; ++i) {
+        if (m->use_graph) {
+            HIP_TRY(hipGraphLaunch(m->exec, s));
+        } else {
+            QD_TRY(enqueue_step(m, s));
+        }
+    }
+    return QD_OK;
+}
+
+// tiny kernel: set position / forced prefix / a stored token (so that setting
+// state is an ordinary stream operation, never a host-synchronous copy)
+__global__ void k_set_state(StepState* st, int32_t* ids, int pos, int n_forced, int tok_pos,
+                            int tok)
+{
+    if (threadIdx.x == 0) {
+        st->pos = pos;
+        if (n_forced >= 0)
+            st->n_forced = n_forced;
+        if (tok_pos >= 0)
+            ids[tok_pos] = tok;
+    }
+}
+
+extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream stream, qd_model** out)
+{
+    if (!out)
+        return fail(QD_EINVAL, "out is null");
+    *out = nullptr;
+    QD_TRY(validate_config(cfg, w));
+    hipStream_t s = (hipStream_t)stream;
+    qd_model* m = new qd_model();
+    auto bail = [&](int rc) {
+        free_model(m);
+        return rc;
+    };
+    const qd_config& c = *cfg;
+    m->H = c.hidden;
+    m->L = c.layers;
+    m->nq = c.n_heads;
+    m->nkv = c.n_kv;
+    m->hd = c.head_dim;
+    m->I = c.intermediate;
+    m->V = c.vocab;
+    m->rot = c.rot_dim;
+    m->eps = c.eps;
+    m->max_seq = c.max_seq;
+    m->qk_norm = c.qk_norm ? 1 : 0;
+    m->paged = c.kv_paged ? 1 : 0;
+    m->nblocks = c.kv_paged ? c.num_kv_blocks : 0;
+    m->qkv_rows = (m->nq + 2 * m->nkv) * m->hd;
+    m->use_graph = c.use_graph ? 1 : 0;
+    const int H = m->H, hd = m->hd, nqd = m->nq * hd, nkd = m->nkv * hd;
+
+    int rc;
+    // weights
+    m->layers.resize(m->L);
+    for (int l = 0; l < m->L; ++l) {
+        const qd_layer_weights& S = w->layers[l];
+        DevLayer& D = m->layers[l];
+        std::vector<RowSrc> rows;
+        rows.reserve(m->qkv_rows);
+        for (int r = 0; r < nqd; ++r) rows.push_back({&S.wq, r});
+        for (int r = 0; r < nkd; ++r) rows.push_back({&S.wk, r});
+        for (int r = 0; r < nkd; ++r) rows.push_back({&S.wv, r});
+        if ((rc = upload_rows(m, &D.qkv, rows, H, s))) return bail(rc);
+        rows.clear();
+        for (int r = 0; r < m->I; ++r) {
+            rows.push_back({&S.wgate, r});
+            rows.push_back({&S.wup, r});
+        }
+        if ((rc = upload_rows(m, &D.gu, rows, H, s))) return bail(rc);
+        if ((rc = upload_whole(m, &D.o, S.wo, s))) return bail(rc);
+        if ((rc = upload_whole(m, &D.down, S.wdown, s))) return bail(rc);
+        if ((rc = upload_f32(m, &D.attn_norm, S.attn_norm, H, s))) return bail(rc);
+        if ((rc = upload_f32(m, &D.ffn_norm, S.ffn_norm, H, s))) return bail(rc);
+        if (m->qk_norm) {
+            if ((rc = upload_f32(m, &D.q_norm, S.q_norm, hd, s))) return bail(rc);
+            if ((rc = upload_f32(m, &D.k_norm, S.k_norm, hd, s))) return bail(rc);
+        }
+    }
+    if ((rc = upload_whole(m, &m->embed, w->embed, s))) return bail(rc);
+    if (c.tied)
+        m->lm = m->embed;
+    else if ((rc = upload_whole(m, &m->lm, w->lm_head, s)))
+        return bail(rc);
+    if ((rc = upload_f32(m, &m->final_norm, w->final_norm, H, s))) return bail(rc);
+
+    // rotary tables: cos/sin of pos * inv_freq[i], evaluated in f64 on the host
+    {
+        const int half = m->rot / 2;
+        const size_t n = (size_t)m->max_seq * (half > 0 ? half : 1);
+        std::vector<float> hc(n, 1.f), hs(n, 0.f);
+        for (int p = 0; p < m->max_seq; ++p)
+            for (int i = 0; i < half; ++i) {
+                const double th = (double)p * (double)c.inv_freq[i];
+                hc[(size_t)p * half + i] = (float)std::cos(th);
+                hs[(size_t)p * half + i] = (float)std::sin(th);
+            }
+        if ((rc = upload_f32(m, &m->rope_cos, hc.data(), n, s))) return bail(rc);
+        if ((rc = upload_f32(m, &m->rope_sin, hs.data(), n, s))) return bail(rc);
+    }
+
+    // KV cache
+    for (int l = 0; l < m->L; ++l) {
+        DevLayer& D = m->layers[l];
+        const size_t n = m->paged ? (size_t)m->nblocks * m->nkv * ATT_BS * hd
+                                  : (size_t)m->nkv * m->max_seq * hd;
+        if ((rc = dev_alloc_t(m, &D.kc, n))) return bail(rc);
+        if ((rc = dev_alloc_t(m, &D.vc, n))) return bail(rc);
+        if (hipMemsetAsync(D.kc, 0, n * 2, s) != hipSuccess || hipMemsetAsync(D.vc, 0, n * 2, s) != hipSuccess)
+            return bail(fail(QD_EHIP, "KV cache clear failed"));
+    }
+    if (m->paged) {
+        const int need = (m->max_seq + ATT_BS - 1) / ATT_BS;
+        std::vector<int32_t> t(need);
+        for (int i = 0; i < need; ++i)
+            t[i] = c.block_table ? c.block_table[i] : i;
+        if ((rc = dev_alloc_t(m, &m->table, need))) return bail(rc);
+        if (hipMemcpyAsync(m->table, t.data(), need * sizeof(int32_t), hipMemcpyHostToDevice, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+            return bail(fail(QD_EHIP, "block table upload failed"));
+    }
+
+    // launch geometry
+    {
+        const int nbH = H / 32;
+        m->lpr_qkv = pick_lpr(nbH);
+        m->rps_qkv = 4;
+        while (m->rps_qkv > 1 && hd % rows_per_tile(m->lpr_qkv, m->rps_qkv))
+            m->rps_qkv /= 2;
+        if (hd % rows_per_tile(m->lpr_qkv, m->rps_qkv))
+            return bail(fail(QD_EUNSUPPORTED, "head_dim %d vs GEMV tile of %d rows", hd,
+                             rows_per_tile(m->lpr_qkv, m->rps_qkv)));
+        const int t_qkv = m->qkv_rows / rows_per_tile(m->lpr_qkv, m->rps_qkv);
+        m->grid_qkv = gemv_grid(t_qkv, 4096);
+        m->lpr_o = pick_lpr(nqd / 32);
+        m->grid_o = gemv_grid((H + rows_per_tile(m->lpr_o, 4) - 1) / rows_per_tile(m->lpr_o, 4), 1024);
+        m->lpr_gu = pick_lpr(nbH);
+        m->grid_gu = gemv_grid((2 * m->I + rows_per_tile(m->lpr_gu, 4) - 1) / rows_per_tile(m->lpr_gu, 4), 2048);
+        m->lpr_down = pick_lpr(m->I / 32);
+        m->grid_down = gemv_grid((H + rows_per_tile(m->lpr_down, 4) - 1) / rows_per_tile(m->lpr_down, 4), 1024);
+        m->lpr_lm = pick_lpr(nbH);
+        m->grid_lm = gemv_grid((m->V + rows_per_tile(m->lpr_lm, 4) - 1) / rows_per_tile(m->lpr_lm, 4), 2048);
+        // attention: fixed split over max_seq so the grid does not depend on the position
+        const int tiles = (m->max_seq + ATT_T - 1) / ATT_T;
+        m->attn_chunk = ATT_T;
+        m->attn_nsplit = tiles;
+    }
+
+    // step buffers
+    const int maxp = 4096;
+    if ((rc = dev_alloc_t(m, &m->x, H)) || (rc = dev_alloc_t(m, &m->u, H)) ||
+        (rc = dev_alloc_t(m, &m->ss_part, maxp)) || (rc = dev_alloc_t(m, &m->qkv_raw, m->qkv_rows)) ||
+        (rc = dev_alloc_t(m, &m->qbuf, nqd)) || (rc = dev_alloc_t(m, &m->attn, nqd)) ||
+        (rc = dev_alloc_t(m, &m->act, m->I)) || (rc = dev_alloc_t(m, &m->logits, m->V)) ||
+        (rc = dev_alloc_t(m, &m->arg_val, maxp)) || (rc = dev_alloc_t(m, &m->arg_idx, maxp)) ||
+        (rc = dev_alloc_t(m, &m->counters, m->nq + 3 * m->nkv + 1)) ||
+        (rc = dev_alloc_t(m, &m->attn_part, (size_t)m->nq * m->attn_nsplit * (hd + 2))) ||
+        (rc = dev_alloc_t(m, &m->st, 1)) || (rc = dev_alloc_t(m, &m->ids, m->max_seq)) ||
+        (rc = dev_alloc_t(m, &m->pred, m->max_seq)))
+        return bail(rc);
+    if (hipMemsetAsync(m->counters, 0, sizeof(unsigned) * (m->nq + 3 * m->nkv + 1), s) != hipSuccess ||
+        hipMemsetAsync(m->st, 0, sizeof(StepState), s) != hipSuccess ||
+        hipMemsetAsync(m->ids, 0, sizeof(int32_t) * m->max_seq, s) != hipSuccess ||
+        hipMemsetAsync(m->pred, 0, sizeof(int32_t) * m->max_seq, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return bail(fail(QD_EHIP, "step buffer clear failed"));
+
+    // graph of one step
+    if (m->use_graph) {
+        if (hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking) != hipSuccess)
+            return bail(fail(QD_EHIP, "stream create failed"));
+        if (hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal) != hipSuccess)
+            return bail(fail(QD_EHIP, "begin capture failed"));
+        int src = enqueue_step(m, m->cap_stream);
+        hipError_t ee = hipStreamEndCapture(m->cap_stream, &m->graph);
+        if (src != QD_OK)
+            return bail(src);
+        if (ee != hipSuccess)
+            return bail(fail(QD_EHIP, "end capture: %s", hipGetErrorString(ee)));
+        ee = hipGraphInstantiate(&m->exec, m->graph, nullptr, nullptr, 0);
+        if (ee != hipSuccess)
+            return bail(fail(QD_EHIP, "graph instantiate: %s", hipGetErrorString(ee)));
+    }
+    *out = m;
+    return QD_OK;
+}
+
+extern "C" int qd_destroy(qd_model* m)
+{
+    if (!m)
+        return fail(QD_EINVAL, "null model");
+    (void)hipDeviceSynchronize();
+    free_model(m);
+    return QD_OK;
+}
+
+extern "C" int qd_decode_step(qd_model* m, int32_t token, int32_t pos, float* d_logits,
+                              int32_t* d_next, qd_stream stream)
+{
+    if (!m)
+        return fail(QD_EINVAL, "null model");
+    if (token < 0 || token >= m->V)
+        return fail(QD_ERANGE, "token %d not in [0, %d)", token, m->V);
+    if (pos < 0 || pos >= m->max_seq)
+        return fail(QD_ERANGE, "pos %d not in [0, %d)", pos, m->max_seq);
+    hipStream_t s = (hipStream_t)stream;
+    hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, s, m->st, m->ids, pos, pos + 1, pos, token);
+    HIP_TRY(hipGetLastError());
+    QD_TRY(run_steps(m, 1, s));
+    if (d_logits)
+        HIP_TRY(hipMemcpyAsync(d_logits, m->logits, sizeof(float) * m->V, hipMemcpyDeviceToDevice, s));
+    if (d_next)
+        HIP_TRY(hipMemcpyAsync(d_next, m->pred + pos, sizeof(int32_t), hipMemcpyDeviceToDevice, s));
+    return QD_OK;
+}
+
+extern "C" int qd_set_prompt(qd_model* m, const int32_t* tokens, int32_t n, qd_stream stream)
+{
+    if (!m)
+        return fail(QD_EINVAL, "null model");
+    if (n < 0 || n > m->max_seq)
+        return fail(QD_ERANGE, "prompt length %d not in [0, %d]", n, m->max_seq);
+    if (n > 0 && !tokens)
+        return fail(QD_EINVAL, "null tokens");
+    for (int i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= m->V)
+            return fail(QD_ERANGE, "token[%d] = %d not in [0, %d)", i, tokens[i], m->V);
+    hipStream_t s = (hipStream_t)stream;
+    if (n > 0) {
+        HIP_TRY(hipMemcpyAsync(m->ids, tokens, sizeof(int32_t) * n, hipMemcpyHostToDevice, s));
+        HIP_TRY(hipStreamSynchronize(s));  // the host array may go away on return
+    }
+    hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, s, m->st, m->ids, 0, n, -1, 0);
+    HIP_TRY(hipGetLastError());
+    return QD_OK;
+}
+
+extern "C" int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* d_tokens,
+                           float* d_logits_last, qd_stream stream)
+{
+    if (!m)
+        return fail(QD_EINVAL, "null model");
+    if (pos0 < 0 || n_steps < 0 || (int64_t)pos0 + n_steps > m->max_seq)
+        return fail(QD_ERANGE, "positions [%d, %d) not within max_seq %d", pos0, pos0 + n_steps,
+                    m->max_seq);
+    hipStream_t s = (hipStream_t)stream;
+    hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, s, m->st, m->ids, pos0, -1, -1, 0);
+    HIP_TRY(hipGetLastError());
+    QD_TRY(run_steps(m, n_steps, s));
+    if (d_tokens && n_steps > 0)
+        HIP_TRY(hipMemcpyAsync(d_tokens, m->pred + pos0, sizeof(int32_t) * n_steps,
+                               hipMemcpyDeviceToDevice, s));
+    if (d_logits_last && n_steps > 0)
+        HIP_TRY(hipMemcpyAsync(d_logits_last, m->logits, sizeof(float) * m->V,
+                               hipMemcpyDeviceToDevice, s));
+    return QD_OK;
+}
+
+// ------------------------------------------------------------------ standalone kernels
+
+extern "C" int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x,
+                            float* d_y, int32_t N, int32_t K, qd_stream stream)
+{
+    if (!d_scales || !d_qs || !d_x || !d_y)
+        return fail(QD_EINVAL, "null pointer");
+    if (N < 0 || K < 0 || K % 32)
+        return fail(QD_EINVAL, "bad shape N=%d K=%d (K %% 32 must be 0)", N, K);
+    if (gemv_lds_bytes(K / 32) > (size_t)GEMV_MAX_LDS)
+        return fail(QD_EUNSUPPORTED, "K=%d above the staged-x limit", K);
+    if ((reinterpret_cast<uintptr_t>(d_qs) | reinterpret_cast<uintptr_t>(d_x)) & 15)
+        return fail(QD_EINVAL, "qs and x must be 16-byte aligned");
+    if (N == 0)
+        return QD_OK;
+    if (K == 0) {
+        HIP_TRY(hipMemsetAsync(d_y, 0, sizeof(float) * (size_t)N, (hipStream_t)stream));
+        return QD_OK;
+    }
+    HIP_TRY(launch_gemv_plain(d_scales, d_qs, d_x, d_y, N, K, (hipStream_t)stream));
+    return QD_OK;
+}
+
+static size_t attn_ws_layout(int32_t B, int32_t nq, int32_t nkv, int32_t hd, int32_t max_kv,
+                             int* chunk, int* nsplit, size_t* counters_off)
+{
+    attn_split(B, nkv, max_kv, chunk, nsplit);
+    size_t part = (size_t)B * nq * (*nsplit) * (hd + 2) * sizeof(float);
+    part = (part + 255) / 256 * 256;
+    *counters_off = part;
+    return part + (size_t)B * nkv * sizeof(unsigned int);
+}
+
+extern "C" size_t qd_attn_workspace_bytes(int32_t B, int32_t nq, int32_t nkv, int32_t head_dim,
+                                          int32_t max_kv_len)
+{
+    if (B <= 0 || nq <= 0 || nkv <= 0 || head_dim <= 0 || max_kv_len < 0)
+        return 0;
+    int chunk, nsplit;
+    size_t off;
+    return attn_ws_layout(B, nq, nkv, head_dim, max_kv_len, &chunk, &nsplit, &off);
+}
+
+extern "C" int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t workspace_bytes,
+                              qd_stream stream)
+{
+    if (!a)
+        return fail(QD_EINVAL, "null args");
+    if (!a->q || !a->k || !a->v || !a->kv_lens || !a->out || !d_workspace)
+        return fail(QD_EINVAL, "null pointer");
+    if (a->B < 0 || a->nq <= 0 || a->nkv <= 0 || a->max_kv_len < 0)
+        return fail(QD_EINVAL, "bad sizes");
+    if (a->nq % a->nkv)
+        return fail(QD_EINVAL, "nq %% nkv != 0");
+    const int gq = a->nq / a->nkv;
+    if (gq != 1 && gq != 2 && gq != 4 && gq != 8)
+        return fail(QD_EUNSUPPORTED, "GQA group %d not in {1,2,4,8}", gq);
+    if (a->head_dim != 64 && a->head_dim != 128)
+        return fail(QD_EUNSUPPORTED, "head_dim %d not in {64,128}", a->head_dim);
+    if (a->block_tables) {
+        if (a->block_size != ATT_BS)
+            return fail(QD_EUNSUPPORTED, "block_size %d (only %d)", a->block_size, ATT_BS);
+        if ((int64_t)a->max_blocks_per_seq * ATT_BS < a->max_kv_len)
+            return fail(QD_EINVAL, "max_blocks_per_seq too small for max_kv_len");
+    }
+    if (a->B == 0)
+        return QD_OK;
+    int chunk, nsplit;
+    size_t coff;
+    const size_t need = attn_ws_layout(a->B, a->nq, a->nkv, a->head_dim, a->max_kv_len, &chunk,
+                                       &nsplit, &coff);
+    if (workspace_bytes < need)
+        return fail(QD_EINVAL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    AttnParams p;
+    p.q = a->q;
+    p.k = a->k;
+    p.v = a->v;
+    p.tables = a->block_tables;
+    p.mbps = a->max_blocks_per_seq;
+    p.kv_lens = a->kv_lens;
+    p.pos = nullptr;
+    p.max_kv = a->max_kv_len;
+    p.nq = a->nq;
+    p.nkv = a->nkv;
+    p.scale = a->scale;
+    p.chunk = chunk;
+    p.nsplit = nsplit;
+    p.part = reinterpret_cast<float*>(d_workspace);
+    p.counters = reinterpret_cast<unsigned int*>(reinterpret_cast<char*>(d_workspace) + coff);
+    p.out = a->out;
+    hipStream_t s = (hipStream_t)stream;
+    const dim3 grid(nsplit, a->nkv, a->B);
+    const bool paged = a->block_tables != nullptr;
+#define QD_ATT(HD_, GQ_)                                                                          \
+    if (paged)                                                                                    \
+        hipLaunchKernelGGL((k_attn_decode<HD_, GQ_, true>), grid, dim3(ATT_NT), 0, s, p);         \
+    else                                                                                          \
+        hipLaunchKernelGGL((k_attn_decode<HD_, GQ_, false>), grid, dim3(ATT_NT), 0, s, p);
+    if (a->head_dim == 128) {
+        if (gq == 1) { QD_ATT(128, 1) } else if (gq == 2) { QD_ATT(128, 2) }
+        else if (gq == 4) { QD_ATT(128, 4) } else { QD_ATT(128, 8) }
+    } else {
+        if (gq == 1) { QD_ATT(64, 1) } else if (gq == 2) { QD_ATT(64, 2) }
+        else if (gq == 4) { QD_ATT(64, 4) } else { QD_ATT(64, 8) }
+    }
+#undef QD_ATT
+    HIP_TRY(hipGetLastError());
+    return QD_OK;
+}
