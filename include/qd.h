@@ -176,9 +176,9 @@ typedef struct {
     float* out;
 } qd_attn_args;
 
-/* Bytes of device workspace qd_attn_decode needs for these sizes.  The
- * workspace must be zero-filled once before its first use; each call leaves
- * it ready for the next (its completion counters return to zero). */
+/* Bytes of device workspace qd_attn_decode needs for these sizes (the
+ * split-KV partials); no initialisation is needed.  A workspace must not be
+ * shared by two calls in flight at the same time. */
 size_t qd_attn_workspace_bytes(int32_t B, int32_t nq, int32_t nkv, int32_t head_dim,
                                int32_t max_kv_len);
 int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t workspace_bytes,

@@ -4,22 +4,31 @@
 // CudaQwen3::gemv: 32-weight blocks, one f16 scale, 16 bytes of nibbles;
 // weight = (nibble - 8) * scale).
 //
-// Work mapping.  A workgroup of NWAVES wave64s owns a tile of rows.  Inside a
+// Work mapping.  A workgroup of NWAVES wave64s owns tiles of rows.  Inside a
 // wave, groups of LPR lanes share a row slot and split that row's blocks
 // (lane i of the group takes blocks i, i+LPR, ...); each lane keeps RPS rows
-// of its slot in flight, so one staged x chunk is reused RPS times.  A lane
-// loads a whole block's 16 nibble bytes with one 128-bit load: consecutive
-// lanes read consecutive blocks of a row, so a wave reads LPR*16 contiguous
-// bytes per row.  x is staged once per workgroup into LDS (block b at float
-// offset b*36: the 4-float pad keeps the per-lane 128-bit reads of 64 lanes
-// on distinct banks) together with each block's sum of x.
+// of its slot in flight, so one staged x chunk serves RPS rows.  A lane loads
+// a block's 16 nibble bytes with one 128-bit load: consecutive lanes read
+// consecutive blocks of a row, so a wave reads LPR*16 contiguous bytes per
+// row.  The grid is persistent: a workgroup walks its tiles in (tile, block
+// group) work items, keeping NBUF-1 items of loads in flight ahead of the one
+// it consumes, and the first items' loads are issued before x is staged.
 //
-// In-register dequant: for one 32-bit word of nibbles, (w & 0x0f0f0f0f) and
-// ((w >> 4) & 0x0f0f0f0f) hold four codes each in byte lanes, which convert
-// to f32 one instruction each; the offset -8 is applied once per block as
-//   sum_j (c_j - 8) x_j = sum_j c_j x_j - 8 * sum_j x_j,
-// with sum_j x_j precomputed per block.  Partial row sums are reduced across
-// the LPR lanes with butterfly shuffles in a fixed order (deterministic).
+// x is staged once per workgroup into LDS, block b at float offset b*36 (the
+// 4-float pad keeps the per-lane 128-bit reads of 64 lanes on distinct banks):
+// x[32b .. 32b+15] as is and x[32b+16 .. 32b+31] divided by 16 (exact), with
+// the block's sum of x beside it.
+//
+// In-register dequant: for one 32-bit word w of nibbles (bytes 4k..4k+3 of a
+// block), w & 0x0f0f0f0f holds the codes of elements 4k..4k+3 and
+// w & 0xf0f0f0f0 sixteen times the codes of elements 16+4k..16+4k+3, one per
+// byte; v_cvt_f32_ubyte{0..3} turns each byte into f32 in one instruction
+// (the factor 16 cancels against the staged x/16), and an FMA accumulates it:
+// 2 ANDs + 8 converts + 8 FMAs per 8 weights, exact products in f32.  The -8
+// offset is applied once per block:
+//   sum_j (c_j - 8) x_j = sum_j c_j x_j - 8 * sum_j x_j.
+// Row sums are reduced across the LPR lanes with butterfly shuffles in a fixed
+// order (deterministic).
 #pragma once
 
 #include "qd_common.h"
@@ -31,39 +40,75 @@ constexpr int XPAD = 36;  // floats per staged x block (32 + pad)
 // LDS floats needed to stage x of nb blocks
 __host__ __device__ constexpr int gemv_lds_floats(int nb) { return nb * XPAD + nb; }
 
-// Stage x[32*nb] (global f32) into LDS: xl[b*XPAD + j] = x[32b + j], xs[b] = sum_j x[32b+j].
+// x staging in two halves, so that the x loads fly together with the weight
+// loads and with the epilogue's prologue loads:
+//   stage_x_load   issues every x load of this thread (K <= 64*NT floats)
+//   stage_x_store  multiplies by *pre (if given: an LDS scalar published by the
+//                  barrier at its start) and writes the LDS layout
 template <int NT>
-QD_DEV void stage_x(const float* __restrict__ x, int nb, float* xl, float* xs)
+struct XStage {
+    static constexpr int MAXU = 16384 / (4 * NT);
+    float4 v[MAXU];
+};
+
+template <int NT>
+QD_DEV void stage_x_load(const float* __restrict__ x, int nb, XStage<NT>& st)
 {
-    // 8 float4 per block; 8 consecutive lanes hold one block, so the block sum
-    // is a butterfly over those 8 lanes.  NT is a multiple of 64.
     const int n4 = nb * 8;
-    for (int i0 = 0; i0 < n4; i0 += NT) {
-        int i = i0 + (int)threadIdx.x;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i < n4) {
-            v = reinterpret_cast<const float4*>(x)[i];
-            *reinterpret_cast<float4*>(xl + (i >> 3) * XPAD + (i & 7) * 4) = v;
+#pragma unroll
+    for (int u = 0; u < XStage<NT>::MAXU; ++u) {
+        const int i = (int)threadIdx.x + u * NT;
+        st.v[u] = (i < n4) ? reinterpret_cast<const float4*>(x)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+// Block b at float offset b*XPAD: x[32b .. 32b+15] as is and x[32b+16 .. 32b+31]
+// divided by 16 (exact); xs[b] = the block's sum of x.  Ends with a barrier.
+template <int NT>
+QD_DEV void stage_x_store(int nb, const XStage<NT>& st, float* xl, float* xs, const float* pre)
+{
+    const int n4 = nb * 8;
+    __syncthreads();   // *pre (if any) is visible
+    const float p = pre ? *pre : 1.f;
+#pragma unroll
+    for (int u = 0; u < XStage<NT>::MAXU; ++u) {
+        if (u * NT < n4) {   // uniform
+            const int i = (int)threadIdx.x + u * NT;
+            float4 w = st.v[u];
+            w.x *= p; w.y *= p; w.z *= p; w.w *= p;
+            // 8 consecutive lanes hold one block: its sum is a butterfly over them
+            float s = (w.x + w.y) + (w.z + w.w);
+            s = group_sum<8>(s);
+            if (i < n4) {
+                const float f = (i & 7) < 4 ? 1.f : 0.0625f;
+                *reinterpret_cast<float4*>(xl + (i >> 3) * XPAD + (i & 7) * 4) =
+                    make_float4(w.x * f, w.y * f, w.z * f, w.w * f);
+                if ((i & 7) == 0)
+                    xs[i >> 3] = s;
+            }
         }
-        float s = (v.x + v.y) + (v.z + v.w);
-        s = group_sum<8>(s);
-        if (i < n4 && (i & 7) == 0)
-            xs[i >> 3] = s;
     }
     __syncthreads();
 }
 
-// sum_j c_j * x_j over one block (codes c_j in [0, 15]); xv = the block's 32 x values
+// w & m through an opaque instruction, so the byte converts below stay
+// v_cvt_f32_ubyteN instead of being re-derived as bit-field extracts
+QD_DEV uint32_t and_opaque(uint32_t w, uint32_t m)
+{
+    uint32_t r;
+    asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(w), "v"(m));
+    return r;
+}
+
+// sum_j c_j * x_j over one block (codes c_j in [0, 15]); xv = the staged block
 QD_DEV float q4_block_dot(uint4 q, const float4 (&xv)[8])
 {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        // word k = bytes 4k..4k+3: low nibbles are elements 4k..4k+3,
-        // high nibbles are elements 16+4k..16+4k+3
-        const uint32_t lo = w[k] & 0x0f0f0f0fu;
-        const uint32_t hi = (w[k] >> 4) & 0x0f0f0f0fu;
+        const uint32_t lo = and_opaque(w[k], 0x0f0f0f0fu);
+        const uint32_t hi = and_opaque(w[k], 0xf0f0f0f0u);
         s0 = fmaf((float)(lo & 0xffu), xv[k].x, s0);
         s0 = fmaf((float)((lo >> 8) & 0xffu), xv[k].y, s0);
         s0 = fmaf((float)((lo >> 16) & 0xffu), xv[k].z, s0);
@@ -84,93 +129,228 @@ struct GemvGeom {
     static constexpr int NT = NWAVES * WAVE;
 };
 
-// Dot products of the RPS rows of this lane's slot in tile `tile`, reduced over
-// the slot's LPR lanes: every lane of the slot returns the same acc[] values.
-// The slot's rows are row0 .. row0+RPS-1 (row0 returned); rows >= N give 0.
-template <int LPR, int RPS, int NWAVES>
-QD_DEV int gemv_tile(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q, int N,
-                     int nb, const float* xl, const float* xs, int tile, float (&acc)[RPS])
+// Registers of one work item: BG blocks x RPS rows of this lane.
+template <int RPS, int BG>
+struct GemvBuf {
+    uint4 q[BG][RPS];
+    uint32_t d[BG][RPS];   // f16 scale bits
+};
+
+// Persistent GEMV driver.  Work items are (tile, block group) pairs, tiles
+// strided by gridDim.x.  NBUF register buffers rotate: the loads of item
+// i + NBUF - 1 are issued before item i is consumed.  `epi` receives every
+// finished tile:
+//   epi.prologue()              before staging (may write *epi.pre in LDS)
+//   epi.tile(row0, acc, lead)   acc[RPS] = dot products of rows row0 .. row0+RPS-1
+// Scales come either in the canonical layout d[row][block] (TS = false) or
+// in the tiled layout written by tile_scales() (TS = true): for every (tile,
+// wave, slot, lane) the lane's scales ordered [block j][row r], so one work
+// item's RPS*BG scales are contiguous and arrive in one load.
+template <int LPR, int RPS, int NWAVES, int BG, int NBUF, bool NTL, bool TS, class Epi>
+QD_DEV void gemv_run(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
+                     const float* __restrict__ x, int N, int nb, float* xl, float* xs, Epi& epi)
 {
+    static_assert(NBUF >= 1 && NBUF <= 3, "buffers");
     using G = GemvGeom<LPR, RPS, NWAVES>;
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
     const int slot = lane / LPR, lr = lane % LPR;
-    const int row0 = tile * G::ROWS + wave * G::RPW + slot * RPS;
+    const int ntiles = (N + G::ROWS - 1) / G::ROWS;
+    const int ngroups = (nb + LPR * BG - 1) / (LPR * BG);
+    const int my_tiles = (int)blockIdx.x < ntiles ? (ntiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+    const int nitems = my_tiles * ngroups;
+
+    // issue the loads of item i (clamped: an item past the end reloads the last one)
+    auto load = [&](GemvBuf<RPS, BG>& bf, int i) {
+        i = min(i, nitems - 1);
+        const int tile = (int)blockIdx.x + (i / ngroups) * (int)gridDim.x;
+        const int grp = i % ngroups;
+        const int row0 = tile * G::ROWS + wave * G::RPW + slot * RPS;
+#pragma unroll
+        for (int g = 0; g < BG; ++g) {
+            const int bc = min(grp * LPR * BG + g * LPR + lr, nb - 1);
+#pragma unroll
+            for (int r = 0; r < RPS; ++r) {
+                const size_t blk = (size_t)min(row0 + r, N - 1) * nb + bc;
+                const uint4* qp = reinterpret_cast<const uint4*>(Q + blk * 16);
+                if (NTL) {
+                    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qp));
+                    bf.q[g][r] = make_uint4(t.x, t.y, t.z, t.w);
+                } else {
+                    bf.q[g][r] = *qp;
+                }
+                if (!TS)
+                    bf.d[g][r] = D[blk];
+            }
+        }
+        if (TS) {
+            // record of this (tile, wave, slot, lane): [j][r], j = block index of the lane
+            constexpr int E = RPS * BG;   // scales of one item
+            const int nj = nb / LPR;
+            const uint16_t* rec = D + ((((size_t)tile * NWAVES + wave) * G::SLOTS + slot) * LPR + lr) *
+                                          (size_t)(nj * RPS) + (size_t)grp * E;
+            if (E == 8) {
+                const uint4 v = *reinterpret_cast<const uint4*>(rec);
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    bf.d[e / RPS][e % RPS] = (w[e / 2] >> (16 * (e % 2))) & 0xffffu;
+            } else if (E == 4) {
+                const uint2 v = *reinterpret_cast<const uint2*>(rec);
+                const uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    bf.d[e / RPS][e % RPS] = (w[e / 2] >> (16 * (e % 2))) & 0xffffu;
+            } else if (E == 2) {
+                const uint32_t v = *reinterpret_cast<const uint32_t*>(rec);
+                bf.d[0 / RPS][0 % RPS] = v & 0xffffu;
+                bf.d[1 / RPS][1 % RPS] = v >> 16;
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    bf.d[e / RPS][e % RPS] = rec[e];
+            }
+        }
+    };
+    float acc[RPS];
 #pragma unroll
     for (int r = 0; r < RPS; ++r)
         acc[r] = 0.f;
-    for (int b = lr; b < nb; b += LPR) {
-        uint4 q[RPS];
-        float d[RPS];
+    // consume item i from buffer bf
+    auto compute = [&](const GemvBuf<RPS, BG>& bf, int i) {
+        const int tile = (int)blockIdx.x + (i / ngroups) * (int)gridDim.x;
+        const int grp = i % ngroups;
 #pragma unroll
-        for (int r = 0; r < RPS; ++r) {
-            const int row = row0 + r;
-            if (row < N) {
-                const size_t blk = (size_t)row * nb + b;
-                q[r] = *reinterpret_cast<const uint4*>(Q + blk * 16);
-                d[r] = f16_to_f32(D[blk]);
-            } else {
-                q[r] = make_uint4(0, 0, 0, 0);
-                d[r] = 0.f;
+        for (int g = 0; g < BG; ++g) {
+            const int b = grp * LPR * BG + g * LPR + lr;
+            if (b < nb) {
+                float4 xv[8];
+                const float4* xp = reinterpret_cast<const float4*>(xl + b * XPAD);
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    xv[k] = xp[k];
+                const float m8 = -8.f * xs[b];
+#pragma unroll
+                for (int r = 0; r < RPS; ++r)
+                    acc[r] = fmaf(f16_to_f32((uint16_t)bf.d[g][r]), q4_block_dot(bf.q[g][r], xv) + m8,
+                                  acc[r]);
             }
         }
-        float4 xv[8];
-        const float4* xp = reinterpret_cast<const float4*>(xl + b * XPAD);
+        if (grp == ngroups - 1) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            xv[k] = xp[k];
-        const float m8 = -8.f * xs[b];
+            for (int r = 0; r < RPS; ++r)
+                acc[r] = group_sum<LPR>(acc[r]);
+            const int row0 = tile * G::ROWS + wave * G::RPW + slot * RPS;
+            epi.tile(row0, acc, lr == 0);
 #pragma unroll
-        for (int r = 0; r < RPS; ++r)
-            acc[r] = fmaf(d[r], q4_block_dot(q[r], xv) + m8, acc[r]);
+            for (int r = 0; r < RPS; ++r)
+                acc[r] = 0.f;
+        }
+    };
+
+    GemvBuf<RPS, BG> bufs[NBUF];
+    if (nitems > 0) {
+#pragma unroll
+        for (int j = 0; j + 1 < NBUF; ++j)
+            load(bufs[j], j);
     }
+    XStage<G::NT> xst;
+    stage_x_load<G::NT>(x, nb, xst);
+    epi.prologue();
+    stage_x_store<G::NT>(nb, xst, xl, xs, epi.pre);   // ends with a barrier
+    for (int i = 0; i < nitems; i += NBUF) {
 #pragma unroll
-    for (int r = 0; r < RPS; ++r)
-        acc[r] = group_sum<LPR>(acc[r]);
-    return row0;
+        for (int j = 0; j < NBUF; ++j) {
+            if (i + j < nitems) {
+                if (NBUF == 1)
+                    load(bufs[0], i + j);
+                else
+                    load(bufs[(j + NBUF - 1) % NBUF], i + j + NBUF - 1);
+                compute(bufs[j], i + j);
+            }
+        }
+    }
 }
 
 // 1 / sqrt(mean(x^2) + eps) from per-workgroup partial sums of x^2 written by
-// the producer of x (summed here in a fixed order).  All threads get the value.
-QD_DEV float inv_rms_from_partials(const float* __restrict__ ss_part, int n_part, int n, float eps,
-                                   float* smem_scalar)
+// the producer of x, summed by wave 0 in a fixed order (each lane issues all of
+// its loads before adding); written to *out by lane 0 of wave 0.  Needs a
+// barrier before other waves read *out.
+QD_DEV void inv_rms_partials(const float* __restrict__ ss_part, int n_part, int n, float eps,
+                             float* out)
 {
     if (threadIdx.x < WAVE) {
+        constexpr int U = 16;
         float s = 0.f;
-        for (int i = threadIdx.x; i < n_part; i += WAVE)
-            s += ss_part[i];
+        for (int i0 = 0; i0 < n_part; i0 += U * WAVE) {
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + (int)threadIdx.x + u * WAVE;
+                v[u] = (i < n_part) ? ss_part[i] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                s += v[u];
+        }
         s = group_sum<WAVE>(s);
         if (threadIdx.x == 0)
-            *smem_scalar = 1.0f / sqrtf(s / (float)n + eps);
+            *out = 1.0f / sqrtf(s / (float)n + eps);
     }
-    __syncthreads();
-    return *smem_scalar;
 }
 
-// ----------------------------------------------------------------- plain GEMV
+// ----------------------------------------------------------------- epilogues
 
-template <int LPR, int RPS, int NWAVES>
-__global__ void __launch_bounds__(NWAVES* WAVE)
-k_gemv_plain(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
-             const float* __restrict__ x, float* __restrict__ y, int N, int nb)
-{
-    using G = GemvGeom<LPR, RPS, NWAVES>;
-    extern __shared__ float smem[];
-    float* xl = smem;
-    float* xs = smem + nb * XPAD;
-    stage_x<G::NT>(x, nb, xl, xs);
-    const int ntiles = (N + G::ROWS - 1) / G::ROWS;
-    const int lr = (threadIdx.x & (WAVE - 1)) % LPR;
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        float acc[RPS];
-        const int row0 = gemv_tile<LPR, RPS, NWAVES>(D, Q, N, nb, xl, xs, tile, acc);
-        if (lr == 0) {
+// y[row] = acc
+struct EpiStore {
+    float* y;
+    int N;
+    const float* pre = nullptr;
+    QD_DEV void prologue() {}
+    template <int RPS>
+    QD_DEV void tile(int row0, const float (&acc)[RPS], bool lead)
+    {
+        if (lead) {
 #pragma unroll
             for (int r = 0; r < RPS; ++r)
                 if (row0 + r < N)
                     y[row0 + r] = acc[r];
         }
     }
+};
+
+template <int LPR, int RPS, int NWAVES, int BG, int NBUF, bool NTL, bool TS = false>
+__global__ void __launch_bounds__(NWAVES* WAVE)
+k_gemv_plain(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
+             const float* __restrict__ x, float* __restrict__ y, int N, int nb)
+{
+    extern __shared__ float smem[];
+    EpiStore e{y, N};
+    gemv_run<LPR, RPS, NWAVES, BG, NBUF, NTL, TS>(D, Q, x, N, nb, smem, smem + nb * XPAD, e);
+}
+
+// Host side: rewrite canonical scales d[N][nb] into the tiled layout for
+// (LPR, RPS, NWAVES): for tile t, wave w, slot s, lane l the record of
+// nb/LPR * RPS scales ordered [j][r] holds d[row0 + r][j*LPR + l] with
+// row0 = t*ROWS + w*RPW + s*RPS (rows past N give 0).  Needs nb % LPR == 0.
+// Returns the number of uint16 written (ntiles * ROWS * nb).
+inline size_t tile_scales(const uint16_t* d, int N, int nb, int lpr, int rps, int nwaves,
+                          uint16_t* out)
+{
+    const int slots = WAVE / lpr, rpw = slots * rps, rows = nwaves * rpw;
+    const int ntiles = (N + rows - 1) / rows, nj = nb / lpr;
+    size_t o = 0;
+    for (int t = 0; t < ntiles; ++t)
+        for (int w = 0; w < nwaves; ++w)
+            for (int s = 0; s < slots; ++s)
+                for (int l = 0; l < lpr; ++l)
+                    for (int j = 0; j < nj; ++j)
+                        for (int r = 0; r < rps; ++r) {
+                            const int row = t * rows + w * rpw + s * rps + r;
+                            out[o++] = row < N ? d[(size_t)row * nb + (size_t)j * lpr + l] : 0;
+                        }
+    return o;
 }
 
 }  // namespace qd

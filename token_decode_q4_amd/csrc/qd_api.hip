@@ -48,7 +48,16 @@ extern "C" const char* qd_last_error(void) { return g_err.c_str(); }
 
 // ------------------------------------------------------------------ GEMV launch
 
-static constexpr int GEMV_NWAVES = 4;
+// GEMV launch configurations (rows per slot, waves, block groups per item,
+// register buffers, non-temporal weight loads), chosen per call site by
+// timing the sweep shapes on MI355X; the lanes-per-row count follows K.
+struct GemvCfg {
+    int rps, nw, bg, nbuf, ntl, grid_cap;
+};
+static constexpr GemvCfg CFG_SMALL = {2, 8, 2, 3, 0, 1 << 30};   // N ~ 4096 (o, down)
+static constexpr GemvCfg CFG_QKV = {4, 8, 1, 2, 0, 1 << 30};     // q|k|v
+static constexpr GemvCfg CFG_WIDE = {4, 4, 1, 2, 0, 1024};       // gate|up
+static constexpr GemvCfg CFG_HEAD = {4, 4, 1, 2, 1, 2048};       // LM head
 static constexpr int GEMV_MAX_LDS = 64 * 1024;
 
 // lanes per row: the largest of 64/32/16/8 dividing the number of blocks
@@ -60,30 +69,54 @@ static int pick_lpr(int nb)
     return 8;
 }
 
-static int rows_per_tile(int lpr, int rps) { return GEMV_NWAVES * (WAVE / lpr) * rps; }
+static int rows_per_tile(const GemvCfg& c, int lpr) { return c.nw * (WAVE / lpr) * c.rps; }
 
 static size_t gemv_lds_bytes(int nb) { return (size_t)gemv_lds_floats(nb) * sizeof(float); }
 
-static int gemv_grid(int ntiles, int cap) { return ntiles < cap ? (ntiles > 0 ? ntiles : 1) : cap; }
+static int gemv_grid(const GemvCfg& c, int lpr, int N)
+{
+    const int nt = (N + rows_per_tile(c, lpr) - 1) / rows_per_tile(c, lpr);
+    const int g = nt < c.grid_cap ? nt : c.grid_cap;
+    return g > 0 ? g : 1;
+}
 
-#define QD_DISPATCH_LPR(lpr, RPS_, BODY)                                                  \
-    switch (lpr) {                                                                        \
-    case 64: { constexpr int LPR = 64, RPS = RPS_; BODY; } break;                         \
-    case 32: { constexpr int LPR = 32, RPS = RPS_; BODY; } break;                         \
-    case 16: { constexpr int LPR = 16, RPS = RPS_; BODY; } break;                         \
-    default: { constexpr int LPR = 8, RPS = RPS_; BODY; } break;                          \
+// Launch kernel template KT<LPR, RPS, NW, BG, NBUF, NTL> for configuration C.
+#define QD_GEMV_LAUNCH(KT, C, lpr, grid, lds, s, ...)                                              \
+    do {                                                                                           \
+        const GemvCfg& c_ = (C);                                                                   \
+        const int l_ = (lpr);                                                                      \
+        if (c_.rps == 2 && c_.nw == 8 && c_.bg == 2 && c_.nbuf == 3 && !c_.ntl) {                  \
+            QD_GEMV_LPR(KT, l_, (2, 8, 2, 3, false), grid, lds, s, __VA_ARGS__);                   \
+        } else if (c_.rps == 4 && c_.nw == 8 && c_.bg == 1 && c_.nbuf == 2 && !c_.ntl) {           \
+            QD_GEMV_LPR(KT, l_, (4, 8, 1, 2, false), grid, lds, s, __VA_ARGS__);                   \
+        } else if (c_.rps == 4 && c_.nw == 4 && c_.bg == 1 && c_.nbuf == 2 && c_.ntl) {            \
+            QD_GEMV_LPR(KT, l_, (4, 4, 1, 2, true), grid, lds, s, __VA_ARGS__);                    \
+        } else {                                                                                   \
+            QD_GEMV_LPR(KT, l_, (4, 4, 1, 2, false), grid, lds, s, __VA_ARGS__);                   \
+        }                                                                                          \
+    } while (0)
+#define QD_UNPACK(...) __VA_ARGS__
+#define QD_GEMV_ONE(KT, L, P, grid, lds, s, ...) \
+    hipLaunchKernelGGL((KT<L, QD_UNPACK P>), dim3(grid), dim3(QD_NW P * WAVE), lds, s, __VA_ARGS__)
+#define QD_NW_(a, b, c, d, e) b
+#define QD_NW(...) QD_NW_(__VA_ARGS__)
+#define QD_GEMV_LPR(KT, l, P, grid, lds, s, ...)                                                   \
+    switch (l) {                                                                                   \
+    case 64: QD_GEMV_ONE(KT, 64, P, grid, lds, s, __VA_ARGS__); break;                              \
+    case 32: QD_GEMV_ONE(KT, 32, P, grid, lds, s, __VA_ARGS__); break;                              \
+    case 16: QD_GEMV_ONE(KT, 16, P, grid, lds, s, __VA_ARGS__); break;                              \
+    default: QD_GEMV_ONE(KT, 8, P, grid, lds, s, __VA_ARGS__); break;                               \
     }
+
+static const GemvCfg& plain_cfg(int N) { return N <= 8192 ? CFG_SMALL : (N <= 65536 ? CFG_WIDE : CFG_HEAD); }
 
 static hipError_t launch_gemv_plain(const uint16_t* d, const uint8_t* q, const float* x, float* y,
                                     int N, int K, hipStream_t s)
 {
     const int nb = K / 32, lpr = pick_lpr(nb);
-    const int ntiles = (N + rows_per_tile(lpr, 4) - 1) / rows_per_tile(lpr, 4);
-    const int grid = gemv_grid(ntiles, 2048);
-    QD_DISPATCH_LPR(lpr, 4, {
-        hipLaunchKernelGGL((k_gemv_plain<LPR, RPS, GEMV_NWAVES>), dim3(grid),
-                           dim3(GEMV_NWAVES * WAVE), gemv_lds_bytes(nb), s, d, q, x, y, N, nb);
-    });
+    const GemvCfg& c = plain_cfg(N);
+    const int grid = gemv_grid(c, lpr, N);
+    QD_GEMV_LAUNCH(k_gemv_plain, c, lpr, grid, gemv_lds_bytes(nb), s, d, q, x, y, N, nb);
     return hipGetLastError();
 }
 
@@ -110,17 +143,16 @@ struct qd_model {
     float *rope_cos = nullptr, *rope_sin = nullptr;
     int32_t* table = nullptr;
     // step buffers
-    float *x = nullptr, *u = nullptr, *ss_part = nullptr, *qkv_raw = nullptr, *qbuf = nullptr;
+    float *x = nullptr, *u = nullptr, *ss_part = nullptr, *qkv_raw = nullptr;
     float *attn = nullptr, *act = nullptr, *logits = nullptr, *arg_val = nullptr;
     int32_t* arg_idx = nullptr;
-    unsigned int* counters = nullptr;  // [qkv heads] [attention nkv] [lm head 1]
     float* attn_part = nullptr;
     int attn_chunk = 0, attn_nsplit = 0;
     StepState* st = nullptr;
     int32_t *ids = nullptr, *pred = nullptr;
     // launch geometry
-    int lpr_qkv, rps_qkv, grid_qkv, lpr_o, grid_o, lpr_gu, grid_gu, lpr_down, grid_down;
-    int lpr_lm, grid_lm;
+    int lpr_qkv, grid_qkv, lpr_o, grid_o, lpr_gu, grid_gu, lpr_down, grid_down;
+    int lpr_lm, grid_lm, grid_embed;
     // graph
     int use_graph = 0;
     hipStream_t cap_stream = nullptr;
@@ -309,65 +341,53 @@ static int validate_config(const qd_config* c, const qd_weights* w)
     return QD_OK;
 }
 
+// Launch the split-KV attention (split + combine).
+template <int QMODE>
+static void launch_attention(const AttnParams& p, int hd, int gq, bool paged, int B, int nq,
+                             hipStream_t s)
+{
+    const dim3 grid(p.nsplit, p.nkv, B);
+#define QD_ATT(HD_, GQ_)                                                                          \
+    if (paged)                                                                                    \
+        hipLaunchKernelGGL((k_attn_split<HD_, GQ_, true, QMODE>), grid, dim3(ATT_NT), 0, s, p);   \
+    else                                                                                          \
+        hipLaunchKernelGGL((k_attn_split<HD_, GQ_, false, QMODE>), grid, dim3(ATT_NT), 0, s, p);
+    if (hd == 128) {
+        if (gq == 1) { QD_ATT(128, 1) } else if (gq == 2) { QD_ATT(128, 2) }
+        else if (gq == 4) { QD_ATT(128, 4) } else { QD_ATT(128, 8) }
+    } else {
+        if (gq == 1) { QD_ATT(64, 1) } else if (gq == 2) { QD_ATT(64, 2) }
+        else if (gq == 4) { QD_ATT(64, 4) } else { QD_ATT(64, 8) }
+    }
+#undef QD_ATT
+    const size_t lds = sizeof(float) * (size_t)p.nsplit;
+    if (hd == 128)
+        hipLaunchKernelGGL((k_attn_combine<128>), dim3(nq, B), dim3(ATT_CNT), lds, s, p.part,
+                           p.nsplit, p.chunk, p.kv_lens, p.pos, p.max_kv, nq, p.out);
+    else
+        hipLaunchKernelGGL((k_attn_combine<64>), dim3(nq, B), dim3(ATT_CNT), lds, s, p.part,
+                           p.nsplit, p.chunk, p.kv_lens, p.pos, p.max_kv, nq, p.out);
+}
+
 // Enqueue one decode step (position and token come from the device state).
 static int enqueue_step(qd_model* m, hipStream_t s)
 {
     const int H = m->H;
-    hipLaunchKernelGGL(k_embed, dim3(1), dim3(256), 0, s, m->embed.d, m->embed.qs, H, m->V, m->st,
-                       m->ids, m->max_seq, m->layers[0].attn_norm, m->x, m->u, m->ss_part);
-    int n_part = 1;
+    hipLaunchKernelGGL(k_embed, dim3(m->grid_embed), dim3(256), 0, s, m->embed.d, m->embed.qs, H,
+                       m->V, m->st, m->ids, m->max_seq, m->layers[0].attn_norm, m->x, m->u,
+                       m->ss_part);
+    int n_part = m->grid_embed;
     for (int l = 0; l < m->L; ++l) {
         DevLayer& Ly = m->layers[l];
-        // q | k | v, per-head norm + rotary + KV write
-        QkvEpi e;
-        e.raw = m->qkv_raw;
-        e.q_out = m->qbuf;
-        e.nq = m->nq;
-        e.nkv = m->nkv;
-        e.hd = m->hd;
-        e.rot = m->rot;
-        e.qk_norm = m->qk_norm;
-        e.eps = m->eps;
-        e.q_norm = Ly.q_norm;
-        e.k_norm = Ly.k_norm;
-        e.rope_cos = m->rope_cos;
-        e.rope_sin = m->rope_sin;
-        e.st = m->st;
-        e.max_seq = m->max_seq;
-        e.kc = Ly.kc;
-        e.vc = Ly.vc;
-        e.paged = m->paged;
-        e.table = m->table;
-        e.counters = m->counters;
-        {
-            const int nb = Ly.qkv.nb;
-            if (m->rps_qkv == 4) {
-                QD_DISPATCH_LPR(m->lpr_qkv, 4, {
-                    hipLaunchKernelGGL((k_gemv_qkv<LPR, RPS, GEMV_NWAVES>), dim3(m->grid_qkv),
-                                       dim3(GEMV_NWAVES * WAVE), gemv_lds_bytes(nb), s, Ly.qkv.d,
-                                       Ly.qkv.qs, m->u, Ly.qkv.rows, nb, m->ss_part, n_part, H,
-                                       m->eps, e);
-                });
-            } else if (m->rps_qkv == 2) {
-                QD_DISPATCH_LPR(m->lpr_qkv, 2, {
-                    hipLaunchKernelGGL((k_gemv_qkv<LPR, RPS, GEMV_NWAVES>), dim3(m->grid_qkv),
-                                       dim3(GEMV_NWAVES * WAVE), gemv_lds_bytes(nb), s, Ly.qkv.d,
-                                       Ly.qkv.qs, m->u, Ly.qkv.rows, nb, m->ss_part, n_part, H,
-                                       m->eps, e);
-                });
-            } else {
-                QD_DISPATCH_LPR(m->lpr_qkv, 1, {
-                    hipLaunchKernelGGL((k_gemv_qkv<LPR, RPS, GEMV_NWAVES>), dim3(m->grid_qkv),
-                                       dim3(GEMV_NWAVES * WAVE), gemv_lds_bytes(nb), s, Ly.qkv.d,
-                                       Ly.qkv.qs, m->u, Ly.qkv.rows, nb, m->ss_part, n_part, H,
-                                       m->eps, e);
-                });
-            }
-        }
-        // attention
+        // q | k | v (raw, before the per-head norm and rotary)
+        QD_GEMV_LAUNCH(k_gemv_scaled, CFG_QKV, m->lpr_qkv, m->grid_qkv, gemv_lds_bytes(Ly.qkv.nb), s,
+                       Ly.qkv.d, Ly.qkv.qs, m->u, Ly.qkv.rows, Ly.qkv.nb, m->ss_part, n_part, H,
+                       m->eps, m->qkv_raw);
+        // per-head norm + rotary, K/V write, split-KV attention, combine
         {
             AttnParams p;
-            p.q = m->qbuf;
+            memset(&p, 0, sizeof p);
+            p.q = m->qkv_raw;
             p.k = Ly.kc;
             p.v = Ly.vc;
             p.tables = m->paged ? m->table : nullptr;
@@ -381,55 +401,38 @@ static int enqueue_step(qd_model* m, hipStream_t s)
             p.chunk = m->attn_chunk;
             p.nsplit = m->attn_nsplit;
             p.part = m->attn_part;
-            p.counters = m->counters + (m->nq + 2 * m->nkv);
             p.out = m->attn;
-            const dim3 grid(m->attn_nsplit, m->nkv, 1);
-            const int gq = m->nq / m->nkv;
-#define QD_ATT(HD_, GQ_)                                                                          \
-    if (m->paged)                                                                                 \
-        hipLaunchKernelGGL((k_attn_decode<HD_, GQ_, true>), grid, dim3(ATT_NT), 0, s, p);         \
-    else                                                                                          \
-        hipLaunchKernelGGL((k_attn_decode<HD_, GQ_, false>), grid, dim3(ATT_NT), 0, s, p);
-            if (m->hd == 128) {
-                if (gq == 1) { QD_ATT(128, 1) } else if (gq == 2) { QD_ATT(128, 2) }
-                else if (gq == 4) { QD_ATT(128, 4) } else { QD_ATT(128, 8) }
-            } else {
-                if (gq == 1) { QD_ATT(64, 1) } else if (gq == 2) { QD_ATT(64, 2) }
-                else if (gq == 4) { QD_ATT(64, 4) } else { QD_ATT(64, 8) }
-            }
-#undef QD_ATT
+            p.q_norm = m->qk_norm ? Ly.q_norm : nullptr;
+            p.k_norm = m->qk_norm ? Ly.k_norm : nullptr;
+            p.eps = m->eps;
+            p.rot = m->rot;
+            p.rope_cos = m->rope_cos;
+            p.rope_sin = m->rope_sin;
+            p.kc = Ly.kc;
+            p.vc = Ly.vc;
+            launch_attention<1>(p, m->hd, m->nq / m->nkv, m->paged, 1, m->nq, s);
         }
         // o-proj + residual, u = x * ffn_norm
-        QD_DISPATCH_LPR(m->lpr_o, 4, {
-            hipLaunchKernelGGL((k_gemv_residual<LPR, RPS, GEMV_NWAVES>), dim3(m->grid_o),
-                               dim3(GEMV_NWAVES * WAVE), gemv_lds_bytes(Ly.o.nb), s, Ly.o.d, Ly.o.qs,
-                               m->attn, Ly.o.rows, Ly.o.nb, m->x, m->u, Ly.ffn_norm, m->ss_part);
-        });
+        QD_GEMV_LAUNCH(k_gemv_residual, CFG_SMALL, m->lpr_o, m->grid_o, gemv_lds_bytes(Ly.o.nb), s,
+                       Ly.o.d, Ly.o.qs, m->attn, Ly.o.rows, Ly.o.nb, m->x, m->u, Ly.ffn_norm,
+                       m->ss_part);
         n_part = m->grid_o;
         // gate|up + SwiGLU
-        QD_DISPATCH_LPR(m->lpr_gu, 4, {
-            hipLaunchKernelGGL((k_gemv_swiglu<LPR, RPS, GEMV_NWAVES>), dim3(m->grid_gu),
-                               dim3(GEMV_NWAVES * WAVE), gemv_lds_bytes(Ly.gu.nb), s, Ly.gu.d,
-                               Ly.gu.qs, m->u, Ly.gu.rows, Ly.gu.nb, m->ss_part, n_part, H, m->eps,
-                               m->act);
-        });
+        QD_GEMV_LAUNCH(k_gemv_swiglu, CFG_WIDE, m->lpr_gu, m->grid_gu, gemv_lds_bytes(Ly.gu.nb), s,
+                       Ly.gu.d, Ly.gu.qs, m->u, Ly.gu.rows, Ly.gu.nb, m->ss_part, n_part, H, m->eps,
+                       m->act);
         // down + residual, u = x * (next attn_norm | final_norm)
         const float* wn = (l + 1 < m->L) ? m->layers[l + 1].attn_norm : m->final_norm;
-        QD_DISPATCH_LPR(m->lpr_down, 4, {
-            hipLaunchKernelGGL((k_gemv_residual<LPR, RPS, GEMV_NWAVES>), dim3(m->grid_down),
-                               dim3(GEMV_NWAVES * WAVE), gemv_lds_bytes(Ly.down.nb), s, Ly.down.d,
-                               Ly.down.qs, m->act, Ly.down.rows, Ly.down.nb, m->x, m->u, wn,
-                               m->ss_part);
-        });
+        QD_GEMV_LAUNCH(k_gemv_residual, CFG_SMALL, m->lpr_down, m->grid_down,
+                       gemv_lds_bytes(Ly.down.nb), s, Ly.down.d, Ly.down.qs, m->act, Ly.down.rows,
+                       Ly.down.nb, m->x, m->u, wn, m->ss_part);
         n_part = m->grid_down;
     }
-    QD_DISPATCH_LPR(m->lpr_lm, 4, {
-        hipLaunchKernelGGL((k_gemv_lmhead<LPR, RPS, GEMV_NWAVES>), dim3(m->grid_lm),
-                           dim3(GEMV_NWAVES * WAVE), gemv_lds_bytes(m->lm.nb), s, m->lm.d, m->lm.qs,
-                           m->u, m->lm.rows, m->lm.nb, m->ss_part, n_part, H, m->eps, m->logits,
-                           m->arg_val, m->arg_idx, m->counters + (m->nq + 2 * m->nkv) + m->nkv,
-                           m->st, m->ids, m->pred, m->max_seq);
-    });
+    QD_GEMV_LAUNCH(k_gemv_lmhead, CFG_HEAD, m->lpr_lm, m->grid_lm, gemv_lds_bytes(m->lm.nb), s,
+                   m->lm.d, m->lm.qs, m->u, m->lm.rows, m->lm.nb, m->ss_part, n_part, H, m->eps,
+                   m->logits, m->arg_val, m->arg_idx);
+    hipLaunchKernelGGL(k_argmax_advance, dim3(1), dim3(256), 0, s, m->arg_val, m->arg_idx,
+                       m->grid_lm, m->V, m->st, m->ids, m->pred, m->max_seq);
     HIP_TRY(hipGetLastError());
     return QD_OK;
 }
@@ -563,43 +566,34 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
     // launch geometry
     {
         const int nbH = H / 32;
+        m->grid_embed = (H + 255) / 256;
         m->lpr_qkv = pick_lpr(nbH);
-        m->rps_qkv = 4;
-        while (m->rps_qkv > 1 && hd % rows_per_tile(m->lpr_qkv, m->rps_qkv))
-            m->rps_qkv /= 2;
-        if (hd % rows_per_tile(m->lpr_qkv, m->rps_qkv))
-            return bail(fail(QD_EUNSUPPORTED, "head_dim %d vs GEMV tile of %d rows", hd,
-                             rows_per_tile(m->lpr_qkv, m->rps_qkv)));
-        const int t_qkv = m->qkv_rows / rows_per_tile(m->lpr_qkv, m->rps_qkv);
-        m->grid_qkv = gemv_grid(t_qkv, 4096);
+        m->grid_qkv = gemv_grid(CFG_QKV, m->lpr_qkv, m->qkv_rows);
         m->lpr_o = pick_lpr(nqd / 32);
-        m->grid_o = gemv_grid((H + rows_per_tile(m->lpr_o, 4) - 1) / rows_per_tile(m->lpr_o, 4), 1024);
+        m->grid_o = gemv_grid(CFG_SMALL, m->lpr_o, H);
         m->lpr_gu = pick_lpr(nbH);
-        m->grid_gu = gemv_grid((2 * m->I + rows_per_tile(m->lpr_gu, 4) - 1) / rows_per_tile(m->lpr_gu, 4), 2048);
+        m->grid_gu = gemv_grid(CFG_WIDE, m->lpr_gu, 2 * m->I);
         m->lpr_down = pick_lpr(m->I / 32);
-        m->grid_down = gemv_grid((H + rows_per_tile(m->lpr_down, 4) - 1) / rows_per_tile(m->lpr_down, 4), 1024);
+        m->grid_down = gemv_grid(CFG_SMALL, m->lpr_down, H);
         m->lpr_lm = pick_lpr(nbH);
-        m->grid_lm = gemv_grid((m->V + rows_per_tile(m->lpr_lm, 4) - 1) / rows_per_tile(m->lpr_lm, 4), 2048);
-        // attention: fixed split over max_seq so the grid does not depend on the position
-        const int tiles = (m->max_seq + ATT_T - 1) / ATT_T;
+        m->grid_lm = gemv_grid(CFG_HEAD, m->lpr_lm, m->V);
+        // attention: 64-key splits over max_seq, so the grid does not depend on the position
         m->attn_chunk = ATT_T;
-        m->attn_nsplit = tiles;
+        m->attn_nsplit = (m->max_seq + ATT_T - 1) / ATT_T;
     }
 
     // step buffers
     const int maxp = 4096;
     if ((rc = dev_alloc_t(m, &m->x, H)) || (rc = dev_alloc_t(m, &m->u, H)) ||
         (rc = dev_alloc_t(m, &m->ss_part, maxp)) || (rc = dev_alloc_t(m, &m->qkv_raw, m->qkv_rows)) ||
-        (rc = dev_alloc_t(m, &m->qbuf, nqd)) || (rc = dev_alloc_t(m, &m->attn, nqd)) ||
-        (rc = dev_alloc_t(m, &m->act, m->I)) || (rc = dev_alloc_t(m, &m->logits, m->V)) ||
-        (rc = dev_alloc_t(m, &m->arg_val, maxp)) || (rc = dev_alloc_t(m, &m->arg_idx, maxp)) ||
-        (rc = dev_alloc_t(m, &m->counters, m->nq + 3 * m->nkv + 1)) ||
+        (rc = dev_alloc_t(m, &m->attn, nqd)) || (rc = dev_alloc_t(m, &m->act, m->I)) ||
+        (rc = dev_alloc_t(m, &m->logits, m->V)) || (rc = dev_alloc_t(m, &m->arg_val, maxp)) ||
+        (rc = dev_alloc_t(m, &m->arg_idx, maxp)) ||
         (rc = dev_alloc_t(m, &m->attn_part, (size_t)m->nq * m->attn_nsplit * (hd + 2))) ||
         (rc = dev_alloc_t(m, &m->st, 1)) || (rc = dev_alloc_t(m, &m->ids, m->max_seq)) ||
         (rc = dev_alloc_t(m, &m->pred, m->max_seq)))
         return bail(rc);
-    if (hipMemsetAsync(m->counters, 0, sizeof(unsigned) * (m->nq + 3 * m->nkv + 1), s) != hipSuccess ||
-        hipMemsetAsync(m->st, 0, sizeof(StepState), s) != hipSuccess ||
+    if (hipMemsetAsync(m->st, 0, sizeof(StepState), s) != hipSuccess ||
         hipMemsetAsync(m->ids, 0, sizeof(int32_t) * m->max_seq, s) != hipSuccess ||
         hipMemsetAsync(m->pred, 0, sizeof(int32_t) * m->max_seq, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)
@@ -720,13 +714,10 @@ extern "C" int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const
 }
 
 static size_t attn_ws_layout(int32_t B, int32_t nq, int32_t nkv, int32_t hd, int32_t max_kv,
-                             int* chunk, int* nsplit, size_t* counters_off)
+                             int* chunk, int* nsplit)
 {
     attn_split(B, nkv, max_kv, chunk, nsplit);
-    size_t part = (size_t)B * nq * (*nsplit) * (hd + 2) * sizeof(float);
-    part = (part + 255) / 256 * 256;
-    *counters_off = part;
-    return part + (size_t)B * nkv * sizeof(unsigned int);
+    return (size_t)B * nq * (*nsplit) * (hd + 2) * sizeof(float);
 }
 
 extern "C" size_t qd_attn_workspace_bytes(int32_t B, int32_t nq, int32_t nkv, int32_t head_dim,
@@ -735,8 +726,7 @@ extern "C" size_t qd_attn_workspace_bytes(int32_t B, int32_t nq, int32_t nkv, in
     if (B <= 0 || nq <= 0 || nkv <= 0 || head_dim <= 0 || max_kv_len < 0)
         return 0;
     int chunk, nsplit;
-    size_t off;
-    return attn_ws_layout(B, nq, nkv, head_dim, max_kv_len, &chunk, &nsplit, &off);
+    return attn_ws_layout(B, nq, nkv, head_dim, max_kv_len, &chunk, &nsplit);
 }
 
 extern "C" int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t workspace_bytes,
@@ -764,12 +754,12 @@ extern "C" int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t w
     if (a->B == 0)
         return QD_OK;
     int chunk, nsplit;
-    size_t coff;
     const size_t need = attn_ws_layout(a->B, a->nq, a->nkv, a->head_dim, a->max_kv_len, &chunk,
-                                       &nsplit, &coff);
+                                       &nsplit);
     if (workspace_bytes < need)
         return fail(QD_EINVAL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
     AttnParams p;
+    memset(&p, 0, sizeof p);
     p.q = a->q;
     p.k = a->k;
     p.v = a->v;
@@ -784,24 +774,9 @@ extern "C" int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t w
     p.chunk = chunk;
     p.nsplit = nsplit;
     p.part = reinterpret_cast<float*>(d_workspace);
-    p.counters = reinterpret_cast<unsigned int*>(reinterpret_cast<char*>(d_workspace) + coff);
     p.out = a->out;
-    hipStream_t s = (hipStream_t)stream;
-    const dim3 grid(nsplit, a->nkv, a->B);
-    const bool paged = a->block_tables != nullptr;
-#define QD_ATT(HD_, GQ_)                                                                          \
-    if (paged)                                                                                    \
-        hipLaunchKernelGGL((k_attn_decode<HD_, GQ_, true>), grid, dim3(ATT_NT), 0, s, p);         \
-    else                                                                                          \
-        hipLaunchKernelGGL((k_attn_decode<HD_, GQ_, false>), grid, dim3(ATT_NT), 0, s, p);
-    if (a->head_dim == 128) {
-        if (gq == 1) { QD_ATT(128, 1) } else if (gq == 2) { QD_ATT(128, 2) }
-        else if (gq == 4) { QD_ATT(128, 4) } else { QD_ATT(128, 8) }
-    } else {
-        if (gq == 1) { QD_ATT(64, 1) } else if (gq == 2) { QD_ATT(64, 2) }
-        else if (gq == 4) { QD_ATT(64, 4) } else { QD_ATT(64, 8) }
-    }
-#undef QD_ATT
+    launch_attention<0>(p, a->head_dim, gq, a->block_tables != nullptr, a->B, a->nq,
+                        (hipStream_t)stream);
     HIP_TRY(hipGetLastError());
     return QD_OK;
 }
