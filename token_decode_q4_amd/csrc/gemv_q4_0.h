@@ -41,10 +41,9 @@ constexpr int XPAD = 36;  // floats per staged x block (32 + pad)
 __host__ __device__ constexpr int gemv_lds_floats(int nb) { return nb * XPAD + nb; }
 
 // x staging in two halves, so that the x loads fly together with the weight
-// loads and with the epilogue's prologue loads:
+// loads and with the epilogue's own prologue loads:
 //   stage_x_load   issues every x load of this thread (K <= 64*NT floats)
-//   stage_x_store  multiplies by *pre (if given: an LDS scalar published by the
-//                  barrier at its start) and writes the LDS layout
+//   stage_x_store  writes the LDS layout
 template <int NT>
 struct XStage {
     static constexpr int MAXU = 16384 / (4 * NT);
@@ -63,19 +62,18 @@ QD_DEV void stage_x_load(const float* __restrict__ x, int nb, XStage<NT>& st)
 }
 
 // Block b at float offset b*XPAD: x[32b .. 32b+15] as is and x[32b+16 .. 32b+31]
-// divided by 16 (exact); xs[b] = the block's sum of x.  Ends with a barrier.
+// divided by 16 (exact); xs[b] = the block's sum of x.  Starts and ends with
+// a barrier (the LDS may still be read by a previous use).
 template <int NT>
-QD_DEV void stage_x_store(int nb, const XStage<NT>& st, float* xl, float* xs, const float* pre)
+QD_DEV void stage_x_store(int nb, const XStage<NT>& st, float* xl, float* xs)
 {
     const int n4 = nb * 8;
-    __syncthreads();   // *pre (if any) is visible
-    const float p = pre ? *pre : 1.f;
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < XStage<NT>::MAXU; ++u) {
         if (u * NT < n4) {   // uniform
             const int i = (int)threadIdx.x + u * NT;
-            float4 w = st.v[u];
-            w.x *= p; w.y *= p; w.z *= p; w.w *= p;
+            const float4 w = st.v[u];
             // 8 consecutive lanes hold one block: its sum is a butterfly over them
             float s = (w.x + w.y) + (w.z + w.w);
             s = group_sum<8>(s);
@@ -140,7 +138,8 @@ struct GemvBuf {
 // strided by gridDim.x.  NBUF register buffers rotate: the loads of item
 // i + NBUF - 1 are issued before item i is consumed.  `epi` receives every
 // finished tile:
-//   epi.prologue()              before staging (may write *epi.pre in LDS)
+//   epi.issue()                 first of all: the epilogue's own loads
+//   epi.finish()                after x is staged: what needs those loads
 //   epi.tile(row0, acc, lead)   acc[RPS] = dot products of rows row0 .. row0+RPS-1
 // Scales come either in the canonical layout d[row][block] (TS = false) or
 // in the tiled layout written by tile_scales() (TS = true): for every (tile,
@@ -249,6 +248,7 @@ QD_DEV void gemv_run(const uint16_t* __restrict__ D, const uint8_t* __restrict__
         }
     };
 
+    epi.issue();
     GemvBuf<RPS, BG> bufs[NBUF];
     if (nitems > 0) {
 #pragma unroll
@@ -257,8 +257,8 @@ QD_DEV void gemv_run(const uint16_t* __restrict__ D, const uint8_t* __restrict__
     }
     XStage<G::NT> xst;
     stage_x_load<G::NT>(x, nb, xst);
-    epi.prologue();
-    stage_x_store<G::NT>(nb, xst, xl, xs, epi.pre);   // ends with a barrier
+    stage_x_store<G::NT>(nb, xst, xl, xs);   // ends with a barrier
+    epi.finish();
     for (int i = 0; i < nitems; i += NBUF) {
 #pragma unroll
         for (int j = 0; j < NBUF; ++j) {
@@ -273,32 +273,38 @@ QD_DEV void gemv_run(const uint16_t* __restrict__ D, const uint8_t* __restrict__
     }
 }
 
-// 1 / sqrt(mean(x^2) + eps) from per-workgroup partial sums of x^2 written by
-// the producer of x, summed by wave 0 in a fixed order (each lane issues all of
-// its loads before adding); written to *out by lane 0 of wave 0.  Needs a
-// barrier before other waves read *out.
-QD_DEV void inv_rms_partials(const float* __restrict__ ss_part, int n_part, int n, float eps,
-                             float* out)
-{
-    if (threadIdx.x < WAVE) {
-        constexpr int U = 16;
-        float s = 0.f;
-        for (int i0 = 0; i0 < n_part; i0 += U * WAVE) {
-            float v[U];
+// 1 / sqrt(mean(x^2) + eps) from the per-workgroup partial sums of x^2 written
+// by the producer of x.  Every wave computes it on its own (no LDS, no
+// barrier): issue() loads up to RMS_U * 64 partials into registers, finish()
+// sums them -- then any further ones -- in a fixed order, so every wave of
+// every workgroup gets the same value.
+constexpr int RMS_U = 16;
+struct RmsPartials {
+    const float* ss_part;
+    int n_part;
+    float v[RMS_U];
+    QD_DEV void issue()
+    {
+        const int lane = threadIdx.x & (WAVE - 1);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int i = i0 + (int)threadIdx.x + u * WAVE;
-                v[u] = (i < n_part) ? ss_part[i] : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                s += v[u];
+        for (int u = 0; u < RMS_U; ++u) {
+            const int i = lane + u * WAVE;
+            v[u] = (i < n_part) ? ss_part[i] : 0.f;
         }
-        s = group_sum<WAVE>(s);
-        if (threadIdx.x == 0)
-            *out = 1.0f / sqrtf(s / (float)n + eps);
     }
-}
+    QD_DEV float finish(int n, float eps) const
+    {
+        const int lane = threadIdx.x & (WAVE - 1);
+        float s = 0.f;
+#pragma unroll
+        for (int u = 0; u < RMS_U; ++u)
+            s += v[u];
+        for (int i = lane + RMS_U * WAVE; i < n_part; i += WAVE)
+            s += ss_part[i];
+        s = group_sum<WAVE>(s);
+        return 1.0f / sqrtf(s / (float)n + eps);
+    }
+};
 
 // ----------------------------------------------------------------- epilogues
 
@@ -306,8 +312,8 @@ QD_DEV void inv_rms_partials(const float* __restrict__ ss_part, int n_part, int 
 struct EpiStore {
     float* y;
     int N;
-    const float* pre = nullptr;
-    QD_DEV void prologue() {}
+    QD_DEV void issue() {}
+    QD_DEV void finish() {}
     template <int RPS>
     QD_DEV void tile(int row0, const float (&acc)[RPS], bool lead)
     {

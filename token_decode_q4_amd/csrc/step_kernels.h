@@ -92,16 +92,16 @@ k_embed(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, int H, 
 
 // ----------------------------------------------------------------- GEMV epilogues
 
-// y[row] = W (u / rms): the 1/rms of the producer's x (from its partial sums)
-// multiplies u when it is staged
+// y[row] = (W u)[row] / rms, with 1/rms from the producer's partial sums
 struct EpiScaled {
     float* y;
     int N;
-    const float* ss_part;
-    int n_part, n_in;
+    RmsPartials rp;
+    int n_in;
     float eps;
-    float* pre;   // LDS scalar
-    QD_DEV void prologue() { inv_rms_partials(ss_part, n_part, n_in, eps, pre); }
+    float inv;
+    QD_DEV void issue() { rp.issue(); }
+    QD_DEV void finish() { inv = rp.finish(n_in, eps); }
     template <int RPS>
     QD_DEV void tile(int row0, const float (&acc)[RPS], bool lead)
     {
@@ -109,7 +109,7 @@ struct EpiScaled {
 #pragma unroll
             for (int r = 0; r < RPS; ++r)
                 if (row0 + r < N)
-                    y[row0 + r] = acc[r];
+                    y[row0 + r] = acc[r] * inv;
         }
     }
 };
@@ -121,8 +121,8 @@ struct EpiResidual {
     const float* w_next;
     int N;
     float ss;
-    const float* pre = nullptr;
-    QD_DEV void prologue() {}
+    QD_DEV void issue() {}
+    QD_DEV void finish() {}
     template <int RPS>
     QD_DEV void tile(int row0, const float (&acc)[RPS], bool lead)
     {
@@ -142,15 +142,16 @@ struct EpiResidual {
 };
 
 // rows interleaved (2i = gate_i, 2i+1 = up_i): act[i] = silu(g) * up, with
-// g and up computed from u / rms
+// g = (Wg u)/rms and up = (Wu u)/rms
 struct EpiSwiglu {
     float* act;
     int N;
-    const float* ss_part;
-    int n_part, n_in;
+    RmsPartials rp;
+    int n_in;
     float eps;
-    float* pre;
-    QD_DEV void prologue() { inv_rms_partials(ss_part, n_part, n_in, eps, pre); }
+    float inv;
+    QD_DEV void issue() { rp.issue(); }
+    QD_DEV void finish() { inv = rp.finish(n_in, eps); }
     template <int RPS>
     QD_DEV void tile(int row0, const float (&acc)[RPS], bool lead)
     {
@@ -159,7 +160,7 @@ struct EpiSwiglu {
 #pragma unroll
             for (int r = 0; r < RPS; r += 2) {
                 if (row0 + r + 1 < N) {
-                    const float gt = acc[r], up = acc[r + 1];
+                    const float gt = acc[r] * inv, up = acc[r + 1] * inv;
                     act[(row0 + r) >> 1] = gt / (1.0f + expf(-gt)) * up;
                 }
             }
@@ -167,17 +168,18 @@ struct EpiSwiglu {
     }
 };
 
-// logits[row] = W (u / rms); running best (value, lowest index among equals)
+// logits[row] = (W u)[row] / rms; running best (value, lowest index among equals)
 struct EpiLmHead {
     float* logits;
     int N;
-    const float* ss_part;
-    int n_part, n_in;
+    RmsPartials rp;
+    int n_in;
     float eps;
-    float* pre;
+    float inv;
     float best;
     int32_t bidx;
-    QD_DEV void prologue() { inv_rms_partials(ss_part, n_part, n_in, eps, pre); }
+    QD_DEV void issue() { rp.issue(); }
+    QD_DEV void finish() { inv = rp.finish(n_in, eps); }
     template <int RPS>
     QD_DEV void tile(int row0, const float (&acc)[RPS], bool lead)
     {
@@ -186,7 +188,7 @@ struct EpiLmHead {
             for (int r = 0; r < RPS; ++r) {
                 const int row = row0 + r;
                 if (row < N) {
-                    const float v = acc[r];
+                    const float v = acc[r] * inv;
                     logits[row] = v;
                     if (v > best || (v == best && row < bidx)) {
                         best = v;
@@ -207,8 +209,7 @@ k_gemv_scaled(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
               int n_part, int n_in, float eps_in, float* __restrict__ y)
 {
     extern __shared__ float smem[];
-    __shared__ float inv;
-    EpiScaled e{y, N, ss_part, n_part, n_in, eps_in, &inv};
+    EpiScaled e{y, N, {ss_part, n_part}, n_in, eps_in};
     gemv_run<LPR, RPS, NWAVES, BG, NBUF, NTL, false>(D, Q, u, N, nb, smem, smem + nb * XPAD, e);
 }
 
@@ -235,8 +236,7 @@ k_gemv_swiglu(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
               int n_part, int n_in, float eps_in, float* __restrict__ act)
 {
     extern __shared__ float smem[];
-    __shared__ float inv;
-    EpiSwiglu e{act, N, ss_part, n_part, n_in, eps_in, &inv};
+    EpiSwiglu e{act, N, {ss_part, n_part}, n_in, eps_in};
     gemv_run<LPR, RPS, NWAVES, BG, NBUF, NTL, false>(D, Q, u, N, nb, smem, smem + nb * XPAD, e);
 }
 
@@ -249,9 +249,9 @@ k_gemv_lmhead(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
               float* __restrict__ part_val, int32_t* __restrict__ part_idx)
 {
     extern __shared__ float smem[];
-    __shared__ float inv, bv[NWAVES];
+    __shared__ float bv[NWAVES];
     __shared__ int32_t bi[NWAVES];
-    EpiLmHead e{logits, N, ss_part, n_part, n_in, eps_in, &inv, -INFINITY, 0x7fffffff};
+    EpiLmHead e{logits, N, {ss_part, n_part}, n_in, eps_in, 0.f, -INFINITY, 0x7fffffff};
     gemv_run<LPR, RPS, NWAVES, BG, NBUF, NTL, false>(D, Q, u, N, nb, smem, smem + nb * XPAD, e);
     float best = e.best;
     int32_t bidx = e.bidx;
