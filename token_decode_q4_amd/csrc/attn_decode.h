@@ -3,29 +3,33 @@
 // Computes, for every query head h of sequence b,
 //   out = softmax(scale * q_h K^T) V   over keys t in [0, kv_len[b])
 // with kv head g = h / (nq/nkv) (inferencelayer cuda_llm.rs page, attn_partial,
-// attn_reduce and the flash-decoding arm that stages a K/V chunk once for the
+// attn_reduce and the flash-decoding arm that reads a K/V chunk once for the
 // whole query group; ferrum-kernels cuda_decode.rs page, flash_decode_attention
 // phase 1/2, paged_decode_attention, batched_decode_attention).
 //
-// k_attn_split: grid (nsplit, nkv, B).  A workgroup owns one (sequence, kv
-// head, key range) and serves all GQ query heads of that kv head: each 64-key
-// tile of K and V is copied to LDS once and read by the GQ heads from there.
-// Per tile:
-//   1. QK: 16 lanes per key (128 dims, 8 dims a lane, one 128-bit LDS read);
-//      each lane holds its 8 dims of all GQ queries in registers.
-//   2. online softmax: one wave per head over the 64 keys (running max m,
-//      running sum l, rescale factor for the accumulators).
-//   3. PV: lanes own 2 output dims, waves own 16 keys; each V element read
-//      once from LDS and used by all GQ heads.
-// It writes its partial (acc[hd], m, l) per head.  k_attn_combine (grid
-// (nq, B)) merges a head's partials with the online-softmax rule
+// k_attn_split: grid (nsplit, nkv, B), 4 waves.  A workgroup owns one
+// (sequence, kv head, key range) and serves all GQ query heads of that kv
+// head.  Each wave works on its own 16-key steps (one paged block) with no
+// workgroup barrier until the end:
+//   QK   lane (key k = lane/4, quarter c = lane%4) holds 8 dims of K[k] in each
+//        32-dim slice (dims 32i + 8c .. +7), reads the matching query dims from
+//        LDS and reduces the 4 quarters with two shuffles;
+//   softmax  per head over the 16 keys (shuffles across the key lanes), online
+//        across the wave's steps (running max m, sum l, rescale of acc);
+//   PV   lane owns HD/64 output dims; the step's probabilities go through a
+//        small per-wave LDS table [key][head]; V is loaded in that layout.
+// The four waves' (m, l, acc) are merged once through LDS and written as the
+// workgroup's partial.  k_attn_combine (grid (nq, B)) merges a head's partials:
 //   M = max_s m_s,  out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s.
 //
-// In the decode step the split kernel also finishes the projection: it reads
-// the raw q|k|v of the token, applies the per-head q/k RMSNorm and the NeoX
-// rotary at the position (ferrum-kernels cuda_decode.rs page, the q/k norm
-// then rope order of decode_step), and the one workgroup whose key range holds
-// the position stores the token's K and V (f16) in the cache and in its tile.
+// In the decode step (QMODE 1) the split kernel also finishes the projection:
+// from the raw q|k|v of the token it applies the per-head q/k RMSNorm and the
+// NeoX rotary at the position (ferrum-kernels cuda_decode.rs page, the q/k
+// norm then rope order of decode_step), and the wave whose keys hold the
+// position stores the token's K and V (f16) in the cache and uses the same f16
+// values.  There the block table covers every position below max_kv, so the
+// first step's table entry and K/V loads are issued before the position is
+// known; keys at or past kv_len are masked (score -inf, V taken as 0).
 #pragma once
 
 #include "qd_common.h"
@@ -43,358 +47,398 @@ struct AttnParams {
     int max_kv;                // contiguous capacity per (b, g); bound on kv_len
     int nq, nkv;
     float scale;
-    int chunk;                 // keys per split, a multiple of 64
+    int chunk;                 // keys per split, a multiple of ATT_T
     int nsplit;
     float* part;               // [B][nq][nsplit][HD + 2]
     float* out;                // [B][nq][HD] (combine)
     // decode-step prologue (QMODE 1)
-    const float* q_norm;       // [HD] or nullptr (no q/k norm)
+    int qk_norm;               // 1: per-head RMSNorm of q and k
+    const float* q_norm;       // [HD] (valid even when qk_norm is 0)
     const float* k_norm;
     float eps;
     int rot;
-    const float* rope_cos;     // [max_kv][rot/2]
-    const float* rope_sin;
+    const float* rope_cur;     // cos [rot/2] then sin [rot/2] at the step's position
     uint16_t* kc;              // cache written at pos (same buffers as k/v)
     uint16_t* vc;
 };
 
-constexpr int ATT_T = 64;      // keys per LDS tile
-constexpr int ATT_BS = 16;     // paged block size
-constexpr int ATT_NT = 256;    // threads per workgroup
+constexpr int ATT_WK = 16;                 // keys per wave step (one paged block)
+constexpr int ATT_NW = 4;                  // waves per workgroup
+constexpr int ATT_T = ATT_WK * ATT_NW;     // keys per workgroup step
+constexpr int ATT_BS = 16;                 // paged block size
+constexpr int ATT_NT = ATT_NW * WAVE;      // threads per workgroup
 
 template <int HD, int GQ>
-struct AttnSmem {
-    uint16_t kt[ATT_T * HD];
-    uint16_t vt[ATT_T * HD];
-    float sc[GQ][ATT_T];       // scores, then probabilities
-    float m[GQ], l[GQ], alpha[GQ];
-    float qv[GQ + 1][HD];      // prologue: q heads (+ the token's k)
-    float red[4][GQ][HD];      // cross-wave reduction of the accumulators
-    float ss[GQ + 1];
+struct alignas(16) AttnSmem {
+    float q[ATT_NW][GQ][HD];        // per wave: queries ready for QK (times scale)
+    float krow[ATT_NW][HD];         // per wave: the token's k during its rotary
+    float p[ATT_NW][ATT_WK][GQ];    // per wave: probabilities of the step, [key][head]
+    uint16_t knew[ATT_NW][HD];      // per wave: the token's k in f16
+    float m[ATT_NW][GQ], l[ATT_NW][GQ];
+    float acc[ATT_NW][GQ][HD];
 };
 
+// LDS writes of this wave are seen by its later LDS reads (no workgroup barrier)
+QD_DEV void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int HD, bool PAGED>
-QD_DEV size_t kv_offset(const AttnParams& p, int phys_or_b, int g, int t)
+QD_DEV size_t kv_row(const AttnParams& p, int phys_or_b, int g, int t)
 {
     if (PAGED)
         return (((size_t)phys_or_b * p.nkv + g) * ATT_BS + (t % ATT_BS)) * HD;
     return (((size_t)phys_or_b * p.nkv + g) * p.max_kv + t) * HD;
 }
 
+// registers of one wave step: K in the QK layout, V in the PV layout
+template <int HD>
+struct AttnStep {
+    static constexpr int NI = HD / 32;     // 32-dim slices
+    static constexpr int DPL = HD / WAVE;  // output dims per lane
+    uint4 k[NI];
+    uint32_t v[ATT_WK];                    // DPL f16 of key kk in the low (and high) half
+};
+
 // QMODE 0: q given (standalone); QMODE 1: decode-step prologue from raw q|k|v
 template <int HD, int GQ, bool PAGED, int QMODE>
 __global__ void __launch_bounds__(ATT_NT) k_attn_split(AttnParams p)
 {
     static_assert(HD == 64 || HD == 128, "head_dim");
-    static_assert(GQ >= 1 && GQ <= 8, "group");
+    static_assert(GQ == 1 || GQ == 2 || GQ == 4 || GQ == 8, "group");
     __shared__ AttnSmem<HD, GQ> sm;
-    constexpr int LPK = HD / 8;          // lanes per key in QK (8 dims each)
-    constexpr int KPP = WAVE / LPK;      // keys per wave pass
-    constexpr int DPL = HD / WAVE;       // output dims per lane in PV (1 or 2)
-    constexpr int PIECES = ATT_T * HD / 8;      // 16-byte pieces per K (or V) tile
-    constexpr int PPT = PIECES / ATT_NT;        // pieces per thread (2 or 4)
-    constexpr int MAXIT = ((GQ + 1) * HD + ATT_NT - 1) / ATT_NT;
+    using Step = AttnStep<HD>;
+    constexpr int NI = Step::NI, DPL = Step::DPL;
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
-    int kv_len = p.kv_lens ? p.kv_lens[b] : (*p.pos + 1);
-    kv_len = max(0, min(kv_len, p.max_kv));
-    const int t_begin = s * p.chunk;
-    const int t_end = min(kv_len, t_begin + p.chunk);
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+    const int kk = lane >> 2, cq = lane & 3;   // QK layout: key, quarter
     const int h0 = g * GQ;
-    const int cur = kv_len - 1;                       // the step's own position (QMODE 1)
-    const bool owner = QMODE == 1 && cur >= t_begin && cur < t_end;
-    if (t_begin >= t_end)
-        return;   // key range past kv_len: the combine reads only active splits
+    const int t_begin = s * p.chunk;
+    QD_MARK(0);
 
-    // ---- every prologue load first: queries (and the token's k, v), rotary
-    // factors and norm weights of this thread's elements
-    const int nrows = owner ? GQ + 1 : GQ;
-    const int half = p.rot / 2;
-    float qe[MAXIT], ce[MAXIT], se[MAXIT], we[MAXIT];
-    float vtok = 0.f;
-#pragma unroll
-    for (int it = 0; it < MAXIT; ++it) {
-        const int i = tid + it * ATT_NT;
-        qe[it] = 0.f;
-        ce[it] = 1.f;
-        se[it] = 0.f;
-        we[it] = 1.f;
-        if (i < nrows * HD) {
-            const int j = i / HD, d = i % HD;
-            if (QMODE == 0) {
-                qe[it] = p.q[((size_t)b * p.nq + h0) * HD + i];
-            } else {
-                qe[it] = (j < GQ) ? p.q[(size_t)(h0 + j) * HD + d] : p.q[((size_t)p.nq + g) * HD + d];
-                if (d < p.rot) {
-                    const int ii = d < half ? d : d - half;
-                    ce[it] = p.rope_cos[(size_t)cur * half + ii];
-                    se[it] = p.rope_sin[(size_t)cur * half + ii];
-                }
-                if (p.q_norm)
-                    we[it] = (j == GQ) ? p.k_norm[d] : p.q_norm[d];
-            }
+    // loads of one wave step at key tw, any tw: rows and table entries are
+    // clamped into range (never a branch around a load); rows past kv_len are
+    // masked where they are used
+    auto load_step = [&](Step& st, int tw) {
+        const int twc = min(tw, p.max_kv - 1);
+        const uint16_t *kp, *vp;
+        if (PAGED) {
+            const int phys = max(0, p.tables[(size_t)b * p.mbps + twc / ATT_BS]);
+            const size_t base = kv_row<HD, PAGED>(p, phys, g, twc & ~(ATT_BS - 1));
+            kp = p.k + base + (size_t)kk * HD;
+            vp = p.v + base;
+        } else {
+            kp = p.k + kv_row<HD, PAGED>(p, b, g, min(tw + kk, p.max_kv - 1));
+            vp = p.v + kv_row<HD, PAGED>(p, b, g, 0);
         }
-    }
-    if (owner && tid < HD)
-        vtok = p.q[((size_t)p.nq + p.nkv + g) * HD + tid];
-
-    // ---- first tile's K/V loads
-    uint4 kr[PPT], vr[PPT];
-    auto load_tile = [&](int t0, int n) {
-        int phys[ATT_T / ATT_BS];
 #pragma unroll
-        for (int k = 0; k < ATT_T / ATT_BS; ++k) {
-            if (PAGED)
-                phys[k] = (k * ATT_BS < n) ? p.tables[(size_t)b * p.mbps + t0 / ATT_BS + k] : 0;
+        for (int i = 0; i < NI; ++i)
+            st.k[i] = *reinterpret_cast<const uint4*>(kp + 8 * cq + 32 * i);
+#pragma unroll
+        for (int j = 0; j < ATT_WK; ++j) {
+            const uint16_t* r = PAGED ? vp + (size_t)j * HD
+                                      : vp + (size_t)min(tw + j, p.max_kv - 1) * HD;
+            if (DPL == 2)
+                st.v[j] = *reinterpret_cast<const uint32_t*>(r + lane * DPL);
             else
-                phys[k] = b;
-        }
-#pragma unroll
-        for (int u = 0; u < PPT; ++u) {
-            const int i = tid + u * ATT_NT;
-            const int tk = i / (HD / 8), off = (i % (HD / 8)) * 8;
-            kr[u] = make_uint4(0, 0, 0, 0);
-            vr[u] = make_uint4(0, 0, 0, 0);
-            if (tk < n) {
-                const size_t o = kv_offset<HD, PAGED>(p, phys[tk / ATT_BS], g, t0 + tk) + off;
-                kr[u] = *reinterpret_cast<const uint4*>(p.k + o);
-                vr[u] = *reinterpret_cast<const uint4*>(p.v + o);
-            }
+                st.v[j] = r[lane * DPL];
         }
     };
-    load_tile(t_begin, min(ATT_T, t_end - t_begin));
 
-    // ---- queries into LDS; per-head q/k RMSNorm and NeoX rotary (QMODE 1)
+    // kv_len first (vector loads return in order): the loads below do not need it
+    int kv_len = p.kv_lens ? p.kv_lens[b] : (*p.pos + 1);
+
+    // ---- loads that do not need kv_len: the token's q|k|v, norm weights,
+    // rotary factors, and (decode step) the first step's K/V
+    float qv[GQ][DPL], kv_[DPL], vv[DPL], wq[DPL], wk[DPL], cs[DPL], sn[DPL];
 #pragma unroll
-    for (int it = 0; it < MAXIT; ++it) {
-        const int i = tid + it * ATT_NT;
-        if (i < nrows * HD)
-            sm.qv[i / HD][i % HD] = qe[it];
+    for (int e = 0; e < DPL; ++e) {
+        const int d = lane * DPL + e;
+#pragma unroll
+        for (int j = 0; j < GQ; ++j)
+            qv[j][e] = (QMODE == 0) ? p.q[((size_t)b * p.nq + h0 + j) * HD + d]
+                                    : p.q[(size_t)(h0 + j) * HD + d];
+        kv_[e] = vv[e] = 0.f;
+        wq[e] = wk[e] = cs[e] = 1.f;
+        sn[e] = 0.f;
+        if (QMODE == 1) {
+            // q_norm / k_norm / rope_cur always point at valid arrays here
+            kv_[e] = p.q[((size_t)p.nq + g) * HD + d];
+            vv[e] = p.q[((size_t)p.nq + p.nkv + g) * HD + d];
+            wq[e] = p.q_norm[d];
+            wk[e] = p.k_norm[d];
+            const int half = p.rot / 2;
+            const int ii = d < half ? d : (d < p.rot ? d - half : 0);
+            const float c0 = p.rope_cur[ii], s0 = p.rope_cur[half + ii];
+            cs[e] = d < p.rot ? c0 : 1.f;
+            sn[e] = d < p.rot ? s0 : 0.f;
+        }
     }
-    __syncthreads();
+    Step cur_st;
+    const int tw0 = t_begin + w * ATT_WK;
+    load_step(cur_st, tw0);
+
+    kv_len = max(0, min(kv_len, p.max_kv));
+    if (kv_len >= 0)
+        QD_MARK(1);
+    const int t_end = min(kv_len, t_begin + p.chunk);
+    if (t_begin >= t_end)
+        return;   // key range past kv_len: the combine reads only active splits
+    const int tcur = kv_len - 1;   // the step's own position (QMODE 1)
+
+    // ---- queries: per-head RMSNorm and rotary (QMODE 1), times scale, into
+    // this wave's LDS rows; the wave holding tcur also prepares the token's K/V
+    // the owner: the wave whose step own_tw holds tcur, at row slot of it
+    float vnew[DPL];
+    const int rel = tcur - t_begin;
+    const bool owner = QMODE == 1 && tcur >= t_begin && tcur < t_end && (rel / ATT_WK) % ATT_NW == w;
+    const int own_tw = t_begin + (rel / ATT_WK) * ATT_WK;
+    const int slot = tcur - own_tw;
     if (QMODE == 1) {
-        if (p.q_norm) {
-            for (int j = wave; j < nrows; j += ATT_NT / WAVE) {
+        const float* nq_w = wq;
+        if (p.qk_norm) {
+#pragma unroll
+            for (int j = 0; j < GQ; ++j) {
                 float ss = 0.f;
-                for (int d = lane; d < HD; d += WAVE)
-                    ss += sm.qv[j][d] * sm.qv[j][d];
+#pragma unroll
+                for (int e = 0; e < DPL; ++e)
+                    ss = fmaf(qv[j][e], qv[j][e], ss);
                 ss = group_sum<WAVE>(ss);
-                if (lane == 0)
-                    sm.ss[j] = 1.0f / sqrtf(ss / (float)HD + p.eps);
-            }
-            __syncthreads();
+                const float r = 1.0f / sqrtf(ss / (float)HD + p.eps);
 #pragma unroll
-            for (int it = 0; it < MAXIT; ++it) {
-                const int i = tid + it * ATT_NT;
-                if (i < nrows * HD) {
-                    qe[it] = qe[it] * sm.ss[i / HD] * we[it];
-                    sm.qv[i / HD][i % HD] = qe[it];
-                }
+                for (int e = 0; e < DPL; ++e)
+                    qv[j][e] = qv[j][e] * r * nq_w[e];
             }
-            __syncthreads();
-        }
+            if (owner) {
+                float ss = 0.f;
 #pragma unroll
-        for (int it = 0; it < MAXIT; ++it) {
-            const int i = tid + it * ATT_NT;
-            if (i < nrows * HD) {
-                const int j = i / HD, d = i % HD;
-                if (d < p.rot)
-                    qe[it] = d < half ? qe[it] * ce[it] - sm.qv[j][d + half] * se[it]
-                                      : sm.qv[j][d - half] * se[it] + qe[it] * ce[it];
+                for (int e = 0; e < DPL; ++e)
+                    ss = fmaf(kv_[e], kv_[e], ss);
+                ss = group_sum<WAVE>(ss);
+                const float r = 1.0f / sqrtf(ss / (float)HD + p.eps);
+#pragma unroll
+                for (int e = 0; e < DPL; ++e)
+                    kv_[e] = kv_[e] * r * wk[e];
             }
         }
-        __syncthreads();
+        // rotary: the partner of dim d is d +- rot/2, read from LDS
 #pragma unroll
-        for (int it = 0; it < MAXIT; ++it) {
-            const int i = tid + it * ATT_NT;
-            if (i < nrows * HD)
-                sm.qv[i / HD][i % HD] = qe[it];
+        for (int e = 0; e < DPL; ++e) {
+#pragma unroll
+            for (int j = 0; j < GQ; ++j)
+                sm.q[w][j][lane * DPL + e] = qv[j][e];
+            sm.krow[w][lane * DPL + e] = kv_[e];
         }
-        __syncthreads();
+        wave_lds_sync();
+        const int half = p.rot / 2;
+        float qpart[GQ][DPL], kpart[DPL];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) {
+            const int d = lane * DPL + e;
+            const int pd = d < half ? d + half : d - half;
+            const bool rd = d < p.rot;
+#pragma unroll
+            for (int j = 0; j < GQ; ++j)
+                qpart[j][e] = rd ? sm.q[w][j][pd] : 0.f;
+            kpart[e] = rd ? sm.krow[w][pd] : 0.f;
+        }
+        wave_lds_sync();   // every partner read done before the rows change
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) {
+            const int d = lane * DPL + e;
+            if (d < p.rot) {
+                const float sg = d < half ? -sn[e] : sn[e];
+#pragma unroll
+                for (int j = 0; j < GQ; ++j)
+                    qv[j][e] = fmaf(qpart[j][e], sg, qv[j][e] * cs[e]);
+                kv_[e] = fmaf(kpart[e], sg, kv_[e] * cs[e]);
+            }
+        }
         if (owner) {
-            // the token's K and V, rounded to f16 once: cache and tile get the same values
             size_t o;
-            if (PAGED) {
-                const int phys = p.tables[(size_t)b * p.mbps + cur / ATT_BS];
-                o = kv_offset<HD, PAGED>(p, phys, g, cur);
-            } else {
-                o = kv_offset<HD, PAGED>(p, b, g, cur);
-            }
-            if (tid < HD) {
-                const uint16_t kh = f32_to_f16(sm.qv[GQ][tid]);
-                const uint16_t vh = f32_to_f16(vtok);
-                p.kc[o + tid] = kh;
-                p.vc[o + tid] = vh;
-                sm.qv[GQ][tid] = __uint_as_float(((uint32_t)vh << 16) | kh);   // stash for the tile
+            if (PAGED)
+                o = kv_row<HD, PAGED>(p, p.tables[(size_t)b * p.mbps + tcur / ATT_BS], g, tcur);
+            else
+                o = kv_row<HD, PAGED>(p, b, g, tcur);
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) {
+                const int d = lane * DPL + e;
+                const uint16_t kh = f32_to_f16(kv_[e]);
+                const uint16_t vh = f32_to_f16(vv[e]);
+                p.kc[o + d] = kh;
+                p.vc[o + d] = vh;
+                sm.knew[w][d] = kh;
+                vnew[e] = f16_to_f32(vh);
             }
         }
     }
-    const int part = lane % LPK;
-    float qr[GQ][8];
 #pragma unroll
-    for (int j = 0; j < GQ; ++j)
+    for (int e = 0; e < DPL; ++e)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            qr[j][e] = sm.qv[j][part * 8 + e] * p.scale;
-    if (tid < GQ) {
-        sm.m[tid] = -INFINITY;
-        sm.l[tid] = 0.f;
-    }
-    float acc[GQ][DPL];
+        for (int j = 0; j < GQ; ++j)
+            sm.q[w][j][lane * DPL + e] = qv[j][e] * p.scale;
+    wave_lds_sync();
+    QD_MARK(2);
+
+    // ---- the wave's steps
+    float m[GQ], l[GQ], acc[GQ][DPL];
 #pragma unroll
-    for (int j = 0; j < GQ; ++j)
+    for (int j = 0; j < GQ; ++j) {
+        m[j] = -INFINITY;
+        l[j] = 0.f;
 #pragma unroll
         for (int e = 0; e < DPL; ++e)
             acc[j][e] = 0.f;
-
-    for (int t0 = t_begin; t0 < t_end; t0 += ATT_T) {
-        const int n = min(ATT_T, t_end - t0);
+    }
+    for (int tw = tw0; tw < t_end; tw += ATT_T) {
+        Step nxt;
+        const bool more = tw + ATT_T < t_end;
+        if (more)
+            load_step(nxt, tw + ATT_T);
+        const int nvalid = min(ATT_WK, t_end - tw);
+        const bool own_here = owner && tw == own_tw;
+        // QK: 8 dims x NI slices of key kk
+        float kf[NI][8];
+        uint4 kr[NI];
 #pragma unroll
-        for (int u = 0; u < PPT; ++u) {
-            const int i = tid + u * ATT_NT;
-            const int tk = i / (HD / 8), off = (i % (HD / 8)) * 8;
-            *reinterpret_cast<uint4*>(&sm.kt[tk * HD + off]) = kr[u];
-            *reinterpret_cast<uint4*>(&sm.vt[tk * HD + off]) = vr[u];
-        }
-        __syncthreads();
-        // the next tile's loads fly while this one is consumed
-        if (t0 + ATT_T < t_end)
-            load_tile(t0 + ATT_T, min(ATT_T, t_end - t0 - ATT_T));
-        if (owner && cur >= t0 && cur < t0 + n) {
-            const int slot = cur - t0;
-            for (int d = tid; d < HD; d += ATT_NT) {
-                const uint32_t kv = __float_as_uint(sm.qv[GQ][d]);
-                sm.kt[slot * HD + d] = (uint16_t)(kv & 0xffffu);
-                sm.vt[slot * HD + d] = (uint16_t)(kv >> 16);
-            }
-            __syncthreads();
-        }
-        // ---- QK
+        for (int i = 0; i < NI; ++i)
+            kr[i] = cur_st.k[i];
+        if (own_here && kk == slot) {
 #pragma unroll
-        for (int pass = 0; pass < (ATT_T / 4) / KPP; ++pass) {
-            const int tk = wave * (ATT_T / 4) + pass * KPP + lane / LPK;
-            const uint4 kraw = *reinterpret_cast<const uint4*>(&sm.kt[tk * HD + part * 8]);
-            const uint32_t kw[4] = {kraw.x, kraw.y, kraw.z, kraw.w};
-            float kf[8];
+            for (int i = 0; i < NI; ++i)
+                kr[i] = *reinterpret_cast<const uint4*>(&sm.knew[w][32 * i + 8 * cq]);
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const uint32_t kw[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                kf[2 * e] = f16_to_f32((uint16_t)(kw[e] & 0xffffu));
-                kf[2 * e + 1] = f16_to_f32((uint16_t)(kw[e] >> 16));
-            }
-#pragma unroll
-            for (int j = 0; j < GQ; ++j) {
-                float d = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    d = fmaf(qr[j][e], kf[e], d);
-                d = group_sum<LPK>(d);
-                if (part == 0)
-                    sm.sc[j][tk] = tk < n ? d : -INFINITY;
+                kf[i][2 * e] = f16_to_f32((uint16_t)(kw[e] & 0xffffu));
+                kf[i][2 * e + 1] = f16_to_f32((uint16_t)(kw[e] >> 16));
             }
         }
-        __syncthreads();
-        // ---- online softmax, one wave per head
-        for (int j = wave; j < GQ; j += ATT_NT / WAVE) {
-            const float sv = sm.sc[j][lane];
-            const float mold = sm.m[j];
-            const float mnew = fmaxf(mold, group_max<WAVE>(sv));
-            const float pr = (lane < n) ? expf(sv - mnew) : 0.f;
-            const float ps = group_sum<WAVE>(pr);
-            const float al = expf(mold - mnew);   // 0 on the first tile (mold = -inf)
-            sm.sc[j][lane] = pr;
-            __builtin_amdgcn_wave_barrier();
-            if (lane == 0) {
-                sm.m[j] = mnew;
-                sm.l[j] = sm.l[j] * al + ps;
-                sm.alpha[j] = al;
-            }
-        }
-        __syncthreads();
-        // ---- PV
+        const bool kvalid = kk < nvalid;
+        float sc[GQ];
 #pragma unroll
         for (int j = 0; j < GQ; ++j) {
-            const float al = sm.alpha[j];
+            float d = 0.f;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const float4 qa = *reinterpret_cast<const float4*>(&sm.q[w][j][32 * i + 8 * cq]);
+                const float4 qb = *reinterpret_cast<const float4*>(&sm.q[w][j][32 * i + 8 * cq + 4]);
+                d = fmaf(qa.x, kf[i][0], d);
+                d = fmaf(qa.y, kf[i][1], d);
+                d = fmaf(qa.z, kf[i][2], d);
+                d = fmaf(qa.w, kf[i][3], d);
+                d = fmaf(qb.x, kf[i][4], d);
+                d = fmaf(qb.y, kf[i][5], d);
+                d = fmaf(qb.z, kf[i][6], d);
+                d = fmaf(qb.w, kf[i][7], d);
+            }
+            d = group_sum<4>(d);   // the 4 quarters of key kk
+            sc[j] = kvalid ? d : -INFINITY;
+        }
+        // online softmax over the step's keys: the 4 lanes of a key hold the
+        // same score, so the max runs over the whole wave and the sum over
+        // the quarter-0 lanes (the others add zeros)
+        float alpha[GQ];
+#pragma unroll
+        for (int j = 0; j < GQ; ++j) {
+            const float mnew = fmaxf(m[j], group_max<WAVE>(sc[j]));
+            const float pr = expf(sc[j] - mnew);
+            const float ps = group_sum<WAVE>(cq == 0 ? pr : 0.f);
+            alpha[j] = expf(m[j] - mnew);   // 0 on the first step (m = -inf)
+            l[j] = fmaf(l[j], alpha[j], ps);
+            m[j] = mnew;
+            if (cq == 0)
+                sm.p[w][kk][j] = pr;
+        }
+        wave_lds_sync();
+        // PV: lane owns dims lane*DPL ..
+#pragma unroll
+        for (int j = 0; j < GQ; ++j)
 #pragma unroll
             for (int e = 0; e < DPL; ++e)
-                acc[j][e] *= al;
-        }
-        for (int i = 0; i < ATT_T / 4; ++i) {
-            const int tk = wave * (ATT_T / 4) + i;
-            float vf[2];
-            if (DPL == 2) {
-                const uint32_t w2 = *reinterpret_cast<const uint32_t*>(&sm.vt[tk * HD + lane * 2]);
-                vf[0] = f16_to_f32((uint16_t)(w2 & 0xffffu));
-                vf[1] = f16_to_f32((uint16_t)(w2 >> 16));
-            } else {
-                vf[0] = f16_to_f32(sm.vt[tk * HD + lane]);
-                vf[1] = 0.f;
-            }
+                acc[j][e] *= alpha[j];
 #pragma unroll
-            for (int j = 0; j < GQ; ++j) {
-                const float pj = sm.sc[j][tk];
+        for (int t = 0; t < ATT_WK; ++t) {
+            float vf[DPL];
+            const uint32_t vw = cur_st.v[t];
+            vf[0] = f16_to_f32((uint16_t)(vw & 0xffffu));
+            if (DPL == 2)
+                vf[DPL - 1] = f16_to_f32((uint16_t)(vw >> 16));
+            if (own_here && t == slot) {
 #pragma unroll
                 for (int e = 0; e < DPL; ++e)
-                    acc[j][e] = fmaf(pj, vf[e], acc[j][e]);
+                    vf[e] = vnew[e];
             }
+            const bool tv = t < nvalid;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e)
+                vf[e] = tv ? vf[e] : 0.f;
+            float pt[GQ];
+#pragma unroll
+            for (int j = 0; j < GQ; ++j)
+                pt[j] = sm.p[w][t][j];
+#pragma unroll
+            for (int j = 0; j < GQ; ++j)
+#pragma unroll
+                for (int e = 0; e < DPL; ++e)
+                    acc[j][e] = fmaf(pt[j], vf[e], acc[j][e]);
         }
-        __syncthreads();
+        wave_lds_sync();   // the p table is rewritten by the next step
+        if (more)
+            cur_st = nxt;
     }
 
-    // ---- cross-wave reduction of the accumulators, partial write
+    // ---- merge the waves, write the workgroup's partial
 #pragma unroll
-    for (int j = 0; j < GQ; ++j)
+    for (int j = 0; j < GQ; ++j) {
+        if (lane == 0) {
+            sm.m[w][j] = m[j];
+            sm.l[w][j] = l[j];
+        }
 #pragma unroll
         for (int e = 0; e < DPL; ++e)
-            sm.red[wave][j][lane * DPL + e] = acc[j][e];
+            sm.acc[w][j][lane * DPL + e] = acc[j][e];
+    }
     __syncthreads();
     const size_t pstride = HD + 2;
     for (int i = tid; i < GQ * HD; i += ATT_NT) {
         const int j = i / HD, d = i % HD;
-        const float v = (sm.red[0][j][d] + sm.red[1][j][d]) + (sm.red[2][j][d] + sm.red[3][j][d]);
+        float M = sm.m[0][j];
+#pragma unroll
+        for (int u = 1; u < ATT_NW; ++u)
+            M = fmaxf(M, sm.m[u][j]);
+        float L = 0.f, A = 0.f;
+#pragma unroll
+        for (int u = 0; u < ATT_NW; ++u) {
+            const float mu = sm.m[u][j];
+            const float f = (mu == -INFINITY) ? 0.f : expf(mu - M);
+            L = fmaf(f, sm.l[u][j], L);
+            A = fmaf(f, sm.acc[u][j][d], A);
+        }
         float* pp = p.part + (((size_t)b * p.nq + h0 + j) * p.nsplit + s) * pstride;
-        pp[d] = v;
+        pp[d] = A;
         if (d == 0) {
-            pp[HD] = sm.m[j];
-            pp[HD + 1] = sm.l[j];
+            pp[HD] = M;
+            pp[HD + 1] = L;
         }
     }
+    QD_MARK(3);
 }
 
 constexpr int ATT_CNT = 512;   // combine threads per head
 
-QD_DEV float block_reduce_max512(float v, float* red)
-{
-    v = group_max<WAVE>(v);
-    if ((threadIdx.x & (WAVE - 1)) == 0)
-        red[threadIdx.x / WAVE] = v;
-    __syncthreads();
-    float r = red[0];
-#pragma unroll
-    for (int i = 1; i < ATT_CNT / WAVE; ++i)
-        r = fmaxf(r, red[i]);
-    __syncthreads();
-    return r;
-}
-
-QD_DEV float block_reduce_sum512(float v, float* red)
-{
-    v = group_sum<WAVE>(v);
-    if ((threadIdx.x & (WAVE - 1)) == 0)
-        red[threadIdx.x / WAVE] = v;
-    __syncthreads();
-    float r = 0.f;
-#pragma unroll
-    for (int i = 0; i < ATT_CNT / WAVE; ++i)
-        r += red[i];
-    __syncthreads();
-    return r;
-}
-
-// Merge the partials of one (sequence, head): grid (nq, B), 512 threads.  Only
-// the splits holding keys below kv_len were written; the others are skipped.
-// Round 1 loads every split's (m, l); round 2 the accumulators, split among
-// 512 / HD thread groups, each thread's loads issued together.
+// Merge the partials of one (sequence, head): grid (nq, B), 512 threads in
+// groups of HD; group sg takes splits sg, sg + SG, ...  Each round issues all
+// of its loads (acc, m, l of up to 16 splits) before using them; only splits
+// holding keys below kv_len count.  The groups' (max, numerator, denominator)
+// are merged through LDS in a fixed order.
 template <int HD>
 __global__ void __launch_bounds__(ATT_CNT) k_attn_combine(const float* __restrict__ part,
                                                           int nsplit_all, int chunk,
@@ -403,59 +447,74 @@ __global__ void __launch_bounds__(ATT_CNT) k_attn_combine(const float* __restric
                                                           int max_kv, int nq, float* __restrict__ out)
 {
     constexpr int SG = ATT_CNT / HD;
-    extern __shared__ float wsh[];          // [nsplit] weights
-    __shared__ float red[ATT_CNT / WAVE];
-    __shared__ float numsh[SG][HD];
+    constexpr int U = 16;
+    __shared__ float gm[SG][HD], gn[SG][HD], gd[SG][HD];
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int d = tid % HD, sg = tid / HD;
     const size_t pstride = HD + 2;
     const float* pp = part + ((size_t)b * nq + h) * nsplit_all * pstride;
-    int kv_len = kv_lens ? kv_lens[b] : (*pos + 1);
-    kv_len = max(0, min(kv_len, max_kv));
-    const int nsplit = min(nsplit_all, (kv_len + chunk - 1) / chunk);
-    float mloc = -INFINITY;
-    for (int s = tid; s < nsplit; s += ATT_CNT) {
-        const float m = pp[s * pstride + HD];
-        wsh[s] = m;
-        mloc = fmaxf(mloc, m);
-    }
-    const float M = block_reduce_max512(mloc, red);
-    float dloc = 0.f;
-    for (int s = tid; s < nsplit; s += ATT_CNT) {
-        const float m = wsh[s];
-        const float e = (m == -INFINITY || M == -INFINITY) ? 0.f : expf(m - M);
-        wsh[s] = e;
-        dloc = fmaf(e, pp[s * pstride + HD + 1], dloc);
-    }
-    const float den = block_reduce_sum512(dloc, red);   // its barriers publish wsh
-    const int d = tid % HD, sg = tid / HD;
-    float num = 0.f;
-    for (int s0 = sg; s0 < nsplit; s0 += 16 * SG) {
-        float a[16];
+    QD_MARK(0);
+    float mt = -INFINITY, num = 0.f, den = 0.f;
+    int nact = -1;
+    for (int s0 = sg; s0 < nsplit_all; s0 += U * SG) {
+        float a[U], mm[U], ll[U];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int s = s0 + u * SG;
-            a[u] = (s < nsplit) ? pp[s * pstride + d] : 0.f;
+        for (int u = 0; u < U; ++u) {
+            const size_t sp = (size_t)min(s0 + u * SG, nsplit_all - 1) * pstride;   // never a branch
+            a[u] = pp[sp + d];
+            mm[u] = pp[sp + HD];
+            ll[u] = pp[sp + HD + 1];
         }
+        if (nact < 0) {
+            int kv_len = kv_lens ? kv_lens[b] : (*pos + 1);
+            kv_len = max(0, min(kv_len, max_kv));
+            nact = min(nsplit_all, (kv_len + chunk - 1) / chunk);
+            QD_MARK(1);
+        }
+        float rm = mt;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int s = s0 + u * SG;
-            if (s < nsplit)
-                num = fmaf(wsh[s], a[u], num);
+        for (int u = 0; u < U; ++u)
+            if (s0 + u * SG < nact)
+                rm = fmaxf(rm, mm[u]);
+        if (rm == -INFINITY)
+            continue;
+        const float sc = (mt == -INFINITY) ? 0.f : expf(mt - rm);
+        num *= sc;
+        den *= sc;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (s0 + u * SG < nact) {
+                const float f = expf(mm[u] - rm);
+                num = fmaf(f, a[u], num);
+                den = fmaf(f, ll[u], den);
+            }
         }
+        mt = rm;
     }
-    numsh[sg][d] = num;
+    gm[sg][d] = mt;
+    gn[sg][d] = num;
+    gd[sg][d] = den;
     __syncthreads();
+    QD_MARK(2);
     if (sg == 0) {
-        float t = numsh[0][d];
+        float M = gm[0][d];
 #pragma unroll
         for (int k = 1; k < SG; ++k)
-            t += numsh[k][d];
-        out[((size_t)b * nq + h) * HD + d] = (den > 0.f) ? t / den : 0.f;
+            M = fmaxf(M, gm[k][d]);
+        float N = 0.f, D = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int k = 0; k < SG; ++k) {
+                const float f = (gm[k][d] == -INFINITY) ? 0.f : expf(gm[k][d] - M);
+                N = fmaf(f, gn[k][d], N);
+                D = fmaf(f, gd[k][d], D);
+            }
+        }
+        out[((size_t)b * nq + h) * HD + d] = (D > 0.f) ? N / D : 0.f;
     }
+    QD_MARK(3);
 }
 
-// Split policy of the standalone entry: about 4 workgroups per CU over all
-// (sequence, kv head) pairs, at least one 64-key tile per split.
 inline void attn_split(int B, int nkv, int max_kv, int* chunk, int* nsplit)
 {
     const int tiles = max(1, (max_kv + ATT_T - 1) / ATT_T);

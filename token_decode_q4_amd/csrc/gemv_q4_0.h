@@ -50,14 +50,19 @@ struct XStage {
     float4 v[MAXU];
 };
 
+// Loads are never under a branch (an index past the end is clamped and its
+// value discarded): a load inside a divergent block makes the compiler wait
+// for every earlier load at the join, which serialises the whole batch.
 template <int NT>
 QD_DEV void stage_x_load(const float* __restrict__ x, int nb, XStage<NT>& st)
 {
     const int n4 = nb * 8;
 #pragma unroll
     for (int u = 0; u < XStage<NT>::MAXU; ++u) {
-        const int i = (int)threadIdx.x + u * NT;
-        st.v[u] = (i < n4) ? reinterpret_cast<const float4*>(x)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (u * NT < n4) {   // uniform
+            const int i = (int)threadIdx.x + u * NT;
+            st.v[u] = reinterpret_cast<const float4*>(x)[min(i, n4 - 1)];
+        }
     }
 }
 
@@ -158,6 +163,7 @@ QD_DEV void gemv_run(const uint16_t* __restrict__ D, const uint8_t* __restrict__
     const int ngroups = (nb + LPR * BG - 1) / (LPR * BG);
     const int my_tiles = (int)blockIdx.x < ntiles ? (ntiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
     const int nitems = my_tiles * ngroups;
+    QD_MARK(0);
 
     // issue the loads of item i (clamped: an item past the end reloads the last one)
     auto load = [&](GemvBuf<RPS, BG>& bf, int i) {
@@ -259,6 +265,7 @@ QD_DEV void gemv_run(const uint16_t* __restrict__ D, const uint8_t* __restrict__
     stage_x_load<G::NT>(x, nb, xst);
     stage_x_store<G::NT>(nb, xst, xl, xs);   // ends with a barrier
     epi.finish();
+    QD_MARK(1);
     for (int i = 0; i < nitems; i += NBUF) {
 #pragma unroll
         for (int j = 0; j < NBUF; ++j) {
@@ -271,6 +278,7 @@ QD_DEV void gemv_run(const uint16_t* __restrict__ D, const uint8_t* __restrict__
             }
         }
     }
+    QD_MARK(2);
 }
 
 // 1 / sqrt(mean(x^2) + eps) from the per-workgroup partial sums of x^2 written
@@ -287,10 +295,8 @@ struct RmsPartials {
     {
         const int lane = threadIdx.x & (WAVE - 1);
 #pragma unroll
-        for (int u = 0; u < RMS_U; ++u) {
-            const int i = lane + u * WAVE;
-            v[u] = (i < n_part) ? ss_part[i] : 0.f;
-        }
+        for (int u = 0; u < RMS_U; ++u)
+            v[u] = ss_part[min(lane + u * WAVE, n_part - 1)];   // n_part >= 1
     }
     QD_DEV float finish(int n, float eps) const
     {
@@ -298,7 +304,7 @@ struct RmsPartials {
         float s = 0.f;
 #pragma unroll
         for (int u = 0; u < RMS_U; ++u)
-            s += v[u];
+            s += (lane + u * WAVE < n_part) ? v[u] : 0.f;
         for (int i = lane + RMS_U * WAVE; i < n_part; i += WAVE)
             s += ss_part[i];
         s = group_sum<WAVE>(s);

@@ -140,7 +140,9 @@ struct qd_model {
     std::vector<DevLayer> layers;
     DevQ4 embed, lm;
     float* final_norm = nullptr;
-    float *rope_cos = nullptr, *rope_sin = nullptr;
+    float *rope_cos = nullptr, *rope_sin = nullptr;   // [max_seq][rot/2]
+    float* rope_cur = nullptr;                        // cos, sin at the step's position
+    float* ones_hd = nullptr;                         // [head_dim] of 1 (no q/k norm)
     int32_t* table = nullptr;
     // step buffers
     float *x = nullptr, *u = nullptr, *ss_part = nullptr, *qkv_raw = nullptr;
@@ -347,8 +349,10 @@ static void launch_attention(const AttnParams& p, int hd, int gq, bool paged, in
                              hipStream_t s)
 {
     const dim3 grid(p.nsplit, p.nkv, B);
+    // with max_kv == 0 every kv_len is 0: no split runs and the combine writes zeros
 #define QD_ATT(HD_, GQ_)                                                                          \
-    if (paged)                                                                                    \
+    if (p.max_kv <= 0) {                                                                          \
+    } else if (paged)                                                                             \
         hipLaunchKernelGGL((k_attn_split<HD_, GQ_, true, QMODE>), grid, dim3(ATT_NT), 0, s, p);   \
     else                                                                                          \
         hipLaunchKernelGGL((k_attn_split<HD_, GQ_, false, QMODE>), grid, dim3(ATT_NT), 0, s, p);
@@ -360,12 +364,11 @@ static void launch_attention(const AttnParams& p, int hd, int gq, bool paged, in
         else if (gq == 4) { QD_ATT(64, 4) } else { QD_ATT(64, 8) }
     }
 #undef QD_ATT
-    const size_t lds = sizeof(float) * (size_t)p.nsplit;
     if (hd == 128)
-        hipLaunchKernelGGL((k_attn_combine<128>), dim3(nq, B), dim3(ATT_CNT), lds, s, p.part,
+        hipLaunchKernelGGL((k_attn_combine<128>), dim3(nq, B), dim3(ATT_CNT), 0, s, p.part,
                            p.nsplit, p.chunk, p.kv_lens, p.pos, p.max_kv, nq, p.out);
     else
-        hipLaunchKernelGGL((k_attn_combine<64>), dim3(nq, B), dim3(ATT_CNT), lds, s, p.part,
+        hipLaunchKernelGGL((k_attn_combine<64>), dim3(nq, B), dim3(ATT_CNT), 0, s, p.part,
                            p.nsplit, p.chunk, p.kv_lens, p.pos, p.max_kv, nq, p.out);
 }
 
@@ -375,7 +378,7 @@ static int enqueue_step(qd_model* m, hipStream_t s)
     const int H = m->H;
     hipLaunchKernelGGL(k_embed, dim3(m->grid_embed), dim3(256), 0, s, m->embed.d, m->embed.qs, H,
                        m->V, m->st, m->ids, m->max_seq, m->layers[0].attn_norm, m->x, m->u,
-                       m->ss_part);
+                       m->ss_part, m->rope_cos, m->rope_sin, m->rot / 2, m->rope_cur);
     int n_part = m->grid_embed;
     for (int l = 0; l < m->L; ++l) {
         DevLayer& Ly = m->layers[l];
@@ -402,12 +405,12 @@ static int enqueue_step(qd_model* m, hipStream_t s)
             p.nsplit = m->attn_nsplit;
             p.part = m->attn_part;
             p.out = m->attn;
-            p.q_norm = m->qk_norm ? Ly.q_norm : nullptr;
-            p.k_norm = m->qk_norm ? Ly.k_norm : nullptr;
+            p.qk_norm = m->qk_norm;
+            p.q_norm = m->qk_norm ? Ly.q_norm : m->ones_hd;   // read either way
+            p.k_norm = m->qk_norm ? Ly.k_norm : m->ones_hd;
             p.eps = m->eps;
             p.rot = m->rot;
-            p.rope_cos = m->rope_cos;
-            p.rope_sin = m->rope_sin;
+            p.rope_cur = m->rope_cur;
             p.kc = Ly.kc;
             p.vc = Ly.vc;
             launch_attention<1>(p, m->hd, m->nq / m->nkv, m->paged, 1, m->nq, s);
@@ -540,6 +543,9 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
             }
         if ((rc = upload_f32(m, &m->rope_cos, hc.data(), n, s))) return bail(rc);
         if ((rc = upload_f32(m, &m->rope_sin, hs.data(), n, s))) return bail(rc);
+        if ((rc = dev_alloc_t(m, &m->rope_cur, (size_t)2 * (half > 0 ? half : 1)))) return bail(rc);
+        const std::vector<float> ones((size_t)m->hd, 1.f);
+        if ((rc = upload_f32(m, &m->ones_hd, ones.data(), (size_t)m->hd, s))) return bail(rc);
     }
 
     // KV cache

@@ -55,12 +55,15 @@ QD_DEV float block_sum256(float v, float* red /* >= 4 floats */)
 
 // ----------------------------------------------------------------- embedding
 
-// grid ceil(H/256): one element per thread; per-workgroup sum of x^2
+// grid ceil(H/256): one element per thread; per-workgroup sum of x^2.
+// Workgroup 0 also copies the rotary factors of the step's position from the
+// tables [max_seq][half] to rope_cur (cos [half] then sin [half]).
 __global__ void __launch_bounds__(256)
 k_embed(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, int H, int vocab,
         StepState* __restrict__ st, const int32_t* __restrict__ ids, int max_seq,
         const float* __restrict__ w_norm, float* __restrict__ x, float* __restrict__ u,
-        float* __restrict__ ss_part)
+        float* __restrict__ ss_part, const float* __restrict__ rope_cos,
+        const float* __restrict__ rope_sin, int half, float* __restrict__ rope_cur)
 {
     __shared__ float red[8];
     int pos = st->pos;
@@ -72,6 +75,12 @@ k_embed(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, int H, 
     if (tok < 0 || tok >= vocab) {
         if (threadIdx.x == 0 && blockIdx.x == 0) st->error |= 1;
         tok = 0;
+    }
+    if (blockIdx.x == 0) {
+        for (int k = threadIdx.x; k < half; k += blockDim.x) {
+            rope_cur[k] = rope_cos[(size_t)pos * half + k];
+            rope_cur[half + k] = rope_sin[(size_t)pos * half + k];
+        }
     }
     const int nb = H / 32;
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -211,6 +220,7 @@ k_gemv_scaled(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
     extern __shared__ float smem[];
     EpiScaled e{y, N, {ss_part, n_part}, n_in, eps_in};
     gemv_run<LPR, RPS, NWAVES, BG, NBUF, NTL, false>(D, Q, u, N, nb, smem, smem + nb * XPAD, e);
+    QD_MARK(3);
 }
 
 template <int LPR, int RPS, int NWAVES, int BG, int NBUF, bool NTL>
@@ -227,6 +237,7 @@ k_gemv_residual(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
     const float ss = block_sum256(e.ss, red);
     if (threadIdx.x == 0)
         ss_part[blockIdx.x] = ss;
+    QD_MARK(3);
 }
 
 template <int LPR, int RPS, int NWAVES, int BG, int NBUF, bool NTL>
@@ -238,6 +249,7 @@ k_gemv_swiglu(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
     extern __shared__ float smem[];
     EpiSwiglu e{act, N, {ss_part, n_part}, n_in, eps_in};
     gemv_run<LPR, RPS, NWAVES, BG, NBUF, NTL, false>(D, Q, u, N, nb, smem, smem + nb * XPAD, e);
+    QD_MARK(3);
 }
 
 // logits = W u / rms; each workgroup's best (value, lowest index among equals)
@@ -301,8 +313,13 @@ k_argmax_advance(const float* __restrict__ part_val, const int32_t* __restrict__
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i = i0 + (int)threadIdx.x + u * 256;
-            v[u] = (i < n_part) ? part_val[i] : -INFINITY;
-            ix[u] = (i < n_part) ? part_idx[i] : 0x7fffffff;
+            const int ic = min(i, n_part - 1);   // loads never under a branch
+            v[u] = part_val[ic];
+            ix[u] = part_idx[ic];
+            if (i >= n_part) {
+                v[u] = -INFINITY;
+                ix[u] = 0x7fffffff;
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
