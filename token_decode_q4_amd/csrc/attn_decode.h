@@ -47,7 +47,7 @@ struct AttnParams {
     int max_kv;                // contiguous capacity per (b, g); bound on kv_len
     int nq, nkv;
     float scale;
-    int chunk;                 // keys per split, a multiple of ATT_T
+    int chunk;                 // keys per split, a multiple of 16 * waves per workgroup
     int nsplit;
     float* part;               // [B][nq][nsplit][HD + 2]
     float* out;                // [B][nq][HD] (combine)
@@ -63,19 +63,24 @@ struct AttnParams {
 };
 
 constexpr int ATT_WK = 16;                 // keys per wave step (one paged block)
-constexpr int ATT_NW = 4;                  // waves per workgroup
-constexpr int ATT_T = ATT_WK * ATT_NW;     // keys per workgroup step
 constexpr int ATT_BS = 16;                 // paged block size
-constexpr int ATT_NT = ATT_NW * WAVE;      // threads per workgroup
+
+// Waves per workgroup: a launch parameter (blockDim.x / 64) up to ATT_MAXW;
+// the host sizes the grid so that it fits the chip in one round.
+template <int GQ>
+struct AttnMaxWaves {
+    static constexpr int value = GQ <= 4 ? 8 : 4;   // keeps the LDS below 64 KB
+};
 
 template <int HD, int GQ>
 struct alignas(16) AttnSmem {
-    float q[ATT_NW][GQ][HD];        // per wave: queries ready for QK (times scale)
-    float krow[ATT_NW][HD];         // per wave: the token's k during its rotary
-    float p[ATT_NW][ATT_WK][GQ];    // per wave: probabilities of the step, [key][head]
-    uint16_t knew[ATT_NW][HD];      // per wave: the token's k in f16
-    float m[ATT_NW][GQ], l[ATT_NW][GQ];
-    float acc[ATT_NW][GQ][HD];
+    static constexpr int W = AttnMaxWaves<GQ>::value;
+    float q[W][GQ][HD];             // per wave: queries ready for QK (times scale)
+    float krow[W][HD];              // per wave: the token's k during its rotary
+    float p[W][ATT_WK][GQ];         // per wave: probabilities of the step, [key][head]
+    uint16_t knew[W][HD];           // per wave: the token's k in f16
+    float m[W][GQ], l[W][GQ];
+    float acc[W][GQ][HD];
 };
 
 // LDS writes of this wave are seen by its later LDS reads (no workgroup barrier)
@@ -105,7 +110,7 @@ struct AttnStep {
 
 // QMODE 0: q given (standalone); QMODE 1: decode-step prologue from raw q|k|v
 template <int HD, int GQ, bool PAGED, int QMODE>
-__global__ void __launch_bounds__(ATT_NT) k_attn_split(AttnParams p)
+__global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(AttnParams p)
 {
     static_assert(HD == 64 || HD == 128, "head_dim");
     static_assert(GQ == 1 || GQ == 2 || GQ == 4 || GQ == 8, "group");
@@ -115,6 +120,8 @@ __global__ void __launch_bounds__(ATT_NT) k_attn_split(AttnParams p)
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+    const int nw = blockDim.x / WAVE;          // waves of this launch
+    const int wstride = nw * ATT_WK;           // keys between a wave's steps
     const int kk = lane >> 2, cq = lane & 3;   // QK layout: key, quarter
     const int h0 = g * GQ;
     const int t_begin = s * p.chunk;
@@ -195,7 +202,7 @@ __global__ void __launch_bounds__(ATT_NT) k_attn_split(AttnParams p)
     // the owner: the wave whose step own_tw holds tcur, at row slot of it
     float vnew[DPL];
     const int rel = tcur - t_begin;
-    const bool owner = QMODE == 1 && tcur >= t_begin && tcur < t_end && (rel / ATT_WK) % ATT_NW == w;
+    const bool owner = QMODE == 1 && tcur >= t_begin && tcur < t_end && (rel / ATT_WK) % nw == w;
     const int own_tw = t_begin + (rel / ATT_WK) * ATT_WK;
     const int slot = tcur - own_tw;
     if (QMODE == 1) {
@@ -294,11 +301,11 @@ __global__ void __launch_bounds__(ATT_NT) k_attn_split(AttnParams p)
         for (int e = 0; e < DPL; ++e)
             acc[j][e] = 0.f;
     }
-    for (int tw = tw0; tw < t_end; tw += ATT_T) {
+    for (int tw = tw0; tw < t_end; tw += wstride) {
         Step nxt;
-        const bool more = tw + ATT_T < t_end;
+        const bool more = tw + wstride < t_end;
         if (more)
-            load_step(nxt, tw + ATT_T);
+            load_step(nxt, tw + wstride);
         const int nvalid = min(ATT_WK, t_end - tw);
         const bool own_here = owner && tw == own_tw;
         // QK: 8 dims x NI slices of key kk
@@ -322,6 +329,7 @@ __global__ void __launch_bounds__(ATT_NT) k_attn_split(AttnParams p)
             }
         }
         const bool kvalid = kk < nvalid;
+        QD_MARK(4);
         float sc[GQ];
 #pragma unroll
         for (int j = 0; j < GQ; ++j) {
@@ -342,6 +350,7 @@ __global__ void __launch_bounds__(ATT_NT) k_attn_split(AttnParams p)
             d = group_sum<4>(d);   // the 4 quarters of key kk
             sc[j] = kvalid ? d : -INFINITY;
         }
+        QD_MARK(5);
         // online softmax over the step's keys: the 4 lanes of a key hold the
         // same score, so the max runs over the whole wave and the sum over
         // the quarter-0 lanes (the others add zeros)
@@ -358,6 +367,7 @@ __global__ void __launch_bounds__(ATT_NT) k_attn_split(AttnParams p)
                 sm.p[w][kk][j] = pr;
         }
         wave_lds_sync();
+        QD_MARK(6);
         // PV: lane owns dims lane*DPL ..
 #pragma unroll
         for (int j = 0; j < GQ; ++j)
@@ -406,17 +416,16 @@ __global__ void __launch_bounds__(ATT_NT) k_attn_split(AttnParams p)
         for (int e = 0; e < DPL; ++e)
             sm.acc[w][j][lane * DPL + e] = acc[j][e];
     }
+    QD_MARK(7);
     __syncthreads();
     const size_t pstride = HD + 2;
-    for (int i = tid; i < GQ * HD; i += ATT_NT) {
+    for (int i = tid; i < GQ * HD; i += nw * WAVE) {
         const int j = i / HD, d = i % HD;
         float M = sm.m[0][j];
-#pragma unroll
-        for (int u = 1; u < ATT_NW; ++u)
+        for (int u = 1; u < nw; ++u)
             M = fmaxf(M, sm.m[u][j]);
         float L = 0.f, A = 0.f;
-#pragma unroll
-        for (int u = 0; u < ATT_NW; ++u) {
+        for (int u = 0; u < nw; ++u) {
             const float mu = sm.m[u][j];
             const float f = (mu == -INFINITY) ? 0.f : expf(mu - M);
             L = fmaf(f, sm.l[u][j], L);
@@ -515,15 +524,32 @@ __global__ void __launch_bounds__(ATT_CNT) k_attn_combine(const float* __restric
     QD_MARK(3);
 }
 
-inline void attn_split(int B, int nkv, int max_kv, int* chunk, int* nsplit)
+// Split policy.  Waves per workgroup and keys per split for a grid of
+// (nsplit, nkv, B): each wave step is 16 keys, a split is `waves` x 16 keys x
+// steps.  The model path aims at one workgroup per CU (256 CUs): a second
+// workgroup on a CU delays both.  The standalone path aims at about 1024
+// workgroups of 4 waves, several 16-key steps each at long contexts.
+struct AttnGeom {
+    int waves, chunk, nsplit;
+};
+inline AttnGeom attn_geom(int B, int nkv, int max_kv, int target_wgs, int max_waves, int fixed_waves)
 {
-    const int tiles = max(1, (max_kv + ATT_T - 1) / ATT_T);
-    int want = (1024 + B * nkv - 1) / (B * nkv);
-    if (want < 1) want = 1;
-    if (want > tiles) want = tiles;
-    const int tiles_per = (tiles + want - 1) / want;
-    *chunk = tiles_per * ATT_T;
-    *nsplit = (max(1, max_kv) + *chunk - 1) / *chunk;
+    AttnGeom a;
+    const int steps16 = max(1, (max_kv + ATT_WK - 1) / ATT_WK);   // 16-key steps in max_kv
+    int want = target_wgs / max(1, B * nkv);                         // splits per (b, g)
+    want = max(1, min(want, steps16));
+    const int per = (steps16 + want - 1) / want;                     // 16-key steps per split
+    if (fixed_waves > 0) {
+        a.waves = fixed_waves;
+        const int st = (per + fixed_waves - 1) / fixed_waves;        // steps per wave
+        a.chunk = st * fixed_waves * ATT_WK;
+    } else {
+        a.waves = min(per, max_waves);
+        const int st = (per + a.waves - 1) / a.waves;
+        a.chunk = st * a.waves * ATT_WK;
+    }
+    a.nsplit = (max(1, max_kv) + a.chunk - 1) / a.chunk;
+    return a;
 }
 
 }  // namespace qd

@@ -12,7 +12,7 @@
 // consecutive blocks of a row, so a wave reads LPR*16 contiguous bytes per
 // row.  The grid is persistent: a workgroup walks its tiles in (tile, block
 // group) work items, keeping NBUF-1 items of loads in flight ahead of the one
-// it consumes, and the first items' loads are issued before x is staged.
+// it consumes; x is loaded first, then the first items, then x is staged.
 //
 // x is staged once per workgroup into LDS, block b at float offset b*36 (the
 // 4-float pad keeps the per-lane 128-bit reads of 64 lanes on distinct banks):
@@ -143,7 +143,8 @@ struct GemvBuf {
 // strided by gridDim.x.  NBUF register buffers rotate: the loads of item
 // i + NBUF - 1 are issued before item i is consumed.  `epi` receives every
 // finished tile:
-//   epi.issue()                 first of all: the epilogue's own loads
+//   epi.issue(row0)             first of all: the epilogue's own loads (row0 =
+//                               this lane's first row of its first tile)
 //   epi.finish()                after x is staged: what needs those loads
 //   epi.tile(row0, acc, lead)   acc[RPS] = dot products of rows row0 .. row0+RPS-1
 // Scales come either in the canonical layout d[row][block] (TS = false) or
@@ -167,7 +168,7 @@ QD_DEV void gemv_run(const uint16_t* __restrict__ D, const uint8_t* __restrict__
 
     // issue the loads of item i (clamped: an item past the end reloads the last one)
     auto load = [&](GemvBuf<RPS, BG>& bf, int i) {
-        i = min(i, nitems - 1);
+        i = max(0, min(i, nitems - 1));   // rows and blocks below are clamped too
         const int tile = (int)blockIdx.x + (i / ngroups) * (int)gridDim.x;
         const int grp = i % ngroups;
         const int row0 = tile * G::ROWS + wave * G::RPW + slot * RPS;
@@ -254,15 +255,15 @@ QD_DEV void gemv_run(const uint16_t* __restrict__ D, const uint8_t* __restrict__
         }
     };
 
-    epi.issue();
-    GemvBuf<RPS, BG> bufs[NBUF];
-    if (nitems > 0) {
-#pragma unroll
-        for (int j = 0; j + 1 < NBUF; ++j)
-            load(bufs[j], j);
-    }
+    // x (and the epilogue's inputs) first: loads return in order, so x can be
+    // staged while the weight items behind it are still arriving
+    epi.issue((int)blockIdx.x * G::ROWS + wave * G::RPW + slot * RPS);
     XStage<G::NT> xst;
     stage_x_load<G::NT>(x, nb, xst);
+    GemvBuf<RPS, BG> bufs[NBUF];
+#pragma unroll
+    for (int j = 0; j + 1 < NBUF; ++j)
+        load(bufs[j], j);
     stage_x_store<G::NT>(nb, xst, xl, xs);   // ends with a barrier
     epi.finish();
     QD_MARK(1);
@@ -318,7 +319,7 @@ struct RmsPartials {
 struct EpiStore {
     float* y;
     int N;
-    QD_DEV void issue() {}
+    QD_DEV void issue(int) {}
     QD_DEV void finish() {}
     template <int RPS>
     QD_DEV void tile(int row0, const float (&acc)[RPS], bool lead)

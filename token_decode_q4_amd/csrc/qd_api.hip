@@ -48,17 +48,25 @@ extern "C" const char* qd_last_error(void) { return g_err.c_str(); }
 
 // ------------------------------------------------------------------ GEMV launch
 
-// GEMV launch configurations (rows per slot, waves, block groups per item,
-// register buffers, non-temporal weight loads), chosen per call site by
-// timing the sweep shapes on MI355X; the lanes-per-row count follows K.
+// GEMV launch configurations: rows per slot, waves, block groups per item,
+// register buffers, non-temporal weight loads (the template arguments), and a
+// cap on the grid.  Chosen per call site by timing the step's shapes on
+// MI355X over rotated weight copies; the lanes-per-row count follows K.
 struct GemvCfg {
     int rps, nw, bg, nbuf, ntl, grid_cap;
 };
-static constexpr GemvCfg CFG_SMALL = {2, 8, 2, 3, 0, 1 << 30};   // N ~ 4096 (o, down)
-static constexpr GemvCfg CFG_QKV = {4, 8, 1, 2, 0, 1 << 30};     // q|k|v
-static constexpr GemvCfg CFG_WIDE = {4, 4, 1, 2, 0, 1024};       // gate|up
-static constexpr GemvCfg CFG_HEAD = {4, 4, 1, 2, 1, 2048};       // LM head
+#define QD_CFG_O 2, 8, 1, 2, false      // o-proj, N ~ hidden
+#define QD_CFG_DOWN 2, 8, 2, 2, false   // down, long rows
+#define QD_CFG_QKV 3, 8, 1, 2, false    // q|k|v
+#define QD_CFG_GU 4, 4, 1, 2, false     // gate|up
+#define QD_CFG_HEAD 4, 4, 1, 2, true    // LM head (streamed once)
+static constexpr GemvCfg CFG_O = {QD_CFG_O, 1 << 30};
+static constexpr GemvCfg CFG_DOWN = {QD_CFG_DOWN, 1 << 30};
+static constexpr GemvCfg CFG_QKV = {QD_CFG_QKV, 1 << 30};
+static constexpr GemvCfg CFG_GU = {QD_CFG_GU, 768};
+static constexpr GemvCfg CFG_HEAD = {QD_CFG_HEAD, 2048};
 static constexpr int GEMV_MAX_LDS = 64 * 1024;
+static constexpr int ATT_MODEL_WGS = 160;   // attention workgroups of a decode step (measured best)
 
 // lanes per row: the largest of 64/32/16/8 dividing the number of blocks
 static int pick_lpr(int nb)
@@ -80,27 +88,13 @@ static int gemv_grid(const GemvCfg& c, int lpr, int N)
     return g > 0 ? g : 1;
 }
 
-// Launch kernel template KT<LPR, RPS, NW, BG, NBUF, NTL> for configuration C.
-#define QD_GEMV_LAUNCH(KT, C, lpr, grid, lds, s, ...)                                              \
-    do {                                                                                           \
-        const GemvCfg& c_ = (C);                                                                   \
-        const int l_ = (lpr);                                                                      \
-        if (c_.rps == 2 && c_.nw == 8 && c_.bg == 2 && c_.nbuf == 3 && !c_.ntl) {                  \
-            QD_GEMV_LPR(KT, l_, (2, 8, 2, 3, false), grid, lds, s, __VA_ARGS__);                   \
-        } else if (c_.rps == 4 && c_.nw == 8 && c_.bg == 1 && c_.nbuf == 2 && !c_.ntl) {           \
-            QD_GEMV_LPR(KT, l_, (4, 8, 1, 2, false), grid, lds, s, __VA_ARGS__);                   \
-        } else if (c_.rps == 4 && c_.nw == 4 && c_.bg == 1 && c_.nbuf == 2 && c_.ntl) {            \
-            QD_GEMV_LPR(KT, l_, (4, 4, 1, 2, true), grid, lds, s, __VA_ARGS__);                    \
-        } else {                                                                                   \
-            QD_GEMV_LPR(KT, l_, (4, 4, 1, 2, false), grid, lds, s, __VA_ARGS__);                   \
-        }                                                                                          \
-    } while (0)
+// Launch kernel template KT<LPR, P...> with P = (RPS, NW, BG, NBUF, NTL).
 #define QD_UNPACK(...) __VA_ARGS__
-#define QD_GEMV_ONE(KT, L, P, grid, lds, s, ...) \
-    hipLaunchKernelGGL((KT<L, QD_UNPACK P>), dim3(grid), dim3(QD_NW P * WAVE), lds, s, __VA_ARGS__)
 #define QD_NW_(a, b, c, d, e) b
 #define QD_NW(...) QD_NW_(__VA_ARGS__)
-#define QD_GEMV_LPR(KT, l, P, grid, lds, s, ...)                                                   \
+#define QD_GEMV_ONE(KT, L, P, grid, lds, s, ...) \
+    hipLaunchKernelGGL((KT<L, QD_UNPACK P>), dim3(grid), dim3(QD_NW P * WAVE), lds, s, __VA_ARGS__)
+#define QD_GEMV(KT, P, l, grid, lds, s, ...)                                                      \
     switch (l) {                                                                                   \
     case 64: QD_GEMV_ONE(KT, 64, P, grid, lds, s, __VA_ARGS__); break;                              \
     case 32: QD_GEMV_ONE(KT, 32, P, grid, lds, s, __VA_ARGS__); break;                              \
@@ -108,15 +102,18 @@ static int gemv_grid(const GemvCfg& c, int lpr, int N)
     default: QD_GEMV_ONE(KT, 8, P, grid, lds, s, __VA_ARGS__); break;                               \
     }
 
-static const GemvCfg& plain_cfg(int N) { return N <= 8192 ? CFG_SMALL : (N <= 65536 ? CFG_WIDE : CFG_HEAD); }
-
 static hipError_t launch_gemv_plain(const uint16_t* d, const uint8_t* q, const float* x, float* y,
                                     int N, int K, hipStream_t s)
 {
     const int nb = K / 32, lpr = pick_lpr(nb);
-    const GemvCfg& c = plain_cfg(N);
-    const int grid = gemv_grid(c, lpr, N);
-    QD_GEMV_LAUNCH(k_gemv_plain, c, lpr, grid, gemv_lds_bytes(nb), s, d, q, x, y, N, nb);
+    const size_t lds = gemv_lds_bytes(nb);
+    if (N <= 8192) {
+        QD_GEMV(k_gemv_plain, (QD_CFG_O), lpr, gemv_grid(CFG_O, lpr, N), lds, s, d, q, x, y, N, nb);
+    } else if (N <= 65536) {
+        QD_GEMV(k_gemv_plain, (QD_CFG_GU), lpr, gemv_grid(CFG_GU, lpr, N), lds, s, d, q, x, y, N, nb);
+    } else {
+        QD_GEMV(k_gemv_plain, (QD_CFG_HEAD), lpr, gemv_grid(CFG_HEAD, lpr, N), lds, s, d, q, x, y, N, nb);
+    }
     return hipGetLastError();
 }
 
@@ -149,7 +146,7 @@ struct qd_model {
     float *attn = nullptr, *act = nullptr, *logits = nullptr, *arg_val = nullptr;
     int32_t* arg_idx = nullptr;
     float* attn_part = nullptr;
-    int attn_chunk = 0, attn_nsplit = 0;
+    int attn_waves = 0, attn_chunk = 0, attn_nsplit = 0;
     StepState* st = nullptr;
     int32_t *ids = nullptr, *pred = nullptr;
     // launch geometry
@@ -345,17 +342,17 @@ static int validate_config(const qd_config* c, const qd_weights* w)
 
 // Launch the split-KV attention (split + combine).
 template <int QMODE>
-static void launch_attention(const AttnParams& p, int hd, int gq, bool paged, int B, int nq,
-                             hipStream_t s)
+static void launch_attention(const AttnParams& p, int waves, int hd, int gq, bool paged, int B,
+                             int nq, hipStream_t s)
 {
-    const dim3 grid(p.nsplit, p.nkv, B);
+    const dim3 grid(p.nsplit, p.nkv, B), block(waves * WAVE);
     // with max_kv == 0 every kv_len is 0: no split runs and the combine writes zeros
 #define QD_ATT(HD_, GQ_)                                                                          \
     if (p.max_kv <= 0) {                                                                          \
     } else if (paged)                                                                             \
-        hipLaunchKernelGGL((k_attn_split<HD_, GQ_, true, QMODE>), grid, dim3(ATT_NT), 0, s, p);   \
+        hipLaunchKernelGGL((k_attn_split<HD_, GQ_, true, QMODE>), grid, block, 0, s, p);          \
     else                                                                                          \
-        hipLaunchKernelGGL((k_attn_split<HD_, GQ_, false, QMODE>), grid, dim3(ATT_NT), 0, s, p);
+        hipLaunchKernelGGL((k_attn_split<HD_, GQ_, false, QMODE>), grid, block, 0, s, p);
     if (hd == 128) {
         if (gq == 1) { QD_ATT(128, 1) } else if (gq == 2) { QD_ATT(128, 2) }
         else if (gq == 4) { QD_ATT(128, 4) } else { QD_ATT(128, 8) }
@@ -383,7 +380,7 @@ static int enqueue_step(qd_model* m, hipStream_t s)
     for (int l = 0; l < m->L; ++l) {
         DevLayer& Ly = m->layers[l];
         // q | k | v (raw, before the per-head norm and rotary)
-        QD_GEMV_LAUNCH(k_gemv_scaled, CFG_QKV, m->lpr_qkv, m->grid_qkv, gemv_lds_bytes(Ly.qkv.nb), s,
+        QD_GEMV(k_gemv_scaled, (QD_CFG_QKV), m->lpr_qkv, m->grid_qkv, gemv_lds_bytes(Ly.qkv.nb), s,
                        Ly.qkv.d, Ly.qkv.qs, m->u, Ly.qkv.rows, Ly.qkv.nb, m->ss_part, n_part, H,
                        m->eps, m->qkv_raw);
         // per-head norm + rotary, K/V write, split-KV attention, combine
@@ -413,25 +410,25 @@ static int enqueue_step(qd_model* m, hipStream_t s)
             p.rope_cur = m->rope_cur;
             p.kc = Ly.kc;
             p.vc = Ly.vc;
-            launch_attention<1>(p, m->hd, m->nq / m->nkv, m->paged, 1, m->nq, s);
+            launch_attention<1>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, 1, m->nq, s);
         }
         // o-proj + residual, u = x * ffn_norm
-        QD_GEMV_LAUNCH(k_gemv_residual, CFG_SMALL, m->lpr_o, m->grid_o, gemv_lds_bytes(Ly.o.nb), s,
+        QD_GEMV(k_gemv_residual, (QD_CFG_O), m->lpr_o, m->grid_o, gemv_lds_bytes(Ly.o.nb), s,
                        Ly.o.d, Ly.o.qs, m->attn, Ly.o.rows, Ly.o.nb, m->x, m->u, Ly.ffn_norm,
                        m->ss_part);
         n_part = m->grid_o;
         // gate|up + SwiGLU
-        QD_GEMV_LAUNCH(k_gemv_swiglu, CFG_WIDE, m->lpr_gu, m->grid_gu, gemv_lds_bytes(Ly.gu.nb), s,
+        QD_GEMV(k_gemv_swiglu, (QD_CFG_GU), m->lpr_gu, m->grid_gu, gemv_lds_bytes(Ly.gu.nb), s,
                        Ly.gu.d, Ly.gu.qs, m->u, Ly.gu.rows, Ly.gu.nb, m->ss_part, n_part, H, m->eps,
                        m->act);
         // down + residual, u = x * (next attn_norm | final_norm)
         const float* wn = (l + 1 < m->L) ? m->layers[l + 1].attn_norm : m->final_norm;
-        QD_GEMV_LAUNCH(k_gemv_residual, CFG_SMALL, m->lpr_down, m->grid_down,
+        QD_GEMV(k_gemv_residual, (QD_CFG_DOWN), m->lpr_down, m->grid_down,
                        gemv_lds_bytes(Ly.down.nb), s, Ly.down.d, Ly.down.qs, m->act, Ly.down.rows,
                        Ly.down.nb, m->x, m->u, wn, m->ss_part);
         n_part = m->grid_down;
     }
-    QD_GEMV_LAUNCH(k_gemv_lmhead, CFG_HEAD, m->lpr_lm, m->grid_lm, gemv_lds_bytes(m->lm.nb), s,
+    QD_GEMV(k_gemv_lmhead, (QD_CFG_HEAD), m->lpr_lm, m->grid_lm, gemv_lds_bytes(m->lm.nb), s,
                    m->lm.d, m->lm.qs, m->u, m->lm.rows, m->lm.nb, m->ss_part, n_part, H, m->eps,
                    m->logits, m->arg_val, m->arg_idx);
     hipLaunchKernelGGL(k_argmax_advance, dim3(1), dim3(256), 0, s, m->arg_val, m->arg_idx,
@@ -576,16 +573,21 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
         m->lpr_qkv = pick_lpr(nbH);
         m->grid_qkv = gemv_grid(CFG_QKV, m->lpr_qkv, m->qkv_rows);
         m->lpr_o = pick_lpr(nqd / 32);
-        m->grid_o = gemv_grid(CFG_SMALL, m->lpr_o, H);
+        m->grid_o = gemv_grid(CFG_O, m->lpr_o, H);   // one tile per workgroup (residual epilogue)
         m->lpr_gu = pick_lpr(nbH);
-        m->grid_gu = gemv_grid(CFG_WIDE, m->lpr_gu, 2 * m->I);
+        m->grid_gu = gemv_grid(CFG_GU, m->lpr_gu, 2 * m->I);
         m->lpr_down = pick_lpr(m->I / 32);
-        m->grid_down = gemv_grid(CFG_SMALL, m->lpr_down, H);
+        m->grid_down = gemv_grid(CFG_DOWN, m->lpr_down, H);   // one tile per workgroup
         m->lpr_lm = pick_lpr(nbH);
         m->grid_lm = gemv_grid(CFG_HEAD, m->lpr_lm, m->V);
         // attention: 64-key splits over max_seq, so the grid does not depend on the position
-        m->attn_chunk = ATT_T;
-        m->attn_nsplit = (m->max_seq + ATT_T - 1) / ATT_T;
+        // attention: splits over max_seq (the grid does not depend on the position),
+        // about one workgroup per CU
+        const int gq = m->nq / m->nkv;
+        const AttnGeom ag = attn_geom(1, m->nkv, m->max_seq, ATT_MODEL_WGS, gq <= 4 ? 8 : 4, 0);
+        m->attn_waves = ag.waves;
+        m->attn_chunk = ag.chunk;
+        m->attn_nsplit = ag.nsplit;
     }
 
     // step buffers
@@ -719,11 +721,16 @@ extern "C" int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const
     return QD_OK;
 }
 
-static size_t attn_ws_layout(int32_t B, int32_t nq, int32_t nkv, int32_t hd, int32_t max_kv,
-                             int* chunk, int* nsplit)
+static AttnGeom standalone_geom(int32_t B, int32_t nkv, int32_t max_kv)
 {
-    attn_split(B, nkv, max_kv, chunk, nsplit);
-    return (size_t)B * nq * (*nsplit) * (hd + 2) * sizeof(float);
+    return attn_geom(B, nkv, max_kv, 1024, 4, 4);
+}
+
+static size_t attn_ws_layout(int32_t B, int32_t nq, int32_t nkv, int32_t hd, int32_t max_kv,
+                             AttnGeom* g)
+{
+    *g = standalone_geom(B, nkv, max_kv);
+    return (size_t)B * nq * g->nsplit * (hd + 2) * sizeof(float);
 }
 
 extern "C" size_t qd_attn_workspace_bytes(int32_t B, int32_t nq, int32_t nkv, int32_t head_dim,
@@ -731,8 +738,8 @@ extern "C" size_t qd_attn_workspace_bytes(int32_t B, int32_t nq, int32_t nkv, in
 {
     if (B <= 0 || nq <= 0 || nkv <= 0 || head_dim <= 0 || max_kv_len < 0)
         return 0;
-    int chunk, nsplit;
-    return attn_ws_layout(B, nq, nkv, head_dim, max_kv_len, &chunk, &nsplit);
+    AttnGeom g;
+    return attn_ws_layout(B, nq, nkv, head_dim, max_kv_len, &g);
 }
 
 extern "C" int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t workspace_bytes,
@@ -759,9 +766,8 @@ extern "C" int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t w
     }
     if (a->B == 0)
         return QD_OK;
-    int chunk, nsplit;
-    const size_t need = attn_ws_layout(a->B, a->nq, a->nkv, a->head_dim, a->max_kv_len, &chunk,
-                                       &nsplit);
+    AttnGeom geo;
+    const size_t need = attn_ws_layout(a->B, a->nq, a->nkv, a->head_dim, a->max_kv_len, &geo);
     if (workspace_bytes < need)
         return fail(QD_EINVAL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
     AttnParams p;
@@ -777,11 +783,11 @@ extern "C" int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t w
     p.nq = a->nq;
     p.nkv = a->nkv;
     p.scale = a->scale;
-    p.chunk = chunk;
-    p.nsplit = nsplit;
+    p.chunk = geo.chunk;
+    p.nsplit = geo.nsplit;
     p.part = reinterpret_cast<float*>(d_workspace);
     p.out = a->out;
-    launch_attention<0>(p, a->head_dim, gq, a->block_tables != nullptr, a->B, a->nq,
+    launch_attention<0>(p, geo.waves, a->head_dim, gq, a->block_tables != nullptr, a->B, a->nq,
                         (hipStream_t)stream);
     HIP_TRY(hipGetLastError());
     return QD_OK;

@@ -97,9 +97,9 @@ QD_DEV float group_max(float v)
 }
 
 // Timeline marks for profiling builds only: with QD_TIMELINE defined, thread 0
-// of every workgroup stores the 100 MHz real-time counter for mark k (0..3) at
-// qd_tl[4 * w + k], w = the linear workgroup index; the profiling host points
-// qd_tl at a buffer of 4 entries per workgroup before each launch (a
+// of every workgroup stores the 100 MHz real-time counter for mark k (0..7) at
+// qd_tl[8 * w + k], w = the linear workgroup index; the profiling host points
+// qd_tl at a buffer of 8 entries per workgroup before each launch (a
 // __constant__ pointer: read with a scalar load, so a mark never waits on the
 // kernel's vector loads).  Without QD_TIMELINE a mark is nothing.
 #ifdef QD_TIMELINE
@@ -107,7 +107,7 @@ __constant__ uint64_t* qd_tl;
 #define QD_MARK(k)                                                          \
     do {                                                                    \
         if (threadIdx.x == 0 && qd_tl)                                      \
-            qd_tl[4 * (blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z)) + (k)] = \
+            qd_tl[8 * (blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z)) + (k)] = \
                 __builtin_amdgcn_s_memrealtime();                              \
     } while (0)
 #else

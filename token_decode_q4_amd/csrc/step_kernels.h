@@ -109,7 +109,7 @@ struct EpiScaled {
     int n_in;
     float eps;
     float inv;
-    QD_DEV void issue() { rp.issue(); }
+    QD_DEV void issue(int) { rp.issue(); }
     QD_DEV void finish() { inv = rp.finish(n_in, eps); }
     template <int RPS>
     QD_DEV void tile(int row0, const float (&acc)[RPS], bool lead)
@@ -123,16 +123,27 @@ struct EpiScaled {
     }
 };
 
-// x[row] += acc; u[row] = x[row] * w_next[row]; running sum of the new x^2
+// x[row] += acc; u[row] = x[row] * w_next[row]; running sum of the new x^2.
+// Launched with one tile per workgroup: issue() loads the tile's x and w_next
+// rows at kernel start, so the epilogue itself loads nothing.
+template <int RPS>
 struct EpiResidual {
     float* x;
     float* u;
     const float* w_next;
     int N;
     float ss;
-    QD_DEV void issue() {}
+    float px[RPS], pw[RPS];
+    QD_DEV void issue(int row0)
+    {
+#pragma unroll
+        for (int r = 0; r < RPS; ++r) {
+            const int row = min(row0 + r, N - 1);
+            px[r] = x[row];
+            pw[r] = w_next[row];
+        }
+    }
     QD_DEV void finish() {}
-    template <int RPS>
     QD_DEV void tile(int row0, const float (&acc)[RPS], bool lead)
     {
         if (lead) {
@@ -140,9 +151,9 @@ struct EpiResidual {
             for (int r = 0; r < RPS; ++r) {
                 const int row = row0 + r;
                 if (row < N) {
-                    const float nx = x[row] + acc[r];
+                    const float nx = px[r] + acc[r];
                     x[row] = nx;
-                    u[row] = nx * w_next[row];
+                    u[row] = nx * pw[r];
                     ss = fmaf(nx, nx, ss);
                 }
             }
@@ -159,7 +170,7 @@ struct EpiSwiglu {
     int n_in;
     float eps;
     float inv;
-    QD_DEV void issue() { rp.issue(); }
+    QD_DEV void issue(int) { rp.issue(); }
     QD_DEV void finish() { inv = rp.finish(n_in, eps); }
     template <int RPS>
     QD_DEV void tile(int row0, const float (&acc)[RPS], bool lead)
@@ -187,7 +198,7 @@ struct EpiLmHead {
     float inv;
     float best;
     int32_t bidx;
-    QD_DEV void issue() { rp.issue(); }
+    QD_DEV void issue(int) { rp.issue(); }
     QD_DEV void finish() { inv = rp.finish(n_in, eps); }
     template <int RPS>
     QD_DEV void tile(int row0, const float (&acc)[RPS], bool lead)
@@ -232,7 +243,7 @@ k_gemv_residual(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
 {
     extern __shared__ float smem[];
     __shared__ float red[8];
-    EpiResidual e{x, u, w_next, N, 0.f};
+    EpiResidual<RPS> e{x, u, w_next, N, 0.f};
     gemv_run<LPR, RPS, NWAVES, BG, NBUF, NTL, false>(D, Q, a, N, nb, smem, smem + nb * XPAD, e);
     const float ss = block_sum256(e.ss, red);
     if (threadIdx.x == 0)
