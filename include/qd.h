@@ -142,8 +142,9 @@ int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* d_tokens,
 
 /* Standalone q4_0 GEMV (inferencelayer cuda_llm.rs page, CudaQwen3::gemv):
  * y[N] = W[N, K] x[K], W in the q4_0 layout above (device d_scales
- * [N][K/32], d_qs [N][K/32][16]), x and y device f32.  K % 32 == 0.  No
- * allocation; capturable. */
+ * [N][K/32], d_qs [N][K/32][16]), x and y device f32.  K % 32 == 0; qs and x
+ * 16-byte aligned.  Supported: K up to 14 144 (x is staged in LDS), N < 2^24,
+ * N*K/2 < 2^32 (QD_EUNSUPPORTED otherwise).  No allocation; capturable. */
 int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x, float* d_y,
                  int32_t N, int32_t K, qd_stream stream);
 

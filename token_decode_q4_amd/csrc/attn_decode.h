@@ -83,6 +83,9 @@ struct alignas(16) AttnSmem {
     float acc[W][GQ][HD];
 };
 
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
 // LDS writes of this wave are seen by its later LDS reads (no workgroup barrier)
 QD_DEV void wave_lds_sync()
 {
@@ -122,7 +125,7 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const int nw = blockDim.x / WAVE;          // waves of this launch
     const int wstride = nw * ATT_WK;           // keys between a wave's steps
-    const int kk = lane >> 2, cq = lane & 3;   // QK layout: key, quarter
+    const int kk = lane & 15;                  // QK: the key of this lane's A rows
     const int h0 = g * GQ;
     const int t_begin = s * p.chunk;
     QD_MARK(0);
@@ -144,7 +147,7 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
         }
 #pragma unroll
         for (int i = 0; i < NI; ++i)
-            st.k[i] = *reinterpret_cast<const uint4*>(kp + 8 * cq + 32 * i);
+            st.k[i] = *reinterpret_cast<const uint4*>(kp + 8 * (lane >> 4) + 32 * i);
 #pragma unroll
         for (int j = 0; j < ATT_WK; ++j) {
             const uint16_t* r = PAGED ? vp + (size_t)j * HD
@@ -156,8 +159,10 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
         }
     };
 
-    // kv_len first (vector loads return in order): the loads below do not need it
-    int kv_len = p.kv_lens ? p.kv_lens[b] : (*p.pos + 1);
+    // kv_len first (vector loads return in order): the loads below do not need
+    // it.  One load from a selected address, so nothing waits for it here.
+    const int32_t* kvp = p.kv_lens ? p.kv_lens + b : p.pos;
+    const int kv_raw = *kvp;
 
     // ---- loads that do not need kv_len: the token's q|k|v, norm weights,
     // rotary factors, and (decode step) the first step's K/V
@@ -189,48 +194,35 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
     const int tw0 = t_begin + w * ATT_WK;
     load_step(cur_st, tw0);
 
-    kv_len = max(0, min(kv_len, p.max_kv));
-    if (kv_len >= 0)
-        QD_MARK(1);
-    const int t_end = min(kv_len, t_begin + p.chunk);
-    if (t_begin >= t_end)
-        return;   // key range past kv_len: the combine reads only active splits
-    const int tcur = kv_len - 1;   // the step's own position (QMODE 1)
-
-    // ---- queries: per-head RMSNorm and rotary (QMODE 1), times scale, into
-    // this wave's LDS rows; the wave holding tcur also prepares the token's K/V
-    // the owner: the wave whose step own_tw holds tcur, at row slot of it
-    float vnew[DPL];
-    const int rel = tcur - t_begin;
-    const bool owner = QMODE == 1 && tcur >= t_begin && tcur < t_end && (rel / ATT_WK) % nw == w;
-    const int own_tw = t_begin + (rel / ATT_WK) * ATT_WK;
-    const int slot = tcur - own_tw;
+    // ---- queries (and the token's k): per-head RMSNorm and rotary (QMODE 1),
+    // times scale, into this wave's LDS rows.  None of it needs kv_len, so it
+    // runs while the position is still in flight.
     if (QMODE == 1) {
-        const float* nq_w = wq;
-        if (p.qk_norm) {
+        // no branch around the uses of the norm weights: a load used only in
+        // a branch is sunk into it, behind the K/V loads, and then waits for them
+        const bool qkn = p.qk_norm != 0;
 #pragma unroll
-            for (int j = 0; j < GQ; ++j) {
-                float ss = 0.f;
+        for (int j = 0; j < GQ; ++j) {
+            float ss = 0.f;
 #pragma unroll
-                for (int e = 0; e < DPL; ++e)
-                    ss = fmaf(qv[j][e], qv[j][e], ss);
-                ss = group_sum<WAVE>(ss);
-                const float r = 1.0f / sqrtf(ss / (float)HD + p.eps);
+            for (int e = 0; e < DPL; ++e)
+                ss = fmaf(qv[j][e], qv[j][e], ss);
+            ss = group_sum<WAVE>(ss);
+            const float r = qkn ? 1.0f / sqrtf(ss / (float)HD + p.eps) : 1.f;
 #pragma unroll
-                for (int e = 0; e < DPL; ++e)
-                    qv[j][e] = qv[j][e] * r * nq_w[e];
-            }
-            if (owner) {
-                float ss = 0.f;
+            for (int e = 0; e < DPL; ++e)
+                qv[j][e] = qv[j][e] * r * (qkn ? wq[e] : 1.f);
+        }
+        {
+            float ss = 0.f;
 #pragma unroll
-                for (int e = 0; e < DPL; ++e)
-                    ss = fmaf(kv_[e], kv_[e], ss);
-                ss = group_sum<WAVE>(ss);
-                const float r = 1.0f / sqrtf(ss / (float)HD + p.eps);
+            for (int e = 0; e < DPL; ++e)
+                ss = fmaf(kv_[e], kv_[e], ss);
+            ss = group_sum<WAVE>(ss);
+            const float r = qkn ? 1.0f / sqrtf(ss / (float)HD + p.eps) : 1.f;
 #pragma unroll
-                for (int e = 0; e < DPL; ++e)
-                    kv_[e] = kv_[e] * r * wk[e];
-            }
+            for (int e = 0; e < DPL; ++e)
+                kv_[e] = kv_[e] * r * (qkn ? wk[e] : 1.f);
         }
         // rotary: the partner of dim d is d +- rot/2, read from LDS
 #pragma unroll
@@ -241,46 +233,27 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
             sm.krow[w][lane * DPL + e] = kv_[e];
         }
         wave_lds_sync();
+        // (dims at or past rot have cos 1 and sin 0: the same formula keeps them)
         const int half = p.rot / 2;
         float qpart[GQ][DPL], kpart[DPL];
 #pragma unroll
         for (int e = 0; e < DPL; ++e) {
             const int d = lane * DPL + e;
-            const int pd = d < half ? d + half : d - half;
-            const bool rd = d < p.rot;
+            const int pd = d < half ? d + half : d - half;   // in [0, HD)
 #pragma unroll
             for (int j = 0; j < GQ; ++j)
-                qpart[j][e] = rd ? sm.q[w][j][pd] : 0.f;
-            kpart[e] = rd ? sm.krow[w][pd] : 0.f;
+                qpart[j][e] = sm.q[w][j][pd];
+            kpart[e] = sm.krow[w][pd];
         }
         wave_lds_sync();   // every partner read done before the rows change
 #pragma unroll
         for (int e = 0; e < DPL; ++e) {
             const int d = lane * DPL + e;
-            if (d < p.rot) {
-                const float sg = d < half ? -sn[e] : sn[e];
+            const float sg = d < half ? -sn[e] : sn[e];
 #pragma unroll
-                for (int j = 0; j < GQ; ++j)
-                    qv[j][e] = fmaf(qpart[j][e], sg, qv[j][e] * cs[e]);
-                kv_[e] = fmaf(kpart[e], sg, kv_[e] * cs[e]);
-            }
-        }
-        if (owner) {
-            size_t o;
-            if (PAGED)
-                o = kv_row<HD, PAGED>(p, p.tables[(size_t)b * p.mbps + tcur / ATT_BS], g, tcur);
-            else
-                o = kv_row<HD, PAGED>(p, b, g, tcur);
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) {
-                const int d = lane * DPL + e;
-                const uint16_t kh = f32_to_f16(kv_[e]);
-                const uint16_t vh = f32_to_f16(vv[e]);
-                p.kc[o + d] = kh;
-                p.vc[o + d] = vh;
-                sm.knew[w][d] = kh;
-                vnew[e] = f16_to_f32(vh);
-            }
+            for (int j = 0; j < GQ; ++j)
+                qv[j][e] = fmaf(qpart[j][e], sg, qv[j][e] * cs[e]);
+            kv_[e] = fmaf(kpart[e], sg, kv_[e] * cs[e]);
         }
     }
 #pragma unroll
@@ -288,19 +261,75 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
 #pragma unroll
         for (int j = 0; j < GQ; ++j)
             sm.q[w][j][lane * DPL + e] = qv[j][e] * p.scale;
+
+    // ---- now the position: the key range, and the wave whose step own_tw
+    // holds the token's own position stores its K and V (f16) and uses them
+    const int kv_len = max(0, min(p.kv_lens ? kv_raw : kv_raw + 1, p.max_kv));
+    if (kv_len >= 0)
+        QD_MARK(1);
+    const int t_end = min(kv_len, t_begin + p.chunk);
+    if (t_begin >= t_end)
+        return;   // key range past kv_len: the combine reads only active splits
+    const int tcur = kv_len - 1;
+    float vnew[DPL];
+    const int rel = tcur - t_begin;
+    const bool owner = QMODE == 1 && tcur >= t_begin && tcur < t_end && (rel / ATT_WK) % nw == w;
+    const int own_tw = t_begin + (rel / ATT_WK) * ATT_WK;
+    const int slot = tcur - own_tw;
+    if (owner) {
+        size_t o;
+        if (PAGED)
+            o = kv_row<HD, PAGED>(p, p.tables[(size_t)b * p.mbps + tcur / ATT_BS], g, tcur);
+        else
+            o = kv_row<HD, PAGED>(p, b, g, tcur);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) {
+            const int d = lane * DPL + e;
+            const uint16_t kh = f32_to_f16(kv_[e]);
+            const uint16_t vh = f32_to_f16(vv[e]);
+            p.kc[o + d] = kh;
+            p.vc[o + d] = vh;
+            sm.knew[w][d] = kh;
+            vnew[e] = f16_to_f32(vh);
+        }
+    }
     wave_lds_sync();
     QD_MARK(2);
 
-    // ---- the wave's steps
-    float m[GQ], l[GQ], acc[GQ][DPL];
+    // ---- QK operands of the matrix core: v_mfma_f32_16x16x32_f16 with
+    // M = the step's 16 keys, N = query heads (columns >= GQ are zero), K = 32
+    // dims per instruction.  Lane l holds dims 8*(l/16) .. +7 of each 32-dim
+    // slice: of key l%16 for A (straight from the K loads) and of head l%16 for
+    // B.  q enters as a pair of f16 (hi + lo, about 22 significant bits); the
+    // two products accumulate in one f32 result, and K is f16 already.
+    half8 bhi[NI], blo[NI];
 #pragma unroll
-    for (int j = 0; j < GQ; ++j) {
-        m[j] = -INFINITY;
-        l[j] = 0.f;
+    for (int i = 0; i < NI; ++i) {
+        const int col = lane & 15;
+        float qf[8];
+        const float* src = &sm.q[w][col < GQ ? col : 0][32 * i + 8 * (lane >> 4)];
+        const float4 q0 = *reinterpret_cast<const float4*>(src);
+        const float4 q1 = *reinterpret_cast<const float4*>(src + 4);
+        qf[0] = q0.x; qf[1] = q0.y; qf[2] = q0.z; qf[3] = q0.w;
+        qf[4] = q1.x; qf[5] = q1.y; qf[6] = q1.z; qf[7] = q1.w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float v = col < GQ ? qf[e] : 0.f;
+            const _Float16 h = (_Float16)v;
+            bhi[i][e] = h;
+            blo[i][e] = (_Float16)(v - (float)h);
+        }
+    }
+
+    // ---- the wave's steps.  m_c, l_c: running max and sum of head
+    // c = lane % 16 (meaningful for c < GQ), the same in the lanes c + 16 k.
+    float m_c = -INFINITY, l_c = 0.f, acc[GQ][DPL];
+#pragma unroll
+    for (int j = 0; j < GQ; ++j)
 #pragma unroll
         for (int e = 0; e < DPL; ++e)
             acc[j][e] = 0.f;
-    }
+    const int col = lane & 15, kg = lane >> 4;
     for (int tw = tw0; tw < t_end; tw += wstride) {
         Step nxt;
         const bool more = tw + wstride < t_end;
@@ -308,8 +337,6 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
             load_step(nxt, tw + wstride);
         const int nvalid = min(ATT_WK, t_end - tw);
         const bool own_here = owner && tw == own_tw;
-        // QK: 8 dims x NI slices of key kk
-        float kf[NI][8];
         uint4 kr[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i)
@@ -317,55 +344,58 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
         if (own_here && kk == slot) {
 #pragma unroll
             for (int i = 0; i < NI; ++i)
-                kr[i] = *reinterpret_cast<const uint4*>(&sm.knew[w][32 * i + 8 * cq]);
+                kr[i] = *reinterpret_cast<const uint4*>(&sm.knew[w][32 * i + 8 * kg]);
         }
+        QD_MARK(4);
+        floatx4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const uint32_t kw[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                kf[i][2 * e] = f16_to_f32((uint16_t)(kw[e] & 0xffffu));
-                kf[i][2 * e + 1] = f16_to_f32((uint16_t)(kw[e] >> 16));
-            }
-        }
-        const bool kvalid = kk < nvalid;
-        QD_MARK(4);
-        float sc[GQ];
-#pragma unroll
-        for (int j = 0; j < GQ; ++j) {
-            float d = 0.f;
-#pragma unroll
-            for (int i = 0; i < NI; ++i) {
-                const float4 qa = *reinterpret_cast<const float4*>(&sm.q[w][j][32 * i + 8 * cq]);
-                const float4 qb = *reinterpret_cast<const float4*>(&sm.q[w][j][32 * i + 8 * cq + 4]);
-                d = fmaf(qa.x, kf[i][0], d);
-                d = fmaf(qa.y, kf[i][1], d);
-                d = fmaf(qa.z, kf[i][2], d);
-                d = fmaf(qa.w, kf[i][3], d);
-                d = fmaf(qb.x, kf[i][4], d);
-                d = fmaf(qb.y, kf[i][5], d);
-                d = fmaf(qb.z, kf[i][6], d);
-                d = fmaf(qb.w, kf[i][7], d);
-            }
-            d = group_sum<4>(d);   // the 4 quarters of key kk
-            sc[j] = kvalid ? d : -INFINITY;
+            const half8 a = __builtin_bit_cast(half8, kr[i]);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bhi[i], sc, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, blo[i], sc, 0, 0, 0);
         }
         QD_MARK(5);
-        // online softmax over the step's keys: the 4 lanes of a key hold the
-        // same score, so the max runs over the whole wave and the sum over
-        // the quarter-0 lanes (the others add zeros)
+        // sc[r] = score of key 4*kg + r for head col; online softmax per head
+        // over the 16 keys: 4 registers, then the 4 lane groups kg
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            sc[r] = (4 * kg + r < nvalid) ? sc[r] : -INFINITY;
+            mx = fmaxf(mx, sc[r]);
+        }
+        {
+            float lo, hi;
+            lanes::swap16(mx, lo, hi);
+            mx = fmaxf(lo, hi);
+            lanes::swap32(mx, lo, hi);
+            mx = fmaxf(lo, hi);
+        }
+        const float mnew = fmaxf(m_c, mx);
+        float pr[4], ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pr[r] = expf(sc[r] - mnew);   // 0 for a masked key
+            ps += pr[r];
+        }
+        {
+            float lo, hi;
+            lanes::swap16(ps, lo, hi);
+            ps = lo + hi;
+            lanes::swap32(ps, lo, hi);
+            ps = lo + hi;
+        }
+        const float alpha_c = expf(m_c - mnew);   // 0 on the first step (m = -inf)
+        l_c = fmaf(l_c, alpha_c, ps);
+        m_c = mnew;
+        if (col < GQ) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sm.p[w][4 * kg + r][col] = pr[r];
+        }
         float alpha[GQ];
 #pragma unroll
-        for (int j = 0; j < GQ; ++j) {
-            const float mnew = fmaxf(m[j], group_max<WAVE>(sc[j]));
-            const float pr = expf(sc[j] - mnew);
-            const float ps = group_sum<WAVE>(cq == 0 ? pr : 0.f);
-            alpha[j] = expf(m[j] - mnew);   // 0 on the first step (m = -inf)
-            l[j] = fmaf(l[j], alpha[j], ps);
-            m[j] = mnew;
-            if (cq == 0)
-                sm.p[w][kk][j] = pr;
-        }
+        for (int j = 0; j < GQ; ++j)
+            alpha[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha_c), j));
         wave_lds_sync();
         QD_MARK(6);
         // PV: lane owns dims lane*DPL ..
@@ -406,12 +436,12 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
     }
 
     // ---- merge the waves, write the workgroup's partial
+    if (lane < GQ) {
+        sm.m[w][lane] = m_c;
+        sm.l[w][lane] = l_c;
+    }
 #pragma unroll
     for (int j = 0; j < GQ; ++j) {
-        if (lane == 0) {
-            sm.m[w][j] = m[j];
-            sm.l[w][j] = l[j];
-        }
 #pragma unroll
         for (int e = 0; e < DPL; ++e)
             sm.acc[w][j][lane * DPL + e] = acc[j][e];

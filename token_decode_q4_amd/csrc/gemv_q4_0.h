@@ -147,15 +147,12 @@ struct GemvBuf {
 //                               this lane's first row of its first tile)
 //   epi.finish()                after x is staged: what needs those loads
 //   epi.tile(row0, acc, lead)   acc[RPS] = dot products of rows row0 .. row0+RPS-1
-// Scales come either in the canonical layout d[row][block] (TS = false) or
-// in the tiled layout written by tile_scales() (TS = true): for every (tile,
-// wave, slot, lane) the lane's scales ordered [block j][row r], so one work
-// item's RPS*BG scales are contiguous and arrive in one load.
-template <int LPR, int RPS, int NWAVES, int BG, int NBUF, bool NTL, bool TS, class Epi>
+template <int LPR, int RPS, int NWAVES, int BG, int NBUF, int UNR, bool NTL, class Epi>
 QD_DEV void gemv_run(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                      const float* __restrict__ x, int N, int nb, float* xl, float* xs, Epi& epi)
 {
-    static_assert(NBUF >= 1 && NBUF <= 3, "buffers");
+    static_assert(NBUF >= 1 && NBUF <= 6, "buffers");
+    static_assert(UNR >= NBUF, "unroll");
     using G = GemvGeom<LPR, RPS, NWAVES>;
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
@@ -173,12 +170,13 @@ QD_DEV void gemv_run(const uint16_t* __restrict__ D, const uint8_t* __restrict__
         const int grp = i % ngroups;
         const int row0 = tile * G::ROWS + wave * G::RPW + slot * RPS;
 #pragma unroll
-        for (int g = 0; g < BG; ++g) {
-            const int bc = min(grp * LPR * BG + g * LPR + lr, nb - 1);
+        for (int r = 0; r < RPS; ++r) {
+            // 32-bit block index (the host keeps N * nb * 16 below 2^32)
+            const uint32_t rb = __umul24((uint32_t)min(row0 + r, N - 1), (uint32_t)nb);
 #pragma unroll
-            for (int r = 0; r < RPS; ++r) {
-                const size_t blk = (size_t)min(row0 + r, N - 1) * nb + bc;
-                const uint4* qp = reinterpret_cast<const uint4*>(Q + blk * 16);
+            for (int g = 0; g < BG; ++g) {
+                const uint32_t blk = rb + (uint32_t)min(grp * LPR * BG + g * LPR + lr, nb - 1);
+                const uint4* qp = reinterpret_cast<const uint4*>(Q + blk * 16u);
                 if (NTL) {
                     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
                     const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qp));
@@ -186,36 +184,7 @@ QD_DEV void gemv_run(const uint16_t* __restrict__ D, const uint8_t* __restrict__
                 } else {
                     bf.q[g][r] = *qp;
                 }
-                if (!TS)
-                    bf.d[g][r] = D[blk];
-            }
-        }
-        if (TS) {
-            // record of this (tile, wave, slot, lane): [j][r], j = block index of the lane
-            constexpr int E = RPS * BG;   // scales of one item
-            const int nj = nb / LPR;
-            const uint16_t* rec = D + ((((size_t)tile * NWAVES + wave) * G::SLOTS + slot) * LPR + lr) *
-                                          (size_t)(nj * RPS) + (size_t)grp * E;
-            if (E == 8) {
-                const uint4 v = *reinterpret_cast<const uint4*>(rec);
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    bf.d[e / RPS][e % RPS] = (w[e / 2] >> (16 * (e % 2))) & 0xffffu;
-            } else if (E == 4) {
-                const uint2 v = *reinterpret_cast<const uint2*>(rec);
-                const uint32_t w[2] = {v.x, v.y};
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    bf.d[e / RPS][e % RPS] = (w[e / 2] >> (16 * (e % 2))) & 0xffffu;
-            } else if (E == 2) {
-                const uint32_t v = *reinterpret_cast<const uint32_t*>(rec);
-                bf.d[0 / RPS][0 % RPS] = v & 0xffffu;
-                bf.d[1 / RPS][1 % RPS] = v >> 16;
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    bf.d[e / RPS][e % RPS] = rec[e];
+                bf.d[g][r] = D[blk];
             }
         }
     };
@@ -267,16 +236,23 @@ QD_DEV void gemv_run(const uint16_t* __restrict__ D, const uint8_t* __restrict__
     stage_x_store<G::NT>(nb, xst, xl, xs);   // ends with a barrier
     epi.finish();
     QD_MARK(1);
-    for (int i = 0; i < nitems; i += NBUF) {
+    // Items in chunks of UNR, each chunk fully unrolled, so that no loaded
+    // register is live across a loop back-edge (the compiler copies such a
+    // register at the latch and waits for every load to do it) and no load
+    // is issued past the chunk.  With UNR >= the items of a workgroup there is
+    // a single chunk.
+    for (int base = 0; base < nitems; base += UNR) {
+        if (base > 0) {
 #pragma unroll
-        for (int j = 0; j < NBUF; ++j) {
-            if (i + j < nitems) {
-                if (NBUF == 1)
-                    load(bufs[0], i + j);
-                else
-                    load(bufs[(j + NBUF - 1) % NBUF], i + j + NBUF - 1);
-                compute(bufs[j], i + j);
-            }
+            for (int j = 0; j + 1 < NBUF; ++j)
+                load(bufs[j], base + j);
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            if (u + NBUF - 1 < UNR)
+                load(bufs[(u + NBUF - 1) % NBUF], base + u + NBUF - 1);
+            if (base + u < nitems)
+                compute(bufs[u % NBUF], base + u);
         }
     }
     QD_MARK(2);
@@ -333,37 +309,14 @@ struct EpiStore {
     }
 };
 
-template <int LPR, int RPS, int NWAVES, int BG, int NBUF, bool NTL, bool TS = false>
+template <int LPR, int RPS, int NWAVES, int BG, int NBUF, int UNR, bool NTL>
 __global__ void __launch_bounds__(NWAVES* WAVE)
 k_gemv_plain(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
              const float* __restrict__ x, float* __restrict__ y, int N, int nb)
 {
     extern __shared__ float smem[];
     EpiStore e{y, N};
-    gemv_run<LPR, RPS, NWAVES, BG, NBUF, NTL, TS>(D, Q, x, N, nb, smem, smem + nb * XPAD, e);
-}
-
-// Host side: rewrite canonical scales d[N][nb] into the tiled layout for
-// (LPR, RPS, NWAVES): for tile t, wave w, slot s, lane l the record of
-// nb/LPR * RPS scales ordered [j][r] holds d[row0 + r][j*LPR + l] with
-// row0 = t*ROWS + w*RPW + s*RPS (rows past N give 0).  Needs nb % LPR == 0.
-// Returns the number of uint16 written (ntiles * ROWS * nb).
-inline size_t tile_scales(const uint16_t* d, int N, int nb, int lpr, int rps, int nwaves,
-                          uint16_t* out)
-{
-    const int slots = WAVE / lpr, rpw = slots * rps, rows = nwaves * rpw;
-    const int ntiles = (N + rows - 1) / rows, nj = nb / lpr;
-    size_t o = 0;
-    for (int t = 0; t < ntiles; ++t)
-        for (int w = 0; w < nwaves; ++w)
-            for (int s = 0; s < slots; ++s)
-                for (int l = 0; l < lpr; ++l)
-                    for (int j = 0; j < nj; ++j)
-                        for (int r = 0; r < rps; ++r) {
-                            const int row = t * rows + w * rpw + s * rps + r;
-                            out[o++] = row < N ? d[(size_t)row * nb + (size_t)j * lpr + l] : 0;
-                        }
-    return o;
+    gemv_run<LPR, RPS, NWAVES, BG, NBUF, UNR, NTL>(D, Q, x, N, nb, smem, smem + nb * XPAD, e);
 }
 
 }  // namespace qd

@@ -13,6 +13,7 @@
 
 #include "step_kernels.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -49,29 +50,30 @@ extern "C" const char* qd_last_error(void) { return g_err.c_str(); }
 // ------------------------------------------------------------------ GEMV launch
 
 // GEMV launch configurations: rows per slot, waves, block groups per item,
-// register buffers, non-temporal weight loads (the template arguments), and a
-// cap on the grid.  Chosen per call site by timing the step's shapes on
+// register buffers, items per unrolled chunk, non-temporal weight loads (the
+// template arguments), and a cap on the grid.  Chosen per call site by timing the step's shapes on
 // MI355X over rotated weight copies; the lanes-per-row count follows K.
 struct GemvCfg {
-    int rps, nw, bg, nbuf, ntl, grid_cap;
+    int rps, nw, bg, nbuf, unr, ntl, grid_cap, lpr_max;
 };
-#define QD_CFG_O 2, 8, 1, 2, false      // o-proj, N ~ hidden
-#define QD_CFG_DOWN 2, 8, 2, 2, false   // down, long rows
-#define QD_CFG_QKV 3, 8, 1, 2, false    // q|k|v
-#define QD_CFG_GU 4, 4, 1, 2, false     // gate|up
-#define QD_CFG_HEAD 4, 4, 1, 2, true    // LM head (streamed once)
-static constexpr GemvCfg CFG_O = {QD_CFG_O, 1 << 30};
-static constexpr GemvCfg CFG_DOWN = {QD_CFG_DOWN, 1 << 30};
-static constexpr GemvCfg CFG_QKV = {QD_CFG_QKV, 1 << 30};
-static constexpr GemvCfg CFG_GU = {QD_CFG_GU, 768};
-static constexpr GemvCfg CFG_HEAD = {QD_CFG_HEAD, 2048};
+#define QD_CFG_O 2, 8, 1, 2, 4, false      // o-proj, N ~ hidden
+#define QD_CFG_DOWN 2, 8, 1, 3, 6, false   // down, long rows
+#define QD_CFG_QKV 3, 8, 1, 2, 4, false    // q|k|v
+#define QD_CFG_GU 2, 4, 2, 2, 8, false     // gate|up (16 lanes per row)
+#define QD_CFG_HEAD 4, 4, 1, 2, 10, true   // LM head (streamed once)
+static constexpr GemvCfg CFG_O = {QD_CFG_O, 1 << 30, 64};
+static constexpr GemvCfg CFG_DOWN = {QD_CFG_DOWN, 1 << 30, 64};
+static constexpr GemvCfg CFG_QKV = {QD_CFG_QKV, 1 << 30, 64};
+static constexpr GemvCfg CFG_GU = {QD_CFG_GU, 512, 16};
+static constexpr GemvCfg CFG_HEAD = {QD_CFG_HEAD, 2048, 64};
 static constexpr int GEMV_MAX_LDS = 64 * 1024;
 static constexpr int ATT_MODEL_WGS = 160;   // attention workgroups of a decode step (measured best)
 
-// lanes per row: the largest of 64/32/16/8 dividing the number of blocks
-static int pick_lpr(int nb)
+// lanes per row: the largest of 64/32/16/8, at most the configuration's
+// limit, dividing the number of blocks
+static int pick_lpr(int nb, int lmax = 64)
 {
-    for (int l = 64; l >= 8; l >>= 1)
+    for (int l = lmax; l >= 8; l >>= 1)
         if (nb % l == 0)
             return l;
     return 8;
@@ -88,9 +90,9 @@ static int gemv_grid(const GemvCfg& c, int lpr, int N)
     return g > 0 ? g : 1;
 }
 
-// Launch kernel template KT<LPR, P...> with P = (RPS, NW, BG, NBUF, NTL).
+// Launch kernel template KT<LPR, P...> with P = (RPS, NW, BG, NBUF, UNR, NTL).
 #define QD_UNPACK(...) __VA_ARGS__
-#define QD_NW_(a, b, c, d, e) b
+#define QD_NW_(a, b, c, d, e, f) b
 #define QD_NW(...) QD_NW_(__VA_ARGS__)
 #define QD_GEMV_ONE(KT, L, P, grid, lds, s, ...) \
     hipLaunchKernelGGL((KT<L, QD_UNPACK P>), dim3(grid), dim3(QD_NW P * WAVE), lds, s, __VA_ARGS__)
@@ -110,7 +112,8 @@ static hipError_t launch_gemv_plain(const uint16_t* d, const uint8_t* q, const f
     if (N <= 8192) {
         QD_GEMV(k_gemv_plain, (QD_CFG_O), lpr, gemv_grid(CFG_O, lpr, N), lds, s, d, q, x, y, N, nb);
     } else if (N <= 65536) {
-        QD_GEMV(k_gemv_plain, (QD_CFG_GU), lpr, gemv_grid(CFG_GU, lpr, N), lds, s, d, q, x, y, N, nb);
+        const int l = pick_lpr(nb, CFG_GU.lpr_max);
+        QD_GEMV(k_gemv_plain, (QD_CFG_GU), l, gemv_grid(CFG_GU, l, N), lds, s, d, q, x, y, N, nb);
     } else {
         QD_GEMV(k_gemv_plain, (QD_CFG_HEAD), lpr, gemv_grid(CFG_HEAD, lpr, N), lds, s, d, q, x, y, N, nb);
     }
@@ -293,6 +296,12 @@ static int validate_config(const qd_config* c, const qd_weights* w)
     if ((size_t)c->hidden > kmax || (size_t)c->intermediate > kmax ||
         (size_t)c->n_heads * c->head_dim > kmax)
         return fail(QD_EUNSUPPORTED, "GEMV input length above %zu", kmax);
+    // the GEMV addresses a matrix's nibbles with 32-bit offsets
+    const uint64_t big = std::max<uint64_t>({(uint64_t)c->vocab * c->hidden,
+                                             (uint64_t)2 * c->intermediate * c->hidden,
+                                             (uint64_t)(c->n_heads + 2 * c->n_kv) * c->head_dim * c->hidden});
+    if (big / 2 >= (uint64_t)1 << 32 || c->vocab >= (1 << 24) || 2 * c->intermediate >= (1 << 24))
+        return fail(QD_EUNSUPPORTED, "a matrix above 2^32 bytes of nibbles or 2^24 rows");
     if (c->kv_paged) {
         if (c->kv_block_size != ATT_BS)
             return fail(QD_EUNSUPPORTED, "kv_block_size %d (only %d)", c->kv_block_size, ATT_BS);
@@ -574,7 +583,7 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
         m->grid_qkv = gemv_grid(CFG_QKV, m->lpr_qkv, m->qkv_rows);
         m->lpr_o = pick_lpr(nqd / 32);
         m->grid_o = gemv_grid(CFG_O, m->lpr_o, H);   // one tile per workgroup (residual epilogue)
-        m->lpr_gu = pick_lpr(nbH);
+        m->lpr_gu = pick_lpr(nbH, CFG_GU.lpr_max);
         m->grid_gu = gemv_grid(CFG_GU, m->lpr_gu, 2 * m->I);
         m->lpr_down = pick_lpr(m->I / 32);
         m->grid_down = gemv_grid(CFG_DOWN, m->lpr_down, H);   // one tile per workgroup
@@ -709,6 +718,8 @@ extern "C" int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const
         return fail(QD_EINVAL, "bad shape N=%d K=%d (K %% 32 must be 0)", N, K);
     if (gemv_lds_bytes(K / 32) > (size_t)GEMV_MAX_LDS)
         return fail(QD_EUNSUPPORTED, "K=%d above the staged-x limit", K);
+    if ((uint64_t)N * (uint64_t)K / 2 >= (uint64_t)1 << 32 || N >= (1 << 24))
+        return fail(QD_EUNSUPPORTED, "N=%d K=%d: above 2^32 bytes of nibbles or 2^24 rows", N, K);
     if ((reinterpret_cast<uintptr_t>(d_qs) | reinterpret_cast<uintptr_t>(d_x)) & 15)
         return fail(QD_EINVAL, "qs and x must be 16-byte aligned");
     if (N == 0)

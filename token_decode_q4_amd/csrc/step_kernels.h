@@ -181,7 +181,8 @@ struct EpiSwiglu {
             for (int r = 0; r < RPS; r += 2) {
                 if (row0 + r + 1 < N) {
                     const float gt = acc[r] * inv, up = acc[r + 1] * inv;
-                    act[(row0 + r) >> 1] = gt / (1.0f + expf(-gt)) * up;
+                    // silu(g) = g / (1 + e^-g); hardware reciprocal (about 1 ulp)
+                    act[(row0 + r) >> 1] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
                 }
             }
         }
@@ -222,7 +223,7 @@ struct EpiLmHead {
 
 // ----------------------------------------------------------------- GEMV kernels
 
-template <int LPR, int RPS, int NWAVES, int BG, int NBUF, bool NTL>
+template <int LPR, int RPS, int NWAVES, int BG, int NBUF, int UNR, bool NTL>
 __global__ void __launch_bounds__(NWAVES* WAVE)
 k_gemv_scaled(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
               const float* __restrict__ u, int N, int nb, const float* __restrict__ ss_part,
@@ -230,11 +231,11 @@ k_gemv_scaled(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
 {
     extern __shared__ float smem[];
     EpiScaled e{y, N, {ss_part, n_part}, n_in, eps_in};
-    gemv_run<LPR, RPS, NWAVES, BG, NBUF, NTL, false>(D, Q, u, N, nb, smem, smem + nb * XPAD, e);
+    gemv_run<LPR, RPS, NWAVES, BG, NBUF, UNR, NTL>(D, Q, u, N, nb, smem, smem + nb * XPAD, e);
     QD_MARK(3);
 }
 
-template <int LPR, int RPS, int NWAVES, int BG, int NBUF, bool NTL>
+template <int LPR, int RPS, int NWAVES, int BG, int NBUF, int UNR, bool NTL>
 __global__ void __launch_bounds__(NWAVES* WAVE)
 k_gemv_residual(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                 const float* __restrict__ a, int N, int nb, float* __restrict__ x,
@@ -244,14 +245,14 @@ k_gemv_residual(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
     extern __shared__ float smem[];
     __shared__ float red[8];
     EpiResidual<RPS> e{x, u, w_next, N, 0.f};
-    gemv_run<LPR, RPS, NWAVES, BG, NBUF, NTL, false>(D, Q, a, N, nb, smem, smem + nb * XPAD, e);
+    gemv_run<LPR, RPS, NWAVES, BG, NBUF, UNR, NTL>(D, Q, a, N, nb, smem, smem + nb * XPAD, e);
     const float ss = block_sum256(e.ss, red);
     if (threadIdx.x == 0)
         ss_part[blockIdx.x] = ss;
     QD_MARK(3);
 }
 
-template <int LPR, int RPS, int NWAVES, int BG, int NBUF, bool NTL>
+template <int LPR, int RPS, int NWAVES, int BG, int NBUF, int UNR, bool NTL>
 __global__ void __launch_bounds__(NWAVES* WAVE)
 k_gemv_swiglu(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
               const float* __restrict__ u, int N, int nb, const float* __restrict__ ss_part,
@@ -259,12 +260,12 @@ k_gemv_swiglu(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
 {
     extern __shared__ float smem[];
     EpiSwiglu e{act, N, {ss_part, n_part}, n_in, eps_in};
-    gemv_run<LPR, RPS, NWAVES, BG, NBUF, NTL, false>(D, Q, u, N, nb, smem, smem + nb * XPAD, e);
+    gemv_run<LPR, RPS, NWAVES, BG, NBUF, UNR, NTL>(D, Q, u, N, nb, smem, smem + nb * XPAD, e);
     QD_MARK(3);
 }
 
 // logits = W u / rms; each workgroup's best (value, lowest index among equals)
-template <int LPR, int RPS, int NWAVES, int BG, int NBUF, bool NTL>
+template <int LPR, int RPS, int NWAVES, int BG, int NBUF, int UNR, bool NTL>
 __global__ void __launch_bounds__(NWAVES* WAVE)
 k_gemv_lmhead(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
               const float* __restrict__ u, int N, int nb, const float* __restrict__ ss_part,
@@ -275,7 +276,7 @@ k_gemv_lmhead(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
     __shared__ float bv[NWAVES];
     __shared__ int32_t bi[NWAVES];
     EpiLmHead e{logits, N, {ss_part, n_part}, n_in, eps_in, 0.f, -INFINITY, 0x7fffffff};
-    gemv_run<LPR, RPS, NWAVES, BG, NBUF, NTL, false>(D, Q, u, N, nb, smem, smem + nb * XPAD, e);
+    gemv_run<LPR, RPS, NWAVES, BG, NBUF, UNR, NTL>(D, Q, u, N, nb, smem, smem + nb * XPAD, e);
     float best = e.best;
     int32_t bidx = e.bidx;
     const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
