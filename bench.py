@@ -9,10 +9,15 @@ decode first; warmup and timed steps are the greedy steps that follow
 
 Also reported, on the same JSON line:
   roofline      the q4_0 GEMV at the fused gate|up shape (24576 x 4096, the
-                step's dominant kernel) through qd_gemv_q4_0, timed with HIP
-                events on its own stream over >= 1 GiB of rotated weight copies
-                (no Infinity-Cache reuse); achieved = algorithmic bytes / mean
-                launch duration, against 8 TB/s.
+                step's largest kernel) through qd_gemv_q4_0 -- the same kernel
+                template and launch configuration as the step's gate|up GEMV --
+                100 launches over >= 1 GiB of rotated weight copies (no launch
+                hits the Infinity Cache) captured in one graph and timed with
+                HIP events on the replay stream; achieved = algorithmic bytes /
+                mean launch duration, against 8 TB/s.  traffic = HBM bytes per
+                launch from the committed rocprofv3 PMC record
+                (profiles/gemv_q4_0_24576x4096_traffic.md) while the kernel
+                sources still match it, else null.
   step_roofline the whole step's algorithmic bytes / measured step time.
   cpu_baseline  the f64 CPU oracle running decode steps of the same model on
                 the host cores (a bounded sample from position 0).
@@ -54,12 +59,48 @@ def step_bytes(s, kv_len: int) -> int:
     return L * per_layer + q4_bytes(V, H) + q4_bytes(1, H) + 4 * H + kv
 
 
+GEMV_SHAPE = (24576, 4096)   # the gate|up GEMV of the step, the largest per-layer kernel
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemv_q4_0_24576x4096_traffic.md")
+KERNEL_SOURCES = ["gemv_q4_0.h", "qd_common.h", "qd_api.hip"]
+
+
+def kernel_source_digest() -> str:
+    """SHA-256 over the sources that define the timed GEMV kernel and its launch."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "token_decode_q4_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch from the committed PMC record, if it was taken on the
+    kernel as it is now (same source digest); else None."""
+    try:
+        with open(TRAFFIC_RECORD) as fh:
+            for line in fh:
+                if line.startswith("traffic_record:"):
+                    rec = json.loads(line.split(":", 1)[1])
+                    if rec.get("kernel_src_sha256") == kernel_source_digest():
+                        return rec
+    except OSError:
+        pass
+    return None
+
+
 def gemv_roofline(reps: int = 100, min_bytes: int = 1 << 30):
-    """Mean duration of qd_gemv_q4_0 at 24576 x 4096 over rotated weight copies."""
+    """qd_gemv_q4_0 at 24576 x 4096 (config 2's gate|up shape, the same kernel
+    template and launch configuration as the step's gate|up GEMV): `reps`
+    launches over rotated weight copies (>= 1 GiB, so no launch hits the
+    Infinity Cache), captured in one graph and replayed; HIP events on the
+    replay stream give the mean launch duration.  Also runs one 1 GiB
+    device-to-device copy, the known-size reference for the PMC byte
+    counters."""
     import torch
     import synth
     import token_decode_q4_amd as qd
-    N, K = 24576, 4096
+    N, K = GEMV_SHAPE
     (W,), x = synth.gemv_case(synth.GEMV_SHAPES.index((N, K)))
     nbytes_w = W.d.nbytes + W.qs.nbytes
     copies = max(1, -(-min_bytes // nbytes_w))
@@ -74,20 +115,33 @@ def gemv_roofline(reps: int = 100, min_bytes: int = 1 << 30):
         for i in range(10):
             qd.gemv_q4_0(ds[i % copies], qs[i % copies], xt, y, stream=stream)
         stream.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(reps):
+                qd.gemv_q4_0(ds[i % copies], qs[i % copies], xt, y, stream=stream)
+        graph.replay()
+        stream.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(reps):
-            qd.gemv_q4_0(ds[i % copies], qs[i % copies], xt, y, stream=stream)
+        graph.replay()
         e1.record(stream)
         stream.synchronize()
+        # the known-size copy for the byte counters
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        stream.synchronize()
+        del src, dst, graph
     us = e0.elapsed_time(e1) * 1e3 / reps
     algo = N * K * 18 // 32 + 4 * K + 4 * N
     achieved = algo / (us * 1e-6) / 1e9
+    rec = stored_traffic()
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "k_gemv_plain (qd_gemv_q4_0) 24576x4096", "mean_us": round(us, 3),
-            "bytes_per_launch": algo, "weight_copies": copies}
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": rec["bytes_per_launch"] if rec else None,
+            "kernel": f"k_gemv_plain (qd_gemv_q4_0) {N}x{K}, graph of {reps} launches",
+            "mean_us": round(us, 3), "bytes_per_launch": algo, "weight_copies": copies}
 
 
 def cpu_baseline(mi, seconds: float = 15.0):
