@@ -51,6 +51,8 @@ struct AttnParams {
     int nsplit;
     float* part;               // [B][nq][nsplit][HD + 2]
     float* out;                // [B][nq][HD] (combine)
+    unsigned* counters;        // [B][nkv], zero between launches: when given, the last
+                               // workgroup of each (b, g) merges the partials itself
     // decode-step prologue (QMODE 1)
     int qk_norm;               // 1: per-head RMSNorm of q and k
     const float* q_norm;       // [HD] (valid even when qk_norm is 0)
@@ -81,6 +83,7 @@ struct alignas(16) AttnSmem {
     uint16_t knew[W][HD];           // per wave: the token's k in f16
     float m[W][GQ], l[W][GQ];
     float acc[W][GQ][HD];
+    int last;
 };
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -110,6 +113,67 @@ struct AttnStep {
     uint4 k[NI];
     uint32_t v[ATT_WK];                    // DPL f16 of key kk in the low (and high) half
 };
+
+// Merge of the split partials of one (sequence b, kv head g) by the last of
+// its workgroups to finish (the online-softmax rule of k_attn_combine).
+// Every workgroup's partial stores are agent-scope; each thread waits for its
+// own, the workgroup counts itself once with a relaxed agent-scope add, and the
+// one that completes the count reads all partials with agent-scope loads.
+// No fence is needed: no plain store is published this way.  The counter is
+// returned to zero for the next launch.
+template <int HD, int GQ>
+QD_DEV void attn_merge_last(const AttnParams& p, int b, int g, int kv_len, int* last)
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's partial stores are done
+    __syncthreads();
+    const int nact = (kv_len + p.chunk - 1) / p.chunk;
+    unsigned* cnt = p.counters + (size_t)b * p.nkv + g;
+    if (threadIdx.x == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *last = (prev + 1 == (unsigned)nact);
+    }
+    __syncthreads();
+    if (!*last)
+        return;
+    const size_t pstride = HD + 2;
+    constexpr int U = 8;
+    for (int i = threadIdx.x; i < GQ * HD; i += blockDim.x) {
+        const int j = i / HD, d = i % HD;
+        const int h = g * GQ + j;
+        const float* pp = p.part + ((size_t)b * p.nq + h) * p.nsplit * pstride;
+        float mt = -INFINITY, num = 0.f, den = 0.f;
+        for (int s0 = 0; s0 < nact; s0 += U) {
+            float a[U], mm[U], ll[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const size_t o = (size_t)min(s0 + u, nact - 1) * pstride;   // never a branch
+                a[u] = __hip_atomic_load(pp + o + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                mm[u] = __hip_atomic_load(pp + o + HD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ll[u] = __hip_atomic_load(pp + o + HD + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            float rm = mt;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (s0 + u < nact)
+                    rm = fmaxf(rm, mm[u]);
+            const float sc = (mt == -INFINITY) ? 0.f : expf(mt - rm);
+            num *= sc;
+            den *= sc;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (s0 + u < nact) {
+                    const float f = expf(mm[u] - rm);
+                    num = fmaf(f, a[u], num);
+                    den = fmaf(f, ll[u], den);
+                }
+            }
+            mt = rm;
+        }
+        p.out[((size_t)b * p.nq + h) * HD + d] = (den > 0.f) ? num / den : 0.f;
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // QMODE 0: q given (standalone); QMODE 1: decode-step prologue from raw q|k|v
 template <int HD, int GQ, bool PAGED, int QMODE>
@@ -449,6 +513,7 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
     QD_MARK(7);
     __syncthreads();
     const size_t pstride = HD + 2;
+    const bool fused = p.counters != nullptr;
     for (int i = tid; i < GQ * HD; i += nw * WAVE) {
         const int j = i / HD, d = i % HD;
         float M = sm.m[0][j];
@@ -462,12 +527,23 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
             A = fmaf(f, sm.acc[u][j][d], A);
         }
         float* pp = p.part + (((size_t)b * p.nq + h0 + j) * p.nsplit + s) * pstride;
-        pp[d] = A;
-        if (d == 0) {
-            pp[HD] = M;
-            pp[HD + 1] = L;
+        if (fused) {
+            // agent-scope stores: seen by the merging workgroup on any XCD
+            __hip_atomic_store(&pp[d], A, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (d == 0) {
+                __hip_atomic_store(&pp[HD], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&pp[HD + 1], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        } else {
+            pp[d] = A;
+            if (d == 0) {
+                pp[HD] = M;
+                pp[HD + 1] = L;
+            }
         }
     }
+    if (fused)
+        attn_merge_last<HD, GQ>(p, b, g, kv_len, &sm.last);
     QD_MARK(3);
 }
 

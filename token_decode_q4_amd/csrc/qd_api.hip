@@ -143,6 +143,7 @@ struct qd_model {
     float *rope_cos = nullptr, *rope_sin = nullptr;   // [max_seq][rot/2]
     float* rope_cur = nullptr;                        // cos, sin at the step's position
     float* ones_hd = nullptr;                         // [head_dim] of 1 (no q/k norm)
+    unsigned* attn_cnt = nullptr;                     // [n_kv] split counters, zero between steps
     int32_t* table = nullptr;
     // step buffers
     float *x = nullptr, *u = nullptr, *ss_part = nullptr, *qkv_raw = nullptr;
@@ -370,6 +371,8 @@ static void launch_attention(const AttnParams& p, int waves, int hd, int gq, boo
         else if (gq == 4) { QD_ATT(64, 4) } else { QD_ATT(64, 8) }
     }
 #undef QD_ATT
+    if (p.counters)
+        return;   // the split kernel merged the partials itself
     if (hd == 128)
         hipLaunchKernelGGL((k_attn_combine<128>), dim3(nq, B), dim3(ATT_CNT), 0, s, p.part,
                            p.nsplit, p.chunk, p.kv_lens, p.pos, p.max_kv, nq, p.out);
@@ -417,6 +420,7 @@ static int enqueue_step(qd_model* m, hipStream_t s)
             p.eps = m->eps;
             p.rot = m->rot;
             p.rope_cur = m->rope_cur;
+            p.counters = m->attn_cnt;
             p.kc = Ly.kc;
             p.vc = Ly.vc;
             launch_attention<1>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, 1, m->nq, s);
@@ -552,6 +556,10 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
         if ((rc = dev_alloc_t(m, &m->rope_cur, (size_t)2 * (half > 0 ? half : 1)))) return bail(rc);
         const std::vector<float> ones((size_t)m->hd, 1.f);
         if ((rc = upload_f32(m, &m->ones_hd, ones.data(), (size_t)m->hd, s))) return bail(rc);
+        if ((rc = dev_alloc_t(m, &m->attn_cnt, (size_t)m->nkv))) return bail(rc);
+        if (hipMemsetAsync(m->attn_cnt, 0, sizeof(unsigned) * m->nkv, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+            return bail(fail(QD_EHIP, "attention counter clear failed"));
     }
 
     // KV cache
