@@ -61,7 +61,7 @@ def step_bytes(s, kv_len: int) -> int:
 
 GEMV_SHAPE = (24576, 4096)   # the gate|up GEMV of the step, the largest per-layer kernel
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemv_q4_0_24576x4096_traffic.md")
-KERNEL_SOURCES = ["gemv_q4_0.h", "qd_common.h", "qd_api.hip"]
+KERNEL_SOURCES = ["gemv_q4_0.h", "qd_common.h", "gemv_cfg.h"]   # kernel + its launch configuration
 
 
 def kernel_source_digest() -> str:
