@@ -114,13 +114,59 @@ struct AttnStep {
     uint32_t v[ATT_WK];                    // DPL f16 of key kk in the low (and high) half
 };
 
+// Online-softmax merge of the split partials of the GQ heads of (sequence b,
+// kv head g), splits [0, nact), in rounds of U <= 64 splits:
+//   M = max_s m_s,  out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s.
+// A wave covers dims of one head (HD >= 64), so lane k loads (m, l) of split
+// s0 + k once for the whole wave and the weights e^(m_s - M) are read across
+// lanes; each lane loads its own dim of every split of the round.  All loads
+// of a round are issued before any is used (indexes clamped, never a branch).
+// Agent-scope loads: the partials come from other workgroups of this launch.
+template <int HD, int GQ, int U>
+QD_DEV void attn_merge_heads(const AttnParams& p, int b, int g, int nact)
+{
+    static_assert(U <= WAVE, "one split per lane");
+    const size_t pstride = HD + 2;
+    const int lane = threadIdx.x & (WAVE - 1);
+    // GQ * HD and blockDim.x are multiples of 64: a wave is wholly in or out
+    for (int i = threadIdx.x; i < GQ * HD; i += blockDim.x) {
+        const int j = i / HD, d = i % HD;
+        const int h = g * GQ + j;
+        const float* pp = p.part + ((size_t)b * p.nq + h) * p.nsplit * pstride;
+        float mt = -INFINITY, num = 0.f, den = 0.f;
+        for (int s0 = 0; s0 < nact; s0 += U) {
+            const int sl = min(s0 + lane, nact - 1);
+            const uint64_t ml = __hip_atomic_load(reinterpret_cast<const uint64_t*>(pp + sl * pstride + HD),
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            float a[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                a[u] = __hip_atomic_load(pp + (size_t)min(s0 + u, nact - 1) * pstride + d,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool act = s0 + lane < nact && lane < U;
+            const float m = act ? __uint_as_float((uint32_t)ml) : -INFINITY;
+            const float l = act ? __uint_as_float((uint32_t)(ml >> 32)) : 0.f;
+            const float rm = fmaxf(mt, group_max<WAVE>(m));
+            const float sc = (mt == -INFINITY) ? 0.f : expf(mt - rm);
+            const float f = (m == -INFINITY) ? 0.f : expf(m - rm);
+            den = fmaf(den, sc, group_sum<WAVE>(f * l));
+            num *= sc;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (s0 + u < nact)   // uniform
+                    num = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), u)), a[u], num);
+            mt = rm;
+        }
+        p.out[((size_t)b * p.nq + h) * HD + d] = (den > 0.f) ? num / den : 0.f;
+    }
+}
+
 // Merge of the split partials of one (sequence b, kv head g) by the last of
-// its workgroups to finish (the online-softmax rule of k_attn_combine).
-// Every workgroup's partial stores are agent-scope; each thread waits for its
-// own, the workgroup counts itself once with a relaxed agent-scope add, and the
-// one that completes the count reads all partials with agent-scope loads.
-// No fence is needed: no plain store is published this way.  The counter is
-// returned to zero for the next launch.
+// its workgroups to finish.  Every workgroup's partial stores are
+// agent-scope; each thread waits for its own, the workgroup counts itself once
+// with a relaxed agent-scope add, and the one that completes the count reads
+// all partials with agent-scope loads.  No fence is needed: no plain store is
+// published this way.  The counter is returned to zero for the next launch.
 template <int HD, int GQ>
 QD_DEV void attn_merge_last(const AttnParams& p, int b, int g, int kv_len, int* last)
 {
@@ -135,42 +181,14 @@ QD_DEV void attn_merge_last(const AttnParams& p, int b, int g, int kv_len, int* 
     __syncthreads();
     if (!*last)
         return;
-    const size_t pstride = HD + 2;
-    constexpr int U = 8;
-    for (int i = threadIdx.x; i < GQ * HD; i += blockDim.x) {
-        const int j = i / HD, d = i % HD;
-        const int h = g * GQ + j;
-        const float* pp = p.part + ((size_t)b * p.nq + h) * p.nsplit * pstride;
-        float mt = -INFINITY, num = 0.f, den = 0.f;
-        for (int s0 = 0; s0 < nact; s0 += U) {
-            float a[U], mm[U], ll[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const size_t o = (size_t)min(s0 + u, nact - 1) * pstride;   // never a branch
-                a[u] = __hip_atomic_load(pp + o + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                mm[u] = __hip_atomic_load(pp + o + HD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                ll[u] = __hip_atomic_load(pp + o + HD + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            float rm = mt;
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (s0 + u < nact)
-                    rm = fmaxf(rm, mm[u]);
-            const float sc = (mt == -INFINITY) ? 0.f : expf(mt - rm);
-            num *= sc;
-            den *= sc;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (s0 + u < nact) {
-                    const float f = expf(mm[u] - rm);
-                    num = fmaf(f, a[u], num);
-                    den = fmaf(f, ll[u], den);
-                }
-            }
-            mt = rm;
-        }
-        p.out[((size_t)b * p.nq + h) * HD + d] = (den > 0.f) ? num / den : 0.f;
-    }
+    // the merge is on the critical path of the step: one round of loads
+    // for up to 32 splits, sized to the active count
+    if (nact <= 8)
+        attn_merge_heads<HD, GQ, 8>(p, b, g, nact);
+    else if (nact <= 16)
+        attn_merge_heads<HD, GQ, 16>(p, b, g, nact);
+    else
+        attn_merge_heads<HD, GQ, 32>(p, b, g, nact);
     if (threadIdx.x == 0)
         __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

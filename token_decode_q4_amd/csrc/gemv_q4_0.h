@@ -314,7 +314,7 @@ __global__ void __launch_bounds__(NWAVES* WAVE)
 k_gemv_plain(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
              const float* __restrict__ x, float* __restrict__ y, int N, int nb)
 {
-    extern __shared__ float smem[];
+    extern __shared__ __align__(16) float smem[];   // 16-byte aligned: x is read as float4
     EpiStore e{y, N};
     gemv_run<LPR, RPS, NWAVES, BG, NBUF, UNR, NTL>(D, Q, x, N, nb, smem, smem + nb * XPAD, e);
 }

@@ -229,7 +229,7 @@ k_gemv_scaled(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
               const float* __restrict__ u, int N, int nb, const float* __restrict__ ss_part,
               int n_part, int n_in, float eps_in, float* __restrict__ y)
 {
-    extern __shared__ float smem[];
+    extern __shared__ __align__(16) float smem[];   // 16-byte aligned: x is read as float4
     EpiScaled e{y, N, {ss_part, n_part}, n_in, eps_in};
     gemv_run<LPR, RPS, NWAVES, BG, NBUF, UNR, NTL>(D, Q, u, N, nb, smem, smem + nb * XPAD, e);
     QD_MARK(3);
@@ -242,7 +242,7 @@ k_gemv_residual(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                 float* __restrict__ u, const float* __restrict__ w_next,
                 float* __restrict__ ss_part)
 {
-    extern __shared__ float smem[];
+    extern __shared__ __align__(16) float smem[];   // 16-byte aligned: x is read as float4
     __shared__ float red[8];
     EpiResidual<RPS> e{x, u, w_next, N, 0.f};
     gemv_run<LPR, RPS, NWAVES, BG, NBUF, UNR, NTL>(D, Q, a, N, nb, smem, smem + nb * XPAD, e);
@@ -258,7 +258,7 @@ k_gemv_swiglu(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
               const float* __restrict__ u, int N, int nb, const float* __restrict__ ss_part,
               int n_part, int n_in, float eps_in, float* __restrict__ act)
 {
-    extern __shared__ float smem[];
+    extern __shared__ __align__(16) float smem[];   // 16-byte aligned: x is read as float4
     EpiSwiglu e{act, N, {ss_part, n_part}, n_in, eps_in};
     gemv_run<LPR, RPS, NWAVES, BG, NBUF, UNR, NTL>(D, Q, u, N, nb, smem, smem + nb * XPAD, e);
     QD_MARK(3);
@@ -272,7 +272,7 @@ k_gemv_lmhead(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
               int n_part, int n_in, float eps_in, float* __restrict__ logits,
               float* __restrict__ part_val, int32_t* __restrict__ part_idx)
 {
-    extern __shared__ float smem[];
+    extern __shared__ __align__(16) float smem[];   // 16-byte aligned: x is read as float4
     __shared__ float bv[NWAVES];
     __shared__ int32_t bi[NWAVES];
     EpiLmHead e{logits, N, {ss_part, n_part}, n_in, eps_in, 0.f, -INFINITY, 0x7fffffff};
