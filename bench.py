@@ -144,6 +144,53 @@ def gemv_roofline(reps: int = 100, min_bytes: int = 1 << 30):
             "mean_us": round(us, 3), "bytes_per_launch": algo, "weight_copies": copies}
 
 
+def read_ceiling(nbytes: int, reps: int = 100, min_bytes: int = 1 << 30):
+    """The measured ceiling the GEMV is compared with: qd_stream_read (plain
+    128-bit non-temporal loads, nothing else) over `nbytes` per launch, the
+    GEMV leg's launch pattern (`reps` launches over rotated slices of >= 1 GiB,
+    one graph, HIP events on the replay stream); and one read of the whole
+    >= 1 GiB buffer per launch."""
+    import torch
+    import token_decode_q4_amd as qd
+    nbytes -= nbytes % 16
+    copies = max(1, -(-min_bytes // nbytes))
+    buf = torch.empty(copies * nbytes, dtype=torch.uint8, device="cuda")
+    buf.random_(0, 256)
+    sink = torch.empty(qd.stream_read_groups(copies * nbytes), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        for i in range(10):
+            qd.stream_read(buf[(i % copies) * nbytes:], sink, nbytes, stream=stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(reps):
+                qd.stream_read(buf[(i % copies) * nbytes:], sink, nbytes, stream=stream)
+        graph.replay()
+        stream.synchronize()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        stream.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        big = copies * nbytes
+        qd.stream_read(buf, sink, big, stream=stream)
+        e0.record(stream)
+        for _ in range(5):
+            qd.stream_read(buf, sink, big, stream=stream)
+        e1.record(stream)
+        stream.synchronize()
+        us_big = e0.elapsed_time(e1) * 1e3 / 5
+        del graph
+    del buf, sink
+    return {"kernel": f"k_stream_read (qd_stream_read), graph of {reps} launches",
+            "bytes_per_launch": nbytes, "mean_us": round(us, 3),
+            "achieved": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "achieved_one_launch_of": big, "achieved_one_launch": round(big / (us_big * 1e-6) / 1e9, 1),
+            "unit": "GB/s"}
+
+
 def cpu_baseline(mi, seconds: float = 15.0):
     """The oracle as it stands, decode steps of the same model from position 0."""
     import oracle
@@ -224,6 +271,12 @@ def main():
     if not args.no_roofline:
         roof = gemv_roofline()
         log(f"gemv roofline: {roof['mean_us']} us, {roof['achieved']} GB/s")
+        torch.cuda.empty_cache()
+        ceil = read_ceiling(roof["bytes_per_launch"])
+        roof["read_ceiling"] = ceil
+        roof["frac_of_read_ceiling"] = round(roof["achieved"] / ceil["achieved"], 4)
+        log(f"read ceiling: {ceil['mean_us']} us for {ceil['bytes_per_launch']} B, {ceil['achieved']} GB/s; "
+            f"{ceil['achieved_one_launch']} GB/s reading {ceil['achieved_one_launch_of']} B in one launch")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(mi)

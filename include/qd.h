@@ -185,6 +185,18 @@ size_t qd_attn_workspace_bytes(int32_t B, int32_t nq, int32_t nkv, int32_t head_
 int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t workspace_bytes,
                    qd_stream stream);
 
+/* Measurement utility, not a step of the decode path: the plain streaming
+ * read that the GEMV's bandwidth is compared with (its measured ceiling on
+ * the same part).  Reads d_src[0, bytes) once with 128-bit non-temporal
+ * loads; workgroup w writes the XOR of the 32-bit words it read to
+ * d_sink[w], so the XOR of all qd_stream_read_groups(bytes) sink words is the
+ * XOR of every word of the buffer.  bytes a positive multiple of 16, d_src
+ * 16-byte aligned (QD_EINVAL otherwise); d_sink holds
+ * qd_stream_read_groups(bytes) words (0 for an invalid size).  No
+ * allocation; capturable. */
+size_t qd_stream_read_groups(size_t bytes);
+int qd_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink, qd_stream stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* qd_last_error(void);
 

@@ -128,3 +128,17 @@ def test_create_rejects_null_weight(qd):
     h = C.c_void_p()
     assert qd.lib().qd_create(C.byref(cfg), C.byref(w), None, C.byref(h)) == qd._native.QD_EINVAL
     assert b"layer 1 wdown" in qd.lib().qd_last_error()
+
+
+def test_stream_read_validation(qd):
+    L = qd.lib()
+    p = C.c_void_p(16)
+    assert L.qd_stream_read(None, 64, p, None) == qd._native.QD_EINVAL
+    assert L.qd_stream_read(p, 0, p, None) == qd._native.QD_EINVAL
+    assert L.qd_stream_read(p, 40, p, None) == qd._native.QD_EINVAL
+    assert L.qd_stream_read(C.c_void_p(24), 64, p, None) == qd._native.QD_EINVAL
+    assert b"aligned" in L.qd_last_error()
+    assert qd.stream_read_groups(0) == 0 and qd.stream_read_groups(40) == 0
+    assert qd.stream_read_groups(16) == 1
+    assert qd.stream_read_groups(16 * 1024) == 1 and qd.stream_read_groups(16 * 1025) == 2
+    assert qd.stream_read_groups(1 << 30) == 2048

@@ -62,3 +62,33 @@ def test_gemv_repeat_is_bitwise_stable():
     a = _gemv(W, x)
     b = _gemv(W, x)
     assert np.array_equal(a, b)
+
+
+def test_gemv_k_zero_fills_zeros():
+    """K = 0: y = 0 (a fill kernel; no memset node, so it stays capturable)."""
+    import ctypes as C
+    import torch
+    import token_decode_q4_amd as qd
+    say("gemv K=0")
+    buf = torch.zeros(64, dtype=torch.float32, device="cuda")
+    y = torch.full((300,), float("nan"), dtype=torch.float32, device="cuda")
+    p = C.c_void_p(buf.data_ptr())
+    assert qd.lib().qd_gemv_q4_0(p, p, p, C.c_void_p(y.data_ptr()), 300, 0, None) == 0
+    assert np.array_equal(host(y), np.zeros(300, dtype=np.float32))
+
+
+@pytest.mark.parametrize("nbytes", [16, 16 * 1023, 16 * 1024 + 48, 16 * 4096 * 3 + 16, 56737792])
+def test_stream_read_xor(nbytes):
+    """The streaming-read utility reads every word once: the XOR of its sink
+    words equals the XOR of the buffer's 32-bit words (bit-exact)."""
+    import torch
+    import token_decode_q4_amd as qd
+    say(f"stream read {nbytes} B")
+    rng = np.random.default_rng(nbytes)
+    words = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint32)
+    src = torch.from_numpy(words.view(np.int32)).cuda()
+    g = qd.stream_read_groups(nbytes)
+    sink = torch.full((g,), -1, dtype=torch.int32, device="cuda")
+    qd.stream_read(src, sink)
+    got = np.bitwise_xor.reduce(host(sink).view(np.uint32))
+    assert got == np.bitwise_xor.reduce(words)

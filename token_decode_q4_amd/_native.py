@@ -19,7 +19,8 @@ QD_OK, QD_EINVAL, QD_ERANGE, QD_ENOMEM, QD_EUNSUPPORTED, QD_EHIP = 0, -1, -2, -3
 
 # every function declared in include/qd.h
 EXPORTS = ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate",
-           "qd_gemv_q4_0", "qd_attn_workspace_bytes", "qd_attn_decode", "qd_last_error")
+           "qd_gemv_q4_0", "qd_attn_workspace_bytes", "qd_attn_decode", "qd_stream_read_groups",
+           "qd_stream_read", "qd_last_error")
 
 
 class QdError(RuntimeError):
@@ -83,9 +84,12 @@ def lib():
         L.qd_attn_workspace_bytes.restype = C.c_size_t
         L.qd_attn_workspace_bytes.argtypes = [C.c_int32] * 5
         L.qd_attn_decode.argtypes = [C.POINTER(AttnArgs), C.c_void_p, C.c_size_t, C.c_void_p]
+        L.qd_stream_read_groups.restype = C.c_size_t
+        L.qd_stream_read_groups.argtypes = [C.c_size_t]
+        L.qd_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
         L.qd_last_error.restype = C.c_char_p
         for n in ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate",
-                  "qd_gemv_q4_0", "qd_attn_decode"):
+                  "qd_gemv_q4_0", "qd_attn_decode", "qd_stream_read"):
             getattr(L, n).restype = C.c_int
         _lib = L
     return _lib
@@ -118,6 +122,18 @@ def gemv_q4_0(d, qs, x, y, stream=None) -> int:
     N = d.shape[0]
     K = x.shape[0]
     return check(lib().qd_gemv_q4_0(_ptr(d), _ptr(qs), _ptr(x), _ptr(y), N, K, _stream(stream)))
+
+
+def stream_read_groups(nbytes: int) -> int:
+    return int(lib().qd_stream_read_groups(nbytes))
+
+
+def stream_read(src, sink, nbytes=None, stream=None) -> int:
+    """Streaming read of the device tensor src (all of it, or its first nbytes):
+    sink (device int32/uint32, stream_read_groups(nbytes) words) gets one XOR per
+    workgroup."""
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    return check(lib().qd_stream_read(_ptr(src), n, _ptr(sink), _stream(stream)))
 
 
 def attn_workspace_bytes(B, nq, nkv, head_dim, max_kv_len) -> int:

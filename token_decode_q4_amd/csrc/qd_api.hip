@@ -13,6 +13,7 @@
 
 #include "step_kernels.h"
 #include "gemv_cfg.h"
+#include "stream_read.h"
 
 #include <algorithm>
 #include <cmath>
@@ -665,6 +666,13 @@ extern "C" int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* 
 
 // ------------------------------------------------------------------ standalone kernels
 
+__global__ void k_fill_f32(float* __restrict__ y, int n, float v)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        y[i] = v;
+}
+
 extern "C" int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x,
                             float* d_y, int32_t N, int32_t K, qd_stream stream)
 {
@@ -680,8 +688,10 @@ extern "C" int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const
         return fail(QD_EINVAL, "qs and x must be 16-byte aligned");
     if (N == 0)
         return QD_OK;
-    if (K == 0) {
-        HIP_TRY(hipMemsetAsync(d_y, 0, sizeof(float) * (size_t)N, (hipStream_t)stream));
+    if (K == 0) {   // y = 0 by a fill kernel (no memset node inside a captured graph)
+        hipLaunchKernelGGL(k_fill_f32, dim3((N + 255) / 256), dim3(256), 0, (hipStream_t)stream, d_y, N,
+                           0.f);
+        HIP_TRY(hipGetLastError());
         return QD_OK;
     }
     HIP_TRY(launch_gemv_plain(d_scales, d_qs, d_x, d_y, N, K, (hipStream_t)stream));
@@ -756,6 +766,25 @@ extern "C" int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t w
     p.out = a->out;
     launch_attention<0>(p, geo.waves, a->head_dim, gq, a->block_tables != nullptr, a->B, a->nq,
                         (hipStream_t)stream);
+    HIP_TRY(hipGetLastError());
+    return QD_OK;
+}
+
+extern "C" size_t qd_stream_read_groups(size_t bytes)
+{
+    return (bytes < 16 || bytes % 16) ? 0 : (size_t)stream_read_groups(bytes);
+}
+
+extern "C" int qd_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink, qd_stream stream)
+{
+    if (!d_src || !d_sink)
+        return fail(QD_EINVAL, "null pointer");
+    if (bytes == 0 || bytes % 16)
+        return fail(QD_EINVAL, "bytes=%zu must be a positive multiple of 16", bytes);
+    if (reinterpret_cast<uintptr_t>(d_src) & 15)
+        return fail(QD_EINVAL, "src must be 16-byte aligned");
+    hipLaunchKernelGGL(k_stream_read, dim3(stream_read_groups(bytes)), dim3(SR_THREADS), 0,
+                       (hipStream_t)stream, reinterpret_cast<const uint4*>(d_src), bytes / 16, d_sink);
     HIP_TRY(hipGetLastError());
     return QD_OK;
 }
