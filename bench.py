@@ -218,10 +218,12 @@ def main():
     ap.add_argument("--config", default="qwen3-8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--layer-kernel", type=int, default=0,
+                    help="1: one persistent kernel launch per layer (qd_config.layer_kernel)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): batch-1 decode of one "
-              "model copy uses a single device; see DESIGN.md for how it would shard.",
+              "model copy uses a single device.",
               file=sys.stderr)
         sys.exit(2)
 
@@ -238,7 +240,7 @@ def main():
     if P - 1 + args.warmup + args.steps > s.max_seq:
         sys.exit(f"warmup + steps must be <= {s.max_seq - P + 1}")
     t0 = time.time()
-    model = qd.Model(mi, use_graph=True)
+    model = qd.Model(mi, use_graph=True, layer_kernel=bool(args.layer_kernel))
     log(f"qd_create {time.time() - t0:.1f}s")
     stream = torch.cuda.current_stream()
     toks = torch.empty(s.max_seq, dtype=torch.int32, device="cuda")
@@ -293,7 +295,8 @@ def main():
                    "layers": s.layers, "hidden": s.hidden, "heads": f"{s.n_heads}/{s.n_kv}",
                    "head_dim": s.head_dim, "intermediate": s.intermediate, "vocab": s.vocab,
                    "kv": "paged f16, block 16, shuffled table" if s.kv_paged else "contiguous f16",
-                   "batch": 1, "parallelism": "single GPU"},
+                   "batch": 1, "parallelism": "single GPU",
+                   "kernels": "one persistent launch per layer" if args.layer_kernel else "five per layer"},
         "step_roofline": {"bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
                           "bytes_per_step": round(mean_bytes)},

@@ -89,6 +89,14 @@ typedef struct {
  *            at create time, so a captured step never needs a table update.
  *   use_graph: 1 = one decode step is captured in a hipGraph at create time
  *            and replayed; 0 = the step's kernels are launched one by one.
+ *   layer_kernel: 0 = five kernels per layer (every model above);
+ *            1 = one persistent kernel launch per layer, one workgroup per
+ *            CU, device-wide barriers between the layer's phases.  It needs
+ *            head_dim 128, n_heads = 4 n_kv, hidden, intermediate and
+ *            n_heads*head_dim multiples of 2048 (at most 14 144), and a
+ *            device that keeps one 512-thread workgroup per CU resident;
+ *            QD_EUNSUPPORTED otherwise.  Same results up to f32 rounding
+ *            order (the RMSNorm partial sums are grouped differently).
  * Supported: head_dim 64 or 128; n_heads / n_kv in {1, 2, 4, 8};
  * kv_block_size 16; hidden, intermediate and n_heads*head_dim multiples of 32. */
 typedef struct {
@@ -102,6 +110,7 @@ typedef struct {
     int32_t kv_paged, kv_block_size, num_kv_blocks;
     const int32_t* block_table;
     int32_t use_graph;
+    int32_t layer_kernel;
 } qd_config;
 
 typedef struct qd_model qd_model;

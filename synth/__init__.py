@@ -71,6 +71,11 @@ MODELS = {
     # Qwen3-0.6B shape, contiguous KV; 512 prompt tokens + 256 greedy tokens
     "qwen3-0.6b": ModelShape("qwen3-0.6b", 4, 28, 1024, 16, 8, 128, 3072, 151936, True,
                              True, 1e6, 128, 1e-6, False, 768, 512, 256),
+    # two layers of the Qwen3-8B family's proportions that fit the persistent
+    # layer kernel (hidden 2048, 16/4 heads of 128, SwiGLU 6144), paged KV;
+    # 136 prompt tokens + 24 greedy tokens (two 128-key attention splits)
+    "layerk": ModelShape("layerk", 6, 2, 2048, 16, 4, 128, 6144, 4096, False, True, 1e6, 128,
+                         1e-6, True, 320, 136, 24),
     # Qwen3-8B shape, untied head, paged KV (block 16, shuffled table);
     # 2048 prompt tokens + 512 greedy tokens
     "qwen3-8b": ModelShape("qwen3-8b", 5, 36, 4096, 32, 8, 128, 12288, 151936, False,

@@ -142,3 +142,14 @@ def test_stream_read_validation(qd):
     assert qd.stream_read_groups(16) == 1
     assert qd.stream_read_groups(16 * 1024) == 1 and qd.stream_read_groups(16 * 1025) == 2
     assert qd.stream_read_groups(1 << 30) == 2048
+
+
+def test_create_rejects_layer_kernel_for_unfit_model(qd):
+    """layer_kernel = 1 needs head_dim 128, 4 query heads per kv head and K
+    multiples of 2048: the tiny model (head_dim 64) is refused before any HIP
+    call."""
+    mi = synth.make_model("tiny")
+    cfg, w, keep = _cfg_weights(qd, mi, layer_kernel=1)
+    h = C.c_void_p()
+    assert qd.lib().qd_create(C.byref(cfg), C.byref(w), None, C.byref(h)) == qd._native.QD_EUNSUPPORTED
+    assert b"layer_kernel" in qd.lib().qd_last_error()

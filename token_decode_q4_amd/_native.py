@@ -51,7 +51,7 @@ class Config(C.Structure):
                 ("inv_freq", C.c_void_p), ("tied", C.c_int32), ("qk_norm", C.c_int32),
                 ("max_seq", C.c_int32), ("kv_paged", C.c_int32), ("kv_block_size", C.c_int32),
                 ("num_kv_blocks", C.c_int32), ("block_table", C.c_void_p),
-                ("use_graph", C.c_int32)]
+                ("use_graph", C.c_int32), ("layer_kernel", C.c_int32)]
 
 
 class AttnArgs(C.Structure):
@@ -160,7 +160,8 @@ class Model:
     """A decode model built from host q4_0 weights (``synth.ModelInputs``-like)."""
 
     def __init__(self, mi, use_graph: bool = True, stream=None, paged: bool | None = None,
-                 max_seq: int | None = None, num_kv_blocks: int | None = None):
+                 max_seq: int | None = None, num_kv_blocks: int | None = None,
+                 layer_kernel: bool = False):
         s = mi.shape
         self.shape = s
         self.vocab = s.vocab
@@ -190,7 +191,8 @@ class Model:
         cfg = Config(s.hidden, s.layers, s.n_heads, s.n_kv, s.head_dim, s.intermediate, s.vocab,
                      float(s.eps), s.rot_dim, inv.ctypes.data, int(s.tied), int(s.qk_norm),
                      self.max_seq, int(bool(paged)), 16, nblocks,
-                     None if table is None else table.ctypes.data, int(bool(use_graph)))
+                     None if table is None else table.ctypes.data, int(bool(use_graph)),
+                     int(bool(layer_kernel)))
         h = C.c_void_p()
         check(lib().qd_create(C.byref(cfg), C.byref(w), _stream(stream), C.byref(h)))
         self._h = h

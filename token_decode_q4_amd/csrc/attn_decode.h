@@ -89,6 +89,24 @@ struct alignas(16) AttnSmem {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
+// float load: agent-scope (COH, a value another workgroup of the same launch
+// stored agent-scope) or plain
+template <bool COH>
+QD_DEV float ld_f32(const float* p)
+{
+    if (COH)
+        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return *p;
+}
+template <bool COH>
+QD_DEV void st_f32(float* p, float v)
+{
+    if (COH)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = v;
+}
+
 // LDS writes of this wave are seen by its later LDS reads (no workgroup barrier)
 QD_DEV void wave_lds_sync()
 {
@@ -122,7 +140,7 @@ struct AttnStep {
 // lanes; each lane loads its own dim of every split of the round.  All loads
 // of a round are issued before any is used (indexes clamped, never a branch).
 // Agent-scope loads: the partials come from other workgroups of this launch.
-template <int HD, int GQ, int U>
+template <int HD, int GQ, int U, bool COH>
 QD_DEV void attn_merge_heads(const AttnParams& p, int b, int g, int nact)
 {
     static_assert(U <= WAVE, "one split per lane");
@@ -157,7 +175,7 @@ QD_DEV void attn_merge_heads(const AttnParams& p, int b, int g, int nact)
                     num = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), u)), a[u], num);
             mt = rm;
         }
-        p.out[((size_t)b * p.nq + h) * HD + d] = (den > 0.f) ? num / den : 0.f;
+        st_f32<COH>(p.out + ((size_t)b * p.nq + h) * HD + d, (den > 0.f) ? num / den : 0.f);
     }
 }
 
@@ -167,7 +185,7 @@ QD_DEV void attn_merge_heads(const AttnParams& p, int b, int g, int nact)
 // with a relaxed agent-scope add, and the one that completes the count reads
 // all partials with agent-scope loads.  No fence is needed: no plain store is
 // published this way.  The counter is returned to zero for the next launch.
-template <int HD, int GQ>
+template <int HD, int GQ, bool COH>
 QD_DEV void attn_merge_last(const AttnParams& p, int b, int g, int kv_len, int* last)
 {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's partial stores are done
@@ -184,26 +202,29 @@ QD_DEV void attn_merge_last(const AttnParams& p, int b, int g, int kv_len, int* 
     // the merge is on the critical path of the step: one round of loads
     // for up to 32 splits, sized to the active count
     if (nact <= 8)
-        attn_merge_heads<HD, GQ, 8>(p, b, g, nact);
+        attn_merge_heads<HD, GQ, 8, COH>(p, b, g, nact);
     else if (nact <= 16)
-        attn_merge_heads<HD, GQ, 16>(p, b, g, nact);
+        attn_merge_heads<HD, GQ, 16, COH>(p, b, g, nact);
     else
-        attn_merge_heads<HD, GQ, 32>(p, b, g, nact);
+        attn_merge_heads<HD, GQ, 32, COH>(p, b, g, nact);
     if (threadIdx.x == 0)
         __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// QMODE 0: q given (standalone); QMODE 1: decode-step prologue from raw q|k|v
-template <int HD, int GQ, bool PAGED, int QMODE>
-__global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(AttnParams p)
+// The work of one split workgroup: (split s, kv head g, sequence b).
+// QMODE 0: q given (standalone); QMODE 1: decode-step prologue from raw q|k|v.
+// FUSED: inside the persistent layer kernel.  wait() runs after the first
+// step's K/V loads are issued (they need nothing of this step) and before
+// anything of this step's q|k|v is read; q|k|v are read and the merged output
+// is stored agent-scope (other workgroups of the same launch wrote / read them).
+template <int HD, int GQ, bool PAGED, int QMODE, bool FUSED, class Wait>
+QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<HD, GQ>& sm, Wait&& wait)
 {
     static_assert(HD == 64 || HD == 128, "head_dim");
     static_assert(GQ == 1 || GQ == 2 || GQ == 4 || GQ == 8, "group");
-    __shared__ AttnSmem<HD, GQ> sm;
     using Step = AttnStep<HD>;
     constexpr int NI = Step::NI, DPL = Step::DPL;
 
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const int nw = blockDim.x / WAVE;          // waves of this launch
     const int wstride = nw * ATT_WK;           // keys between a wave's steps
@@ -241,6 +262,16 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
         }
     };
 
+    Step cur_st;
+    const int tw0 = t_begin + w * ATT_WK;
+    if (FUSED) {
+        // K/V of the wave's first step before the wait: the cache rows below
+        // the position were written by earlier launches
+        load_step(cur_st, tw0);
+        asm volatile("" ::: "memory");   // keep these loads ahead of the wait
+        wait();
+    }
+
     // kv_len first (vector loads return in order): the loads below do not need
     // it.  One load from a selected address, so nothing waits for it here.
     const int32_t* kvp = p.kv_lens ? p.kv_lens + b : p.pos;
@@ -254,15 +285,15 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
         const int d = lane * DPL + e;
 #pragma unroll
         for (int j = 0; j < GQ; ++j)
-            qv[j][e] = (QMODE == 0) ? p.q[((size_t)b * p.nq + h0 + j) * HD + d]
-                                    : p.q[(size_t)(h0 + j) * HD + d];
+            qv[j][e] = (QMODE == 0) ? ld_f32<FUSED>(p.q + ((size_t)b * p.nq + h0 + j) * HD + d)
+                                    : ld_f32<FUSED>(p.q + (size_t)(h0 + j) * HD + d);
         kv_[e] = vv[e] = 0.f;
         wq[e] = wk[e] = cs[e] = 1.f;
         sn[e] = 0.f;
         if (QMODE == 1) {
             // q_norm / k_norm / rope_cur always point at valid arrays here
-            kv_[e] = p.q[((size_t)p.nq + g) * HD + d];
-            vv[e] = p.q[((size_t)p.nq + p.nkv + g) * HD + d];
+            kv_[e] = ld_f32<FUSED>(p.q + ((size_t)p.nq + g) * HD + d);
+            vv[e] = ld_f32<FUSED>(p.q + ((size_t)p.nq + p.nkv + g) * HD + d);
             wq[e] = p.q_norm[d];
             wk[e] = p.k_norm[d];
             const int half = p.rot / 2;
@@ -272,9 +303,8 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
             sn[e] = d < p.rot ? s0 : 0.f;
         }
     }
-    Step cur_st;
-    const int tw0 = t_begin + w * ATT_WK;
-    load_step(cur_st, tw0);
+    if (!FUSED)
+        load_step(cur_st, tw0);
 
     // ---- queries (and the token's k): per-head RMSNorm and rotary (QMODE 1),
     // times scale, into this wave's LDS rows.  None of it needs kv_len, so it
@@ -531,7 +561,7 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
     QD_MARK(7);
     __syncthreads();
     const size_t pstride = HD + 2;
-    const bool fused = p.counters != nullptr;
+    const bool merge_here = p.counters != nullptr;
     for (int i = tid; i < GQ * HD; i += nw * WAVE) {
         const int j = i / HD, d = i % HD;
         float M = sm.m[0][j];
@@ -545,7 +575,7 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
             A = fmaf(f, sm.acc[u][j][d], A);
         }
         float* pp = p.part + (((size_t)b * p.nq + h0 + j) * p.nsplit + s) * pstride;
-        if (fused) {
+        if (merge_here) {
             // agent-scope stores: seen by the merging workgroup on any XCD
             __hip_atomic_store(&pp[d], A, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (d == 0) {
@@ -560,9 +590,17 @@ __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(A
             }
         }
     }
-    if (fused)
-        attn_merge_last<HD, GQ>(p, b, g, kv_len, &sm.last);
+    if (merge_here)
+        attn_merge_last<HD, GQ, FUSED>(p, b, g, kv_len, &sm.last);
     QD_MARK(3);
+}
+
+template <int HD, int GQ, bool PAGED, int QMODE>
+__global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(AttnParams p)
+{
+    __shared__ AttnSmem<HD, GQ> sm;
+    attn_split_body<HD, GQ, PAGED, QMODE, false>(p, (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z, sm,
+                                                 [] {});
 }
 
 constexpr int ATT_CNT = 512;   // combine threads per head

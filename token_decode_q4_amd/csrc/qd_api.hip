@@ -11,7 +11,7 @@
 // and init_kv_cache_paged.)
 #include "qd.h"
 
-#include "step_kernels.h"
+#include "fused_layers.h"
 #include "gemv_cfg.h"
 #include "stream_read.h"
 
@@ -112,6 +112,13 @@ struct qd_model {
     hipGraphExec_t exec = nullptr;
     std::vector<void*> allocs;
     StepState* h_state = nullptr;  // pinned host staging
+    // persistent layer kernel (fused = 1): one workgroup per CU runs every layer
+    int fused = 0, fused_grid = 0, fused_nsplit = 0, fused_chunk = 0;
+    size_t fused_lds = 0;
+    FusedLayer* flayers = nullptr;   // device table [L]
+    unsigned* fbar = nullptr;        // barrier counters [FB_WORDS]
+    float *fX = nullptr, *fU = nullptr, *fSS = nullptr;   // [L+1] chains: x, u, sum-of-squares partials
+    int fss_stride = 0;
 };
 
 static int dev_alloc(qd_model* m, void** p, size_t bytes)
@@ -296,6 +303,16 @@ static int validate_config(const qd_config* c, const qd_weights* w)
         snprintf(nm, sizeof nm, "layer %d wdown", l);
         QD_TRY(check_q4(L.wdown, H, c->intermediate, nm));
     }
+    if (c->layer_kernel) {
+        const int nqd = c->n_heads * c->head_dim;
+        if (c->head_dim != 128 || c->n_heads != 4 * c->n_kv || c->hidden % 2048 || nqd % 2048 ||
+            c->intermediate % 2048)
+            return fail(QD_EUNSUPPORTED, "layer_kernel needs head_dim 128, n_heads = 4 n_kv and "
+                                         "hidden, intermediate, n_heads*head_dim multiples of 2048");
+        const int k_max = std::max(c->hidden, std::max(nqd, c->intermediate));
+        if (gemv_lds_bytes(k_max / 32) > (size_t)GEMV_MAX_LDS)
+            return fail(QD_EUNSUPPORTED, "layer_kernel: a GEMV's K (%d) is above 14 144", k_max);
+    }
     return QD_OK;
 }
 
@@ -331,12 +348,62 @@ static void launch_attention(const AttnParams& p, int waves, int hd, int gq, boo
 }
 
 // Enqueue one decode step (position and token come from the device state).
-static int enqueue_step(qd_model* m, hipStream_t s)
+static int enqueue_step_fused(qd_model* m, hipStream_t s)
 {
     const int H = m->H;
     hipLaunchKernelGGL(k_embed, dim3(m->grid_embed), dim3(256), 0, s, m->embed.d, m->embed.qs, H,
+                       m->V, m->st, m->ids, m->max_seq, m->layers[0].attn_norm, m->fX, m->fU,
+                       m->fSS, m->rope_cos, m->rope_sin, m->rot / 2, m->rope_cur, m->fbar, FB_WORDS);
+    FusedArgs a;
+    a.layers = m->flayers;
+    a.L = m->L;
+    a.H = H;
+    a.nq = m->nq;
+    a.nkv = m->nkv;
+    a.hd = m->hd;
+    a.I = m->I;
+    a.qkv_rows = m->qkv_rows;
+    a.eps = m->eps;
+    a.tables = m->paged ? m->table : nullptr;
+    a.mbps = (m->max_seq + ATT_BS - 1) / ATT_BS;
+    a.pos = &m->st->pos;
+    a.max_kv = m->max_seq;
+    a.scale = 1.0f / sqrtf((float)m->hd);
+    a.chunk = m->fused_chunk;
+    a.nsplit = m->fused_nsplit;
+    a.qk_norm = m->qk_norm;
+    a.rot = m->rot;
+    a.rope_cur = m->rope_cur;
+    a.bar = m->fbar;
+    a.err = &m->st->error;
+    for (int l = 0; l < m->L; ++l) {
+        if (m->paged)
+            hipLaunchKernelGGL((k_layer_fused<128, 4, true>), dim3(m->fused_grid), dim3(FUSED_THREADS),
+                               m->fused_lds, s, a, l);
+        else
+            hipLaunchKernelGGL((k_layer_fused<128, 4, false>), dim3(m->fused_grid), dim3(FUSED_THREADS),
+                               m->fused_lds, s, a, l);
+    }
+    const float* uL = m->fU + (size_t)m->L * H;
+    const float* ssL = m->fSS + (size_t)m->L * m->fss_stride;
+    QD_GEMV(k_gemv_lmhead, (QD_CFG_HEAD), m->lpr_lm, m->grid_lm, gemv_lds_bytes(m->lm.nb), s,
+                   m->lm.d, m->lm.qs, uL, m->lm.rows, m->lm.nb, ssL, m->fused_grid, H, m->eps,
+                   m->logits, m->arg_val, m->arg_idx);
+    hipLaunchKernelGGL(k_argmax_advance, dim3(1), dim3(256), 0, s, m->arg_val, m->arg_idx,
+                       m->grid_lm, m->V, m->st, m->ids, m->pred, m->max_seq);
+    HIP_TRY(hipGetLastError());
+    return QD_OK;
+}
+
+static int enqueue_step(qd_model* m, hipStream_t s)
+{
+    if (m->fused)
+        return enqueue_step_fused(m, s);
+    const int H = m->H;
+    hipLaunchKernelGGL(k_embed, dim3(m->grid_embed), dim3(256), 0, s, m->embed.d, m->embed.qs, H,
                        m->V, m->st, m->ids, m->max_seq, m->layers[0].attn_norm, m->x, m->u,
-                       m->ss_part, m->rope_cos, m->rope_sin, m->rot / 2, m->rope_cur);
+                       m->ss_part, m->rope_cos, m->rope_sin, m->rot / 2, m->rope_cur,
+                       (unsigned*)nullptr, 0);
     int n_part = m->grid_embed;
     for (int l = 0; l < m->L; ++l) {
         DevLayer& Ly = m->layers[l];
@@ -423,6 +490,82 @@ __global__ void k_set_state(StepState* st, int32_t* ids, int pos, int n_forced, 
         if (tok_pos >= 0)
             ids[tok_pos] = tok;
     }
+}
+
+// The persistent layer kernel (layer_kernel = 1) needs a model that fits its
+// instantiation: head_dim 128, 4 query heads per kv head, every GEMV's K a
+// multiple of 2048 and at most 14 144, one workgroup per CU resident, and the
+// attention splits (8 waves x 16 keys each, over max_seq) at most one per
+// workgroup.
+static int setup_fused(qd_model* m, hipStream_t s, int want)
+{
+    m->fused = 0;
+    if (!want)
+        return QD_OK;
+    const int H = m->H, nqd = m->nq * m->hd;   // shapes checked by validate_config
+    const int nb_max = std::max(H, std::max(nqd, m->I)) / 32;
+    int dev = 0, cus = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    const size_t lds = fused_lds_bytes<128, 4>(nb_max);
+    int per_cu = 0;
+    const void* kfn = m->paged ? (const void*)k_layer_fused<128, 4, true> : (const void*)k_layer_fused<128, 4, false>;
+    HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, FUSED_THREADS, lds));
+    if (per_cu < 1 || cus < 1)
+        return fail(QD_EUNSUPPORTED, "layer_kernel: a workgroup does not fit a CU");
+    const int G = cus;
+    const AttnGeom ag = attn_geom(1, m->nkv, m->max_seq, G, FUSED_WAVES, FUSED_WAVES);
+    if (ag.nsplit * m->nkv > G)
+        return fail(QD_EUNSUPPORTED, "layer_kernel: %d attention splits for %d workgroups",
+                    ag.nsplit * m->nkv, G);
+    m->fused_grid = G;
+    m->fused_lds = lds;
+    m->fused_nsplit = ag.nsplit;
+    m->fused_chunk = ag.chunk;
+    m->fss_stride = std::max(G, m->grid_embed);
+    const int L = m->L;
+    int rc;
+    if ((rc = dev_alloc_t(m, &m->fbar, FB_WORDS)) || (rc = dev_alloc_t(m, &m->fX, (size_t)(L + 1) * H)) ||
+        (rc = dev_alloc_t(m, &m->fU, (size_t)(L + 1) * H)) ||
+        (rc = dev_alloc_t(m, &m->fSS, (size_t)(L + 1) * m->fss_stride)) ||
+        (rc = dev_alloc_t(m, &m->flayers, (size_t)L)))
+        return rc;
+    std::vector<FusedLayer> t(L);
+    for (int l = 0; l < L; ++l) {
+        DevLayer& D = m->layers[l];
+        FusedLayer& F = t[l];
+        F.qkv_d = D.qkv.d; F.qkv_q = D.qkv.qs;
+        F.o_d = D.o.d; F.o_q = D.o.qs;
+        F.gu_d = D.gu.d; F.gu_q = D.gu.qs;
+        F.down_d = D.down.d; F.down_q = D.down.qs;
+        F.ffn_norm = D.ffn_norm;
+        F.w_next = (l + 1 < L) ? m->layers[l + 1].attn_norm : m->final_norm;
+        F.q_norm = m->qk_norm ? D.q_norm : m->ones_hd;
+        F.k_norm = m->qk_norm ? D.k_norm : m->ones_hd;
+        F.kc = D.kc;
+        F.vc = D.vc;
+        F.x_in = m->fX + (size_t)l * H;
+        F.u_in = m->fU + (size_t)l * H;
+        F.ss_in = m->fSS + (size_t)l * m->fss_stride;
+        F.n_in = l == 0 ? m->grid_embed : G;
+        F.x_out = m->fX + (size_t)(l + 1) * H;
+        F.u_out = m->fU + (size_t)(l + 1) * H;
+        F.ss_out = m->fSS + (size_t)(l + 1) * m->fss_stride;
+        if ((rc = dev_alloc_t(m, &F.qkv, m->qkv_rows)) ||
+            (rc = dev_alloc_t(m, &F.part, (size_t)m->nq * ag.nsplit * (m->hd + 2))) ||
+            (rc = dev_alloc_t(m, &F.att, nqd)) || (rc = dev_alloc_t(m, &F.xm, H)) ||
+            (rc = dev_alloc_t(m, &F.um, H)) || (rc = dev_alloc_t(m, &F.ssa, G)) ||
+            (rc = dev_alloc_t(m, &F.act, m->I)) || (rc = dev_alloc_t(m, &F.cnt, m->nkv)))
+            return rc;
+        if (hipMemsetAsync(F.cnt, 0, sizeof(unsigned) * m->nkv, s) != hipSuccess)
+            return fail(QD_EHIP, "fused counter clear failed");
+    }
+    if (hipMemcpyAsync(m->flayers, t.data(), sizeof(FusedLayer) * L, hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipMemsetAsync(m->fbar, 0, sizeof(unsigned) * FB_WORDS, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return fail(QD_EHIP, "fused layer table upload failed");
+    m->fused = 1;
+    return QD_OK;
 }
 
 extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream stream, qd_model** out)
@@ -572,6 +715,8 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
         hipMemsetAsync(m->pred, 0, sizeof(int32_t) * m->max_seq, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)
         return bail(fail(QD_EHIP, "step buffer clear failed"));
+    if ((rc = setup_fused(m, s, c.layer_kernel)))
+        return bail(rc);
 
     // graph of one step
     if (m->use_graph) {

@@ -57,15 +57,21 @@ QD_DEV float block_sum256(float v, float* red /* >= 4 floats */)
 
 // grid ceil(H/256): one element per thread; per-workgroup sum of x^2.
 // Workgroup 0 also copies the rotary factors of the step's position from the
-// tables [max_seq][half] to rope_cur (cos [half] then sin [half]).
+// tables [max_seq][half] to rope_cur (cos [half] then sin [half]), and zeroes
+// the n_zero words at zero_words (the persistent layer kernel's barrier
+// counters; nothing when n_zero is 0).
 __global__ void __launch_bounds__(256)
 k_embed(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, int H, int vocab,
         StepState* __restrict__ st, const int32_t* __restrict__ ids, int max_seq,
         const float* __restrict__ w_norm, float* __restrict__ x, float* __restrict__ u,
         float* __restrict__ ss_part, const float* __restrict__ rope_cos,
-        const float* __restrict__ rope_sin, int half, float* __restrict__ rope_cur)
+        const float* __restrict__ rope_sin, int half, float* __restrict__ rope_cur,
+        unsigned* __restrict__ zero_words, int n_zero)
 {
     __shared__ float red[8];
+    if (blockIdx.x == 0)
+        for (int k = threadIdx.x; k < n_zero; k += blockDim.x)
+            zero_words[k] = 0u;
     int pos = st->pos;
     if (pos < 0 || pos >= max_seq) {
         if (threadIdx.x == 0 && blockIdx.x == 0) st->error |= 2;
