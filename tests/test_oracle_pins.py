@@ -259,6 +259,41 @@ def test_attention_gqa_equals_repeated_mha(oracle_lib):
     assert np.array_equal(g, m)
 
 
+def test_split_kv_merge_equals_unsplit(oracle_lib):
+    """The split-KV combine rule (inferencelayer cuda_llm.rs page, attn_reduce;
+    ferrum-kernels cuda_decode.rs page, flash_decode_attention phase 2): the
+    oracle's attention over each key range s, with its range max m_s and
+    softmax denominator l_s, merged as
+        out = sum_s e^(m_s - M) l_s out_s / sum_s e^(m_s - M) l_s,  M = max m_s,
+    equals the oracle's attention over the whole range, for uneven splits."""
+    rng = np.random.default_rng(31)
+    hd, nq, nkv, n = 64, 4, 2, 203
+    scale = 1 / np.sqrt(hd)
+    q = rng.standard_normal((1, nq, hd)).astype(np.float32)
+    k = _f16(rng.standard_normal((1, nkv, n, hd)) * 2.0)
+    v = _f16(rng.standard_normal((1, nkv, n, hd)))
+    full = oracle_lib.attn_decode(q, k, v, [n], nkv, scale, contig_max_kv=n)[0]
+    kf = k.view(np.float16).astype(np.float64)[0]
+    for cuts in ([0, 64, 128, 192, n], [0, 1, 2, 150, n], [0, 100, n]):
+        num = np.zeros((nq, hd))
+        den = np.zeros(nq)
+        ms, ls, outs = [], [], []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            ks = np.ascontiguousarray(k[:, :, a:b])
+            vs = np.ascontiguousarray(v[:, :, a:b])
+            outs.append(oracle_lib.attn_decode(q, ks, vs, [b - a], nkv, scale, contig_max_kv=b - a)[0])
+            sc = np.stack([scale * kf[h // (nq // nkv), a:b] @ q[0, h].astype(np.float64) for h in range(nq)])
+            m = sc.max(axis=1)
+            ms.append(m)
+            ls.append(np.exp(sc - m[:, None]).sum(axis=1))
+        M = np.max(ms, axis=0)
+        for m, l, o in zip(ms, ls, outs):
+            f = np.exp(m - M) * l
+            num += f[:, None] * o
+            den += f
+        assert np.allclose(num / den[:, None], full, rtol=1e-13, atol=1e-14)
+
+
 # ----------------------------------------------------------------- greedy
 
 def test_greedy_lowest_index_on_ties(oracle_lib):
