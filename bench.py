@@ -265,6 +265,7 @@ def main():
     mean_bytes = float(np.mean([step_bytes(s, int(k)) for k in kv_lens]))
     step_gbs = mean_bytes / (ms * 1e-3 / args.steps) / 1e9
     log(f"decode {args.steps} steps: {ms:.2f} ms, {tok_s:.1f} tok/s, {step_gbs:.0f} GB/s")
+    model.check()   # raises if the device recorded an error during the run
     model.close()
     del model
     torch.cuda.empty_cache()

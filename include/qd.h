@@ -194,6 +194,14 @@ size_t qd_attn_workspace_bytes(int32_t B, int32_t nq, int32_t nkv, int32_t head_
 int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t workspace_bytes,
                    qd_stream stream);
 
+/* Synchronises `stream` and reports what the device recorded since the last
+ * check, then clears it: QD_ERANGE if a step saw a token or a position out of
+ * range (a stored token or position the host did not validate), QD_EHIP if a
+ * device-wide barrier of the layer kernel (layer_kernel = 1) gave up waiting,
+ * in which case the steps since the last check are invalid; QD_OK otherwise.
+ * Blocks the host; not capturable. */
+int qd_check(qd_model* m, qd_stream stream);
+
 /* Measurement utility, not a step of the decode path: the plain streaming
  * read that the GEMV's bandwidth is compared with (its measured ceiling on
  * the same part).  Reads d_src[0, bytes) once with 128-bit non-temporal

@@ -104,3 +104,26 @@ def test_layer_kernel_graph_equals_eager_bitwise(lk):
         m.close()
     assert np.array_equal(res[0][0], res[1][0])
     assert np.array_equal(res[0][1], res[1][1])
+
+
+def test_layer_kernel_barrier_timeout_is_reported(lk, monkeypatch):
+    """A barrier that gives up waiting (forced from the host with a spin bound
+    of 0 polls; every wait still ends) is reported by qd_check, and a model
+    with the normal bound reports nothing."""
+    import token_decode_q4_amd as qd
+    P = lk.shape.prompt_len
+    monkeypatch.setenv("QD_LAYER_KERNEL_SPIN_LIMIT", "0")
+    m = qd.Model(lk, use_graph=True, layer_kernel=True)
+    monkeypatch.delenv("QD_LAYER_KERNEL_SPIN_LIMIT")
+    m.set_prompt(lk.prompt)
+    m.generate(0, 8)
+    with pytest.raises(qd.QdError) as ei:
+        m.check()
+    assert ei.value.code == qd._native.QD_EHIP and "barrier" in str(ei.value)
+    m.check()   # cleared
+    m.close()
+    m = qd.Model(lk, use_graph=True, layer_kernel=True)
+    m.set_prompt(lk.prompt)
+    m.generate(0, P - 1)
+    m.check()
+    m.close()

@@ -151,6 +151,7 @@ def _golden_run(name, layer_kernel=False):
                 got_logits[points[stop]] = host(lg).copy()
         say(f"{name}: reached position {pos}")
     all_toks = host(toks)
+    m.check()
     m.close()
     greedy = all_toks[P - 1:]
     n_eq = check_greedy(greedy, g["tokens"], g["margins"], name)

@@ -19,8 +19,8 @@ QD_OK, QD_EINVAL, QD_ERANGE, QD_ENOMEM, QD_EUNSUPPORTED, QD_EHIP = 0, -1, -2, -3
 
 # every function declared in include/qd.h
 EXPORTS = ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate",
-           "qd_gemv_q4_0", "qd_attn_workspace_bytes", "qd_attn_decode", "qd_stream_read_groups",
-           "qd_stream_read", "qd_last_error")
+           "qd_gemv_q4_0", "qd_attn_workspace_bytes", "qd_attn_decode", "qd_check",
+           "qd_stream_read_groups", "qd_stream_read", "qd_last_error")
 
 
 class QdError(RuntimeError):
@@ -84,12 +84,13 @@ def lib():
         L.qd_attn_workspace_bytes.restype = C.c_size_t
         L.qd_attn_workspace_bytes.argtypes = [C.c_int32] * 5
         L.qd_attn_decode.argtypes = [C.POINTER(AttnArgs), C.c_void_p, C.c_size_t, C.c_void_p]
+        L.qd_check.argtypes = [C.c_void_p, C.c_void_p]
         L.qd_stream_read_groups.restype = C.c_size_t
         L.qd_stream_read_groups.argtypes = [C.c_size_t]
         L.qd_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
         L.qd_last_error.restype = C.c_char_p
         for n in ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate",
-                  "qd_gemv_q4_0", "qd_attn_decode", "qd_stream_read"):
+                  "qd_gemv_q4_0", "qd_attn_decode", "qd_check", "qd_stream_read"):
             getattr(L, n).restype = C.c_int
         _lib = L
     return _lib
@@ -209,6 +210,11 @@ class Model:
     def generate(self, pos0: int, n_steps: int, tokens=None, logits_last=None, stream=None):
         return check(lib().qd_generate(self._h, int(pos0), int(n_steps), _ptr(tokens),
                                        _ptr(logits_last), _stream(stream)))
+
+    def check(self, stream=None):
+        """Synchronise and raise QdError if the device recorded an error since
+        the last check (qd_check)."""
+        return check(lib().qd_check(self._h, _stream(stream)))
 
     def close(self):
         if getattr(self, "_h", None):

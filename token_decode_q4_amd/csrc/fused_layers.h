@@ -63,6 +63,7 @@ struct FusedBarrier {
     unsigned* ctr;
     int32_t* err;
     int* broken;   // LDS flag of this workgroup
+    int spin_limit;
     QD_DEV void arrive() const
     {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's stores are done
@@ -84,7 +85,7 @@ struct FusedBarrier {
                 const unsigned v = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (__all(v >= target))
                     break;
-                if (spins >= FB_SPIN_LIMIT) {
+                if (spins >= spin_limit) {
                     if (threadIdx.x == 0) {
                         *broken = 1;
                         __hip_atomic_fetch_or(err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -368,6 +369,7 @@ struct FusedArgs {
     const float* rope_cur;
     unsigned* bar;
     int32_t* err;
+    int spin_limit;   // polls before a wait gives up (FB_SPIN_LIMIT)
 };
 
 // GEMV configurations of the phases (LPR, RPS, block group, buffers, unroll):
@@ -399,7 +401,7 @@ __global__ void __launch_bounds__(FUSED_THREADS) k_layer_fused(FusedArgs a, int 
     if (threadIdx.x == 0)
         broken = 0;
     __syncthreads();
-    const FusedBarrier bar{a.bar, a.err, &broken};
+    const FusedBarrier bar{a.bar, a.err, &broken, a.spin_limit};
     const unsigned nbar0 = 4u * (unsigned)l;
     unsigned nbar = nbar0;   // barriers completed before the phase to come
     int phase = 0;   // marks 3 phase (entry), 3 phase + 1 (after the wait), 3 phase + 2 (end)

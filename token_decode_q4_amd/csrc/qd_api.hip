@@ -18,6 +18,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -119,6 +120,7 @@ struct qd_model {
     unsigned* fbar = nullptr;        // barrier counters [FB_WORDS]
     float *fX = nullptr, *fU = nullptr, *fSS = nullptr;   // [L+1] chains: x, u, sum-of-squares partials
     int fss_stride = 0;
+    int fused_spin = FB_SPIN_LIMIT;
 };
 
 static int dev_alloc(qd_model* m, void** p, size_t bytes)
@@ -376,6 +378,7 @@ static int enqueue_step_fused(qd_model* m, hipStream_t s)
     a.rope_cur = m->rope_cur;
     a.bar = m->fbar;
     a.err = &m->st->error;
+    a.spin_limit = m->fused_spin;
     for (int l = 0; l < m->L; ++l) {
         if (m->paged)
             hipLaunchKernelGGL((k_layer_fused<128, 4, true>), dim3(m->fused_grid), dim3(FUSED_THREADS),
@@ -520,6 +523,9 @@ static int setup_fused(qd_model* m, hipStream_t s, int want)
                     ag.nsplit * m->nkv, G);
     m->fused_grid = G;
     m->fused_lds = lds;
+    // testing only: a smaller bound on the barrier polls (forces the timeout path)
+    if (const char* e = getenv("QD_LAYER_KERNEL_SPIN_LIMIT"))
+        m->fused_spin = std::max(0, atoi(e));
     m->fused_nsplit = ag.nsplit;
     m->fused_chunk = ag.chunk;
     m->fss_stride = std::max(G, m->grid_embed);
@@ -913,6 +919,23 @@ extern "C" int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t w
                         (hipStream_t)stream);
     HIP_TRY(hipGetLastError());
     return QD_OK;
+}
+
+extern "C" int qd_check(qd_model* m, qd_stream stream)
+{
+    if (!m)
+        return fail(QD_EINVAL, "null model");
+    HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
+    int32_t err = 0;
+    HIP_TRY(hipMemcpy(&err, &m->st->error, sizeof err, hipMemcpyDeviceToHost));
+    if (err == 0)
+        return QD_OK;
+    const int32_t zero = 0;
+    HIP_TRY(hipMemcpy(&m->st->error, &zero, sizeof zero, hipMemcpyHostToDevice));
+    if (err & 4)
+        return fail(QD_EHIP, "a device-wide barrier of the layer kernel timed out: the steps since "
+                             "the last check are invalid");
+    return fail(QD_ERANGE, "a step saw a %s out of range", (err & 1) ? "token" : "position");
 }
 
 extern "C" size_t qd_stream_read_groups(size_t bytes)
