@@ -52,7 +52,15 @@ extern "C" const char* qd_last_error(void) { return g_err.c_str(); }
 
 // ------------------------------------------------------------------ GEMV launch
 
-static constexpr int ATT_MODEL_WGS = 160;   // attention workgroups of a decode step (measured best)
+// attention workgroups of a decode step and the most waves per workgroup
+// (measured best on MI355X; compile-time overridable for tuning builds)
+#ifndef QD_ATT_MODEL_WGS
+#define QD_ATT_MODEL_WGS 160
+#endif
+#ifndef QD_ATT_MODEL_WAVES
+#define QD_ATT_MODEL_WAVES 8
+#endif
+static constexpr int ATT_MODEL_WGS = QD_ATT_MODEL_WGS;
 
 static hipError_t launch_gemv_plain(const uint16_t* d, const uint8_t* q, const float* x, float* y,
                                     int N, int K, hipStream_t s)
@@ -695,11 +703,10 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
         m->grid_down = gemv_grid(CFG_DOWN, m->lpr_down, H);   // one tile per workgroup
         m->lpr_lm = pick_lpr(nbH);
         m->grid_lm = gemv_grid(CFG_HEAD, m->lpr_lm, m->V);
-        // attention: 64-key splits over max_seq, so the grid does not depend on the position
         // attention: splits over max_seq (the grid does not depend on the position),
         // about one workgroup per CU
         const int gq = m->nq / m->nkv;
-        const AttnGeom ag = attn_geom(1, m->nkv, m->max_seq, ATT_MODEL_WGS, gq <= 4 ? 8 : 4, 0);
+        const AttnGeom ag = attn_geom(1, m->nkv, m->max_seq, ATT_MODEL_WGS, gq <= 4 ? QD_ATT_MODEL_WAVES : 4, 0);
         m->attn_waves = ag.waves;
         m->attn_chunk = ag.chunk;
         m->attn_nsplit = ag.nsplit;
