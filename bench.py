@@ -22,7 +22,13 @@ Also reported, on the same JSON line:
   cpu_baseline  the f64 CPU oracle running decode steps of the same model on
                 the host cores (a bounded sample from position 0).
 
-Usage: python bench.py [--gpus 1] [--steps 448] [--warmup 16]
+  rows          per-row measurements: the isolated GEMV at the five sweep
+                shapes and the isolated attention at the four cases (graphs of
+                100 launches over >= 1 GiB of rotated copies, each output
+                checked against the f64 oracle, the oracle's host time beside
+                it), and greedy decode at the Qwen3-0.6B shape.
+
+Usage: python bench.py [--gpus 1] [--steps 448] [--warmup 16] [--no-rows]
 """
 from __future__ import annotations
 
@@ -111,37 +117,200 @@ def gemv_roofline(reps: int = 100, min_bytes: int = 1 << 30):
     xt = torch.from_numpy(x).cuda()
     y = torch.empty(N, dtype=torch.float32, device="cuda")
     stream = torch.cuda.Stream()
+    us = _graph_time(stream, lambda i: qd.gemv_q4_0(ds[i % copies], qs[i % copies], xt, y,
+                                                    stream=stream), reps)
     with torch.cuda.stream(stream):
-        for i in range(10):
-            qd.gemv_q4_0(ds[i % copies], qs[i % copies], xt, y, stream=stream)
-        stream.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(reps):
-                qd.gemv_q4_0(ds[i % copies], qs[i % copies], xt, y, stream=stream)
-        graph.replay()
-        stream.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        graph.replay()
-        e1.record(stream)
-        stream.synchronize()
         # the known-size copy for the byte counters
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         stream.synchronize()
-        del src, dst, graph
-    us = e0.elapsed_time(e1) * 1e3 / reps
+        del src, dst
     algo = N * K * 18 // 32 + 4 * K + 4 * N
     achieved = algo / (us * 1e-6) / 1e9
     rec = stored_traffic()
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": rec["bytes_per_launch"] if rec else None,
-            "kernel": f"k_gemv_plain (qd_gemv_q4_0) {N}x{K}, graph of {reps} launches",
+            "kernel": f"k_gemv_plain (qd_gemv_q4_0) {N}x{K}, graph of {reps} launches "
+                      f"replayed {TIMED_REPLAYS} times",
             "mean_us": round(us, 3), "bytes_per_launch": algo, "weight_copies": copies}
+
+
+TIMED_REPLAYS = 5
+
+
+def _graph_time(stream, launch, reps: int, replays: int = TIMED_REPLAYS) -> float:
+    """Mean microseconds per launch: 10 warm-up launches, then `reps` launches
+    captured in one graph, replayed once untimed and then `replays` times back
+    to back between two HIP events on the replay stream (the mean over
+    reps x replays launches)."""
+    import torch
+    with torch.cuda.stream(stream):
+        for i in range(10):
+            launch(i)
+        stream.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(reps):
+                launch(i)
+        graph.replay()
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(replays):
+            graph.replay()
+        e1.record(stream)
+        stream.synchronize()
+        del graph
+    return e0.elapsed_time(e1) * 1e3 / (reps * replays)
+
+
+def _timed(fn, reps: int = 3):
+    """(best wall seconds of `reps` calls, the last result)"""
+    best, r = float("inf"), None
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        r = fn()
+        best = min(best, time.perf_counter() - t0)
+    return best, r
+
+
+def gemv_sweep_rows(reps: int = 100, min_bytes: int = 1 << 30):
+    """The isolated q4_0 GEMV at the five sweep shapes through qd_gemv_q4_0:
+    `reps` launches over >= 1 GiB of rotated weight copies in one graph (no
+    launch hits the Infinity Cache); the output of the first launch against
+    the f64 oracle (normwise error); the oracle's own time on the host cores
+    (best of 3), as GB/s of the same algorithmic bytes."""
+    import torch
+    import oracle
+    import synth
+    import token_decode_q4_amd as qd
+    rows, tot_bytes, tot_us = [], 0, 0.0
+    for i, (N, K) in enumerate(synth.GEMV_SHAPES):
+        (W,), x = synth.gemv_case(i)
+        copies = max(1, -(-min_bytes // (W.d.nbytes + W.qs.nbytes)))
+        d0 = torch.from_numpy(W.d.view(np.int16)).cuda()
+        q0 = torch.from_numpy(W.qs).cuda()
+        ds = [d0] + [d0.clone() for _ in range(copies - 1)]
+        qs = [q0] + [q0.clone() for _ in range(copies - 1)]
+        xt = torch.from_numpy(x).cuda()
+        y = torch.empty(N, dtype=torch.float32, device="cuda")
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            qd.gemv_q4_0(d0, q0, xt, y, stream=stream)
+        stream.synchronize()
+        got = y.cpu().numpy().astype(np.float64)
+        t_or, ref = _timed(lambda: oracle.gemv(W, x))
+        err = float(np.max(np.abs(got - ref)) / max(1e-300, float(np.max(np.abs(ref)))))
+        us = _graph_time(stream, lambda k: qd.gemv_q4_0(ds[k % copies], qs[k % copies], xt, y,
+                                                        stream=stream), reps)
+        algo = N * K * 18 // 32 + 4 * K + 4 * N
+        gbs = algo / (us * 1e-6) / 1e9
+        rows.append({"shape": f"{N}x{K}", "mean_us": round(us, 3), "achieved": round(gbs, 1),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": algo,
+                     "weight_copies": copies, "normwise_err_vs_oracle": err,
+                     "oracle_s": round(t_or, 4), "oracle_gbs": round(algo / t_or / 1e9, 2)})
+        tot_bytes += algo
+        tot_us += us
+        del ds, qs, d0, q0, xt, y
+        torch.cuda.empty_cache()
+    agg = tot_bytes / (tot_us * 1e-6) / 1e9
+    return rows, {"achieved": round(agg, 1), "frac": round(agg / HBM_PEAK_GBS, 4), "unit": "GB/s",
+                  "note": "byte-weighted over the five shapes: total bytes / total mean launch time"}
+
+
+def attention_rows(reps: int = 100, min_bytes: int = 1 << 30):
+    """The isolated GQA decode attention (qd_attn_decode: split + combine) at
+    the four cases (32 q / 8 kv heads, head_dim 128, paged block 16, shuffled
+    tables): `reps` launches over >= 1 GiB of rotated K/V pool replicas in one
+    graph; the output against the f64 oracle (normwise error) and the oracle's
+    time on the host cores.  Algorithmic bytes = K/V rows read (sum of kv_len x
+    nkv x hd x 2 B x 2) + q and out (f32) + the block-table entries used."""
+    import torch
+    import oracle
+    import synth
+    import token_decode_q4_amd as qd
+    out_rows = []
+    for name in sorted(synth.ATTN_CASES):
+        a = synth.attn_case(name)
+        max_kv = max(1, a.max_kv_len)
+        pool_bytes = a.k_pool.nbytes + a.v_pool.nbytes
+        copies = max(1, -(-min_bytes // pool_bytes))
+        k0 = torch.from_numpy(a.k_pool.view(np.int16)).cuda()
+        v0 = torch.from_numpy(a.v_pool.view(np.int16)).cuda()
+        ks = [k0] + [k0.clone() for _ in range(copies - 1)]
+        vs = [v0] + [v0.clone() for _ in range(copies - 1)]
+        q = torch.from_numpy(np.ascontiguousarray(a.q)).cuda()
+        lens = torch.from_numpy(np.ascontiguousarray(a.kv_lens)).cuda()
+        tables = torch.from_numpy(np.ascontiguousarray(a.block_tables)).cuda()
+        out = torch.empty((a.B, a.nq, a.hd), dtype=torch.float32, device="cuda")
+        ws = torch.empty(qd.attn_workspace_bytes(a.B, a.nq, a.nkv, a.hd, max_kv), dtype=torch.uint8,
+                         device="cuda")
+        scale = 1.0 / np.sqrt(a.hd)
+        stream = torch.cuda.Stream()
+
+        def launch(k):
+            qd.attn_decode(q, ks[k % copies], vs[k % copies], lens, max_kv, a.nkv, scale, out, ws,
+                           block_tables=tables, stream=stream)
+
+        with torch.cuda.stream(stream):
+            launch(0)
+        stream.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        t_or, ref = _timed(lambda: oracle.attn_inputs(a), reps=1)
+        err = float(np.max(np.abs(got - ref)) / max(1e-300, float(np.max(np.abs(ref)))))
+        us = _graph_time(stream, launch, reps)
+        kv = [int(v) for v in a.kv_lens]
+        algo = (sum(kv) * a.nkv * a.hd * 2 * 2 + 2 * a.B * a.nq * a.hd * 4
+                + 4 * sum(-(-v // synth.ATTN_BLOCK) for v in kv))
+        gbs = algo / (us * 1e-6) / 1e9
+        out_rows.append({"case": name, "batch": a.B, "kv_lens": kv if a.B <= 8 else None,
+                         "mean_us": round(us, 3), "achieved": round(gbs, 1),
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": algo,
+                         "pool_copies": copies, "normwise_err_vs_oracle": err,
+                         "oracle_s": round(t_or, 4), "oracle_gbs": round(algo / t_or / 1e9, 2)})
+        del ks, vs, k0, v0, q, lens, tables, out, ws
+        torch.cuda.empty_cache()
+    return out_rows
+
+
+def decode_row(config: str, warmup: int = 16):
+    """Greedy decode tok/s of another model shape through qd_generate (graph
+    replays, no host sync): the prompt prefilled by sequential decode, then
+    `warmup` untimed and the rest of the shape's greedy steps timed."""
+    import torch
+    import synth
+    import token_decode_q4_amd as qd
+    mi = synth.make_model(config)
+    s = mi.shape
+    P, G = s.prompt_len, s.gen
+    model = qd.Model(mi, use_graph=True)
+    toks = torch.empty(s.max_seq, dtype=torch.int32, device="cuda")
+    model.set_prompt(mi.prompt)
+    model.generate(0, P - 1 + warmup, tokens=toks[: P - 1 + warmup])
+    torch.cuda.synchronize()
+    pos, n = P - 1 + warmup, G - warmup
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    model.generate(pos, n, tokens=toks[pos:pos + n])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    model.check()
+    model.close()
+    del model
+    torch.cuda.empty_cache()
+    mean_bytes = float(np.mean([step_bytes(s, k) for k in range(pos + 1, pos + n + 1)]))
+    gbs = mean_bytes / (ms * 1e-3 / n) / 1e9
+    return {"workload": f"{s.name} batch-1 greedy decode, positions {pos}..{pos + n - 1} after a "
+                        f"{P}-token sequential-decode prefill", "steps": n,
+            "tok_s": round(n / (ms * 1e-3), 1), "ms_per_step": round(ms / n, 4),
+            "step_roofline": {"achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                              "unit": "GB/s", "bytes_per_step": round(mean_bytes)}}
 
 
 def read_ceiling(nbytes: int, reps: int = 100, min_bytes: int = 1 << 30):
@@ -160,20 +329,9 @@ def read_ceiling(nbytes: int, reps: int = 100, min_bytes: int = 1 << 30):
     stream = torch.cuda.Stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    us = _graph_time(stream, lambda i: qd.stream_read(buf[(i % copies) * nbytes:], sink, nbytes,
+                                                      stream=stream), reps)
     with torch.cuda.stream(stream):
-        for i in range(10):
-            qd.stream_read(buf[(i % copies) * nbytes:], sink, nbytes, stream=stream)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(reps):
-                qd.stream_read(buf[(i % copies) * nbytes:], sink, nbytes, stream=stream)
-        graph.replay()
-        stream.synchronize()
-        e0.record(stream)
-        graph.replay()
-        e1.record(stream)
-        stream.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
         big = copies * nbytes
         qd.stream_read(buf, sink, big, stream=stream)
         e0.record(stream)
@@ -182,9 +340,9 @@ def read_ceiling(nbytes: int, reps: int = 100, min_bytes: int = 1 << 30):
         e1.record(stream)
         stream.synchronize()
         us_big = e0.elapsed_time(e1) * 1e3 / 5
-        del graph
     del buf, sink
-    return {"kernel": f"k_stream_read (qd_stream_read), graph of {reps} launches",
+    return {"kernel": f"k_stream_read (qd_stream_read), graph of {reps} launches replayed "
+                      f"{TIMED_REPLAYS} times",
             "bytes_per_launch": nbytes, "mean_us": round(us, 3),
             "achieved": round(nbytes / (us * 1e-6) / 1e9, 1),
             "achieved_one_launch_of": big, "achieved_one_launch": round(big / (us_big * 1e-6) / 1e9, 1),
@@ -218,6 +376,8 @@ def main():
     ap.add_argument("--config", default="qwen3-8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the per-row legs (GEMV sweep shapes, attention cases, 0.6B decode)")
     ap.add_argument("--layer-kernel", type=int, default=0,
                     help="1: one persistent kernel launch per layer (qd_config.layer_kernel)")
     args = ap.parse_args()
@@ -280,6 +440,24 @@ def main():
         roof["frac_of_read_ceiling"] = round(roof["achieved"] / ceil["achieved"], 4)
         log(f"read ceiling: {ceil['mean_us']} us for {ceil['bytes_per_launch']} B, {ceil['achieved']} GB/s; "
             f"{ceil['achieved_one_launch']} GB/s reading {ceil['achieved_one_launch_of']} B in one launch")
+    rows = None
+    if not args.no_rows:
+        t0 = time.time()
+        g_rows, g_agg = gemv_sweep_rows()
+        for r in g_rows:
+            log(f"gemv {r['shape']}: {r['mean_us']} us, {r['achieved']} GB/s ({r['frac']:.3f}), "
+                f"err {r['normwise_err_vs_oracle']:.1e}, oracle {r['oracle_gbs']} GB/s")
+        log(f"gemv sweep aggregate: {g_agg['achieved']} GB/s ({g_agg['frac']:.3f})")
+        a_rows = attention_rows()
+        for r in a_rows:
+            log(f"attention {r['case']}: {r['mean_us']} us, {r['achieved']} GB/s ({r['frac']:.3f}), "
+                f"err {r['normwise_err_vs_oracle']:.1e}, oracle {r['oracle_s']} s")
+        d06 = decode_row("qwen3-0.6b") if args.config != "qwen3-0.6b" else None
+        if d06:
+            log(f"decode {d06['workload']}: {d06['tok_s']} tok/s ({d06['step_roofline']['frac']:.3f})")
+        rows = {"gemv_sweep": g_rows, "gemv_sweep_aggregate": g_agg, "attention": a_rows,
+                "decode_qwen3_0.6b": d06}
+        log(f"row legs {time.time() - t0:.1f}s")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(mi)
@@ -303,6 +481,7 @@ def main():
                           "bytes_per_step": round(mean_bytes)},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "rows": rows,
     }
     print(json.dumps(out), flush=True)
 
