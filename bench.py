@@ -221,6 +221,50 @@ def gemv_sweep_rows(reps: int = 100, min_bytes: int = 1 << 30):
                   "note": "byte-weighted over the five shapes: total bytes / total mean launch time"}
 
 
+def gemv_batch_rows(batches=(1, 2, 4, 8), reps: int = 100, min_bytes: int = 1 << 30):
+    """The batched GEMV (qd_gemv_q4_0_batch) at the gate|up shape 24576 x 4096:
+    Y[b] = W X[b] for B vectors, every weight read once; `reps` launches over
+    >= 1 GiB of rotated weight copies in one graph.  Algorithmic bytes =
+    N*K*18/32 + 4*B*(K + N); vectors per second = B / mean launch time."""
+    import torch
+    import oracle
+    import synth
+    import token_decode_q4_amd as qd
+    idx = synth.GEMV_SHAPES.index(GEMV_SHAPE)
+    N, K = GEMV_SHAPE
+    (W,), _ = synth.gemv_case(idx)
+    copies = max(1, -(-min_bytes // (W.d.nbytes + W.qs.nbytes)))
+    d0 = torch.from_numpy(W.d.view(np.int16)).cuda()
+    q0 = torch.from_numpy(W.qs).cuda()
+    ds = [d0] + [d0.clone() for _ in range(copies - 1)]
+    qs = [q0] + [q0.clone() for _ in range(copies - 1)]
+    rows = []
+    for B in batches:
+        X = synth.batch_x(9000 + B, B, K)
+        xt = torch.from_numpy(X).cuda()
+        Y = torch.empty((B, N), dtype=torch.float32, device="cuda")
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            qd.gemv_q4_0_batch(d0, q0, xt, Y, stream=stream)
+        stream.synchronize()
+        got = Y.cpu().numpy().astype(np.float64)
+        err = 0.0
+        for b in range(B):
+            ref = oracle.gemv(W, X[b])
+            err = max(err, float(np.max(np.abs(got[b] - ref)) / float(np.max(np.abs(ref)))))
+        us = _graph_time(stream, lambda i: qd.gemv_q4_0_batch(ds[i % copies], qs[i % copies], xt, Y,
+                                                              stream=stream), reps)
+        algo = N * K * 18 // 32 + 4 * B * (K + N)
+        gbs = algo / (us * 1e-6) / 1e9
+        rows.append({"shape": f"{N}x{K}", "batch": B, "mean_us": round(us, 3), "achieved": round(gbs, 1),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": algo,
+                     "vectors_per_s": round(B / (us * 1e-6), 1), "normwise_err_vs_oracle": err})
+        del xt, Y
+    del ds, qs, d0, q0
+    torch.cuda.empty_cache()
+    return rows
+
+
 def attention_rows(reps: int = 100, min_bytes: int = 1 << 30):
     """The isolated GQA decode attention (qd_attn_decode: split + combine) at
     the four cases (32 q / 8 kv heads, head_dim 128, paged block 16, shuffled
@@ -448,6 +492,10 @@ def main():
             log(f"gemv {r['shape']}: {r['mean_us']} us, {r['achieved']} GB/s ({r['frac']:.3f}), "
                 f"err {r['normwise_err_vs_oracle']:.1e}, oracle {r['oracle_gbs']} GB/s")
         log(f"gemv sweep aggregate: {g_agg['achieved']} GB/s ({g_agg['frac']:.3f})")
+        b_rows = gemv_batch_rows()
+        for r in b_rows:
+            log(f"gemv batch {r['batch']} {r['shape']}: {r['mean_us']} us, {r['achieved']} GB/s "
+                f"({r['frac']:.3f}), {r['vectors_per_s']:.0f} vectors/s, err {r['normwise_err_vs_oracle']:.1e}")
         a_rows = attention_rows()
         for r in a_rows:
             log(f"attention {r['case']}: {r['mean_us']} us, {r['achieved']} GB/s ({r['frac']:.3f}), "
@@ -455,7 +503,8 @@ def main():
         d06 = decode_row("qwen3-0.6b") if args.config != "qwen3-0.6b" else None
         if d06:
             log(f"decode {d06['workload']}: {d06['tok_s']} tok/s ({d06['step_roofline']['frac']:.3f})")
-        rows = {"gemv_sweep": g_rows, "gemv_sweep_aggregate": g_agg, "attention": a_rows,
+        rows = {"gemv_sweep": g_rows, "gemv_sweep_aggregate": g_agg, "gemv_batch": b_rows,
+                "attention": a_rows,
                 "decode_qwen3_0.6b": d06}
         log(f"row legs {time.time() - t0:.1f}s")
     cpu = None

@@ -157,6 +157,18 @@ int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* d_tokens,
 int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x, float* d_y,
                  int32_t N, int32_t K, qd_stream stream);
 
+/* Batched q4_0 GEMV (inferencelayer cuda_llm.rs page, the batched decode
+ * head-to-head of its q4 GEMV arm at M = 1 .. 16 tokens): Y[b] = W X[b] for
+ * b < B, every weight read once for the whole batch.  W as for qd_gemv_q4_0;
+ * d_x device f32 [B][K] and d_y device f32 [B][N], both contiguous; qs and x
+ * 16-byte aligned.  1 <= B <= 8 and B*K <= 32 768 (the batch is staged in
+ * LDS), N < 2^24, N*K/2 < 2^32; QD_EINVAL / QD_EUNSUPPORTED otherwise, with
+ * nothing enqueued.  B == 1 runs the single-vector kernel.  Each output is
+ * the same f32 sum of exact products as the single-vector GEMV (its order
+ * may differ).  No allocation; capturable. */
+int qd_gemv_q4_0_batch(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x, float* d_y,
+                       int32_t N, int32_t K, int32_t B, qd_stream stream);
+
 /* Standalone GQA decode attention with split-KV partials and an
  * online-softmax combine (inferencelayer cuda_llm.rs page, attn_partial /
  * attn_reduce and the flash-decoding arm; ferrum-kernels cuda_decode.rs page,

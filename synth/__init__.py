@@ -328,6 +328,13 @@ def random_gemv(seed: int, N: int, K: int, x_scale: float = 1.0):
     return W, x
 
 
+def batch_x(seed: int, B: int, K: int) -> np.ndarray:
+    """B input vectors of a batched GEMV case: f32 [B, K], N(0,1), each row from
+    its own seed key."""
+    return np.stack([_ss(seed, 3, b).standard_normal(K, dtype=np.float32) for b in range(B)]) \
+        if B > 0 else np.zeros((0, K), np.float32)
+
+
 # --------------------------------------------------------------------------- attention
 
 @dataclass

@@ -47,6 +47,25 @@ def test_gemv_validation(qd):
     assert b"aligned" in L.qd_last_error()
 
 
+def test_gemv_batch_validation(qd):
+    L = qd.lib()
+    p = C.c_void_p(16)
+    E, U = qd._native.QD_EINVAL, qd._native.QD_EUNSUPPORTED
+    assert L.qd_gemv_q4_0_batch(None, p, p, p, 4, 32, 2, None) == E
+    assert L.qd_gemv_q4_0_batch(p, p, p, p, 4, 33, 2, None) == E
+    assert L.qd_gemv_q4_0_batch(p, p, p, p, -1, 32, 2, None) == E
+    assert L.qd_gemv_q4_0_batch(p, p, p, p, 4, 32, 0, None) == E
+    assert L.qd_gemv_q4_0_batch(p, p, p, p, 4, 32, 9, None) == E
+    assert b"batch" in L.qd_last_error()
+    assert L.qd_gemv_q4_0_batch(p, p, p, p, 4, 4096, 9, None) == E
+    # the batch is staged in LDS: B * K <= 32768
+    assert L.qd_gemv_q4_0_batch(p, p, p, p, 4, 8192, 8, None) == U
+    assert L.qd_gemv_q4_0_batch(p, p, p, p, 4, 12288, 3, None) == U
+    assert L.qd_gemv_q4_0_batch(p, p, C.c_void_p(20), p, 4, 32, 2, None) == E
+    assert b"aligned" in L.qd_last_error()
+    assert L.qd_gemv_q4_0_batch(p, p, p, p, 1 << 24, 64, 2, None) == U
+
+
 def test_attention_validation(qd):
     L = qd.lib()
     p = 16

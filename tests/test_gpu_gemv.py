@@ -1,4 +1,4 @@
-"""q4_0 GEMV through the C ABI (qd_gemv_q4_0) against the f64 oracle."""
+"""q4_0 GEMV through the C ABI (qd_gemv_q4_0, qd_gemv_q4_0_batch) against the f64 oracle."""
 import numpy as np
 import pytest
 
@@ -75,6 +75,101 @@ def test_gemv_k_zero_fills_zeros():
     p = C.c_void_p(buf.data_ptr())
     assert qd.lib().qd_gemv_q4_0(p, p, p, C.c_void_p(y.data_ptr()), 300, 0, None) == 0
     assert np.array_equal(host(y), np.zeros(300, dtype=np.float32))
+
+
+def _gemv_batch(W, X):
+    import torch
+    import token_decode_q4_amd as qd
+    Y = torch.full((X.shape[0], W.rows), float("nan"), dtype=torch.float32, device="cuda")
+    qd.gemv_q4_0_batch(dev(W.d), dev(W.qs), dev(X), Y)
+    return host(Y)
+
+
+@pytest.mark.parametrize("idx", range(len(synth.GEMV_SHAPES)))
+@pytest.mark.parametrize("B", [2, 8])
+def test_gemv_batch_sweep_shape(idx, B):
+    """Y[b] = W X[b] at the sweep shapes, every column against the f64 oracle."""
+    N, K = synth.GEMV_SHAPES[idx]
+    if B * K > 32768:
+        B = 32768 // K
+    say(f"gemv batch {B} x {N}x{K}")
+    (W,), _ = synth.gemv_case(idx)
+    X = synth.batch_x(7000 + idx, B, K)
+    Y = _gemv_batch(W, X)
+    assert np.all(np.isfinite(Y))
+    for b in range(B):
+        err = normwise(Y[b], oracle.gemv(W, X[b]))
+        assert err <= 2e-6, (b, err)
+
+
+def _f32_bound(W, x):
+    """Per-row scale of the f32 rounding error of the kernels' sum: the magnitudes
+    the arithmetic handles, sum_j |w_j x_j| plus the -8 * d * sum(x) offset of
+    every block (a forward error bound for a dot product is a small multiple of
+    the unit roundoff times this)."""
+    dense = oracle.dequant(W)
+    d = np.abs(oracle.f16_to_f64(W.d))
+    xa = np.abs(x.astype(np.float64))
+    blk = xa.reshape(-1, 32).sum(axis=1)
+    return np.abs(dense) @ xa + 8.0 * (d @ blk)
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N,K", [(1, 32), (17, 96), (100, 1024), (257, 3072), (4097, 2048),
+                                 (70, 160), (1000, 4096)])
+def test_gemv_batch_ragged(N, K, B):
+    if B * K > 32768:
+        pytest.skip("B * K above the staged limit")
+    W, _ = synth.random_gemv(2000 + N, N, K)
+    X = synth.batch_x(3000 + N + B, B, K)
+    Y = _gemv_batch(W, X)
+    for b in range(B):
+        # elementwise against the f32 error bound (a single short row can cancel
+        # to far below its terms, where a relative bar would test rounding luck)
+        err = np.abs(Y[b].astype(np.float64) - oracle.gemv(W, X[b]))
+        assert np.all(err <= 1e-6 * _f32_bound(W, X[b])), b
+
+
+def test_gemv_batch_equals_single_per_column():
+    """Each column of the batch is the single-vector GEMV of that vector (to f32 rounding:
+    the two kernels may sum in a different order)."""
+    W, _ = synth.random_gemv(11, 6144, 4096)
+    X = synth.batch_x(12, 8, 4096)
+    Y = _gemv_batch(W, X)
+    for b in range(8):
+        y1 = _gemv(W, X[b])
+        assert normwise(Y[b], y1.astype(np.float64)) <= 1e-6
+
+
+def test_gemv_batch_special_values():
+    """Hand-built blocks, unit vectors in every column: exact."""
+    K = 64
+    codes = np.tile(np.arange(16, dtype=np.uint8), 8).reshape(2, 64)
+    qs = (codes.reshape(2, 2, 32)[..., :16] | (codes.reshape(2, 2, 32)[..., 16:] << 4)).astype(np.uint8)
+    d = np.array([[0x3C00, 0x3C00], [0xC000, 0x3C00]], dtype=np.uint16)
+    W = synth.Q4Matrix(d, qs)
+    dense = oracle.dequant(W)
+    cols = [0, 1, 15, 16, 31, 32, 63, 40]
+    X = np.zeros((len(cols), K), dtype=np.float32)
+    for b, c in enumerate(cols):
+        X[b, c] = 1.0
+    Y = _gemv_batch(W, X)
+    for b, c in enumerate(cols):
+        assert np.array_equal(Y[b], dense[:, c].astype(np.float32)), b
+
+
+def test_gemv_batch_k_zero_and_repeat():
+    import ctypes as C
+    import torch
+    import token_decode_q4_amd as qd
+    buf = torch.zeros(64, dtype=torch.float32, device="cuda")
+    Y = torch.full((3, 300), float("nan"), dtype=torch.float32, device="cuda")
+    p = C.c_void_p(buf.data_ptr())
+    assert qd.lib().qd_gemv_q4_0_batch(p, p, p, C.c_void_p(Y.data_ptr()), 300, 0, 3, None) == 0
+    assert np.array_equal(host(Y), np.zeros((3, 300), dtype=np.float32))
+    W, _ = synth.random_gemv(5, 4096, 4096)
+    X = synth.batch_x(6, 4, 4096)
+    assert np.array_equal(_gemv_batch(W, X), _gemv_batch(W, X))
 
 
 @pytest.mark.parametrize("nbytes", [16, 16 * 1023, 16 * 1024 + 48, 16 * 4096 * 3 + 16, 56737792])

@@ -19,7 +19,7 @@ QD_OK, QD_EINVAL, QD_ERANGE, QD_ENOMEM, QD_EUNSUPPORTED, QD_EHIP = 0, -1, -2, -3
 
 # every function declared in include/qd.h
 EXPORTS = ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate",
-           "qd_gemv_q4_0", "qd_attn_workspace_bytes", "qd_attn_decode", "qd_check",
+           "qd_gemv_q4_0", "qd_gemv_q4_0_batch", "qd_attn_workspace_bytes", "qd_attn_decode", "qd_check",
            "qd_stream_read_groups", "qd_stream_read", "qd_last_error")
 
 
@@ -81,6 +81,8 @@ def lib():
                                   C.c_void_p]
         L.qd_gemv_q4_0.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
                                    C.c_int32, C.c_void_p]
+        L.qd_gemv_q4_0_batch.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                                         C.c_int32, C.c_int32, C.c_void_p]
         L.qd_attn_workspace_bytes.restype = C.c_size_t
         L.qd_attn_workspace_bytes.argtypes = [C.c_int32] * 5
         L.qd_attn_decode.argtypes = [C.POINTER(AttnArgs), C.c_void_p, C.c_size_t, C.c_void_p]
@@ -123,6 +125,14 @@ def gemv_q4_0(d, qs, x, y, stream=None) -> int:
     N = d.shape[0]
     K = x.shape[0]
     return check(lib().qd_gemv_q4_0(_ptr(d), _ptr(qs), _ptr(x), _ptr(y), N, K, _stream(stream)))
+
+
+def gemv_q4_0_batch(d, qs, x, y, stream=None) -> int:
+    """Y[b] = W X[b]: x device f32 [B][K], y device f32 [B][N] (both contiguous)."""
+    B, K = x.shape
+    N = y.shape[1]
+    return check(lib().qd_gemv_q4_0_batch(_ptr(d), _ptr(qs), _ptr(x), _ptr(y), N, K, B,
+                                          _stream(stream)))
 
 
 def stream_read_groups(nbytes: int) -> int:

@@ -13,6 +13,7 @@
 
 #include "fused_layers.h"
 #include "gemv_cfg.h"
+#include "gemv_batch.h"
 #include "stream_read.h"
 
 #include <algorithm>
@@ -853,6 +854,89 @@ extern "C" int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const
         return QD_OK;
     }
     HIP_TRY(launch_gemv_plain(d_scales, d_qs, d_x, d_y, N, K, (hipStream_t)stream));
+    return QD_OK;
+}
+
+// ------------------------------------------------------------------ batched GEMV
+
+// launch configuration of the batched GEMV: rows per slot, waves, block
+// groups per item, register buffers, items per unrolled chunk, non-temporal
+// weight loads (lanes per row: 16 or 8, following K)
+constexpr int GB_RPS = 2, GB_NW = 8, GB_BG = 1, GB_NBUF = 2, GB_UNR = 8;
+constexpr bool GB_NTL = true;
+constexpr int GB_GRID_CAP = 512;
+
+template <int NC, int L>
+static hipError_t launch_gemv_batch_l(const uint16_t* d, const uint8_t* q, const float* x, float* y,
+                                      int N, int nb, hipStream_t s)
+{
+    const size_t lds = gemv_batch_lds_bytes(nb, NC);
+    if (lds > 64 * 1024) {
+        // dynamic LDS above 64 KB is opted into per kernel (160 KB per CU on gfx950)
+        static size_t allowed = 0;
+        if (lds > allowed) {
+            const hipError_t e = hipFuncSetAttribute(
+                reinterpret_cast<const void*>(&k_gemv_batch<NC, L, GB_RPS, GB_NW, GB_BG, GB_NBUF, GB_UNR, GB_NTL>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess)
+                return e;
+            allowed = lds;
+        }
+    }
+    const int rows = GB_NW * (WAVE / L) * GB_RPS;
+    const int grid = std::max(1, std::min((N + rows - 1) / rows, GB_GRID_CAP));
+    hipLaunchKernelGGL((k_gemv_batch<NC, L, GB_RPS, GB_NW, GB_BG, GB_NBUF, GB_UNR, GB_NTL>), dim3(grid),
+                       dim3(GB_NW * WAVE), lds, s, d, q, x, y, N, nb);
+    return hipGetLastError();
+}
+
+template <int NC>
+static hipError_t launch_gemv_batch(const uint16_t* d, const uint8_t* q, const float* x, float* y,
+                                    int N, int K, hipStream_t s)
+{
+    const int nb = K / 32;
+    if (pick_lpr(nb, 16) == 16)
+        return launch_gemv_batch_l<NC, 16>(d, q, x, y, N, nb, s);
+    return launch_gemv_batch_l<NC, 8>(d, q, x, y, N, nb, s);
+}
+
+extern "C" int qd_gemv_q4_0_batch(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x,
+                                  float* d_y, int32_t N, int32_t K, int32_t B, qd_stream stream)
+{
+    if (!d_scales || !d_qs || !d_x || !d_y)
+        return fail(QD_EINVAL, "null pointer");
+    if (N < 0 || K < 0 || K % 32)
+        return fail(QD_EINVAL, "bad shape N=%d K=%d (K %% 32 must be 0)", N, K);
+    if (B < 1 || B > GB_MAXB)
+        return fail(QD_EINVAL, "batch B=%d outside [1, %d]", B, GB_MAXB);
+    if ((int64_t)B * K > GB_MAXKB)
+        return fail(QD_EUNSUPPORTED, "B*K = %lld above %d (the batch is staged in LDS)",
+                    (long long)B * K, GB_MAXKB);
+    if (B == 1 && gemv_lds_bytes(K / 32) > (size_t)GEMV_MAX_LDS)
+        return fail(QD_EUNSUPPORTED, "K=%d above the staged-x limit", K);
+    if ((uint64_t)N * (uint64_t)K / 2 >= (uint64_t)1 << 32 || N >= (1 << 24))
+        return fail(QD_EUNSUPPORTED, "N=%d K=%d: above 2^32 bytes of nibbles or 2^24 rows", N, K);
+    if ((reinterpret_cast<uintptr_t>(d_qs) | reinterpret_cast<uintptr_t>(d_x)) & 15)
+        return fail(QD_EINVAL, "qs and x must be 16-byte aligned");
+    if (N == 0)
+        return QD_OK;
+    const hipStream_t s = (hipStream_t)stream;
+    if (K == 0) {   // Y = 0 by a fill kernel (no memset node inside a captured graph)
+        const int n = N * B;
+        hipLaunchKernelGGL(k_fill_f32, dim3((n + 255) / 256), dim3(256), 0, s, d_y, n, 0.f);
+        HIP_TRY(hipGetLastError());
+        return QD_OK;
+    }
+    switch (B) {
+    case 1: HIP_TRY(launch_gemv_plain(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    case 2: HIP_TRY(launch_gemv_batch<2>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    case 3: HIP_TRY(launch_gemv_batch<3>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    case 4: HIP_TRY(launch_gemv_batch<4>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    case 5: HIP_TRY(launch_gemv_batch<5>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    case 6: HIP_TRY(launch_gemv_batch<6>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    case 7: HIP_TRY(launch_gemv_batch<7>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    default: HIP_TRY(launch_gemv_batch<8>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    }
     return QD_OK;
 }
 
