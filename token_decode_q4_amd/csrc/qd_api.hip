@@ -862,8 +862,15 @@ extern "C" int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const
 // launch configuration of the batched GEMV: rows per slot, waves, block
 // groups per item, register buffers, items per unrolled chunk, non-temporal
 // weight loads (lanes per row: 16 or 8, following K)
-constexpr int GB_RPS = 2, GB_NW = 8, GB_BG = 1, GB_NBUF = 2, GB_UNR = 8;
+// (rows per slot: 4 up to 4 vectors, 2 above, where the registers of 4 rows of
+// decoded codes and 8 accumulators per row cost more than the shared LDS reads)
+#ifndef QD_CFG_BATCH
+#define QD_CFG_BATCH 8, 1, 2, 8   // waves, block groups, buffers, unroll; tunable at compile time
+#endif
+constexpr int GB_CFG[4] = {QD_CFG_BATCH};
+constexpr int GB_NW = GB_CFG[0], GB_BG = GB_CFG[1], GB_NBUF = GB_CFG[2], GB_UNR = GB_CFG[3];
 constexpr bool GB_NTL = true;
+__host__ __device__ constexpr int gb_rps(int nc) { return nc <= 4 ? 4 : 2; }
 constexpr int GB_GRID_CAP = 512;
 
 template <int NC, int L>
@@ -876,16 +883,16 @@ static hipError_t launch_gemv_batch_l(const uint16_t* d, const uint8_t* q, const
         static size_t allowed = 0;
         if (lds > allowed) {
             const hipError_t e = hipFuncSetAttribute(
-                reinterpret_cast<const void*>(&k_gemv_batch<NC, L, GB_RPS, GB_NW, GB_BG, GB_NBUF, GB_UNR, GB_NTL>),
+                reinterpret_cast<const void*>(&k_gemv_batch<NC, L, gb_rps(NC), GB_NW, GB_BG, GB_NBUF, GB_UNR, GB_NTL>),
                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess)
                 return e;
             allowed = lds;
         }
     }
-    const int rows = GB_NW * (WAVE / L) * GB_RPS;
+    const int rows = GB_NW * (WAVE / L) * gb_rps(NC);
     const int grid = std::max(1, std::min((N + rows - 1) / rows, GB_GRID_CAP));
-    hipLaunchKernelGGL((k_gemv_batch<NC, L, GB_RPS, GB_NW, GB_BG, GB_NBUF, GB_UNR, GB_NTL>), dim3(grid),
+    hipLaunchKernelGGL((k_gemv_batch<NC, L, gb_rps(NC), GB_NW, GB_BG, GB_NBUF, GB_UNR, GB_NTL>), dim3(grid),
                        dim3(GB_NW * WAVE), lds, s, d, q, x, y, N, nb);
     return hipGetLastError();
 }
