@@ -169,6 +169,24 @@ int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x
 int qd_gemv_q4_0_batch(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x, float* d_y,
                        int32_t N, int32_t K, int32_t B, qd_stream stream);
 
+/* Rotary frequencies for qd_config.inv_freq (host only, no device work):
+ * out[i] = theta^(-2i/rot_dim) for i < rot_dim/2, evaluated in f64 and rounded
+ * to f32, with the rotary scaling of the inferencelayer cuda_llm.rs page
+ * (Cfg::rope_inv_freq): QD_ROPE_DEFAULT none; QD_ROPE_LINEAR every frequency
+ * divided by `factor`; QD_ROPE_LLAMA3 with wavelength wl = 2*pi/f: wl above
+ * original_max_pos/low_freq_factor -> f/factor, wl below
+ * original_max_pos/high_freq_factor -> f, between them (1-s)*f/factor + s*f
+ * with s = (original_max_pos/wl - low_freq_factor) / (high_freq_factor -
+ * low_freq_factor).  The last three arguments are read for LLAMA3 only.
+ * `out` is a host float array [rot_dim/2] owned by the caller.  Errors:
+ * QD_EINVAL (null out, odd or non-positive rot_dim, theta <= 1, factor <= 0,
+ * llama3 factors out of order), QD_EUNSUPPORTED (any other scaling type:
+ * refused, never ignored). */
+enum { QD_ROPE_DEFAULT = 0, QD_ROPE_LINEAR = 1, QD_ROPE_LLAMA3 = 2 };
+int qd_rope_inv_freq(float theta, int32_t rot_dim, int32_t scaling, float factor,
+                     float low_freq_factor, float high_freq_factor, float original_max_pos,
+                     float* out);
+
 /* Standalone GQA decode attention with split-KV partials and an
  * online-softmax combine (inferencelayer cuda_llm.rs page, attn_partial /
  * attn_reduce and the flash-decoding arm; ferrum-kernels cuda_decode.rs page,

@@ -135,6 +135,39 @@ def rope(v, rot: int, inv_freq, pos: int) -> np.ndarray:
     return vv
 
 
+def rope_inv_freq(theta: float, rot_dim: int, scaling: str = "default", factor: float = 1.0,
+                  low_freq_factor: float = 1.0, high_freq_factor: float = 4.0,
+                  original_max_pos: float = 8192.0) -> np.ndarray:
+    """Rotary frequencies with rotary scaling, in f64 (inferencelayer cuda_llm.rs
+    page, Cfg::rope_inv_freq; the exponent over rot_dim as in the partial-rotary
+    reading): base f_i = theta^(-2i/rot_dim).  "linear": every f_i / factor.
+    "llama3": with wavelength w_i = 2 pi / f_i, low = orig / low_freq_factor and
+    high = orig / high_freq_factor: w_i > low -> f_i / factor; high <= w_i <= low
+    -> (1 - s) f_i / factor + s f_i with s = (orig / w_i - low_freq_factor) /
+    (high_freq_factor - low_freq_factor); w_i < high -> f_i.  Other types are
+    refused (ValueError)."""
+    out = []
+    for i in range(rot_dim // 2):
+        f = float(theta) ** (-(2.0 * i) / float(rot_dim))
+        if scaling == "default":
+            pass
+        elif scaling == "linear":
+            f = f / factor
+        elif scaling == "llama3":
+            wavelength = 2.0 * np.pi / f
+            low_wl = original_max_pos / low_freq_factor
+            high_wl = original_max_pos / high_freq_factor
+            if wavelength > low_wl:
+                f = f / factor
+            elif wavelength >= high_wl:
+                s = (original_max_pos / wavelength - low_freq_factor) / (high_freq_factor - low_freq_factor)
+                f = (1.0 - s) * (f / factor) + s * f
+        else:
+            raise ValueError(f"rotary scaling type {scaling!r} is not implemented")
+        out.append(f)
+    return np.array(out, dtype=np.float64)
+
+
 def attn_decode(q, k, v, kv_lens, nkv: int, scale: float, block_tables=None,
                 block_size: int = 16, contig_max_kv: int = 0,
                 nthreads: int | None = None) -> np.ndarray:

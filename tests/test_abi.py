@@ -172,3 +172,40 @@ def test_create_rejects_layer_kernel_for_unfit_model(qd):
     h = C.c_void_p()
     assert qd.lib().qd_create(C.byref(cfg), C.byref(w), None, C.byref(h)) == qd._native.QD_EUNSUPPORTED
     assert b"layer_kernel" in qd.lib().qd_last_error()
+
+
+@pytest.mark.parametrize("case", [
+    dict(theta=1e6, rot_dim=128),
+    dict(theta=1e4, rot_dim=64, scaling="linear", factor=4.0),
+    dict(theta=5e5, rot_dim=128, scaling="llama3", factor=8.0, low_freq_factor=1.0,
+         high_freq_factor=4.0, original_max_pos=8192.0),
+    dict(theta=1e6, rot_dim=64, scaling="llama3", factor=16.0, low_freq_factor=2.0,
+         high_freq_factor=8.0, original_max_pos=64.0),
+    dict(theta=1e6, rot_dim=32),
+])
+def test_rope_inv_freq_matches_oracle(qd, case):
+    """qd_rope_inv_freq (host code in the library, no device work) against the
+    f64 oracle of the same rule: equal to f32 rounding."""
+    import oracle
+    got = qd.rope_inv_freq(**case)
+    ref = oracle.rope_inv_freq(**case)
+    assert got.dtype == np.float32 and got.shape == ref.shape
+    np.testing.assert_allclose(got.astype(np.float64), ref, rtol=2 ** -23, atol=0)
+
+
+def test_rope_inv_freq_validation(qd):
+    L = qd.lib()
+    out = np.empty(64, dtype=np.float32)
+    p = out.ctypes.data
+    E, U = qd._native.QD_EINVAL, qd._native.QD_EUNSUPPORTED
+    assert L.qd_rope_inv_freq(1e4, 64, 0, 1.0, 1.0, 4.0, 8192.0, None) == E
+    assert L.qd_rope_inv_freq(1e4, 63, 0, 1.0, 1.0, 4.0, 8192.0, p) == E
+    assert L.qd_rope_inv_freq(1e4, 0, 0, 1.0, 1.0, 4.0, 8192.0, p) == E
+    assert L.qd_rope_inv_freq(1.0, 64, 0, 1.0, 1.0, 4.0, 8192.0, p) == E
+    assert L.qd_rope_inv_freq(1e4, 64, 1, 0.0, 1.0, 4.0, 8192.0, p) == E
+    assert L.qd_rope_inv_freq(1e4, 64, 2, 8.0, 4.0, 1.0, 8192.0, p) == E
+    assert L.qd_rope_inv_freq(1e4, 64, 2, 8.0, 1.0, 4.0, 0.0, p) == E
+    assert L.qd_rope_inv_freq(1e4, 64, 3, 2.0, 1.0, 4.0, 8192.0, p) == U
+    assert b"not implemented" in L.qd_last_error()
+    with pytest.raises(qd.QdError):
+        qd.rope_inv_freq(1e4, 64, "yarn", 2.0)

@@ -189,3 +189,37 @@ def test_qwen3_8b_shape_layer_kernel_vs_golden():
     paged KV."""
     n_eq, worst = _golden_run("qwen3-8b", layer_kernel=True)
     assert worst <= 5e-3
+
+
+def test_tiny_llama3_rope_scaling_vs_oracle(tiny):
+    """The tiny model with llama3 rotary scaling (frequencies from
+    qd_rope_inv_freq on the library side, from the oracle's own rule on the
+    oracle side; original_max_pos 32 so that all three regimes of the rule
+    occur among the 32 frequencies): teacher-forced logits and free-running
+    greedy tokens."""
+    import dataclasses
+    import token_decode_q4_amd as qd
+    s = tiny.shape
+    kw = dict(scaling="llama3", factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,
+              original_max_pos=32.0)
+    f_lib = qd.rope_inv_freq(1e6, s.rot_dim, **kw)
+    f_ref = oracle.rope_inv_freq(1e6, s.rot_dim, **kw).astype(np.float32)
+    base = oracle.rope_inv_freq(1e6, s.rot_dim)
+    wl = 2 * np.pi / base
+    assert (wl < 8).any() and (wl > 32).any() and ((wl >= 8) & (wl <= 32)).any()
+    mi_lib = dataclasses.replace(tiny, inv_freq=f_lib)
+    mi_ref = dataclasses.replace(tiny, inv_freq=f_ref)
+    say("tiny llama3 rotary scaling")
+    om = oracle.Model(mi_ref)
+    toks, margins, _ = oracle.generate(om, tiny.prompt, s.gen)
+    seq = list(tiny.prompt) + list(toks[:-1])
+    om2 = oracle.Model(mi_ref)
+    ref = np.stack([om2.step(int(t), p) for p, t in enumerate(seq)])
+    m = qd.Model(mi_lib, use_graph=True)
+    lg, _ = _teacher_forced_logits(m, seq, s.vocab)
+    err = float(np.max(np.abs(lg - ref)))
+    say(f"tiny llama3 logits max abs err {err:.3e}")
+    assert err <= 1e-4
+    got = _gen(m, tiny.prompt, s.gen)[s.prompt_len - 1:]
+    m.close()
+    check_greedy(got, toks, margins, "tiny llama3")

@@ -303,3 +303,58 @@ def test_greedy_lowest_index_on_ties(oracle_lib):
     # the pick happens on f32-rounded logits: an f64-only difference is a tie
     lg = np.array([1.0, 1.0 + 1e-12])
     assert oracle_lib.greedy_pick(lg)[0] == 0
+
+
+# --------------------------------------------------------------------------- rotary scaling
+# inferencelayer cuda_llm.rs page, Cfg::rope_inv_freq: default / linear / llama3.
+
+def test_rope_inv_freq_default_closed_form(oracle_lib):
+    f = oracle_lib.rope_inv_freq(1e6, 128)
+    assert f.shape == (64,)
+    assert f[0] == 1.0
+    # f_i = theta^(-2i/rot): consecutive ratios are all theta^(-2/rot)
+    np.testing.assert_allclose(f[1:] / f[:-1], 1e6 ** (-2.0 / 128), rtol=1e-13)
+    np.testing.assert_allclose(f[32], 1e6 ** -0.5, rtol=1e-13)
+
+
+def test_rope_inv_freq_factor_one_is_identity(oracle_lib):
+    base = oracle_lib.rope_inv_freq(5e5, 64)
+    for sc in ("linear", "llama3"):
+        np.testing.assert_allclose(oracle_lib.rope_inv_freq(5e5, 64, sc, factor=1.0), base, rtol=1e-15)
+
+
+def test_rope_inv_freq_linear_divides(oracle_lib):
+    base = oracle_lib.rope_inv_freq(1e4, 128)
+    np.testing.assert_allclose(oracle_lib.rope_inv_freq(1e4, 128, "linear", factor=4.0), base / 4.0,
+                               rtol=1e-15)
+
+
+def test_rope_inv_freq_llama3_regions_and_continuity(oracle_lib):
+    theta, rot, fac, lo, hi, orig = 5e5, 128, 8.0, 1.0, 4.0, 8192.0
+    base = oracle_lib.rope_inv_freq(theta, rot)
+    f = oracle_lib.rope_inv_freq(theta, rot, "llama3", fac, lo, hi, orig)
+    wl = 2 * np.pi / base
+    short, long_ = wl < orig / hi, wl > orig / lo
+    mid = ~short & ~long_
+    assert short.any() and long_.any() and mid.any()
+    np.testing.assert_allclose(f[short], base[short], rtol=1e-15)        # high frequencies kept
+    np.testing.assert_allclose(f[long_], base[long_] / fac, rtol=1e-15)  # low frequencies scaled
+    # in between: strictly between f/factor and f
+    assert np.all(f[mid] < base[mid]) and np.all(f[mid] > base[mid] / fac)
+    # the blend is continuous at both edges: evaluate the rule at wavelengths
+    # on either side of each boundary (theta chosen so that f_1 sits on it)
+    for edge in (orig / lo, orig / hi):
+        for eps in (1e-9, -1e-9):
+            w = edge * (1 + eps)
+            th = (2 * np.pi / w) ** (-rot / 2.0)   # f_1 = th^(-2/rot) = 2 pi / w
+            g = oracle_lib.rope_inv_freq(th, rot, "llama3", fac, lo, hi, orig)[1]
+            b = oracle_lib.rope_inv_freq(th, rot)[1]
+            expect = b / fac if edge == orig / lo else b
+            assert abs(g - expect) <= 1e-6 * b
+    # the scaled frequencies still decrease with i
+    assert np.all(np.diff(f) < 0)
+
+
+def test_rope_inv_freq_unknown_type_refused(oracle_lib):
+    with pytest.raises(ValueError):
+        oracle_lib.rope_inv_freq(1e4, 64, "yarn", factor=2.0)

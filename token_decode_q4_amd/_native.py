@@ -19,7 +19,7 @@ QD_OK, QD_EINVAL, QD_ERANGE, QD_ENOMEM, QD_EUNSUPPORTED, QD_EHIP = 0, -1, -2, -3
 
 # every function declared in include/qd.h
 EXPORTS = ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate",
-           "qd_gemv_q4_0", "qd_gemv_q4_0_batch", "qd_attn_workspace_bytes", "qd_attn_decode", "qd_check",
+           "qd_gemv_q4_0", "qd_gemv_q4_0_batch", "qd_rope_inv_freq", "qd_attn_workspace_bytes", "qd_attn_decode", "qd_check",
            "qd_stream_read_groups", "qd_stream_read", "qd_last_error")
 
 
@@ -70,6 +70,12 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built: run python token_decode_q4_amd/build.py")
+        # torch first: its HIP runtime carries the same soname as the one the
+        # library links (libamdhip64.so.7), so the library binds to it and the
+        # process holds one HIP runtime, the one that owns the tensors passed
+        # in.  (Loaded on its own inside a process that later imports torch,
+        # the library's runtime has reported no device at its first call.)
+        import torch  # noqa: F401
         L = C.CDLL(LIB_PATH)
         L.qd_create.argtypes = [C.POINTER(Config), C.POINTER(Weights), C.c_void_p,
                                 C.POINTER(C.c_void_p)]
@@ -83,6 +89,8 @@ def lib():
                                    C.c_int32, C.c_void_p]
         L.qd_gemv_q4_0_batch.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
                                          C.c_int32, C.c_int32, C.c_void_p]
+        L.qd_rope_inv_freq.argtypes = [C.c_float, C.c_int32, C.c_int32, C.c_float, C.c_float,
+                                       C.c_float, C.c_float, C.c_void_p]
         L.qd_attn_workspace_bytes.restype = C.c_size_t
         L.qd_attn_workspace_bytes.argtypes = [C.c_int32] * 5
         L.qd_attn_decode.argtypes = [C.POINTER(AttnArgs), C.c_void_p, C.c_size_t, C.c_void_p]
@@ -133,6 +141,21 @@ def gemv_q4_0_batch(d, qs, x, y, stream=None) -> int:
     N = y.shape[1]
     return check(lib().qd_gemv_q4_0_batch(_ptr(d), _ptr(qs), _ptr(x), _ptr(y), N, K, B,
                                           _stream(stream)))
+
+
+ROPE_SCALING = {"default": 0, "linear": 1, "llama3": 2}
+
+
+def rope_inv_freq(theta: float, rot_dim: int, scaling: str = "default", factor: float = 1.0,
+                  low_freq_factor: float = 1.0, high_freq_factor: float = 4.0,
+                  original_max_pos: float = 8192.0) -> np.ndarray:
+    """f32 [rot_dim/2] rotary frequencies from the library (qd_rope_inv_freq)."""
+    if scaling not in ROPE_SCALING:
+        raise QdError(QD_EUNSUPPORTED, f"rotary scaling type {scaling!r} is not implemented")
+    out = np.empty(max(0, rot_dim // 2), dtype=np.float32)
+    check(lib().qd_rope_inv_freq(theta, rot_dim, ROPE_SCALING[scaling], factor, low_freq_factor,
+                                 high_freq_factor, original_max_pos, out.ctypes.data))
+    return out
 
 
 def stream_read_groups(nbytes: int) -> int:

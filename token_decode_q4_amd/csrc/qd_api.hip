@@ -857,6 +857,55 @@ extern "C" int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const
     return QD_OK;
 }
 
+// ------------------------------------------------------------------ rotary frequencies
+
+// inv_freq for qd_config (host only): theta^(-2i/rot_dim) for i < rot_dim/2,
+// evaluated in f64 and rounded to f32 once, with the rotary-scaling rules of
+// the inferencelayer cuda_llm.rs page (Cfg::rope_inv_freq): linear divides
+// every frequency by `factor`; llama3 divides the frequencies whose wavelength
+// 2*pi/f is above original_max_pos/low_freq_factor by `factor`, keeps those
+// below original_max_pos/high_freq_factor, and between the two blends
+// (1 - s) * f/factor + s * f with s = (original_max_pos/wavelength -
+// low_freq_factor) / (high_freq_factor - low_freq_factor).  Any other type is
+// refused, as on the page.
+extern "C" int qd_rope_inv_freq(float theta, int32_t rot_dim, int32_t scaling, float factor,
+                                float low_freq_factor, float high_freq_factor,
+                                float original_max_pos, float* out)
+{
+    if (!out)
+        return fail(QD_EINVAL, "null output");
+    if (rot_dim <= 0 || rot_dim % 2)
+        return fail(QD_EINVAL, "rot_dim %d must be positive and even", rot_dim);
+    if (!(theta > 1.0f) || !std::isfinite(theta))
+        return fail(QD_EINVAL, "theta %g must be finite and above 1", (double)theta);
+    if (scaling < QD_ROPE_DEFAULT || scaling > QD_ROPE_LLAMA3)
+        return fail(QD_EUNSUPPORTED, "rotary scaling type %d is not implemented", scaling);
+    const double fac = factor, lo = low_freq_factor, hi = high_freq_factor, orig = original_max_pos;
+    if (scaling != QD_ROPE_DEFAULT && !(fac > 0.0 && std::isfinite(fac)))
+        return fail(QD_EINVAL, "scaling factor %g must be finite and positive", fac);
+    if (scaling == QD_ROPE_LLAMA3 &&
+        !(lo > 0.0 && hi > lo && std::isfinite(hi) && orig > 0.0 && std::isfinite(orig)))
+        return fail(QD_EINVAL, "llama3 scaling needs 0 < low_freq_factor < high_freq_factor and "
+                    "original_max_pos > 0 (got %g, %g, %g)", lo, hi, orig);
+    const double pi = 3.14159265358979323846;
+    for (int i = 0; i < rot_dim / 2; ++i) {
+        double f = std::pow((double)theta, -2.0 * i / (double)rot_dim);
+        if (scaling == QD_ROPE_LINEAR) {
+            f /= fac;
+        } else if (scaling == QD_ROPE_LLAMA3) {
+            const double wl = 2.0 * pi / f;
+            if (wl > orig / lo) {
+                f /= fac;
+            } else if (wl >= orig / hi) {
+                const double sm = (orig / wl - lo) / (hi - lo);
+                f = (1.0 - sm) * (f / fac) + sm * f;
+            }
+        }
+        out[i] = (float)f;
+    }
+    return QD_OK;
+}
+
 // ------------------------------------------------------------------ batched GEMV
 
 // launch configuration of the batched GEMV: rows per slot, waves, block
