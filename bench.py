@@ -265,13 +265,16 @@ def gemv_batch_rows(batches=(1, 2, 4, 8), reps: int = 100, min_bytes: int = 1 <<
     return rows
 
 
-def attention_rows(reps: int = 100, min_bytes: int = 1 << 30):
+def attention_rows(reps: int = 100, min_bytes: int = 1 << 30, kv8: bool = False):
     """The isolated GQA decode attention (qd_attn_decode: split + combine) at
     the four cases (32 q / 8 kv heads, head_dim 128, paged block 16, shuffled
     tables): `reps` launches over >= 1 GiB of rotated K/V pool replicas in one
     graph; the output against the f64 oracle (normwise error) and the oracle's
     time on the host cores.  Algorithmic bytes = K/V rows read (sum of kv_len x
-    nkv x hd x 2 B x 2) + q and out (f32) + the block-table entries used."""
+    nkv x hd x 2 B x 2) + q and out (f32) + the block-table entries used.
+    kv8: the same cases over an fp8 e4m3 cache (qd_attn_decode_kv8; the f16
+    values through the harness quantizer, K/V scales 0.625 / 1.75): 1 byte
+    per K/V element."""
     import torch
     import oracle
     import synth
@@ -280,10 +283,16 @@ def attention_rows(reps: int = 100, min_bytes: int = 1 << 30):
     for name in sorted(synth.ATTN_CASES):
         a = synth.attn_case(name)
         max_kv = max(1, a.max_kv_len)
-        pool_bytes = a.k_pool.nbytes + a.v_pool.nbytes
+        ksc, vsc = 0.625, 1.75
+        if kv8:
+            k8 = synth.quantize_e4m3(a.k_pool.view(np.float16).astype(np.float64))
+            v8 = synth.quantize_e4m3(a.v_pool.view(np.float16).astype(np.float64))
+            pool_bytes = k8.nbytes + v8.nbytes
+        else:
+            pool_bytes = a.k_pool.nbytes + a.v_pool.nbytes
         copies = max(1, -(-min_bytes // pool_bytes))
-        k0 = torch.from_numpy(a.k_pool.view(np.int16)).cuda()
-        v0 = torch.from_numpy(a.v_pool.view(np.int16)).cuda()
+        k0 = torch.from_numpy(k8 if kv8 else a.k_pool.view(np.int16)).cuda()
+        v0 = torch.from_numpy(v8 if kv8 else a.v_pool.view(np.int16)).cuda()
         ks = [k0] + [k0.clone() for _ in range(copies - 1)]
         vs = [v0] + [v0.clone() for _ in range(copies - 1)]
         q = torch.from_numpy(np.ascontiguousarray(a.q)).cuda()
@@ -296,21 +305,29 @@ def attention_rows(reps: int = 100, min_bytes: int = 1 << 30):
         stream = torch.cuda.Stream()
 
         def launch(k):
-            qd.attn_decode(q, ks[k % copies], vs[k % copies], lens, max_kv, a.nkv, scale, out, ws,
-                           block_tables=tables, stream=stream)
+            if kv8:
+                qd.attn_decode_kv8(q, ks[k % copies], vs[k % copies], lens, max_kv, a.nkv, scale, ksc,
+                                   vsc, out, ws, block_tables=tables, stream=stream)
+            else:
+                qd.attn_decode(q, ks[k % copies], vs[k % copies], lens, max_kv, a.nkv, scale, out, ws,
+                               block_tables=tables, stream=stream)
 
         with torch.cuda.stream(stream):
             launch(0)
         stream.synchronize()
         got = out.cpu().numpy().astype(np.float64)
-        t_or, ref = _timed(lambda: oracle.attn_inputs(a), reps=1)
+        if kv8:
+            t_or, ref = _timed(lambda: oracle.attn_decode_e4m3(a.q, k8, v8, a.kv_lens, a.nkv, scale, ksc,
+                                                               vsc, a.block_tables), reps=1)
+        else:
+            t_or, ref = _timed(lambda: oracle.attn_inputs(a), reps=1)
         err = float(np.max(np.abs(got - ref)) / max(1e-300, float(np.max(np.abs(ref)))))
         us = _graph_time(stream, launch, reps)
         kv = [int(v) for v in a.kv_lens]
-        algo = (sum(kv) * a.nkv * a.hd * 2 * 2 + 2 * a.B * a.nq * a.hd * 4
+        algo = (sum(kv) * a.nkv * a.hd * (1 if kv8 else 2) * 2 + 2 * a.B * a.nq * a.hd * 4
                 + 4 * sum(-(-v // synth.ATTN_BLOCK) for v in kv))
         gbs = algo / (us * 1e-6) / 1e9
-        out_rows.append({"case": name, "batch": a.B, "kv_lens": kv if a.B <= 8 else None,
+        out_rows.append({"case": name, "kv": "fp8 e4m3" if kv8 else "f16", "batch": a.B, "kv_lens": kv if a.B <= 8 else None,
                          "mean_us": round(us, 3), "achieved": round(gbs, 1),
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": algo,
                          "pool_copies": copies, "normwise_err_vs_oracle": err,
@@ -497,9 +514,10 @@ def main():
             log(f"gemv batch {r['batch']} {r['shape']}: {r['mean_us']} us, {r['achieved']} GB/s "
                 f"({r['frac']:.3f}), {r['vectors_per_s']:.0f} vectors/s, err {r['normwise_err_vs_oracle']:.1e}")
         a_rows = attention_rows()
+        a_rows += attention_rows(kv8=True)
         for r in a_rows:
-            log(f"attention {r['case']}: {r['mean_us']} us, {r['achieved']} GB/s ({r['frac']:.3f}), "
-                f"err {r['normwise_err_vs_oracle']:.1e}, oracle {r['oracle_s']} s")
+            log(f"attention {r['case']} {r['kv']}: {r['mean_us']} us, {r['achieved']} GB/s "
+                f"({r['frac']:.3f}), err {r['normwise_err_vs_oracle']:.1e}, oracle {r['oracle_s']} s")
         d06 = decode_row("qwen3-0.6b") if args.config != "qwen3-0.6b" else None
         if d06:
             log(f"decode {d06['workload']}: {d06['tok_s']} tok/s ({d06['step_roofline']['frac']:.3f})")

@@ -224,6 +224,17 @@ size_t qd_attn_workspace_bytes(int32_t B, int32_t nq, int32_t nkv, int32_t head_
 int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t workspace_bytes,
                    qd_stream stream);
 
+/* The same attention over an fp8 KV cache (reduced-precision KV, the
+ * inferencelayer cuda_llm.rs page's KV-format discussion; OCP e4m3, 1 byte
+ * per element): a->k and a->v point at e4m3 bytes in the layouts above
+ * (element counts unchanged), 16-byte aligned; element value = e4m3 value *
+ * k_scale (K) or * v_scale (V), both finite and positive.  Arithmetic as
+ * qd_attn_decode (f16 matrix-core QK with q as an f16 hi + lo pair, f32
+ * softmax and PV).  Workspace as qd_attn_workspace_bytes.  Same errors;
+ * QD_EINVAL also for a bad scale or alignment.  No allocation; capturable. */
+int qd_attn_decode_kv8(const qd_attn_args* a, float k_scale, float v_scale, void* d_workspace,
+                       size_t workspace_bytes, qd_stream stream);
+
 /* Synchronises `stream` and reports what the device recorded since the last
  * check, then clears it: QD_ERANGE if a step saw a token or a position out of
  * range (a stored token or position the host did not validate), QD_EHIP if a

@@ -168,6 +168,40 @@ def rope_inv_freq(theta: float, rot_dim: int, scaling: str = "default", factor: 
     return np.array(out, dtype=np.float64)
 
 
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Exact values of OCP fp8 e4m3 codes (the fp8 KV cache): sign bit 7,
+    exponent bits 6..3 with bias 7, mantissa bits 2..0; exponent 0 is
+    subnormal (m * 2^-9); 0x7f and 0xff are NaN; there is no infinity."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    val = np.where(c >> 7, -mag, mag)
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+def attn_decode_e4m3(q, k8, v8, kv_lens, nkv: int, scale: float, k_scale: float, v_scale: float,
+                     block_tables=None, block_size: int = 16, contig_max_kv: int = 0,
+                     nthreads: int | None = None) -> np.ndarray:
+    """The attention of attn_decode over an fp8 e4m3 cache: K = e4m3(k8) *
+    k_scale, V = e4m3(v8) * v_scale.  Every e4m3 value is an f16 value, so the
+    decoded caches go to attn_decode as f16 bits unchanged; k_scale multiplies
+    every score (folded into the softmax scale) and v_scale every output."""
+    kv = e4m3_to_f64(k8)
+    vv = e4m3_to_f64(v8)
+    if np.isnan(kv).any() or np.isnan(vv).any():
+        raise ValueError("NaN code in the cache")
+    # exact (no rounding happens), checked on every element
+    kb = kv.astype(np.float16).view(np.uint16)
+    vb = vv.astype(np.float16).view(np.uint16)
+    if not (np.array_equal(kb.view(np.float16).astype(np.float64), kv)
+            and np.array_equal(vb.view(np.float16).astype(np.float64), vv)):
+        raise AssertionError("an e4m3 value was not exact in f16")
+    out = attn_decode(q, kb, vb, kv_lens, nkv, float(scale) * float(k_scale), block_tables,
+                      block_size, contig_max_kv, nthreads)
+    return out * float(v_scale)
+
+
 def attn_decode(q, k, v, kv_lens, nkv: int, scale: float, block_tables=None,
                 block_size: int = 16, contig_max_kv: int = 0,
                 nthreads: int | None = None) -> np.ndarray:

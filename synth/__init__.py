@@ -335,6 +335,37 @@ def batch_x(seed: int, B: int, K: int) -> np.ndarray:
         if B > 0 else np.zeros((0, K), np.float32)
 
 
+# --------------------------------------------------------------------------- fp8 e4m3 (harness)
+
+def _e4m3_table() -> np.ndarray:
+    """Values of the 256 OCP e4m3 codes (sign, 4-bit exponent with bias 7, 3-bit
+    mantissa; exponent 0 subnormal; 0x7f / 0xff NaN, no infinities)."""
+    c = np.arange(256)
+    sgn = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    v = sgn * mag
+    v[(c & 0x7F) == 0x7F] = np.nan
+    return v
+
+
+def quantize_e4m3(x: np.ndarray) -> np.ndarray:
+    """f32/f64 -> e4m3 code bytes, round to nearest (ties to the even code),
+    saturating at +-448 (input generation for the fp8 KV cases; NaN refused)."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.isnan(x).any():
+        raise ValueError("NaN has no finite e4m3 code")
+    pos = _e4m3_table()[:127]                      # codes 0 .. 126: 0 .. 448, increasing
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(pos, a, side="left"), 0, 126)
+    lo = np.maximum(hi - 1, 0)
+    dl, dh = a - pos[lo], pos[hi] - a
+    pick_hi = (dh < dl) | ((dh == dl) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)   # -0 keeps its sign
+
+
 # --------------------------------------------------------------------------- attention
 
 @dataclass

@@ -209,3 +209,26 @@ def test_rope_inv_freq_validation(qd):
     assert b"not implemented" in L.qd_last_error()
     with pytest.raises(qd.QdError):
         qd.rope_inv_freq(1e4, 64, "yarn", 2.0)
+
+
+def test_attention_kv8_validation(qd):
+    L = qd.lib()
+    A = qd._native.AttnArgs
+    E = qd._native.QD_EINVAL
+    good = dict(q=16, k=16, v=16, block_tables=16, max_blocks_per_seq=4, block_size=16, kv_lens=16,
+                max_kv_len=64, B=1, nq=32, nkv=8, head_dim=128, scale=0.1, out=16)
+
+    def call(ks=1.0, vs=1.0, **kw):
+        d = dict(good, **kw)
+        a = A(*[d[n] for n, _ in A._fields_])
+        return L.qd_attn_decode_kv8(C.byref(a), ks, vs, C.c_void_p(16), 1 << 30, None)
+
+    assert call(ks=0.0) == E
+    assert call(vs=-1.0) == E
+    assert call(ks=float("inf")) == E
+    assert b"scale" in L.qd_last_error()
+    assert call(k=24) == E
+    assert b"aligned" in L.qd_last_error()
+    assert call(head_dim=96) == qd._native.QD_EUNSUPPORTED
+    assert call(nq=12) == E                              # nq % nkv != 0
+    assert call(nq=48) == qd._native.QD_EUNSUPPORTED     # GQA group 6

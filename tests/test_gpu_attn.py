@@ -99,3 +99,69 @@ def test_attention_large_scores():
     got, _ = _run(a, scale=8.0)
     assert np.all(np.isfinite(got))
     assert normwise(got, ref) <= 1e-4
+
+
+# --------------------------------------------------------------------------- fp8 e4m3 cache
+
+KV8_SCALES = (0.625, 1.75)   # k_scale, v_scale (not powers of two)
+
+
+def _run_kv8(a: synth.AttnInputs, k8, v8, paged=True, contig=None):
+    import torch
+    import token_decode_q4_amd as qd
+    scale = 1.0 / np.sqrt(a.hd)
+    out = torch.full((a.B, a.nq, a.hd), float("nan"), dtype=torch.float32, device="cuda")
+    max_kv = max(1, a.max_kv_len)
+    ws = torch.zeros(qd.attn_workspace_bytes(a.B, a.nq, a.nkv, a.hd, max_kv), dtype=torch.uint8,
+                     device="cuda")
+    ks, vs = KV8_SCALES
+    if paged:
+        qd.attn_decode_kv8(dev(a.q), dev(k8), dev(v8), dev(a.kv_lens), max_kv, a.nkv, scale, ks, vs,
+                           out, ws, block_tables=dev(a.block_tables))
+    else:
+        kc, vc = contig
+        qd.attn_decode_kv8(dev(a.q), dev(kc), dev(vc), dev(a.kv_lens), max_kv, a.nkv, scale, ks, vs,
+                           out, ws)
+    return host(out)
+
+
+def _kv8_pools(a: synth.AttnInputs):
+    """the case's K/V values (f16 N(0,1)) in e4m3 through the harness quantizer"""
+    k = a.k_pool.view(np.float16).astype(np.float64)
+    v = a.v_pool.view(np.float16).astype(np.float64)
+    return synth.quantize_e4m3(k), synth.quantize_e4m3(v)
+
+
+def _ref_kv8(a, k8, v8, paged=True, contig_max_kv=0):
+    ks, vs = KV8_SCALES
+    return oracle.attn_decode_e4m3(a.q, k8, v8, a.kv_lens, a.nkv, 1.0 / np.sqrt(a.hd), ks, vs,
+                                   a.block_tables if paged else None, contig_max_kv=contig_max_kv)
+
+
+@pytest.mark.parametrize("name", sorted(synth.ATTN_CASES))
+def test_attention_kv8_config_cases_full(name):
+    say(f"attention fp8 case {name}")
+    a = synth.attn_case(name)
+    k8, v8 = _kv8_pools(a)
+    got = _run_kv8(a, k8, v8)
+    err = normwise(got, _ref_kv8(a, k8, v8))
+    say(f"attention fp8 {name}: normwise err {err:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("hd,nq,nkv", [(128, 32, 8), (64, 4, 2), (128, 16, 2), (64, 8, 1),
+                                       (128, 8, 8)])
+def test_attention_kv8_ragged_and_contiguous(hd, nq, nkv):
+    a = synth.random_attn(500 + hd + nq, 3, [0, 1, 37], nq=nq, nkv=nkv, hd=hd)
+    k8, v8 = _kv8_pools(a)
+    got = _run_kv8(a, k8, v8)
+    ref = _ref_kv8(a, k8, v8)
+    assert np.array_equal(got[0], np.zeros_like(got[0]))     # kv_len 0 -> zeros
+    assert normwise(got, ref) <= ATTN_TOL
+    # the same cache laid out contiguously: bitwise the same result
+    kc, vc = synth.contiguous_from_paged(a, max(1, a.max_kv_len))
+    kc8 = synth.quantize_e4m3(kc.view(np.float16).astype(np.float64))
+    vc8 = synth.quantize_e4m3(vc.view(np.float16).astype(np.float64))
+    got_c = _run_kv8(a, k8, v8, paged=False, contig=(kc8, vc8))
+    assert np.array_equal(got, got_c)

@@ -358,3 +358,52 @@ def test_rope_inv_freq_llama3_regions_and_continuity(oracle_lib):
 def test_rope_inv_freq_unknown_type_refused(oracle_lib):
     with pytest.raises(ValueError):
         oracle_lib.rope_inv_freq(1e4, 64, "yarn", factor=2.0)
+
+
+# --------------------------------------------------------------------------- fp8 e4m3 (KV cache)
+
+def test_e4m3_decode_all_codes_vs_torch(oracle_lib):
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle_lib.e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan) and nan.sum() == 2
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # closed forms: 1.0 = 0x38, max 448 = 0x7e, smallest subnormal 2^-9 = 0x01
+    assert ours[0x38] == 1.0 and ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9
+    assert ours[0xB8] == -1.0 and ours[0x80] == 0.0 and np.signbit(ours[0x80])
+
+
+def test_e4m3_harness_quantizer_vs_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 0.1, 1.0, 30.0)])
+    ours = synth.quantize_e4m3(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+    # ties go to the even code: 1 + 1/16 lies halfway between 0x38 and 0x39
+    assert synth.quantize_e4m3(np.array([1.0 + 1 / 16]))[0] == 0x38
+    assert synth.quantize_e4m3(np.array([1.0 + 3 / 16]))[0] == 0x3A
+    # saturation (torch would give NaN there)
+    assert list(synth.quantize_e4m3(np.array([1e4, -1e4, 449.0]))) == [0x7E, 0xFE, 0x7E]
+
+
+def test_attn_decode_e4m3_scales(oracle_lib):
+    """The fp8 attention is the f16 attention of the decoded values with K
+    scaled into the scores and V into the outputs: check against an explicit
+    f64 softmax on a small case."""
+    rng = np.random.default_rng(3)
+    B, nq, nkv, hd, T = 1, 4, 2, 64, 37
+    q = rng.standard_normal((B, nq, hd)).astype(np.float32)
+    k8 = synth.quantize_e4m3(rng.standard_normal((B, nkv, T, hd)))
+    v8 = synth.quantize_e4m3(rng.standard_normal((B, nkv, T, hd)))
+    ks, vs, sc = 0.75, 1.5, 0.125
+    got = oracle_lib.attn_decode_e4m3(q, k8, v8, np.array([T], np.int32), nkv, sc, ks, vs,
+                                      contig_max_kv=T)
+    K = oracle_lib.e4m3_to_f64(k8) * ks
+    V = oracle_lib.e4m3_to_f64(v8) * vs
+    for h in range(nq):
+        g = h // (nq // nkv)
+        s_ = K[0, g] @ q[0, h].astype(np.float64) * sc
+        p_ = np.exp(s_ - s_.max())
+        p_ /= p_.sum()
+        np.testing.assert_allclose(got[0, h], p_ @ V[0, g], rtol=1e-12, atol=1e-14)

@@ -19,7 +19,8 @@ QD_OK, QD_EINVAL, QD_ERANGE, QD_ENOMEM, QD_EUNSUPPORTED, QD_EHIP = 0, -1, -2, -3
 
 # every function declared in include/qd.h
 EXPORTS = ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate",
-           "qd_gemv_q4_0", "qd_gemv_q4_0_batch", "qd_rope_inv_freq", "qd_attn_workspace_bytes", "qd_attn_decode", "qd_check",
+           "qd_gemv_q4_0", "qd_gemv_q4_0_batch", "qd_rope_inv_freq", "qd_attn_workspace_bytes",
+           "qd_attn_decode_kv8", "qd_attn_decode", "qd_check",
            "qd_stream_read_groups", "qd_stream_read", "qd_last_error")
 
 
@@ -94,6 +95,8 @@ def lib():
         L.qd_attn_workspace_bytes.restype = C.c_size_t
         L.qd_attn_workspace_bytes.argtypes = [C.c_int32] * 5
         L.qd_attn_decode.argtypes = [C.POINTER(AttnArgs), C.c_void_p, C.c_size_t, C.c_void_p]
+        L.qd_attn_decode_kv8.argtypes = [C.POINTER(AttnArgs), C.c_float, C.c_float, C.c_void_p,
+                                         C.c_size_t, C.c_void_p]
         L.qd_check.argtypes = [C.c_void_p, C.c_void_p]
         L.qd_stream_read_groups.restype = C.c_size_t
         L.qd_stream_read_groups.argtypes = [C.c_size_t]
@@ -182,6 +185,19 @@ def attn_decode(q, k, v, kv_lens, max_kv_len, nkv, scale, out, workspace, block_
                  int(max_kv_len), B, nq, nkv, hd, float(scale), _ptr(out))
     return check(lib().qd_attn_decode(C.byref(a), _ptr(workspace), workspace.numel() *
                                       workspace.element_size(), _stream(stream)))
+
+
+def attn_decode_kv8(q, k8, v8, kv_lens, max_kv_len, nkv, scale, k_scale, v_scale, out, workspace,
+                    block_tables=None, block_size=16, stream=None) -> int:
+    """attn_decode over an fp8 e4m3 cache: k8 / v8 device uint8 pools (same
+    layouts as the f16 ones), element = e4m3 value * k_scale (K) or * v_scale (V)."""
+    B, nq, hd = q.shape
+    a = AttnArgs(_ptr(q), _ptr(k8), _ptr(v8), _ptr(block_tables),
+                 0 if block_tables is None else block_tables.shape[1], block_size, _ptr(kv_lens),
+                 int(max_kv_len), B, nq, nkv, hd, float(scale), _ptr(out))
+    return check(lib().qd_attn_decode_kv8(C.byref(a), float(k_scale), float(v_scale), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(),
+                                          _stream(stream)))
 
 
 # ----------------------------------------------------------------- model

@@ -62,6 +62,8 @@ struct AttnParams {
     const float* rope_cur;     // cos [rot/2] then sin [rot/2] at the step's position
     uint16_t* kc;              // cache written at pos (same buffers as k/v)
     uint16_t* vc;
+    // K/V in fp8 e4m3 (standalone only): element = e4m3 value * scale
+    float k_scale, v_scale;
 };
 
 constexpr int ATT_WK = 16;                 // keys per wave step (one paged block)
@@ -217,10 +219,11 @@ QD_DEV void attn_merge_last(const AttnParams& p, int b, int g, int kv_len, int* 
 // step's K/V loads are issued (they need nothing of this step) and before
 // anything of this step's q|k|v is read; q|k|v are read and the merged output
 // is stored agent-scope (other workgroups of the same launch wrote / read them).
-template <int HD, int GQ, bool PAGED, int QMODE, bool FUSED, class Wait>
+template <int HD, int GQ, bool PAGED, int QMODE, bool FUSED, bool KV8, class Wait>
 QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<HD, GQ>& sm, Wait&& wait)
 {
     static_assert(HD == 64 || HD == 128, "head_dim");
+    static_assert(!KV8 || (QMODE == 0 && !FUSED), "fp8 K/V: standalone attention only");
     static_assert(GQ == 1 || GQ == 2 || GQ == 4 || GQ == 8, "group");
     using Step = AttnStep<HD>;
     constexpr int NI = Step::NI, DPL = Step::DPL;
@@ -238,6 +241,36 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
     // masked where they are used
     auto load_step = [&](Step& st, int tw) {
         const int twc = min(tw, p.max_kv - 1);
+        if (KV8) {
+            // e4m3 bytes.  K: this lane takes the 8*NI contiguous dims
+            // kg*8*NI .. (the QK dim order of the fp8 path, matched by q).
+            // V: the lane's DPL bytes of each key.
+            const uint8_t* k8 = reinterpret_cast<const uint8_t*>(p.k);
+            const uint8_t* v8 = reinterpret_cast<const uint8_t*>(p.v);
+            size_t kb, vb;
+            if (PAGED) {
+                const int phys = max(0, p.tables[(size_t)b * p.mbps + twc / ATT_BS]);
+                const size_t base = kv_row<HD, PAGED>(p, phys, g, twc & ~(ATT_BS - 1));
+                kb = base + (size_t)kk * HD;
+                vb = base;
+            } else {
+                kb = kv_row<HD, PAGED>(p, b, g, min(tw + kk, p.max_kv - 1));
+                vb = kv_row<HD, PAGED>(p, b, g, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < NI / 2; ++i)
+                st.k[i] = *reinterpret_cast<const uint4*>(k8 + kb + 8 * NI * (lane >> 4) + 16 * i);
+#pragma unroll
+            for (int j = 0; j < ATT_WK; ++j) {
+                const size_t r = PAGED ? vb + (size_t)j * HD
+                                       : vb + (size_t)min(tw + j, p.max_kv - 1) * HD;
+                if (DPL == 2)
+                    st.v[j] = *reinterpret_cast<const uint16_t*>(v8 + r + lane * DPL);
+                else
+                    st.v[j] = v8[r + lane * DPL];
+            }
+            return;
+        }
         const uint16_t *kp, *vp;
         if (PAGED) {
             const int phys = max(0, p.tables[(size_t)b * p.mbps + twc / ATT_BS]);
@@ -372,7 +405,7 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
     for (int e = 0; e < DPL; ++e)
 #pragma unroll
         for (int j = 0; j < GQ; ++j)
-            sm.q[w][j][lane * DPL + e] = qv[j][e] * p.scale;
+            sm.q[w][j][lane * DPL + e] = qv[j][e] * (KV8 ? p.scale * p.k_scale : p.scale);
 
     // ---- now the position: the key range, and the wave whose step own_tw
     // holds the token's own position stores its K and V (f16) and uses them
@@ -419,7 +452,10 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
     for (int i = 0; i < NI; ++i) {
         const int col = lane & 15;
         float qf[8];
-        const float* src = &sm.q[w][col < GQ ? col : 0][32 * i + 8 * (lane >> 4)];
+        // dims of slice i in this lane group: 32i + 8kg .. (f16 K, the loads'
+        // order), or kg*8*NI + 8i .. (fp8 K: a lane loads contiguous dims)
+        const float* src = &sm.q[w][col < GQ ? col : 0][KV8 ? 8 * NI * (lane >> 4) + 8 * i
+                                                            : 32 * i + 8 * (lane >> 4)];
         const float4 q0 = *reinterpret_cast<const float4*>(src);
         const float4 q1 = *reinterpret_cast<const float4*>(src + 4);
         qf[0] = q0.x; qf[1] = q0.y; qf[2] = q0.z; qf[3] = q0.w;
@@ -462,7 +498,22 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
         floatx4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const half8 a = __builtin_bit_cast(half8, kr[i]);
+            half8 a;
+            if (KV8) {
+                // 8 e4m3 bytes of slice i -> f16 (exact: every e4m3 value is an f16 value)
+                const uint4 kq = kr[i / 2];
+                const uint32_t w0 = (i & 1) ? kq.z : kq.x, w1 = (i & 1) ? kq.w : kq.y;
+                const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+                const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+                const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+                const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+                a[0] = (_Float16)f0[0]; a[1] = (_Float16)f0[1];
+                a[2] = (_Float16)f1[0]; a[3] = (_Float16)f1[1];
+                a[4] = (_Float16)f2[0]; a[5] = (_Float16)f2[1];
+                a[6] = (_Float16)f3[0]; a[7] = (_Float16)f3[1];
+            } else {
+                a = __builtin_bit_cast(half8, kr[i]);
+            }
             sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bhi[i], sc, 0, 0, 0);
             sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, blo[i], sc, 0, 0, 0);
         }
@@ -520,9 +571,16 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
         for (int t = 0; t < ATT_WK; ++t) {
             float vf[DPL];
             const uint32_t vw = cur_st.v[t];
-            vf[0] = f16_to_f32((uint16_t)(vw & 0xffffu));
-            if (DPL == 2)
-                vf[DPL - 1] = f16_to_f32((uint16_t)(vw >> 16));
+            if (KV8) {
+                const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw, false);
+                vf[0] = f[0];
+                if (DPL == 2)
+                    vf[DPL - 1] = f[1];
+            } else {
+                vf[0] = f16_to_f32((uint16_t)(vw & 0xffffu));
+                if (DPL == 2)
+                    vf[DPL - 1] = f16_to_f32((uint16_t)(vw >> 16));
+            }
             if (own_here && t == slot) {
 #pragma unroll
                 for (int e = 0; e < DPL; ++e)
@@ -556,7 +614,7 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
     for (int j = 0; j < GQ; ++j) {
 #pragma unroll
         for (int e = 0; e < DPL; ++e)
-            sm.acc[w][j][lane * DPL + e] = acc[j][e];
+            sm.acc[w][j][lane * DPL + e] = KV8 ? acc[j][e] * p.v_scale : acc[j][e];
     }
     QD_MARK(7);
     __syncthreads();
@@ -595,11 +653,11 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
     QD_MARK(3);
 }
 
-template <int HD, int GQ, bool PAGED, int QMODE>
+template <int HD, int GQ, bool PAGED, int QMODE, bool KV8 = false>
 __global__ void __launch_bounds__(AttnMaxWaves<GQ>::value * WAVE) k_attn_split(AttnParams p)
 {
     __shared__ AttnSmem<HD, GQ> sm;
-    attn_split_body<HD, GQ, PAGED, QMODE, false>(p, (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z, sm,
+    attn_split_body<HD, GQ, PAGED, QMODE, false, KV8>(p, (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z, sm,
                                                  [] {});
 }
 

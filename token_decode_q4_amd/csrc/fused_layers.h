@@ -462,7 +462,7 @@ __global__ void __launch_bounds__(FUSED_THREADS) k_layer_fused(FusedArgs a, int 
             p.vc = Lw.vc;
             const int w = blockIdx.x;
             if (w < a.nsplit * a.nkv)
-                attn_split_body<HD, GQ, PAGED, 1, true>(p, w % a.nsplit, w / a.nsplit, 0, asm_, wait);
+                attn_split_body<HD, GQ, PAGED, 1, true, false>(p, w % a.nsplit, w / a.nsplit, 0, asm_, wait);
             else
                 wait();
         }

@@ -328,7 +328,7 @@ static int validate_config(const qd_config* c, const qd_weights* w)
 }
 
 // Launch the split-KV attention (split + combine).
-template <int QMODE>
+template <int QMODE, bool KV8 = false>
 static void launch_attention(const AttnParams& p, int waves, int hd, int gq, bool paged, int B,
                              int nq, hipStream_t s)
 {
@@ -337,9 +337,9 @@ static void launch_attention(const AttnParams& p, int waves, int hd, int gq, boo
 #define QD_ATT(HD_, GQ_)                                                                          \
     if (p.max_kv <= 0) {                                                                          \
     } else if (paged)                                                                             \
-        hipLaunchKernelGGL((k_attn_split<HD_, GQ_, true, QMODE>), grid, block, 0, s, p);          \
+        hipLaunchKernelGGL((k_attn_split<HD_, GQ_, true, QMODE, KV8>), grid, block, 0, s, p);     \
     else                                                                                          \
-        hipLaunchKernelGGL((k_attn_split<HD_, GQ_, false, QMODE>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((k_attn_split<HD_, GQ_, false, QMODE, KV8>), grid, block, 0, s, p);
     if (hd == 128) {
         if (gq == 1) { QD_ATT(128, 1) } else if (gq == 2) { QD_ATT(128, 2) }
         else if (gq == 4) { QD_ATT(128, 4) } else { QD_ATT(128, 8) }
@@ -1017,8 +1017,9 @@ extern "C" size_t qd_attn_workspace_bytes(int32_t B, int32_t nq, int32_t nkv, in
     return attn_ws_layout(B, nq, nkv, head_dim, max_kv_len, &g);
 }
 
-extern "C" int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t workspace_bytes,
-                              qd_stream stream)
+template <bool KV8>
+static int attn_decode_impl(const qd_attn_args* a, float k_scale, float v_scale, void* d_workspace,
+                            size_t workspace_bytes, qd_stream stream)
 {
     if (!a)
         return fail(QD_EINVAL, "null args");
@@ -1038,6 +1039,12 @@ extern "C" int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t w
             return fail(QD_EUNSUPPORTED, "block_size %d (only %d)", a->block_size, ATT_BS);
         if ((int64_t)a->max_blocks_per_seq * ATT_BS < a->max_kv_len)
             return fail(QD_EINVAL, "max_blocks_per_seq too small for max_kv_len");
+    }
+    if (KV8) {
+        if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+            return fail(QD_EINVAL, "fp8 K/V scales must be finite and positive");
+        if ((reinterpret_cast<uintptr_t>(a->k) | reinterpret_cast<uintptr_t>(a->v)) & 15)
+            return fail(QD_EINVAL, "fp8 K/V pools must be 16-byte aligned");
     }
     if (a->B == 0)
         return QD_OK;
@@ -1062,10 +1069,24 @@ extern "C" int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t w
     p.nsplit = geo.nsplit;
     p.part = reinterpret_cast<float*>(d_workspace);
     p.out = a->out;
-    launch_attention<0>(p, geo.waves, a->head_dim, gq, a->block_tables != nullptr, a->B, a->nq,
-                        (hipStream_t)stream);
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    launch_attention<0, KV8>(p, geo.waves, a->head_dim, gq, a->block_tables != nullptr, a->B, a->nq,
+                             (hipStream_t)stream);
     HIP_TRY(hipGetLastError());
     return QD_OK;
+}
+
+extern "C" int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t workspace_bytes,
+                              qd_stream stream)
+{
+    return attn_decode_impl<false>(a, 1.f, 1.f, d_workspace, workspace_bytes, stream);
+}
+
+extern "C" int qd_attn_decode_kv8(const qd_attn_args* a, float k_scale, float v_scale,
+                                  void* d_workspace, size_t workspace_bytes, qd_stream stream)
+{
+    return attn_decode_impl<true>(a, k_scale, v_scale, d_workspace, workspace_bytes, stream);
 }
 
 extern "C" int qd_check(qd_model* m, qd_stream stream)
