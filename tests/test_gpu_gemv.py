@@ -85,8 +85,15 @@ def _gemv_batch(W, X):
     return host(Y)
 
 
+# Batched bar: normwise 1e-5.  From 6 vectors the matrix-core kernel runs (f16
+# hi + lo operands, exact products, matrix-core f32 accumulation): measured
+# 1.4e-6 .. 2.9e-6 against the f64 oracle, 0.3e-6 for the vector kernel; the
+# GEMV bar itself is 1e-3.
+BATCH_BAR = 1e-5
+
+
 @pytest.mark.parametrize("idx", range(len(synth.GEMV_SHAPES)))
-@pytest.mark.parametrize("B", [2, 8])
+@pytest.mark.parametrize("B", [2, 6, 8])
 def test_gemv_batch_sweep_shape(idx, B):
     """Y[b] = W X[b] at the sweep shapes, every column against the f64 oracle."""
     N, K = synth.GEMV_SHAPES[idx]
@@ -99,7 +106,7 @@ def test_gemv_batch_sweep_shape(idx, B):
     assert np.all(np.isfinite(Y))
     for b in range(B):
         err = normwise(Y[b], oracle.gemv(W, X[b]))
-        assert err <= 2e-6, (b, err)
+        assert err <= BATCH_BAR, (b, err)
 
 
 def _f32_bound(W, x):
@@ -138,7 +145,7 @@ def test_gemv_batch_equals_single_per_column():
     Y = _gemv_batch(W, X)
     for b in range(8):
         y1 = _gemv(W, X[b])
-        assert normwise(Y[b], y1.astype(np.float64)) <= 1e-6
+        assert normwise(Y[b], y1.astype(np.float64)) <= BATCH_BAR
 
 
 def test_gemv_batch_special_values():

@@ -14,6 +14,7 @@
 #include "fused_layers.h"
 #include "gemv_cfg.h"
 #include "gemv_batch.h"
+#include "gemv_batch_mfma.h"
 #include "stream_read.h"
 
 #include <algorithm>
@@ -946,11 +947,24 @@ static hipError_t launch_gemv_batch_l(const uint16_t* d, const uint8_t* q, const
     return hipGetLastError();
 }
 
+// the matrix-core kernel from QD_BATCH_MFMA_MIN vectors on (measured faster at
+// 6 and more at 24576 x 4096; below that the vector kernel is faster)
+#ifndef QD_BATCH_MFMA_MIN
+#define QD_BATCH_MFMA_MIN 6
+#endif
+constexpr int GBM_GRID_CAP = 1024;
+
 template <int NC>
 static hipError_t launch_gemv_batch(const uint16_t* d, const uint8_t* q, const float* x, float* y,
                                     int N, int K, hipStream_t s)
 {
     const int nb = K / 32;
+    if (NC >= QD_BATCH_MFMA_MIN) {
+        const int ntiles = (N + GBM_ROWS - 1) / GBM_ROWS;
+        hipLaunchKernelGGL((k_gemv_batch_mfma<NC>), dim3(std::max(1, std::min(ntiles, GBM_GRID_CAP))),
+                           dim3(GBM_NW * WAVE), gemv_batch_mfma_lds_bytes(NC), s, d, q, x, y, N, nb);
+        return hipGetLastError();
+    }
     if (pick_lpr(nb, 16) == 16)
         return launch_gemv_batch_l<NC, 16>(d, q, x, y, N, nb, s);
     return launch_gemv_batch_l<NC, 8>(d, q, x, y, N, nb, s);
