@@ -221,7 +221,7 @@ def gemv_sweep_rows(reps: int = 100, min_bytes: int = 1 << 30):
                   "note": "byte-weighted over the five shapes: total bytes / total mean launch time"}
 
 
-def gemv_batch_rows(batches=(1, 2, 4, 8), reps: int = 100, min_bytes: int = 1 << 30):
+def gemv_batch_rows(batches=(1, 2, 4, 8, 16), reps: int = 100, min_bytes: int = 1 << 30):
     """The batched GEMV (qd_gemv_q4_0_batch) at the gate|up shape 24576 x 4096:
     Y[b] = W X[b] for B vectors, every weight read once; `reps` launches over
     >= 1 GiB of rotated weight copies in one graph.  Algorithmic bytes =

@@ -161,11 +161,13 @@ int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x
  * head-to-head of its q4 GEMV arm at M = 1 .. 16 tokens): Y[b] = W X[b] for
  * b < B, every weight read once for the whole batch.  W as for qd_gemv_q4_0;
  * d_x device f32 [B][K] and d_y device f32 [B][N], both contiguous; qs and x
- * 16-byte aligned.  1 <= B <= 8 and B*K <= 32 768 (the batch is staged in
- * LDS), N < 2^24, N*K/2 < 2^32; QD_EINVAL / QD_EUNSUPPORTED otherwise, with
- * nothing enqueued.  B == 1 runs the single-vector kernel.  Each output is
- * the same f32 sum of exact products as the single-vector GEMV (its order
- * may differ).  No allocation; capturable. */
+ * 16-byte aligned.  1 <= B <= 16; B == 1 runs the single-vector kernel,
+ * 2 <= B <= 5 a vector kernel that stages the whole batch in LDS (B*K <=
+ * 32 768), B >= 6 the matrix cores (any K; the weight scales must satisfy
+ * |d| < 8192, since (code - 8) * d is formed in f16).  N < 2^24,
+ * N*K/2 < 2^32.  QD_EINVAL / QD_EUNSUPPORTED otherwise, with nothing
+ * enqueued.  Products are exact in f32 on every path; the summation order
+ * differs from the single-vector GEMV.  No allocation; capturable. */
 int qd_gemv_q4_0_batch(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x, float* d_y,
                        int32_t N, int32_t K, int32_t B, qd_stream stream);
 

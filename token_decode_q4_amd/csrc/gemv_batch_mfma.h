@@ -1,5 +1,5 @@
 // gemv_batch_mfma.h -- batched q4_0 GEMV on the matrix cores (gfx950):
-// Y[b] = W X[b] for 2 <= B <= 8 vectors, every weight read once.
+// Y[b] = W X[b] for 2 <= B <= 16 vectors, every weight read once.
 //
 // The batched decode of the inferencelayer cuda_llm.rs page (its q4 GEMV arm
 // against the bf16 GEMM arm at M = 1 .. 16 tokens, section on the batched
@@ -24,9 +24,11 @@
 // values 1024 + code; a packed f16 add of -1032 leaves code - 8, exactly.
 //
 // x is staged per chunk of 32 blocks in LDS, already in the B-operand
-// layout: [block][word][vector][8 hi, 8 lo] halves.  The weight loads of the
-// next chunk are issued before the current one is computed (two register
-// buffers, the chunk loop unrolled by two).
+// layout: [block][word][vector][8 hi, 8 lo] halves.  The weight loads (two
+// register buffers, the chunk loop unrolled by two) and the x loads (one
+// buffer, refilled as soon as it is staged) of the next chunk are issued
+// before the current one is computed, so staging a chunk is conversions and
+// LDS writes only.
 #pragma once
 
 #include "qd_common.h"
@@ -37,6 +39,7 @@ typedef _Float16 gbm_half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 gbm_half2 __attribute__((ext_vector_type(2)));
 typedef float gbm_floatx4 __attribute__((ext_vector_type(4)));
 
+constexpr int GBM_MAXB = 16;   // vectors per launch
 constexpr int GBM_KC = 32;     // blocks per staged chunk
 constexpr int GBM_NW = 4;      // waves per workgroup
 constexpr int GBM_ROWS = 64;   // rows per workgroup tile
@@ -70,10 +73,20 @@ QD_DEV void gbm_a_operand(uint32_t w, gbm_half2 d2, gbm_half8& hi, gbm_half8& lo
     }
 }
 
+// staging items (block, word, vector) per thread per chunk
 template <int NC>
+struct GbmItems {
+    static constexpr int N = (GBM_KC * 4 * NC + GBM_NW * WAVE - 1) / (GBM_NW * WAVE);
+};
+
 struct GbmBuf {
-    uint4 q[GBM_KC / 4];       // block 4j + kg of this lane's row, j = 0..7
-    uint32_t d[GBM_KC / 4];    // its f16 scale
+    uint4 q[GBM_KC / 4];               // block 4j + kg of this lane's row, j = 0..7
+    uint32_t d[GBM_KC / 4];            // its f16 scale
+};
+template <int NC>
+struct GbmX {
+    float4 xa[GbmItems<NC>::N];        // x of this thread's staging items: elements 4w .. 4w+3
+    float4 xb[GbmItems<NC>::N];        //   and 16+4w .. 16+4w+3
 };
 
 template <int NC>
@@ -81,7 +94,8 @@ __global__ void __launch_bounds__(GBM_NW* WAVE)
 k_gemv_batch_mfma(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                   const float* __restrict__ X, float* __restrict__ Y, int N, int nb)
 {
-    static_assert(NC >= 2 && NC <= 8, "batch");
+    static_assert(NC >= 2 && NC <= 16, "batch");
+    constexpr int NITEM = GBM_KC * 4 * NC;   // staging items of a chunk
     extern __shared__ __align__(16) _Float16 xs[];   // [KC][4][NC][16]
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
@@ -95,8 +109,10 @@ k_gemv_batch_mfma(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
         const int row0 = tile * GBM_ROWS + wave * 16;
         const uint32_t rb = (uint32_t)min(row0 + r, N - 1) * (uint32_t)nb;
 
-        // weight loads of chunk c (clamped: never a branch around a load)
-        auto load = [&](GbmBuf<NC>& bf, int c) {
+        // weight and x loads of chunk c (clamped: never a branch around a
+        // load; x of a block past nb is zeroed where it is staged).  Staging
+        // item i = (block, word, vector) takes 8 values of x.
+        auto load = [&](GbmBuf& bf, int c) {
 #pragma unroll
             for (int j = 0; j < GBM_KC / 4; ++j) {
                 const uint32_t blk = rb + (uint32_t)min(c * GBM_KC + 4 * j + kg, nb - 1);
@@ -104,24 +120,32 @@ k_gemv_batch_mfma(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                 bf.d[j] = D[blk];
             }
         };
-        // stage x of chunk c: item i = (block, word, vector), 8 values each
-        auto stage = [&](int c) {
-            __syncthreads();   // the previous chunk's reads are done
-            for (int i = threadIdx.x; i < GBM_KC * 4 * NC; i += GBM_NW * WAVE) {
-                const int v = i % NC, w = (i / NC) & 3, bl = i / (4 * NC);
-                const int b = c * GBM_KC + bl;
-                float e[8];
-                if (b < nb) {
-                    const float* xp = X + (size_t)v * K + (size_t)b * 32 + 4 * w;
-                    const float4 a = *reinterpret_cast<const float4*>(xp);
-                    const float4 h = *reinterpret_cast<const float4*>(xp + 16);
-                    e[0] = a.x; e[1] = a.z; e[2] = a.y; e[3] = a.w;
-                    e[4] = h.x; e[5] = h.z; e[6] = h.y; e[7] = h.w;
-                } else {
+        auto load_x = [&](GbmX<NC>& bf, int c) {
 #pragma unroll
-                    for (int k = 0; k < 8; ++k)
-                        e[k] = 0.f;
-                }
+            for (int u = 0; u < GbmItems<NC>::N; ++u) {
+                const int i = min((int)threadIdx.x + u * GBM_NW * WAVE, NITEM - 1);
+                const int v = i % NC, w = (i / NC) & 3, bl = i / (4 * NC);
+                const int b = min(c * GBM_KC + bl, nb - 1);
+                const float* xp = X + (size_t)v * K + (size_t)b * 32 + 4 * w;
+                bf.xa[u] = *reinterpret_cast<const float4*>(xp);
+                bf.xb[u] = *reinterpret_cast<const float4*>(xp + 16);
+            }
+        };
+        // stage x of chunk c from the registers of its loads
+        auto stage = [&](const GbmX<NC>& bf, int c) {
+            __syncthreads();   // the previous chunk's reads are done
+#pragma unroll
+            for (int u = 0; u < GbmItems<NC>::N; ++u) {
+                const int i = (int)threadIdx.x + u * GBM_NW * WAVE;
+                if (i >= NITEM)   // uniform except in the last round of an odd batch
+                    continue;
+                const int bl = i / (4 * NC);
+                const bool in = c * GBM_KC + bl < nb;
+                const float4 a = bf.xa[u], h = bf.xb[u];
+                float e[8] = {a.x, a.z, a.y, a.w, h.x, h.z, h.y, h.w};
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    e[k] = in ? e[k] : 0.f;
                 gbm_half8 xh, xl;
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
@@ -136,7 +160,7 @@ k_gemv_batch_mfma(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
             __syncthreads();
         };
         gbm_floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        auto compute = [&](const GbmBuf<NC>& bf) {
+        auto compute = [&](const GbmBuf& bf) {
 #pragma unroll
             for (int j = 0; j < GBM_KC / 4; ++j) {
                 const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)bf.d[j]);
@@ -157,15 +181,19 @@ k_gemv_batch_mfma(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                 }
             }
         };
-        GbmBuf<NC> b0, b1;
+        GbmBuf b0, b1;
+        GbmX<NC> xr;
         load(b0, 0);
+        load_x(xr, 0);
         for (int c = 0; c < nch; c += 2) {
+            stage(xr, c);
             load(b1, min(c + 1, nch - 1));
-            stage(c);
+            load_x(xr, min(c + 1, nch - 1));
             compute(b0);
             if (c + 1 < nch) {   // uniform
+                stage(xr, c + 1);
                 load(b0, min(c + 2, nch - 1));
-                stage(c + 1);
+                load_x(xr, min(c + 2, nch - 1));
                 compute(b1);
             }
         }

@@ -959,15 +959,17 @@ static hipError_t launch_gemv_batch(const uint16_t* d, const uint8_t* q, const f
                                     int N, int K, hipStream_t s)
 {
     const int nb = K / 32;
-    if (NC >= QD_BATCH_MFMA_MIN) {
+    static_assert(QD_BATCH_MFMA_MIN >= 2 && QD_BATCH_MFMA_MIN <= GB_MAXB + 1, "kernel switch");
+    if constexpr (NC >= QD_BATCH_MFMA_MIN) {
         const int ntiles = (N + GBM_ROWS - 1) / GBM_ROWS;
         hipLaunchKernelGGL((k_gemv_batch_mfma<NC>), dim3(std::max(1, std::min(ntiles, GBM_GRID_CAP))),
                            dim3(GBM_NW * WAVE), gemv_batch_mfma_lds_bytes(NC), s, d, q, x, y, N, nb);
         return hipGetLastError();
+    } else {
+        if (pick_lpr(nb, 16) == 16)
+            return launch_gemv_batch_l<NC, 16>(d, q, x, y, N, nb, s);
+        return launch_gemv_batch_l<NC, 8>(d, q, x, y, N, nb, s);
     }
-    if (pick_lpr(nb, 16) == 16)
-        return launch_gemv_batch_l<NC, 16>(d, q, x, y, N, nb, s);
-    return launch_gemv_batch_l<NC, 8>(d, q, x, y, N, nb, s);
 }
 
 extern "C" int qd_gemv_q4_0_batch(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x,
@@ -977,11 +979,11 @@ extern "C" int qd_gemv_q4_0_batch(const uint16_t* d_scales, const uint8_t* d_qs,
         return fail(QD_EINVAL, "null pointer");
     if (N < 0 || K < 0 || K % 32)
         return fail(QD_EINVAL, "bad shape N=%d K=%d (K %% 32 must be 0)", N, K);
-    if (B < 1 || B > GB_MAXB)
-        return fail(QD_EINVAL, "batch B=%d outside [1, %d]", B, GB_MAXB);
-    if ((int64_t)B * K > GB_MAXKB)
-        return fail(QD_EUNSUPPORTED, "B*K = %lld above %d (the batch is staged in LDS)",
-                    (long long)B * K, GB_MAXKB);
+    if (B < 1 || B > GBM_MAXB)
+        return fail(QD_EINVAL, "batch B=%d outside [1, %d]", B, GBM_MAXB);
+    if (B < QD_BATCH_MFMA_MIN && (int64_t)B * K > GB_MAXKB)
+        return fail(QD_EUNSUPPORTED, "B*K = %lld above %d for B < %d (the batch is staged in LDS)",
+                    (long long)B * K, GB_MAXKB, QD_BATCH_MFMA_MIN);
     if (B == 1 && gemv_lds_bytes(K / 32) > (size_t)GEMV_MAX_LDS)
         return fail(QD_EUNSUPPORTED, "K=%d above the staged-x limit", K);
     if ((uint64_t)N * (uint64_t)K / 2 >= (uint64_t)1 << 32 || N >= (1 << 24))
@@ -1005,7 +1007,15 @@ extern "C" int qd_gemv_q4_0_batch(const uint16_t* d_scales, const uint8_t* d_qs,
     case 5: HIP_TRY(launch_gemv_batch<5>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
     case 6: HIP_TRY(launch_gemv_batch<6>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
     case 7: HIP_TRY(launch_gemv_batch<7>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    default: HIP_TRY(launch_gemv_batch<8>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    case 8: HIP_TRY(launch_gemv_batch<8>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    case 9: HIP_TRY(launch_gemv_batch<9>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    case 10: HIP_TRY(launch_gemv_batch<10>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    case 11: HIP_TRY(launch_gemv_batch<11>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    case 12: HIP_TRY(launch_gemv_batch<12>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    case 13: HIP_TRY(launch_gemv_batch<13>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    case 14: HIP_TRY(launch_gemv_batch<14>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    case 15: HIP_TRY(launch_gemv_batch<15>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
+    default: HIP_TRY(launch_gemv_batch<16>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
     }
     return QD_OK;
 }
