@@ -137,7 +137,7 @@ def gemv_roofline(reps: int = 100, min_bytes: int = 1 << 30):
             "mean_us": round(us, 3), "bytes_per_launch": algo, "weight_copies": copies}
 
 
-TIMED_REPLAYS = 5
+TIMED_REPLAYS = 10
 
 
 def _graph_time(stream, launch, reps: int, replays: int = TIMED_REPLAYS) -> float:
