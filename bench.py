@@ -54,14 +54,15 @@ def q4_bytes(rows: int, cols: int) -> int:
     return rows * cols * 18 // 32
 
 
-def step_bytes(s, kv_len: int) -> int:
+def step_bytes(s, kv_len: int, kv_bytes: int = 2) -> int:
     """Algorithmic HBM bytes of one decode step at context kv_len (K/V read for
     kv_len positions, one position written): q4_0 weights (+ the embedding row),
-    f32 norm vectors, the f16 KV traffic."""
+    f32 norm vectors, the K/V traffic at kv_bytes per element (2 for the f16
+    cache, 1 for fp8)."""
     H, I, hd, nq, nkv, V, L = s.hidden, s.intermediate, s.head_dim, s.n_heads, s.n_kv, s.vocab, s.layers
     per_layer = (q4_bytes((nq + 2 * nkv) * hd, H) + q4_bytes(H, nq * hd) + q4_bytes(2 * I, H)
                  + q4_bytes(H, I) + 4 * (2 * H + 2 * hd))
-    kv = L * (kv_len * nkv * hd * 2 * 2 + nkv * hd * 2 * 2)
+    kv = L * (kv_len * nkv * hd * kv_bytes * 2 + nkv * hd * kv_bytes * 2)
     return L * per_layer + q4_bytes(V, H) + q4_bytes(1, H) + 4 * H + kv
 
 
@@ -437,6 +438,8 @@ def main():
     ap.add_argument("--config", default="qwen3-8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--kv-fp8", action="store_true",
+                    help="fp8 e4m3 K/V cache (qd_config.kv_fp8; k_scale 0.5, v_scale 0.125)")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the per-row legs (GEMV sweep shapes, attention cases, 0.6B decode)")
     ap.add_argument("--layer-kernel", type=int, default=0,
@@ -461,7 +464,8 @@ def main():
     if P - 1 + args.warmup + args.steps > s.max_seq:
         sys.exit(f"warmup + steps must be <= {s.max_seq - P + 1}")
     t0 = time.time()
-    model = qd.Model(mi, use_graph=True, layer_kernel=bool(args.layer_kernel))
+    model = qd.Model(mi, use_graph=True, layer_kernel=bool(args.layer_kernel), kv_fp8=args.kv_fp8,
+                     k_scale=0.5, v_scale=0.125)
     log(f"qd_create {time.time() - t0:.1f}s")
     stream = torch.cuda.current_stream()
     toks = torch.empty(s.max_seq, dtype=torch.int32, device="cuda")
@@ -483,7 +487,7 @@ def main():
     ms = e0.elapsed_time(e1)
     tok_s = args.steps / (ms * 1e-3)
     kv_lens = np.arange(pos + 1, pos + args.steps + 1)
-    mean_bytes = float(np.mean([step_bytes(s, int(k)) for k in kv_lens]))
+    mean_bytes = float(np.mean([step_bytes(s, int(k), 1 if args.kv_fp8 else 2) for k in kv_lens]))
     step_gbs = mean_bytes / (ms * 1e-3 / args.steps) / 1e9
     log(f"decode {args.steps} steps: {ms:.2f} ms, {tok_s:.1f} tok/s, {step_gbs:.0f} GB/s")
     model.check()   # raises if the device recorded an error during the run
@@ -540,7 +544,9 @@ def main():
                                f"after a {P}-token sequential-decode prefill",
                    "layers": s.layers, "hidden": s.hidden, "heads": f"{s.n_heads}/{s.n_kv}",
                    "head_dim": s.head_dim, "intermediate": s.intermediate, "vocab": s.vocab,
-                   "kv": "paged f16, block 16, shuffled table" if s.kv_paged else "contiguous f16",
+                   "kv": ("paged " if s.kv_paged else "contiguous ")
+                         + ("fp8 e4m3 (k_scale 0.5, v_scale 0.125)" if args.kv_fp8 else "f16")
+                         + (", block 16, shuffled table" if s.kv_paged else ""),
                    "batch": 1, "parallelism": "single GPU",
                    "kernels": "one persistent launch per layer" if args.layer_kernel else "five per layer"},
         "step_roofline": {"bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS,

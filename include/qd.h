@@ -97,6 +97,13 @@ typedef struct {
  *            device that keeps one 512-thread workgroup per CU resident;
  *            QD_EUNSUPPORTED otherwise.  Same results up to f32 rounding
  *            order (the RMSNorm partial sums are grouped differently).
+ *   kv_fp8:  0 = f16 K/V cache; 1 = fp8 e4m3 cache (OCP e4m3, 1 byte per
+ *            element): the step stores e4m3(k / k_scale) and e4m3(v /
+ *            v_scale), rounded to nearest even and saturated at +-448, and the
+ *            attention reads value * scale (as qd_attn_decode_kv8).  k_scale
+ *            and v_scale finite and positive; not with layer_kernel = 1
+ *            (QD_EUNSUPPORTED).  Fields past layer_kernel: a caller that
+ *            zero-fills the struct gets the f16 cache.
  * Supported: head_dim 64 or 128; n_heads / n_kv in {1, 2, 4, 8};
  * kv_block_size 16; hidden, intermediate and n_heads*head_dim multiples of 32. */
 typedef struct {
@@ -111,6 +118,8 @@ typedef struct {
     const int32_t* block_table;
     int32_t use_graph;
     int32_t layer_kernel;
+    int32_t kv_fp8;
+    float k_scale, v_scale;
 } qd_config;
 
 typedef struct qd_model qd_model;

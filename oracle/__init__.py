@@ -31,7 +31,8 @@ class _Cfg(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("hidden", "layers", "n_heads", "n_kv", "head_dim",
                                          "intermediate", "vocab", "rot_dim", "qk_norm",
                                          "max_seq", "kv_round")] + \
-               [("eps", C.c_double), ("inv_freq", C.c_void_p)]
+               [("eps", C.c_double), ("inv_freq", C.c_void_p), ("k_scale", C.c_double),
+                ("v_scale", C.c_double)]
 
 
 def lib():
@@ -47,6 +48,10 @@ def lib():
         L.or_f16_to_f64.argtypes = [C.c_uint16]
         L.or_f64_to_f16.restype = C.c_uint16
         L.or_f64_to_f16.argtypes = [C.c_double]
+        L.or_e4m3_to_f64.restype = C.c_double
+        L.or_e4m3_to_f64.argtypes = [C.c_uint8]
+        L.or_f64_to_e4m3.restype = C.c_uint8
+        L.or_f64_to_e4m3.argtypes = [C.c_double]
         L.or_dequant_q4_0.argtypes = [C.POINTER(_Q4), C.c_void_p]
         L.or_gemv_q4_0.argtypes = [C.POINTER(_Q4), C.c_void_p, C.c_void_p, C.c_int]
         L.or_rmsnorm.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_double, C.c_void_p]
@@ -168,6 +173,21 @@ def rope_inv_freq(theta: float, rot_dim: int, scaling: str = "default", factor: 
     return np.array(out, dtype=np.float64)
 
 
+def f64_to_e4m3(vals) -> np.ndarray:
+    """fp8 e4m3 codes of f64 values (qd_oracle.c or_f64_to_e4m3: round to
+    nearest even, saturating at +-448)."""
+    L = lib()
+    v = np.asarray(vals, dtype=np.float64)
+    return np.array([L.or_f64_to_e4m3(float(x)) for x in v.ravel()], dtype=np.uint8).reshape(v.shape)
+
+
+def e4m3_to_f64_c(codes) -> np.ndarray:
+    """qd_oracle.c's own e4m3 decode (the one its model uses)."""
+    L = lib()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([L.or_e4m3_to_f64(int(x)) for x in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
 def e4m3_to_f64(codes) -> np.ndarray:
     """Exact values of OCP fp8 e4m3 codes (the fp8 KV cache): sign bit 7,
     exponent bits 6..3 with bias 7, mantissa bits 2..0; exponent 0 is
@@ -236,7 +256,11 @@ def attn_inputs(a, nthreads: int | None = None) -> np.ndarray:
 class Model:
     """The oracle decoder over a ``synth.ModelInputs``; KV cache kept inside."""
 
-    def __init__(self, mi, nthreads: int | None = None, kv_round: bool = True):
+    def __init__(self, mi, nthreads: int | None = None, kv_round: bool = True,
+                 kv_fp8: bool = False, k_scale: float = 1.0, v_scale: float = 1.0):
+        """kv_round: K/V stored as binary16 (the method) or kept in f64 (for
+        pins); kv_fp8: stored as fp8 e4m3 of value / k_scale (K) and value /
+        v_scale (V) instead."""
         s = mi.shape
         self.mi = mi
         self.vocab = s.vocab
@@ -254,8 +278,9 @@ class Model:
         self._final = np.ascontiguousarray(mi.final_norm, dtype=np.float32)
         self._inv = np.ascontiguousarray(mi.inv_freq, dtype=np.float32)
         self._cfg = _Cfg(s.hidden, s.layers, s.n_heads, s.n_kv, s.head_dim, s.intermediate,
-                         s.vocab, s.rot_dim, int(s.qk_norm), s.max_seq, int(kv_round),
-                         float(s.eps), _p(self._inv))
+                         s.vocab, s.rot_dim, int(s.qk_norm), s.max_seq,
+                         2 if kv_fp8 else int(kv_round), float(s.eps), _p(self._inv),
+                         float(k_scale), float(v_scale))
         self.nthreads = nthreads or default_threads()
         h = lib().or_model_create(C.byref(self._cfg), C.byref(self._embed), self._layers,
                                   _p(self._final), C.byref(self._lm), self.nthreads)

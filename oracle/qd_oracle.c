@@ -302,8 +302,44 @@ void or_model_destroy(or_model* m)
     free(m);
 }
 
-static double kv_store(const or_model* m, double val)
+double or_e4m3_to_f64(uint8_t c)
 {
+    const int e = (c >> 3) & 15, mant = c & 7;
+    if ((c & 0x7F) == 0x7F)
+        return NAN;
+    const double mag = e == 0 ? ldexp((double)mant, -9) : ldexp(1.0 + mant / 8.0, e - 7);
+    return (c & 0x80) ? -mag : mag;
+}
+
+uint8_t or_f64_to_e4m3(double v)
+{
+    if (isnan(v))
+        return 0x7F;
+    const uint8_t sgn = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    if (a > 448.0)
+        a = 448.0;                                   /* saturate */
+    if (a < ldexp(1.0, -6)) {                        /* subnormal: multiples of 2^-9 */
+        const int mant = (int)nearbyint(ldexp(a, 9)); /* 0 .. 8; 8 is the smallest normal */
+        return (uint8_t)(sgn | mant);
+    }
+    int e;
+    const double f = frexp(a, &e);                   /* a = (2f) * 2^(e-1), 2f in [1, 2) */
+    int E = e - 1;
+    int mant = (int)nearbyint((2.0 * f - 1.0) * 8.0);
+    if (mant == 8) {                                 /* rounded up to the next power of two */
+        mant = 0;
+        E += 1;
+    }
+    return (uint8_t)(sgn | ((E + 7) << 3) | mant);
+}
+
+static double kv_store(const or_model* m, double val, int which_v)
+{
+    if (m->cfg.kv_round == 2) {
+        const double sc = which_v ? m->cfg.v_scale : m->cfg.k_scale;
+        return or_e4m3_to_f64(or_f64_to_e4m3(val / sc)) * sc;
+    }
     return m->cfg.kv_round ? or_f16_to_f64(or_f64_to_f16(val)) : val;
 }
 
@@ -360,8 +396,8 @@ int or_model_step(or_model* m, int32_t token, int32_t pos, double* logits)
         for (int64_t gg = 0; gg < nkv; gg++)
             or_rope_neox(m->k + gg * hd, (int32_t)hd, c->rot_dim, c->inv_freq, pos);
         for (int64_t i = 0; i < kvd; i++) {
-            kc[(int64_t)pos * kvd + i] = kv_store(m, m->k[i]);
-            vc[(int64_t)pos * kvd + i] = kv_store(m, m->v[i]);
+            kc[(int64_t)pos * kvd + i] = kv_store(m, m->k[i], 0);
+            vc[(int64_t)pos * kvd + i] = kv_store(m, m->v[i], 1);
         }
         /* attention over positions 0..pos (the new token's K/V included) */
         for (int64_t hh = 0; hh < nq; hh++) {

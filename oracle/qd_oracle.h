@@ -27,6 +27,11 @@ extern "C" {
 double or_f16_to_f64(uint16_t h);
 /* f64 -> binary16 bit pattern, round to nearest, ties to even; overflow -> inf */
 uint16_t or_f64_to_f16(double v);
+/* OCP fp8 e4m3 (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0
+ * subnormal; 0x7f / 0xff NaN; no infinity; largest 448): exact decode, and
+ * round to nearest even with saturation at +-448 (NaN input -> 0x7f). */
+double or_e4m3_to_f64(uint8_t c);
+uint8_t or_f64_to_e4m3(double v);
 
 /* q4_0 matrix [rows, cols], row-major: d[rows][cols/32] f16 bits,
  * qs[rows][cols/32][16]: byte j = code of element j (low nibble) and of
@@ -71,9 +76,11 @@ typedef struct {
     int32_t rot_dim;       /* even, <= head_dim */
     int32_t qk_norm;       /* per-head RMSNorm of q and k before the rotary */
     int32_t max_seq;
-    int32_t kv_round;      /* 1: K/V stored as binary16 (the method); 0: kept f64 */
+    int32_t kv_round;      /* 1: K/V stored as binary16 (the method); 0: kept f64;
+                              2: stored as fp8 e4m3 of value / k_scale (K) or / v_scale (V) */
     double eps;
     const float* inv_freq; /* [rot_dim/2] */
+    double k_scale, v_scale; /* kv_round 2 only */
 } or_config;
 
 typedef struct or_model or_model;

@@ -121,6 +121,9 @@ def _cfg_weights(qd, mi, **over):
     (dict(hidden=0), -1), (dict(n_heads=12, n_kv=1), -4), (dict(kv_paged=1, kv_block_size=32), -4),
     (dict(kv_paged=1, num_kv_blocks=2), -1), (dict(inv_freq=None), -1), (dict(vocab=1000), -1),
     (dict(intermediate=512), -1), (dict(eps=-1.0), -1),
+    (dict(kv_fp8=2), -1), (dict(kv_fp8=1, k_scale=0.0, v_scale=1.0), -1),
+    (dict(kv_fp8=1, k_scale=1.0, v_scale=float("nan")), -1),
+    (dict(kv_fp8=1, k_scale=1.0, v_scale=1.0, layer_kernel=1), -4),
 ])
 def test_create_validation(qd, over, code):
     mi = synth.make_model("tiny")

@@ -223,3 +223,32 @@ def test_tiny_llama3_rope_scaling_vs_oracle(tiny):
     got = _gen(m, tiny.prompt, s.gen)[s.prompt_len - 1:]
     m.close()
     check_greedy(got, toks, margins, "tiny llama3")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_tiny_kv_fp8_vs_oracle(tiny, paged):
+    """The tiny model with an fp8 e4m3 K/V cache (k_scale 0.5, v_scale 0.125)
+    against the oracle storing its own K/V the same way (value / scale
+    rounded to e4m3, nearest even, saturating): teacher-forced logits,
+    free-running greedy tokens, and graph == eager bitwise."""
+    import token_decode_q4_amd as qd
+    s = tiny.shape
+    ks, vs = 0.5, 0.125
+    say(f"tiny fp8 KV paged={paged}")
+    om = oracle.Model(tiny, kv_fp8=True, k_scale=ks, v_scale=vs)
+    toks, margins, _ = oracle.generate(om, tiny.prompt, s.gen)
+    seq = list(tiny.prompt) + list(toks[:-1])
+    om2 = oracle.Model(tiny, kv_fp8=True, k_scale=ks, v_scale=vs)
+    ref = np.stack([om2.step(int(t), p) for p, t in enumerate(seq)])
+    m = qd.Model(tiny, use_graph=True, paged=paged, kv_fp8=True, k_scale=ks, v_scale=vs)
+    lg, _ = _teacher_forced_logits(m, seq, s.vocab)
+    err = float(np.max(np.abs(lg - ref)))
+    say(f"tiny fp8 KV logits max abs err {err:.3e}")
+    assert err <= LOGITS_BAR
+    got = _gen(m, tiny.prompt, s.gen)[s.prompt_len - 1:]
+    m.close()
+    check_greedy(got, toks, margins, "tiny fp8 KV")
+    me = qd.Model(tiny, use_graph=False, paged=paged, kv_fp8=True, k_scale=ks, v_scale=vs)
+    lg_e, _ = _teacher_forced_logits(me, seq, s.vocab)
+    me.close()
+    assert np.array_equal(lg, lg_e)

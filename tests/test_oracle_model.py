@@ -145,3 +145,30 @@ def test_generate_counts(oracle_lib, tiny):
     assert len(toks) == 5 and len(margins) == 5 and set(kept) == {0, 4}
     assert steps == list(range(P + 5 - 1))
     assert toks[0] == int(np.argmax(kept[0].astype(np.float32)))
+
+
+def test_fp8_cache_stores_e4m3_values(oracle_lib):
+    """With kv_fp8 the oracle model stores e4m3(value / scale) * scale: every
+    stored K value divided by k_scale (V by v_scale) is an e4m3 value, and it is
+    the nearest one to the value the f64 step computed (the f64-kept cache)."""
+    import synth
+    mi = synth.make_model("tiny")
+    ks, vs = 0.5, 0.125
+    m8 = oracle_lib.Model(mi, kv_fp8=True, k_scale=ks, v_scale=vs)
+    m64 = oracle_lib.Model(mi, kv_round=False)
+    grid = oracle_lib.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    grid = np.unique(grid[~np.isnan(grid)])
+    for p, t in enumerate(mi.prompt[:6]):
+        m8.step(int(t), p)
+        m64.step(int(t), p)
+    for layer in range(mi.shape.layers):
+        for p in range(6):
+            for g in range(mi.shape.n_kv):
+                for which, sc in ((0, ks), (1, vs)):
+                    got = m8.kv(layer, p, g, which) / sc
+                    assert np.all(np.isin(got, grid))
+                    # only layer 0 at position 0 is comparable: everything later reads
+                    # the rounded cache through the attention
+                    if p == 0 and layer == 0:
+                        want = oracle_lib.e4m3_to_f64(oracle_lib.f64_to_e4m3(m64.kv(layer, p, g, which) / sc))
+                        assert np.array_equal(got, want)

@@ -407,3 +407,25 @@ def test_attn_decode_e4m3_scales(oracle_lib):
         p_ = np.exp(s_ - s_.max())
         p_ /= p_.sum()
         np.testing.assert_allclose(got[0, h], p_ @ V[0, g], rtol=1e-12, atol=1e-14)
+
+
+def test_e4m3_c_codec_vs_torch(oracle_lib):
+    """The C oracle's e4m3 decode (all codes) and encode (round to nearest even,
+    ties to even codes, in-range values) against torch float8_e4m3fn; saturation
+    by closed form."""
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle_lib.e4m3_to_f64_c(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(3000) * s for s in (1e-3, 0.05, 1.0, 40.0)])
+    # every exact midpoint between neighbouring finite codes (ties)
+    vals = np.sort(ours[~nan & (codes < 0x7F)])
+    mids = (vals[1:] + vals[:-1]) / 2
+    x = np.concatenate([x, mids, -mids, vals, -vals])
+    enc = oracle_lib.f64_to_e4m3(x)
+    ref_enc = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(enc, ref_enc)
+    assert list(oracle_lib.f64_to_e4m3(np.array([449.0, 1e6, -1e6]))) == [0x7E, 0x7E, 0xFE]

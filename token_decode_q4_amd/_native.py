@@ -52,7 +52,8 @@ class Config(C.Structure):
                 ("inv_freq", C.c_void_p), ("tied", C.c_int32), ("qk_norm", C.c_int32),
                 ("max_seq", C.c_int32), ("kv_paged", C.c_int32), ("kv_block_size", C.c_int32),
                 ("num_kv_blocks", C.c_int32), ("block_table", C.c_void_p),
-                ("use_graph", C.c_int32), ("layer_kernel", C.c_int32)]
+                ("use_graph", C.c_int32), ("layer_kernel", C.c_int32),
+                ("kv_fp8", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float)]
 
 
 class AttnArgs(C.Structure):
@@ -211,7 +212,8 @@ class Model:
 
     def __init__(self, mi, use_graph: bool = True, stream=None, paged: bool | None = None,
                  max_seq: int | None = None, num_kv_blocks: int | None = None,
-                 layer_kernel: bool = False):
+                 layer_kernel: bool = False, kv_fp8: bool = False, k_scale: float = 1.0,
+                 v_scale: float = 1.0):
         s = mi.shape
         self.shape = s
         self.vocab = s.vocab
@@ -242,7 +244,7 @@ class Model:
                      float(s.eps), s.rot_dim, inv.ctypes.data, int(s.tied), int(s.qk_norm),
                      self.max_seq, int(bool(paged)), 16, nblocks,
                      None if table is None else table.ctypes.data, int(bool(use_graph)),
-                     int(bool(layer_kernel)))
+                     int(bool(layer_kernel)), int(bool(kv_fp8)), float(k_scale), float(v_scale))
         h = C.c_void_p()
         check(lib().qd_create(C.byref(cfg), C.byref(w), _stream(stream), C.byref(h)))
         self._h = h

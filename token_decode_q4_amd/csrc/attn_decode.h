@@ -89,6 +89,27 @@ struct alignas(16) AttnSmem {
 };
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+// f32 -> OCP fp8 e4m3 code (sign, 4 exponent bits with bias 7, 3 mantissa
+// bits), rounded to nearest even and saturated at +-448: the decode step's
+// store into an fp8 cache.  Written out rather than left to a conversion
+// instruction, so that its rounding and saturation are the stated ones.
+QD_DEV uint32_t f32_to_e4m3(float x)
+{
+    const uint32_t sgn = (__float_as_uint(x) >> 24) & 0x80u;
+    const float a = fminf(fabsf(x), 448.f);
+    if (a < 0.015625f)                                   // subnormal: multiples of 2^-9
+        return sgn | (uint32_t)rintf(a * 512.f);         // 0 .. 8 (8 is the smallest normal)
+    int e;
+    const float f = frexpf(a, &e);                       // a = (2f) 2^(e-1), 2f in [1, 2)
+    int E = e - 1;
+    int mant = (int)rintf((2.f * f - 1.f) * 8.f);        // exact argument, ties to even
+    if (mant == 8) {                                     // rounded up to the next power of two
+        mant = 0;
+        E += 1;
+    }
+    return sgn | (uint32_t)(((E + 7) << 3) | mant);
+}
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // float load: agent-scope (COH, a value another workgroup of the same launch
@@ -223,7 +244,7 @@ template <int HD, int GQ, bool PAGED, int QMODE, bool FUSED, bool KV8, class Wai
 QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<HD, GQ>& sm, Wait&& wait)
 {
     static_assert(HD == 64 || HD == 128, "head_dim");
-    static_assert(!KV8 || (QMODE == 0 && !FUSED), "fp8 K/V: standalone attention only");
+    static_assert(!KV8 || !FUSED, "fp8 K/V: not in the persistent layer kernel");
     static_assert(GQ == 1 || GQ == 2 || GQ == 4 || GQ == 8, "group");
     using Step = AttnStep<HD>;
     constexpr int NI = Step::NI, DPL = Step::DPL;
@@ -427,15 +448,34 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
             o = kv_row<HD, PAGED>(p, p.tables[(size_t)b * p.mbps + tcur / ATT_BS], g, tcur);
         else
             o = kv_row<HD, PAGED>(p, b, g, tcur);
+        if (KV8) {
+            // e4m3 of value / scale; the wave's own row keeps the bytes in the
+            // order of the fp8 QK operand (plain dim order: a lane loads
+            // contiguous dims)
+            uint8_t* kc8 = reinterpret_cast<uint8_t*>(p.kc);
+            uint8_t* vc8 = reinterpret_cast<uint8_t*>(p.vc);
+            uint8_t* kn8 = reinterpret_cast<uint8_t*>(&sm.knew[w][0]);
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) {
-            const int d = lane * DPL + e;
-            const uint16_t kh = f32_to_f16(kv_[e]);
-            const uint16_t vh = f32_to_f16(vv[e]);
-            p.kc[o + d] = kh;
-            p.vc[o + d] = vh;
-            sm.knew[w][d] = kh;
-            vnew[e] = f16_to_f32(vh);
+            for (int e = 0; e < DPL; ++e) {
+                const int d = lane * DPL + e;
+                const uint32_t k8 = f32_to_e4m3(kv_[e] / p.k_scale);
+                const uint32_t v8 = f32_to_e4m3(vv[e] / p.v_scale);
+                kc8[o + d] = (uint8_t)k8;
+                vc8[o + d] = (uint8_t)v8;
+                kn8[d] = (uint8_t)k8;
+                vnew[e] = __builtin_amdgcn_cvt_pk_f32_fp8((int)v8, false)[0];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) {
+                const int d = lane * DPL + e;
+                const uint16_t kh = f32_to_f16(kv_[e]);
+                const uint16_t vh = f32_to_f16(vv[e]);
+                p.kc[o + d] = kh;
+                p.vc[o + d] = vh;
+                sm.knew[w][d] = kh;
+                vnew[e] = f16_to_f32(vh);
+            }
         }
     }
     wave_lds_sync();
@@ -490,9 +530,16 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
         for (int i = 0; i < NI; ++i)
             kr[i] = cur_st.k[i];
         if (own_here && kk == slot) {
+            if (KV8) {
+                const uint8_t* kn8 = reinterpret_cast<const uint8_t*>(&sm.knew[w][0]);
 #pragma unroll
-            for (int i = 0; i < NI; ++i)
-                kr[i] = *reinterpret_cast<const uint4*>(&sm.knew[w][32 * i + 8 * kg]);
+                for (int u = 0; u < NI / 2; ++u)
+                    kr[u] = *reinterpret_cast<const uint4*>(kn8 + 8 * NI * kg + 16 * u);
+            } else {
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+                    kr[i] = *reinterpret_cast<const uint4*>(&sm.knew[w][32 * i + 8 * kg]);
+            }
         }
         QD_MARK(4);
         floatx4 sc = {0.f, 0.f, 0.f, 0.f};

@@ -97,6 +97,8 @@ struct DevLayer {
 struct qd_model {
     int H, L, nq, nkv, hd, I, V, rot, qkv_rows, max_seq, qk_norm, paged, nblocks;
     float eps;
+    int kv_fp8 = 0;                 // fp8 e4m3 K/V cache (1 byte per element)
+    float k_scale = 1.f, v_scale = 1.f;
     std::vector<DevLayer> layers;
     DevQ4 embed, lm;
     float* final_norm = nullptr;
@@ -315,6 +317,15 @@ static int validate_config(const qd_config* c, const qd_weights* w)
         snprintf(nm, sizeof nm, "layer %d wdown", l);
         QD_TRY(check_q4(L.wdown, H, c->intermediate, nm));
     }
+    if (c->kv_fp8 != 0 && c->kv_fp8 != 1)
+        return fail(QD_EINVAL, "kv_fp8 %d (0 or 1)", c->kv_fp8);
+    if (c->kv_fp8) {
+        if (!(c->k_scale > 0.f) || !(c->v_scale > 0.f) || !std::isfinite(c->k_scale) ||
+            !std::isfinite(c->v_scale))
+            return fail(QD_EINVAL, "kv_fp8: k_scale and v_scale must be finite and positive");
+        if (c->layer_kernel)
+            return fail(QD_EUNSUPPORTED, "kv_fp8 with layer_kernel = 1");
+    }
     if (c->layer_kernel) {
         const int nqd = c->n_heads * c->head_dim;
         if (c->head_dim != 128 || c->n_heads != 4 * c->n_kv || c->hidden % 2048 || nqd % 2048 ||
@@ -452,7 +463,12 @@ static int enqueue_step(qd_model* m, hipStream_t s)
             p.counters = m->attn_cnt;
             p.kc = Ly.kc;
             p.vc = Ly.vc;
-            launch_attention<1>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, 1, m->nq, s);
+            p.k_scale = m->k_scale;
+            p.v_scale = m->v_scale;
+            if (m->kv_fp8)
+                launch_attention<1, true>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, 1, m->nq, s);
+            else
+                launch_attention<1>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, 1, m->nq, s);
         }
         // o-proj + residual, u = x * ffn_norm
         QD_GEMV(k_gemv_residual, (QD_CFG_O), m->lpr_o, m->grid_o, gemv_lds_bytes(Ly.o.nb), s,
@@ -609,6 +625,9 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
     m->max_seq = c.max_seq;
     m->qk_norm = c.qk_norm ? 1 : 0;
     m->paged = c.kv_paged ? 1 : 0;
+    m->kv_fp8 = c.kv_fp8;
+    m->k_scale = c.kv_fp8 ? c.k_scale : 1.f;
+    m->v_scale = c.kv_fp8 ? c.v_scale : 1.f;
     m->nblocks = c.kv_paged ? c.num_kv_blocks : 0;
     m->qkv_rows = (m->nq + 2 * m->nkv) * m->hd;
     m->use_graph = c.use_graph ? 1 : 0;
@@ -675,9 +694,11 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
         DevLayer& D = m->layers[l];
         const size_t n = m->paged ? (size_t)m->nblocks * m->nkv * ATT_BS * hd
                                   : (size_t)m->nkv * m->max_seq * hd;
-        if ((rc = dev_alloc_t(m, &D.kc, n))) return bail(rc);
-        if ((rc = dev_alloc_t(m, &D.vc, n))) return bail(rc);
-        if (hipMemsetAsync(D.kc, 0, n * 2, s) != hipSuccess || hipMemsetAsync(D.vc, 0, n * 2, s) != hipSuccess)
+        // n elements of 2 bytes (f16) or 1 byte (fp8; hd is even, so n / 2 halves)
+        const size_t nh = m->kv_fp8 ? n / 2 : n;
+        if ((rc = dev_alloc_t(m, &D.kc, nh))) return bail(rc);
+        if ((rc = dev_alloc_t(m, &D.vc, nh))) return bail(rc);
+        if (hipMemsetAsync(D.kc, 0, nh * 2, s) != hipSuccess || hipMemsetAsync(D.vc, 0, nh * 2, s) != hipSuccess)
             return bail(fail(QD_EHIP, "KV cache clear failed"));
     }
     if (m->paged) {
