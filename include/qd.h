@@ -59,6 +59,7 @@ typedef struct {
 typedef struct {
     const float *attn_norm, *ffn_norm, *q_norm, *k_norm;
     qd_q4_0 wq, wk, wv, wo, wgate, wup, wdown;
+    qd_q4_0 attn_gate;   /* [n_heads*head_dim, hidden], read only with attn_out_gate */
 } qd_layer_weights;
 
 /* embed [vocab, hidden] q4_0: a token's embedding is its dequantised row.
@@ -104,6 +105,12 @@ typedef struct {
  *            and v_scale finite and positive; not with layer_kernel = 1
  *            (QD_EUNSUPPORTED).  Fields past layer_kernel: a caller that
  *            zero-fills the struct gets the f16 cache.
+ *   attn_out_gate: 1 = attention output gate (inferencelayer cuda_llm.rs
+ *            page, Cfg::attn_out_gate): each layer's attn_gate rows project
+ *            the same normed input as q|k|v (fused after them), and the
+ *            attention result is multiplied elementwise by their sigmoid
+ *            before the o-projection.  Not with layer_kernel = 1
+ *            (QD_EUNSUPPORTED).
  * Supported: head_dim 64 or 128; n_heads / n_kv in {1, 2, 4, 8};
  * kv_block_size 16; hidden, intermediate and n_heads*head_dim multiples of 32. */
 typedef struct {
@@ -120,6 +127,7 @@ typedef struct {
     int32_t layer_kernel;
     int32_t kv_fp8;
     float k_scale, v_scale;
+    int32_t attn_out_gate;
 } qd_config;
 
 typedef struct qd_model qd_model;

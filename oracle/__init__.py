@@ -24,7 +24,8 @@ class _Q4(C.Structure):
 class _Layer(C.Structure):
     _fields_ = [("attn_norm", C.c_void_p), ("ffn_norm", C.c_void_p), ("q_norm", C.c_void_p),
                 ("k_norm", C.c_void_p)] + [(n, _Q4) for n in
-                                           ("wq", "wk", "wv", "wo", "wgate", "wup", "wdown")]
+                                           ("wq", "wk", "wv", "wo", "wgate", "wup", "wdown",
+                                            "wag")]
 
 
 class _Cfg(C.Structure):
@@ -32,7 +33,7 @@ class _Cfg(C.Structure):
                                          "intermediate", "vocab", "rot_dim", "qk_norm",
                                          "max_seq", "kv_round")] + \
                [("eps", C.c_double), ("inv_freq", C.c_void_p), ("k_scale", C.c_double),
-                ("v_scale", C.c_double)]
+                ("v_scale", C.c_double), ("attn_out_gate", C.c_int32)]
 
 
 def lib():
@@ -272,6 +273,8 @@ class Model:
             ns = [np.ascontiguousarray(a, dtype=np.float32) for a in
                   (Lw.attn_norm, Lw.ffn_norm, Lw.q_norm, Lw.k_norm)]
             qs = [_q4(m) for m in (Lw.wq, Lw.wk, Lw.wv, Lw.wo, Lw.wgate, Lw.wup, Lw.wdown)]
+            ag = getattr(Lw, "attn_gate", None)
+            qs.append(_q4(ag) if ag is not None else _Q4(None, None, 0, 0))
             self._keep.append((ns, qs))
             layers[i] = _Layer(_p(ns[0]), _p(ns[1]), _p(ns[2]), _p(ns[3]), *qs)
         self._layers = layers
@@ -280,7 +283,8 @@ class Model:
         self._cfg = _Cfg(s.hidden, s.layers, s.n_heads, s.n_kv, s.head_dim, s.intermediate,
                          s.vocab, s.rot_dim, int(s.qk_norm), s.max_seq,
                          2 if kv_fp8 else int(kv_round), float(s.eps), _p(self._inv),
-                         float(k_scale), float(v_scale))
+                         float(k_scale), float(v_scale),
+                         int(getattr(mi.layers[0], "attn_gate", None) is not None))
         self.nthreads = nthreads or default_threads()
         h = lib().or_model_create(C.byref(self._cfg), C.byref(self._embed), self._layers,
                                   _p(self._final), C.byref(self._lm), self.nthreads)

@@ -259,6 +259,8 @@ or_model* or_model_create(const or_config* cfg, const or_q4* embed, const or_lay
             L->wup.cols != c->hidden || L->wdown.rows != c->hidden ||
             L->wdown.cols != c->intermediate)
             return NULL;
+        if (c->attn_out_gate && (L->wag.rows != qd0 || L->wag.cols != c->hidden || !L->wag.d))
+            return NULL;
     }
     or_model* m = (or_model*)calloc(1, sizeof(or_model));
     m->cfg = *c;
@@ -427,6 +429,14 @@ int or_model_step(or_model* m, int32_t token, int32_t pos, double* logits)
                 for (int64_t d = 0; d < hd; d++)
                     oh[d] += p * vr[d];
             }
+        }
+        /* attention output gate (inferencelayer cuda_llm.rs page, Cfg::attn_out_gate:
+         * a second projection of the same normed input, sigmoid, elementwise on the
+         * attention result before the o-projection) */
+        if (c->attn_out_gate) {
+            or_gemv_q4_0(&L->wag, m->h, m->o, nt);
+            for (int64_t i = 0; i < nq * hd; i++)
+                m->att[i] *= 1.0 / (1.0 + exp(-m->o[i]));
         }
         or_gemv_q4_0(&L->wo, m->att, m->o, nt);
         for (int64_t i = 0; i < H; i++)

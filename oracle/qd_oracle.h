@@ -69,6 +69,7 @@ int or_attn_decode(const float* q, const uint16_t* k, const uint16_t* v,
 typedef struct {
     const float *attn_norm, *ffn_norm, *q_norm, *k_norm; /* [H], [H], [hd], [hd] */
     or_q4 wq, wk, wv, wo, wgate, wup, wdown;
+    or_q4 wag;             /* attention output gate [n_heads*hd, H] (attn_out_gate only) */
 } or_layer;
 
 typedef struct {
@@ -81,6 +82,7 @@ typedef struct {
     double eps;
     const float* inv_freq; /* [rot_dim/2] */
     double k_scale, v_scale; /* kv_round 2 only */
+    int32_t attn_out_gate;   /* 1: attention output *= sigmoid(wag h) before o-proj */
 } or_config;
 
 typedef struct or_model or_model;

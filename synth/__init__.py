@@ -222,6 +222,7 @@ class LayerWeights:
     ffn_norm: np.ndarray
     q_norm: np.ndarray
     k_norm: np.ndarray
+    attn_gate: Q4Matrix | None = None   # attention output gate rows [n_heads*hd, H], if any
 
 
 @dataclass
@@ -246,7 +247,10 @@ def _lt(layer: int, k: int) -> int:
     return 16 + 16 * layer + k
 
 
-def make_model(name_or_shape, workers: int | None = None) -> ModelInputs:
+def make_model(name_or_shape, workers: int | None = None, attn_out_gate: bool = False) -> ModelInputs:
+    """Seeded inputs of a model.  attn_out_gate adds an attention output gate
+    matrix per layer, drawn from tensor ids of its own: every other tensor is
+    the same as without it."""
     s = MODELS[name_or_shape] if isinstance(name_or_shape, str) else name_or_shape
     H, hd, I = s.hidden, s.head_dim, s.intermediate
     nq, nkv = s.n_heads * hd, s.n_kv * hd
@@ -267,7 +271,8 @@ def make_model(name_or_shape, workers: int | None = None) -> ModelInputs:
                                    attn_norm=random_norm(s.seed, _lt(li, 7), H),
                                    ffn_norm=random_norm(s.seed, _lt(li, 8), H),
                                    q_norm=random_norm(s.seed, _lt(li, 9), hd),
-                                   k_norm=random_norm(s.seed, _lt(li, 10), hd)))
+                                   k_norm=random_norm(s.seed, _lt(li, 10), hd),
+                                   attn_gate=mat(_lt(li, 11), nq, H) if attn_out_gate else None))
     lm = embed if s.tied else mat(_T_LM, s.vocab, H)
     # largest chunks first keeps the pool busy to the end
     items.sort(key=lambda it: -it[1])
@@ -301,6 +306,8 @@ def model_digest(mi: ModelInputs) -> str:
             add(m.d); add(m.qs)
         for v in (L.attn_norm, L.ffn_norm, L.q_norm, L.k_norm):
             add(v)
+        if L.attn_gate is not None:   # only when present: digests of ungated models unchanged
+            add(L.attn_gate.d); add(L.attn_gate.qs)
     add(mi.final_norm)
     if not mi.shape.tied:
         add(mi.lm_head.d); add(mi.lm_head.qs)

@@ -124,6 +124,7 @@ def _cfg_weights(qd, mi, **over):
     (dict(kv_fp8=2), -1), (dict(kv_fp8=1, k_scale=0.0, v_scale=1.0), -1),
     (dict(kv_fp8=1, k_scale=1.0, v_scale=float("nan")), -1),
     (dict(kv_fp8=1, k_scale=1.0, v_scale=1.0, layer_kernel=1), -4),
+    (dict(attn_out_gate=2), -1), (dict(attn_out_gate=1), -1),   # the tiny weights carry no gate
 ])
 def test_create_validation(qd, over, code):
     mi = synth.make_model("tiny")

@@ -252,3 +252,31 @@ def test_tiny_kv_fp8_vs_oracle(tiny, paged):
     lg_e, _ = _teacher_forced_logits(me, seq, s.vocab)
     me.close()
     assert np.array_equal(lg, lg_e)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_tiny_attn_out_gate_vs_oracle(paged):
+    """The tiny model with an attention output gate (gate rows fused after
+    q|k|v, sigmoid applied to the merged attention output): teacher-forced
+    logits, free-running greedy tokens, graph == eager bitwise."""
+    import token_decode_q4_amd as qd
+    mi = synth.make_model("tiny", attn_out_gate=True)
+    s = mi.shape
+    say(f"tiny attention output gate paged={paged}")
+    om = oracle.Model(mi)
+    toks, margins, _ = oracle.generate(om, mi.prompt, s.gen)
+    seq = list(mi.prompt) + list(toks[:-1])
+    om2 = oracle.Model(mi)
+    ref = np.stack([om2.step(int(t), p) for p, t in enumerate(seq)])
+    m = qd.Model(mi, use_graph=True, paged=paged)
+    lg, _ = _teacher_forced_logits(m, seq, s.vocab)
+    err = float(np.max(np.abs(lg - ref)))
+    say(f"tiny gated logits max abs err {err:.3e}")
+    assert err <= 1e-4
+    got = _gen(m, mi.prompt, s.gen)[s.prompt_len - 1:]
+    m.close()
+    check_greedy(got, toks, margins, "tiny gated")
+    me = qd.Model(mi, use_graph=False, paged=paged)
+    lg_e, _ = _teacher_forced_logits(me, seq, s.vocab)
+    me.close()
+    assert np.array_equal(lg, lg_e)

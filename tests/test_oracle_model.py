@@ -172,3 +172,71 @@ def test_fp8_cache_stores_e4m3_values(oracle_lib):
                     if p == 0 and layer == 0:
                         want = oracle_lib.e4m3_to_f64(oracle_lib.f64_to_e4m3(m64.kv(layer, p, g, which) / sc))
                         assert np.array_equal(got, want)
+
+
+
+# ----------------------------------------------------------------- attention output gate
+# inferencelayer cuda_llm.rs page, Cfg::attn_out_gate and the loader's q|k|v|gate
+# rows: a second projection of the normed input, sigmoid, applied to the
+# attention result before the o-projection.
+
+def _one_layer_gated(oracle_lib):
+    import dataclasses
+    import synth
+    shape = dataclasses.replace(synth.MODELS["tiny"], layers=1, name="tiny-1l")
+    return synth.make_model(shape, attn_out_gate=True)
+
+
+def test_attn_gate_first_step_closed_form(oracle_lib):
+    """Position 0 of a one-layer gated model in plain numpy f64: the attention
+    over one key is V[0] (rounded to f16 as stored), so the step is embedding,
+    RMSNorm, the projections, the gate sigmoid(Wag h) on V, o-projection,
+    residual, SwiGLU MLP, final norm and LM head."""
+    mi = _one_layer_gated(oracle_lib)
+    s, L = mi.shape, mi.layers[0]
+    D = oracle_lib.dequant
+    tok = int(mi.prompt[0])
+    x = D(mi.embed)[tok]
+
+    def rms(v, w):
+        return v / np.sqrt(np.mean(v * v) + s.eps) * w.astype(np.float64)
+
+    h = rms(x, L.attn_norm)
+    v = D(L.wv) @ h
+    v16 = oracle_lib.f16_to_f64(oracle_lib.f64_to_f16(v))
+    gate = D(L.attn_gate) @ h
+    hd, grp = s.head_dim, s.n_heads // s.n_kv
+    att = np.concatenate([v16[(hh // grp) * hd:(hh // grp + 1) * hd] for hh in range(s.n_heads)])
+    att = att / (1.0 + np.exp(-gate))
+    x = x + D(L.wo) @ att
+    h2 = rms(x, L.ffn_norm)
+    g, u = D(L.wgate) @ h2, D(L.wup) @ h2
+    x = x + D(L.wdown) @ (g / (1.0 + np.exp(-g)) * u)
+    ref = D(mi.lm_head) @ rms(x, mi.final_norm)
+    import dataclasses
+    got = oracle_lib.Model(mi).step(tok, 0)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+    # and the gate matters: the ungated model differs
+    ungated = oracle_lib.Model(dataclasses.replace(
+        mi, layers=[dataclasses.replace(L, attn_gate=None)])).step(tok, 0)
+    assert np.max(np.abs(ungated - got)) > 1e-3
+
+
+def test_attn_gate_zero_is_half(oracle_lib):
+    """A gate of zero weights gives sigmoid(0) = 1/2 everywhere, which equals the
+    ungated model with every o-projection scale halved (exact in f64)."""
+    import dataclasses
+    import synth
+    mi = synth.make_model("tiny", attn_out_gate=True)
+    layers_g, layers_h = [], []
+    for L in mi.layers:
+        zero = synth.Q4Matrix(np.zeros_like(L.attn_gate.d), L.attn_gate.qs)
+        layers_g.append(dataclasses.replace(L, attn_gate=zero))
+        dh = (L.wo.d.view(np.float16) / np.float16(2)).view(np.uint16)   # exact: normal scales
+        assert np.array_equal(dh.view(np.float16).astype(np.float64) * 2,
+                              L.wo.d.view(np.float16).astype(np.float64))
+        layers_h.append(dataclasses.replace(L, attn_gate=None, wo=synth.Q4Matrix(dh, L.wo.qs)))
+    mg = oracle_lib.Model(dataclasses.replace(mi, layers=layers_g))
+    mh = oracle_lib.Model(dataclasses.replace(mi, layers=layers_h))
+    for p, t in enumerate(mi.prompt[:8]):
+        assert np.array_equal(mg.step(int(t), p), mh.step(int(t), p))

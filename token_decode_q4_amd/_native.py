@@ -37,7 +37,8 @@ class Q4(C.Structure):
 class LayerWeights(C.Structure):
     _fields_ = [("attn_norm", C.c_void_p), ("ffn_norm", C.c_void_p), ("q_norm", C.c_void_p),
                 ("k_norm", C.c_void_p)] + [(n, Q4) for n in
-                                           ("wq", "wk", "wv", "wo", "wgate", "wup", "wdown")]
+                                           ("wq", "wk", "wv", "wo", "wgate", "wup", "wdown",
+                                            "attn_gate")]
 
 
 class Weights(C.Structure):
@@ -53,7 +54,8 @@ class Config(C.Structure):
                 ("max_seq", C.c_int32), ("kv_paged", C.c_int32), ("kv_block_size", C.c_int32),
                 ("num_kv_blocks", C.c_int32), ("block_table", C.c_void_p),
                 ("use_graph", C.c_int32), ("layer_kernel", C.c_int32),
-                ("kv_fp8", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float)]
+                ("kv_fp8", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float),
+                ("attn_out_gate", C.c_int32)]
 
 
 class AttnArgs(C.Structure):
@@ -221,13 +223,15 @@ class Model:
         paged = s.kv_paged if paged is None else paged
         keep = []
         layers = (LayerWeights * s.layers)()
+        gated = getattr(mi.layers[0], "attn_gate", None) is not None
         for i, L in enumerate(mi.layers):
             ns = [np.ascontiguousarray(a, dtype=np.float32) for a in
                   (L.attn_norm, L.ffn_norm, L.q_norm, L.k_norm)]
             keep.append(ns)
+            ag = _q4(L.attn_gate) if gated else Q4(None, None, 0, 0)
             layers[i] = LayerWeights(*[a.ctypes.data for a in ns],
                                      *[_q4(m) for m in (L.wq, L.wk, L.wv, L.wo, L.wgate, L.wup,
-                                                        L.wdown)])
+                                                        L.wdown)], ag)
         fn = np.ascontiguousarray(mi.final_norm, dtype=np.float32)
         inv = np.ascontiguousarray(mi.inv_freq, dtype=np.float32)
         nblk_need = (self.max_seq + 15) // 16
@@ -244,7 +248,8 @@ class Model:
                      float(s.eps), s.rot_dim, inv.ctypes.data, int(s.tied), int(s.qk_norm),
                      self.max_seq, int(bool(paged)), 16, nblocks,
                      None if table is None else table.ctypes.data, int(bool(use_graph)),
-                     int(bool(layer_kernel)), int(bool(kv_fp8)), float(k_scale), float(v_scale))
+                     int(bool(layer_kernel)), int(bool(kv_fp8)), float(k_scale), float(v_scale),
+                     int(gated))
         h = C.c_void_p()
         check(lib().qd_create(C.byref(cfg), C.byref(w), _stream(stream), C.byref(h)))
         self._h = h

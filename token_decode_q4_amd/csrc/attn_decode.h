@@ -62,8 +62,11 @@ struct AttnParams {
     const float* rope_cur;     // cos [rot/2] then sin [rot/2] at the step's position
     uint16_t* kc;              // cache written at pos (same buffers as k/v)
     uint16_t* vc;
-    // K/V in fp8 e4m3 (standalone only): element = e4m3 value * scale
+    // K/V in fp8 e4m3: element = e4m3 value * scale
     float k_scale, v_scale;
+    // attention output gate (decode step): the merged output of head h, dim d
+    // is multiplied by sigmoid(gate[h * HD + d]); nullptr = none
+    const float* gate;
 };
 
 constexpr int ATT_WK = 16;                 // keys per wave step (one paged block)
@@ -198,7 +201,10 @@ QD_DEV void attn_merge_heads(const AttnParams& p, int b, int g, int nact)
                     num = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), u)), a[u], num);
             mt = rm;
         }
-        st_f32<COH>(p.out + ((size_t)b * p.nq + h) * HD + d, (den > 0.f) ? num / den : 0.f);
+        float o = (den > 0.f) ? num / den : 0.f;
+        if (p.gate)   // uniform
+            o *= 1.0f / (1.0f + expf(-ld_f32<COH>(p.gate + (size_t)h * HD + d)));
+        st_f32<COH>(p.out + ((size_t)b * p.nq + h) * HD + d, o);
     }
 }
 

@@ -98,6 +98,7 @@ struct qd_model {
     int H, L, nq, nkv, hd, I, V, rot, qkv_rows, max_seq, qk_norm, paged, nblocks;
     float eps;
     int kv_fp8 = 0;                 // fp8 e4m3 K/V cache (1 byte per element)
+    int attn_gate = 0;              // attention output gate rows after q | k | v
     float k_scale = 1.f, v_scale = 1.f;
     std::vector<DevLayer> layers;
     DevQ4 embed, lm;
@@ -310,6 +311,10 @@ static int validate_config(const qd_config* c, const qd_weights* w)
         QD_TRY(check_q4(L.wv, nkd, H, nm));
         snprintf(nm, sizeof nm, "layer %d wo", l);
         QD_TRY(check_q4(L.wo, H, nqd, nm));
+        if (c->attn_out_gate) {
+            snprintf(nm, sizeof nm, "layer %d attn_gate", l);
+            QD_TRY(check_q4(L.attn_gate, nqd, H, nm));
+        }
         snprintf(nm, sizeof nm, "layer %d wgate", l);
         QD_TRY(check_q4(L.wgate, c->intermediate, H, nm));
         snprintf(nm, sizeof nm, "layer %d wup", l);
@@ -319,6 +324,10 @@ static int validate_config(const qd_config* c, const qd_weights* w)
     }
     if (c->kv_fp8 != 0 && c->kv_fp8 != 1)
         return fail(QD_EINVAL, "kv_fp8 %d (0 or 1)", c->kv_fp8);
+    if (c->attn_out_gate != 0 && c->attn_out_gate != 1)
+        return fail(QD_EINVAL, "attn_out_gate %d (0 or 1)", c->attn_out_gate);
+    if (c->attn_out_gate && c->layer_kernel)
+        return fail(QD_EUNSUPPORTED, "attn_out_gate with layer_kernel = 1");
     if (c->kv_fp8) {
         if (!(c->k_scale > 0.f) || !(c->v_scale > 0.f) || !std::isfinite(c->k_scale) ||
             !std::isfinite(c->v_scale))
@@ -465,6 +474,7 @@ static int enqueue_step(qd_model* m, hipStream_t s)
             p.vc = Ly.vc;
             p.k_scale = m->k_scale;
             p.v_scale = m->v_scale;
+            p.gate = m->attn_gate ? m->qkv_raw + (size_t)(m->nq + 2 * m->nkv) * m->hd : nullptr;
             if (m->kv_fp8)
                 launch_attention<1, true>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, 1, m->nq, s);
             else
@@ -629,7 +639,9 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
     m->k_scale = c.kv_fp8 ? c.k_scale : 1.f;
     m->v_scale = c.kv_fp8 ? c.v_scale : 1.f;
     m->nblocks = c.kv_paged ? c.num_kv_blocks : 0;
-    m->qkv_rows = (m->nq + 2 * m->nkv) * m->hd;
+    m->attn_gate = c.attn_out_gate;
+    // q | k | v (| gate): the gate rows project the same normed input
+    m->qkv_rows = (m->nq + 2 * m->nkv + (m->attn_gate ? m->nq : 0)) * m->hd;
     m->use_graph = c.use_graph ? 1 : 0;
     const int H = m->H, hd = m->hd, nqd = m->nq * hd, nkd = m->nkv * hd;
 
@@ -644,6 +656,8 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
         for (int r = 0; r < nqd; ++r) rows.push_back({&S.wq, r});
         for (int r = 0; r < nkd; ++r) rows.push_back({&S.wk, r});
         for (int r = 0; r < nkd; ++r) rows.push_back({&S.wv, r});
+        if (m->attn_gate)
+            for (int r = 0; r < nqd; ++r) rows.push_back({&S.attn_gate, r});
         if ((rc = upload_rows(m, &D.qkv, rows, H, s))) return bail(rc);
         rows.clear();
         for (int r = 0; r < m->I; ++r) {
