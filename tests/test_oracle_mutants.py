@@ -42,6 +42,14 @@ MUTANTS = {
                       "or_rmsnorm(m->k + gg * hd, L->q_norm, hd, c->eps, m->tmp);"),
     "model_kv_unrounded": ("return m->cfg.kv_round ? or_f16_to_f64(or_f64_to_f16(val)) : val;",
                            "return val;"),
+    "e4m3_bias": ("ldexp(1.0 + mant / 8.0, e - 7)", "ldexp(1.0 + mant / 8.0, e - 8)"),
+    "e4m3_round_trunc": ("int mant = (int)nearbyint((2.0 * f - 1.0) * 8.0);",
+                         "int mant = (int)floor((2.0 * f - 1.0) * 8.0);"),
+    "e4m3_no_saturation": ("    if (a > 448.0)\n        a = 448.0;", "    if (a > 480.0)\n        a = 480.0;"),
+    "fp8_scale_ignored": ("return or_e4m3_to_f64(or_f64_to_e4m3(val / sc)) * sc;",
+                          "return or_e4m3_to_f64(or_f64_to_e4m3(val));"),
+    "out_gate_sign": ("m->att[i] *= 1.0 / (1.0 + exp(-m->o[i]));", "m->att[i] *= 1.0 / (1.0 + exp(m->o[i]));"),
+    "out_gate_input": ("or_gemv_q4_0(&L->wag, m->h, m->o, nt);", "or_gemv_q4_0(&L->wag, m->x, m->o, nt);"),
     "model_rope_pos": ("or_rope_neox(m->q + hh * hd, (int32_t)hd, c->rot_dim, c->inv_freq, pos);",
                        "or_rope_neox(m->q + hh * hd, (int32_t)hd, c->rot_dim, c->inv_freq, pos + 1);"),
 }
