@@ -165,3 +165,39 @@ def test_attention_kv8_ragged_and_contiguous(hd, nq, nkv):
     vc8 = synth.quantize_e4m3(vc.view(np.float16).astype(np.float64))
     got_c = _run_kv8(a, k8, v8, paged=False, contig=(kc8, vc8))
     assert np.array_equal(got, got_c)
+
+
+def test_attention_kv8_graph_replays_equal_eager():
+    """qd_attn_decode_kv8 captured in a graph, replayed several times with eager
+    work and synchronisations between the replays: every replay equals the
+    eager call (bitwise)."""
+    import torch
+    import token_decode_q4_amd as qd
+    a = synth.random_attn(77, 2, [300, 1000], nq=32, nkv=8, hd=128)
+    k8, v8 = _kv8_pools(a)
+    ref = _run_kv8(a, k8, v8)
+    max_kv = max(1, a.max_kv_len)
+    ws = torch.zeros(qd.attn_workspace_bytes(a.B, a.nq, a.nkv, a.hd, max_kv), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.full((a.B, a.nq, a.hd), float("nan"), dtype=torch.float32, device="cuda")
+    q, K, V, L, T = dev(a.q), dev(k8), dev(v8), dev(a.kv_lens), dev(a.block_tables)
+    ks, vs = KV8_SCALES
+    s = torch.cuda.Stream()
+
+    def call():
+        qd.attn_decode_kv8(q, K, V, L, max_kv, a.nkv, 1.0 / np.sqrt(a.hd), ks, vs, out, ws,
+                           block_tables=T, stream=s)
+
+    with torch.cuda.stream(s):
+        call()
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            call()
+    for _ in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref)
+        _run_kv8(a, k8, v8)   # eager work between the replays

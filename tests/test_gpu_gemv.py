@@ -194,3 +194,35 @@ def test_stream_read_xor(nbytes):
     qd.stream_read(src, sink)
     got = np.bitwise_xor.reduce(host(sink).view(np.uint32))
     assert got == np.bitwise_xor.reduce(words)
+
+
+def test_gemv_batch_graph_replays_equal_eager():
+    """qd_gemv_q4_0_batch captured in a graph (vector kernel at B = 3, matrix
+    cores at B = 12), replayed several times with eager work and
+    synchronisations between the replays: every replay equals the eager call."""
+    import torch
+    import token_decode_q4_amd as qd
+    W, _ = synth.random_gemv(21, 4096, 2048)
+    d, q = dev(W.d), dev(W.qs)
+    for B in (3, 12):
+        X = dev(synth.batch_x(22 + B, B, 2048))
+        eager = torch.empty((B, 4096), dtype=torch.float32, device="cuda")
+        qd.gemv_q4_0_batch(d, q, X, eager)
+        torch.cuda.synchronize()
+        ref = eager.cpu().numpy()
+        Y = torch.full((B, 4096), float("nan"), dtype=torch.float32, device="cuda")
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            qd.gemv_q4_0_batch(d, q, X, Y, stream=s)   # warm-up outside the capture
+            s.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                qd.gemv_q4_0_batch(d, q, X, Y, stream=s)
+        for _ in range(3):
+            Y.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(Y.cpu().numpy(), ref)
+            qd.gemv_q4_0_batch(d, q, X, eager)   # eager work between the replays
+            torch.cuda.synchronize()
