@@ -23,7 +23,8 @@ Also reported, on the same JSON line:
                 the host cores (a bounded sample from position 0).
 
   rows          per-row measurements: the isolated GEMV at the five sweep
-                shapes and the isolated attention at the four cases (graphs of
+                shapes, the batched and the expert GEMV, and the isolated
+                attention at the four cases (f16 and fp8 caches) (graphs of
                 100 launches over >= 1 GiB of rotated copies, each output
                 checked against the f64 oracle, the oracle's host time beside
                 it), and greedy decode at the Qwen3-0.6B shape.
@@ -264,6 +265,48 @@ def gemv_batch_rows(batches=(1, 2, 4, 8, 16), reps: int = 100, min_bytes: int = 
     del ds, qs, d0, q0
     torch.cuda.empty_cache()
     return rows
+
+
+def experts_row(reps: int = 100, min_bytes: int = 1 << 30):
+    """The expert GEMV (qd_gemv_q4_0_experts) at a mixture-of-experts decode
+    shape: 8 of 64 experts of 1536 x 2048 (gate|up of a 768-wide expert over a
+    2048 hidden), stacks rotated over >= 1 GiB so every launch reads its
+    experts cold.  Algorithmic bytes = 8 * (N*K*18/32 + 4N) + 4K."""
+    import torch
+    import oracle
+    import synth
+    import token_decode_q4_amd as qd
+    E, N, K, k = 64, 1536, 2048, 8
+    W = synth.random_experts(4242, E, N, K)
+    x = synth.batch_x(4243, 1, K)[0]
+    picks = np.array([2, 9, 17, 30, 33, 41, 50, 63], dtype=np.int32)
+    stack = W.d.nbytes + W.qs.nbytes
+    copies = max(1, -(-min_bytes // stack))
+    d0 = torch.from_numpy(W.d.view(np.int16).reshape(E, N, -1)).cuda()
+    q0 = torch.from_numpy(W.qs.reshape(E, N, K // 32, 16)).cuda()
+    ds = [d0] + [d0.clone() for _ in range(copies - 1)]
+    qs = [q0] + [q0.clone() for _ in range(copies - 1)]
+    e_t = torch.from_numpy(picks).cuda()
+    xt = torch.from_numpy(x).cuda()
+    y = torch.empty((k, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        qd.gemv_q4_0_experts(d0, q0, e_t, xt, y, stream=stream)
+    stream.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    err = 0.0
+    for j, e in enumerate(picks):
+        ref = oracle.gemv(synth.expert_rows(W, int(e), N), x)
+        err = max(err, float(np.max(np.abs(got[j] - ref)) / float(np.max(np.abs(ref)))))
+    us = _graph_time(stream, lambda i: qd.gemv_q4_0_experts(ds[i % copies], qs[i % copies], e_t, xt, y,
+                                                            stream=stream), reps)
+    algo = k * (N * K * 18 // 32 + 4 * N) + 4 * K
+    gbs = algo / (us * 1e-6) / 1e9
+    del ds, qs, d0, q0
+    torch.cuda.empty_cache()
+    return {"shape": f"{k} of {E} experts, {N}x{K}", "mean_us": round(us, 3), "achieved": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": algo, "stack_copies": copies,
+            "normwise_err_vs_oracle": err}
 
 
 def attention_rows(reps: int = 100, min_bytes: int = 1 << 30, kv8: bool = False):
@@ -517,6 +560,9 @@ def main():
         for r in b_rows:
             log(f"gemv batch {r['batch']} {r['shape']}: {r['mean_us']} us, {r['achieved']} GB/s "
                 f"({r['frac']:.3f}), {r['vectors_per_s']:.0f} vectors/s, err {r['normwise_err_vs_oracle']:.1e}")
+        x_row = experts_row()
+        log(f"gemv experts {x_row['shape']}: {x_row['mean_us']} us, {x_row['achieved']} GB/s "
+            f"({x_row['frac']:.3f}), err {x_row['normwise_err_vs_oracle']:.1e}")
         a_rows = attention_rows()
         a_rows += attention_rows(kv8=True)
         for r in a_rows:
@@ -526,6 +572,7 @@ def main():
         if d06:
             log(f"decode {d06['workload']}: {d06['tok_s']} tok/s ({d06['step_roofline']['frac']:.3f})")
         rows = {"gemv_sweep": g_rows, "gemv_sweep_aggregate": g_agg, "gemv_batch": b_rows,
+                "gemv_experts": x_row,
                 "attention": a_rows,
                 "decode_qwen3_0.6b": d06}
         log(f"row legs {time.time() - t0:.1f}s")

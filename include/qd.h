@@ -188,6 +188,21 @@ int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x
 int qd_gemv_q4_0_batch(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x, float* d_y,
                        int32_t N, int32_t K, int32_t B, qd_stream stream);
 
+/* Expert GEMV for mixture-of-experts decode (inferencelayer cuda_llm.rs page,
+ * its MoE expert matrices): y[j] = W[experts[j]] x for j < k.  W is a stack
+ * of n_experts q4_0 matrices [N, K] (d_scales [n_experts][N][K/32], d_qs
+ * [n_experts][N][K/32][16], device); d_experts device int32 [k], the indices
+ * a router picked (not read by the host); d_x device f32 [K]; d_y device f32
+ * [k][N].  Each selected matrix is read once per call (an expert picked twice
+ * is read twice).  An index outside [0, n_experts) gives a NaN row and reads
+ * nothing.  K % 32 == 0, qs and x 16-byte aligned, K up to 14 144, N < 2^24,
+ * N*K/2 < 2^32 per expert, k <= 65535 and N*k < 2^31 (QD_EINVAL /
+ * QD_EUNSUPPORTED otherwise).  Routing itself is the caller's.  No
+ * allocation; capturable. */
+int qd_gemv_q4_0_experts(const uint16_t* d_scales, const uint8_t* d_qs, const int32_t* d_experts,
+                         int32_t n_experts, int32_t k, const float* d_x, float* d_y, int32_t N,
+                         int32_t K, qd_stream stream);
+
 /* Rotary frequencies for qd_config.inv_freq (host only, no device work):
  * out[i] = theta^(-2i/rot_dim) for i < rot_dim/2, evaluated in f64 and rounded
  * to f32, with the rotary scaling of the inferencelayer cuda_llm.rs page

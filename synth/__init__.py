@@ -335,6 +335,17 @@ def random_gemv(seed: int, N: int, K: int, x_scale: float = 1.0):
     return W, x
 
 
+def random_experts(seed: int, n_experts: int, N: int, K: int) -> Q4Matrix:
+    """A stack of n_experts q4_0 matrices [N, K] (weights N(0, 0.02)) as one
+    [n_experts * N, K] matrix: expert e is rows e*N .. (e+1)*N."""
+    return random_q4_matrix(seed, 5, n_experts * N, K, _workers())
+
+
+def expert_rows(W: Q4Matrix, e: int, N: int) -> Q4Matrix:
+    """Expert e of a stack as its own matrix (a view)."""
+    return Q4Matrix(W.d[e * N:(e + 1) * N], W.qs[e * N:(e + 1) * N])
+
+
 def batch_x(seed: int, B: int, K: int) -> np.ndarray:
     """B input vectors of a batched GEMV case: f32 [B, K], N(0,1), each row from
     its own seed key."""

@@ -236,3 +236,18 @@ def test_attention_kv8_validation(qd):
     assert call(head_dim=96) == qd._native.QD_EUNSUPPORTED
     assert call(nq=12) == E                              # nq % nkv != 0
     assert call(nq=48) == qd._native.QD_EUNSUPPORTED     # GQA group 6
+
+
+
+def test_gemv_experts_validation(qd):
+    L = qd.lib()
+    p = C.c_void_p(16)
+    E, U = qd._native.QD_EINVAL, qd._native.QD_EUNSUPPORTED
+    assert L.qd_gemv_q4_0_experts(p, p, None, 8, 2, p, p, 64, 64, None) == E
+    assert L.qd_gemv_q4_0_experts(p, p, p, 0, 2, p, p, 64, 64, None) == E
+    assert L.qd_gemv_q4_0_experts(p, p, p, 8, -1, p, p, 64, 64, None) == E
+    assert L.qd_gemv_q4_0_experts(p, p, p, 8, 2, p, p, 64, 65, None) == E
+    assert L.qd_gemv_q4_0_experts(p, p, p, 8, 70000, p, p, 64, 64, None) == U
+    assert L.qd_gemv_q4_0_experts(p, p, p, 8, 2, p, p, 64, 32 * 100000, None) == U
+    assert L.qd_gemv_q4_0_experts(p, C.c_void_p(18), p, 8, 2, p, p, 64, 64, None) == E
+    assert b"aligned" in L.qd_last_error()

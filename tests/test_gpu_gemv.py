@@ -226,3 +226,28 @@ def test_gemv_batch_graph_replays_equal_eager():
             assert np.array_equal(Y.cpu().numpy(), ref)
             qd.gemv_q4_0_batch(d, q, X, eager)   # eager work between the replays
             torch.cuda.synchronize()
+
+
+
+@pytest.mark.parametrize("N,K", [(1536, 2048), (100, 1024), (4097, 96)])
+def test_gemv_experts_vs_oracle(N, K):
+    """y[j] = W[experts[j]] x for picked experts (a repeat and the last expert
+    included) against the f64 oracle of each expert's matrix; indices outside
+    the stack give NaN rows and leave the other rows intact."""
+    import torch
+    import token_decode_q4_amd as qd
+    E = 16
+    W = synth.random_experts(900 + N, E, N, K)
+    x = synth.batch_x(901, 1, K)[0]
+    picks = np.array([3, 15, 0, 3, 9, -1, 7, 16], dtype=np.int32)
+    y = torch.full((len(picks), N), 0.0, dtype=torch.float32, device="cuda")
+    qd.gemv_q4_0_experts(dev(W.d.reshape(E, N, -1)), dev(W.qs.reshape(E, N, K // 32, 16)),
+                         dev(picks), dev(x), y)
+    got = host(y)
+    for j, e in enumerate(picks):
+        if 0 <= e < E:
+            ref = oracle.gemv(synth.expert_rows(W, int(e), N), x)
+            assert normwise(got[j], ref) <= 2e-6, (j, e)
+        else:
+            assert np.all(np.isnan(got[j])), (j, e)
+    assert np.array_equal(got[0], got[3])   # the same expert twice: the same row, bitwise

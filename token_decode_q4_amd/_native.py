@@ -19,7 +19,7 @@ QD_OK, QD_EINVAL, QD_ERANGE, QD_ENOMEM, QD_EUNSUPPORTED, QD_EHIP = 0, -1, -2, -3
 
 # every function declared in include/qd.h
 EXPORTS = ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate",
-           "qd_gemv_q4_0", "qd_gemv_q4_0_batch", "qd_rope_inv_freq", "qd_attn_workspace_bytes",
+           "qd_gemv_q4_0", "qd_gemv_q4_0_batch", "qd_gemv_q4_0_experts", "qd_rope_inv_freq", "qd_attn_workspace_bytes",
            "qd_attn_decode_kv8", "qd_attn_decode", "qd_check",
            "qd_stream_read_groups", "qd_stream_read", "qd_last_error")
 
@@ -93,6 +93,8 @@ def lib():
                                    C.c_int32, C.c_void_p]
         L.qd_gemv_q4_0_batch.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
                                          C.c_int32, C.c_int32, C.c_void_p]
+        L.qd_gemv_q4_0_experts.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
+                                           C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]
         L.qd_rope_inv_freq.argtypes = [C.c_float, C.c_int32, C.c_int32, C.c_float, C.c_float,
                                        C.c_float, C.c_float, C.c_void_p]
         L.qd_attn_workspace_bytes.restype = C.c_size_t
@@ -147,6 +149,16 @@ def gemv_q4_0_batch(d, qs, x, y, stream=None) -> int:
     N = y.shape[1]
     return check(lib().qd_gemv_q4_0_batch(_ptr(d), _ptr(qs), _ptr(x), _ptr(y), N, K, B,
                                           _stream(stream)))
+
+
+def gemv_q4_0_experts(d, qs, experts, x, y, stream=None) -> int:
+    """y[j] = W[experts[j]] x: d [E, N, K/32] uint16/int16, qs [E, N, K/32, 16] uint8,
+    experts device int32 [k], x device f32 [K], y device f32 [k, N]."""
+    E, N = d.shape[0], d.shape[1]
+    K = x.shape[0]
+    k = experts.shape[0]
+    return check(lib().qd_gemv_q4_0_experts(_ptr(d), _ptr(qs), _ptr(experts), E, k, _ptr(x),
+                                            _ptr(y), N, K, _stream(stream)))
 
 
 ROPE_SCALING = {"default": 0, "linear": 1, "llama3": 2}

@@ -15,6 +15,7 @@
 #include "gemv_cfg.h"
 #include "gemv_batch.h"
 #include "gemv_batch_mfma.h"
+#include "gemv_experts.h"
 #include "stream_read.h"
 
 #include <algorithm>
@@ -1052,6 +1053,52 @@ extern "C" int qd_gemv_q4_0_batch(const uint16_t* d_scales, const uint8_t* d_qs,
     case 15: HIP_TRY(launch_gemv_batch<15>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
     default: HIP_TRY(launch_gemv_batch<16>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
     }
+    return QD_OK;
+}
+
+// ------------------------------------------------------------------ expert GEMV
+
+extern "C" int qd_gemv_q4_0_experts(const uint16_t* d_scales, const uint8_t* d_qs,
+                                    const int32_t* d_experts, int32_t n_experts, int32_t k,
+                                    const float* d_x, float* d_y, int32_t N, int32_t K,
+                                    qd_stream stream)
+{
+    if (!d_scales || !d_qs || !d_experts || !d_x || !d_y)
+        return fail(QD_EINVAL, "null pointer");
+    if (N < 0 || K < 0 || K % 32 || n_experts <= 0 || k < 0)
+        return fail(QD_EINVAL, "bad shape N=%d K=%d n_experts=%d k=%d", N, K, n_experts, k);
+    if (k > 65535 || (int64_t)N * k >= ((int64_t)1 << 31))
+        return fail(QD_EUNSUPPORTED, "k=%d experts per call (above 65535, or N*k >= 2^31)", k);
+    if (gemv_lds_bytes(K / 32) > (size_t)GEMV_MAX_LDS)
+        return fail(QD_EUNSUPPORTED, "K=%d above the staged-x limit", K);
+    if ((uint64_t)N * (uint64_t)K / 2 >= (uint64_t)1 << 32 || N >= (1 << 24))
+        return fail(QD_EUNSUPPORTED, "N=%d K=%d: above 2^32 bytes of nibbles or 2^24 rows", N, K);
+    if ((reinterpret_cast<uintptr_t>(d_qs) | reinterpret_cast<uintptr_t>(d_x)) & 15)
+        return fail(QD_EINVAL, "qs and x must be 16-byte aligned");
+    if (N == 0 || k == 0)
+        return QD_OK;
+    const hipStream_t s = (hipStream_t)stream;
+    if (K == 0) {
+        hipLaunchKernelGGL(k_fill_f32, dim3((N * k + 255) / 256), dim3(256), 0, s, d_y, N * k, 0.f);
+        HIP_TRY(hipGetLastError());
+        return QD_OK;
+    }
+    const int nb = K / 32, lpr = pick_lpr(nb);
+    const dim3 grid(gemv_grid(CFG_O, lpr, N), k);
+    switch (lpr) {
+#define QD_EXP(L)                                                                                  \
+    case L:                                                                                        \
+        hipLaunchKernelGGL((k_gemv_experts<L, QD_CFG_O>), grid, dim3(QD_NW(QD_CFG_O) * WAVE),        \
+                           gemv_lds_bytes(nb), s, d_scales, d_qs, d_experts, n_experts, d_x, d_y, N, nb); \
+        break;
+    QD_EXP(64) QD_EXP(32) QD_EXP(16)
+    default:
+        hipLaunchKernelGGL((k_gemv_experts<8, QD_CFG_O>), grid, dim3(QD_NW(QD_CFG_O) * WAVE),
+                           gemv_lds_bytes(nb), s, d_scales, d_qs, d_experts, n_experts, d_x, d_y, N, nb);
+        break;
+#undef QD_EXP
+    }
+    HIP_TRY(hipGetLastError());
     return QD_OK;
 }
 
