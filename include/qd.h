@@ -166,6 +166,24 @@ int qd_set_prompt(qd_model* m, const int32_t* tokens, int32_t n, qd_stream strea
 int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* d_tokens,
                 float* d_logits_last, qd_stream stream);
 
+/* Chunked prompt prefill (inferencelayer cuda_llm.rs page: prefill as the
+ * many-token form of the decode step, its q4 GEMV arm at M > 1): runs the
+ * positions pos0 .. pos0+n-1 in chunks of up to 16, each chunk one batched
+ * GEMV per matrix (every weight read once per chunk), with the tokens
+ * stored by qd_set_prompt (or an earlier step).  It writes the K/V cache of
+ * every position as n decode steps would, and at the last position p =
+ * pos0+n-1 it records what a decode step at p records: the argmax of its
+ * logits as the prediction at p and, if p+1 is not forced, the token at
+ * p+1.  d_logits_last (device f32 [vocab] or NULL) receives the logits at p.
+ * Each position's values equal the decode step's up to f32 rounding order.
+ * Continue with qd_generate(pos0 + n, ...).  Buffers (about 16 positions of
+ * activations plus an attention workspace) are allocated by the first call,
+ * which synchronises; later calls allocate nothing.  The weight scales must
+ * satisfy |d| < 8192 (the matrix-core GEMV, as qd_gemv_q4_0_batch).
+ * QD_ERANGE unless 0 <= pos0, n >= 1 and pos0 + n <= max_seq;
+ * QD_EUNSUPPORTED for a model with attn_out_gate. */
+int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_last, qd_stream stream);
+
 /* Standalone q4_0 GEMV (inferencelayer cuda_llm.rs page, CudaQwen3::gemv):
  * y[N] = W[N, K] x[K], W in the q4_0 layout above (device d_scales
  * [N][K/32], d_qs [N][K/32][16]), x and y device f32.  K % 32 == 0; qs and x

@@ -251,3 +251,9 @@ def test_gemv_experts_validation(qd):
     assert L.qd_gemv_q4_0_experts(p, p, p, 8, 2, p, p, 64, 32 * 100000, None) == U
     assert L.qd_gemv_q4_0_experts(p, C.c_void_p(18), p, 8, 2, p, p, 64, 64, None) == E
     assert b"aligned" in L.qd_last_error()
+
+
+def test_model_entry_points_reject_null_model(qd):
+    L = qd.lib()
+    assert L.qd_prefill(None, 0, 1, None, None) == qd._native.QD_EINVAL
+    assert L.qd_generate(None, 0, 1, None, None, None) == qd._native.QD_EINVAL

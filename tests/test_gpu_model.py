@@ -115,7 +115,7 @@ def test_tiny_decode_step_rejects_out_of_range(tiny):
     m.close()
 
 
-def _golden_run(name, layer_kernel=False):
+def _golden_run(name, layer_kernel=False, prefill=False):
     import torch
     import token_decode_q4_amd as qd
     g = load_golden(name)
@@ -127,6 +127,7 @@ def _golden_run(name, layer_kernel=False):
     s = mi.shape
     P, G = s.prompt_len, s.gen
     say(f"{name}: qd_create")
+    say(f"{name}: qd_create (layer_kernel={layer_kernel}, prefill={prefill})")
     m = qd.Model(mi, use_graph=True, layer_kernel=layer_kernel)
     V = s.vocab
     # sample points: prefill positions and greedy steps (greedy step i is at position P-1+i)
@@ -140,12 +141,18 @@ def _golden_run(name, layer_kernel=False):
     m.set_prompt(mi.prompt)
     got_logits = {}
     pos = 0
-    for stop in sorted(points) + [P + G - 1]:
+    # with prefill: positions 0 .. P-2 through qd_prefill (sampled ones as the
+    # last position of a prefill call), the step at P-1 onwards as generation
+    stops = sorted(set(points) | ({P - 1} if prefill else set())) + [P + G - 1]
+    for stop in stops:
         if stop < pos:
             continue
         n = stop + 1 - pos if stop in points else stop - pos
         if n > 0:
-            m.generate(pos, n, tokens=toks[pos:pos + n], logits_last=lg)
+            if prefill and pos + n <= P - 1:
+                m.prefill(pos, n, logits_last=lg)
+            else:
+                m.generate(pos, n, tokens=toks[pos:pos + n], logits_last=lg)
             pos += n
             if stop in points:
                 got_logits[points[stop]] = host(lg).copy()
@@ -174,6 +181,18 @@ def _golden_run(name, layer_kernel=False):
 def test_qwen3_06b_shape_vs_golden():
     n_eq, worst = _golden_run("qwen3-0.6b")
     assert worst <= 1e-3
+
+
+def test_qwen3_06b_shape_prefill_vs_golden():
+    """Chunked prefill (qd_prefill) of the 512-token prompt, then greedy
+    generation, against the same golden file as the sequential decode."""
+    n_eq, worst = _golden_run("qwen3-0.6b", prefill=True)
+    assert worst <= 1e-3
+
+
+def test_qwen3_8b_shape_prefill_vs_golden():
+    n_eq, worst = _golden_run("qwen3-8b", prefill=True)
+    assert worst <= 5e-3
 
 
 def test_qwen3_8b_shape_vs_golden():
@@ -280,3 +299,84 @@ def test_tiny_attn_out_gate_vs_oracle(paged):
     lg_e, _ = _teacher_forced_logits(me, seq, s.vocab)
     me.close()
     assert np.array_equal(lg, lg_e)
+
+
+@pytest.mark.parametrize("paged,kv_fp8", [(False, False), (True, False), (False, True), (True, True)])
+def test_tiny_prefill_vs_oracle(tiny, paged, kv_fp8):
+    """qd_prefill of the 16-token prompt (one full chunk: the matrix-core
+    GEMV), then qd_generate from position 16: logits at the last prompt
+    position against the oracle's, and the free-running greedy tokens."""
+    import torch
+    import token_decode_q4_amd as qd
+    s = tiny.shape
+    P, G = s.prompt_len, s.gen
+    kw = dict(kv_fp8=True, k_scale=0.5, v_scale=0.125) if kv_fp8 else {}
+    say(f"tiny prefill paged={paged} kv_fp8={kv_fp8}")
+    om = oracle.Model(tiny, **kw)
+    toks, margins, _ = oracle.generate(om, tiny.prompt, G)
+    om2 = oracle.Model(tiny, **kw)
+    for p, t in enumerate(tiny.prompt):
+        ref = om2.step(int(t), p)
+    m = qd.Model(tiny, use_graph=True, paged=paged, **kw)
+    m.set_prompt(tiny.prompt)
+    lg = torch.empty(s.vocab, dtype=torch.float32, device="cuda")
+    m.prefill(0, P, logits_last=lg)
+    err = float(np.max(np.abs(host(lg) - ref)))
+    say(f"tiny prefill logits max abs err {err:.3e}")
+    assert err <= 1e-4
+    out = torch.full((G - 1,), -1, dtype=torch.int32, device="cuda")
+    m.generate(P, G - 1, tokens=out)
+    m.check()
+    m.close()
+    # the prefill's prediction at P-1 became the token at P; the generated
+    # steps predict the rest
+    got = np.concatenate([[int(np.argmax(host(lg)))], host(out)])
+    check_greedy(got, toks, margins, "tiny prefill")
+
+
+def test_tiny_prefill_ragged_chunks_vs_oracle(tiny, tiny_ref):
+    """40 teacher-forced positions prefilled as 21 + 19 (chunks of 16, 5, 16
+    and 3 positions: both batched GEMV kernels), logits at positions 20 and
+    39 against the oracle's, then generation of the remaining greedy tokens."""
+    import torch
+    import token_decode_q4_amd as qd
+    toks, margins, seq, ref = tiny_ref
+    s = tiny.shape
+    P = s.prompt_len
+    n = 40
+    say("tiny prefill ragged chunks")
+    m = qd.Model(tiny, use_graph=True)
+    m.set_prompt(seq[:n])
+    lg = torch.empty(s.vocab, dtype=torch.float32, device="cuda")
+    m.prefill(0, 21, logits_last=lg)
+    e1 = float(np.max(np.abs(host(lg) - ref[20])))
+    m.prefill(21, n - 21, logits_last=lg)
+    e2 = float(np.max(np.abs(host(lg) - ref[n - 1])))
+    say(f"tiny ragged prefill logits max abs err {e1:.3e} {e2:.3e}")
+    assert max(e1, e2) <= 1e-4
+    rest = s.max_seq - 1 - n
+    out = torch.full((rest,), -1, dtype=torch.int32, device="cuda")
+    m.generate(n, rest, tokens=out)
+    m.check()
+    m.close()
+    # the step at position p predicts greedy token p - (P - 1); the first
+    # compared token is the prefill's prediction at n - 1
+    i0 = n - P
+    got = np.concatenate([[int(np.argmax(host(lg)))], host(out)])
+    check_greedy(got, toks[i0:i0 + len(got)], margins[i0:i0 + len(got)], "tiny ragged prefill")
+
+
+def test_tiny_prefill_rejects(tiny):
+    import token_decode_q4_amd as qd
+    m = qd.Model(tiny)
+    for pos0, n in [(0, 0), (-1, 4), (tiny.shape.max_seq, 1), (tiny.shape.max_seq - 3, 4)]:
+        with pytest.raises(qd.QdError) as ei:
+            m.prefill(pos0, n)
+        assert ei.value.code == qd._native.QD_ERANGE
+    m.close()
+    mi = synth.make_model("tiny", attn_out_gate=True)
+    mg = qd.Model(mi)
+    with pytest.raises(qd.QdError) as ei:
+        mg.prefill(0, 4)
+    assert ei.value.code == qd._native.QD_EUNSUPPORTED
+    mg.close()

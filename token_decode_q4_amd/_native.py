@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libqd.so")
 QD_OK, QD_EINVAL, QD_ERANGE, QD_ENOMEM, QD_EUNSUPPORTED, QD_EHIP = 0, -1, -2, -3, -4, -5
 
 # every function declared in include/qd.h
-EXPORTS = ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate",
+EXPORTS = ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate", "qd_prefill",
            "qd_gemv_q4_0", "qd_gemv_q4_0_batch", "qd_gemv_q4_0_experts", "qd_rope_inv_freq", "qd_attn_workspace_bytes",
            "qd_attn_decode_kv8", "qd_attn_decode", "qd_check",
            "qd_stream_read_groups", "qd_stream_read", "qd_last_error")
@@ -89,6 +89,7 @@ def lib():
         L.qd_set_prompt.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p]
         L.qd_generate.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                   C.c_void_p]
+        L.qd_prefill.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
         L.qd_gemv_q4_0.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
                                    C.c_int32, C.c_void_p]
         L.qd_gemv_q4_0_batch.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
@@ -107,7 +108,7 @@ def lib():
         L.qd_stream_read_groups.argtypes = [C.c_size_t]
         L.qd_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
         L.qd_last_error.restype = C.c_char_p
-        for n in ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate",
+        for n in ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate", "qd_prefill",
                   "qd_gemv_q4_0", "qd_attn_decode", "qd_check", "qd_stream_read"):
             getattr(L, n).restype = C.c_int
         _lib = L
@@ -278,6 +279,10 @@ class Model:
     def generate(self, pos0: int, n_steps: int, tokens=None, logits_last=None, stream=None):
         return check(lib().qd_generate(self._h, int(pos0), int(n_steps), _ptr(tokens),
                                        _ptr(logits_last), _stream(stream)))
+
+    def prefill(self, pos0: int, n: int, logits_last=None, stream=None):
+        """Chunked prefill of positions pos0 .. pos0+n-1 (qd_prefill)."""
+        return check(lib().qd_prefill(self._h, int(pos0), int(n), _ptr(logits_last), _stream(stream)))
 
     def check(self, stream=None):
         """Synchronise and raise QdError if the device recorded an error since

@@ -67,6 +67,9 @@ struct AttnParams {
     // attention output gate (decode step): the merged output of head h, dim d
     // is multiplied by sigmoid(gate[h * HD + d]); nullptr = none
     const float* gate;
+    // 1: every sequence b reads the cache of sequence 0 (the B queries of a
+    // prefill chunk over one cache, each with its own kv_len)
+    int shared_kv;
 };
 
 constexpr int ATT_WK = 16;                 // keys per wave step (one paged block)
@@ -261,6 +264,7 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
     const int kk = lane & 15;                  // QK: the key of this lane's A rows
     const int h0 = g * GQ;
     const int t_begin = s * p.chunk;
+    const int bk = p.shared_kv ? 0 : b;        // the sequence whose cache is read
     QD_MARK(0);
 
     // loads of one wave step at key tw, any tw: rows and table entries are
@@ -276,13 +280,13 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
             const uint8_t* v8 = reinterpret_cast<const uint8_t*>(p.v);
             size_t kb, vb;
             if (PAGED) {
-                const int phys = max(0, p.tables[(size_t)b * p.mbps + twc / ATT_BS]);
+                const int phys = max(0, p.tables[(size_t)bk * p.mbps + twc / ATT_BS]);
                 const size_t base = kv_row<HD, PAGED>(p, phys, g, twc & ~(ATT_BS - 1));
                 kb = base + (size_t)kk * HD;
                 vb = base;
             } else {
-                kb = kv_row<HD, PAGED>(p, b, g, min(tw + kk, p.max_kv - 1));
-                vb = kv_row<HD, PAGED>(p, b, g, 0);
+                kb = kv_row<HD, PAGED>(p, bk, g, min(tw + kk, p.max_kv - 1));
+                vb = kv_row<HD, PAGED>(p, bk, g, 0);
             }
 #pragma unroll
             for (int i = 0; i < NI / 2; ++i)
@@ -300,13 +304,13 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
         }
         const uint16_t *kp, *vp;
         if (PAGED) {
-            const int phys = max(0, p.tables[(size_t)b * p.mbps + twc / ATT_BS]);
+            const int phys = max(0, p.tables[(size_t)bk * p.mbps + twc / ATT_BS]);
             const size_t base = kv_row<HD, PAGED>(p, phys, g, twc & ~(ATT_BS - 1));
             kp = p.k + base + (size_t)kk * HD;
             vp = p.v + base;
         } else {
-            kp = p.k + kv_row<HD, PAGED>(p, b, g, min(tw + kk, p.max_kv - 1));
-            vp = p.v + kv_row<HD, PAGED>(p, b, g, 0);
+            kp = p.k + kv_row<HD, PAGED>(p, bk, g, min(tw + kk, p.max_kv - 1));
+            vp = p.v + kv_row<HD, PAGED>(p, bk, g, 0);
         }
 #pragma unroll
         for (int i = 0; i < NI; ++i)

@@ -1,0 +1,148 @@
+// prefill_kernels.h -- the elementwise and per-row kernels of a chunked
+// prefill (gfx950): T <= 16 prompt positions at a time, every weight read once
+// per chunk by the batched GEMV, the same arithmetic per position as the
+// decode step (inferencelayer cuda_llm.rs page: prefill as the M > 1 form of
+// the step; the step's order of operations).
+#pragma once
+
+#include "step_kernels.h"
+
+namespace qd {
+
+constexpr int PF_T = 16;   // positions per chunk
+
+// X[t][i] = dequant(E)[ids[p0 + t]][i]; grid (ceil(H/256), T)
+__global__ void __launch_bounds__(256)
+k_pf_embed(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, int H,
+           const int32_t* __restrict__ ids, int p0, float* __restrict__ X)
+{
+    const int t = blockIdx.y, i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= H)
+        return;
+    const int tok = ids[p0 + t];   // validated by the host when stored
+    const int nb = H / 32, bk = i >> 5, j = i & 31;
+    const size_t blk = (size_t)tok * nb + bk;
+    const uint8_t byte = Eq[blk * 16 + (j & 15)];
+    const int code = (j < 16) ? (byte & 15) : (byte >> 4);
+    X[(size_t)t * H + i] = (float)(code - 8) * f16_to_f32(Ed[blk]);
+}
+
+// out[t] = X[t] * (1 / sqrt(mean(X[t]^2) + eps)) * w; grid T, 256 threads
+__global__ void __launch_bounds__(256)
+k_pf_rmsnorm(const float* __restrict__ X, const float* __restrict__ w, int H, float eps,
+             float* __restrict__ out)
+{
+    __shared__ float red[8];
+    const float* x = X + (size_t)blockIdx.x * H;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < H; i += blockDim.x)
+        ss = fmaf(x[i], x[i], ss);
+    ss = block_sum256(ss, red);
+    const float r = 1.0f / sqrtf(ss / (float)H + eps);
+    for (int i = threadIdx.x; i < H; i += blockDim.x)
+        out[(size_t)blockIdx.x * H + i] = x[i] * r * w[i];
+}
+
+// X += Y over n elements
+__global__ void __launch_bounds__(256) k_pf_add(float* __restrict__ X, const float* __restrict__ Y, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        X[i] += Y[i];
+}
+
+// A[t][i] = silu(G[t][2i]) * G[t][2i+1] (gate and up rows interleaved); n = T * I
+__global__ void __launch_bounds__(256) k_pf_swiglu(const float* __restrict__ G, float* __restrict__ A, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        const float g = G[2 * (size_t)i], u = G[2 * (size_t)i + 1];
+        A[i] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;   // as the step's SwiGLU epilogue
+    }
+}
+
+// Per position t (grid.y) and head (grid.x: nq query heads, then nkv kv heads),
+// one wave per head: q/k RMSNorm over the head (if qk_norm), NeoX rotary at
+// position p0 + t from the tables, then q -> Qr[t][h], and for a kv head K and
+// V into the cache at p0 + t (f16, or e4m3 of value / scale).  Also
+// kv_lens[t] = p0 + t + 1.
+template <int HD, bool KV8>
+__global__ void __launch_bounds__(WAVE)
+k_pf_qk(const float* __restrict__ QKV, int qkv_rows, int nq, int nkv, const float* __restrict__ q_norm,
+        const float* __restrict__ k_norm, int qk_norm, float eps, int rot,
+        const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int p0,
+        float* __restrict__ Qr, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+        const int32_t* __restrict__ table, int max_seq, float k_scale, float v_scale,
+        int32_t* __restrict__ kv_lens)
+{
+    constexpr int DPL = HD / WAVE;
+    const int t = blockIdx.y, hh = blockIdx.x, lane = threadIdx.x;
+    const int pos = p0 + t;
+    const bool is_q = hh < nq;
+    const int g = hh - nq;
+    const float* src = QKV + (size_t)t * qkv_rows + (size_t)(is_q ? hh : nq + g) * HD;
+    const float* w = is_q ? q_norm : k_norm;
+    float v[DPL];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+        v[e] = src[lane * DPL + e];
+        ss = fmaf(v[e], v[e], ss);
+    }
+    ss = group_sum<WAVE>(ss);
+    const float r = qk_norm ? 1.0f / sqrtf(ss / (float)HD + eps) : 1.f;
+    __shared__ float row[HD];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+        v[e] = v[e] * r * (qk_norm ? w[lane * DPL + e] : 1.f);
+        row[lane * DPL + e] = v[e];
+    }
+    __syncthreads();
+    const int half = rot / 2;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+        const int d = lane * DPL + e;
+        if (d < rot) {
+            const int i = d < half ? d : d - half;
+            const float c = rope_cos[(size_t)pos * half + i], s = rope_sin[(size_t)pos * half + i];
+            const float partner = row[d < half ? d + half : d - half];
+            v[e] = fmaf(partner, d < half ? -s : s, v[e] * c);
+        }
+    }
+    if (is_q) {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e)
+            Qr[((size_t)t * nq + hh) * HD + lane * DPL + e] = v[e];
+    } else {
+        size_t o;
+        if (table)
+            o = ((((size_t)table[pos / ATT_BS] * nkv + g) * ATT_BS) + pos % ATT_BS) * HD;
+        else
+            o = (((size_t)g * max_seq) + pos) * HD;
+        const float* vsrc = QKV + (size_t)t * qkv_rows + (size_t)(nq + nkv + g) * HD;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) {
+            const int d = lane * DPL + e;
+            const float vv = vsrc[d];
+            if (KV8) {
+                reinterpret_cast<uint8_t*>(kc)[o + d] = (uint8_t)f32_to_e4m3(v[e] / k_scale);
+                reinterpret_cast<uint8_t*>(vc)[o + d] = (uint8_t)f32_to_e4m3(vv / v_scale);
+            } else {
+                kc[o + d] = f32_to_f16(v[e]);
+                vc[o + d] = f32_to_f16(vv);
+            }
+        }
+    }
+    if (hh == 0 && lane == 0)
+        kv_lens[t] = pos + 1;
+}
+
+// logit i -> candidate (value, index i): the argmax kernel's input form
+__global__ void __launch_bounds__(256) k_pf_iota(int32_t* __restrict__ idx, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        idx[i] = i;
+}
+
+}  // namespace qd

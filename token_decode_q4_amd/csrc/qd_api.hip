@@ -16,6 +16,7 @@
 #include "gemv_batch.h"
 #include "gemv_batch_mfma.h"
 #include "gemv_experts.h"
+#include "prefill_kernels.h"
 #include "stream_read.h"
 
 #include <algorithm>
@@ -98,6 +99,15 @@ struct DevLayer {
 struct qd_model {
     int H, L, nq, nkv, hd, I, V, rot, qkv_rows, max_seq, qk_norm, paged, nblocks;
     float eps;
+    // chunked prefill buffers (allocated by the first qd_prefill)
+    struct {
+        float *X = nullptr, *Hn = nullptr, *QKV = nullptr, *Q = nullptr, *O = nullptr,
+              *Y = nullptr, *G = nullptr, *A = nullptr, *hf = nullptr;
+        int32_t *lens = nullptr, *iota = nullptr;
+        float* ws = nullptr;
+        AttnGeom geo;
+        bool ready = false;
+    } pf;
     int kv_fp8 = 0;                 // fp8 e4m3 K/V cache (1 byte per element)
     int attn_gate = 0;              // attention output gate rows after q | k | v
     float k_scale = 1.f, v_scale = 1.f;
@@ -1228,5 +1238,145 @@ extern "C" int qd_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink,
     hipLaunchKernelGGL(k_stream_read, dim3(stream_read_groups(bytes)), dim3(SR_THREADS), 0,
                        (hipStream_t)stream, reinterpret_cast<const uint4*>(d_src), bytes / 16, d_sink);
     HIP_TRY(hipGetLastError());
+    return QD_OK;
+}
+
+// ------------------------------------------------------------------ chunked prefill
+
+// y[t] = W x[t] for t < T through the batched GEMV (the single-vector kernel
+// for one; T single-vector launches where the vector kernel's staged batch
+// would not fit)
+static hipError_t pf_gemv(const DevQ4& W, const float* x, float* y, int T, hipStream_t s)
+{
+    const int N = W.rows, K = W.nb * 32;
+    if (T == 1 || (T < QD_BATCH_MFMA_MIN && (int64_t)T * K > GB_MAXKB)) {
+        for (int t = 0; t < T; ++t) {
+            const hipError_t e = launch_gemv_plain(W.d, W.qs, x + (size_t)t * K, y + (size_t)t * N, N, K, s);
+            if (e != hipSuccess)
+                return e;
+        }
+        return hipSuccess;
+    }
+    switch (T) {
+    case 2: return launch_gemv_batch<2>(W.d, W.qs, x, y, N, K, s);
+    case 3: return launch_gemv_batch<3>(W.d, W.qs, x, y, N, K, s);
+    case 4: return launch_gemv_batch<4>(W.d, W.qs, x, y, N, K, s);
+    case 5: return launch_gemv_batch<5>(W.d, W.qs, x, y, N, K, s);
+    case 6: return launch_gemv_batch<6>(W.d, W.qs, x, y, N, K, s);
+    case 7: return launch_gemv_batch<7>(W.d, W.qs, x, y, N, K, s);
+    case 8: return launch_gemv_batch<8>(W.d, W.qs, x, y, N, K, s);
+    case 9: return launch_gemv_batch<9>(W.d, W.qs, x, y, N, K, s);
+    case 10: return launch_gemv_batch<10>(W.d, W.qs, x, y, N, K, s);
+    case 11: return launch_gemv_batch<11>(W.d, W.qs, x, y, N, K, s);
+    case 12: return launch_gemv_batch<12>(W.d, W.qs, x, y, N, K, s);
+    case 13: return launch_gemv_batch<13>(W.d, W.qs, x, y, N, K, s);
+    case 14: return launch_gemv_batch<14>(W.d, W.qs, x, y, N, K, s);
+    case 15: return launch_gemv_batch<15>(W.d, W.qs, x, y, N, K, s);
+    default: return launch_gemv_batch<16>(W.d, W.qs, x, y, N, K, s);
+    }
+}
+
+static int pf_setup(qd_model* m)
+{
+    if (m->pf.ready)
+        return QD_OK;
+    auto& P = m->pf;
+    const size_t T = PF_T, nqd = (size_t)m->nq * m->hd;
+    const size_t ws = attn_ws_layout(PF_T, m->nq, m->nkv, m->hd, m->max_seq, &P.geo);
+    int rc;
+    if ((rc = dev_alloc_t(m, &P.X, T * m->H)) || (rc = dev_alloc_t(m, &P.Hn, T * m->H)) ||
+        (rc = dev_alloc_t(m, &P.QKV, T * m->qkv_rows)) || (rc = dev_alloc_t(m, &P.Q, T * nqd)) ||
+        (rc = dev_alloc_t(m, &P.O, T * nqd)) || (rc = dev_alloc_t(m, &P.Y, T * m->H)) ||
+        (rc = dev_alloc_t(m, &P.G, T * 2 * (size_t)m->I)) || (rc = dev_alloc_t(m, &P.A, T * m->I)) ||
+        (rc = dev_alloc_t(m, &P.hf, (size_t)m->H)) || (rc = dev_alloc_t(m, &P.lens, T)) ||
+        (rc = dev_alloc_t(m, &P.iota, (size_t)m->V)) || (rc = dev_alloc_t(m, &P.ws, ws / sizeof(float) + 1)))
+        return rc;
+    hipLaunchKernelGGL(k_pf_iota, dim3((m->V + 255) / 256), dim3(256), 0, 0, P.iota, m->V);
+    if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+        return fail(QD_EHIP, "prefill buffer set-up failed");
+    P.ready = true;
+    return QD_OK;
+}
+
+extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_last, qd_stream stream)
+{
+    if (!m)
+        return fail(QD_EINVAL, "null model");
+    if (n <= 0 || pos0 < 0 || (int64_t)pos0 + n > m->max_seq)
+        return fail(QD_ERANGE, "positions [%d, %d) not in [0, %d)", pos0, pos0 + n, m->max_seq);
+    if (m->attn_gate)
+        return fail(QD_EUNSUPPORTED, "qd_prefill with attn_out_gate");
+    QD_TRY(pf_setup(m));
+    auto& P = m->pf;
+    const hipStream_t s = (hipStream_t)stream;
+    const int H = m->H, hd = m->hd, gq = m->nq / m->nkv;
+    const int mbps = (m->max_seq + ATT_BS - 1) / ATT_BS;
+    int T = 0;
+    for (int c0 = 0; c0 < n; c0 += PF_T) {
+        T = std::min(PF_T, n - c0);
+        const int p0 = pos0 + c0;
+        hipLaunchKernelGGL(k_pf_embed, dim3((H + 255) / 256, T), dim3(256), 0, s, m->embed.d, m->embed.qs,
+                           H, m->ids, p0, P.X);
+        for (int l = 0; l < m->L; ++l) {
+            DevLayer& Ly = m->layers[l];
+            hipLaunchKernelGGL(k_pf_rmsnorm, dim3(T), dim3(256), 0, s, P.X, Ly.attn_norm, H, m->eps, P.Hn);
+            HIP_TRY(pf_gemv(Ly.qkv, P.Hn, P.QKV, T, s));
+            const float* qn = m->qk_norm ? Ly.q_norm : m->ones_hd;
+            const float* kn = m->qk_norm ? Ly.k_norm : m->ones_hd;
+            const int32_t* tbl = m->paged ? m->table : nullptr;
+            const dim3 g(m->nq + m->nkv, T);
+#define QD_PFQK(HD_, K8_)                                                                            \
+    hipLaunchKernelGGL((k_pf_qk<HD_, K8_>), g, dim3(WAVE), 0, s, P.QKV, m->qkv_rows, m->nq, m->nkv, qn,  \
+                       kn, m->qk_norm, m->eps, m->rot, m->rope_cos, m->rope_sin, p0, P.Q, Ly.kc, Ly.vc, \
+                       tbl, m->max_seq, m->k_scale, m->v_scale, P.lens)
+            if (hd == 128) {
+                if (m->kv_fp8) QD_PFQK(128, true); else QD_PFQK(128, false);
+            } else {
+                if (m->kv_fp8) QD_PFQK(64, true); else QD_PFQK(64, false);
+            }
+#undef QD_PFQK
+            AttnParams p;
+            memset(&p, 0, sizeof p);
+            p.q = P.Q;
+            p.k = Ly.kc;
+            p.v = Ly.vc;
+            p.tables = tbl;
+            p.mbps = mbps;
+            p.kv_lens = P.lens;
+            p.max_kv = m->max_seq;
+            p.nq = m->nq;
+            p.nkv = m->nkv;
+            p.scale = 1.0f / sqrtf((float)hd);
+            p.chunk = P.geo.chunk;
+            p.nsplit = P.geo.nsplit;
+            p.part = P.ws;
+            p.out = P.O;
+            p.k_scale = m->k_scale;
+            p.v_scale = m->v_scale;
+            p.shared_kv = 1;
+            if (m->kv_fp8)
+                launch_attention<0, true>(p, P.geo.waves, hd, gq, m->paged, T, m->nq, s);
+            else
+                launch_attention<0>(p, P.geo.waves, hd, gq, m->paged, T, m->nq, s);
+            HIP_TRY(pf_gemv(Ly.o, P.O, P.Y, T, s));
+            hipLaunchKernelGGL(k_pf_add, dim3((T * H + 255) / 256), dim3(256), 0, s, P.X, P.Y, T * H);
+            hipLaunchKernelGGL(k_pf_rmsnorm, dim3(T), dim3(256), 0, s, P.X, Ly.ffn_norm, H, m->eps, P.Hn);
+            HIP_TRY(pf_gemv(Ly.gu, P.Hn, P.G, T, s));
+            hipLaunchKernelGGL(k_pf_swiglu, dim3((T * m->I + 255) / 256), dim3(256), 0, s, P.G, P.A,
+                               T * m->I);
+            HIP_TRY(pf_gemv(Ly.down, P.A, P.Y, T, s));
+            hipLaunchKernelGGL(k_pf_add, dim3((T * H + 255) / 256), dim3(256), 0, s, P.X, P.Y, T * H);
+        }
+    }
+    // the last position: final norm, LM head, greedy token as a decode step records it
+    hipLaunchKernelGGL(k_pf_rmsnorm, dim3(1), dim3(256), 0, s, P.X + (size_t)(T - 1) * H, m->final_norm, H,
+                       m->eps, P.hf);
+    HIP_TRY(launch_gemv_plain(m->lm.d, m->lm.qs, P.hf, m->logits, m->V, H, s));
+    hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, s, m->st, m->ids, pos0 + n - 1, -1, -1, 0);
+    hipLaunchKernelGGL(k_argmax_advance, dim3(1), dim3(256), 0, s, m->logits, P.iota, m->V, m->V, m->st,
+                       m->ids, m->pred, m->max_seq);
+    HIP_TRY(hipGetLastError());
+    if (d_logits_last)
+        HIP_TRY(hipMemcpyAsync(d_logits_last, m->logits, sizeof(float) * m->V, hipMemcpyDeviceToDevice, s));
     return QD_OK;
 }
