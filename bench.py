@@ -473,6 +473,44 @@ def cpu_baseline(mi, seconds: float = 15.0):
                       f"0..{n - 1} (prompt tokens), {el:.1f} s"}
 
 
+def prefill_row(model, s, n: int, reps: int = 3):
+    """Prompt positions 0..n-1 of a created model: chunked prefill (qd_prefill,
+    chunks of 16 through the batched GEMV) against prefill as sequential
+    decode steps (qd_generate over the prompt).  The K/V cache is rewritten
+    with the same values; each is timed with events around `reps` runs after
+    one untimed run.  Weight bytes per chunk give its GB/s."""
+    import torch
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_c = timed(lambda: model.prefill(0, n))
+    ms_s = timed(lambda: model.generate(0, n))
+    model.check()
+    chunks = -(-n // 16)
+    H, I = s.hidden, s.intermediate
+    qkv = (s.n_heads + 2 * s.n_kv) * s.head_dim
+    wbytes = s.layers * (q4_bytes(qkv, H) + q4_bytes(H, s.n_heads * s.head_dim) + q4_bytes(2 * I, H)
+                         + q4_bytes(H, I))
+    gbs = chunks * wbytes / (ms_c * 1e-3) / 1e9
+    return {"workload": f"{s.name} prompt positions 0..{n - 1}", "positions": n, "chunk": 16,
+            "chunked_ms": round(ms_c, 3), "chunked_tok_s": round(n / (ms_c * 1e-3), 1),
+            "sequential_ms": round(ms_s, 3), "sequential_tok_s": round(n / (ms_s * 1e-3), 1),
+            "speedup": round(ms_s / ms_c, 2),
+            "layer_weight_bytes_per_chunk": wbytes,
+            "layer_weight_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -487,6 +525,8 @@ def main():
                     help="skip the per-row legs (GEMV sweep shapes, attention cases, 0.6B decode)")
     ap.add_argument("--layer-kernel", type=int, default=0,
                     help="1: one persistent kernel launch per layer (qd_config.layer_kernel)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="print only the prefill row (chunked vs sequential) of --config")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): batch-1 decode of one "
@@ -510,6 +550,11 @@ def main():
     model = qd.Model(mi, use_graph=True, layer_kernel=bool(args.layer_kernel), kv_fp8=args.kv_fp8,
                      k_scale=0.5, v_scale=0.125)
     log(f"qd_create {time.time() - t0:.1f}s")
+    if args.prefill_only:
+        model.set_prompt(mi.prompt)
+        print(json.dumps(prefill_row(model, s, P - 1)), flush=True)
+        model.close()
+        return
     stream = torch.cuda.current_stream()
     toks = torch.empty(s.max_seq, dtype=torch.int32, device="cuda")
     model.set_prompt(mi.prompt)
@@ -534,6 +579,10 @@ def main():
     step_gbs = mean_bytes / (ms * 1e-3 / args.steps) / 1e9
     log(f"decode {args.steps} steps: {ms:.2f} ms, {tok_s:.1f} tok/s, {step_gbs:.0f} GB/s")
     model.check()   # raises if the device recorded an error during the run
+    pf_row = None if args.no_rows else prefill_row(model, s, P - 1)
+    if pf_row:
+        log(f"prefill {P - 1} positions: chunked {pf_row['chunked_tok_s']} tok/s, sequential decode "
+            f"{pf_row['sequential_tok_s']} tok/s")
     model.close()
     del model
     torch.cuda.empty_cache()
@@ -574,6 +623,7 @@ def main():
         rows = {"gemv_sweep": g_rows, "gemv_sweep_aggregate": g_agg, "gemv_batch": b_rows,
                 "gemv_experts": x_row,
                 "attention": a_rows,
+                "prefill": pf_row,
                 "decode_qwen3_0.6b": d06}
         log(f"row legs {time.time() - t0:.1f}s")
     cpu = None

@@ -323,7 +323,10 @@ def test_tiny_prefill_vs_oracle(tiny, paged, kv_fp8):
     m.prefill(0, P, logits_last=lg)
     err = float(np.max(np.abs(host(lg) - ref)))
     say(f"tiny prefill logits max abs err {err:.3e}")
-    assert err <= 1e-4
+    # an fp8 cache turns f32-vs-f64 differences into whole e4m3 steps where a
+    # value sits near a rounding boundary, so it gets the bar of the fp8
+    # decode test
+    assert err <= (LOGITS_BAR if kv_fp8 else 1e-4)
     out = torch.full((G - 1,), -1, dtype=torch.int32, device="cuda")
     m.generate(P, G - 1, tokens=out)
     m.check()

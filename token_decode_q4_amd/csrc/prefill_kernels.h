@@ -6,6 +6,7 @@
 #pragma once
 
 #include "step_kernels.h"
+#include "prefill_gemm.h"
 
 namespace qd {
 
@@ -41,24 +42,6 @@ k_pf_rmsnorm(const float* __restrict__ X, const float* __restrict__ w, int H, fl
     const float r = 1.0f / sqrtf(ss / (float)H + eps);
     for (int i = threadIdx.x; i < H; i += blockDim.x)
         out[(size_t)blockIdx.x * H + i] = x[i] * r * w[i];
-}
-
-// X += Y over n elements
-__global__ void __launch_bounds__(256) k_pf_add(float* __restrict__ X, const float* __restrict__ Y, int n)
-{
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n)
-        X[i] += Y[i];
-}
-
-// A[t][i] = silu(G[t][2i]) * G[t][2i+1] (gate and up rows interleaved); n = T * I
-__global__ void __launch_bounds__(256) k_pf_swiglu(const float* __restrict__ G, float* __restrict__ A, int n)
-{
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) {
-        const float g = G[2 * (size_t)i], u = G[2 * (size_t)i + 1];
-        A[i] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;   // as the step's SwiGLU epilogue
-    }
 }
 
 // Per position t (grid.y) and head (grid.x: nq query heads, then nkv kv heads),

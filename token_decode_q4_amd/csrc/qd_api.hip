@@ -101,8 +101,8 @@ struct qd_model {
     float eps;
     // chunked prefill buffers (allocated by the first qd_prefill)
     struct {
-        float *X = nullptr, *Hn = nullptr, *QKV = nullptr, *Q = nullptr, *O = nullptr,
-              *Y = nullptr, *G = nullptr, *A = nullptr, *hf = nullptr;
+        float *X = nullptr, *QKV = nullptr, *Q = nullptr, *O = nullptr, *hf = nullptr;
+        _Float16 *XP1 = nullptr, *XP2 = nullptr;   // split activations (prefill_gemm.h)
         int32_t *lens = nullptr, *iota = nullptr;
         float* ws = nullptr;
         AttnGeom geo;
@@ -1243,37 +1243,23 @@ extern "C" int qd_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink,
 
 // ------------------------------------------------------------------ chunked prefill
 
-// y[t] = W x[t] for t < T through the batched GEMV (the single-vector kernel
-// for one; T single-vector launches where the vector kernel's staged batch
-// would not fit)
-static hipError_t pf_gemv(const DevQ4& W, const float* x, float* y, int T, hipStream_t s)
+// Y[t] = W x[t] for the chunk's positions on the matrix cores (k_pf_gemm):
+// two rows slices per workgroup for tall matrices, eight waves splitting K
+// where there are fewer than 512 row groups
+template <int MODE>
+static hipError_t pf_gemm(const DevQ4& W, const _Float16* XP, int T, float* Y, _Float16* XPo, hipStream_t s)
 {
-    const int N = W.rows, K = W.nb * 32;
-    if (T == 1 || (T < QD_BATCH_MFMA_MIN && (int64_t)T * K > GB_MAXKB)) {
-        for (int t = 0; t < T; ++t) {
-            const hipError_t e = launch_gemv_plain(W.d, W.qs, x + (size_t)t * K, y + (size_t)t * N, N, K, s);
-            if (e != hipSuccess)
-                return e;
-        }
-        return hipSuccess;
-    }
-    switch (T) {
-    case 2: return launch_gemv_batch<2>(W.d, W.qs, x, y, N, K, s);
-    case 3: return launch_gemv_batch<3>(W.d, W.qs, x, y, N, K, s);
-    case 4: return launch_gemv_batch<4>(W.d, W.qs, x, y, N, K, s);
-    case 5: return launch_gemv_batch<5>(W.d, W.qs, x, y, N, K, s);
-    case 6: return launch_gemv_batch<6>(W.d, W.qs, x, y, N, K, s);
-    case 7: return launch_gemv_batch<7>(W.d, W.qs, x, y, N, K, s);
-    case 8: return launch_gemv_batch<8>(W.d, W.qs, x, y, N, K, s);
-    case 9: return launch_gemv_batch<9>(W.d, W.qs, x, y, N, K, s);
-    case 10: return launch_gemv_batch<10>(W.d, W.qs, x, y, N, K, s);
-    case 11: return launch_gemv_batch<11>(W.d, W.qs, x, y, N, K, s);
-    case 12: return launch_gemv_batch<12>(W.d, W.qs, x, y, N, K, s);
-    case 13: return launch_gemv_batch<13>(W.d, W.qs, x, y, N, K, s);
-    case 14: return launch_gemv_batch<14>(W.d, W.qs, x, y, N, K, s);
-    case 15: return launch_gemv_batch<15>(W.d, W.qs, x, y, N, K, s);
-    default: return launch_gemv_batch<16>(W.d, W.qs, x, y, N, K, s);
-    }
+    const int N = W.rows, nb = W.nb, g1 = (N + 15) / 16;
+    if (g1 >= 1024)
+        hipLaunchKernelGGL((k_pf_gemm<2, 4, MODE>), dim3((N + 31) / 32), dim3(4 * WAVE), 0, s, W.d, W.qs, XP, N,
+                           nb, T, Y, XPo);
+    else if (g1 >= 512)
+        hipLaunchKernelGGL((k_pf_gemm<1, 4, MODE>), dim3(g1), dim3(4 * WAVE), 0, s, W.d, W.qs, XP, N, nb, T, Y,
+                           XPo);
+    else
+        hipLaunchKernelGGL((k_pf_gemm<1, 8, MODE>), dim3(g1), dim3(8 * WAVE), 0, s, W.d, W.qs, XP, N, nb, T, Y,
+                           XPo);
+    return hipGetLastError();
 }
 
 static int pf_setup(qd_model* m)
@@ -1284,14 +1270,18 @@ static int pf_setup(qd_model* m)
     const size_t T = PF_T, nqd = (size_t)m->nq * m->hd;
     const size_t ws = attn_ws_layout(PF_T, m->nq, m->nkv, m->hd, m->max_seq, &P.geo);
     int rc;
-    if ((rc = dev_alloc_t(m, &P.X, T * m->H)) || (rc = dev_alloc_t(m, &P.Hn, T * m->H)) ||
-        (rc = dev_alloc_t(m, &P.QKV, T * m->qkv_rows)) || (rc = dev_alloc_t(m, &P.Q, T * nqd)) ||
-        (rc = dev_alloc_t(m, &P.O, T * nqd)) || (rc = dev_alloc_t(m, &P.Y, T * m->H)) ||
-        (rc = dev_alloc_t(m, &P.G, T * 2 * (size_t)m->I)) || (rc = dev_alloc_t(m, &P.A, T * m->I)) ||
+    const size_t kx = std::max((size_t)m->H, nqd);
+    if ((rc = dev_alloc_t(m, &P.X, T * m->H)) || (rc = dev_alloc_t(m, &P.QKV, T * m->qkv_rows)) ||
+        (rc = dev_alloc_t(m, &P.Q, T * nqd)) || (rc = dev_alloc_t(m, &P.O, T * nqd)) ||
+        (rc = dev_alloc_t(m, &P.XP1, T * kx * 2)) || (rc = dev_alloc_t(m, &P.XP2, T * (size_t)m->I * 2)) ||
         (rc = dev_alloc_t(m, &P.hf, (size_t)m->H)) || (rc = dev_alloc_t(m, &P.lens, T)) ||
         (rc = dev_alloc_t(m, &P.iota, (size_t)m->V)) || (rc = dev_alloc_t(m, &P.ws, ws / sizeof(float) + 1)))
         return rc;
     hipLaunchKernelGGL(k_pf_iota, dim3((m->V + 255) / 256), dim3(256), 0, 0, P.iota, m->V);
+    // positions past a short chunk read these rows: keep them finite
+    if (hipMemset(P.XP1, 0, T * kx * 2 * sizeof(_Float16)) != hipSuccess ||
+        hipMemset(P.XP2, 0, T * (size_t)m->I * 2 * sizeof(_Float16)) != hipSuccess)
+        return fail(QD_EHIP, "prefill buffer set-up failed");
     if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess)
         return fail(QD_EHIP, "prefill buffer set-up failed");
     P.ready = true;
@@ -1319,8 +1309,8 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
                            H, m->ids, p0, P.X);
         for (int l = 0; l < m->L; ++l) {
             DevLayer& Ly = m->layers[l];
-            hipLaunchKernelGGL(k_pf_rmsnorm, dim3(T), dim3(256), 0, s, P.X, Ly.attn_norm, H, m->eps, P.Hn);
-            HIP_TRY(pf_gemv(Ly.qkv, P.Hn, P.QKV, T, s));
+            hipLaunchKernelGGL(k_pf_rmsnorm_xp, dim3(T), dim3(1024), 0, s, P.X, Ly.attn_norm, H, m->eps, P.XP1);
+            HIP_TRY(pf_gemm<PG_STORE>(Ly.qkv, P.XP1, T, P.QKV, nullptr, s));
             const float* qn = m->qk_norm ? Ly.q_norm : m->ones_hd;
             const float* kn = m->qk_norm ? Ly.k_norm : m->ones_hd;
             const int32_t* tbl = m->paged ? m->table : nullptr;
@@ -1358,14 +1348,12 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
                 launch_attention<0, true>(p, P.geo.waves, hd, gq, m->paged, T, m->nq, s);
             else
                 launch_attention<0>(p, P.geo.waves, hd, gq, m->paged, T, m->nq, s);
-            HIP_TRY(pf_gemv(Ly.o, P.O, P.Y, T, s));
-            hipLaunchKernelGGL(k_pf_add, dim3((T * H + 255) / 256), dim3(256), 0, s, P.X, P.Y, T * H);
-            hipLaunchKernelGGL(k_pf_rmsnorm, dim3(T), dim3(256), 0, s, P.X, Ly.ffn_norm, H, m->eps, P.Hn);
-            HIP_TRY(pf_gemv(Ly.gu, P.Hn, P.G, T, s));
-            hipLaunchKernelGGL(k_pf_swiglu, dim3((T * m->I + 255) / 256), dim3(256), 0, s, P.G, P.A,
-                               T * m->I);
-            HIP_TRY(pf_gemv(Ly.down, P.A, P.Y, T, s));
-            hipLaunchKernelGGL(k_pf_add, dim3((T * H + 255) / 256), dim3(256), 0, s, P.X, P.Y, T * H);
+            const int kq = m->nq * hd;
+            hipLaunchKernelGGL(k_pf_xsplit, dim3((kq + 255) / 256, T), dim3(256), 0, s, P.O, kq, P.XP1);
+            HIP_TRY(pf_gemm<PG_RESID>(Ly.o, P.XP1, T, P.X, nullptr, s));
+            hipLaunchKernelGGL(k_pf_rmsnorm_xp, dim3(T), dim3(1024), 0, s, P.X, Ly.ffn_norm, H, m->eps, P.XP1);
+            HIP_TRY(pf_gemm<PG_SWIGLU>(Ly.gu, P.XP1, T, nullptr, P.XP2, s));
+            HIP_TRY(pf_gemm<PG_RESID>(Ly.down, P.XP2, T, P.X, nullptr, s));
         }
     }
     // the last position: final norm, LM head, greedy token as a decode step records it
