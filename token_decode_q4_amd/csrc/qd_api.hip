@@ -1243,19 +1243,26 @@ extern "C" int qd_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink,
 
 // ------------------------------------------------------------------ chunked prefill
 
-// Y[t] = W x[t] for the chunk's positions on the matrix cores (k_pf_gemm):
-// two rows slices per workgroup for tall matrices, eight waves splitting K
-// where there are fewer than 512 row groups
+// Y[t] = W x[t] for the chunk's positions on the matrix cores (k_pf_gemm).
+// Launch shapes measured at the Qwen3-8B matrices (16 positions): 4 waves of
+// 2 row slices for the tall gate|up (24576 rows), 8 waves of 2 slices for
+// q|k|v (6144 rows), 8 waves of 1 slice below 6144 rows.
 template <int MODE>
 static hipError_t pf_gemm(const DevQ4& W, const _Float16* XP, int T, float* Y, _Float16* XPo, hipStream_t s)
 {
     const int N = W.rows, nb = W.nb, g1 = (N + 15) / 16;
+#ifdef QD_PG_FORCE   // compile-time override: rows slices per wave, waves per workgroup
+    constexpr int FR[2] = {QD_PG_FORCE};
+    hipLaunchKernelGGL((k_pf_gemm<FR[0], FR[1], MODE>), dim3((N + 16 * FR[0] - 1) / (16 * FR[0])),
+                       dim3(FR[1] * WAVE), 0, s, W.d, W.qs, XP, N, nb, T, Y, XPo);
+    return hipGetLastError();
+#endif
     if (g1 >= 1024)
         hipLaunchKernelGGL((k_pf_gemm<2, 4, MODE>), dim3((N + 31) / 32), dim3(4 * WAVE), 0, s, W.d, W.qs, XP, N,
                            nb, T, Y, XPo);
-    else if (g1 >= 512)
-        hipLaunchKernelGGL((k_pf_gemm<1, 4, MODE>), dim3(g1), dim3(4 * WAVE), 0, s, W.d, W.qs, XP, N, nb, T, Y,
-                           XPo);
+    else if (g1 >= 384)
+        hipLaunchKernelGGL((k_pf_gemm<2, 8, MODE>), dim3((N + 31) / 32), dim3(8 * WAVE), 0, s, W.d, W.qs, XP, N,
+                           nb, T, Y, XPo);
     else
         hipLaunchKernelGGL((k_pf_gemm<1, 8, MODE>), dim3(g1), dim3(8 * WAVE), 0, s, W.d, W.qs, XP, N, nb, T, Y,
                            XPo);
