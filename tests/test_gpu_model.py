@@ -195,6 +195,13 @@ def test_qwen3_8b_shape_prefill_vs_golden():
     assert worst <= 5e-3
 
 
+def test_qwen3_8b_shape_layer_kernel_prefill_vs_golden():
+    """qd_prefill into a model that decodes with the persistent layer kernel:
+    both read and write the same paged cache."""
+    n_eq, worst = _golden_run("qwen3-8b", layer_kernel=True, prefill=True)
+    assert worst <= 5e-3
+
+
 def test_qwen3_8b_shape_vs_golden():
     n_eq, worst = _golden_run("qwen3-8b")
     # regression guard well inside the 2e-2 bar: 36 layers, rows of 12288 and
