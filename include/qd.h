@@ -180,8 +180,9 @@ int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* d_tokens,
  * activations plus an attention workspace) are allocated by the first call,
  * which synchronises; later calls allocate nothing.  The weight scales must
  * satisfy |d| < 8192 (the matrix-core GEMV, as qd_gemv_q4_0_batch).
- * QD_ERANGE unless 0 <= pos0, n >= 1 and pos0 + n <= max_seq;
- * QD_EUNSUPPORTED for a model with attn_out_gate. */
+ * A model with attn_out_gate gates each position's attention output as the
+ * decode step does.  QD_ERANGE unless 0 <= pos0, n >= 1 and
+ * pos0 + n <= max_seq. */
 int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_last, qd_stream stream);
 
 /* Standalone q4_0 GEMV (inferencelayer cuda_llm.rs page, CudaQwen3::gemv):

@@ -384,9 +384,32 @@ def test_tiny_prefill_rejects(tiny):
             m.prefill(pos0, n)
         assert ei.value.code == qd._native.QD_ERANGE
     m.close()
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_tiny_gated_prefill_vs_oracle(paged):
+    """qd_prefill of a model with the attention output gate: logits at the
+    last prompt position against the oracle, then greedy generation."""
+    import torch
+    import token_decode_q4_amd as qd
     mi = synth.make_model("tiny", attn_out_gate=True)
-    mg = qd.Model(mi)
-    with pytest.raises(qd.QdError) as ei:
-        mg.prefill(0, 4)
-    assert ei.value.code == qd._native.QD_EUNSUPPORTED
-    mg.close()
+    s = mi.shape
+    P, G = s.prompt_len, s.gen
+    say(f"tiny gated prefill paged={paged}")
+    toks, margins, _ = oracle.generate(oracle.Model(mi), mi.prompt, G)
+    om = oracle.Model(mi)
+    for p, t in enumerate(mi.prompt):
+        ref = om.step(int(t), p)
+    m = qd.Model(mi, use_graph=True, paged=paged)
+    m.set_prompt(mi.prompt)
+    lg = torch.empty(s.vocab, dtype=torch.float32, device="cuda")
+    m.prefill(0, P, logits_last=lg)
+    err = float(np.max(np.abs(host(lg) - ref)))
+    say(f"tiny gated prefill logits max abs err {err:.3e}")
+    assert err <= 1e-4
+    out = torch.full((G - 1,), -1, dtype=torch.int32, device="cuda")
+    m.generate(P, G - 1, tokens=out)
+    m.check()
+    m.close()
+    got = np.concatenate([[int(np.argmax(host(lg)))], host(out)])
+    check_greedy(got, toks, margins, "tiny gated prefill")

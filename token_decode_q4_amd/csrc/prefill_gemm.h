@@ -212,13 +212,20 @@ k_pf_gemm(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q, const _
     }
 }
 
-// X [T][K] f32 -> XP (split, A-operand order); grid (ceil(K/256), T)
+// X [T][K] f32 -> XP (split, A-operand order); grid (ceil(K/256), T).  With
+// a gate (row t at gate + t * gstride), x is multiplied by sigmoid(gate)
+// first, as the decode step gates the merged attention output.
 __global__ void __launch_bounds__(256)
-k_pf_xsplit(const float* __restrict__ X, int K, _Float16* __restrict__ XP)
+k_pf_xsplit(const float* __restrict__ X, int K, const float* __restrict__ gate, int gstride,
+            _Float16* __restrict__ XP)
 {
     const int t = blockIdx.y, k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k < K)
-        xp_store(XP, t, k, K >> 5, X[(size_t)t * K + k]);
+    if (k < K) {
+        float x = X[(size_t)t * K + k];
+        if (gate)   // uniform
+            x *= 1.0f / (1.0f + expf(-gate[(size_t)t * gstride + k]));
+        xp_store(XP, t, k, K >> 5, x);
+    }
 }
 
 // RMSNorm of X[t] (weight w) written split into XP; grid T, 1024 threads,

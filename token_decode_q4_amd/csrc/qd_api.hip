@@ -1301,8 +1301,6 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
         return fail(QD_EINVAL, "null model");
     if (n <= 0 || pos0 < 0 || (int64_t)pos0 + n > m->max_seq)
         return fail(QD_ERANGE, "positions [%d, %d) not in [0, %d)", pos0, pos0 + n, m->max_seq);
-    if (m->attn_gate)
-        return fail(QD_EUNSUPPORTED, "qd_prefill with attn_out_gate");
     QD_TRY(pf_setup(m));
     auto& P = m->pf;
     const hipStream_t s = (hipStream_t)stream;
@@ -1356,7 +1354,10 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
             else
                 launch_attention<0>(p, P.geo.waves, hd, gq, m->paged, T, m->nq, s);
             const int kq = m->nq * hd;
-            hipLaunchKernelGGL(k_pf_xsplit, dim3((kq + 255) / 256, T), dim3(256), 0, s, P.O, kq, P.XP1);
+            // the gate rows follow q|k|v in the fused product
+            const float* gate = m->attn_gate ? P.QKV + (size_t)(m->nq + 2 * m->nkv) * hd : nullptr;
+            hipLaunchKernelGGL(k_pf_xsplit, dim3((kq + 255) / 256, T), dim3(256), 0, s, P.O, kq, gate,
+                               m->qkv_rows, P.XP1);
             HIP_TRY(pf_gemm<PG_RESID>(Ly.o, P.XP1, T, P.X, nullptr, s));
             hipLaunchKernelGGL(k_pf_rmsnorm_xp, dim3(T), dim3(1024), 0, s, P.X, Ly.ffn_norm, H, m->eps, P.XP1);
             HIP_TRY(pf_gemm<PG_SWIGLU>(Ly.gu, P.XP1, T, nullptr, P.XP2, s));
