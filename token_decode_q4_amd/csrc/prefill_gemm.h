@@ -115,7 +115,12 @@ k_pf_gemm(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q, const _
         const int bq = min(b0 + g, nb - 1);
 #pragma unroll
         for (int s = 0; s < R; ++s) {
-            L.q[s] = *reinterpret_cast<const uint4*>(Q + ((size_t)rbase[s] + bq) * 16);
+            // weights stream through once per chunk: non-temporal, so that
+            // they do not push the chunk's activations out of L2
+            typedef unsigned int pg_u32x4 __attribute__((ext_vector_type(4)));
+            const pg_u32x4 qv =
+                __builtin_nontemporal_load(reinterpret_cast<const pg_u32x4*>(Q + ((size_t)rbase[s] + bq) * 16));
+            L.q[s] = make_uint4(qv.x, qv.y, qv.z, qv.w);
             L.d[s] = D[rbase[s] + bq];
         }
 #pragma unroll
