@@ -20,7 +20,9 @@ k_pf_embed(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, int 
     const int t = blockIdx.y, i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= H)
         return;
-    const int tok = ids[p0 + t];   // validated by the host when stored
+    // every stored token is in range: the buffer starts zeroed, host tokens
+    // are checked when stored, and the greedy step stores a clamped argmax
+    const int tok = ids[p0 + t];
     const int nb = H / 32, bk = i >> 5, j = i & 31;
     const size_t blk = (size_t)tok * nb + bk;
     const uint8_t byte = Eq[blk * 16 + (j & 15)];
