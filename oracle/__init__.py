@@ -69,6 +69,9 @@ def lib():
         L.or_model_kv.restype = C.c_int
         L.or_model_kv.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                   C.c_void_p]
+        L.or_model_load_kv.restype = C.c_int
+        L.or_model_load_kv.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                       C.c_void_p]
         L.or_model_destroy.argtypes = [C.c_void_p]
         _lib = L
     return _lib
@@ -303,6 +306,16 @@ class Model:
         if lib().or_model_kv(self._h, layer, pos, kv_head, int(which_v), _p(out)) != 0:
             raise ValueError("bad kv index")
         return out
+
+    def load_kv(self, layer: int, pos0: int, k, v):
+        """Store k, v [n, n_kv*head_dim] as the K/V of one layer at positions
+        pos0 .. pos0+n-1 (no arithmetic; for timing steps at a long context)."""
+        kk = np.ascontiguousarray(k, dtype=np.float64)
+        vv = np.ascontiguousarray(v, dtype=np.float64)
+        s = self.mi.shape
+        assert kk.shape == vv.shape and kk.ndim == 2 and kk.shape[1] == s.n_kv * s.head_dim
+        if lib().or_model_load_kv(self._h, int(layer), int(pos0), kk.shape[0], _p(kk), _p(vv)) != 0:
+            raise ValueError("bad kv range")
 
     def close(self):
         if getattr(self, "_h", None):

@@ -469,3 +469,16 @@ int or_model_kv(const or_model* m, int32_t layer, int32_t pos, int32_t kv_head, 
            sizeof(double) * (size_t)c->head_dim);
     return 0;
 }
+
+int or_model_load_kv(or_model* m, int32_t layer, int32_t pos0, int32_t n, const double* k,
+                     const double* v)
+{
+    const or_config* c = &m->cfg;
+    if (layer < 0 || layer >= c->layers || pos0 < 0 || n < 0 || (int64_t)pos0 + n > c->max_seq)
+        return -1;
+    int64_t kvd = (int64_t)c->n_kv * c->head_dim;
+    int64_t off = ((int64_t)layer * c->max_seq + pos0) * kvd;
+    memcpy(m->kc + off, k, sizeof(double) * (size_t)(n * kvd));
+    memcpy(m->vc + off, v, sizeof(double) * (size_t)(n * kvd));
+    return 0;
+}

@@ -96,6 +96,11 @@ int or_model_step(or_model* m, int32_t token, int32_t pos, double* logits);
 /* The K or V the model stored for (layer, pos, kv head), as f64 [hd]. */
 int or_model_kv(const or_model* m, int32_t layer, int32_t pos, int32_t kv_head, int32_t which_v,
                 double* out);
+/* Overwrite the stored K and V of one layer at positions pos0 .. pos0+n-1
+ * with k, v [n][n_kv*head_dim] (stored as given; no arithmetic).  For timing
+ * steps at a long context without running the steps before it.  0 or -1. */
+int or_model_load_kv(or_model* m, int32_t layer, int32_t pos0, int32_t n, const double* k,
+                     const double* v);
 void or_model_destroy(or_model* m);
 
 #ifdef __cplusplus

@@ -68,6 +68,14 @@ MODELS = {
     # vocab 1024, tied, contiguous KV; 16 prompt tokens + 32 greedy tokens
     "tiny": ModelShape("tiny", 1, 2, 256, 4, 2, 64, 768, 1024, True, True, 1e6, 64, 1e-6,
                        False, 48, 16, 32),
+    # the tiny decoder with an LM head of its own (drawn from its own tensor
+    # id; every other tensor equals the tiny one's)
+    "tiny-untied": ModelShape("tiny-untied", 1, 2, 256, 4, 2, 64, 768, 1024, False, True, 1e6,
+                              64, 1e-6, False, 48, 16, 32),
+    # the tiny decoder with partial rotary: the first 32 of 64 dims of each
+    # q/k head turn (inv_freq = 1e6^(-2i/32), 16 frequencies), the rest pass
+    "tiny-rot32": ModelShape("tiny-rot32", 1, 2, 256, 4, 2, 64, 768, 1024, True, True, 1e6,
+                             32, 1e-6, False, 48, 16, 32),
     # Qwen3-0.6B shape, contiguous KV; 512 prompt tokens + 256 greedy tokens
     "qwen3-0.6b": ModelShape("qwen3-0.6b", 4, 28, 1024, 16, 8, 128, 3072, 151936, True,
                              True, 1e6, 128, 1e-6, False, 768, 512, 256),

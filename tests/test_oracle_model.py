@@ -240,3 +240,116 @@ def test_attn_gate_zero_is_half(oracle_lib):
     mh = oracle_lib.Model(dataclasses.replace(mi, layers=layers_h))
     for p, t in enumerate(mi.prompt[:8]):
         assert np.array_equal(mg.step(int(t), p), mh.step(int(t), p))
+
+
+# ----------------------------------------------------------------- untied head, partial rotary
+# The whole step as a separate numpy f64 program: full-sequence causal
+# forward with no cache, written from the definition (inferencelayer
+# cuda_llm.rs page, CudaQwen3::step and Cfg: rot_dim, tied embeddings;
+# memra-engine qwen4exp_gpu.rs page, its host rotary twin: pairs (i, i + rot/2)
+# over the first rot dims with theta^(-2i/rot), the other dims unchanged).
+# It shares nothing with qd_oracle.c: its own q4_0 decode, norms, rotary,
+# attention and MLP.
+
+def _np_dequant(W) -> np.ndarray:
+    d = np.asarray(W.d, dtype=np.uint16).view(np.float16).astype(np.float64)
+    qs = np.asarray(W.qs, dtype=np.uint8)
+    codes = np.concatenate([qs & 15, qs >> 4], axis=2).astype(np.float64)   # elements 0..15, 16..31
+    return ((codes - 8.0) * d[:, :, None]).reshape(d.shape[0], d.shape[1] * 32)
+
+
+def _np_forward(mi) -> np.ndarray:
+    """Logits of every prompt position, f64, no K/V rounding."""
+    s = mi.shape
+    H, hd, nq, nkv = s.hidden, s.head_dim, s.n_heads, s.n_kv
+    rot, half = s.rot_dim, s.rot_dim // 2
+    P = len(mi.prompt)
+
+    def rms(v, w):
+        return v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + s.eps) * np.asarray(w, np.float64)
+
+    pos = np.arange(P, dtype=np.float64)[:, None]
+    ang = pos * np.asarray(mi.inv_freq[:half], dtype=np.float32).astype(np.float64)[None, :]
+    cos, sin = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]   # [P, 1, half]
+
+    def rotary(t):   # t [P, heads, hd]
+        out = t.copy()
+        a, b = t[..., :half], t[..., half:rot]
+        out[..., :half] = a * cos - b * sin
+        out[..., half:rot] = a * sin + b * cos
+        return out
+
+    x = _np_dequant(mi.embed)[np.asarray(mi.prompt)]
+    mask = np.tril(np.ones((P, P), dtype=bool))
+    for L in mi.layers:
+        h = rms(x, L.attn_norm)
+        q = (h @ _np_dequant(L.wq).T).reshape(P, nq, hd)
+        k = (h @ _np_dequant(L.wk).T).reshape(P, nkv, hd)
+        v = (h @ _np_dequant(L.wv).T).reshape(P, nkv, hd)
+        if s.qk_norm:
+            q, k = rms(q, L.q_norm), rms(k, L.k_norm)
+        q, k = rotary(q), rotary(k)
+        att = np.empty((P, nq, hd))
+        for hh in range(nq):
+            g = hh // (nq // nkv)
+            sc = (q[:, hh] @ k[:, g].T) / np.sqrt(hd)
+            sc = np.where(mask, sc, -np.inf)
+            p = np.exp(sc - sc.max(axis=1, keepdims=True))
+            att[:, hh] = (p / p.sum(axis=1, keepdims=True)) @ v[:, g]
+        x = x + att.reshape(P, nq * hd) @ _np_dequant(L.wo).T
+        h2 = rms(x, L.ffn_norm)
+        gt, up = h2 @ _np_dequant(L.wgate).T, h2 @ _np_dequant(L.wup).T
+        x = x + (gt / (1.0 + np.exp(-gt)) * up) @ _np_dequant(L.wdown).T
+    head = mi.embed if s.tied else mi.lm_head
+    return rms(x, mi.final_norm) @ _np_dequant(head).T
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny-untied", "tiny-rot32"])
+def test_sequential_decode_equals_numpy_causal_forward(oracle_lib, name):
+    """The oracle's sequential decode (K/V kept in f64) against the numpy
+    full-sequence forward, for the tiny decoder, its untied-head variant and
+    its partial-rotary (rot_dim 32 of head_dim 64) variant."""
+    mi = synth.make_model(name)
+    om = oracle_lib.Model(mi, kv_round=False)
+    ours = np.stack([om.step(int(t), p) for p, t in enumerate(mi.prompt)])
+    ref = _np_forward(mi)
+    scale = np.abs(ref).max()
+    assert np.max(np.abs(ours - ref)) <= 1e-11 * scale
+
+
+def test_untied_head_equals_transformers(oracle_lib):
+    """The untied-head tiny decoder against the installed transformers Qwen3
+    (tie_word_embeddings=False, its own lm_head weights), in f64."""
+    mi = synth.make_model("tiny-untied")
+    assert not mi.shape.tied and mi.lm_head is not mi.embed
+    om = oracle_lib.Model(mi, kv_round=False)
+    ours = np.stack([om.step(int(t), p) for p, t in enumerate(mi.prompt)])
+    with _hf_in_f64():
+        ref = _hf_logits(mi, oracle_lib, attn="sdpa")
+    assert np.max(np.abs(ours - ref)) <= 1e-12 * np.abs(ref).max()
+    # the head matters: the tied model's logits are far from these
+    tied = synth.make_model("tiny")
+    ot = oracle_lib.Model(tied, kv_round=False)
+    lt = np.stack([ot.step(int(t), p) for p, t in enumerate(tied.prompt)])
+    assert np.max(np.abs(lt - ours)) > 0.1 * np.abs(ref).max()
+
+
+def test_partial_rotary_leaves_tail_dims(oracle_lib):
+    """With rot_dim 32 of 64 the rotary changes the logits (the variant differs
+    from the full-rotary model with the same weights), yet a model whose
+    frequencies are all zero equals one with rot_dim 0 (nothing turns)."""
+    import dataclasses
+    mi = synth.make_model("tiny-rot32")
+    full = synth.make_model("tiny")
+    a = oracle_lib.Model(mi, kv_round=False)
+    b = oracle_lib.Model(full, kv_round=False)
+    la = np.stack([a.step(int(t), p) for p, t in enumerate(mi.prompt[:6])])
+    lb = np.stack([b.step(int(t), p) for p, t in enumerate(full.prompt[:6])])
+    assert np.array_equal(la[0], lb[0])            # position 0: no rotation anywhere
+    assert np.max(np.abs(la[1:] - lb[1:])) > 1e-3  # later positions: the widths differ
+    z = dataclasses.replace(mi, inv_freq=np.zeros_like(mi.inv_freq))
+    z0 = dataclasses.replace(mi, shape=dataclasses.replace(mi.shape, rot_dim=0),
+                             inv_freq=np.zeros(0, np.float32))
+    oz, o0 = oracle_lib.Model(z, kv_round=False), oracle_lib.Model(z0, kv_round=False)
+    for p, t in enumerate(mi.prompt[:6]):
+        assert np.array_equal(oz.step(int(t), p), o0.step(int(t), p))

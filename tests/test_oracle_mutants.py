@@ -50,6 +50,12 @@ MUTANTS = {
                           "return or_e4m3_to_f64(or_f64_to_e4m3(val));"),
     "out_gate_sign": ("m->att[i] *= 1.0 / (1.0 + exp(-m->o[i]));", "m->att[i] *= 1.0 / (1.0 + exp(m->o[i]));"),
     "out_gate_input": ("or_gemv_q4_0(&L->wag, m->h, m->o, nt);", "or_gemv_q4_0(&L->wag, m->x, m->o, nt);"),
+    "lm_head_is_embed": ("or_gemv_q4_0(&m->lm_head, m->h, logits, nt);",
+                         "or_gemv_q4_0(&m->embed, m->h, logits, nt);"),
+    "model_rope_q_full_width": ("or_rope_neox(m->q + hh * hd, (int32_t)hd, c->rot_dim, c->inv_freq, pos);",
+                                "or_rope_neox(m->q + hh * hd, (int32_t)hd, (int32_t)hd, c->inv_freq, pos);"),
+    "model_rope_k_half_width": ("or_rope_neox(m->k + gg * hd, (int32_t)hd, c->rot_dim, c->inv_freq, pos);",
+                                "or_rope_neox(m->k + gg * hd, (int32_t)hd, c->rot_dim / 2, c->inv_freq, pos);"),
     "model_rope_pos": ("or_rope_neox(m->q + hh * hd, (int32_t)hd, c->rot_dim, c->inv_freq, pos);",
                        "or_rope_neox(m->q + hh * hd, (int32_t)hd, c->rot_dim, c->inv_freq, pos + 1);"),
 }

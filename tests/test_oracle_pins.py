@@ -248,6 +248,32 @@ def test_attention_special_cases(oracle_lib):
     assert np.all(o == 0)
 
 
+def test_attention_softmax_rows_sum_to_one(oracle_lib):
+    """With V[t] = e_t (one-hot, kv_len <= head_dim) the output of head h is its
+    softmax row over the keys: non-negative, summing to 1 (within f64 rounding),
+    equal to exp(s - max) / sum exp(s - max) of the scores, also for scores near
+    +-1e3; with V = all ones every output element is that sum."""
+    rng = np.random.default_rng(17)
+    hd, nq, nkv, n = 64, 4, 2, 40
+    for amp in (1.0, 1e3):
+        q = (rng.standard_normal((1, nq, hd)) * amp).astype(np.float32)
+        k = _f16(rng.standard_normal((1, nkv, n, hd)))
+        eye = np.zeros((1, nkv, n, hd))
+        eye[0, :, np.arange(n), np.arange(n)] = 1.0
+        o = oracle_lib.attn_decode(q, k, _f16(eye), [n], nkv, 0.125, contig_max_kv=n)[0]
+        p = o[:, :n]
+        assert np.all(o[:, n:] == 0) and np.all(p >= 0)
+        assert np.allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+        kf = k.view(np.float16).astype(np.float64)[0]
+        for h in range(nq):
+            sc = 0.125 * kf[h // (nq // nkv)] @ q[0, h].astype(np.float64)
+            e = np.exp(sc - sc.max())
+            assert np.allclose(p[h], e / e.sum(), rtol=1e-12, atol=1e-300)
+        ones = oracle_lib.attn_decode(q, k, _f16(np.ones((1, nkv, n, hd))), [n], nkv, 0.125,
+                                      contig_max_kv=n)[0]
+        assert np.allclose(ones, 1.0, rtol=0, atol=1e-14)
+
+
 def test_attention_gqa_equals_repeated_mha(oracle_lib):
     a = synth.random_attn(22, 1, [70], nq=8, nkv=2, hd=64, shuffle=False)
     scale = 0.125
