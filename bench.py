@@ -20,7 +20,8 @@ Also reported, on the same JSON line:
                 sources still match it, else null.
   step_roofline the whole step's algorithmic bytes / measured step time.
   cpu_baseline  the f64 CPU oracle running decode steps of the same model on
-                the host cores (a bounded sample from position 0).
+                the host cores, a bounded sample at the first positions the
+                GPU timed (same kv_len; the CPU model and thread count named).
 
   rows          per-row measurements: the isolated GEMV at the five sweep
                 shapes, the batched and the expert GEMV, and the isolated
@@ -454,23 +455,48 @@ def read_ceiling(nbytes: int, reps: int = 100, min_bytes: int = 1 << 30):
             "unit": "GB/s"}
 
 
-def cpu_baseline(mi, seconds: float = 15.0):
-    """The oracle as it stands, decode steps of the same model from position 0."""
+def cpu_model_name() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(mi, pos0: int, tokens, seconds: float = 15.0):
+    """The oracle as it stands, decode steps of the same model at the positions
+    the GPU timed: positions pos0, pos0+1, ... fed `tokens` (the GPU's greedy
+    tokens there), for about `seconds`.  The K/V of positions 0..pos0-1 are
+    loaded with seeded f16 values instead of running those steps (the oracle
+    needs minutes per hundred steps at this shape), so every timed step
+    attends over the same kv_len as the GPU step at that position."""
     import oracle
+    s = mi.shape
     threads = oracle.default_threads()
     om = oracle.Model(mi, nthreads=threads)
+    kvd = s.n_kv * s.head_dim
+    fill = np.random.default_rng(12345).standard_normal((pos0, kvd)).astype(np.float16).astype(np.float64)
+    for layer in range(s.layers):
+        om.load_kv(layer, 0, fill, fill)
     t0 = time.time()
     n = 0
     while True:
-        om.step(int(mi.prompt[n]), n)
+        om.step(int(tokens[n]), pos0 + n)
         n += 1
-        if time.time() - t0 >= seconds or n >= len(mi.prompt):
+        if time.time() - t0 >= seconds or n >= len(tokens):
             break
     el = time.time() - t0
     om.close()
     return {"value": round(n / el, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} f64 oracle decode steps of the Qwen3-8B-shape model at positions "
-                      f"0..{n - 1} (prompt tokens), {el:.1f} s"}
+            "cpu": cpu_model_name(),
+            "sample": f"{n} f64 oracle decode steps of the {s.name}-shape model at positions "
+                      f"{pos0}..{pos0 + n - 1} (the first positions of the timed GPU steps, "
+                      f"kv_len {pos0 + 1}..{pos0 + n}; K/V of positions 0..{pos0 - 1} loaded with "
+                      f"seeded f16 values), {el:.1f} s on {threads} threads"}
 
 
 def prefill_row(model, s, n: int, reps: int = 3):
@@ -574,6 +600,8 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
     tok_s = args.steps / (ms * 1e-3)
+    t_pos0 = pos
+    toks_host = toks[pos - 1:pos - 1 + args.steps].cpu().numpy()   # the token fed at each position
     kv_lens = np.arange(pos + 1, pos + args.steps + 1)
     mean_bytes = float(np.mean([step_bytes(s, int(k), 1 if args.kv_fp8 else 2) for k in kv_lens]))
     step_gbs = mean_bytes / (ms * 1e-3 / args.steps) / 1e9
@@ -628,7 +656,7 @@ def main():
         log(f"row legs {time.time() - t0:.1f}s")
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(mi)
+        cpu = cpu_baseline(mi, t_pos0, toks_host)
         log(f"cpu baseline: {cpu['value']} tok/s on {cpu['cores']} threads")
 
     out = {

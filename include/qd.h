@@ -144,9 +144,13 @@ int qd_destroy(qd_model* m);
 /* One decode step (inferencelayer cuda_llm.rs page, CudaQwen3::step): embed
  * `token` at position `pos`, write its K/V at `pos`, attend over positions
  * 0..pos, produce f32 logits [vocab].  Positions 0..pos-1 must have been
- * written by earlier steps (prefill is sequential decode).  d_logits (device
- * f32 [vocab]) and d_next (device int32, greedy argmax, lowest index on ties)
- * may each be NULL.  Asynchronous on `stream`. */
+ * written by earlier steps (prefill is sequential decode): the library keeps
+ * the written prefix on the host (none after qd_create; a step at p makes
+ * it 0..p, so a step may also go back and rewrite) and refuses a pos more
+ * than one past it with QD_ERANGE, as for a token outside [0, vocab) or a pos
+ * outside [0, max_seq).  d_logits (device f32 [vocab]) and d_next (device
+ * int32, greedy argmax, lowest index on ties) may each be NULL.  Asynchronous
+ * on `stream`. */
 int qd_decode_step(qd_model* m, int32_t token, int32_t pos, float* d_logits, int32_t* d_next,
                    qd_stream stream);
 
@@ -161,7 +165,9 @@ int qd_decode_step(qd_model* m, int32_t token, int32_t pos, float* d_logits, int
  * (device f32 [vocab] or NULL) the logits of the last step.  Prompt prefill
  * plus G greedy tokens is qd_set_prompt(prompt, P) then
  * qd_generate(0, P+G-1, ...): entries P-1 .. P+G-2 of d_tokens are the
- * greedy tokens.  Requires pos0 + n_steps <= max_seq. */
+ * greedy tokens.  Requires pos0 + n_steps <= max_seq and, for n_steps > 0,
+ * pos0 at most one past the written prefix (QD_ERANGE otherwise); afterwards
+ * the prefix is 0 .. pos0+n_steps-1. */
 int qd_set_prompt(qd_model* m, const int32_t* tokens, int32_t n, qd_stream stream);
 int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* d_tokens,
                 float* d_logits_last, qd_stream stream);
@@ -178,11 +184,15 @@ int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* d_tokens,
  * Each position's values equal the decode step's up to f32 rounding order.
  * Continue with qd_generate(pos0 + n, ...).  Buffers (about 16 positions of
  * activations plus an attention workspace) are allocated by the first call,
- * which synchronises; later calls allocate nothing.  The weight scales must
- * satisfy |d| < 8192 (the matrix-core GEMV, as qd_gemv_q4_0_batch).
- * A model with attn_out_gate gates each position's attention output as the
- * decode step does.  QD_ERANGE unless 0 <= pos0, n >= 1 and
- * pos0 + n <= max_seq. */
+ * which synchronises; later calls allocate nothing.  The matrix products
+ * take each position's activations as an f16 pair (hi + lo, about 22
+ * significant bits) after scaling the position's vector by a power of two
+ * that puts its largest magnitude in [2^13, 2^14), undone exactly in f32, so
+ * any finite activation scale is handled; the block scales d are applied in
+ * f32.  A model with attn_out_gate gates each position's attention output as the
+ * decode step does.  QD_ERANGE unless 0 <= pos0, n >= 1, pos0 + n <= max_seq
+ * and pos0 is at most one past the written prefix; afterwards the prefix is
+ * 0 .. pos0+n-1. */
 int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_last, qd_stream stream);
 
 /* Standalone q4_0 GEMV (inferencelayer cuda_llm.rs page, CudaQwen3::gemv):
@@ -198,12 +208,15 @@ int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x
  * b < B, every weight read once for the whole batch.  W as for qd_gemv_q4_0;
  * d_x device f32 [B][K] and d_y device f32 [B][N], both contiguous; qs and x
  * 16-byte aligned.  1 <= B <= 16; B == 1 runs the single-vector kernel,
- * 2 <= B <= 5 a vector kernel that stages the whole batch in LDS (B*K <=
- * 32 768), B >= 6 the matrix cores (any K; the weight scales must satisfy
- * |d| < 8192, since (code - 8) * d is formed in f16).  N < 2^24,
- * N*K/2 < 2^32.  QD_EINVAL / QD_EUNSUPPORTED otherwise, with nothing
- * enqueued.  Products are exact in f32 on every path; the summation order
- * differs from the single-vector GEMV.  No allocation; capturable. */
+ * 2 <= B <= 5 a vector kernel that stages the whole batch in LDS when
+ * B*K <= 32 768, otherwise (and always for B >= 6) the matrix cores: any K,
+ * the weight scales must satisfy |d| < 8192 (since (code - 8) * d is formed
+ * in f16), and x enters as an f16 pair (about 22 significant bits) after a
+ * power-of-two scaling per vector and 1024-element chunk, undone exactly in
+ * f32, so any finite input scale is handled.  N < 2^24, N*K/2 < 2^32.
+ * QD_EINVAL / QD_EUNSUPPORTED otherwise, with nothing enqueued.  The
+ * summation order differs from the single-vector GEMV.  No allocation;
+ * capturable. */
 int qd_gemv_q4_0_batch(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x, float* d_y,
                        int32_t N, int32_t K, int32_t B, qd_stream stream);
 

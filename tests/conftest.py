@@ -13,9 +13,13 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running CPU test")
 
 
-def pytest_collection_modifyitems(config, items):
-    # gpu tests first within their module order is irrelevant; keep collection order
-    pass
+def pytest_terminal_summary(terminalreporter):
+    helpers = sys.modules.get("gpu_helpers")
+    lines = getattr(helpers, "SUMMARY", None)
+    if lines:
+        terminalreporter.section("greedy parity")
+        for line in lines:
+            terminalreporter.write_line(line)
 
 
 @pytest.fixture(scope="session")

@@ -15,15 +15,22 @@ GOLDEN = os.path.join(HERE, "golden")
 # max |y - y_ref| / max |y_ref|), final logits max abs error <= 2e-2.
 GEMV_BAR = 1e-3
 LOGITS_BAR = 2e-2
-# Greedy near-tie: a differing token counts as a tie only when the oracle's
-# top-1 minus top-2 logit margin is below this (well above the f32-vs-f64
-# logit error measured on these configs, far below the typical margin).
-TIE_MARGIN = 1e-3
+
+
+
+# lines repeated in the session's terminal summary (compared greedy counts and
+# logit errors), so they show even when passing tests' output is captured
+SUMMARY: list = []
 
 
 def say(*a):
     print("[gpu-test]", *a, flush=True)
     sys.stdout.flush()
+
+
+def record(line: str):
+    say(line)
+    SUMMARY.append(line)
 
 
 def dev(a, dtype=None):
@@ -64,17 +71,24 @@ def first_mismatch(a, b) -> int:
     return n if len(a) == len(b) else n
 
 
-def check_greedy(gpu_tokens, ref_tokens, ref_margins, label: str) -> int:
-    """Greedy tokens must be equal.  A first difference is accepted only as a
-    near-tie (oracle margin < TIE_MARGIN); the sequences are not comparable
-    after it.  Returns the number of compared (equal) tokens."""
+def check_greedy(gpu_tokens, ref_tokens, ref_margins, label: str, step_err=None):
+    """Greedy tokens must be equal.  A first difference at step i is accepted
+    only as a near-tie: the oracle's top-1 minus top-2 margin at i must be below
+    the logit error measured at that same step, step_err(i) (max |gpu - oracle|
+    over the step's compared logits; None when that step's logits are not
+    available, and then nothing is accepted).  The sequences are not comparable
+    after an accepted tie.  Returns (number of equal leading tokens, whether a
+    tie was accepted); the count is printed."""
+    G = len(ref_tokens)
     i = first_mismatch(gpu_tokens, ref_tokens)
-    if i < len(ref_tokens):
-        m = float(ref_margins[i])
-        say(f"{label}: first greedy difference at step {i}: gpu {int(gpu_tokens[i])} vs oracle "
-            f"{int(ref_tokens[i])}, oracle top-2 margin {m:.3e}")
-        assert m < TIE_MARGIN, f"{label}: greedy token {i} differs with margin {m:.3e}"
-    else:
-        say(f"{label}: all {len(ref_tokens)} greedy tokens equal "
-            f"(min oracle margin {float(np.min(ref_margins)):.3e})")
-    return i
+    if i >= G:
+        record(f"{label}: {G}/{G} greedy tokens equal (min oracle margin {float(np.min(ref_margins)):.3e})")
+        return G, False
+    m = float(ref_margins[i])
+    e = step_err(i) if step_err is not None else None
+    record(f"{label}: {i}/{G} greedy tokens equal; step {i}: gpu {int(gpu_tokens[i])} vs oracle "
+        f"{int(ref_tokens[i])}, oracle top-2 margin {m:.3e}, measured logit error at that step "
+        f"{'not available' if e is None else f'{e:.3e}'}")
+    assert e is not None and m < e, f"{label}: greedy token {i} differs (margin {m:.3e}, error {e})"
+    record(f"{label}: step {i} accepted as a near-tie (margin below the measured error)")
+    return i, True

@@ -85,7 +85,7 @@ def test_layer_kernel_free_running_greedy(lk, lk_ref):
     m.generate(0, P + G - 1, tokens=out)
     got = host(out)[P - 1:]
     m.close()
-    assert check_greedy(got, toks, margins, "layerk") == G
+    assert check_greedy(got, toks, margins, "layerk") == (G, False)
 
 
 def test_layer_kernel_graph_equals_eager_bitwise(lk):

@@ -16,9 +16,12 @@
 // group.  Because the blocks differ in scale, the scale is part of the A
 // operand: (code - 8) * d as an f16 pair hi + lo with hi = RN((code-8)*d)
 // and lo = (code-8)*d - hi, both exact in f16 for |d| < 8192 ((code-8)*d has
-// at most 15 significant bits).  x enters as an f16 pair too (hi = RN(x),
-// lo = RN(x - hi), about 22 bits), and the four products hi*hi, hi*lo, lo*hi,
-// lo*lo accumulate in f32: every product is exact in f32.
+// at most 15 significant bits).  x enters as an f16 pair too, after a power
+// of two s per (vector, chunk of 32 blocks) that puts the chunk's largest
+// |x| in [2^13, 2^14): hi = RN(x s), lo = RN(x s - hi), about 22 bits at any
+// input scale and no f16 overflow.  The four products hi*hi, hi*lo, lo*hi,
+// lo*lo accumulate in f32 (every product exact); each chunk's sum is
+// multiplied by 1/s, exactly, into the result.
 //
 // Codes to f16: (w & 0x000F000F) | 0x64006400 holds two codes as the f16
 // values 1024 + code; a packed f16 add of -1032 leaves code - 8, exactly.
@@ -73,6 +76,17 @@ QD_DEV void gbm_a_operand(uint32_t w, gbm_half2 d2, gbm_half8& hi, gbm_half8& lo
     }
 }
 
+// s = 2^k with a * s in [2^13, 2^14) for the largest magnitude a of a chunk
+// of a vector (k clamped to [-100, 100]; 1 when a is 0 or not finite)
+QD_DEV float gbm_scale_for(float a)
+{
+    if (!(a > 0.f) || !(a <= 3.4e38f))
+        return 1.f;
+    int e;
+    (void)frexpf(a, &e);   // a in [2^(e-1), 2^e)
+    return ldexpf(1.f, max(-100, min(100, 14 - e)));
+}
+
 // staging items (block, word, vector) per thread per chunk
 template <int NC>
 struct GbmItems {
@@ -97,6 +111,8 @@ k_gemv_batch_mfma(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
     static_assert(NC >= 2 && NC <= 16, "batch");
     constexpr int NITEM = GBM_KC * 4 * NC;   // staging items of a chunk
     extern __shared__ __align__(16) _Float16 xs[];   // [KC][4][NC][16]
+    __shared__ unsigned xmax[2][GBM_MAXB];            // |x| maxima (f32 bits), by chunk parity
+    __shared__ float xinv[GBM_MAXB];                  // 1/s of the staged chunk, per vector
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
     const int r = lane & 15, kg = lane >> 4;
@@ -104,6 +120,9 @@ k_gemv_batch_mfma(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
     const int K = nb * 32;
     const int nch = (nb + GBM_KC - 1) / GBM_KC;
     const int ntiles = (N + GBM_ROWS - 1) / GBM_ROWS;
+    if (threadIdx.x < 2 * GBM_MAXB)
+        xmax[threadIdx.x / GBM_MAXB][threadIdx.x % GBM_MAXB] = 0u;   // ordered by the first stage's barrier
+    int gc = 0;   // chunks staged so far by this workgroup (parity of xmax)
 
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {   // uniform per workgroup
         const int row0 = tile * GBM_ROWS + wave * 16;
@@ -131,21 +150,38 @@ k_gemv_batch_mfma(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                 bf.xb[u] = *reinterpret_cast<const float4*>(xp + 16);
             }
         };
-        // stage x of chunk c from the registers of its loads
+        // stage x of chunk c from the registers of its loads: the chunk's
+        // largest |x| per vector (LDS atomic max of the f32 bits, which order
+        // like the values for |x|), then the scaled split
         auto stage = [&](const GbmX<NC>& bf, int c) {
-            __syncthreads();   // the previous chunk's reads are done
+            unsigned* xm = xmax[gc & 1];
+            __syncthreads();   // the previous chunk's reads (x, 1/s) are done
 #pragma unroll
             for (int u = 0; u < GbmItems<NC>::N; ++u) {
                 const int i = (int)threadIdx.x + u * GBM_NW * WAVE;
                 if (i >= NITEM)   // uniform except in the last round of an odd batch
                     continue;
+                const bool in = c * GBM_KC + i / (4 * NC) < nb;
+                const float4 a = bf.xa[u], h = bf.xb[u];
+                const float mx = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                                       fmaxf(fmaxf(fabsf(h.x), fabsf(h.y)), fmaxf(fabsf(h.z), fabsf(h.w))));
+                if (in)
+                    atomicMax(&xm[i % NC], __float_as_uint(mx));
+            }
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < GbmItems<NC>::N; ++u) {
+                const int i = (int)threadIdx.x + u * GBM_NW * WAVE;
+                if (i >= NITEM)
+                    continue;
                 const int bl = i / (4 * NC);
                 const bool in = c * GBM_KC + bl < nb;
+                const float sc = gbm_scale_for(__uint_as_float(xm[i % NC]));
                 const float4 a = bf.xa[u], h = bf.xb[u];
                 float e[8] = {a.x, a.z, a.y, a.w, h.x, h.z, h.y, h.w};
 #pragma unroll
                 for (int k = 0; k < 8; ++k)
-                    e[k] = in ? e[k] : 0.f;
+                    e[k] = in ? e[k] * sc : 0.f;
                 gbm_half8 xh, xl;
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
@@ -157,10 +193,18 @@ k_gemv_batch_mfma(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                 dst[0] = xh;
                 dst[1] = xl;
             }
+            if (threadIdx.x < NC) {
+                xinv[threadIdx.x] = 1.0f / gbm_scale_for(__uint_as_float(xm[threadIdx.x]));
+                // the other parity was last read before this stage's first barrier
+                // and is next written after the following stage's first barrier
+                xmax[(gc + 1) & 1][threadIdx.x] = 0u;
+            }
+            ++gc;
             __syncthreads();
         };
         gbm_floatx4 acc = {0.f, 0.f, 0.f, 0.f};
         auto compute = [&](const GbmBuf& bf) {
+            gbm_floatx4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < GBM_KC / 4; ++j) {
                 const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)bf.d[j]);
@@ -174,12 +218,16 @@ k_gemv_batch_mfma(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                     const gbm_half8* src =
                         reinterpret_cast<const gbm_half8*>(xs + ((size_t)(bl * 4 + w) * NC + col) * 16);
                     const gbm_half8 bhi = src[0], blo = src[1];
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bhi, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, blo, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bhi, acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, blo, acc, 0, 0, 0);
+                    part = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bhi, part, 0, 0, 0);
+                    part = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, blo, part, 0, 0, 0);
+                    part = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bhi, part, 0, 0, 0);
+                    part = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, blo, part, 0, 0, 0);
                 }
             }
+            const float inv = xinv[col];   // column col = this lane's vector
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i] = fmaf(part[i], inv, acc[i]);
         };
         GbmBuf b0, b1;
         GbmX<NC> xr;

@@ -17,8 +17,12 @@
 // XP layout: [16 positions][nb blocks][hi, lo][4 lane groups][8 halves];
 // lane group g of block j holds the elements of word g of the q4_0 block
 // (low nibbles 4g..4g+3, high nibbles 16+4g..16+4g+3) in the order xp_pos
-// gives.  hi = RN_f16(x), lo = RN_f16(x - hi).  A position's hi halves of a
-// block are 64 contiguous bytes, as are its lo halves.
+// gives.  hi = RN_f16(x s), lo = RN_f16(x s - hi), with s = 2^k a power of two
+// per position chosen from the position's largest |x| so that |x s| lies in
+// [2^13, 2^14): hi never overflows f16 and the pair keeps about 22
+// significant bits at any input scale.  1/s (XS[t]) multiplies the position's
+// sums in f32, exactly.  A position's hi halves of a block are 64 contiguous
+// bytes, as are its lo halves.
 //
 // Weights are read coalesced: lane (r, g) loads block b0 + g of row r whole
 // (16 bytes; four lanes read 64 contiguous bytes of a row) and its scale,
@@ -45,6 +49,17 @@ QD_DEV size_t xp_index(int t, int k, int nb)   // half index of hi; lo is +32
     const int j = k >> 5, e = k & 31;
     return ((size_t)t * nb + j) * 64 + ((e & 15) >> 2) * 8 + xp_pos(e);
 }
+// s = 2^k with a * s in [2^13, 2^14) for the largest magnitude a of a
+// vector (k clamped to [-100, 100]; 1 when a is 0 or not finite)
+QD_DEV float xp_scale_for(float a)
+{
+    if (!(a > 0.f) || !(a <= 3.4e38f))
+        return 1.f;
+    int e;
+    (void)frexpf(a, &e);   // a in [2^(e-1), 2^e)
+    return ldexpf(1.f, max(-100, min(100, 14 - e)));
+}
+
 QD_DEV void xp_store(_Float16* XP, int t, int k, int nb, float x)
 {
     const _Float16 h = (_Float16)x;
@@ -73,18 +88,34 @@ QD_DEV pg_half8 pg_codes(uint32_t w)
 
 enum PgMode { PG_STORE = 0, PG_RESID = 1, PG_SWIGLU = 2 };
 
+// largest |value| over a workgroup (every thread gets it); red >= 16 floats
+QD_DEV float pg_block_max(float v, float* red)
+{
+    v = group_max<WAVE>(v);
+    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    __syncthreads();
+    if (lane == 0)
+        red[wv] = v;
+    __syncthreads();
+    float m = 0.f;
+    for (int i = 0; i < (int)(blockDim.x / WAVE); ++i)
+        m = fmaxf(m, red[i]);
+    return m;
+}
+
 // One workgroup of NW waves owns 16*R weight rows; wave w takes the 4-block
 // steps w, w + NW, ... of every row (the next step's loads issued before the
 // current one is computed), and the NW partial sums are added in wave order
 // through LDS.  Epilogue (T positions written):
+// (sum = the product of position t's split input, times XS[t]):
 //   PG_STORE : Y[t][row] = sum
 //   PG_RESID : Y[t][row] += sum                     (residual add)
 //   PG_SWIGLU: rows 2i, 2i+1 are gate and up of unit i; silu(gate) * up is
-//              written split into XPo (the next product's input), K = N / 2
+//              written to Y[t][i] (Y is [T][N/2]), split by k_pf_xsplit
 template <int R, int NW, int MODE>
 __global__ void __launch_bounds__(NW* WAVE)
 k_pf_gemm(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q, const _Float16* __restrict__ XP,
-          int N, int nb, int T, float* __restrict__ Y, _Float16* __restrict__ XPo)
+          const float* __restrict__ XS, int N, int nb, int T, float* __restrict__ Y)
 {
     constexpr int CB = 4;   // blocks per step
     __shared__ uint4 wl[NW][R][16][CB + 1];   // codes [row][block], one pad per row
@@ -191,17 +222,20 @@ k_pf_gemm(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q, const _
             for (int i = 0; i < 4; ++i)
                 v[i] += o[i];
         }
-        // v[i]: position 4g + i, row row0 + 16 s + r
+        // v[i]: position 4g + i, row row0 + 16 s + r; undo the input scale
         const int row = row0 + 16 * s + r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] *= XS[min(4 * g + i, T - 1)];
         if (MODE == PG_SWIGLU) {
-            const int K2 = N >> 1, nb2 = K2 >> 5;
+            const int K2 = N >> 1;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float up = __shfl_xor(v[i], 1, WAVE);
                 const int t = 4 * g + i;
                 if (!(r & 1) && row < N && t < T) {
                     const float gt = v[i];
-                    xp_store(XPo, t, row >> 1, nb2, gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up);
+                    Y[(size_t)t * K2 + (row >> 1)] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
                 }
             }
         } else if (row < N) {
@@ -217,36 +251,48 @@ k_pf_gemm(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q, const _
     }
 }
 
-// X [T][K] f32 -> XP (split, A-operand order); grid (ceil(K/256), T).  With
-// a gate (row t at gate + t * gstride), x is multiplied by sigmoid(gate)
-// first, as the decode step gates the merged attention output.
-__global__ void __launch_bounds__(256)
+// X [T][K] f32 -> XP (split, A-operand order) and XS[t] = 1/s; grid T, 1024
+// threads.  With a gate (row t at gate + t * gstride), x is multiplied by
+// sigmoid(gate) first, as the decode step gates the merged attention output.
+__global__ void __launch_bounds__(1024)
 k_pf_xsplit(const float* __restrict__ X, int K, const float* __restrict__ gate, int gstride,
-            _Float16* __restrict__ XP)
+            _Float16* __restrict__ XP, float* __restrict__ XS)
 {
-    const int t = blockIdx.y, k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k < K) {
+    __shared__ float red[16];
+    const int t = blockIdx.x;
+    auto val = [&](int k) {
         float x = X[(size_t)t * K + k];
         if (gate)   // uniform
             x *= 1.0f / (1.0f + expf(-gate[(size_t)t * gstride + k]));
-        xp_store(XP, t, k, K >> 5, x);
-    }
+        return x;
+    };
+    float a = 0.f;
+    for (int k = threadIdx.x; k < K; k += blockDim.x)
+        a = fmaxf(a, fabsf(val(k)));
+    const float sc = xp_scale_for(pg_block_max(a, red));
+    for (int k = threadIdx.x; k < K; k += blockDim.x)
+        xp_store(XP, t, k, K >> 5, val(k) * sc);
+    if (threadIdx.x == 0)
+        XS[t] = 1.0f / sc;
 }
 
-// RMSNorm of X[t] (weight w) written split into XP; grid T, 1024 threads,
-// H a multiple of 32 (each thread 4 consecutive elements per round)
+// RMSNorm of X[t] (weight w) written split into XP, XS[t] = 1/s; grid T,
+// 1024 threads, H a multiple of 32 (each thread 4 consecutive elements per
+// round)
 __global__ void __launch_bounds__(1024)
 k_pf_rmsnorm_xp(const float* __restrict__ X, const float* __restrict__ w, int H, float eps,
-                _Float16* __restrict__ XP)
+                _Float16* __restrict__ XP, float* __restrict__ XS)
 {
     __shared__ float red[16];
     const int t = blockIdx.x;
     const float4* x4 = reinterpret_cast<const float4*>(X + (size_t)t * H);
+    const float4* w4 = reinterpret_cast<const float4*>(w);
     const int n4 = H >> 2;
-    float ss = 0.f;
+    float ss = 0.f, a = 0.f;
     for (int i = threadIdx.x; i < n4; i += blockDim.x) {
-        const float4 v = x4[i];
+        const float4 v = x4[i], g = w4[i];
         ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+        a = fmaxf(fmaxf(a, fmaxf(fabsf(v.x * g.x), fabsf(v.y * g.y))), fmaxf(fabsf(v.z * g.z), fabsf(v.w * g.w)));
     }
     ss = group_sum<WAVE>(ss);
     const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
@@ -257,14 +303,18 @@ k_pf_rmsnorm_xp(const float* __restrict__ X, const float* __restrict__ w, int H,
     for (int i = 0; i < (int)(blockDim.x / WAVE); ++i)   // fixed order
         tot += red[i];
     const float rs = 1.0f / sqrtf(tot / (float)H + eps);
-    const float4* w4 = reinterpret_cast<const float4*>(w);
+    // largest |x w rs| up to rounding: the scale only has to keep it below 2^15
+    const float sc = xp_scale_for(pg_block_max(a, red) * rs);
+    const float f = rs * sc;
     for (int i = threadIdx.x; i < n4; i += blockDim.x) {
         const float4 v = x4[i], g = w4[i];
-        xp_store(XP, t, 4 * i, H >> 5, v.x * rs * g.x);
-        xp_store(XP, t, 4 * i + 1, H >> 5, v.y * rs * g.y);
-        xp_store(XP, t, 4 * i + 2, H >> 5, v.z * rs * g.z);
-        xp_store(XP, t, 4 * i + 3, H >> 5, v.w * rs * g.w);
+        xp_store(XP, t, 4 * i, H >> 5, v.x * f * g.x);
+        xp_store(XP, t, 4 * i + 1, H >> 5, v.y * f * g.y);
+        xp_store(XP, t, 4 * i + 2, H >> 5, v.z * f * g.z);
+        xp_store(XP, t, 4 * i + 3, H >> 5, v.w * f * g.w);
     }
+    if (threadIdx.x == 0)
+        XS[t] = 1.0f / sc;
 }
 
 }  // namespace qd

@@ -99,10 +99,15 @@ struct DevLayer {
 struct qd_model {
     int H, L, nq, nkv, hd, I, V, rot, qkv_rows, max_seq, qk_norm, paged, nblocks;
     float eps;
+    // the written prefix of the KV cache: positions 0 .. hw hold K/V of the
+    // current sequence (-1: none).  A step at p writes p and makes [0, p] the
+    // prefix; a step may start at most one position past it.
+    int hw = -1;
     // chunked prefill buffers (allocated by the first qd_prefill)
     struct {
-        float *X = nullptr, *QKV = nullptr, *Q = nullptr, *O = nullptr, *hf = nullptr;
+        float *X = nullptr, *QKV = nullptr, *Q = nullptr, *O = nullptr, *hf = nullptr, *A = nullptr;
         _Float16 *XP1 = nullptr, *XP2 = nullptr;   // split activations (prefill_gemm.h)
+        float *XS1 = nullptr, *XS2 = nullptr;      // their per-position scales
         int32_t *lens = nullptr, *iota = nullptr;
         float* ws = nullptr;
         AttnGeom geo;
@@ -817,10 +822,14 @@ extern "C" int qd_decode_step(qd_model* m, int32_t token, int32_t pos, float* d_
         return fail(QD_ERANGE, "token %d not in [0, %d)", token, m->V);
     if (pos < 0 || pos >= m->max_seq)
         return fail(QD_ERANGE, "pos %d not in [0, %d)", pos, m->max_seq);
+    if (pos > m->hw + 1)
+        return fail(QD_ERANGE, "pos %d past the written prefix: positions 0..%d hold K/V, so the "
+                               "next step is at most at %d", pos, m->hw, m->hw + 1);
     hipStream_t s = (hipStream_t)stream;
     hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, s, m->st, m->ids, pos, pos + 1, pos, token);
     HIP_TRY(hipGetLastError());
     QD_TRY(run_steps(m, 1, s));
+    m->hw = pos;
     if (d_logits)
         HIP_TRY(hipMemcpyAsync(d_logits, m->logits, sizeof(float) * m->V, hipMemcpyDeviceToDevice, s));
     if (d_next)
@@ -857,10 +866,15 @@ extern "C" int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* 
     if (pos0 < 0 || n_steps < 0 || (int64_t)pos0 + n_steps > m->max_seq)
         return fail(QD_ERANGE, "positions [%d, %d) not within max_seq %d", pos0, pos0 + n_steps,
                     m->max_seq);
+    if (n_steps > 0 && pos0 > m->hw + 1)
+        return fail(QD_ERANGE, "pos0 %d past the written prefix: positions 0..%d hold K/V, so the "
+                               "next step is at most at %d", pos0, m->hw, m->hw + 1);
     hipStream_t s = (hipStream_t)stream;
     hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, s, m->st, m->ids, pos0, -1, -1, 0);
     HIP_TRY(hipGetLastError());
     QD_TRY(run_steps(m, n_steps, s));
+    if (n_steps > 0)
+        m->hw = pos0 + n_steps - 1;
     if (d_tokens && n_steps > 0)
         HIP_TRY(hipMemcpyAsync(d_tokens, m->pred + pos0, sizeof(int32_t) * n_steps,
                                hipMemcpyDeviceToDevice, s));
@@ -1001,17 +1015,26 @@ static hipError_t launch_gemv_batch_l(const uint16_t* d, const uint8_t* q, const
 constexpr int GBM_GRID_CAP = 1024;
 
 template <int NC>
+static hipError_t launch_gemv_batch_mfma(const uint16_t* d, const uint8_t* q, const float* x, float* y,
+                                         int N, int nb, hipStream_t s)
+{
+    const int ntiles = (N + GBM_ROWS - 1) / GBM_ROWS;
+    hipLaunchKernelGGL((k_gemv_batch_mfma<NC>), dim3(std::max(1, std::min(ntiles, GBM_GRID_CAP))),
+                       dim3(GBM_NW * WAVE), gemv_batch_mfma_lds_bytes(NC), s, d, q, x, y, N, nb);
+    return hipGetLastError();
+}
+
+template <int NC>
 static hipError_t launch_gemv_batch(const uint16_t* d, const uint8_t* q, const float* x, float* y,
                                     int N, int K, hipStream_t s)
 {
     const int nb = K / 32;
     static_assert(QD_BATCH_MFMA_MIN >= 2 && QD_BATCH_MFMA_MIN <= GB_MAXB + 1, "kernel switch");
     if constexpr (NC >= QD_BATCH_MFMA_MIN) {
-        const int ntiles = (N + GBM_ROWS - 1) / GBM_ROWS;
-        hipLaunchKernelGGL((k_gemv_batch_mfma<NC>), dim3(std::max(1, std::min(ntiles, GBM_GRID_CAP))),
-                           dim3(GBM_NW * WAVE), gemv_batch_mfma_lds_bytes(NC), s, d, q, x, y, N, nb);
-        return hipGetLastError();
+        return launch_gemv_batch_mfma<NC>(d, q, x, y, N, nb, s);
     } else {
+        if ((int64_t)NC * K > GB_MAXKB)   // the batch does not fit the vector kernel's LDS
+            return launch_gemv_batch_mfma<NC>(d, q, x, y, N, nb, s);
         if (pick_lpr(nb, 16) == 16)
             return launch_gemv_batch_l<NC, 16>(d, q, x, y, N, nb, s);
         return launch_gemv_batch_l<NC, 8>(d, q, x, y, N, nb, s);
@@ -1027,9 +1050,6 @@ extern "C" int qd_gemv_q4_0_batch(const uint16_t* d_scales, const uint8_t* d_qs,
         return fail(QD_EINVAL, "bad shape N=%d K=%d (K %% 32 must be 0)", N, K);
     if (B < 1 || B > GBM_MAXB)
         return fail(QD_EINVAL, "batch B=%d outside [1, %d]", B, GBM_MAXB);
-    if (B < QD_BATCH_MFMA_MIN && (int64_t)B * K > GB_MAXKB)
-        return fail(QD_EUNSUPPORTED, "B*K = %lld above %d for B < %d (the batch is staged in LDS)",
-                    (long long)B * K, GB_MAXKB, QD_BATCH_MFMA_MIN);
     if (B == 1 && gemv_lds_bytes(K / 32) > (size_t)GEMV_MAX_LDS)
         return fail(QD_EUNSUPPORTED, "K=%d above the staged-x limit", K);
     if ((uint64_t)N * (uint64_t)K / 2 >= (uint64_t)1 << 32 || N >= (1 << 24))
@@ -1248,24 +1268,24 @@ extern "C" int qd_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink,
 // 2 row slices for the tall gate|up (24576 rows), 8 waves of 2 slices for
 // q|k|v (6144 rows), 8 waves of 1 slice below 6144 rows.
 template <int MODE>
-static hipError_t pf_gemm(const DevQ4& W, const _Float16* XP, int T, float* Y, _Float16* XPo, hipStream_t s)
+static hipError_t pf_gemm(const DevQ4& W, const _Float16* XP, const float* XS, int T, float* Y, hipStream_t s)
 {
     const int N = W.rows, nb = W.nb, g1 = (N + 15) / 16;
 #ifdef QD_PG_FORCE   // compile-time override: rows slices per wave, waves per workgroup
     constexpr int FR[2] = {QD_PG_FORCE};
     hipLaunchKernelGGL((k_pf_gemm<FR[0], FR[1], MODE>), dim3((N + 16 * FR[0] - 1) / (16 * FR[0])),
-                       dim3(FR[1] * WAVE), 0, s, W.d, W.qs, XP, N, nb, T, Y, XPo);
+                       dim3(FR[1] * WAVE), 0, s, W.d, W.qs, XP, XS, N, nb, T, Y);
     return hipGetLastError();
 #endif
     if (g1 >= 1024)
-        hipLaunchKernelGGL((k_pf_gemm<2, 4, MODE>), dim3((N + 31) / 32), dim3(4 * WAVE), 0, s, W.d, W.qs, XP, N,
-                           nb, T, Y, XPo);
+        hipLaunchKernelGGL((k_pf_gemm<2, 4, MODE>), dim3((N + 31) / 32), dim3(4 * WAVE), 0, s, W.d, W.qs, XP, XS,
+                           N, nb, T, Y);
     else if (g1 >= 384)
-        hipLaunchKernelGGL((k_pf_gemm<2, 8, MODE>), dim3((N + 31) / 32), dim3(8 * WAVE), 0, s, W.d, W.qs, XP, N,
-                           nb, T, Y, XPo);
+        hipLaunchKernelGGL((k_pf_gemm<2, 8, MODE>), dim3((N + 31) / 32), dim3(8 * WAVE), 0, s, W.d, W.qs, XP, XS,
+                           N, nb, T, Y);
     else
-        hipLaunchKernelGGL((k_pf_gemm<1, 8, MODE>), dim3(g1), dim3(8 * WAVE), 0, s, W.d, W.qs, XP, N, nb, T, Y,
-                           XPo);
+        hipLaunchKernelGGL((k_pf_gemm<1, 8, MODE>), dim3(g1), dim3(8 * WAVE), 0, s, W.d, W.qs, XP, XS, N, nb, T,
+                           Y);
     return hipGetLastError();
 }
 
@@ -1281,13 +1301,17 @@ static int pf_setup(qd_model* m)
     if ((rc = dev_alloc_t(m, &P.X, T * m->H)) || (rc = dev_alloc_t(m, &P.QKV, T * m->qkv_rows)) ||
         (rc = dev_alloc_t(m, &P.Q, T * nqd)) || (rc = dev_alloc_t(m, &P.O, T * nqd)) ||
         (rc = dev_alloc_t(m, &P.XP1, T * kx * 2)) || (rc = dev_alloc_t(m, &P.XP2, T * (size_t)m->I * 2)) ||
+        (rc = dev_alloc_t(m, &P.A, T * (size_t)m->I)) || (rc = dev_alloc_t(m, &P.XS1, T)) ||
+        (rc = dev_alloc_t(m, &P.XS2, T)) ||
         (rc = dev_alloc_t(m, &P.hf, (size_t)m->H)) || (rc = dev_alloc_t(m, &P.lens, T)) ||
         (rc = dev_alloc_t(m, &P.iota, (size_t)m->V)) || (rc = dev_alloc_t(m, &P.ws, ws / sizeof(float) + 1)))
         return rc;
     hipLaunchKernelGGL(k_pf_iota, dim3((m->V + 255) / 256), dim3(256), 0, 0, P.iota, m->V);
-    // positions past a short chunk read these rows: keep them finite
+    // positions past a short chunk read these rows and scales: keep them finite
     if (hipMemset(P.XP1, 0, T * kx * 2 * sizeof(_Float16)) != hipSuccess ||
-        hipMemset(P.XP2, 0, T * (size_t)m->I * 2 * sizeof(_Float16)) != hipSuccess)
+        hipMemset(P.XP2, 0, T * (size_t)m->I * 2 * sizeof(_Float16)) != hipSuccess ||
+        hipMemset(P.XS1, 0, T * sizeof(float)) != hipSuccess ||
+        hipMemset(P.XS2, 0, T * sizeof(float)) != hipSuccess)
         return fail(QD_EHIP, "prefill buffer set-up failed");
     if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess)
         return fail(QD_EHIP, "prefill buffer set-up failed");
@@ -1301,6 +1325,9 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
         return fail(QD_EINVAL, "null model");
     if (n <= 0 || pos0 < 0 || (int64_t)pos0 + n > m->max_seq)
         return fail(QD_ERANGE, "positions [%d, %d) not in [0, %d)", pos0, pos0 + n, m->max_seq);
+    if (pos0 > m->hw + 1)
+        return fail(QD_ERANGE, "pos0 %d past the written prefix: positions 0..%d hold K/V, so the "
+                               "next position is at most %d", pos0, m->hw, m->hw + 1);
     QD_TRY(pf_setup(m));
     auto& P = m->pf;
     const hipStream_t s = (hipStream_t)stream;
@@ -1314,8 +1341,9 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
                            H, m->ids, p0, P.X);
         for (int l = 0; l < m->L; ++l) {
             DevLayer& Ly = m->layers[l];
-            hipLaunchKernelGGL(k_pf_rmsnorm_xp, dim3(T), dim3(1024), 0, s, P.X, Ly.attn_norm, H, m->eps, P.XP1);
-            HIP_TRY(pf_gemm<PG_STORE>(Ly.qkv, P.XP1, T, P.QKV, nullptr, s));
+            hipLaunchKernelGGL(k_pf_rmsnorm_xp, dim3(T), dim3(1024), 0, s, P.X, Ly.attn_norm, H, m->eps, P.XP1,
+                               P.XS1);
+            HIP_TRY(pf_gemm<PG_STORE>(Ly.qkv, P.XP1, P.XS1, T, P.QKV, s));
             const float* qn = m->qk_norm ? Ly.q_norm : m->ones_hd;
             const float* kn = m->qk_norm ? Ly.k_norm : m->ones_hd;
             const int32_t* tbl = m->paged ? m->table : nullptr;
@@ -1356,12 +1384,14 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
             const int kq = m->nq * hd;
             // the gate rows follow q|k|v in the fused product
             const float* gate = m->attn_gate ? P.QKV + (size_t)(m->nq + 2 * m->nkv) * hd : nullptr;
-            hipLaunchKernelGGL(k_pf_xsplit, dim3((kq + 255) / 256, T), dim3(256), 0, s, P.O, kq, gate,
-                               m->qkv_rows, P.XP1);
-            HIP_TRY(pf_gemm<PG_RESID>(Ly.o, P.XP1, T, P.X, nullptr, s));
-            hipLaunchKernelGGL(k_pf_rmsnorm_xp, dim3(T), dim3(1024), 0, s, P.X, Ly.ffn_norm, H, m->eps, P.XP1);
-            HIP_TRY(pf_gemm<PG_SWIGLU>(Ly.gu, P.XP1, T, nullptr, P.XP2, s));
-            HIP_TRY(pf_gemm<PG_RESID>(Ly.down, P.XP2, T, P.X, nullptr, s));
+            hipLaunchKernelGGL(k_pf_xsplit, dim3(T), dim3(1024), 0, s, P.O, kq, gate, m->qkv_rows, P.XP1,
+                               P.XS1);
+            HIP_TRY(pf_gemm<PG_RESID>(Ly.o, P.XP1, P.XS1, T, P.X, s));
+            hipLaunchKernelGGL(k_pf_rmsnorm_xp, dim3(T), dim3(1024), 0, s, P.X, Ly.ffn_norm, H, m->eps, P.XP1,
+                               P.XS1);
+            HIP_TRY(pf_gemm<PG_SWIGLU>(Ly.gu, P.XP1, P.XS1, T, P.A, s));
+            hipLaunchKernelGGL(k_pf_xsplit, dim3(T), dim3(1024), 0, s, P.A, m->I, nullptr, 0, P.XP2, P.XS2);
+            HIP_TRY(pf_gemm<PG_RESID>(Ly.down, P.XP2, P.XS2, T, P.X, s));
         }
     }
     // the last position: final norm, LM head, greedy token as a decode step records it
@@ -1372,6 +1402,7 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
     hipLaunchKernelGGL(k_argmax_advance, dim3(1), dim3(256), 0, s, m->logits, P.iota, m->V, m->V, m->st,
                        m->ids, m->pred, m->max_seq);
     HIP_TRY(hipGetLastError());
+    m->hw = pos0 + n - 1;
     if (d_logits_last)
         HIP_TRY(hipMemcpyAsync(d_logits_last, m->logits, sizeof(float) * m->V, hipMemcpyDeviceToDevice, s));
     return QD_OK;
