@@ -301,6 +301,22 @@ int qd_attn_decode(const qd_attn_args* a, void* d_workspace, size_t workspace_by
 int qd_attn_decode_kv8(const qd_attn_args* a, float k_scale, float v_scale, void* d_workspace,
                        size_t workspace_bytes, qd_stream stream);
 
+/* The attention of qd_attn_decode without a workspace argument and without
+ * any allocation, for callers that cannot allocate (code under graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * split-KV partials live in a library scratch array of
+ * qd_attn_noalloc_max_bytes() bytes (8 MiB) in each GPU's memory, kept until
+ * the process ends.  Arguments and results as qd_attn_decode (f16 K/V);
+ * sizes whose partials exceed the scratch
+ * (qd_attn_workspace_bytes(B, nq, nkv, head_dim, max_kv_len) > the maximum)
+ * are refused with QD_EUNSUPPORTED, nothing enqueued.  Every call on one GPU
+ * uses that GPU's one scratch array: calls that overlap on a GPU (two
+ * streams, or two threads) race and must be serialised by the caller.  The
+ * scratch needs no initialisation (every partial read was written by the same
+ * call).  No allocation; capturable. */
+size_t qd_attn_noalloc_max_bytes(void);
+int qd_attn_decode_noalloc(const qd_attn_args* a, qd_stream stream);
+
 /* Synchronises `stream` and reports what the device recorded since the last
  * check, then clears it: QD_ERANGE if a step saw a token or a position out of
  * range (a stored token or position the host did not validate), QD_EHIP if a

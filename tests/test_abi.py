@@ -212,6 +212,24 @@ def test_rope_inv_freq_validation(qd):
         qd.rope_inv_freq(1e4, 64, "yarn", 2.0)
 
 
+def test_attention_noalloc_validation(qd):
+    """The no-allocation attention refuses bad arguments and sizes beyond its
+    scratch before any HIP call."""
+    L = qd.lib()
+    E, U = qd._native.QD_EINVAL, qd._native.QD_EUNSUPPORTED
+    assert qd.attn_noalloc_max_bytes() == 8 << 20
+    assert L.qd_attn_decode_noalloc(None, None) == E
+    p = C.c_void_p(16)
+    assert qd.attn_workspace_bytes(512, 64, 8, 128, 64) > qd.attn_noalloc_max_bytes()
+    a = qd._native.AttnArgs(p, p, p, p, 4, 16, p, 64, 512, 64, 8, 128, 0.1, p)
+    assert L.qd_attn_decode_noalloc(C.byref(a), None) == U
+    assert b"scratch" in L.qd_last_error()
+    a = qd._native.AttnArgs(p, p, p, p, 4, 16, p, 64, 1, 32, 8, 96, 0.1, p)   # head_dim 96
+    assert L.qd_attn_decode_noalloc(C.byref(a), None) == U
+    a = qd._native.AttnArgs(p, p, None, p, 4, 16, p, 64, 1, 32, 8, 128, 0.1, p)
+    assert L.qd_attn_decode_noalloc(C.byref(a), None) == E
+
+
 def test_attention_kv8_validation(qd):
     L = qd.lib()
     A = qd._native.AttnArgs

@@ -20,7 +20,8 @@ QD_OK, QD_EINVAL, QD_ERANGE, QD_ENOMEM, QD_EUNSUPPORTED, QD_EHIP = 0, -1, -2, -3
 # every function declared in include/qd.h
 EXPORTS = ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate", "qd_prefill",
            "qd_gemv_q4_0", "qd_gemv_q4_0_batch", "qd_gemv_q4_0_experts", "qd_rope_inv_freq", "qd_attn_workspace_bytes",
-           "qd_attn_decode_kv8", "qd_attn_decode", "qd_check",
+           "qd_attn_decode_kv8", "qd_attn_decode", "qd_attn_noalloc_max_bytes", "qd_attn_decode_noalloc",
+           "qd_check",
            "qd_stream_read_groups", "qd_stream_read", "qd_last_error")
 
 
@@ -103,6 +104,10 @@ def lib():
         L.qd_attn_decode.argtypes = [C.POINTER(AttnArgs), C.c_void_p, C.c_size_t, C.c_void_p]
         L.qd_attn_decode_kv8.argtypes = [C.POINTER(AttnArgs), C.c_float, C.c_float, C.c_void_p,
                                          C.c_size_t, C.c_void_p]
+        L.qd_attn_noalloc_max_bytes.restype = C.c_size_t
+        L.qd_attn_noalloc_max_bytes.argtypes = []
+        L.qd_attn_decode_noalloc.restype = C.c_int
+        L.qd_attn_decode_noalloc.argtypes = [C.POINTER(AttnArgs), C.c_void_p]
         L.qd_check.argtypes = [C.c_void_p, C.c_void_p]
         L.qd_stream_read_groups.restype = C.c_size_t
         L.qd_stream_read_groups.argtypes = [C.c_size_t]
@@ -201,6 +206,21 @@ def attn_decode(q, k, v, kv_lens, max_kv_len, nkv, scale, out, workspace, block_
                  int(max_kv_len), B, nq, nkv, hd, float(scale), _ptr(out))
     return check(lib().qd_attn_decode(C.byref(a), _ptr(workspace), workspace.numel() *
                                       workspace.element_size(), _stream(stream)))
+
+
+def attn_noalloc_max_bytes() -> int:
+    return int(lib().qd_attn_noalloc_max_bytes())
+
+
+def attn_decode_noalloc(q, k, v, kv_lens, max_kv_len, nkv, scale, out, block_tables=None,
+                        block_size=16, stream=None) -> int:
+    """attn_decode with its split partials in the library's per-GPU scratch
+    array (no workspace argument, no allocation)."""
+    B, nq, hd = q.shape
+    a = AttnArgs(_ptr(q), _ptr(k), _ptr(v), _ptr(block_tables),
+                 0 if block_tables is None else block_tables.shape[1], block_size, _ptr(kv_lens),
+                 int(max_kv_len), B, nq, nkv, hd, float(scale), _ptr(out))
+    return check(lib().qd_attn_decode_noalloc(C.byref(a), _stream(stream)))
 
 
 def attn_decode_kv8(q, k8, v8, kv_lens, max_kv_len, nkv, scale, k_scale, v_scale, out, workspace,

@@ -25,6 +25,7 @@
 #include <cstdlib>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1153,13 +1154,13 @@ extern "C" size_t qd_attn_workspace_bytes(int32_t B, int32_t nq, int32_t nkv, in
     return attn_ws_layout(B, nq, nkv, head_dim, max_kv_len, &g);
 }
 
+// Argument checks of the standalone attention (no HIP call).
 template <bool KV8>
-static int attn_decode_impl(const qd_attn_args* a, float k_scale, float v_scale, void* d_workspace,
-                            size_t workspace_bytes, qd_stream stream)
+static int attn_validate(const qd_attn_args* a, float k_scale, float v_scale)
 {
     if (!a)
         return fail(QD_EINVAL, "null args");
-    if (!a->q || !a->k || !a->v || !a->kv_lens || !a->out || !d_workspace)
+    if (!a->q || !a->k || !a->v || !a->kv_lens || !a->out)
         return fail(QD_EINVAL, "null pointer");
     if (a->B < 0 || a->nq <= 0 || a->nkv <= 0 || a->max_kv_len < 0)
         return fail(QD_EINVAL, "bad sizes");
@@ -1182,6 +1183,16 @@ static int attn_decode_impl(const qd_attn_args* a, float k_scale, float v_scale,
         if ((reinterpret_cast<uintptr_t>(a->k) | reinterpret_cast<uintptr_t>(a->v)) & 15)
             return fail(QD_EINVAL, "fp8 K/V pools must be 16-byte aligned");
     }
+    return QD_OK;
+}
+
+template <bool KV8>
+static int attn_decode_impl(const qd_attn_args* a, float k_scale, float v_scale, void* d_workspace,
+                            size_t workspace_bytes, qd_stream stream)
+{
+    QD_TRY(attn_validate<KV8>(a, k_scale, v_scale));
+    if (!d_workspace)
+        return fail(QD_EINVAL, "null workspace");
     if (a->B == 0)
         return QD_OK;
     AttnGeom geo;
@@ -1207,7 +1218,7 @@ static int attn_decode_impl(const qd_attn_args* a, float k_scale, float v_scale,
     p.out = a->out;
     p.k_scale = k_scale;
     p.v_scale = v_scale;
-    launch_attention<0, KV8>(p, geo.waves, a->head_dim, gq, a->block_tables != nullptr, a->B, a->nq,
+    launch_attention<0, KV8>(p, geo.waves, a->head_dim, a->nq / a->nkv, a->block_tables != nullptr, a->B, a->nq,
                              (hipStream_t)stream);
     HIP_TRY(hipGetLastError());
     return QD_OK;
@@ -1223,6 +1234,59 @@ extern "C" int qd_attn_decode_kv8(const qd_attn_args* a, float k_scale, float v_
                                   void* d_workspace, size_t workspace_bytes, qd_stream stream)
 {
     return attn_decode_impl<true>(a, k_scale, v_scale, d_workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------------------------------ attention without allocation
+
+// The split-KV partials of qd_attn_decode_noalloc: a file-scope device array,
+// one copy per GPU the library runs on, held until the process ends.  On the
+// host its name is only a stand-in for the symbol: the device address of each
+// GPU's copy comes from hipGetSymbolAddress (looked up once per device, with
+// that device current, on the entry point's first call there) and only that
+// address is handed to kernels.
+constexpr size_t QD_NOALLOC_SCRATCH_BYTES = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[QD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int QD_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[QD_MAX_DEVICES];
+
+// device address of the current device's scratch array
+static int noalloc_scratch(void** out)
+{
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= QD_MAX_DEVICES)
+        return fail(QD_EUNSUPPORTED, "device %d: the no-allocation entry point keeps scratch for "
+                                     "devices 0..%d", dev, QD_MAX_DEVICES - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(QD_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return QD_OK;
+}
+
+extern "C" size_t qd_attn_noalloc_max_bytes(void) { return QD_NOALLOC_SCRATCH_BYTES; }
+
+extern "C" int qd_attn_decode_noalloc(const qd_attn_args* a, qd_stream stream)
+{
+    QD_TRY(attn_validate<false>(a, 1.f, 1.f));
+    if (a->B == 0)
+        return QD_OK;
+    AttnGeom geo;
+    const size_t need = attn_ws_layout(a->B, a->nq, a->nkv, a->head_dim, a->max_kv_len, &geo);
+    if (need > QD_NOALLOC_SCRATCH_BYTES)
+        return fail(QD_EUNSUPPORTED, "these sizes need %zu bytes of split partials, above the %zu bytes "
+                                     "of the no-allocation entry point's scratch (use qd_attn_decode "
+                                     "with a workspace)", need, QD_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    QD_TRY(noalloc_scratch(&ws));
+    return attn_decode_impl<false>(a, 1.f, 1.f, ws, QD_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 extern "C" int qd_check(qd_model* m, qd_stream stream)
