@@ -28,7 +28,8 @@ Also reported, on the same JSON line:
                 attention at the four cases (f16 and fp8 caches) (graphs of
                 100 launches over >= 1 GiB of rotated copies, each output
                 checked against the f64 oracle, the oracle's host time beside
-                it), and greedy decode at the Qwen3-0.6B shape.
+                it), greedy decode at the Qwen3-0.6B shape, and batched decode
+                of 4, 8 and 16 sequences at the benchmarked shape.
 
 Usage: python bench.py [--gpus 1] [--steps 448] [--warmup 16] [--no-rows]
 """
@@ -419,6 +420,55 @@ def decode_row(config: str, warmup: int = 16):
                               "unit": "GB/s", "bytes_per_step": round(mean_bytes)}}
 
 
+def batch_decode_rows(mi, batches=(4, 8, 16), prompt: int = 512, warmup: int = 8, steps: int = 64):
+    """Batched greedy decode at the model's shape (qd_create_batch): B
+    sequences with their own seeded prompts of `prompt` tokens, prefilled by
+    sequential batched steps, then `warmup` untimed and `steps` timed batched
+    steps (graph replays, no host sync).  Aggregate tok/s = B * steps / time;
+    paged K/V with a shuffled table per sequence."""
+    import torch
+    import token_decode_q4_amd as qd
+    s = mi.shape
+    out = []
+    max_seq = prompt + warmup + steps
+    need = (max_seq + 15) // 16
+    for B in batches:
+        rng = np.random.default_rng(1000 + B)
+        table = rng.permutation(B * need).astype(np.int32).reshape(B, need)
+        m = qd.Model(mi, batch=B, paged=True, max_seq=max_seq, block_table=table, num_kv_blocks=B * need)
+        for b in range(B):
+            m.set_prompt_seq(b, rng.integers(0, s.vocab, size=prompt).astype(np.int32))
+        m.generate_batch([0] * B, prompt - 1 + warmup)
+        torch.cuda.synchronize()
+        pos = prompt - 1 + warmup
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        m.generate_batch([pos] * B, steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        m.check()
+        m.close()
+        del m
+        torch.cuda.empty_cache()
+        # bytes of a batched step: the weights once, each sequence's K/V (its
+        # reads at its kv_len and its one written position)
+        kv_w = s.layers * s.n_kv * s.head_dim * 2 * 2
+        kv_seq = float(np.mean([step_bytes(s, k) - step_bytes(s, 0) for k in range(pos + 1, pos + steps + 1)])) + kv_w
+        step_b = step_bytes(s, 0) - kv_w + B * kv_seq
+        gbs = step_b / (ms * 1e-3 / steps) / 1e9
+        out.append({"batch": B, "workload": f"{s.name} {B} sequences, {prompt}-token prompts, positions "
+                                            f"{pos}..{pos + steps - 1}", "steps": steps,
+                    "ms_per_step": round(ms / steps, 4), "tok_s": round(B * steps / (ms * 1e-3), 1),
+                    "step_bytes": round(step_b), "achieved_gbs": round(gbs, 1),
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)})
+        log(f"batched decode B={B}: {out[-1]['ms_per_step']} ms/step, {out[-1]['tok_s']} tok/s aggregate, "
+            f"{gbs:.0f} GB/s")
+    return out
+
+
 def read_ceiling(nbytes: int, reps: int = 100, min_bytes: int = 1 << 30):
     """The measured ceiling the GEMV is compared with: qd_stream_read (plain
     128-bit non-temporal loads, nothing else) over `nbytes` per launch, the
@@ -553,6 +603,8 @@ def main():
                     help="1: one persistent kernel launch per layer (qd_config.layer_kernel)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="print only the prefill row (chunked vs sequential) of --config")
+    ap.add_argument("--batch-only", action="store_true",
+                    help="print only the batched decode rows (B = 4, 8, 16) of --config")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): batch-1 decode of one "
@@ -572,6 +624,9 @@ def main():
     P = s.prompt_len
     if P - 1 + args.warmup + args.steps > s.max_seq:
         sys.exit(f"warmup + steps must be <= {s.max_seq - P + 1}")
+    if args.batch_only:
+        print(json.dumps(batch_decode_rows(mi)), flush=True)
+        return
     t0 = time.time()
     model = qd.Model(mi, use_graph=True, layer_kernel=bool(args.layer_kernel), kv_fp8=args.kv_fp8,
                      k_scale=0.5, v_scale=0.125)
@@ -645,6 +700,7 @@ def main():
         for r in a_rows:
             log(f"attention {r['case']} {r['kv']}: {r['mean_us']} us, {r['achieved']} GB/s "
                 f"({r['frac']:.3f}), err {r['normwise_err_vs_oracle']:.1e}, oracle {r['oracle_s']} s")
+        bd_rows = batch_decode_rows(mi)
         d06 = decode_row("qwen3-0.6b") if args.config != "qwen3-0.6b" else None
         if d06:
             log(f"decode {d06['workload']}: {d06['tok_s']} tok/s ({d06['step_roofline']['frac']:.3f})")
@@ -652,6 +708,7 @@ def main():
                 "gemv_experts": x_row,
                 "attention": a_rows,
                 "prefill": pf_row,
+                "decode_batch": bd_rows,
                 "decode_qwen3_0.6b": d06}
         log(f"row legs {time.time() - t0:.1f}s")
     cpu = None

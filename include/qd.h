@@ -195,6 +195,45 @@ int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* d_tokens,
  * 0 .. pos0+n-1. */
 int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_last, qd_stream stream);
 
+/* Batched decode (inferencelayer cuda_llm.rs page, step_batch_inner and its
+ * batched head-to-head of the q4 GEMV arm at M = 2 .. 16 tokens;
+ * ferrum-kernels cuda_decode.rs page, batched_decode_attention): a model of
+ * `batch` sequences (2 .. 16) stepped together, every weight read once per
+ * step for all of them.  Each sequence has its own tokens, position, written
+ * prefix, greedy predictions and K/V cache: contiguous (batch copies of
+ * max_seq positions) or paged, where cfg->block_table (NULL = identity) holds
+ * batch tables of ceil(max_seq/16) entries, sequence b's at
+ * [b * ceil(max_seq/16)], all distinct and below num_kv_blocks.  Each
+ * sequence's step computes what qd_decode_step computes for it (up to f32
+ * rounding order: the RMSNorm is applied to the activations before the
+ * batched GEMV instead of after it).  Not with layer_kernel or attn_out_gate;
+ * every weight scale must satisfy |d| < 8192 (QD_EUNSUPPORTED otherwise).
+ * The one-sequence entry points (qd_decode_step, qd_set_prompt, qd_generate,
+ * qd_prefill) refuse a batched model and the batch entry points below refuse
+ * a one-sequence model (QD_EINVAL).  Synchronous; *out receives the handle. */
+int qd_create_batch(const qd_config* cfg, const qd_weights* w, int32_t batch, qd_stream stream,
+                    qd_model** out);
+
+/* qd_set_prompt for sequence `seq` of a batched model (host tokens [n] at
+ * positions 0 .. n-1, marked forced). */
+int qd_set_prompt_seq(qd_model* m, int32_t seq, const int32_t* tokens, int32_t n, qd_stream stream);
+
+/* qd_generate for all sequences of a batched model at once: sequence b runs
+ * positions pos0[b] .. pos0[b]+n_steps-1 (pos0: host int32 [batch]), each
+ * start at most one past that sequence's written prefix, with no host
+ * synchronisation.  d_tokens (device int32 [batch][n_steps] or NULL) receives
+ * every step's argmax per sequence; d_logits_last (device f32 [batch][vocab]
+ * or NULL) the logits of the last step.  QD_ERANGE for a position out of
+ * range, nothing enqueued. */
+int qd_generate_batch(qd_model* m, const int32_t* pos0, int32_t n_steps, int32_t* d_tokens,
+                      float* d_logits_last, qd_stream stream);
+
+/* qd_decode_step for all sequences of a batched model: sequence b embeds
+ * tokens[b] at position pos[b] (host int32 [batch] each).  d_logits (device
+ * f32 [batch][vocab]) and d_next (device int32 [batch]) may be NULL. */
+int qd_decode_step_batch(qd_model* m, const int32_t* tokens, const int32_t* pos, float* d_logits,
+                         int32_t* d_next, qd_stream stream);
+
 /* Standalone q4_0 GEMV (inferencelayer cuda_llm.rs page, CudaQwen3::gemv):
  * y[N] = W[N, K] x[K], W in the q4_0 layout above (device d_scales
  * [N][K/32], d_qs [N][K/32][16]), x and y device f32.  K % 32 == 0; qs and x

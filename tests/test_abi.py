@@ -270,5 +270,10 @@ def test_gemv_experts_validation(qd):
 
 def test_model_entry_points_reject_null_model(qd):
     L = qd.lib()
+    assert L.qd_set_prompt_seq(None, 0, None, 0, None) == qd._native.QD_EINVAL
+    assert L.qd_generate_batch(None, None, 1, None, None, None) == qd._native.QD_EINVAL
+    assert L.qd_decode_step_batch(None, None, None, None, None, None) == qd._native.QD_EINVAL
+    assert L.qd_create_batch(None, None, 1, None, None) == qd._native.QD_EINVAL
+    assert L.qd_create_batch(None, None, 4, None, None) == qd._native.QD_EINVAL
     assert L.qd_prefill(None, 0, 1, None, None) == qd._native.QD_EINVAL
     assert L.qd_generate(None, 0, 1, None, None, None) == qd._native.QD_EINVAL

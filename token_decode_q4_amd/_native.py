@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(HERE, "libqd.so")
 QD_OK, QD_EINVAL, QD_ERANGE, QD_ENOMEM, QD_EUNSUPPORTED, QD_EHIP = 0, -1, -2, -3, -4, -5
 
 # every function declared in include/qd.h
-EXPORTS = ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate", "qd_prefill",
+EXPORTS = ("qd_create", "qd_create_batch", "qd_set_prompt_seq", "qd_generate_batch", "qd_decode_step_batch",
+           "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate", "qd_prefill",
            "qd_gemv_q4_0", "qd_gemv_q4_0_batch", "qd_gemv_q4_0_experts", "qd_rope_inv_freq", "qd_attn_workspace_bytes",
            "qd_attn_decode_kv8", "qd_attn_decode", "qd_attn_noalloc_max_bytes", "qd_attn_decode_noalloc",
            "qd_check",
@@ -113,6 +114,15 @@ def lib():
         L.qd_stream_read_groups.argtypes = [C.c_size_t]
         L.qd_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]
         L.qd_last_error.restype = C.c_char_p
+        L.qd_create_batch.argtypes = [C.POINTER(Config), C.POINTER(Weights), C.c_int32, C.c_void_p,
+                                      C.POINTER(C.c_void_p)]
+        L.qd_set_prompt_seq.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p]
+        L.qd_generate_batch.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                        C.c_void_p]
+        L.qd_decode_step_batch.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                           C.c_void_p]
+        for n in ("qd_create_batch", "qd_set_prompt_seq", "qd_generate_batch", "qd_decode_step_batch"):
+            getattr(L, n).restype = C.c_int
         for n in ("qd_create", "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate", "qd_prefill",
                   "qd_gemv_q4_0", "qd_attn_decode", "qd_check", "qd_stream_read"):
             getattr(L, n).restype = C.c_int
@@ -248,8 +258,12 @@ class Model:
     def __init__(self, mi, use_graph: bool = True, stream=None, paged: bool | None = None,
                  max_seq: int | None = None, num_kv_blocks: int | None = None,
                  layer_kernel: bool = False, kv_fp8: bool = False, k_scale: float = 1.0,
-                 v_scale: float = 1.0):
+                 v_scale: float = 1.0, batch: int = 1, block_table=None):
+        """batch > 1: a batched model of that many sequences (qd_create_batch);
+        block_table (paged) then holds batch tables of ceil(max_seq/16) entries
+        (None: the identity)."""
         s = mi.shape
+        self.batch = int(batch)
         self.shape = s
         self.vocab = s.vocab
         self.max_seq = max_seq or s.max_seq
@@ -270,10 +284,12 @@ class Model:
         nblk_need = (self.max_seq + 15) // 16
         table = None
         if paged:
-            if len(mi.block_table) >= nblk_need:
+            if block_table is not None:
+                table = np.ascontiguousarray(block_table, dtype=np.int32).ravel()
+            elif self.batch == 1 and len(mi.block_table) >= nblk_need:
                 table = np.ascontiguousarray(mi.block_table[:nblk_need], dtype=np.int32)
-            nblocks = num_kv_blocks or (max(int(table.max()) + 1, nblk_need) if table is not None
-                                        else nblk_need)
+            need = nblk_need * self.batch
+            nblocks = num_kv_blocks or (max(int(table.max()) + 1, need) if table is not None else need)
         else:
             nblocks = 0
         w = Weights(_q4(mi.embed), _q4(mi.lm_head), fn.ctypes.data, layers)
@@ -284,9 +300,30 @@ class Model:
                      int(bool(layer_kernel)), int(bool(kv_fp8)), float(k_scale), float(v_scale),
                      int(gated))
         h = C.c_void_p()
-        check(lib().qd_create(C.byref(cfg), C.byref(w), _stream(stream), C.byref(h)))
+        if self.batch == 1:
+            check(lib().qd_create(C.byref(cfg), C.byref(w), _stream(stream), C.byref(h)))
+        else:
+            check(lib().qd_create_batch(C.byref(cfg), C.byref(w), self.batch, _stream(stream), C.byref(h)))
         self._h = h
         del keep
+
+    # batched model (batch > 1)
+    def set_prompt_seq(self, seq: int, tokens, stream=None):
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        return check(lib().qd_set_prompt_seq(self._h, int(seq), t.ctypes.data, t.size, _stream(stream)))
+
+    def generate_batch(self, pos0, n_steps: int, tokens=None, logits_last=None, stream=None):
+        """Every sequence b runs positions pos0[b] .. pos0[b]+n_steps-1;
+        tokens: device int32 [batch, n_steps]; logits_last: device f32 [batch, vocab]."""
+        p = np.ascontiguousarray(pos0, dtype=np.int32)
+        return check(lib().qd_generate_batch(self._h, p.ctypes.data, int(n_steps), _ptr(tokens),
+                                             _ptr(logits_last), _stream(stream)))
+
+    def decode_step_batch(self, tokens, pos, logits=None, next_tok=None, stream=None):
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        p = np.ascontiguousarray(pos, dtype=np.int32)
+        return check(lib().qd_decode_step_batch(self._h, t.ctypes.data, p.ctypes.data, _ptr(logits),
+                                                _ptr(next_tok), _stream(stream)))
 
     def decode_step(self, token: int, pos: int, logits=None, next_tok=None, stream=None):
         return check(lib().qd_decode_step(self._h, int(token), int(pos), _ptr(logits),

@@ -70,6 +70,10 @@ struct AttnParams {
     // 1: every sequence b reads the cache of sequence 0 (the B queries of a
     // prefill chunk over one cache, each with its own kv_len)
     int shared_kv;
+    // decode step of B sequences (QMODE 1): sequence b's raw q|k|v at
+    // q + b * q_stride, its position at pos[b * pos_stride], its rotary
+    // factors at rope_cur + b * rope_stride (all 0 for one sequence)
+    int q_stride, pos_stride, rope_stride;
 };
 
 constexpr int ATT_WK = 16;                 // keys per wave step (one paged block)
@@ -338,11 +342,13 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
 
     // kv_len first (vector loads return in order): the loads below do not need
     // it.  One load from a selected address, so nothing waits for it here.
-    const int32_t* kvp = p.kv_lens ? p.kv_lens + b : p.pos;
+    const int32_t* kvp = p.kv_lens ? p.kv_lens + b : p.pos + (size_t)b * p.pos_stride;
     const int kv_raw = *kvp;
 
     // ---- loads that do not need kv_len: the token's q|k|v, norm weights,
     // rotary factors, and (decode step) the first step's K/V
+    const float* qb = p.q + (size_t)b * p.q_stride;              // QMODE 1: this sequence's q|k|v
+    const float* rc = p.rope_cur + (size_t)b * p.rope_stride;    // QMODE 1: its rotary factors
     float qv[GQ][DPL], kv_[DPL], vv[DPL], wq[DPL], wk[DPL], cs[DPL], sn[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
@@ -350,19 +356,19 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
 #pragma unroll
         for (int j = 0; j < GQ; ++j)
             qv[j][e] = (QMODE == 0) ? ld_f32<FUSED>(p.q + ((size_t)b * p.nq + h0 + j) * HD + d)
-                                    : ld_f32<FUSED>(p.q + (size_t)(h0 + j) * HD + d);
+                                    : ld_f32<FUSED>(qb + (size_t)(h0 + j) * HD + d);
         kv_[e] = vv[e] = 0.f;
         wq[e] = wk[e] = cs[e] = 1.f;
         sn[e] = 0.f;
         if (QMODE == 1) {
             // q_norm / k_norm / rope_cur always point at valid arrays here
-            kv_[e] = ld_f32<FUSED>(p.q + ((size_t)p.nq + g) * HD + d);
-            vv[e] = ld_f32<FUSED>(p.q + ((size_t)p.nq + p.nkv + g) * HD + d);
+            kv_[e] = ld_f32<FUSED>(qb + ((size_t)p.nq + g) * HD + d);
+            vv[e] = ld_f32<FUSED>(qb + ((size_t)p.nq + p.nkv + g) * HD + d);
             wq[e] = p.q_norm[d];
             wk[e] = p.k_norm[d];
             const int half = p.rot / 2;
             const int ii = d < half ? d : (d < p.rot ? d - half : 0);
-            const float c0 = p.rope_cur[ii], s0 = p.rope_cur[half + ii];
+            const float c0 = rc[ii], s0 = rc[half + ii];
             cs[e] = d < p.rot ? c0 : 1.f;
             sn[e] = d < p.rot ? s0 : 0.f;
         }

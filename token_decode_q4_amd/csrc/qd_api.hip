@@ -17,6 +17,7 @@
 #include "gemv_batch_mfma.h"
 #include "gemv_experts.h"
 #include "prefill_kernels.h"
+#include "step_batch.h"
 #include "stream_read.h"
 
 #include <algorithm>
@@ -83,6 +84,11 @@ static hipError_t launch_gemv_plain(const uint16_t* d, const uint8_t* q, const f
     return hipGetLastError();
 }
 
+// Y[b] = W X[b] for b < B (1 <= B <= 16) through the batched GEMV kernels
+// (defined with qd_gemv_q4_0_batch below)
+static hipError_t gemv_batch_launch(const uint16_t* d, const uint8_t* q, const float* x, float* y, int N, int K,
+                                    int B, hipStream_t s);
+
 // ------------------------------------------------------------------ model
 
 struct DevQ4 {
@@ -100,6 +106,16 @@ struct DevLayer {
 struct qd_model {
     int H, L, nq, nkv, hd, I, V, rot, qkv_rows, max_seq, qk_norm, paged, nblocks;
     float eps;
+    // sequences stepped together (qd_create_batch; 1 for qd_create) and the
+    // written prefix of each (see hw below)
+    int B = 1;
+    std::vector<int> hwb;
+    int rstride = 2;                  // floats of rotary factors per sequence
+    // buffers of the batched step ([B] rows each)
+    float *bx = nullptr, *bh = nullptr, *bqkv = nullptr, *battn = nullptr, *bo = nullptr;
+    float *bgu = nullptr, *bact = nullptr, *blog = nullptr, *bcval = nullptr;
+    int32_t* bcidx = nullptr;
+    int bG = 1, bchunk = 1;
     // the written prefix of the KV cache: positions 0 .. hw hold K/V of the
     // current sequence (-1: none).  A step at p writes p and makes [0, p] the
     // prefix; a step may start at most one position past it.
@@ -259,7 +275,7 @@ static void free_model(qd_model* m)
     delete m;
 }
 
-static int validate_config(const qd_config* c, const qd_weights* w)
+static int validate_config(const qd_config* c, const qd_weights* w, int B)
 {
     if (!c || !w)
         return fail(QD_EINVAL, "null config or weights");
@@ -294,12 +310,14 @@ static int validate_config(const qd_config* c, const qd_weights* w)
     if (c->kv_paged) {
         if (c->kv_block_size != ATT_BS)
             return fail(QD_EUNSUPPORTED, "kv_block_size %d (only %d)", c->kv_block_size, ATT_BS);
+        // B sequences: B tables of `need` entries, all distinct
         const int need = (c->max_seq + ATT_BS - 1) / ATT_BS;
-        if (c->num_kv_blocks < need)
-            return fail(QD_EINVAL, "num_kv_blocks %d < %d blocks for max_seq", c->num_kv_blocks, need);
+        if ((int64_t)c->num_kv_blocks < (int64_t)need * B)
+            return fail(QD_EINVAL, "num_kv_blocks %d < %d blocks for max_seq x %d sequences", c->num_kv_blocks,
+                        need * B, B);
         if (c->block_table) {
             std::vector<char> seen(c->num_kv_blocks, 0);
-            for (int i = 0; i < need; ++i) {
+            for (int i = 0; i < need * B; ++i) {
                 const int p = c->block_table[i];
                 if (p < 0 || p >= c->num_kv_blocks)
                     return fail(QD_EINVAL, "block_table[%d] = %d out of range", i, p);
@@ -345,6 +363,27 @@ static int validate_config(const qd_config* c, const qd_weights* w)
         return fail(QD_EINVAL, "attn_out_gate %d (0 or 1)", c->attn_out_gate);
     if (c->attn_out_gate && c->layer_kernel)
         return fail(QD_EUNSUPPORTED, "attn_out_gate with layer_kernel = 1");
+    if (B > 1 && (c->layer_kernel || c->attn_out_gate))
+        return fail(QD_EUNSUPPORTED, "a batched model supports neither layer_kernel nor attn_out_gate");
+    if (B > 1) {
+        // the matrix-core batched GEMV forms (code - 8) * d in f16
+        auto scales_ok = [](const qd_q4_0& q) {
+            const size_t n = (size_t)q.rows * (q.cols / 32);
+            for (size_t i = 0; i < n; ++i)
+                if ((q.d[i] & 0x7fff) >= 0x7000)   // |d| >= 8192, infinity or NaN
+                    return false;
+            return true;
+        };
+        bool ok = scales_ok(w->embed) && (c->tied || scales_ok(w->lm_head));
+        for (int l = 0; ok && l < c->layers; ++l) {
+            const qd_layer_weights& L = w->layers[l];
+            ok = scales_ok(L.wq) && scales_ok(L.wk) && scales_ok(L.wv) && scales_ok(L.wo) &&
+                 scales_ok(L.wgate) && scales_ok(L.wup) && scales_ok(L.wdown);
+        }
+        if (!ok)
+            return fail(QD_EUNSUPPORTED, "a batched model needs every weight scale |d| < 8192 "
+                                         "(the matrix-core GEMV forms (code - 8) * d in f16)");
+    }
     if (c->kv_fp8) {
         if (!(c->k_scale > 0.f) || !(c->v_scale > 0.f) || !std::isfinite(c->k_scale) ||
             !std::isfinite(c->v_scale))
@@ -445,8 +484,77 @@ static int enqueue_step_fused(qd_model* m, hipStream_t s)
     return QD_OK;
 }
 
+// One step of the B sequences of a batched model: every weight read once for
+// all of them (gemv_batch_launch), the attention over the B caches with each
+// sequence's own position, the norms and SwiGLU as small kernels per sequence
+// (step_batch.h), the greedy pick per sequence.
+static int enqueue_step_batch(qd_model* m, hipStream_t s)
+{
+    const int B = m->B, H = m->H, nqd = m->nq * m->hd, I = m->I;
+    hipLaunchKernelGGL(k_embed_batch, dim3(B), dim3(SB_THREADS), 0, s, m->embed.d, m->embed.qs, H, m->V, m->st,
+                       m->ids, m->max_seq, m->layers[0].attn_norm, m->eps, m->bx, m->bh, m->rope_cos,
+                       m->rope_sin, m->rot / 2, m->rope_cur, m->rstride);
+    for (int l = 0; l < m->L; ++l) {
+        DevLayer& Ly = m->layers[l];
+        HIP_TRY(gemv_batch_launch(Ly.qkv.d, Ly.qkv.qs, m->bh, m->bqkv, Ly.qkv.rows, H, B, s));
+        AttnParams p;
+        memset(&p, 0, sizeof p);
+        p.q = m->bqkv;
+        p.q_stride = m->qkv_rows;
+        p.k = Ly.kc;
+        p.v = Ly.vc;
+        p.tables = m->paged ? m->table : nullptr;
+        p.mbps = (m->max_seq + ATT_BS - 1) / ATT_BS;
+        p.kv_lens = nullptr;
+        p.pos = &m->st->pos;
+        p.pos_stride = sizeof(StepState) / sizeof(int32_t);
+        p.max_kv = m->max_seq;
+        p.nq = m->nq;
+        p.nkv = m->nkv;
+        p.scale = 1.0f / sqrtf((float)m->hd);
+        p.chunk = m->attn_chunk;
+        p.nsplit = m->attn_nsplit;
+        p.part = m->attn_part;
+        p.out = m->battn;
+        p.qk_norm = m->qk_norm;
+        p.q_norm = m->qk_norm ? Ly.q_norm : m->ones_hd;   // read either way
+        p.k_norm = m->qk_norm ? Ly.k_norm : m->ones_hd;
+        p.eps = m->eps;
+        p.rot = m->rot;
+        p.rope_cur = m->rope_cur;
+        p.rope_stride = m->rstride;
+        p.counters = m->attn_cnt;
+        p.kc = Ly.kc;
+        p.vc = Ly.vc;
+        p.k_scale = m->k_scale;
+        p.v_scale = m->v_scale;
+        if (m->kv_fp8)
+            launch_attention<1, true>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, B, m->nq, s);
+        else
+            launch_attention<1>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, B, m->nq, s);
+        HIP_TRY(gemv_batch_launch(Ly.o.d, Ly.o.qs, m->battn, m->bo, H, nqd, B, s));
+        hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(B), dim3(SB_THREADS), 0, s, m->bx, m->bo, H, Ly.ffn_norm,
+                           m->eps, m->bh);
+        HIP_TRY(gemv_batch_launch(Ly.gu.d, Ly.gu.qs, m->bh, m->bgu, 2 * I, H, B, s));
+        hipLaunchKernelGGL(k_swiglu_batch, dim3((I + 255) / 256, B), dim3(256), 0, s, m->bgu, I, m->bact);
+        HIP_TRY(gemv_batch_launch(Ly.down.d, Ly.down.qs, m->bact, m->bo, H, I, B, s));
+        const float* wn = (l + 1 < m->L) ? m->layers[l + 1].attn_norm : m->final_norm;
+        hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(B), dim3(SB_THREADS), 0, s, m->bx, m->bo, H, wn, m->eps,
+                           m->bh);
+    }
+    HIP_TRY(gemv_batch_launch(m->lm.d, m->lm.qs, m->bh, m->blog, m->V, H, B, s));
+    hipLaunchKernelGGL(k_argmax_batch, dim3(m->bG, B), dim3(256), 0, s, m->blog, m->V, m->bchunk, m->bcval,
+                       m->bcidx);
+    hipLaunchKernelGGL(k_argmax_advance_batch, dim3(B), dim3(256), 0, s, m->bcval, m->bcidx, m->bG, m->V, m->st,
+                       m->ids, m->pred, m->max_seq);
+    HIP_TRY(hipGetLastError());
+    return QD_OK;
+}
+
 static int enqueue_step(qd_model* m, hipStream_t s)
 {
+    if (m->B > 1)
+        return enqueue_step_batch(m, s);
     if (m->fused)
         return enqueue_step_fused(m, s);
     const int H = m->H;
@@ -627,14 +735,16 @@ static int setup_fused(qd_model* m, hipStream_t s, int want)
     return QD_OK;
 }
 
-extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream stream, qd_model** out)
+static int create_model(const qd_config* cfg, const qd_weights* w, int B, qd_stream stream, qd_model** out)
 {
     if (!out)
         return fail(QD_EINVAL, "out is null");
     *out = nullptr;
-    QD_TRY(validate_config(cfg, w));
+    QD_TRY(validate_config(cfg, w, B));
     hipStream_t s = (hipStream_t)stream;
     qd_model* m = new qd_model();
+    m->B = B;
+    m->hwb.assign(B, -1);
     auto bail = [&](int rc) {
         free_model(m);
         return rc;
@@ -711,11 +821,12 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
             }
         if ((rc = upload_f32(m, &m->rope_cos, hc.data(), n, s))) return bail(rc);
         if ((rc = upload_f32(m, &m->rope_sin, hs.data(), n, s))) return bail(rc);
-        if ((rc = dev_alloc_t(m, &m->rope_cur, (size_t)2 * (half > 0 ? half : 1)))) return bail(rc);
+        m->rstride = 2 * (half > 0 ? half : 1);
+        if ((rc = dev_alloc_t(m, &m->rope_cur, (size_t)B * m->rstride))) return bail(rc);
         const std::vector<float> ones((size_t)m->hd, 1.f);
         if ((rc = upload_f32(m, &m->ones_hd, ones.data(), (size_t)m->hd, s))) return bail(rc);
-        if ((rc = dev_alloc_t(m, &m->attn_cnt, (size_t)m->nkv))) return bail(rc);
-        if (hipMemsetAsync(m->attn_cnt, 0, sizeof(unsigned) * m->nkv, s) != hipSuccess ||
+        if ((rc = dev_alloc_t(m, &m->attn_cnt, (size_t)B * m->nkv))) return bail(rc);
+        if (hipMemsetAsync(m->attn_cnt, 0, sizeof(unsigned) * B * m->nkv, s) != hipSuccess ||
             hipStreamSynchronize(s) != hipSuccess)
             return bail(fail(QD_EHIP, "attention counter clear failed"));
     }
@@ -724,7 +835,7 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
     for (int l = 0; l < m->L; ++l) {
         DevLayer& D = m->layers[l];
         const size_t n = m->paged ? (size_t)m->nblocks * m->nkv * ATT_BS * hd
-                                  : (size_t)m->nkv * m->max_seq * hd;
+                                  : (size_t)B * m->nkv * m->max_seq * hd;
         // n elements of 2 bytes (f16) or 1 byte (fp8; hd is even, so n / 2 halves)
         const size_t nh = m->kv_fp8 ? n / 2 : n;
         if ((rc = dev_alloc_t(m, &D.kc, nh))) return bail(rc);
@@ -733,12 +844,13 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
             return bail(fail(QD_EHIP, "KV cache clear failed"));
     }
     if (m->paged) {
+        // one table per sequence: [B][need]
         const int need = (m->max_seq + ATT_BS - 1) / ATT_BS;
-        std::vector<int32_t> t(need);
-        for (int i = 0; i < need; ++i)
+        std::vector<int32_t> t((size_t)B * need);
+        for (int i = 0; i < B * need; ++i)
             t[i] = c.block_table ? c.block_table[i] : i;
-        if ((rc = dev_alloc_t(m, &m->table, need))) return bail(rc);
-        if (hipMemcpyAsync(m->table, t.data(), need * sizeof(int32_t), hipMemcpyHostToDevice, s) != hipSuccess ||
+        if ((rc = dev_alloc_t(m, &m->table, (size_t)B * need))) return bail(rc);
+        if (hipMemcpyAsync(m->table, t.data(), t.size() * sizeof(int32_t), hipMemcpyHostToDevice, s) != hipSuccess ||
             hipStreamSynchronize(s) != hipSuccess)
             return bail(fail(QD_EHIP, "block table upload failed"));
     }
@@ -759,8 +871,10 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
         m->grid_lm = gemv_grid(CFG_HEAD, m->lpr_lm, m->V);
         // attention: splits over max_seq (the grid does not depend on the position),
         // about one workgroup per CU
+        // (B sequences: about two workgroups per CU over all of them)
         const int gq = m->nq / m->nkv;
-        const AttnGeom ag = attn_geom(1, m->nkv, m->max_seq, ATT_MODEL_WGS, gq <= 4 ? QD_ATT_MODEL_WAVES : 4, 0);
+        const AttnGeom ag = attn_geom(B, m->nkv, m->max_seq, B == 1 ? ATT_MODEL_WGS : 512,
+                                      gq <= 4 ? QD_ATT_MODEL_WAVES : 4, 0);
         m->attn_waves = ag.waves;
         m->attn_chunk = ag.chunk;
         m->attn_nsplit = ag.nsplit;
@@ -773,13 +887,24 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
         (rc = dev_alloc_t(m, &m->attn, nqd)) || (rc = dev_alloc_t(m, &m->act, m->I)) ||
         (rc = dev_alloc_t(m, &m->logits, m->V)) || (rc = dev_alloc_t(m, &m->arg_val, maxp)) ||
         (rc = dev_alloc_t(m, &m->arg_idx, maxp)) ||
-        (rc = dev_alloc_t(m, &m->attn_part, (size_t)m->nq * m->attn_nsplit * (hd + 2))) ||
-        (rc = dev_alloc_t(m, &m->st, 1)) || (rc = dev_alloc_t(m, &m->ids, m->max_seq)) ||
-        (rc = dev_alloc_t(m, &m->pred, m->max_seq)))
+        (rc = dev_alloc_t(m, &m->attn_part, (size_t)B * m->nq * m->attn_nsplit * (hd + 2))) ||
+        (rc = dev_alloc_t(m, &m->st, B)) || (rc = dev_alloc_t(m, &m->ids, (size_t)B * m->max_seq)) ||
+        (rc = dev_alloc_t(m, &m->pred, (size_t)B * m->max_seq)))
         return bail(rc);
-    if (hipMemsetAsync(m->st, 0, sizeof(StepState), s) != hipSuccess ||
-        hipMemsetAsync(m->ids, 0, sizeof(int32_t) * m->max_seq, s) != hipSuccess ||
-        hipMemsetAsync(m->pred, 0, sizeof(int32_t) * m->max_seq, s) != hipSuccess ||
+    if (B > 1) {
+        m->bchunk = 4096;
+        m->bG = (m->V + m->bchunk - 1) / m->bchunk;
+        const size_t Bz = B;
+        if ((rc = dev_alloc_t(m, &m->bx, Bz * H)) || (rc = dev_alloc_t(m, &m->bh, Bz * H)) ||
+            (rc = dev_alloc_t(m, &m->bqkv, Bz * m->qkv_rows)) || (rc = dev_alloc_t(m, &m->battn, Bz * nqd)) ||
+            (rc = dev_alloc_t(m, &m->bo, Bz * H)) || (rc = dev_alloc_t(m, &m->bgu, Bz * 2 * m->I)) ||
+            (rc = dev_alloc_t(m, &m->bact, Bz * m->I)) || (rc = dev_alloc_t(m, &m->blog, Bz * m->V)) ||
+            (rc = dev_alloc_t(m, &m->bcval, Bz * m->bG)) || (rc = dev_alloc_t(m, &m->bcidx, Bz * m->bG)))
+            return bail(rc);
+    }
+    if (hipMemsetAsync(m->st, 0, sizeof(StepState) * B, s) != hipSuccess ||
+        hipMemsetAsync(m->ids, 0, sizeof(int32_t) * B * m->max_seq, s) != hipSuccess ||
+        hipMemsetAsync(m->pred, 0, sizeof(int32_t) * B * m->max_seq, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)
         return bail(fail(QD_EHIP, "step buffer clear failed"));
     if ((rc = setup_fused(m, s, c.layer_kernel)))
@@ -805,6 +930,21 @@ extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream st
     return QD_OK;
 }
 
+extern "C" int qd_create(const qd_config* cfg, const qd_weights* w, qd_stream stream, qd_model** out)
+{
+    return create_model(cfg, w, 1, stream, out);
+}
+
+extern "C" int qd_create_batch(const qd_config* cfg, const qd_weights* w, int32_t batch, qd_stream stream,
+                               qd_model** out)
+{
+    if (out)
+        *out = nullptr;
+    if (batch < 2 || batch > SB_MAXB)
+        return fail(QD_EINVAL, "batch %d not in [2, %d]", batch, SB_MAXB);
+    return create_model(cfg, w, batch, stream, out);
+}
+
 extern "C" int qd_destroy(qd_model* m)
 {
     if (!m)
@@ -814,11 +954,20 @@ extern "C" int qd_destroy(qd_model* m)
     return QD_OK;
 }
 
+// entry points of one sequence refuse a batched model, and the reverse
+#define QD_ONE_SEQUENCE(m)                                                                         \
+    if ((m)->B != 1)                                                                               \
+        return fail(QD_EINVAL, "a model of %d sequences (qd_create_batch): use the batch entry points", (m)->B)
+#define QD_BATCHED(m)                                                                              \
+    if ((m)->B == 1)                                                                               \
+        return fail(QD_EINVAL, "a model of one sequence (qd_create): use the one-sequence entry points")
+
 extern "C" int qd_decode_step(qd_model* m, int32_t token, int32_t pos, float* d_logits,
                               int32_t* d_next, qd_stream stream)
 {
     if (!m)
         return fail(QD_EINVAL, "null model");
+    QD_ONE_SEQUENCE(m);
     if (token < 0 || token >= m->V)
         return fail(QD_ERANGE, "token %d not in [0, %d)", token, m->V);
     if (pos < 0 || pos >= m->max_seq)
@@ -842,6 +991,7 @@ extern "C" int qd_set_prompt(qd_model* m, const int32_t* tokens, int32_t n, qd_s
 {
     if (!m)
         return fail(QD_EINVAL, "null model");
+    QD_ONE_SEQUENCE(m);
     if (n < 0 || n > m->max_seq)
         return fail(QD_ERANGE, "prompt length %d not in [0, %d]", n, m->max_seq);
     if (n > 0 && !tokens)
@@ -864,6 +1014,7 @@ extern "C" int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* 
 {
     if (!m)
         return fail(QD_EINVAL, "null model");
+    QD_ONE_SEQUENCE(m);
     if (pos0 < 0 || n_steps < 0 || (int64_t)pos0 + n_steps > m->max_seq)
         return fail(QD_ERANGE, "positions [%d, %d) not within max_seq %d", pos0, pos0 + n_steps,
                     m->max_seq);
@@ -882,6 +1033,107 @@ extern "C" int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* 
     if (d_logits_last && n_steps > 0)
         HIP_TRY(hipMemcpyAsync(d_logits_last, m->logits, sizeof(float) * m->V,
                                hipMemcpyDeviceToDevice, s));
+    return QD_OK;
+}
+
+// ------------------------------------------------------------------ batched decode entry points
+
+extern "C" int qd_set_prompt_seq(qd_model* m, int32_t seq, const int32_t* tokens, int32_t n, qd_stream stream)
+{
+    if (!m)
+        return fail(QD_EINVAL, "null model");
+    QD_BATCHED(m);
+    if (seq < 0 || seq >= m->B)
+        return fail(QD_EINVAL, "sequence %d not in [0, %d)", seq, m->B);
+    if (n < 0 || n > m->max_seq)
+        return fail(QD_ERANGE, "prompt length %d not in [0, %d]", n, m->max_seq);
+    if (n > 0 && !tokens)
+        return fail(QD_EINVAL, "null tokens");
+    for (int i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= m->V)
+            return fail(QD_ERANGE, "token[%d] = %d not in [0, %d)", i, tokens[i], m->V);
+    hipStream_t s = (hipStream_t)stream;
+    int32_t* ids = m->ids + (size_t)seq * m->max_seq;
+    if (n > 0) {
+        HIP_TRY(hipMemcpyAsync(ids, tokens, sizeof(int32_t) * n, hipMemcpyHostToDevice, s));
+        HIP_TRY(hipStreamSynchronize(s));  // the host array may go away on return
+    }
+    hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, s, m->st + seq, ids, 0, n, -1, 0);
+    HIP_TRY(hipGetLastError());
+    return QD_OK;
+}
+
+// host checks of per-sequence start positions of n steps
+static int check_batch_positions(qd_model* m, const int32_t* pos, int32_t n_steps)
+{
+    if (!pos)
+        return fail(QD_EINVAL, "null positions");
+    for (int b = 0; b < m->B; ++b) {
+        if (pos[b] < 0 || (int64_t)pos[b] + n_steps > m->max_seq)
+            return fail(QD_ERANGE, "sequence %d: positions [%d, %d) not within max_seq %d", b, pos[b],
+                        pos[b] + n_steps, m->max_seq);
+        if (n_steps > 0 && pos[b] > m->hwb[b] + 1)
+            return fail(QD_ERANGE, "sequence %d: position %d past the written prefix: positions 0..%d hold "
+                                   "K/V, so the next step is at most at %d", b, pos[b], m->hwb[b], m->hwb[b] + 1);
+    }
+    return QD_OK;
+}
+
+extern "C" int qd_generate_batch(qd_model* m, const int32_t* pos0, int32_t n_steps, int32_t* d_tokens,
+                                 float* d_logits_last, qd_stream stream)
+{
+    if (!m)
+        return fail(QD_EINVAL, "null model");
+    QD_BATCHED(m);
+    if (n_steps < 0)
+        return fail(QD_ERANGE, "n_steps %d < 0", n_steps);
+    QD_TRY(check_batch_positions(m, pos0, n_steps));
+    hipStream_t s = (hipStream_t)stream;
+    for (int b = 0; b < m->B; ++b)
+        hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, s, m->st + b, m->ids + (size_t)b * m->max_seq,
+                           pos0[b], -1, -1, 0);
+    HIP_TRY(hipGetLastError());
+    QD_TRY(run_steps(m, n_steps, s));
+    if (n_steps > 0) {
+        for (int b = 0; b < m->B; ++b)
+            m->hwb[b] = pos0[b] + n_steps - 1;
+        if (d_tokens)
+            for (int b = 0; b < m->B; ++b)
+                HIP_TRY(hipMemcpyAsync(d_tokens + (size_t)b * n_steps, m->pred + (size_t)b * m->max_seq + pos0[b],
+                                       sizeof(int32_t) * n_steps, hipMemcpyDeviceToDevice, s));
+        if (d_logits_last)
+            HIP_TRY(hipMemcpyAsync(d_logits_last, m->blog, sizeof(float) * m->B * m->V, hipMemcpyDeviceToDevice,
+                                   s));
+    }
+    return QD_OK;
+}
+
+extern "C" int qd_decode_step_batch(qd_model* m, const int32_t* tokens, const int32_t* pos, float* d_logits,
+                                    int32_t* d_next, qd_stream stream)
+{
+    if (!m)
+        return fail(QD_EINVAL, "null model");
+    QD_BATCHED(m);
+    if (!tokens)
+        return fail(QD_EINVAL, "null tokens");
+    for (int b = 0; b < m->B; ++b)
+        if (tokens[b] < 0 || tokens[b] >= m->V)
+            return fail(QD_ERANGE, "sequence %d: token %d not in [0, %d)", b, tokens[b], m->V);
+    QD_TRY(check_batch_positions(m, pos, 1));
+    hipStream_t s = (hipStream_t)stream;
+    for (int b = 0; b < m->B; ++b)
+        hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, s, m->st + b, m->ids + (size_t)b * m->max_seq,
+                           pos[b], pos[b] + 1, pos[b], tokens[b]);
+    HIP_TRY(hipGetLastError());
+    QD_TRY(run_steps(m, 1, s));
+    for (int b = 0; b < m->B; ++b)
+        m->hwb[b] = pos[b];
+    if (d_logits)
+        HIP_TRY(hipMemcpyAsync(d_logits, m->blog, sizeof(float) * m->B * m->V, hipMemcpyDeviceToDevice, s));
+    if (d_next)
+        for (int b = 0; b < m->B; ++b)
+            HIP_TRY(hipMemcpyAsync(d_next + b, m->pred + (size_t)b * m->max_seq + pos[b], sizeof(int32_t),
+                                   hipMemcpyDeviceToDevice, s));
     return QD_OK;
 }
 
@@ -1066,25 +1318,31 @@ extern "C" int qd_gemv_q4_0_batch(const uint16_t* d_scales, const uint8_t* d_qs,
         HIP_TRY(hipGetLastError());
         return QD_OK;
     }
-    switch (B) {
-    case 1: HIP_TRY(launch_gemv_plain(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    case 2: HIP_TRY(launch_gemv_batch<2>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    case 3: HIP_TRY(launch_gemv_batch<3>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    case 4: HIP_TRY(launch_gemv_batch<4>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    case 5: HIP_TRY(launch_gemv_batch<5>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    case 6: HIP_TRY(launch_gemv_batch<6>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    case 7: HIP_TRY(launch_gemv_batch<7>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    case 8: HIP_TRY(launch_gemv_batch<8>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    case 9: HIP_TRY(launch_gemv_batch<9>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    case 10: HIP_TRY(launch_gemv_batch<10>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    case 11: HIP_TRY(launch_gemv_batch<11>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    case 12: HIP_TRY(launch_gemv_batch<12>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    case 13: HIP_TRY(launch_gemv_batch<13>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    case 14: HIP_TRY(launch_gemv_batch<14>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    case 15: HIP_TRY(launch_gemv_batch<15>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    default: HIP_TRY(launch_gemv_batch<16>(d_scales, d_qs, d_x, d_y, N, K, s)); break;
-    }
+    HIP_TRY(gemv_batch_launch(d_scales, d_qs, d_x, d_y, N, K, B, s));
     return QD_OK;
+}
+
+static hipError_t gemv_batch_launch(const uint16_t* d, const uint8_t* q, const float* x, float* y, int N, int K,
+                                    int B, hipStream_t s)
+{
+    switch (B) {
+    case 1: return launch_gemv_plain(d, q, x, y, N, K, s);
+    case 2: return launch_gemv_batch<2>(d, q, x, y, N, K, s);
+    case 3: return launch_gemv_batch<3>(d, q, x, y, N, K, s);
+    case 4: return launch_gemv_batch<4>(d, q, x, y, N, K, s);
+    case 5: return launch_gemv_batch<5>(d, q, x, y, N, K, s);
+    case 6: return launch_gemv_batch<6>(d, q, x, y, N, K, s);
+    case 7: return launch_gemv_batch<7>(d, q, x, y, N, K, s);
+    case 8: return launch_gemv_batch<8>(d, q, x, y, N, K, s);
+    case 9: return launch_gemv_batch<9>(d, q, x, y, N, K, s);
+    case 10: return launch_gemv_batch<10>(d, q, x, y, N, K, s);
+    case 11: return launch_gemv_batch<11>(d, q, x, y, N, K, s);
+    case 12: return launch_gemv_batch<12>(d, q, x, y, N, K, s);
+    case 13: return launch_gemv_batch<13>(d, q, x, y, N, K, s);
+    case 14: return launch_gemv_batch<14>(d, q, x, y, N, K, s);
+    case 15: return launch_gemv_batch<15>(d, q, x, y, N, K, s);
+    default: return launch_gemv_batch<16>(d, q, x, y, N, K, s);
+    }
 }
 
 // ------------------------------------------------------------------ expert GEMV
@@ -1294,12 +1552,16 @@ extern "C" int qd_check(qd_model* m, qd_stream stream)
     if (!m)
         return fail(QD_EINVAL, "null model");
     HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
+    std::vector<StepState> hs(m->B);
+    HIP_TRY(hipMemcpy(hs.data(), m->st, sizeof(StepState) * m->B, hipMemcpyDeviceToHost));
     int32_t err = 0;
-    HIP_TRY(hipMemcpy(&err, &m->st->error, sizeof err, hipMemcpyDeviceToHost));
+    for (const StepState& x : hs)
+        err |= x.error;
     if (err == 0)
         return QD_OK;
     const int32_t zero = 0;
-    HIP_TRY(hipMemcpy(&m->st->error, &zero, sizeof zero, hipMemcpyHostToDevice));
+    for (int b = 0; b < m->B; ++b)
+        HIP_TRY(hipMemcpy(&m->st[b].error, &zero, sizeof zero, hipMemcpyHostToDevice));
     if (err & 4)
         return fail(QD_EHIP, "a device-wide barrier of the layer kernel timed out: the steps since "
                              "the last check are invalid");
@@ -1387,6 +1649,7 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
 {
     if (!m)
         return fail(QD_EINVAL, "null model");
+    QD_ONE_SEQUENCE(m);
     if (n <= 0 || pos0 < 0 || (int64_t)pos0 + n > m->max_seq)
         return fail(QD_ERANGE, "positions [%d, %d) not in [0, %d)", pos0, pos0 + n, m->max_seq);
     if (pos0 > m->hw + 1)

@@ -1,0 +1,186 @@
+// step_batch.h -- the elementwise kernels of the decode step of B sequences
+// at once (batched decode: the inferencelayer cuda_llm.rs page, its batched
+// head-to-head of the q4 GEMV arm at M = 2 .. 16 tokens, and
+// step_batch_inner; ferrum-kernels cuda_decode.rs page,
+// batched_decode_attention).
+//
+// Each of the B sequences has its own position, stored tokens, K/V cache and
+// greedy prediction; every weight is read once per step for all of them by
+// the batched GEMVs (gemv_batch.h, gemv_batch_mfma.h), which take the
+// normalised activations whole.  So here, unlike the one-sequence step, the
+// RMSNorm is applied before the product: one workgroup per sequence adds the
+// residual, takes the mean square of the row in a fixed order and writes the
+// normalised row for the next product.
+//   k_embed_batch           x[b] = E[token_b]; h[b] = rms(x[b]) * w; rotary factors
+//   (batched q|k|v GEMV; split-KV attention over the B caches; batched o GEMV)
+//   k_resid_rmsnorm_batch   x[b] += y[b]; h[b] = rms(x[b]) * w
+//   (batched gate|up GEMV)  k_swiglu_batch: a[b][i] = silu(g) * up
+//   (batched down GEMV)     k_resid_rmsnorm_batch (next layer's or the final norm)
+//   (batched LM head)       k_argmax_batch, k_argmax_advance_batch
+#pragma once
+
+#include "step_kernels.h"
+
+namespace qd {
+
+constexpr int SB_MAXB = 16;    // sequences of a batched model
+constexpr int SB_THREADS = 1024;
+
+// sum over a workgroup of SB_THREADS threads in a fixed order (every thread
+// gets it); red >= 16 floats
+QD_DEV float sb_block_sum(float v, float* red)
+{
+    v = group_sum<WAVE>(v);
+    const int lane = threadIdx.x & (WAVE - 1), wv = threadIdx.x / WAVE;
+    __syncthreads();
+    if (lane == 0)
+        red[wv] = v;
+    __syncthreads();
+    float s = 0.f;
+    for (int i = 0; i < (int)(blockDim.x / WAVE); ++i)
+        s += red[i];
+    return s;
+}
+
+// grid B: sequence b at its position st[b].pos reads its stored token, writes
+// x[b] (the embedding row) and h[b] = x[b] / rms * w, and the rotary factors
+// of its position (cos [half] then sin [half]) at rope_cur + b * rstride.
+// A position or token out of range is recorded in st[b].error and replaced
+// by 0 (reported by qd_check).
+__global__ void __launch_bounds__(SB_THREADS)
+k_embed_batch(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, int H, int vocab,
+              StepState* __restrict__ st, const int32_t* __restrict__ ids, int max_seq,
+              const float* __restrict__ w, float eps, float* __restrict__ x, float* __restrict__ h,
+              const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int half,
+              float* __restrict__ rope_cur, int rstride)
+{
+    __shared__ float red[16];
+    const int b = blockIdx.x;
+    StepState* sb = st + b;
+    int pos = sb->pos;
+    if (pos < 0 || pos >= max_seq) {
+        if (threadIdx.x == 0) sb->error |= 2;
+        pos = 0;
+    }
+    int tok = ids[(size_t)b * max_seq + pos];
+    if (tok < 0 || tok >= vocab) {
+        if (threadIdx.x == 0) sb->error |= 1;
+        tok = 0;
+    }
+    for (int k = threadIdx.x; k < half; k += blockDim.x) {
+        rope_cur[(size_t)b * rstride + k] = rope_cos[(size_t)pos * half + k];
+        rope_cur[(size_t)b * rstride + half + k] = rope_sin[(size_t)pos * half + k];
+    }
+    const int nb = H / 32;
+    float* xb = x + (size_t)b * H;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < H; i += blockDim.x) {
+        const int bk = i >> 5, j = i & 31;
+        const size_t blk = (size_t)tok * nb + bk;
+        const uint8_t byte = Eq[blk * 16 + (j & 15)];
+        const int code = (j < 16) ? (byte & 15) : (byte >> 4);
+        const float v = (float)(code - 8) * f16_to_f32(Ed[blk]);
+        xb[i] = v;
+        ss = fmaf(v, v, ss);
+    }
+    const float inv = 1.0f / sqrtf(sb_block_sum(ss, red) / (float)H + eps);
+    for (int i = threadIdx.x; i < H; i += blockDim.x)
+        h[(size_t)b * H + i] = xb[i] * inv * w[i];   // each thread rereads its own x
+}
+
+// grid B: x[b] += y[b] (y may be null: no residual); h[b] = x[b] / rms * w
+__global__ void __launch_bounds__(SB_THREADS)
+k_resid_rmsnorm_batch(float* __restrict__ x, const float* __restrict__ y, int H,
+                      const float* __restrict__ w, float eps, float* __restrict__ h)
+{
+    __shared__ float red[16];
+    const int b = blockIdx.x;
+    float* xb = x + (size_t)b * H;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < H; i += blockDim.x) {
+        float v = xb[i];
+        if (y) {   // uniform
+            v += y[(size_t)b * H + i];
+            xb[i] = v;
+        }
+        ss = fmaf(v, v, ss);
+    }
+    const float inv = 1.0f / sqrtf(sb_block_sum(ss, red) / (float)H + eps);
+    for (int i = threadIdx.x; i < H; i += blockDim.x)
+        h[(size_t)b * H + i] = xb[i] * inv * w[i];
+}
+
+// grid (ceil(I/256), B): a[b][i] = silu(gu[b][2i]) * gu[b][2i+1] (gate and up
+// rows interleaved as in the one-sequence step)
+__global__ void __launch_bounds__(256)
+k_swiglu_batch(const float* __restrict__ gu, int I, float* __restrict__ a)
+{
+    const int b = blockIdx.y, i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < I) {
+        const float2 v = reinterpret_cast<const float2*>(gu + (size_t)b * 2 * I)[i];
+        a[(size_t)b * I + i] = v.x * __builtin_amdgcn_rcpf(1.0f + __expf(-v.x)) * v.y;
+    }
+}
+
+// (value, index) better than (bv, bi): larger value, lowest index among equals
+QD_DEV bool sb_better(float v, int32_t i, float bv, int32_t bi) { return v > bv || (v == bv && i < bi); }
+
+// stage 1 of the greedy pick, grid (G, B), 256 threads: workgroup g of
+// sequence b takes logits[b][g*chunk .. (g+1)*chunk) and writes its best
+// (value, lowest index) to cand[b * G + g]
+__global__ void __launch_bounds__(256)
+k_argmax_batch(const float* __restrict__ logits, int V, int chunk, float* __restrict__ cval,
+               int32_t* __restrict__ cidx)
+{
+    __shared__ float bv[4];
+    __shared__ int32_t bi[4];
+    const int g = blockIdx.x, b = blockIdx.y, G = gridDim.x;
+    const float* lb = logits + (size_t)b * V;
+    float best = -INFINITY;
+    int32_t bidx = 0x7fffffff;
+    const int i1 = min(V, (g + 1) * chunk);
+    for (int i = g * chunk + (int)threadIdx.x; i < i1; i += blockDim.x) {
+        const float v = lb[i];
+        if (sb_better(v, i, best, bidx)) {
+            best = v;
+            bidx = i;
+        }
+    }
+    for (int m = WAVE / 2; m >= 1; m >>= 1) {
+        const float ov = __shfl_xor(best, m, WAVE);
+        const int32_t oi = __shfl_xor(bidx, m, WAVE);
+        if (sb_better(ov, oi, best, bidx)) {
+            best = ov;
+            bidx = oi;
+        }
+    }
+    const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+    if (lane == 0) {
+        bv[wave] = best;
+        bi[wave] = bidx;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w2 = 1; w2 < (int)(blockDim.x / WAVE); ++w2)
+            if (sb_better(bv[w2], bi[w2], best, bidx)) {
+                best = bv[w2];
+                bidx = bi[w2];
+            }
+        cval[(size_t)b * G + g] = best;
+        cidx[(size_t)b * G + g] = bidx;
+    }
+}
+
+// stage 2, grid B: sequence b's greedy token from its G candidates, recorded
+// and advanced as k_argmax_advance does for one sequence
+__global__ void __launch_bounds__(256)
+k_argmax_advance_batch(const float* __restrict__ cval, const int32_t* __restrict__ cidx, int G, int vocab,
+                       StepState* __restrict__ st, int32_t* __restrict__ ids, int32_t* __restrict__ pred,
+                       int max_seq)
+{
+    const int b = blockIdx.x;
+    argmax_advance_body(cval + (size_t)b * G, cidx + (size_t)b * G, G, vocab, st + b,
+                        ids + (size_t)b * max_seq, pred + (size_t)b * max_seq, max_seq);
+}
+
+}  // namespace qd

@@ -314,10 +314,9 @@ k_gemv_lmhead(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
 // fixed-order reduction, lowest index among equal maxima), recorded as the
 // step's prediction; it becomes the stored token of the next position unless
 // that position is forced; the position advances.
-__global__ void __launch_bounds__(256)
-k_argmax_advance(const float* __restrict__ part_val, const int32_t* __restrict__ part_idx,
-                 int n_part, int vocab, StepState* __restrict__ st, int32_t* __restrict__ ids,
-                 int32_t* __restrict__ pred, int max_seq)
+QD_DEV void argmax_advance_body(const float* __restrict__ part_val, const int32_t* __restrict__ part_idx,
+                                int n_part, int vocab, StepState* __restrict__ st, int32_t* __restrict__ ids,
+                                int32_t* __restrict__ pred, int max_seq)
 {
     __shared__ float bv[4];
     __shared__ int32_t bi[4];
@@ -375,6 +374,14 @@ k_argmax_advance(const float* __restrict__ part_val, const int32_t* __restrict__
         }
         st->pos = p + 1;
     }
+}
+
+__global__ void __launch_bounds__(256)
+k_argmax_advance(const float* __restrict__ part_val, const int32_t* __restrict__ part_idx,
+                 int n_part, int vocab, StepState* __restrict__ st, int32_t* __restrict__ ids,
+                 int32_t* __restrict__ pred, int max_seq)
+{
+    argmax_advance_body(part_val, part_idx, n_part, vocab, st, ids, pred, max_seq);
 }
 
 }  // namespace qd
