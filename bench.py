@@ -604,7 +604,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="print only the prefill row (chunked vs sequential) of --config")
     ap.add_argument("--batch-only", action="store_true",
-                    help="print only the batched decode rows (B = 4, 8, 16) of --config")
+                    help="print only the batched decode rows of --config")
+    ap.add_argument("--batch-sizes", default="4,8,16", help="sequences of the batched decode rows")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): batch-1 decode of one "
@@ -625,7 +626,7 @@ def main():
     if P - 1 + args.warmup + args.steps > s.max_seq:
         sys.exit(f"warmup + steps must be <= {s.max_seq - P + 1}")
     if args.batch_only:
-        print(json.dumps(batch_decode_rows(mi)), flush=True)
+        print(json.dumps(batch_decode_rows(mi, tuple(int(b) for b in args.batch_sizes.split(",")))), flush=True)
         return
     t0 = time.time()
     model = qd.Model(mi, use_graph=True, layer_kernel=bool(args.layer_kernel), kv_fp8=args.kv_fp8,
@@ -700,7 +701,7 @@ def main():
         for r in a_rows:
             log(f"attention {r['case']} {r['kv']}: {r['mean_us']} us, {r['achieved']} GB/s "
                 f"({r['frac']:.3f}), err {r['normwise_err_vs_oracle']:.1e}, oracle {r['oracle_s']} s")
-        bd_rows = batch_decode_rows(mi)
+        bd_rows = batch_decode_rows(mi, tuple(int(b) for b in args.batch_sizes.split(",")))
         d06 = decode_row("qwen3-0.6b") if args.config != "qwen3-0.6b" else None
         if d06:
             log(f"decode {d06['workload']}: {d06['tok_s']} tok/s ({d06['step_roofline']['frac']:.3f})")

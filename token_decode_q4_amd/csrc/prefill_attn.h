@@ -1,0 +1,221 @@
+// prefill_attn.h -- causal attention of a prefill chunk with each K/V tile
+// read once for all of the chunk's queries (gfx950 matrix cores).
+//
+// The T <= 16 positions p0 .. p0+T-1 of a chunk attend over one cache: query
+// t sees keys 0 .. p0+t (inferencelayer cuda_llm.rs page, fa_prefill: a tile
+// of queries, K and V tiles staged once and shared, the causal mask inside
+// the tile; the online-softmax partials merged as in attn_reduce).
+//
+// Workgroup (split s, kv head g) owns keys [s*chunk, (s+1)*chunk) of that kv
+// head and every query row of its GQA group: T*GQ rows (t, j), row R = t*GQ
+// + j (head g*GQ + j), 16 rows per wave (wave w: rows 16w .. 16w+15), so
+// GQ waves.  Per 16-key step (one paged block) the K and V tiles are loaded
+// once into LDS and every wave uses them:
+//   S^T = K Q^T   v_mfma_f32_16x16x32_f16, M = the 16 keys, N = the wave's 16
+//                 query rows, K = 32 dims per instruction; q enters as an f16
+//                 hi + lo pair (about 22 bits), K is f16 already
+//   mask          key > p0 + t (or t >= T): -inf
+//   softmax       online per query column (max and sum over the 16 keys:
+//                 4 registers, then the 4 lane groups)
+//   O^T += V^T P  v_mfma_f32_16x16x16_f16, M = 16 dims of a tile, K = the 16
+//                 keys, N = the queries; the B operand is the softmax's own
+//                 accumulator layout (lane l: keys 4*(l/16) .. +3 of query
+//                 l%16), as an f16 hi + lo pair; V^T from a transposed LDS tile
+// The partial (m, l, acc) of every (position, head, split) goes to the
+// partials layout of k_attn_combine, which merges the active splits of each
+// query (kv_len = p0 + t + 1).
+#pragma once
+
+#include "attn_decode.h"
+
+namespace qd {
+
+typedef _Float16 fa_half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 fa_half8 __attribute__((ext_vector_type(8)));
+typedef float fa_floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int FA_KPAD = 8;   // halves of padding per K row in LDS
+constexpr int FA_VPAD = 4;   // halves of padding per transposed V row
+
+struct FaParams {
+    const float* q;           // [T][nq][HD], normed and rotated
+    const uint16_t* k;        // cache (paged [nblocks][nkv][16][HD] or contiguous [nkv][max_kv][HD])
+    const uint16_t* v;
+    const int32_t* table;     // sequence 0's block table, or nullptr (contiguous)
+    int max_kv;
+    int nq, nkv, T, p0;
+    float scale;
+    int chunk, nsplit;        // keys per split (a multiple of 16), splits
+    float* part;              // [T][nq][nsplit][HD + 2]
+};
+
+template <int HD, int GQ>
+__global__ void __launch_bounds__(GQ* WAVE) k_pf_attn(FaParams p)
+{
+    constexpr int NI = HD / 32;     // 32-dim slices (QK)
+    constexpr int NT = HD / 16;     // 16-dim tiles (PV)
+    constexpr int NTH = GQ * WAVE;
+    constexpr int KROW = HD + FA_KPAD, VROW = 16 + FA_VPAD;
+    __shared__ __align__(16) _Float16 kt[16 * KROW];    // K tile [key][dim]
+    __shared__ __align__(16) _Float16 vt[HD * VROW];    // V tile transposed [dim][key]
+    const int s = blockIdx.x, g = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+    const int c = lane & 15, kg = lane >> 4;            // query column, lane group
+    const int kv_total = p.p0 + p.T;
+    const int k_begin = s * p.chunk, k_end = min(kv_total, k_begin + p.chunk);
+    if (k_begin >= k_end)
+        return;   // uniform: no query reads this split
+
+    // this lane's query row: R = 16 w + c -> (t, j)
+    const int R = 16 * w + c, t = R / GQ, j = R % GQ, h = g * GQ + j;
+    const bool qvalid = t < p.T;
+    const int klim = qvalid ? p.p0 + t : -1;             // last key this query sees
+
+    // q as f16 hi + lo in the B layout: dims 32i + 8kg .. +7 of query row R
+    fa_half8 bhi[NI], blo[NI];
+    {
+        const float* qp = p.q + ((size_t)min(t, p.T - 1) * p.nq + h) * HD;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const float4 a = *reinterpret_cast<const float4*>(qp + 32 * i + 8 * kg);
+            const float4 b = *reinterpret_cast<const float4*>(qp + 32 * i + 8 * kg + 4);
+            const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = qvalid ? f[e] * p.scale : 0.f;
+                const _Float16 hh = (_Float16)v;
+                bhi[i][e] = hh;
+                blo[i][e] = (_Float16)(v - (float)hh);
+            }
+        }
+    }
+
+    // global loads of one 16-key tile (clamped rows, never a branch around a load)
+    constexpr int NU = (16 * HD / 8 + NTH - 1) / NTH;   // 8-half units per thread
+    uint4 kr[NU], vr[NU];
+    auto load_tile = [&](int k0) {
+        const uint16_t *kb, *vb;
+        if (p.table) {
+            const int phys = max(0, p.table[min(k0, p.max_kv - 1) / ATT_BS]);
+            const size_t base = ((size_t)phys * p.nkv + g) * ATT_BS * HD;
+            kb = p.k + base;
+            vb = p.v + base;
+        } else {
+            const size_t base = (size_t)g * p.max_kv * HD;
+            kb = p.k + base;
+            vb = p.v + base;
+        }
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int idx = min(tid + u * NTH, 16 * HD / 8 - 1);
+            const int row = idx / (HD / 8), col = (idx % (HD / 8)) * 8;
+            const size_t r = p.table ? (size_t)row : (size_t)min(k0 + row, p.max_kv - 1);
+            kr[u] = *reinterpret_cast<const uint4*>(kb + r * HD + col);
+            vr[u] = *reinterpret_cast<const uint4*>(vb + r * HD + col);
+        }
+    };
+    auto store_tile = [&] {
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int idx = tid + u * NTH;
+            if (idx < 16 * HD / 8) {
+                const int row = idx / (HD / 8), col = (idx % (HD / 8)) * 8;
+                *reinterpret_cast<uint4*>(&kt[row * KROW + col]) = kr[u];
+                const fa_half8 vv = __builtin_bit_cast(fa_half8, vr[u]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    vt[(col + e) * VROW + row] = vv[e];
+            }
+        }
+    };
+
+    float m_c = -INFINITY, l_c = 0.f;
+    fa_floatx4 acc[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+        acc[n] = fa_floatx4{0.f, 0.f, 0.f, 0.f};
+
+    load_tile(k_begin);
+    for (int k0 = k_begin; k0 < k_end; k0 += 16) {
+        __syncthreads();   // the previous step's LDS reads are done
+        store_tile();
+        __syncthreads();
+        if (k0 + 16 < k_end)   // uniform
+            load_tile(k0 + 16);
+        // S^T: keys 4kg + r of the step, query c
+        fa_floatx4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const fa_half8 a = *reinterpret_cast<const fa_half8*>(&kt[c * KROW + 32 * i + 8 * kg]);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bhi[i], sc, 0, 0, 0);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, blo[i], sc, 0, 0, 0);
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int key = k0 + 4 * kg + r;
+            sc[r] = (key <= klim && key < k_end) ? sc[r] : -INFINITY;
+            mx = fmaxf(mx, sc[r]);
+        }
+        {
+            float lo, hi;
+            lanes::swap16(mx, lo, hi);
+            mx = fmaxf(lo, hi);
+            lanes::swap32(mx, lo, hi);
+            mx = fmaxf(lo, hi);
+        }
+        const float mnew = fmaxf(m_c, mx);
+        // a query with no key in this step so far keeps everything at zero
+        const bool none = mnew == -INFINITY;
+        float pr[4], ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pr[r] = none ? 0.f : expf(sc[r] - mnew);   // 0 for a masked key
+            ps += pr[r];
+        }
+        {
+            float lo, hi;
+            lanes::swap16(ps, lo, hi);
+            ps = lo + hi;
+            lanes::swap32(ps, lo, hi);
+            ps = lo + hi;
+        }
+        const float alpha = (m_c == -INFINITY) ? 0.f : expf(m_c - mnew);
+        l_c = fmaf(l_c, alpha, ps);
+        m_c = mnew;
+        fa_half4 phi, plo;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const _Float16 hh = (_Float16)pr[r];
+            phi[r] = hh;
+            plo[r] = (_Float16)(pr[r] - (float)hh);
+        }
+        // O^T tile n: dims 16n + 4kg + i of query c
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const fa_half4 a = *reinterpret_cast<const fa_half4*>(&vt[(16 * n + c) * VROW + 4 * kg]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[n][i] *= alpha;
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, phi, acc[n], 0, 0, 0);
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, plo, acc[n], 0, 0, 0);
+        }
+    }
+
+    // the partial of (position t, head h, split s)
+    if (qvalid) {
+        const size_t pstride = HD + 2;
+        float* pp = p.part + (((size_t)t * p.nq + h) * p.nsplit + s) * pstride;
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                pp[16 * n + 4 * kg + i] = acc[n][i];
+        if (kg == 0) {
+            pp[HD] = m_c;
+            pp[HD + 1] = l_c;
+        }
+    }
+}
+
+}  // namespace qd

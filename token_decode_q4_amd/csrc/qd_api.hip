@@ -17,6 +17,7 @@
 #include "gemv_batch_mfma.h"
 #include "gemv_experts.h"
 #include "prefill_kernels.h"
+#include "prefill_attn.h"
 #include "step_batch.h"
 #include "stream_read.h"
 
@@ -125,6 +126,7 @@ struct qd_model {
         float *X = nullptr, *QKV = nullptr, *Q = nullptr, *O = nullptr, *hf = nullptr, *A = nullptr;
         _Float16 *XP1 = nullptr, *XP2 = nullptr;   // split activations (prefill_gemm.h)
         float *XS1 = nullptr, *XS2 = nullptr;      // their per-position scales
+        float* fa = nullptr;                       // k_pf_attn partials [T][nq][FA_MAXS][hd + 2]
         int32_t *lens = nullptr, *iota = nullptr;
         float* ws = nullptr;
         AttnGeom geo;
@@ -1615,6 +1617,51 @@ static hipError_t pf_gemm(const DevQ4& W, const _Float16* XP, const float* XS, i
     return hipGetLastError();
 }
 
+// Chunk attention with each K/V tile read once for the chunk's queries
+// (k_pf_attn, f16 caches): about 256 workgroups over the keys 0 .. p0+T-1,
+// at most PF_FA_MAXS splits of a multiple of 16 keys, then the combine.
+constexpr int PF_FA_MAXS = 64;
+static void pf_attention(qd_model* m, DevLayer& Ly, int p0, int T, hipStream_t s)
+{
+    auto& P = m->pf;
+    const int kv_total = p0 + T, gq = m->nq / m->nkv;
+    const int target = std::max(1, 256 / m->nkv);
+    int chunk = (kv_total + target - 1) / target;
+    chunk = std::max(chunk, (kv_total + PF_FA_MAXS - 1) / PF_FA_MAXS);
+    chunk = std::max(16, (chunk + 15) / 16 * 16);
+    const int nsplit = (kv_total + chunk - 1) / chunk;
+    FaParams f;
+    f.q = P.Q;
+    f.k = Ly.kc;
+    f.v = Ly.vc;
+    f.table = m->paged ? m->table : nullptr;
+    f.max_kv = m->max_seq;
+    f.nq = m->nq;
+    f.nkv = m->nkv;
+    f.T = T;
+    f.p0 = p0;
+    f.scale = 1.0f / sqrtf((float)m->hd);
+    f.chunk = chunk;
+    f.nsplit = nsplit;
+    f.part = P.fa;
+    const dim3 grid(nsplit, m->nkv), block(gq * WAVE);
+#define QD_FA(HD_)                                                                                 \
+    switch (gq) {                                                                                  \
+    case 1: hipLaunchKernelGGL((k_pf_attn<HD_, 1>), grid, block, 0, s, f); break;                  \
+    case 2: hipLaunchKernelGGL((k_pf_attn<HD_, 2>), grid, block, 0, s, f); break;                  \
+    case 4: hipLaunchKernelGGL((k_pf_attn<HD_, 4>), grid, block, 0, s, f); break;                  \
+    default: hipLaunchKernelGGL((k_pf_attn<HD_, 8>), grid, block, 0, s, f); break;                 \
+    }                                                                                              \
+    hipLaunchKernelGGL((k_attn_combine<HD_>), dim3(m->nq, T), dim3(ATT_CNT), 0, s, P.fa, nsplit, chunk, \
+                       P.lens, (const int32_t*)nullptr, m->max_seq, m->nq, P.O);
+    if (m->hd == 128) {
+        QD_FA(128)
+    } else {
+        QD_FA(64)
+    }
+#undef QD_FA
+}
+
 static int pf_setup(qd_model* m)
 {
     if (m->pf.ready)
@@ -1628,6 +1675,7 @@ static int pf_setup(qd_model* m)
         (rc = dev_alloc_t(m, &P.Q, T * nqd)) || (rc = dev_alloc_t(m, &P.O, T * nqd)) ||
         (rc = dev_alloc_t(m, &P.XP1, T * kx * 2)) || (rc = dev_alloc_t(m, &P.XP2, T * (size_t)m->I * 2)) ||
         (rc = dev_alloc_t(m, &P.A, T * (size_t)m->I)) || (rc = dev_alloc_t(m, &P.XS1, T)) ||
+        (rc = dev_alloc_t(m, &P.fa, T * nqd / m->hd * PF_FA_MAXS * (m->hd + 2))) ||
         (rc = dev_alloc_t(m, &P.XS2, T)) ||
         (rc = dev_alloc_t(m, &P.hf, (size_t)m->H)) || (rc = dev_alloc_t(m, &P.lens, T)) ||
         (rc = dev_alloc_t(m, &P.iota, (size_t)m->V)) || (rc = dev_alloc_t(m, &P.ws, ws / sizeof(float) + 1)))
@@ -1685,29 +1733,31 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
                 if (m->kv_fp8) QD_PFQK(64, true); else QD_PFQK(64, false);
             }
 #undef QD_PFQK
-            AttnParams p;
-            memset(&p, 0, sizeof p);
-            p.q = P.Q;
-            p.k = Ly.kc;
-            p.v = Ly.vc;
-            p.tables = tbl;
-            p.mbps = mbps;
-            p.kv_lens = P.lens;
-            p.max_kv = m->max_seq;
-            p.nq = m->nq;
-            p.nkv = m->nkv;
-            p.scale = 1.0f / sqrtf((float)hd);
-            p.chunk = P.geo.chunk;
-            p.nsplit = P.geo.nsplit;
-            p.part = P.ws;
-            p.out = P.O;
-            p.k_scale = m->k_scale;
-            p.v_scale = m->v_scale;
-            p.shared_kv = 1;
-            if (m->kv_fp8)
+            if (m->kv_fp8) {
+                // fp8 cache: the decode attention, each query of the chunk as a sequence
+                AttnParams p;
+                memset(&p, 0, sizeof p);
+                p.q = P.Q;
+                p.k = Ly.kc;
+                p.v = Ly.vc;
+                p.tables = tbl;
+                p.mbps = mbps;
+                p.kv_lens = P.lens;
+                p.max_kv = m->max_seq;
+                p.nq = m->nq;
+                p.nkv = m->nkv;
+                p.scale = 1.0f / sqrtf((float)hd);
+                p.chunk = P.geo.chunk;
+                p.nsplit = P.geo.nsplit;
+                p.part = P.ws;
+                p.out = P.O;
+                p.k_scale = m->k_scale;
+                p.v_scale = m->v_scale;
+                p.shared_kv = 1;
                 launch_attention<0, true>(p, P.geo.waves, hd, gq, m->paged, T, m->nq, s);
-            else
-                launch_attention<0>(p, P.geo.waves, hd, gq, m->paged, T, m->nq, s);
+            } else {
+                pf_attention(m, Ly, p0, T, s);
+            }
             const int kq = m->nq * hd;
             // the gate rows follow q|k|v in the fused product
             const float* gate = m->attn_gate ? P.QKV + (size_t)(m->nq + 2 * m->nkv) * hd : nullptr;
