@@ -72,8 +72,12 @@ struct AttnParams {
     int shared_kv;
     // decode step of B sequences (QMODE 1): sequence b's raw q|k|v at
     // q + b * q_stride, its position at pos[b * pos_stride], its rotary
-    // factors at rope_cur + b * rope_stride (all 0 for one sequence)
+    // factors at rope_cur + b * rope_stride (all 0 for one sequence); the raw
+    // q|k|v may come as q_slabs partial products q_slab_stride floats apart,
+    // summed here in slab order (0 or 1: one)
     int q_stride, pos_stride, rope_stride;
+    int q_slabs;
+    size_t q_slab_stride;
 };
 
 constexpr int ATT_WK = 16;                 // keys per wave step (one paged block)
@@ -348,6 +352,12 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
     // ---- loads that do not need kv_len: the token's q|k|v, norm weights,
     // rotary factors, and (decode step) the first step's K/V
     const float* qb = p.q + (size_t)b * p.q_stride;              // QMODE 1: this sequence's q|k|v
+    auto qkv_at = [&](size_t off) {                               // QMODE 1: summed over the slabs
+        float v = ld_f32<FUSED>(qb + off);
+        for (int sl = 1; sl < p.q_slabs; ++sl)
+            v += ld_f32<FUSED>(qb + sl * p.q_slab_stride + off);
+        return v;
+    };
     const float* rc = p.rope_cur + (size_t)b * p.rope_stride;    // QMODE 1: its rotary factors
     float qv[GQ][DPL], kv_[DPL], vv[DPL], wq[DPL], wk[DPL], cs[DPL], sn[DPL];
 #pragma unroll
@@ -356,14 +366,14 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
 #pragma unroll
         for (int j = 0; j < GQ; ++j)
             qv[j][e] = (QMODE == 0) ? ld_f32<FUSED>(p.q + ((size_t)b * p.nq + h0 + j) * HD + d)
-                                    : ld_f32<FUSED>(qb + (size_t)(h0 + j) * HD + d);
+                                    : qkv_at((size_t)(h0 + j) * HD + d);
         kv_[e] = vv[e] = 0.f;
         wq[e] = wk[e] = cs[e] = 1.f;
         sn[e] = 0.f;
         if (QMODE == 1) {
             // q_norm / k_norm / rope_cur always point at valid arrays here
-            kv_[e] = ld_f32<FUSED>(qb + ((size_t)p.nq + g) * HD + d);
-            vv[e] = ld_f32<FUSED>(qb + ((size_t)p.nq + p.nkv + g) * HD + d);
+            kv_[e] = qkv_at(((size_t)p.nq + g) * HD + d);
+            vv[e] = qkv_at(((size_t)p.nq + p.nkv + g) * HD + d);
             wq[e] = p.q_norm[d];
             wk[e] = p.k_norm[d];
             const int half = p.rot / 2;

@@ -103,10 +103,12 @@ struct GbmX {
     float4 xb[GbmItems<NC>::N];        //   and 16+4w .. 16+4w+3
 };
 
+// grid (row tiles, K slices): slice y takes chunks [y * kch, (y + 1) * kch)
+// and writes its partial products to Y + y * ystride (one slice: Y itself)
 template <int NC>
 __global__ void __launch_bounds__(GBM_NW* WAVE)
 k_gemv_batch_mfma(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
-                  const float* __restrict__ X, float* __restrict__ Y, int N, int nb)
+                  const float* __restrict__ X, float* __restrict__ Y, int N, int nb, int kch, size_t ystride)
 {
     static_assert(NC >= 2 && NC <= 16, "batch");
     constexpr int NITEM = GBM_KC * 4 * NC;   // staging items of a chunk
@@ -119,6 +121,8 @@ k_gemv_batch_mfma(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
     const int col = min(lane & 15, NC - 1);          // columns past NC repeat the last vector
     const int K = nb * 32;
     const int nch = (nb + GBM_KC - 1) / GBM_KC;
+    const int c0 = (int)blockIdx.y * kch, c1 = min(nch, c0 + kch);   // this slice's chunks
+    Y += (size_t)blockIdx.y * ystride;
     const int ntiles = (N + GBM_ROWS - 1) / GBM_ROWS;
     if (threadIdx.x < 2 * GBM_MAXB)
         xmax[threadIdx.x / GBM_MAXB][threadIdx.x % GBM_MAXB] = 0u;   // ordered by the first stage's barrier
@@ -231,17 +235,17 @@ k_gemv_batch_mfma(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
         };
         GbmBuf b0, b1;
         GbmX<NC> xr;
-        load(b0, 0);
-        load_x(xr, 0);
-        for (int c = 0; c < nch; c += 2) {
+        load(b0, c0);
+        load_x(xr, c0);
+        for (int c = c0; c < c1; c += 2) {
             stage(xr, c);
-            load(b1, min(c + 1, nch - 1));
-            load_x(xr, min(c + 1, nch - 1));
+            load(b1, min(c + 1, c1 - 1));
+            load_x(xr, min(c + 1, c1 - 1));
             compute(b0);
-            if (c + 1 < nch) {   // uniform
+            if (c + 1 < c1) {   // uniform
                 stage(xr, c + 1);
-                load(b0, min(c + 2, nch - 1));
-                load_x(xr, min(c + 2, nch - 1));
+                load(b0, min(c + 2, c1 - 1));
+                load_x(xr, min(c + 2, c1 - 1));
                 compute(b1);
             }
         }

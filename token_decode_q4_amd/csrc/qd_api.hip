@@ -89,6 +89,10 @@ static hipError_t launch_gemv_plain(const uint16_t* d, const uint8_t* q, const f
 // (defined with qd_gemv_q4_0_batch below)
 static hipError_t gemv_batch_launch(const uint16_t* d, const uint8_t* q, const float* x, float* y, int N, int K,
                                     int B, hipStream_t s);
+// the matrix-core batched GEMV, K in ks slices (defined below)
+template <int NC>
+static hipError_t launch_gemv_batch_mfma(const uint16_t* d, const uint8_t* q, const float* x, float* y,
+                                         int N, int nb, hipStream_t s, int ks = 1);
 
 // ------------------------------------------------------------------ model
 
@@ -117,6 +121,7 @@ struct qd_model {
     float *bgu = nullptr, *bact = nullptr, *blog = nullptr, *bcval = nullptr;
     int32_t* bcidx = nullptr;
     int bG = 1, bchunk = 1;
+    int ks_qkv = 1, ks_o = 1, ks_gu = 1, ks_down = 1;   // K slices of the batched products
     // the written prefix of the KV cache: positions 0 .. hw hold K/V of the
     // current sequence (-1: none).  A step at p writes p and makes [0, p] the
     // prefix; a step may start at most one position past it.
@@ -486,6 +491,36 @@ static int enqueue_step_fused(qd_model* m, hipStream_t s)
     return QD_OK;
 }
 
+// K slices of a batched step's product of N rows and nb blocks: the row tiles
+// of the matrix-core GEMV alone give too few workgroups for short matrices,
+// so K is cut into slices (whole 32-block chunks) up to about 256 workgroups
+static int step_kslices(int N, int nb)
+{
+    const int tiles = (N + GBM_ROWS - 1) / GBM_ROWS;
+    const int nch = (nb + GBM_KC - 1) / GBM_KC;
+    int ks = std::min({nch, SB_MAXSLAB, std::max(1, (256 + tiles / 2) / tiles)});
+    if (ks > 1) {
+        const int kch = (nch + ks - 1) / ks;
+        ks = (nch + kch - 1) / kch;
+    }
+    return ks;
+}
+
+// the batched step's product Y = W X: in ks K slices on the matrix cores
+// (partial slabs of B*N floats, summed by the consumer), or whole
+static hipError_t step_gemv(const qd_model* m, const DevQ4& W, const float* X, float* Y, int ks, hipStream_t s)
+{
+    if (ks <= 1)
+        return gemv_batch_launch(W.d, W.qs, X, Y, W.rows, W.cols, m->B, s);
+    switch (m->B) {
+#define QD_SG(NC_) case NC_: return launch_gemv_batch_mfma<NC_>(W.d, W.qs, X, Y, W.rows, W.nb, s, ks);
+    QD_SG(2) QD_SG(3) QD_SG(4) QD_SG(5) QD_SG(6) QD_SG(7) QD_SG(8) QD_SG(9)
+    QD_SG(10) QD_SG(11) QD_SG(12) QD_SG(13) QD_SG(14) QD_SG(15)
+#undef QD_SG
+    default: return launch_gemv_batch_mfma<16>(W.d, W.qs, X, Y, W.rows, W.nb, s, ks);
+    }
+}
+
 // One step of the B sequences of a batched model: every weight read once for
 // all of them (gemv_batch_launch), the attention over the B caches with each
 // sequence's own position, the norms and SwiGLU as small kernels per sequence
@@ -498,11 +533,13 @@ static int enqueue_step_batch(qd_model* m, hipStream_t s)
                        m->rope_sin, m->rot / 2, m->rope_cur, m->rstride);
     for (int l = 0; l < m->L; ++l) {
         DevLayer& Ly = m->layers[l];
-        HIP_TRY(gemv_batch_launch(Ly.qkv.d, Ly.qkv.qs, m->bh, m->bqkv, Ly.qkv.rows, H, B, s));
+        HIP_TRY(step_gemv(m, Ly.qkv, m->bh, m->bqkv, m->ks_qkv, s));
         AttnParams p;
         memset(&p, 0, sizeof p);
         p.q = m->bqkv;
         p.q_stride = m->qkv_rows;
+        p.q_slabs = m->ks_qkv;
+        p.q_slab_stride = (size_t)B * m->qkv_rows;
         p.k = Ly.kc;
         p.v = Ly.vc;
         p.tables = m->paged ? m->table : nullptr;
@@ -534,15 +571,17 @@ static int enqueue_step_batch(qd_model* m, hipStream_t s)
             launch_attention<1, true>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, B, m->nq, s);
         else
             launch_attention<1>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, B, m->nq, s);
-        HIP_TRY(gemv_batch_launch(Ly.o.d, Ly.o.qs, m->battn, m->bo, H, nqd, B, s));
-        hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(B), dim3(SB_THREADS), 0, s, m->bx, m->bo, H, Ly.ffn_norm,
-                           m->eps, m->bh);
-        HIP_TRY(gemv_batch_launch(Ly.gu.d, Ly.gu.qs, m->bh, m->bgu, 2 * I, H, B, s));
-        hipLaunchKernelGGL(k_swiglu_batch, dim3((I + 255) / 256, B), dim3(256), 0, s, m->bgu, I, m->bact);
-        HIP_TRY(gemv_batch_launch(Ly.down.d, Ly.down.qs, m->bact, m->bo, H, I, B, s));
+        const size_t slab_h = (size_t)B * H;
+        HIP_TRY(step_gemv(m, Ly.o, m->battn, m->bo, m->ks_o, s));
+        hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(B), dim3(SB_THREADS), 0, s, m->bx, m->bo, m->ks_o, slab_h,
+                           H, Ly.ffn_norm, m->eps, m->bh);
+        HIP_TRY(step_gemv(m, Ly.gu, m->bh, m->bgu, m->ks_gu, s));
+        hipLaunchKernelGGL(k_swiglu_batch, dim3((I + 255) / 256, B), dim3(256), 0, s, m->bgu, m->ks_gu,
+                           (size_t)B * 2 * I, I, m->bact);
+        HIP_TRY(step_gemv(m, Ly.down, m->bact, m->bo, m->ks_down, s));
         const float* wn = (l + 1 < m->L) ? m->layers[l + 1].attn_norm : m->final_norm;
-        hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(B), dim3(SB_THREADS), 0, s, m->bx, m->bo, H, wn, m->eps,
-                           m->bh);
+        hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(B), dim3(SB_THREADS), 0, s, m->bx, m->bo, m->ks_down,
+                           slab_h, H, wn, m->eps, m->bh);
     }
     HIP_TRY(gemv_batch_launch(m->lm.d, m->lm.qs, m->bh, m->blog, m->V, H, B, s));
     hipLaunchKernelGGL(k_argmax_batch, dim3(m->bG, B), dim3(256), 0, s, m->blog, m->V, m->bchunk, m->bcval,
@@ -896,10 +935,16 @@ static int create_model(const qd_config* cfg, const qd_weights* w, int B, qd_str
     if (B > 1) {
         m->bchunk = 4096;
         m->bG = (m->V + m->bchunk - 1) / m->bchunk;
+        m->ks_qkv = step_kslices(m->qkv_rows, H / 32);
+        m->ks_o = step_kslices(H, nqd / 32);
+        m->ks_gu = step_kslices(2 * m->I, H / 32);
+        m->ks_down = step_kslices(H, m->I / 32);
         const size_t Bz = B;
         if ((rc = dev_alloc_t(m, &m->bx, Bz * H)) || (rc = dev_alloc_t(m, &m->bh, Bz * H)) ||
-            (rc = dev_alloc_t(m, &m->bqkv, Bz * m->qkv_rows)) || (rc = dev_alloc_t(m, &m->battn, Bz * nqd)) ||
-            (rc = dev_alloc_t(m, &m->bo, Bz * H)) || (rc = dev_alloc_t(m, &m->bgu, Bz * 2 * m->I)) ||
+            (rc = dev_alloc_t(m, &m->bqkv, Bz * m->ks_qkv * m->qkv_rows)) ||
+            (rc = dev_alloc_t(m, &m->battn, Bz * nqd)) ||
+            (rc = dev_alloc_t(m, &m->bo, Bz * std::max(m->ks_o, m->ks_down) * H)) ||
+            (rc = dev_alloc_t(m, &m->bgu, Bz * m->ks_gu * 2 * m->I)) ||
             (rc = dev_alloc_t(m, &m->bact, Bz * m->I)) || (rc = dev_alloc_t(m, &m->blog, Bz * m->V)) ||
             (rc = dev_alloc_t(m, &m->bcval, Bz * m->bG)) || (rc = dev_alloc_t(m, &m->bcidx, Bz * m->bG)))
             return bail(rc);
@@ -1269,13 +1314,19 @@ static hipError_t launch_gemv_batch_l(const uint16_t* d, const uint8_t* q, const
 #endif
 constexpr int GBM_GRID_CAP = 1024;
 
+// ks > 1: K in ks slices of whole chunks, partial products to y + k * NC * N
 template <int NC>
 static hipError_t launch_gemv_batch_mfma(const uint16_t* d, const uint8_t* q, const float* x, float* y,
-                                         int N, int nb, hipStream_t s)
+                                         int N, int nb, hipStream_t s, int ks)
 {
     const int ntiles = (N + GBM_ROWS - 1) / GBM_ROWS;
-    hipLaunchKernelGGL((k_gemv_batch_mfma<NC>), dim3(std::max(1, std::min(ntiles, GBM_GRID_CAP))),
-                       dim3(GBM_NW * WAVE), gemv_batch_mfma_lds_bytes(NC), s, d, q, x, y, N, nb);
+    const int nch = (nb + GBM_KC - 1) / GBM_KC;
+    const int kch = (nch + ks - 1) / ks;
+    if (ks < 1 || (int64_t)(ks - 1) * kch >= nch)   // every slice holds at least one chunk
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemv_batch_mfma<NC>), dim3(std::max(1, std::min(ntiles, GBM_GRID_CAP)), ks),
+                       dim3(GBM_NW * WAVE), gemv_batch_mfma_lds_bytes(NC), s, d, q, x, y, N, nb, kch,
+                       (size_t)NC * N);
     return hipGetLastError();
 }
 

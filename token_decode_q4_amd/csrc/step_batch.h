@@ -25,6 +25,7 @@ namespace qd {
 
 constexpr int SB_MAXB = 16;    // sequences of a batched model
 constexpr int SB_THREADS = 1024;
+constexpr int SB_MAXSLAB = 4;  // K slices of a batched step's product
 
 // sum over a workgroup of SB_THREADS threads in a fixed order (every thread
 // gets it); red >= 16 floats
@@ -88,9 +89,10 @@ k_embed_batch(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, i
         h[(size_t)b * H + i] = xb[i] * inv * w[i];   // each thread rereads its own x
 }
 
-// grid B: x[b] += y[b] (y may be null: no residual); h[b] = x[b] / rms * w
+// grid B: x[b] += y[b] (y may be null: no residual; y may come as nslab
+// partial products slab floats apart, added in slab order); h[b] = x[b] / rms * w
 __global__ void __launch_bounds__(SB_THREADS)
-k_resid_rmsnorm_batch(float* __restrict__ x, const float* __restrict__ y, int H,
+k_resid_rmsnorm_batch(float* __restrict__ x, const float* __restrict__ y, int nslab, size_t slab, int H,
                       const float* __restrict__ w, float eps, float* __restrict__ h)
 {
     __shared__ float red[16];
@@ -100,7 +102,10 @@ k_resid_rmsnorm_batch(float* __restrict__ x, const float* __restrict__ y, int H,
     for (int i = threadIdx.x; i < H; i += blockDim.x) {
         float v = xb[i];
         if (y) {   // uniform
-            v += y[(size_t)b * H + i];
+            float r = y[(size_t)b * H + i];
+            for (int k = 1; k < nslab; ++k)
+                r += y[k * slab + (size_t)b * H + i];
+            v += r;
             xb[i] = v;
         }
         ss = fmaf(v, v, ss);
@@ -111,13 +116,19 @@ k_resid_rmsnorm_batch(float* __restrict__ x, const float* __restrict__ y, int H,
 }
 
 // grid (ceil(I/256), B): a[b][i] = silu(gu[b][2i]) * gu[b][2i+1] (gate and up
-// rows interleaved as in the one-sequence step)
+// rows interleaved as in the one-sequence step; gu as nslab partial products
+// slab floats apart, added in slab order)
 __global__ void __launch_bounds__(256)
-k_swiglu_batch(const float* __restrict__ gu, int I, float* __restrict__ a)
+k_swiglu_batch(const float* __restrict__ gu, int nslab, size_t slab, int I, float* __restrict__ a)
 {
     const int b = blockIdx.y, i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < I) {
-        const float2 v = reinterpret_cast<const float2*>(gu + (size_t)b * 2 * I)[i];
+        float2 v = reinterpret_cast<const float2*>(gu + (size_t)b * 2 * I)[i];
+        for (int k = 1; k < nslab; ++k) {
+            const float2 u = reinterpret_cast<const float2*>(gu + k * slab + (size_t)b * 2 * I)[i];
+            v.x += u.x;
+            v.y += u.y;
+        }
         a[(size_t)b * I + i] = v.x * __builtin_amdgcn_rcpf(1.0f + __expf(-v.x)) * v.y;
     }
 }
