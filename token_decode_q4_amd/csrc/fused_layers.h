@@ -291,7 +291,7 @@ QD_DEV void fused_gemv(const uint16_t* D, const uint8_t* Q, const float* x, int 
 #pragma unroll
                 for (int k = 0; k < 8; ++k)
                     xv[k] = xp[k];
-                const float m8 = -8.f * xs[b];
+                const float m8 = (-8.f * Q4_SUB) * xs[b];
 #pragma unroll
                 for (int r = 0; r < RPS; ++r)
                     acc[r] = fmaf(f16_to_f32((uint16_t)bf.d[g][r]), q4_block_dot(bf.q[g][r], xv) + m8,
@@ -301,7 +301,7 @@ QD_DEV void fused_gemv(const uint16_t* D, const uint8_t* Q, const float* x, int 
         if (grp == ngroups - 1) {
 #pragma unroll
             for (int r = 0; r < RPS; ++r)
-                acc[r] = group_sum<LPR>(acc[r]);
+                acc[r] = group_sum<LPR>(acc[r]) * Q4_UNSUB;
             const int row0 = tile * G::ROWS + wave * G::RPW + slot * RPS;
             epi.tile(row0, acc, lr == 0);
 #pragma unroll

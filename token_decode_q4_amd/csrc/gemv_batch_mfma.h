@@ -1,37 +1,48 @@
 // gemv_batch_mfma.h -- batched q4_0 GEMV on the matrix cores (gfx950):
-// Y[b] = W X[b] for 2 <= B <= 16 vectors, every weight read once.
+// Y[b] = W X[b] for 1 <= B <= 16 vectors, every weight read once.
 //
 // The batched decode of the inferencelayer cuda_llm.rs page (its q4 GEMV arm
 // against the bf16 GEMM arm at M = 1 .. 16 tokens, section on the batched
-// head-to-head).  With B vectors the GEMV is a skinny matrix product, so it
-// runs on v_mfma_f32_16x16x32_f16: M = 16 weight rows, N = 16 columns (the B
-// vectors, the rest discarded), K = 32.
+// head-to-head).  With B vectors the GEMV is a skinny matrix product; here it
+// runs as one v_mfma_f32_16x16x32_f16 per q4_0 block and 16 weight rows.
 //
-// Layout.  A workgroup of 4 waves owns a 64-row tile, a wave one 16-row
-// slice of it.  Lane l = (r, kg), r = l % 16, kg = l / 16, loads block
-// 4j + kg of row r whole (16 bytes; 4 lanes read 64 contiguous bytes of a
-// row).  MFMA w (w = 0..3) of group j takes from every lane its block's word
-// w: the 8 codes there (low nibbles: elements 4w..4w+3, high nibbles:
-// 16+4w..16+4w+3), so one MFMA spans the four blocks 4j..4j+3, one per lane
-// group.  Because the blocks differ in scale, the scale is part of the A
-// operand: (code - 8) * d as an f16 pair hi + lo with hi = RN((code-8)*d)
-// and lo = (code-8)*d - hi, both exact in f16 for |d| < 8192 ((code-8)*d has
-// at most 15 significant bits).  x enters as an f16 pair too, after a power
-// of two s per (vector, chunk of 32 blocks) that puts the chunk's largest
-// |x| in [2^13, 2^14): hi = RN(x s), lo = RN(x s - hi), about 22 bits at any
-// input scale and no f16 overflow.  The four products hi*hi, hi*lo, lo*hi,
-// lo*lo accumulate in f32 (every product exact); each chunk's sum is
-// multiplied by 1/s, exactly, into the result.
+// Operands.  The first operand (M = 16) is the vectors, the second (N = 16)
+// the weight rows, K = 32 = one block.  Lane l = (r, kg), r = l % 16,
+// kg = l / 16, supplies 8 values of vector r (first operand) and 8 codes of
+// weight row r (second operand), both at the K slots of lane group kg, and
+// receives the products of vectors 4kg .. 4kg+3 with row r.  A lane's outputs
+// therefore share one weight row, and the block's scale d is one number per
+// lane: each block's MFMA starts from zero and the lane adds d * P to its
+// sums (v_fma_mix_f32 takes d as an f16 half, no conversion).
 //
-// Codes to f16: (w & 0x000F000F) | 0x64006400 holds two codes as the f16
-// values 1024 + code; a packed f16 add of -1032 leaves code - 8, exactly.
+// Codes.  Lane group kg takes word kg (bytes 4kg .. 4kg+3) of the block: the
+// low nibbles are elements 4kg .. 4kg+3, the high ones 16+4kg .. 16+4kg+3.
+// (w & 0x000F000F) | 0x64006400 holds two codes as the f16 values 1024 + c,
+// (w & 0x00F000F0) | 0x64006400 two as 1024 + 16c; packed f16 adds of -1032
+// and -1152 leave c - 8 and 16(c - 8), exactly.  With t = w >> 8 the same two
+// masks give the odd elements.  K slot order of a lane group: 4kg, 4kg+2,
+// 4kg+1, 4kg+3, then the same four plus 16; x of the high four is staged
+// divided by 16 (exact).  Each lane loads 16 bytes (one block of its row) per
+// 4 blocks; a 4 x 4 transpose of words across the lane groups (v_permlane32
+// and v_permlane16 swaps) gives every lane group its word of each of the
+// four blocks.  The 8 f16 scales of a lane group's eighth of a 32-block chunk
+// come with one 16-byte load and are shared by the same swaps.
 //
-// x is staged per chunk of 32 blocks in LDS, already in the B-operand
-// layout: [block][word][vector][8 hi, 8 lo] halves.  The weight loads (two
-// register buffers, the chunk loop unrolled by two) and the x loads (one
-// buffer, refilled as soon as it is staged) of the next chunk are issued
-// before the current one is computed, so staging a chunk is conversions and
-// LDS writes only.
+// x enters as an f16 pair after a power of two s per (vector, chunk of 32
+// blocks) that puts the chunk's largest |x| in [2^13, 2^14): hi = RN(x s),
+// lo = RN(x s - hi), about 22 significant bits at any input scale, no f16
+// overflow.  Both pairs meet the same codes (two MFMAs per block, products
+// exact in f32); each chunk's sums are multiplied by 1/s, exactly.  x is
+// staged per chunk in LDS in the first operand's layout
+// [block][lane group][hi, lo][vector][8 halves].  All weight loads of a chunk
+// (one 16-byte load per lane, row group and step of 4 blocks) are in flight
+// before the chunk is staged; the next chunk's x, scales and weights are
+// issued while the current one is computed.
+//
+// Grid (row tiles, K slices): slice y takes chunks [y * kch, (y + 1) * kch)
+// and writes its partial products to Y + y * ystride.  A workgroup of 4 waves
+// owns 64 * RG rows (RG groups of 16 per wave).  dvec: the scales may be
+// loaded 16 bytes at a time (nb % 8 == 0 and D 16-byte aligned).
 #pragma once
 
 #include "qd_common.h"
@@ -42,38 +53,66 @@ typedef _Float16 gbm_half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 gbm_half2 __attribute__((ext_vector_type(2)));
 typedef float gbm_floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int GBM_MAXB = 16;   // vectors per launch
-constexpr int GBM_KC = 32;     // blocks per staged chunk
-constexpr int GBM_NW = 4;      // waves per workgroup
-constexpr int GBM_ROWS = 64;   // rows per workgroup tile
+constexpr int GBM_MAXB = 16;              // vectors per launch
+constexpr int GBM_KC = 32;                // blocks per staged chunk
+constexpr int GBM_NW = 4;                 // waves per workgroup
+constexpr int GBM_STEPS = GBM_KC / 4;     // 4-block steps per chunk
 
-// LDS bytes of one staged chunk of B vectors
-__host__ __device__ constexpr size_t gemv_batch_mfma_lds_bytes(int B)
+// rows per workgroup with RG row groups per wave
+__host__ __device__ constexpr int gbm_rows(int rg) { return GBM_NW * 16 * rg; }
+
+// LDS bytes of one staged chunk (16 vector slots)
+__host__ __device__ constexpr size_t gemv_batch_mfma_lds_bytes()
 {
-    return (size_t)GBM_KC * 4 * B * 16 * sizeof(_Float16);
+    return (size_t)GBM_KC * 4 * 2 * 16 * 8 * sizeof(_Float16);
 }
 
-// Element (within its block) of position e (0..7) of word w in both operands:
-// e -> 16*(e/4) + 4w + (0, 2, 1, 3)[e%4]
-QD_DEV int gbm_elem(int w, int e) { return 16 * (e >> 2) + 4 * w + ((e & 1) << 1) + ((e >> 1) & 1); }
-
-// (code - 8) * d of word w as the f16 pair (hi, lo), in gbm_elem order
-QD_DEV void gbm_a_operand(uint32_t w, gbm_half2 d2, gbm_half8& hi, gbm_half8& lo)
+// 4 x 4 transpose of words across the lane groups: before, lane group g holds
+// word w of block g in w[w]; after, lane group g holds word g of block b in w[b]
+QD_DEV void gbm_transpose4(uint32_t (&w)[4])
 {
-    const uint32_t m = 0x000F000Fu, bias = 0x64006400u;
-    const uint32_t t[4] = {(w & m) | bias, ((w >> 8) & m) | bias, ((w >> 4) & m) | bias,
-                           ((w >> 12) & m) | bias};
-    const gbm_half2 off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const gbm_half2 c = __builtin_bit_cast(gbm_half2, t[k]) + off;   // code - 8, exact
-        const gbm_half2 h = c * d2;
-        const gbm_half2 l = __builtin_elementwise_fma(c, d2, -h);        // exact remainder
-        hi[2 * k] = h[0];
-        hi[2 * k + 1] = h[1];
-        lo[2 * k] = l[0];
-        lo[2 * k + 1] = l[1];
-    }
+    const auto a = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto e = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    w[0] = c[0];
+    w[1] = c[1];
+    w[2] = e[0];
+    w[3] = e[1];
+}
+
+// the word v of lane groups 0..3 (same r) into g[0..3], in every lane group
+QD_DEV void gbm_allgather4(uint32_t v, uint32_t (&g)[4])
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);     // groups kg & 1, (kg & 1) | 2
+    const auto b = __builtin_amdgcn_permlane16_swap(a[0], a[0], false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[1], a[1], false, false);
+    g[0] = b[0];
+    g[1] = b[1];
+    g[2] = c[0];
+    g[3] = c[1];
+}
+
+// (a & m) | o in one instruction (the compiler would emit an AND and an OR:
+// a VOP3 instruction takes no literal on gfx9, so m and o come in registers)
+QD_DEV uint32_t gbm_and_or(uint32_t a, uint32_t m, uint32_t o)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+    return r;
+}
+
+// the second operand of one block from this lane group's word w of it
+QD_DEV gbm_half8 gbm_codes(uint32_t w)
+{
+    const uint32_t bias = 0x64006400u, t = w >> 8;
+    const gbm_half2 k8 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const gbm_half2 k128 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    const gbm_half2 p0 = __builtin_bit_cast(gbm_half2, gbm_and_or(w, 0x000F000Fu, bias)) + k8;     // 4kg, 4kg+2
+    const gbm_half2 p2 = __builtin_bit_cast(gbm_half2, gbm_and_or(t, 0x000F000Fu, bias)) + k8;     // 4kg+1, 4kg+3
+    const gbm_half2 p1 = __builtin_bit_cast(gbm_half2, gbm_and_or(w, 0x00F000F0u, bias)) + k128;   // 16 x (16+4kg, ..+2)
+    const gbm_half2 p3 = __builtin_bit_cast(gbm_half2, gbm_and_or(t, 0x00F000F0u, bias)) + k128;   // 16 x (..+1, ..+3)
+    return gbm_half8{p0[0], p0[1], p2[0], p2[1], p1[0], p1[1], p3[0], p3[1]};
 }
 
 // s = 2^k with a * s in [2^13, 2^14) for the largest magnitude a of a chunk
@@ -87,176 +126,528 @@ QD_DEV float gbm_scale_for(float a)
     return ldexpf(1.f, max(-100, min(100, 14 - e)));
 }
 
-// staging items (block, word, vector) per thread per chunk
+// staging items (block, lane group, vector) per thread per chunk
 template <int NC>
 struct GbmItems {
     static constexpr int N = (GBM_KC * 4 * NC + GBM_NW * WAVE - 1) / (GBM_NW * WAVE);
 };
-
-struct GbmBuf {
-    uint4 q[GBM_KC / 4];               // block 4j + kg of this lane's row, j = 0..7
-    uint32_t d[GBM_KC / 4];            // its f16 scale
-};
 template <int NC>
 struct GbmX {
-    float4 xa[GbmItems<NC>::N];        // x of this thread's staging items: elements 4w .. 4w+3
-    float4 xb[GbmItems<NC>::N];        //   and 16+4w .. 16+4w+3
+    float4 xa[GbmItems<NC>::N];        // x of this thread's staging items: elements 4kg .. 4kg+3
+    float4 xb[GbmItems<NC>::N];        //   and 16+4kg .. 16+4kg+3
 };
 
-// grid (row tiles, K slices): slice y takes chunks [y * kch, (y + 1) * kch)
-// and writes its partial products to Y + y * ystride (one slice: Y itself)
-template <int NC>
+template <int NC, int RG>
 __global__ void __launch_bounds__(GBM_NW* WAVE)
 k_gemv_batch_mfma(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
-                  const float* __restrict__ X, float* __restrict__ Y, int N, int nb, int kch, size_t ystride)
+                  const float* __restrict__ X, float* __restrict__ Y, int N, int nb, int kch, size_t ystride,
+                  int dvec)
 {
-    static_assert(NC >= 2 && NC <= 16, "batch");
-    constexpr int NITEM = GBM_KC * 4 * NC;   // staging items of a chunk
-    extern __shared__ __align__(16) _Float16 xs[];   // [KC][4][NC][16]
+    static_assert(NC >= 1 && NC <= 16, "batch");
+    constexpr int NT = GBM_NW * WAVE;
+    constexpr int NITEM = GBM_KC * 4 * NC;           // staging items of a chunk
+    extern __shared__ __align__(16) _Float16 xs[];   // [KC][4][2][16][8]
     __shared__ unsigned xmax[2][GBM_MAXB];            // |x| maxima (f32 bits), by chunk parity
-    __shared__ float xinv[GBM_MAXB];                  // 1/s of the staged chunk, per vector
+    __shared__ float xinv[2][GBM_MAXB];               // 1/s of a staged chunk, by parity
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
     const int r = lane & 15, kg = lane >> 4;
-    const int col = min(lane & 15, NC - 1);          // columns past NC repeat the last vector
     const int K = nb * 32;
     const int nch = (nb + GBM_KC - 1) / GBM_KC;
     const int c0 = (int)blockIdx.y * kch, c1 = min(nch, c0 + kch);   // this slice's chunks
     Y += (size_t)blockIdx.y * ystride;
-    const int ntiles = (N + GBM_ROWS - 1) / GBM_ROWS;
-    if (threadIdx.x < 2 * GBM_MAXB)
-        xmax[threadIdx.x / GBM_MAXB][threadIdx.x % GBM_MAXB] = 0u;   // ordered by the first stage's barrier
-    int gc = 0;   // chunks staged so far by this workgroup (parity of xmax)
-
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {   // uniform per workgroup
-        const int row0 = tile * GBM_ROWS + wave * 16;
-        const uint32_t rb = (uint32_t)min(row0 + r, N - 1) * (uint32_t)nb;
-
-        // weight and x loads of chunk c (clamped: never a branch around a
-        // load; x of a block past nb is zeroed where it is staged).  Staging
-        // item i = (block, word, vector) takes 8 values of x.
-        auto load = [&](GbmBuf& bf, int c) {
+    const int row0 = (int)blockIdx.x * gbm_rows(RG) + wave * 16 * RG;
+    size_t rb[RG];   // first block of this lane's row in each row group
 #pragma unroll
-            for (int j = 0; j < GBM_KC / 4; ++j) {
-                const uint32_t blk = rb + (uint32_t)min(c * GBM_KC + 4 * j + kg, nb - 1);
-                bf.q[j] = *reinterpret_cast<const uint4*>(Q + blk * 16u);
-                bf.d[j] = D[blk];
-            }
-        };
-        auto load_x = [&](GbmX<NC>& bf, int c) {
-#pragma unroll
-            for (int u = 0; u < GbmItems<NC>::N; ++u) {
-                const int i = min((int)threadIdx.x + u * GBM_NW * WAVE, NITEM - 1);
-                const int v = i % NC, w = (i / NC) & 3, bl = i / (4 * NC);
-                const int b = min(c * GBM_KC + bl, nb - 1);
-                const float* xp = X + (size_t)v * K + (size_t)b * 32 + 4 * w;
-                bf.xa[u] = *reinterpret_cast<const float4*>(xp);
-                bf.xb[u] = *reinterpret_cast<const float4*>(xp + 16);
-            }
-        };
-        // stage x of chunk c from the registers of its loads: the chunk's
-        // largest |x| per vector (LDS atomic max of the f32 bits, which order
-        // like the values for |x|), then the scaled split
-        auto stage = [&](const GbmX<NC>& bf, int c) {
-            unsigned* xm = xmax[gc & 1];
-            __syncthreads();   // the previous chunk's reads (x, 1/s) are done
-#pragma unroll
-            for (int u = 0; u < GbmItems<NC>::N; ++u) {
-                const int i = (int)threadIdx.x + u * GBM_NW * WAVE;
-                if (i >= NITEM)   // uniform except in the last round of an odd batch
-                    continue;
-                const bool in = c * GBM_KC + i / (4 * NC) < nb;
-                const float4 a = bf.xa[u], h = bf.xb[u];
-                const float mx = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
-                                       fmaxf(fmaxf(fabsf(h.x), fabsf(h.y)), fmaxf(fabsf(h.z), fabsf(h.w))));
-                if (in)
-                    atomicMax(&xm[i % NC], __float_as_uint(mx));
-            }
-            __syncthreads();
-#pragma unroll
-            for (int u = 0; u < GbmItems<NC>::N; ++u) {
-                const int i = (int)threadIdx.x + u * GBM_NW * WAVE;
-                if (i >= NITEM)
-                    continue;
-                const int bl = i / (4 * NC);
-                const bool in = c * GBM_KC + bl < nb;
-                const float sc = gbm_scale_for(__uint_as_float(xm[i % NC]));
-                const float4 a = bf.xa[u], h = bf.xb[u];
-                float e[8] = {a.x, a.z, a.y, a.w, h.x, h.z, h.y, h.w};
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    e[k] = in ? e[k] * sc : 0.f;
-                gbm_half8 xh, xl;
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const _Float16 t = (_Float16)e[k];
-                    xh[k] = t;
-                    xl[k] = (_Float16)(e[k] - (float)t);
-                }
-                gbm_half8* dst = reinterpret_cast<gbm_half8*>(xs + (size_t)i * 16);
-                dst[0] = xh;
-                dst[1] = xl;
-            }
-            if (threadIdx.x < NC) {
-                xinv[threadIdx.x] = 1.0f / gbm_scale_for(__uint_as_float(xm[threadIdx.x]));
-                // the other parity was last read before this stage's first barrier
-                // and is next written after the following stage's first barrier
-                xmax[(gc + 1) & 1][threadIdx.x] = 0u;
-            }
-            ++gc;
-            __syncthreads();
-        };
-        gbm_floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        auto compute = [&](const GbmBuf& bf) {
-            gbm_floatx4 part = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < GBM_KC / 4; ++j) {
-                const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)bf.d[j]);
-                const gbm_half2 d2 = {dh, dh};
-                const uint32_t wd[4] = {bf.q[j].x, bf.q[j].y, bf.q[j].z, bf.q[j].w};
-                const int bl = 4 * j + kg;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    gbm_half8 ahi, alo;
-                    gbm_a_operand(wd[w], d2, ahi, alo);
-                    const gbm_half8* src =
-                        reinterpret_cast<const gbm_half8*>(xs + ((size_t)(bl * 4 + w) * NC + col) * 16);
-                    const gbm_half8 bhi = src[0], blo = src[1];
-                    part = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bhi, part, 0, 0, 0);
-                    part = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, blo, part, 0, 0, 0);
-                    part = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bhi, part, 0, 0, 0);
-                    part = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, blo, part, 0, 0, 0);
-                }
-            }
-            const float inv = xinv[col];   // column col = this lane's vector
-#pragma unroll
+    for (int g = 0; g < RG; ++g)
+        rb[g] = (size_t)min(row0 + 16 * g + r, N - 1) * (size_t)nb;
+    const int nsteps = (c1 - c0) * GBM_STEPS;
+    if (nsteps <= 0) {   // an empty slice (the host never launches one): zeros
+        for (int g = 0; g < RG; ++g) {
+            const int row = row0 + 16 * g + r;
             for (int i = 0; i < 4; ++i)
-                acc[i] = fmaf(part[i], inv, acc[i]);
-        };
-        GbmBuf b0, b1;
-        GbmX<NC> xr;
-        load(b0, c0);
-        load_x(xr, c0);
-        for (int c = c0; c < c1; c += 2) {
-            stage(xr, c);
-            load(b1, min(c + 1, c1 - 1));
-            load_x(xr, min(c + 1, c1 - 1));
-            compute(b0);
-            if (c + 1 < c1) {   // uniform
-                stage(xr, c + 1);
-                load(b0, min(c + 2, c1 - 1));
-                load_x(xr, min(c + 2, c1 - 1));
-                compute(b1);
+                if (row < N && 4 * kg + i < NC)
+                    Y[(size_t)(4 * kg + i) * N + row] = 0.f;
+        }
+        return;
+    }
+
+    if (threadIdx.x < 2 * GBM_MAXB) {   // ordered by the first stage's barriers
+        xmax[threadIdx.x / GBM_MAXB][threadIdx.x % GBM_MAXB] = 0u;
+        xinv[threadIdx.x / GBM_MAXB][threadIdx.x % GBM_MAXB] = 0.f;
+    }
+    if constexpr (NC < 16) {   // vector slots past the batch stay zero
+        constexpr int NZ = GBM_KC * 4 * 2 * (16 - NC);
+        for (int i = threadIdx.x; i < NZ; i += NT) {
+            const int v = NC + i % (16 - NC), q = i / (16 - NC);
+            *reinterpret_cast<uint4*>(xs + ((size_t)q * 16 + v) * 8) = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+
+    // weight loads of step s (blocks 4j .. 4j+3 of its chunk; this lane: 4j + kg;
+    // clamped, never a branch around a load)
+    struct Buf {
+        uint4 q[RG];
+    };
+    auto load = [&](Buf& bf, int s) {
+        s = min(s, nsteps - 1);
+        const int blk = min((c0 + s / GBM_STEPS) * GBM_KC + (s % GBM_STEPS) * 4 + kg, nb - 1);
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+            bf.q[g] = *reinterpret_cast<const uint4*>(Q + (rb[g] + (size_t)blk) * 16u);
+    };
+    // scales of chunk c: this lane group's eighth, blocks 32c + 8kg .. 8kg+7
+    auto load_d = [&](uint4 (&dq)[RG], int c) {
+        const int b0 = c * GBM_KC + 8 * kg;
+        if (dvec) {   // uniform: nb % 8 == 0 and D 16-byte aligned
+            const int bq = min(b0, nb - 8);
+#pragma unroll
+            for (int g = 0; g < RG; ++g)
+                dq[g] = *reinterpret_cast<const uint4*>(D + rb[g] + (size_t)bq);
+        } else {
+#pragma unroll
+            for (int g = 0; g < RG; ++g) {
+                uint32_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    h[e] = D[rb[g] + (size_t)min(b0 + e, nb - 1)];
+                dq[g] = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
             }
         }
-        // acc[i] = row 4*kg + i of the slice, vector lane % 16
-        if ((lane & 15) < NC) {
+    };
+    auto load_x = [&](GbmX<NC>& bf, int c) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = row0 + 4 * kg + i;
-                if (row < N)
-                    Y[(size_t)(lane & 15) * N + row] = acc[i];
+        for (int u = 0; u < GbmItems<NC>::N; ++u) {
+            const int i = min((int)threadIdx.x + u * NT, NITEM - 1);
+            const int v = i % NC, q = (i / NC) & 3, bl = i / (4 * NC);
+            const int b = min(c * GBM_KC + bl, nb - 1);
+            const float* xp = X + (size_t)v * K + (size_t)b * 32 + 4 * q;
+            bf.xa[u] = *reinterpret_cast<const float4*>(xp);
+            bf.xb[u] = *reinterpret_cast<const float4*>(xp + 16);
+        }
+    };
+    // stage chunk c from the registers of its loads: the chunk's largest |x|
+    // per vector (LDS atomic max of the f32 bits, which order like the values
+    // for |x|), then the scaled split
+    auto stage = [&](const GbmX<NC>& bf, int c, int par) {
+        __syncthreads();   // the previous chunk's reads of x are done
+#pragma unroll
+        for (int u = 0; u < GbmItems<NC>::N; ++u) {
+            const int i = (int)threadIdx.x + u * NT;
+            if (i >= NITEM)   // uniform except in the last round of an odd batch
+                continue;
+            const bool in = c * GBM_KC + i / (4 * NC) < nb;
+            const float4 a = bf.xa[u], h = bf.xb[u];
+            const float mx = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                                   fmaxf(fmaxf(fabsf(h.x), fabsf(h.y)), fmaxf(fabsf(h.z), fabsf(h.w))));
+            if (in)
+                atomicMax(&xmax[par][i % NC], __float_as_uint(mx));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < GbmItems<NC>::N; ++u) {
+            const int i = (int)threadIdx.x + u * NT;
+            if (i >= NITEM)
+                continue;
+            const int v = i % NC, q = (i / NC) & 3, bl = i / (4 * NC);
+            const bool in = c * GBM_KC + bl < nb;
+            const float sc = gbm_scale_for(__uint_as_float(xmax[par][v]));
+            const float sh = sc * 0.0625f;
+            const float4 a = bf.xa[u], h = bf.xb[u];
+            float e[8] = {a.x * sc, a.z * sc, a.y * sc, a.w * sc, h.x * sh, h.z * sh, h.y * sh, h.w * sh};
+            gbm_half8 xh, xl;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float f = in ? e[k] : 0.f;
+                const _Float16 t = (_Float16)f;
+                xh[k] = t;
+                xl[k] = (_Float16)(f - (float)t);
             }
+            _Float16* dst = xs + ((size_t)(bl * 4 + q) * 2 * 16 + v) * 8;
+            *reinterpret_cast<gbm_half8*>(dst) = xh;
+            *reinterpret_cast<gbm_half8*>(dst + 16 * 8) = xl;
+        }
+        if (threadIdx.x < NC) {
+            xinv[par][threadIdx.x] = 1.0f / gbm_scale_for(__uint_as_float(xmax[par][threadIdx.x]));
+            // the other parity was last read before this stage's first barrier
+            // and is next written after the following stage's first barrier
+            xmax[par ^ 1][threadIdx.x] = 0u;
+        }
+        __syncthreads();
+    };
+
+    float acc[RG][4];
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc[g][i] = 0.f;
+    // A whole chunk of weight loads is in flight before its x is staged: the
+    // first chunk's are issued here, the next chunk's step by step as the
+    // current chunk frees its buffers; its scales and x come with them.
+    // x and scales first: loads return in order, so the chunk is staged while
+    // its weight loads are still arriving
+    GbmX<NC> xr;
+    load_x(xr, c0);
+    uint4 dq[RG];
+    load_d(dq, c0);
+    Buf bufs[GBM_STEPS];
+#pragma unroll
+    for (int u = 0; u < GBM_STEPS; ++u)
+        load(bufs[u], u);
+    const gbm_floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+    int par = 0;
+    for (int c = c0; c < c1; ++c, par ^= 1) {
+        stage(xr, c, par);
+        uint32_t dg[RG][4][4];   // [group][lane group q][dword]: halves = scales of blocks 8q ..
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const uint32_t dw[4] = {dq[g].x, dq[g].y, dq[g].z, dq[g].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                uint32_t t[4];
+                gbm_allgather4(dw[k], t);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    dg[g][q][k] = t[q];
+            }
+        }
+        if (c + 1 < c1) {   // uniform
+            load_x(xr, c + 1);
+            load_d(dq, c + 1);
+        }
+        float cacc[RG][4];
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                cacc[g][i] = 0.f;
+        const int sbase = (c - c0) * GBM_STEPS;
+#pragma unroll
+        for (int j = 0; j < GBM_STEPS; ++j) {
+            uint32_t w[RG][4];
+#pragma unroll
+            for (int g = 0; g < RG; ++g) {
+                w[g][0] = bufs[j].q[g].x;
+                w[g][1] = bufs[j].q[g].y;
+                w[g][2] = bufs[j].q[g].z;
+                w[g][3] = bufs[j].q[g].w;
+                gbm_transpose4(w[g]);
+            }
+            load(bufs[j], sbase + GBM_STEPS + j);   // the same step of the next chunk
+            // the step's 4 blocks side by side: their x operands, codes, 8
+            // independent MFMAs into 4 accumulators, then the scaled sums
+            gbm_half8 xh[4], xl[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const _Float16* src = xs + ((size_t)((4 * j + b) * 4 + kg) * 2 * 16 + r) * 8;
+                xh[b] = *reinterpret_cast<const gbm_half8*>(src);
+                xl[b] = *reinterpret_cast<const gbm_half8*>(src + 16 * 8);
+            }
+#pragma unroll
+            for (int g = 0; g < RG; ++g) {
+                gbm_floatx4 p[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const gbm_half8 wop = gbm_codes(w[g][b]);
+                    p[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[b], wop, zero, 0, 0, 0);
+                    p[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[b], wop, p[b], 0, 0, 0);
+                }
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int bl = 4 * j + b;   // block within the chunk
+                    const uint32_t dd = dg[g][bl >> 3][(bl & 7) >> 1];
+                    const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)((bl & 1) ? dd >> 16 : dd));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        cacc[g][i] = fmaf((float)dh, p[b][i], cacc[g][i]);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float inv = xinv[par][4 * kg + i];   // vector 4kg + i
+#pragma unroll
+            for (int g = 0; g < RG; ++g)
+                acc[g][i] = fmaf(cacc[g][i], inv, acc[g][i]);
+        }
+        // keeps the next chunk's loads where they are issued (the compiler would
+        // otherwise sink them to the top of the next iteration, next to their use)
+        asm volatile("" ::: "memory");
+    }
+    // acc[g][i] = vector 4kg + i, row row0 + 16g + r
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        const int row = row0 + 16 * g + r;
+        if (row < N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * kg + i < NC)
+                    Y[(size_t)(4 * kg + i) * N + row] = acc[g][i];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// x split once, outside the product (the batched decode step).  The producer
+// of a product's input writes it already split, in the staged layout, one
+// 64 KB chunk per 32 blocks: XP[chunk][block][lane group][hi, lo][16 vector
+// slots][8 halves], and XS[chunk][16] = 1/s of each vector's chunk.  Slots
+// past the batch and blocks past the end stay zero (the buffers are cleared
+// once when allocated).  The product then copies a chunk into LDS with
+// global-to-LDS loads: no registers, no arithmetic, once per workgroup.
+constexpr int GBM_XP_CHUNK = GBM_KC * 4 * 2 * 16 * 8;   // halves per chunk
+
+// the 8 elements of lane group kg of the block at xb, in the K slot order
+// (the high four divided by 16)
+QD_DEV void gbm_xp_gather(const float* __restrict__ xb, int kg, float (&e)[8])
+{
+    const float4 a = *reinterpret_cast<const float4*>(xb + 4 * kg);
+    const float4 h = *reinterpret_cast<const float4*>(xb + 16 + 4 * kg);
+    e[0] = a.x;
+    e[1] = a.z;
+    e[2] = a.y;
+    e[3] = a.w;
+    e[4] = h.x * 0.0625f;
+    e[5] = h.z * 0.0625f;
+    e[6] = h.y * 0.0625f;
+    e[7] = h.w * 0.0625f;
+}
+
+// largest |.| of the 8 elements in slot order (the high four undone)
+QD_DEV float gbm_xp_absmax(const float (&e)[8])
+{
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        m = fmaxf(m, fabsf(e[k]) * (k < 4 ? 1.f : 16.f));
+    return m;
+}
+
+// writes the split pair of (chunk c, block bl, lane group kg, slot v), scale s
+QD_DEV void gbm_xp_put(_Float16* __restrict__ XP, int c, int bl, int kg, int v, const float (&e)[8], float s)
+{
+    gbm_half8 xh, xl;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float f = e[k] * s;
+        const _Float16 t = (_Float16)f;
+        xh[k] = t;
+        xl[k] = (_Float16)(f - (float)t);
+    }
+    _Float16* dst = XP + (size_t)c * GBM_XP_CHUNK + ((size_t)(bl * 4 + kg) * 2 * 16 + v) * 8;
+    *reinterpret_cast<gbm_half8*>(dst) = xh;
+    *reinterpret_cast<gbm_half8*>(dst + 16 * 8) = xl;
+}
+
+// largest value over the 128 threads of a chunk workgroup (2 waves); every
+// thread gets it; red >= 2 floats
+QD_DEV float gbm_chunk_max(float m, float* red)
+{
+    m = group_max<WAVE>(m);
+    if ((threadIdx.x & (WAVE - 1)) == 0)
+        red[threadIdx.x / WAVE] = m;
+    __syncthreads();
+    return fmaxf(red[0], red[1]);
+}
+
+// grid (chunks, B), 128 threads: vector b of X [B][nb * 32] into XP / XS
+__global__ void __launch_bounds__(128)
+k_xsplit_batch(const float* __restrict__ X, int nb, _Float16* __restrict__ XP, float* __restrict__ XS)
+{
+    __shared__ float red[2];
+    const int c = blockIdx.x, b = blockIdx.y;
+    const int bl = threadIdx.x >> 2, kg = threadIdx.x & 3, blk = c * GBM_KC + bl;
+    const bool in = blk < nb;
+    float e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (in)
+        gbm_xp_gather(X + (size_t)b * nb * 32 + (size_t)blk * 32, kg, e);
+    const float s = gbm_scale_for(gbm_chunk_max(gbm_xp_absmax(e), red));
+    if (in)
+        gbm_xp_put(XP, c, bl, kg, b, e, s);
+    if (threadIdx.x == 0)
+        XS[c * 16 + b] = 1.0f / s;
+}
+
+// The product on a split x: grid (row tiles, K slices) as k_gemv_batch_mfma,
+// B vectors at run time (slots past B are zero in XP); Y[b] for b < B.
+template <int RG>
+__global__ void __launch_bounds__(GBM_NW* WAVE)
+k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
+                const _Float16* __restrict__ XP, const float* __restrict__ XS, float* __restrict__ Y,
+                int N, int nb, int B, int kch, size_t ystride, int dvec)
+{
+    extern __shared__ __align__(16) _Float16 xs[];   // one chunk of XP
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int r = lane & 15, kg = lane >> 4;
+    const int nch = (nb + GBM_KC - 1) / GBM_KC;
+    const int c0 = (int)blockIdx.y * kch, c1 = min(nch, c0 + kch);
+    Y += (size_t)blockIdx.y * ystride;
+    const int row0 = (int)blockIdx.x * gbm_rows(RG) + wave * 16 * RG;
+    size_t rb[RG];
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+        rb[g] = (size_t)min(row0 + 16 * g + r, N - 1) * (size_t)nb;
+    const int nsteps = (c1 - c0) * GBM_STEPS;
+    if (nsteps <= 0) {   // an empty slice (the host never launches one): zeros
+        for (int g = 0; g < RG; ++g) {
+            const int row = row0 + 16 * g + r;
+            for (int i = 0; i < 4; ++i)
+                if (row < N && 4 * kg + i < B)
+                    Y[(size_t)(4 * kg + i) * N + row] = 0.f;
+        }
+        return;
+    }
+    struct Buf {
+        uint4 q[RG];
+    };
+    auto load = [&](Buf& bf, int s) {
+        s = min(s, nsteps - 1);
+        const int blk = min((c0 + s / GBM_STEPS) * GBM_KC + (s % GBM_STEPS) * 4 + kg, nb - 1);
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+            bf.q[g] = *reinterpret_cast<const uint4*>(Q + (rb[g] + (size_t)blk) * 16u);
+    };
+    auto load_d = [&](uint4 (&dq)[RG], int c) {
+        const int b0 = c * GBM_KC + 8 * kg;
+        if (dvec) {   // uniform: nb % 8 == 0 and D 16-byte aligned
+            const int bq = min(b0, nb - 8);
+#pragma unroll
+            for (int g = 0; g < RG; ++g)
+                dq[g] = *reinterpret_cast<const uint4*>(D + rb[g] + (size_t)bq);
+        } else {
+#pragma unroll
+            for (int g = 0; g < RG; ++g) {
+                uint32_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    h[e] = D[rb[g] + (size_t)min(b0 + e, nb - 1)];
+                dq[g] = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
+            }
+        }
+    };
+    // chunk c of XP into LDS: wave w copies 16 KB, 1 KB per instruction
+    auto dma_x = [&](int c) {
+        const _Float16* src = XP + (size_t)c * GBM_XP_CHUNK + (size_t)wave * 16 * 512 + lane * 8;
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(src + q * 512),
+                (__attribute__((address_space(3))) void*)(xs + (wave * 16 + q) * 512), 16, 0, 0);
+    };
+    auto load_inv = [&](float (&inv)[4], int c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            inv[i] = XS[c * 16 + 4 * kg + i];
+    };
+
+    float acc[RG][4];
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc[g][i] = 0.f;
+    // x first (loads complete in order), then the scales, then every weight
+    // load of the first chunk; the next chunk's weights are issued while the
+    // current one is computed, its x and scales right after it
+    dma_x(c0);
+    uint4 dq[RG];
+    load_d(dq, c0);
+    float inv[4];
+    load_inv(inv, c0);
+    Buf bufs[GBM_STEPS];
+#pragma unroll
+    for (int u = 0; u < GBM_STEPS; ++u)
+        load(bufs[u], u);
+    const gbm_floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+    for (int c = c0; c < c1; ++c) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this chunk's x (and everything before it) landed
+        __syncthreads();
+        uint32_t dg[RG][4][4];
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const uint32_t dw[4] = {dq[g].x, dq[g].y, dq[g].z, dq[g].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                uint32_t t[4];
+                gbm_allgather4(dw[k], t);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    dg[g][q][k] = t[q];
+            }
+        }
+        float cinv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            cinv[i] = inv[i];
+        float cacc[RG][4];
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                cacc[g][i] = 0.f;
+        const int sbase = (c - c0) * GBM_STEPS;
+#pragma unroll
+        for (int j = 0; j < GBM_STEPS; ++j) {
+            uint32_t w[RG][4];
+#pragma unroll
+            for (int g = 0; g < RG; ++g) {
+                w[g][0] = bufs[j].q[g].x;
+                w[g][1] = bufs[j].q[g].y;
+                w[g][2] = bufs[j].q[g].z;
+                w[g][3] = bufs[j].q[g].w;
+                gbm_transpose4(w[g]);
+            }
+            load(bufs[j], sbase + GBM_STEPS + j);   // the same step of the next chunk
+            gbm_half8 xh[4], xl[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const _Float16* src = xs + ((size_t)((4 * j + b) * 4 + kg) * 2 * 16 + r) * 8;
+                xh[b] = *reinterpret_cast<const gbm_half8*>(src);
+                xl[b] = *reinterpret_cast<const gbm_half8*>(src + 16 * 8);
+            }
+#pragma unroll
+            for (int g = 0; g < RG; ++g) {
+                gbm_floatx4 p[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const gbm_half8 wop = gbm_codes(w[g][b]);
+                    p[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[b], wop, zero, 0, 0, 0);
+                    p[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[b], wop, p[b], 0, 0, 0);
+                }
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int bl = 4 * j + b;
+                    const uint32_t dd = dg[g][bl >> 3][(bl & 7) >> 1];
+                    const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)((bl & 1) ? dd >> 16 : dd));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        cacc[g][i] = fmaf((float)dh, p[b][i], cacc[g][i]);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int g = 0; g < RG; ++g)
+                acc[g][i] = fmaf(cacc[g][i], cinv[i], acc[g][i]);
+        if (c + 1 < c1) {   // uniform
+            __syncthreads();   // every wave is done with this chunk's x
+            dma_x(c + 1);
+            load_d(dq, c + 1);
+            load_inv(inv, c + 1);
+        }
+        asm volatile("" ::: "memory");   // keeps the next chunk's loads where they are issued
+    }
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        const int row = row0 + 16 * g + r;
+        if (row < N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * kg + i < B)
+                    Y[(size_t)(4 * kg + i) * N + row] = acc[g][i];
         }
     }
 }

@@ -19,13 +19,19 @@
 // x[32b .. 32b+15] as is and x[32b+16 .. 32b+31] divided by 16 (exact), with
 // the block's sum of x beside it.
 //
-// In-register dequant: for one 32-bit word w of nibbles (bytes 4k..4k+3 of a
-// block), w & 0x0f0f0f0f holds the codes of elements 4k..4k+3 and
-// w & 0xf0f0f0f0 sixteen times the codes of elements 16+4k..16+4k+3, one per
-// byte; v_cvt_f32_ubyte{0..3} turns each byte into f32 in one instruction
-// (the factor 16 cancels against the staged x/16), and an FMA accumulates it:
-// 2 ANDs + 8 converts + 8 FMAs per 8 weights, exact products in f32.  The -8
-// offset is applied once per block:
+// In-register dequant: a 16-bit field whose only set bits are among its low
+// 8 is an f16 subnormal, value field * 2^-24 exactly.  For one 32-bit word w
+// of nibbles (bytes 4k..4k+3 of a block) w & 0x000F000F holds the codes of
+// elements 4k and 4k+2 as such a pair, w & 0x00F000F0 sixteen times those of
+// 16+4k and 16+4k+2, and the same two masks of w >> 8 cover 4k+1, 4k+3,
+// 16+4k+1 and 16+4k+3.  v_fma_mix_f32 takes one f16 half as a multiplicand
+// of an f32 FMA (subnormal inputs kept, exactly), so the conversion costs
+// nothing: 1 shift + 4 ANDs + 8 FMAs per 8 weights, exact products in f32.
+// The factor 16 cancels against the staged x/16; the factor 2^-24 is carried
+// through the row sums (every partial result is the exact-arithmetic one
+// scaled by a power of two, so nothing changes unless a value leaves the
+// normal f32 range) and removed once per row.  The -8 offset is applied once
+// per block:
 //   sum_j (c_j - 8) x_j = sum_j c_j x_j - 8 * sum_j x_j.
 // Row sums are reduced across the LPR lanes with butterfly shuffles in a fixed
 // order (deterministic).
@@ -94,8 +100,8 @@ QD_DEV void stage_x_store(int nb, const XStage<NT>& st, float* xl, float* xs)
     __syncthreads();
 }
 
-// w & m through an opaque instruction, so the byte converts below stay
-// v_cvt_f32_ubyteN instead of being re-derived as bit-field extracts
+// w & m through an opaque instruction, so that each mask stays one v_and_b32
+// instead of being re-derived per field (bit-field extracts, per-half masks)
 QD_DEV uint32_t and_opaque(uint32_t w, uint32_t m)
 {
     uint32_t r;
@@ -103,23 +109,32 @@ QD_DEV uint32_t and_opaque(uint32_t w, uint32_t m)
     return r;
 }
 
-// sum_j c_j * x_j over one block (codes c_j in [0, 15]); xv = the staged block
+// Q4_SUB = 2^-24, the value of the f16 subnormal with field 1
+constexpr float Q4_SUB = 0x1p-24f;
+constexpr float Q4_UNSUB = 0x1p24f;
+
+// Q4_SUB * sum_j c_j * x_j over one block (codes c_j in [0, 15]); xv = the
+// staged block (x[16..31] divided by 16)
 QD_DEV float q4_block_dot(uint4 q, const float4 (&xv)[8])
 {
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint32_t lo = and_opaque(w[k], 0x0f0f0f0fu);
-        const uint32_t hi = and_opaque(w[k], 0xf0f0f0f0u);
-        s0 = fmaf((float)(lo & 0xffu), xv[k].x, s0);
-        s0 = fmaf((float)((lo >> 8) & 0xffu), xv[k].y, s0);
-        s0 = fmaf((float)((lo >> 16) & 0xffu), xv[k].z, s0);
-        s0 = fmaf((float)(lo >> 24), xv[k].w, s0);
-        s1 = fmaf((float)(hi & 0xffu), xv[4 + k].x, s1);
-        s1 = fmaf((float)((hi >> 8) & 0xffu), xv[4 + k].y, s1);
-        s1 = fmaf((float)((hi >> 16) & 0xffu), xv[4 + k].z, s1);
-        s1 = fmaf((float)(hi >> 24), xv[4 + k].w, s1);
+        const uint32_t t = w[k] >> 8;
+        const half2_t a = __builtin_bit_cast(half2_t, and_opaque(w[k], 0x000F000Fu));   // 4k, 4k+2
+        const half2_t b = __builtin_bit_cast(half2_t, and_opaque(t, 0x000F000Fu));      // 4k+1, 4k+3
+        const half2_t c = __builtin_bit_cast(half2_t, and_opaque(w[k], 0x00F000F0u));   // 16 x (16+4k, 16+4k+2)
+        const half2_t e = __builtin_bit_cast(half2_t, and_opaque(t, 0x00F000F0u));      // 16 x (16+4k+1, 16+4k+3)
+        s0 = fmaf((float)a[0], xv[k].x, s0);
+        s0 = fmaf((float)b[0], xv[k].y, s0);
+        s0 = fmaf((float)a[1], xv[k].z, s0);
+        s0 = fmaf((float)b[1], xv[k].w, s0);
+        s1 = fmaf((float)c[0], xv[4 + k].x, s1);
+        s1 = fmaf((float)e[0], xv[4 + k].y, s1);
+        s1 = fmaf((float)c[1], xv[4 + k].z, s1);
+        s1 = fmaf((float)e[1], xv[4 + k].w, s1);
     }
     return s0 + s1;
 }
@@ -205,7 +220,7 @@ QD_DEV void gemv_run(const uint16_t* __restrict__ D, const uint8_t* __restrict__
 #pragma unroll
                 for (int k = 0; k < 8; ++k)
                     xv[k] = xp[k];
-                const float m8 = -8.f * xs[b];
+                const float m8 = (-8.f * Q4_SUB) * xs[b];
 #pragma unroll
                 for (int r = 0; r < RPS; ++r)
                     acc[r] = fmaf(f16_to_f32((uint16_t)bf.d[g][r]), q4_block_dot(bf.q[g][r], xv) + m8,
@@ -215,7 +230,7 @@ QD_DEV void gemv_run(const uint16_t* __restrict__ D, const uint8_t* __restrict__
         if (grp == ngroups - 1) {
 #pragma unroll
             for (int r = 0; r < RPS; ++r)
-                acc[r] = group_sum<LPR>(acc[r]);
+                acc[r] = group_sum<LPR>(acc[r]) * Q4_UNSUB;
             const int row0 = tile * G::ROWS + wave * G::RPW + slot * RPS;
             epi.tile(row0, acc, lr == 0);
 #pragma unroll

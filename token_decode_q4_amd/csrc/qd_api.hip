@@ -119,6 +119,10 @@ struct qd_model {
     // buffers of the batched step ([B] rows each)
     float *bx = nullptr, *bh = nullptr, *bqkv = nullptr, *battn = nullptr, *bo = nullptr;
     float *bgu = nullptr, *bact = nullptr, *blog = nullptr, *bcval = nullptr;
+    // the batched products' inputs, split (gemv_batch_mfma.h): hidden-sized
+    // (q|k|v, gate|up, LM head), attention output (o), SwiGLU output (down)
+    _Float16 *xp_h = nullptr, *xp_o = nullptr, *xp_i = nullptr;
+    float *xs_h = nullptr, *xs_o = nullptr, *xs_i = nullptr;
     int32_t* bcidx = nullptr;
     int bG = 1, bchunk = 1;
     int ks_qkv = 1, ks_o = 1, ks_gu = 1, ks_down = 1;   // K slices of the batched products
@@ -372,6 +376,8 @@ static int validate_config(const qd_config* c, const qd_weights* w, int B)
         return fail(QD_EUNSUPPORTED, "attn_out_gate with layer_kernel = 1");
     if (B > 1 && (c->layer_kernel || c->attn_out_gate))
         return fail(QD_EUNSUPPORTED, "a batched model supports neither layer_kernel nor attn_out_gate");
+    if (B > 1 && c->hidden > 16384)   // the batched RMSNorm splits at most 2 items per thread
+        return fail(QD_EUNSUPPORTED, "a batched model supports hidden <= 16384 (got %d)", c->hidden);
     if (B > 1) {
         // the matrix-core batched GEMV forms (code - 8) * d in f16
         auto scales_ok = [](const qd_q4_0& q) {
@@ -493,12 +499,12 @@ static int enqueue_step_fused(qd_model* m, hipStream_t s)
 
 // K slices of a batched step's product of N rows and nb blocks: the row tiles
 // of the matrix-core GEMV alone give too few workgroups for short matrices,
-// so K is cut into slices (whole 32-block chunks) up to about 256 workgroups
+// so K is cut into slices (whole 32-block chunks) up to about 512 workgroups
 static int step_kslices(int N, int nb)
 {
-    const int tiles = (N + GBM_ROWS - 1) / GBM_ROWS;
+    const int tiles = (N + gbm_rows(1) - 1) / gbm_rows(1);
     const int nch = (nb + GBM_KC - 1) / GBM_KC;
-    int ks = std::min({nch, SB_MAXSLAB, std::max(1, (256 + tiles / 2) / tiles)});
+    int ks = std::min({nch, SB_MAXSLAB, std::max(1, (512 + tiles / 2) / tiles)});
     if (ks > 1) {
         const int kch = (nch + ks - 1) / ks;
         ks = (nch + kch - 1) / kch;
@@ -506,19 +512,27 @@ static int step_kslices(int N, int nb)
     return ks;
 }
 
-// the batched step's product Y = W X: in ks K slices on the matrix cores
-// (partial slabs of B*N floats, summed by the consumer), or whole
-static hipError_t step_gemv(const qd_model* m, const DevQ4& W, const float* X, float* Y, int ks, hipStream_t s)
+// the batched step's product Y = W X on the matrix cores from x split in
+// XP / XS, in ks K slices (partial slabs of B*N floats, summed by the
+// consumer); two row groups per wave once one would give 768 workgroups
+static hipError_t step_gemv(const qd_model* m, const DevQ4& W, const _Float16* XP, const float* XS, float* Y,
+                            int ks, hipStream_t s)
 {
-    if (ks <= 1)
-        return gemv_batch_launch(W.d, W.qs, X, Y, W.rows, W.cols, m->B, s);
-    switch (m->B) {
-#define QD_SG(NC_) case NC_: return launch_gemv_batch_mfma<NC_>(W.d, W.qs, X, Y, W.rows, W.nb, s, ks);
-    QD_SG(2) QD_SG(3) QD_SG(4) QD_SG(5) QD_SG(6) QD_SG(7) QD_SG(8) QD_SG(9)
-    QD_SG(10) QD_SG(11) QD_SG(12) QD_SG(13) QD_SG(14) QD_SG(15)
-#undef QD_SG
-    default: return launch_gemv_batch_mfma<16>(W.d, W.qs, X, Y, W.rows, W.nb, s, ks);
-    }
+    const int N = W.rows, nb = W.nb;
+    const int nch = (nb + GBM_KC - 1) / GBM_KC;
+    const int kch = (nch + ks - 1) / ks;
+    if (ks < 1 || (int64_t)(ks - 1) * kch >= nch)   // every slice holds at least one chunk
+        return hipErrorInvalidValue;
+    const int dvec = (nb % 8 == 0 && reinterpret_cast<uintptr_t>(W.d) % 16 == 0) ? 1 : 0;
+    const int t1 = (N + gbm_rows(1) - 1) / gbm_rows(1);
+    const size_t ystride = (size_t)m->B * N;
+    if ((int64_t)t1 * ks >= 768)
+        hipLaunchKernelGGL((k_gemv_batch_xp<2>), dim3((N + gbm_rows(2) - 1) / gbm_rows(2), ks), dim3(GBM_NW * WAVE),
+                           gemv_batch_mfma_lds_bytes(), s, W.d, W.qs, XP, XS, Y, N, nb, m->B, kch, ystride, dvec);
+    else
+        hipLaunchKernelGGL((k_gemv_batch_xp<1>), dim3(t1, ks), dim3(GBM_NW * WAVE), gemv_batch_mfma_lds_bytes(), s,
+                           W.d, W.qs, XP, XS, Y, N, nb, m->B, kch, ystride, dvec);
+    return hipGetLastError();
 }
 
 // One step of the B sequences of a batched model: every weight read once for
@@ -527,13 +541,14 @@ static hipError_t step_gemv(const qd_model* m, const DevQ4& W, const float* X, f
 // (step_batch.h), the greedy pick per sequence.
 static int enqueue_step_batch(qd_model* m, hipStream_t s)
 {
-    const int B = m->B, H = m->H, nqd = m->nq * m->hd, I = m->I;
+    const int B = m->B, H = m->H, I = m->I;
+    const int nqd = m->nq * m->hd;
     hipLaunchKernelGGL(k_embed_batch, dim3(B), dim3(SB_THREADS), 0, s, m->embed.d, m->embed.qs, H, m->V, m->st,
-                       m->ids, m->max_seq, m->layers[0].attn_norm, m->eps, m->bx, m->bh, m->rope_cos,
-                       m->rope_sin, m->rot / 2, m->rope_cur, m->rstride);
+                       m->ids, m->max_seq, m->layers[0].attn_norm, m->eps, m->bx, nullptr, m->xp_h, m->xs_h,
+                       m->rope_cos, m->rope_sin, m->rot / 2, m->rope_cur, m->rstride);
     for (int l = 0; l < m->L; ++l) {
         DevLayer& Ly = m->layers[l];
-        HIP_TRY(step_gemv(m, Ly.qkv, m->bh, m->bqkv, m->ks_qkv, s));
+        HIP_TRY(step_gemv(m, Ly.qkv, m->xp_h, m->xs_h, m->bqkv, m->ks_qkv, s));
         AttnParams p;
         memset(&p, 0, sizeof p);
         p.q = m->bqkv;
@@ -572,18 +587,20 @@ static int enqueue_step_batch(qd_model* m, hipStream_t s)
         else
             launch_attention<1>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, B, m->nq, s);
         const size_t slab_h = (size_t)B * H;
-        HIP_TRY(step_gemv(m, Ly.o, m->battn, m->bo, m->ks_o, s));
+        hipLaunchKernelGGL(k_xsplit_batch, dim3((nqd / 32 + GBM_KC - 1) / GBM_KC, B), dim3(128), 0, s, m->battn,
+                           nqd / 32, m->xp_o, m->xs_o);
+        HIP_TRY(step_gemv(m, Ly.o, m->xp_o, m->xs_o, m->bo, m->ks_o, s));
         hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(B), dim3(SB_THREADS), 0, s, m->bx, m->bo, m->ks_o, slab_h,
-                           H, Ly.ffn_norm, m->eps, m->bh);
-        HIP_TRY(step_gemv(m, Ly.gu, m->bh, m->bgu, m->ks_gu, s));
-        hipLaunchKernelGGL(k_swiglu_batch, dim3((I + 255) / 256, B), dim3(256), 0, s, m->bgu, m->ks_gu,
-                           (size_t)B * 2 * I, I, m->bact);
-        HIP_TRY(step_gemv(m, Ly.down, m->bact, m->bo, m->ks_down, s));
+                           H, Ly.ffn_norm, m->eps, nullptr, m->xp_h, m->xs_h);
+        HIP_TRY(step_gemv(m, Ly.gu, m->xp_h, m->xs_h, m->bgu, m->ks_gu, s));
+        hipLaunchKernelGGL(k_swiglu_xp_batch, dim3((I / 32 + GBM_KC - 1) / GBM_KC, B), dim3(128), 0, s, m->bgu,
+                           m->ks_gu, (size_t)B * 2 * I, I, m->xp_i, m->xs_i);
+        HIP_TRY(step_gemv(m, Ly.down, m->xp_i, m->xs_i, m->bo, m->ks_down, s));
         const float* wn = (l + 1 < m->L) ? m->layers[l + 1].attn_norm : m->final_norm;
         hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(B), dim3(SB_THREADS), 0, s, m->bx, m->bo, m->ks_down,
-                           slab_h, H, wn, m->eps, m->bh);
+                           slab_h, H, wn, m->eps, nullptr, m->xp_h, m->xs_h);
     }
-    HIP_TRY(gemv_batch_launch(m->lm.d, m->lm.qs, m->bh, m->blog, m->V, H, B, s));
+    HIP_TRY(step_gemv(m, m->lm, m->xp_h, m->xs_h, m->blog, 1, s));
     hipLaunchKernelGGL(k_argmax_batch, dim3(m->bG, B), dim3(256), 0, s, m->blog, m->V, m->bchunk, m->bcval,
                        m->bcidx);
     hipLaunchKernelGGL(k_argmax_advance_batch, dim3(B), dim3(256), 0, s, m->bcval, m->bcidx, m->bG, m->V, m->st,
@@ -948,6 +965,21 @@ static int create_model(const qd_config* cfg, const qd_weights* w, int B, qd_str
             (rc = dev_alloc_t(m, &m->bact, Bz * m->I)) || (rc = dev_alloc_t(m, &m->blog, Bz * m->V)) ||
             (rc = dev_alloc_t(m, &m->bcval, Bz * m->bG)) || (rc = dev_alloc_t(m, &m->bcidx, Bz * m->bG)))
             return bail(rc);
+        const size_t ch_h = (H / 32 + GBM_KC - 1) / GBM_KC, ch_o = (nqd / 32 + GBM_KC - 1) / GBM_KC,
+                     ch_i = (m->I / 32 + GBM_KC - 1) / GBM_KC;
+        if ((rc = dev_alloc_t(m, &m->xp_h, ch_h * GBM_XP_CHUNK)) ||
+            (rc = dev_alloc_t(m, &m->xp_o, ch_o * GBM_XP_CHUNK)) ||
+            (rc = dev_alloc_t(m, &m->xp_i, ch_i * GBM_XP_CHUNK)) || (rc = dev_alloc_t(m, &m->xs_h, ch_h * 16)) ||
+            (rc = dev_alloc_t(m, &m->xs_o, ch_o * 16)) || (rc = dev_alloc_t(m, &m->xs_i, ch_i * 16)))
+            return bail(rc);
+        // slots past the batch and blocks past the end are read as zeros forever
+        if (hipMemsetAsync(m->xp_h, 0, ch_h * GBM_XP_CHUNK * sizeof(_Float16), s) != hipSuccess ||
+            hipMemsetAsync(m->xp_o, 0, ch_o * GBM_XP_CHUNK * sizeof(_Float16), s) != hipSuccess ||
+            hipMemsetAsync(m->xp_i, 0, ch_i * GBM_XP_CHUNK * sizeof(_Float16), s) != hipSuccess ||
+            hipMemsetAsync(m->xs_h, 0, ch_h * 16 * sizeof(float), s) != hipSuccess ||
+            hipMemsetAsync(m->xs_o, 0, ch_o * 16 * sizeof(float), s) != hipSuccess ||
+            hipMemsetAsync(m->xs_i, 0, ch_i * 16 * sizeof(float), s) != hipSuccess)
+            return bail(fail(QD_EHIP, "batch buffer clear failed"));
     }
     if (hipMemsetAsync(m->st, 0, sizeof(StepState) * B, s) != hipSuccess ||
         hipMemsetAsync(m->ids, 0, sizeof(int32_t) * B * m->max_seq, s) != hipSuccess ||
@@ -1312,21 +1344,27 @@ static hipError_t launch_gemv_batch_l(const uint16_t* d, const uint8_t* q, const
 #ifndef QD_BATCH_MFMA_MIN
 #define QD_BATCH_MFMA_MIN 6
 #endif
-constexpr int GBM_GRID_CAP = 1024;
 
-// ks > 1: K in ks slices of whole chunks, partial products to y + k * NC * N
+// K in ks slices of whole chunks, partial products to y + k * NC * N; two row
+// groups per wave once one would give 768 workgroups or more
 template <int NC>
 static hipError_t launch_gemv_batch_mfma(const uint16_t* d, const uint8_t* q, const float* x, float* y,
                                          int N, int nb, hipStream_t s, int ks)
 {
-    const int ntiles = (N + GBM_ROWS - 1) / GBM_ROWS;
     const int nch = (nb + GBM_KC - 1) / GBM_KC;
     const int kch = (nch + ks - 1) / ks;
     if (ks < 1 || (int64_t)(ks - 1) * kch >= nch)   // every slice holds at least one chunk
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_gemv_batch_mfma<NC>), dim3(std::max(1, std::min(ntiles, GBM_GRID_CAP)), ks),
-                       dim3(GBM_NW * WAVE), gemv_batch_mfma_lds_bytes(NC), s, d, q, x, y, N, nb, kch,
-                       (size_t)NC * N);
+    const int dvec = (nb % 8 == 0 && reinterpret_cast<uintptr_t>(d) % 16 == 0) ? 1 : 0;
+    const int t1 = (N + gbm_rows(1) - 1) / gbm_rows(1);
+    if ((int64_t)t1 * ks >= 768) {
+        hipLaunchKernelGGL((k_gemv_batch_mfma<NC, 2>), dim3((N + gbm_rows(2) - 1) / gbm_rows(2), ks),
+                           dim3(GBM_NW * WAVE), gemv_batch_mfma_lds_bytes(), s, d, q, x, y, N, nb, kch,
+                           (size_t)NC * N, dvec);
+    } else {
+        hipLaunchKernelGGL((k_gemv_batch_mfma<NC, 1>), dim3(t1, ks), dim3(GBM_NW * WAVE),
+                           gemv_batch_mfma_lds_bytes(), s, d, q, x, y, N, nb, kch, (size_t)NC * N, dvec);
+    }
     return hipGetLastError();
 }
 

@@ -12,20 +12,25 @@
 // residual, takes the mean square of the row in a fixed order and writes the
 // normalised row for the next product.
 //   k_embed_batch           x[b] = E[token_b]; h[b] = rms(x[b]) * w; rotary factors
-//   (batched q|k|v GEMV; split-KV attention over the B caches; batched o GEMV)
+//   (batched q|k|v GEMV; split-KV attention over the B caches; k_xsplit_batch;
+//    batched o GEMV)
 //   k_resid_rmsnorm_batch   x[b] += y[b]; h[b] = rms(x[b]) * w
-//   (batched gate|up GEMV)  k_swiglu_batch: a[b][i] = silu(g) * up
+//   (batched gate|up GEMV)  k_swiglu_xp_batch: a[b][i] = silu(g) * up
 //   (batched down GEMV)     k_resid_rmsnorm_batch (next layer's or the final norm)
+// The products take their input already split (XP / XS, gemv_batch_mfma.h):
+// the normalised rows, the SwiGLU output and the attention output are written
+// in that form by their producers.
 //   (batched LM head)       k_argmax_batch, k_argmax_advance_batch
 #pragma once
 
+#include "gemv_batch_mfma.h"
 #include "step_kernels.h"
 
 namespace qd {
 
 constexpr int SB_MAXB = 16;    // sequences of a batched model
 constexpr int SB_THREADS = 1024;
-constexpr int SB_MAXSLAB = 4;  // K slices of a batched step's product
+constexpr int SB_MAXSLAB = 8;  // K slices of a batched step's product
 
 // sum over a workgroup of SB_THREADS threads in a fixed order (every thread
 // gets it); red >= 16 floats
@@ -43,19 +48,72 @@ QD_DEV float sb_block_sum(float v, float* red)
     return s;
 }
 
+// The second pass of the batched RMSNorm: row b of x normalised, x / rms * w,
+// written as f32 to hb (if not null) and split for the batched product into
+// XP / XS (if not null; one split per 32-block chunk, see gemv_batch_mfma.h).
+// H <= 16384 (at most 2 split items per thread); cmax >= 32 floats.
+QD_DEV void sb_norm_out(const float* __restrict__ xb, int H, float inv, const float* __restrict__ w,
+                        float* __restrict__ hb, int b, _Float16* __restrict__ XP, float* __restrict__ XS,
+                        float* cmax)
+{
+    if (hb)
+        for (int i = threadIdx.x; i < H; i += blockDim.x)
+            hb[i] = xb[i] * inv * w[i];
+    if (!XP)
+        return;
+    const int nb = H / 32, nit = ((nb + GBM_KC - 1) / GBM_KC) * 128;   // items (chunk, block, lane group)
+    float e[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int it = (int)threadIdx.x + u * SB_THREADS;
+        if (it < nit) {   // uniform per wave (nit is a multiple of 128)
+            const int c = it >> 7, bl = (it >> 2) & 31, kg = it & 3, blk = c * GBM_KC + bl;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                e[u][k] = 0.f;
+            if (blk < nb) {
+                float xe[8], we[8];
+                gbm_xp_gather(xb + (size_t)blk * 32, kg, xe);
+                gbm_xp_gather(w + (size_t)blk * 32, kg, we);
+#pragma unroll
+                for (int k = 0; k < 8; ++k)   // (x / 16) * inv * (w / 16) * 16 = x * inv * w / 16
+                    e[u][k] = k < 4 ? xe[k] * inv * we[k] : (xe[k] * 16.f) * inv * we[k];
+            }
+            const float m = group_max<WAVE>(gbm_xp_absmax(e[u]));
+            if ((threadIdx.x & (WAVE - 1)) == 0)
+                cmax[it / WAVE] = m;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int it = (int)threadIdx.x + u * SB_THREADS;
+        if (it < nit) {
+            const int c = it >> 7, bl = (it >> 2) & 31, kg = it & 3;
+            const float s = gbm_scale_for(fmaxf(cmax[2 * c], cmax[2 * c + 1]));
+            if (c * GBM_KC + bl < nb)
+                gbm_xp_put(XP, c, bl, kg, b, e[u], s);
+            if ((it & 127) == 0)
+                XS[c * 16 + b] = 1.0f / s;
+        }
+    }
+}
+
 // grid B: sequence b at its position st[b].pos reads its stored token, writes
-// x[b] (the embedding row) and h[b] = x[b] / rms * w, and the rotary factors
-// of its position (cos [half] then sin [half]) at rope_cur + b * rstride.
-// A position or token out of range is recorded in st[b].error and replaced
-// by 0 (reported by qd_check).
+// x[b] (the embedding row) and x[b] / rms * w (to h and/or XP / XS, as
+// sb_norm_out), and the rotary factors of its position (cos [half] then sin
+// [half]) at rope_cur + b * rstride.  A position or token out of range is
+// recorded in st[b].error and replaced by 0 (reported by qd_check).
 __global__ void __launch_bounds__(SB_THREADS)
 k_embed_batch(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, int H, int vocab,
               StepState* __restrict__ st, const int32_t* __restrict__ ids, int max_seq,
               const float* __restrict__ w, float eps, float* __restrict__ x, float* __restrict__ h,
+              _Float16* __restrict__ XP, float* __restrict__ XS,
               const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int half,
               float* __restrict__ rope_cur, int rstride)
 {
     __shared__ float red[16];
+    __shared__ float cmax[32];
     const int b = blockIdx.x;
     StepState* sb = st + b;
     int pos = sb->pos;
@@ -84,18 +142,20 @@ k_embed_batch(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, i
         xb[i] = v;
         ss = fmaf(v, v, ss);
     }
-    const float inv = 1.0f / sqrtf(sb_block_sum(ss, red) / (float)H + eps);
-    for (int i = threadIdx.x; i < H; i += blockDim.x)
-        h[(size_t)b * H + i] = xb[i] * inv * w[i];   // each thread rereads its own x
+    const float inv = 1.0f / sqrtf(sb_block_sum(ss, red) / (float)H + eps);   // its barriers order xb
+    sb_norm_out(xb, H, inv, w, h ? h + (size_t)b * H : nullptr, b, XP, XS, cmax);
 }
 
 // grid B: x[b] += y[b] (y may be null: no residual; y may come as nslab
-// partial products slab floats apart, added in slab order); h[b] = x[b] / rms * w
+// partial products slab floats apart, added in slab order); x[b] / rms * w to
+// h and/or XP / XS (as sb_norm_out)
 __global__ void __launch_bounds__(SB_THREADS)
 k_resid_rmsnorm_batch(float* __restrict__ x, const float* __restrict__ y, int nslab, size_t slab, int H,
-                      const float* __restrict__ w, float eps, float* __restrict__ h)
+                      const float* __restrict__ w, float eps, float* __restrict__ h,
+                      _Float16* __restrict__ XP, float* __restrict__ XS)
 {
     __shared__ float red[16];
+    __shared__ float cmax[32];
     const int b = blockIdx.x;
     float* xb = x + (size_t)b * H;
     float ss = 0.f;
@@ -110,9 +170,8 @@ k_resid_rmsnorm_batch(float* __restrict__ x, const float* __restrict__ y, int ns
         }
         ss = fmaf(v, v, ss);
     }
-    const float inv = 1.0f / sqrtf(sb_block_sum(ss, red) / (float)H + eps);
-    for (int i = threadIdx.x; i < H; i += blockDim.x)
-        h[(size_t)b * H + i] = xb[i] * inv * w[i];
+    const float inv = 1.0f / sqrtf(sb_block_sum(ss, red) / (float)H + eps);   // its barriers order xb
+    sb_norm_out(xb, H, inv, w, h ? h + (size_t)b * H : nullptr, b, XP, XS, cmax);
 }
 
 // grid (ceil(I/256), B): a[b][i] = silu(gu[b][2i]) * gu[b][2i+1] (gate and up
@@ -131,6 +190,49 @@ k_swiglu_batch(const float* __restrict__ gu, int nslab, size_t slab, int I, floa
         }
         a[(size_t)b * I + i] = v.x * __builtin_amdgcn_rcpf(1.0f + __expf(-v.x)) * v.y;
     }
+}
+
+// grid (chunks of I, B), 128 threads: a = silu(g) * up of sequence b, chunk
+// by chunk, split for the down product into XP / XS (gate and up rows
+// interleaved; gu as nslab partial products slab floats apart, added in slab
+// order)
+__global__ void __launch_bounds__(128)
+k_swiglu_xp_batch(const float* __restrict__ gu, int nslab, size_t slab, int I, _Float16* __restrict__ XP,
+                  float* __restrict__ XS)
+{
+    __shared__ float red[2];
+    const int c = blockIdx.x, b = blockIdx.y;
+    const int bl = threadIdx.x >> 2, kg = threadIdx.x & 3, blk = c * GBM_KC + bl;
+    const bool in = blk < I / 32;
+    float e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (in) {
+        const float2* g2 = reinterpret_cast<const float2*>(gu + (size_t)b * 2 * I);
+        float a[8];   // elements 4kg .. 4kg+3, then 16+4kg .. 16+4kg+3 of the block
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int i = blk * 32 + 4 * kg + (q < 4 ? q : 12 + q);
+            float2 v = g2[i];
+            for (int k = 1; k < nslab; ++k) {
+                const float2 u = reinterpret_cast<const float2*>(gu + k * slab + (size_t)b * 2 * I)[i];
+                v.x += u.x;
+                v.y += u.y;
+            }
+            a[q] = v.x * __builtin_amdgcn_rcpf(1.0f + __expf(-v.x)) * v.y;
+        }
+        e[0] = a[0];
+        e[1] = a[2];
+        e[2] = a[1];
+        e[3] = a[3];
+        e[4] = a[4] * 0.0625f;
+        e[5] = a[6] * 0.0625f;
+        e[6] = a[5] * 0.0625f;
+        e[7] = a[7] * 0.0625f;
+    }
+    const float s = gbm_scale_for(gbm_chunk_max(gbm_xp_absmax(e), red));
+    if (in)
+        gbm_xp_put(XP, c, bl, kg, b, e, s);
+    if (threadIdx.x == 0)
+        XS[c * 16 + b] = 1.0f / s;
 }
 
 // (value, index) better than (bv, bi): larger value, lowest index among equals
