@@ -499,12 +499,13 @@ static int enqueue_step_fused(qd_model* m, hipStream_t s)
 
 // K slices of a batched step's product of N rows and nb blocks: the row tiles
 // of the matrix-core GEMV alone give too few workgroups for short matrices,
-// so K is cut into slices (whole 32-block chunks) up to about 512 workgroups
+// so K is cut into slices (whole 32-block chunks) up to about 768 workgroups
+// (measured at the Qwen3-8B shapes: gate|up 2 slices, q|k|v and o 4, down 6)
 static int step_kslices(int N, int nb)
 {
     const int tiles = (N + gbm_rows(1) - 1) / gbm_rows(1);
     const int nch = (nb + GBM_KC - 1) / GBM_KC;
-    int ks = std::min({nch, SB_MAXSLAB, std::max(1, (512 + tiles / 2) / tiles)});
+    int ks = std::min({nch, SB_MAXSLAB, std::max(1, (768 + tiles / 2) / tiles)});
     if (ks > 1) {
         const int kch = (nch + ks - 1) / ks;
         ks = (nch + kch - 1) / kch;
@@ -514,7 +515,8 @@ static int step_kslices(int N, int nb)
 
 // the batched step's product Y = W X on the matrix cores from x split in
 // XP / XS, in ks K slices (partial slabs of B*N floats, summed by the
-// consumer); two row groups per wave once one would give 768 workgroups
+// consumer); one row group per wave (two need more registers than a wave
+// has and spill: measured 2-3x slower at every shape of the step)
 static hipError_t step_gemv(const qd_model* m, const DevQ4& W, const _Float16* XP, const float* XS, float* Y,
                             int ks, hipStream_t s)
 {
@@ -524,14 +526,9 @@ static hipError_t step_gemv(const qd_model* m, const DevQ4& W, const _Float16* X
     if (ks < 1 || (int64_t)(ks - 1) * kch >= nch)   // every slice holds at least one chunk
         return hipErrorInvalidValue;
     const int dvec = (nb % 8 == 0 && reinterpret_cast<uintptr_t>(W.d) % 16 == 0) ? 1 : 0;
-    const int t1 = (N + gbm_rows(1) - 1) / gbm_rows(1);
-    const size_t ystride = (size_t)m->B * N;
-    if ((int64_t)t1 * ks >= 768)
-        hipLaunchKernelGGL((k_gemv_batch_xp<2>), dim3((N + gbm_rows(2) - 1) / gbm_rows(2), ks), dim3(GBM_NW * WAVE),
-                           gemv_batch_mfma_lds_bytes(), s, W.d, W.qs, XP, XS, Y, N, nb, m->B, kch, ystride, dvec);
-    else
-        hipLaunchKernelGGL((k_gemv_batch_xp<1>), dim3(t1, ks), dim3(GBM_NW * WAVE), gemv_batch_mfma_lds_bytes(), s,
-                           W.d, W.qs, XP, XS, Y, N, nb, m->B, kch, ystride, dvec);
+    hipLaunchKernelGGL((k_gemv_batch_xp<1>), dim3((N + gbm_rows(1) - 1) / gbm_rows(1), ks), dim3(GBM_NW * WAVE),
+                       gemv_batch_mfma_lds_bytes(), s, W.d, W.qs, XP, XS, Y, N, nb, m->B, kch, (size_t)m->B * N,
+                       dvec);
     return hipGetLastError();
 }
 
