@@ -48,50 +48,71 @@ QD_DEV float sb_block_sum(float v, float* red)
     return s;
 }
 
-// The second pass of the batched RMSNorm: row b of x normalised, x / rms * w,
-// written as f32 to hb (if not null) and split for the batched product into
-// XP / XS (if not null; one split per 32-block chunk, see gemv_batch_mfma.h).
-// H <= 16384 (at most 2 split items per thread); cmax >= 32 floats.
-QD_DEV void sb_norm_out(const float* __restrict__ xb, int H, float inv, const float* __restrict__ w,
-                        float* __restrict__ hb, int b, _Float16* __restrict__ XP, float* __restrict__ XS,
-                        float* cmax)
+// The batched RMSNorm works on items (chunk, block, lane group) of 8
+// elements: 4kg .. 4kg+3 and 16+4kg .. 16+4kg+3 of the block, as the split
+// for the product groups them.  A thread holds at most SB_ITEMS items (item
+// it = thread + u * SB_THREADS), so every load of a row is issued in one
+// round and the values stay in registers between the two passes.
+constexpr int SB_ITEMS = 2;   // H <= 16384
+
+QD_DEV int sb_nitems(int H) { return ((H / 32 + GBM_KC - 1) / GBM_KC) * 128; }
+
+// item it of a row: its chunk, block within the chunk, lane group, block
+QD_DEV void sb_item(int it, int& c, int& bl, int& kg, int& blk)
 {
-    if (hb)
-        for (int i = threadIdx.x; i < H; i += blockDim.x)
-            hb[i] = xb[i] * inv * w[i];
-    if (!XP)
-        return;
-    const int nb = H / 32, nit = ((nb + GBM_KC - 1) / GBM_KC) * 128;   // items (chunk, block, lane group)
-    float e[2][8];
+    c = it >> 7;
+    bl = (it >> 2) & 31;
+    kg = it & 3;
+    blk = c * GBM_KC + bl;
+}
+
+// the second pass: v[u] (element order 4kg.., 16+4kg..) / rms * w of the
+// thread's items, written as f32 to h (if not null) and split into XP / XS
+// (if not null) for the product; cmax >= 32 floats
+QD_DEV void sb_norm_items(const float (&v)[SB_ITEMS][8], const float (&wv)[SB_ITEMS][8], float inv, int H,
+                          int b, float* __restrict__ h, _Float16* __restrict__ XP, float* __restrict__ XS,
+                          float* cmax)
+{
+    const int nb = H / 32, nit = sb_nitems(H);
+    float e[SB_ITEMS][8];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < SB_ITEMS; ++u) {
         const int it = (int)threadIdx.x + u * SB_THREADS;
         if (it < nit) {   // uniform per wave (nit is a multiple of 128)
-            const int c = it >> 7, bl = (it >> 2) & 31, kg = it & 3, blk = c * GBM_KC + bl;
+            int c, bl, kg, blk;
+            sb_item(it, c, bl, kg, blk);
+            float hv[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k)
-                e[u][k] = 0.f;
-            if (blk < nb) {
-                float xe[8], we[8];
-                gbm_xp_gather(xb + (size_t)blk * 32, kg, xe);
-                gbm_xp_gather(w + (size_t)blk * 32, kg, we);
-#pragma unroll
-                for (int k = 0; k < 8; ++k)   // (x / 16) * inv * (w / 16) * 16 = x * inv * w / 16
-                    e[u][k] = k < 4 ? xe[k] * inv * we[k] : (xe[k] * 16.f) * inv * we[k];
+                hv[k] = v[u][k] * inv * wv[u][k];
+            if (h && blk < nb) {
+                float* hp = h + (size_t)b * H + (size_t)blk * 32 + 4 * kg;
+                *reinterpret_cast<float4*>(hp) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+                *reinterpret_cast<float4*>(hp + 16) = make_float4(hv[4], hv[5], hv[6], hv[7]);
             }
-            const float m = group_max<WAVE>(gbm_xp_absmax(e[u]));
-            if ((threadIdx.x & (WAVE - 1)) == 0)
-                cmax[it / WAVE] = m;
+            const float q = 0.0625f;   // the split order (high four divided by 16)
+            const float ev[8] = {hv[0], hv[2], hv[1], hv[3], hv[4] * q, hv[6] * q, hv[5] * q, hv[7] * q};
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                e[u][k] = ev[k];
+            if (XP) {   // uniform
+                const float m = group_max<WAVE>(gbm_xp_absmax(e[u]));
+                if ((threadIdx.x & (WAVE - 1)) == 0)
+                    cmax[it / WAVE] = m;
+            }
         }
     }
+    if (!XP)
+        return;
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < SB_ITEMS; ++u) {
         const int it = (int)threadIdx.x + u * SB_THREADS;
         if (it < nit) {
-            const int c = it >> 7, bl = (it >> 2) & 31, kg = it & 3;
+            int c, bl, kg, blk;
+            sb_item(it, c, bl, kg, blk);
             const float s = gbm_scale_for(fmaxf(cmax[2 * c], cmax[2 * c + 1]));
-            if (c * GBM_KC + bl < nb)
+            if (blk < nb)
                 gbm_xp_put(XP, c, bl, kg, b, e[u], s);
             if ((it & 127) == 0)
                 XS[c * 16 + b] = 1.0f / s;
@@ -101,7 +122,7 @@ QD_DEV void sb_norm_out(const float* __restrict__ xb, int H, float inv, const fl
 
 // grid B: sequence b at its position st[b].pos reads its stored token, writes
 // x[b] (the embedding row) and x[b] / rms * w (to h and/or XP / XS, as
-// sb_norm_out), and the rotary factors of its position (cos [half] then sin
+// sb_norm_items), and the rotary factors of its position (cos [half] then sin
 // [half]) at rope_cur + b * rstride.  A position or token out of range is
 // recorded in st[b].error and replaced by 0 (reported by qd_check).
 __global__ void __launch_bounds__(SB_THREADS)
@@ -130,25 +151,48 @@ k_embed_batch(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, i
         rope_cur[(size_t)b * rstride + k] = rope_cos[(size_t)pos * half + k];
         rope_cur[(size_t)b * rstride + half + k] = rope_sin[(size_t)pos * half + k];
     }
-    const int nb = H / 32;
+    const int nb = H / 32, nit = sb_nitems(H);
     float* xb = x + (size_t)b * H;
+    float v[SB_ITEMS][8], wv[SB_ITEMS][8];
     float ss = 0.f;
-    for (int i = threadIdx.x; i < H; i += blockDim.x) {
-        const int bk = i >> 5, j = i & 31;
-        const size_t blk = (size_t)tok * nb + bk;
-        const uint8_t byte = Eq[blk * 16 + (j & 15)];
-        const int code = (j < 16) ? (byte & 15) : (byte >> 4);
-        const float v = (float)(code - 8) * f16_to_f32(Ed[blk]);
-        xb[i] = v;
-        ss = fmaf(v, v, ss);
+#pragma unroll
+    for (int u = 0; u < SB_ITEMS; ++u) {
+        const int it = (int)threadIdx.x + u * SB_THREADS;
+        int c, bl, kg, blk;
+        sb_item(it, c, bl, kg, blk);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            v[u][k] = wv[u][k] = 0.f;
+        if (it < nit && blk < nb) {
+            // word kg of the token's block: codes of elements 4kg.. (low nibbles) and 16+4kg.. (high)
+            const size_t blkg = (size_t)tok * nb + blk;
+            const uint32_t wd = *reinterpret_cast<const uint32_t*>(Eq + blkg * 16 + 4 * kg);
+            const float d = f16_to_f32(Ed[blkg]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[u][k] = (float)((int)((wd >> (8 * k)) & 15u) - 8) * d;
+                v[u][4 + k] = (float)((int)((wd >> (8 * k + 4)) & 15u) - 8) * d;
+            }
+            float* xp = xb + (size_t)blk * 32 + 4 * kg;
+            *reinterpret_cast<float4*>(xp) = make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
+            *reinterpret_cast<float4*>(xp + 16) = make_float4(v[u][4], v[u][5], v[u][6], v[u][7]);
+            const float4 wa = *reinterpret_cast<const float4*>(w + (size_t)blk * 32 + 4 * kg);
+            const float4 wh = *reinterpret_cast<const float4*>(w + (size_t)blk * 32 + 16 + 4 * kg);
+            const float wl[8] = {wa.x, wa.y, wa.z, wa.w, wh.x, wh.y, wh.z, wh.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                wv[u][k] = wl[k];
+                ss = fmaf(v[u][k], v[u][k], ss);
+            }
+        }
     }
-    const float inv = 1.0f / sqrtf(sb_block_sum(ss, red) / (float)H + eps);   // its barriers order xb
-    sb_norm_out(xb, H, inv, w, h ? h + (size_t)b * H : nullptr, b, XP, XS, cmax);
+    const float inv = 1.0f / sqrtf(sb_block_sum(ss, red) / (float)H + eps);
+    sb_norm_items(v, wv, inv, H, b, h, XP, XS, cmax);
 }
 
-// grid B: x[b] += y[b] (y may be null: no residual; y may come as nslab
-// partial products slab floats apart, added in slab order); x[b] / rms * w to
-// h and/or XP / XS (as sb_norm_out)
+// grid B: x[b] += y[b] (y may be null: no residual; y may come as nslab <=
+// SB_MAXSLAB partial products slab floats apart, added in slab order);
+// x[b] / rms * w to h and/or XP / XS (as sb_norm_items)
 __global__ void __launch_bounds__(SB_THREADS)
 k_resid_rmsnorm_batch(float* __restrict__ x, const float* __restrict__ y, int nslab, size_t slab, int H,
                       const float* __restrict__ w, float eps, float* __restrict__ h,
@@ -157,39 +201,54 @@ k_resid_rmsnorm_batch(float* __restrict__ x, const float* __restrict__ y, int ns
     __shared__ float red[16];
     __shared__ float cmax[32];
     const int b = blockIdx.x;
+    const int nb = H / 32, nit = sb_nitems(H);
     float* xb = x + (size_t)b * H;
+    float v[SB_ITEMS][8], wv[SB_ITEMS][8];
     float ss = 0.f;
-    for (int i = threadIdx.x; i < H; i += blockDim.x) {
-        float v = xb[i];
-        if (y) {   // uniform
-            float r = y[(size_t)b * H + i];
-            for (int k = 1; k < nslab; ++k)
-                r += y[k * slab + (size_t)b * H + i];
-            v += r;
-            xb[i] = v;
+#pragma unroll
+    for (int u = 0; u < SB_ITEMS; ++u) {
+        const int it = (int)threadIdx.x + u * SB_THREADS;
+        int c, bl, kg, blk;
+        sb_item(it, c, bl, kg, blk);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            v[u][k] = wv[u][k] = 0.f;
+        if (it < nit && blk < nb) {
+            const size_t off = (size_t)blk * 32 + 4 * kg;
+            float4 a = *reinterpret_cast<const float4*>(xb + off);
+            float4 e = *reinterpret_cast<const float4*>(xb + off + 16);
+            const float4 wa = *reinterpret_cast<const float4*>(w + off);
+            const float4 wh = *reinterpret_cast<const float4*>(w + off + 16);
+            if (y) {   // uniform
+                const float* yb = y + (size_t)b * H + off;
+                float4 ra = *reinterpret_cast<const float4*>(yb);
+                float4 re = *reinterpret_cast<const float4*>(yb + 16);
+#pragma unroll
+                for (int k = 1; k < SB_MAXSLAB; ++k) {
+                    if (k < nslab) {   // uniform
+                        const float4 pa = *reinterpret_cast<const float4*>(yb + k * slab);
+                        const float4 pe = *reinterpret_cast<const float4*>(yb + k * slab + 16);
+                        ra = make_float4(ra.x + pa.x, ra.y + pa.y, ra.z + pa.z, ra.w + pa.w);
+                        re = make_float4(re.x + pe.x, re.y + pe.y, re.z + pe.z, re.w + pe.w);
+                    }
+                }
+                a = make_float4(a.x + ra.x, a.y + ra.y, a.z + ra.z, a.w + ra.w);
+                e = make_float4(e.x + re.x, e.y + re.y, e.z + re.z, e.w + re.w);
+                *reinterpret_cast<float4*>(xb + off) = a;
+                *reinterpret_cast<float4*>(xb + off + 16) = e;
+            }
+            const float vl[8] = {a.x, a.y, a.z, a.w, e.x, e.y, e.z, e.w};
+            const float wl[8] = {wa.x, wa.y, wa.z, wa.w, wh.x, wh.y, wh.z, wh.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                v[u][k] = vl[k];
+                wv[u][k] = wl[k];
+                ss = fmaf(vl[k], vl[k], ss);
+            }
         }
-        ss = fmaf(v, v, ss);
     }
-    const float inv = 1.0f / sqrtf(sb_block_sum(ss, red) / (float)H + eps);   // its barriers order xb
-    sb_norm_out(xb, H, inv, w, h ? h + (size_t)b * H : nullptr, b, XP, XS, cmax);
-}
-
-// grid (ceil(I/256), B): a[b][i] = silu(gu[b][2i]) * gu[b][2i+1] (gate and up
-// rows interleaved as in the one-sequence step; gu as nslab partial products
-// slab floats apart, added in slab order)
-__global__ void __launch_bounds__(256)
-k_swiglu_batch(const float* __restrict__ gu, int nslab, size_t slab, int I, float* __restrict__ a)
-{
-    const int b = blockIdx.y, i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < I) {
-        float2 v = reinterpret_cast<const float2*>(gu + (size_t)b * 2 * I)[i];
-        for (int k = 1; k < nslab; ++k) {
-            const float2 u = reinterpret_cast<const float2*>(gu + k * slab + (size_t)b * 2 * I)[i];
-            v.x += u.x;
-            v.y += u.y;
-        }
-        a[(size_t)b * I + i] = v.x * __builtin_amdgcn_rcpf(1.0f + __expf(-v.x)) * v.y;
-    }
+    const float inv = 1.0f / sqrtf(sb_block_sum(ss, red) / (float)H + eps);
+    sb_norm_items(v, wv, inv, H, b, h, XP, XS, cmax);
 }
 
 // grid (chunks of I, B), 128 threads: a = silu(g) * up of sequence b, chunk
