@@ -94,6 +94,13 @@ template <int NC>
 static hipError_t launch_gemv_batch_mfma(const uint16_t* d, const uint8_t* q, const float* x, float* y,
                                          int N, int nb, hipStream_t s, int ks = 1);
 
+// workgroups of the attention of a batched decode step over all its sequences
+// (measured at the Qwen3-8B shape, 16 / 8 / 4 sequences at kv_len ~550:
+// 256 against 64 .. 2048 is the fastest for each)
+#ifndef QD_ATT_BATCH_WGS
+#define QD_ATT_BATCH_WGS 256
+#endif
+
 // ------------------------------------------------------------------ model
 
 struct DevQ4 {
@@ -925,10 +932,9 @@ static int create_model(const qd_config* cfg, const qd_weights* w, int B, qd_str
         m->lpr_lm = pick_lpr(nbH);
         m->grid_lm = gemv_grid(CFG_HEAD, m->lpr_lm, m->V);
         // attention: splits over max_seq (the grid does not depend on the position),
-        // about one workgroup per CU
-        // (B sequences: about two workgroups per CU over all of them)
+        // about one workgroup per CU (B sequences: as many over all of them)
         const int gq = m->nq / m->nkv;
-        const AttnGeom ag = attn_geom(B, m->nkv, m->max_seq, B == 1 ? ATT_MODEL_WGS : 512,
+        const AttnGeom ag = attn_geom(B, m->nkv, m->max_seq, B == 1 ? ATT_MODEL_WGS : QD_ATT_BATCH_WGS,
                                       gq <= 4 ? QD_ATT_MODEL_WAVES : 4, 0);
         m->attn_waves = ag.waves;
         m->attn_chunk = ag.chunk;
