@@ -185,14 +185,16 @@ int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* d_tokens,
  * Continue with qd_generate(pos0 + n, ...).  Buffers (about 16 positions of
  * activations plus an attention workspace) are allocated by the first call,
  * which synchronises; later calls allocate nothing.  The matrix products
- * take each position's activations as an f16 pair (hi + lo, about 22
- * significant bits) after scaling the position's vector by a power of two
- * that puts its largest magnitude in [2^13, 2^14), undone exactly in f32, so
- * any finite activation scale is handled; the block scales d are applied in
- * f32.  A model with attn_out_gate gates each position's attention output as the
- * decode step does.  QD_ERANGE unless 0 <= pos0, n >= 1, pos0 + n <= max_seq
- * and pos0 is at most one past the written prefix; afterwards the prefix is
- * 0 .. pos0+n-1. */
+ * are those of the batched decode step with the chunk's positions as its
+ * vectors: each position's activations enter as an f16 pair (hi + lo, about
+ * 22 significant bits) after scaling each 1024-element chunk of the position's
+ * vector by a power of two that puts its largest magnitude in [2^13, 2^14),
+ * undone exactly in f32, so any finite activation scale is handled; the block
+ * scales d are applied in f32.  A model with attn_out_gate gates each
+ * position's attention output as the decode step does.  hidden <= 16384
+ * (QD_EUNSUPPORTED otherwise).  QD_ERANGE unless 0 <= pos0, n >= 1,
+ * pos0 + n <= max_seq and pos0 is at most one past the written prefix;
+ * afterwards the prefix is 0 .. pos0+n-1. */
 int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_last, qd_stream stream);
 
 /* Batched decode (inferencelayer cuda_llm.rs page, step_batch_inner and its
@@ -206,8 +208,8 @@ int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_last, qd_st
  * [b * ceil(max_seq/16)], all distinct and below num_kv_blocks.  Each
  * sequence's step computes what qd_decode_step computes for it (up to f32
  * rounding order: the RMSNorm is applied to the activations before the
- * batched GEMV instead of after it).  Not with layer_kernel or attn_out_gate;
- * every weight scale must satisfy |d| < 8192 (QD_EUNSUPPORTED otherwise).
+ * batched GEMV instead of after it).  Not with layer_kernel or attn_out_gate,
+ * and hidden <= 16384 (QD_EUNSUPPORTED otherwise).
  * The one-sequence entry points (qd_decode_step, qd_set_prompt, qd_generate,
  * qd_prefill) refuse a batched model and the batch entry points below refuse
  * a one-sequence model (QD_EINVAL).  Synchronous; *out receives the handle. */
@@ -249,10 +251,11 @@ int qd_gemv_q4_0(const uint16_t* d_scales, const uint8_t* d_qs, const float* d_x
  * 16-byte aligned.  1 <= B <= 16; B == 1 runs the single-vector kernel,
  * 2 <= B <= 5 a vector kernel that stages the whole batch in LDS when
  * B*K <= 32 768, otherwise (and always for B >= 6) the matrix cores: any K,
- * the weight scales must satisfy |d| < 8192 (since (code - 8) * d is formed
- * in f16), and x enters as an f16 pair (about 22 significant bits) after a
- * power-of-two scaling per vector and 1024-element chunk, undone exactly in
- * f32, so any finite input scale is handled.  N < 2^24, N*K/2 < 2^32.
+ * one product per q4_0 block with the codes as exact f16 values and the
+ * block's scale applied to the product in f32, and x as an f16 pair (about
+ * 22 significant bits) after a power-of-two scaling per vector and
+ * 1024-element chunk, undone exactly in f32, so any finite input scale is
+ * handled.  N < 2^24, N*K/2 < 2^32.
  * QD_EINVAL / QD_EUNSUPPORTED otherwise, with nothing enqueued.  The
  * summation order differs from the single-vector GEMV.  No allocation;
  * capturable. */

@@ -404,7 +404,7 @@ __global__ void __launch_bounds__(FUSED_THREADS) k_layer_fused(FusedArgs a, int 
     const FusedBarrier bar{a.bar, a.err, &broken, a.spin_limit};
     const unsigned nbar0 = 4u * (unsigned)l;
     unsigned nbar = nbar0;   // barriers completed before the phase to come
-    int phase = 0;   // marks 3 phase (entry), 3 phase + 1 (after the wait), 3 phase + 2 (end)
+    [[maybe_unused]] int phase = 0;   // marks 3 phase (entry), 3 phase + 1 (after the wait), 3 phase + 2 (end)
     auto wait = [&] {
         if (nbar > nbar0)   // the layer's first phase follows a kernel boundary
             bar.wait(nbar);

@@ -398,22 +398,6 @@ k_gemv_batch_mfma(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
 // global-to-LDS loads: no registers, no arithmetic, once per workgroup.
 constexpr int GBM_XP_CHUNK = GBM_KC * 4 * 2 * 16 * 8;   // halves per chunk
 
-// the 8 elements of lane group kg of the block at xb, in the K slot order
-// (the high four divided by 16)
-QD_DEV void gbm_xp_gather(const float* __restrict__ xb, int kg, float (&e)[8])
-{
-    const float4 a = *reinterpret_cast<const float4*>(xb + 4 * kg);
-    const float4 h = *reinterpret_cast<const float4*>(xb + 16 + 4 * kg);
-    e[0] = a.x;
-    e[1] = a.z;
-    e[2] = a.y;
-    e[3] = a.w;
-    e[4] = h.x * 0.0625f;
-    e[5] = h.z * 0.0625f;
-    e[6] = h.y * 0.0625f;
-    e[7] = h.w * 0.0625f;
-}
-
 // largest |.| of the 8 elements in slot order (the high four undone)
 QD_DEV float gbm_xp_absmax(const float (&e)[8])
 {
@@ -451,17 +435,45 @@ QD_DEV float gbm_chunk_max(float m, float* red)
     return fmaxf(red[0], red[1]);
 }
 
-// grid (chunks, B), 128 threads: vector b of X [B][nb * 32] into XP / XS
+// grid (chunks, B), 128 threads: vector b of X [B][nb * 32] into XP / XS.
+// With a gate (vector b's at gate + b * gstride, as ngslab partial products
+// gslab floats apart, added in slab order) x is first multiplied by
+// sigmoid(gate), as the decode step gates the merged attention output.
 __global__ void __launch_bounds__(128)
-k_xsplit_batch(const float* __restrict__ X, int nb, _Float16* __restrict__ XP, float* __restrict__ XS)
+k_xsplit_batch(const float* __restrict__ X, int nb, _Float16* __restrict__ XP, float* __restrict__ XS,
+               const float* __restrict__ gate = nullptr, int gstride = 0, int ngslab = 1, size_t gslab = 0)
 {
     __shared__ float red[2];
     const int c = blockIdx.x, b = blockIdx.y;
     const int bl = threadIdx.x >> 2, kg = threadIdx.x & 3, blk = c * GBM_KC + bl;
     const bool in = blk < nb;
     float e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (in)
-        gbm_xp_gather(X + (size_t)b * nb * 32 + (size_t)blk * 32, kg, e);
+    if (in) {
+        const size_t off = (size_t)blk * 32 + 4 * kg;
+        float xv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const size_t i = off + (k < 4 ? k : 12 + k);   // elements 4kg.., then 16+4kg..
+            float x = X[(size_t)b * nb * 32 + i];
+            if (gate) {   // uniform
+                const float* gp = gate + (size_t)b * gstride + i;
+                float g = gp[0];
+                for (int q = 1; q < ngslab; ++q)
+                    g += gp[q * gslab];
+                x *= 1.0f / (1.0f + expf(-g));
+            }
+            xv[k] = x;
+        }
+        const float q = 0.0625f;
+        e[0] = xv[0];
+        e[1] = xv[2];
+        e[2] = xv[1];
+        e[3] = xv[3];
+        e[4] = xv[4] * q;
+        e[5] = xv[6] * q;
+        e[6] = xv[5] * q;
+        e[7] = xv[7] * q;
+    }
     const float s = gbm_scale_for(gbm_chunk_max(gbm_xp_absmax(e), red));
     if (in)
         gbm_xp_put(XP, c, bl, kg, b, e, s);

@@ -1,12 +1,14 @@
-// prefill_kernels.h -- the elementwise and per-row kernels of a chunked
-// prefill (gfx950): T <= 16 prompt positions at a time, every weight read once
-// per chunk by the batched GEMV, the same arithmetic per position as the
-// decode step (inferencelayer cuda_llm.rs page: prefill as the M > 1 form of
-// the step; the step's order of operations).
+// prefill_kernels.h -- the kernels of a chunked prefill (gfx950) of its own:
+// T <= 16 prompt positions at a time, every weight read once per chunk by the
+// batched GEMV on split inputs (gemv_batch_mfma.h: the positions are its
+// vectors), the norms, SwiGLU and splits of the batched decode step
+// (step_batch.h), the same arithmetic per position as the decode step
+// (inferencelayer cuda_llm.rs page: prefill as the M > 1 form of the step; the
+// step's order of operations).  Here: the embedding rows, the per-head q/k
+// norm + rotary + K/V store, and the index table of the greedy pick.
 #pragma once
 
 #include "step_kernels.h"
-#include "prefill_gemm.h"
 
 namespace qd {
 
@@ -30,22 +32,6 @@ k_pf_embed(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, int 
     X[(size_t)t * H + i] = (float)(code - 8) * f16_to_f32(Ed[blk]);
 }
 
-// out[t] = X[t] * (1 / sqrt(mean(X[t]^2) + eps)) * w; grid T, 256 threads
-__global__ void __launch_bounds__(256)
-k_pf_rmsnorm(const float* __restrict__ X, const float* __restrict__ w, int H, float eps,
-             float* __restrict__ out)
-{
-    __shared__ float red[8];
-    const float* x = X + (size_t)blockIdx.x * H;
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < H; i += blockDim.x)
-        ss = fmaf(x[i], x[i], ss);
-    ss = block_sum256(ss, red);
-    const float r = 1.0f / sqrtf(ss / (float)H + eps);
-    for (int i = threadIdx.x; i < H; i += blockDim.x)
-        out[(size_t)blockIdx.x * H + i] = x[i] * r * w[i];
-}
-
 // Per position t (grid.y) and head (grid.x: nq query heads, then nkv kv heads),
 // one wave per head: q/k RMSNorm over the head (if qk_norm), NeoX rotary at
 // position p0 + t from the tables, then q -> Qr[t][h], and for a kv head K and
@@ -58,20 +44,27 @@ k_pf_qk(const float* __restrict__ QKV, int qkv_rows, int nq, int nkv, const floa
         const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int p0,
         float* __restrict__ Qr, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
         const int32_t* __restrict__ table, int max_seq, float k_scale, float v_scale,
-        int32_t* __restrict__ kv_lens)
+        int32_t* __restrict__ kv_lens, int nslab, size_t slab)
 {
     constexpr int DPL = HD / WAVE;
     const int t = blockIdx.y, hh = blockIdx.x, lane = threadIdx.x;
     const int pos = p0 + t;
     const bool is_q = hh < nq;
     const int g = hh - nq;
+    // QKV may come as nslab partial products slab floats apart: added in slab order
+    auto ld = [&](const float* p) {
+        float a = p[0];
+        for (int k = 1; k < nslab; ++k)
+            a += p[k * slab];
+        return a;
+    };
     const float* src = QKV + (size_t)t * qkv_rows + (size_t)(is_q ? hh : nq + g) * HD;
     const float* w = is_q ? q_norm : k_norm;
     float v[DPL];
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
-        v[e] = src[lane * DPL + e];
+        v[e] = ld(src + lane * DPL + e);
         ss = fmaf(v[e], v[e], ss);
     }
     ss = group_sum<WAVE>(ss);
@@ -108,7 +101,7 @@ k_pf_qk(const float* __restrict__ QKV, int qkv_rows, int nq, int nkv, const floa
 #pragma unroll
         for (int e = 0; e < DPL; ++e) {
             const int d = lane * DPL + e;
-            const float vv = vsrc[d];
+            const float vv = ld(vsrc + d);
             if (KV8) {
                 reinterpret_cast<uint8_t*>(kc)[o + d] = (uint8_t)f32_to_e4m3(v[e] / k_scale);
                 reinterpret_cast<uint8_t*>(vc)[o + d] = (uint8_t)f32_to_e4m3(vv / v_scale);

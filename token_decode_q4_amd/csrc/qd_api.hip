@@ -139,9 +139,14 @@ struct qd_model {
     int hw = -1;
     // chunked prefill buffers (allocated by the first qd_prefill)
     struct {
-        float *X = nullptr, *QKV = nullptr, *Q = nullptr, *O = nullptr, *hf = nullptr, *A = nullptr;
-        _Float16 *XP1 = nullptr, *XP2 = nullptr;   // split activations (prefill_gemm.h)
-        float *XS1 = nullptr, *XS2 = nullptr;      // their per-position scales
+        float *X = nullptr, *Q = nullptr, *O = nullptr, *HF = nullptr;
+        // the products' outputs as K-slice partial slabs: q|k|v, o and down, gate|up
+        float *QKV = nullptr, *OD = nullptr, *GU = nullptr;
+        int ks_qkv = 1, ks_o = 1, ks_gu = 1, ks_down = 1;
+        // the products' inputs split (gemv_batch_mfma.h), one vector slot per
+        // position: hidden-sized, attention output, SwiGLU output
+        _Float16 *xp_h = nullptr, *xp_o = nullptr, *xp_i = nullptr;
+        float *xs_h = nullptr, *xs_o = nullptr, *xs_i = nullptr;
         float* fa = nullptr;                       // k_pf_attn partials [T][nq][FA_MAXS][hd + 2]
         int32_t *lens = nullptr, *iota = nullptr;
         float* ws = nullptr;
@@ -385,25 +390,6 @@ static int validate_config(const qd_config* c, const qd_weights* w, int B)
         return fail(QD_EUNSUPPORTED, "a batched model supports neither layer_kernel nor attn_out_gate");
     if (B > 1 && c->hidden > 16384)   // the batched RMSNorm splits at most 2 items per thread
         return fail(QD_EUNSUPPORTED, "a batched model supports hidden <= 16384 (got %d)", c->hidden);
-    if (B > 1) {
-        // the matrix-core batched GEMV forms (code - 8) * d in f16
-        auto scales_ok = [](const qd_q4_0& q) {
-            const size_t n = (size_t)q.rows * (q.cols / 32);
-            for (size_t i = 0; i < n; ++i)
-                if ((q.d[i] & 0x7fff) >= 0x7000)   // |d| >= 8192, infinity or NaN
-                    return false;
-            return true;
-        };
-        bool ok = scales_ok(w->embed) && (c->tied || scales_ok(w->lm_head));
-        for (int l = 0; ok && l < c->layers; ++l) {
-            const qd_layer_weights& L = w->layers[l];
-            ok = scales_ok(L.wq) && scales_ok(L.wk) && scales_ok(L.wv) && scales_ok(L.wo) &&
-                 scales_ok(L.wgate) && scales_ok(L.wup) && scales_ok(L.wdown);
-        }
-        if (!ok)
-            return fail(QD_EUNSUPPORTED, "a batched model needs every weight scale |d| < 8192 "
-                                         "(the matrix-core GEMV forms (code - 8) * d in f16)");
-    }
     if (c->kv_fp8) {
         if (!(c->k_scale > 0.f) || !(c->v_scale > 0.f) || !std::isfinite(c->k_scale) ||
             !std::isfinite(c->v_scale))
@@ -1683,32 +1669,6 @@ extern "C" int qd_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink,
 
 // ------------------------------------------------------------------ chunked prefill
 
-// Y[t] = W x[t] for the chunk's positions on the matrix cores (k_pf_gemm).
-// Launch shapes measured at the Qwen3-8B matrices (16 positions): 4 waves of
-// 2 row slices for the tall gate|up (24576 rows), 8 waves of 2 slices for
-// q|k|v (6144 rows), 8 waves of 1 slice below 6144 rows.
-template <int MODE>
-static hipError_t pf_gemm(const DevQ4& W, const _Float16* XP, const float* XS, int T, float* Y, hipStream_t s)
-{
-    const int N = W.rows, nb = W.nb, g1 = (N + 15) / 16;
-#ifdef QD_PG_FORCE   // compile-time override: rows slices per wave, waves per workgroup
-    constexpr int FR[2] = {QD_PG_FORCE};
-    hipLaunchKernelGGL((k_pf_gemm<FR[0], FR[1], MODE>), dim3((N + 16 * FR[0] - 1) / (16 * FR[0])),
-                       dim3(FR[1] * WAVE), 0, s, W.d, W.qs, XP, XS, N, nb, T, Y);
-    return hipGetLastError();
-#endif
-    if (g1 >= 1024)
-        hipLaunchKernelGGL((k_pf_gemm<2, 4, MODE>), dim3((N + 31) / 32), dim3(4 * WAVE), 0, s, W.d, W.qs, XP, XS,
-                           N, nb, T, Y);
-    else if (g1 >= 384)
-        hipLaunchKernelGGL((k_pf_gemm<2, 8, MODE>), dim3((N + 31) / 32), dim3(8 * WAVE), 0, s, W.d, W.qs, XP, XS,
-                           N, nb, T, Y);
-    else
-        hipLaunchKernelGGL((k_pf_gemm<1, 8, MODE>), dim3(g1), dim3(8 * WAVE), 0, s, W.d, W.qs, XP, XS, N, nb, T,
-                           Y);
-    return hipGetLastError();
-}
-
 // Chunk attention with each K/V tile read once for the chunk's queries
 // (k_pf_attn, f16 caches): about 256 workgroups over the keys 0 .. p0+T-1,
 // at most PF_FA_MAXS splits of a multiple of 16 keys, then the combine.
@@ -1759,30 +1719,59 @@ static int pf_setup(qd_model* m)
     if (m->pf.ready)
         return QD_OK;
     auto& P = m->pf;
-    const size_t T = PF_T, nqd = (size_t)m->nq * m->hd;
+    const size_t T = PF_T, nqd = (size_t)m->nq * m->hd, H = m->H, I = m->I;
     const size_t ws = attn_ws_layout(PF_T, m->nq, m->nkv, m->hd, m->max_seq, &P.geo);
+    if (m->H > 16384)   // the batched RMSNorm splits at most 2 items per thread
+        return fail(QD_EUNSUPPORTED, "qd_prefill supports hidden <= 16384 (got %d)", m->H);
+    P.ks_qkv = step_kslices(m->qkv_rows, m->H / 32);
+    P.ks_o = step_kslices(m->H, (int)nqd / 32);
+    P.ks_gu = step_kslices(2 * m->I, m->H / 32);
+    P.ks_down = step_kslices(m->H, m->I / 32);
+    const size_t ch_h = (H / 32 + GBM_KC - 1) / GBM_KC, ch_o = (nqd / 32 + GBM_KC - 1) / GBM_KC,
+                 ch_i = (I / 32 + GBM_KC - 1) / GBM_KC;
     int rc;
-    const size_t kx = std::max((size_t)m->H, nqd);
-    if ((rc = dev_alloc_t(m, &P.X, T * m->H)) || (rc = dev_alloc_t(m, &P.QKV, T * m->qkv_rows)) ||
-        (rc = dev_alloc_t(m, &P.Q, T * nqd)) || (rc = dev_alloc_t(m, &P.O, T * nqd)) ||
-        (rc = dev_alloc_t(m, &P.XP1, T * kx * 2)) || (rc = dev_alloc_t(m, &P.XP2, T * (size_t)m->I * 2)) ||
-        (rc = dev_alloc_t(m, &P.A, T * (size_t)m->I)) || (rc = dev_alloc_t(m, &P.XS1, T)) ||
+    if ((rc = dev_alloc_t(m, &P.X, T * H)) || (rc = dev_alloc_t(m, &P.Q, T * nqd)) ||
+        (rc = dev_alloc_t(m, &P.O, T * nqd)) || (rc = dev_alloc_t(m, &P.HF, T * H)) ||
+        (rc = dev_alloc_t(m, &P.QKV, (size_t)P.ks_qkv * T * m->qkv_rows)) ||
+        (rc = dev_alloc_t(m, &P.OD, (size_t)std::max(P.ks_o, P.ks_down) * T * H)) ||
+        (rc = dev_alloc_t(m, &P.GU, (size_t)P.ks_gu * T * 2 * I)) ||
+        (rc = dev_alloc_t(m, &P.xp_h, ch_h * GBM_XP_CHUNK)) || (rc = dev_alloc_t(m, &P.xp_o, ch_o * GBM_XP_CHUNK)) ||
+        (rc = dev_alloc_t(m, &P.xp_i, ch_i * GBM_XP_CHUNK)) || (rc = dev_alloc_t(m, &P.xs_h, ch_h * 16)) ||
+        (rc = dev_alloc_t(m, &P.xs_o, ch_o * 16)) || (rc = dev_alloc_t(m, &P.xs_i, ch_i * 16)) ||
         (rc = dev_alloc_t(m, &P.fa, T * nqd / m->hd * PF_FA_MAXS * (m->hd + 2))) ||
-        (rc = dev_alloc_t(m, &P.XS2, T)) ||
-        (rc = dev_alloc_t(m, &P.hf, (size_t)m->H)) || (rc = dev_alloc_t(m, &P.lens, T)) ||
-        (rc = dev_alloc_t(m, &P.iota, (size_t)m->V)) || (rc = dev_alloc_t(m, &P.ws, ws / sizeof(float) + 1)))
+        (rc = dev_alloc_t(m, &P.lens, T)) || (rc = dev_alloc_t(m, &P.iota, (size_t)m->V)) ||
+        (rc = dev_alloc_t(m, &P.ws, ws / sizeof(float) + 1)))
         return rc;
     hipLaunchKernelGGL(k_pf_iota, dim3((m->V + 255) / 256), dim3(256), 0, 0, P.iota, m->V);
-    // positions past a short chunk read these rows and scales: keep them finite
-    if (hipMemset(P.XP1, 0, T * kx * 2 * sizeof(_Float16)) != hipSuccess ||
-        hipMemset(P.XP2, 0, T * (size_t)m->I * 2 * sizeof(_Float16)) != hipSuccess ||
-        hipMemset(P.XS1, 0, T * sizeof(float)) != hipSuccess ||
-        hipMemset(P.XS2, 0, T * sizeof(float)) != hipSuccess)
+    // the split inputs are read for all 16 slots: slots past a short chunk
+    // (stale from an earlier chunk, or zero) only feed outputs never written
+    if (hipMemset(P.xp_h, 0, ch_h * GBM_XP_CHUNK * sizeof(_Float16)) != hipSuccess ||
+        hipMemset(P.xp_o, 0, ch_o * GBM_XP_CHUNK * sizeof(_Float16)) != hipSuccess ||
+        hipMemset(P.xp_i, 0, ch_i * GBM_XP_CHUNK * sizeof(_Float16)) != hipSuccess ||
+        hipMemset(P.xs_h, 0, ch_h * 16 * sizeof(float)) != hipSuccess ||
+        hipMemset(P.xs_o, 0, ch_o * 16 * sizeof(float)) != hipSuccess ||
+        hipMemset(P.xs_i, 0, ch_i * 16 * sizeof(float)) != hipSuccess)
         return fail(QD_EHIP, "prefill buffer set-up failed");
     if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess)
         return fail(QD_EHIP, "prefill buffer set-up failed");
     P.ready = true;
     return QD_OK;
+}
+
+// the chunk's product Y = W X on the matrix cores from x split in XP / XS,
+// T positions (vector slots), in ks K slices (partial slabs of T*N floats)
+static hipError_t pf_gemv(const DevQ4& W, const _Float16* XP, const float* XS, int T, float* Y, int ks,
+                          hipStream_t s)
+{
+    const int N = W.rows, nb = W.nb;
+    const int nch = (nb + GBM_KC - 1) / GBM_KC;
+    const int kch = (nch + ks - 1) / ks;
+    if (ks < 1 || (int64_t)(ks - 1) * kch >= nch)
+        return hipErrorInvalidValue;
+    const int dvec = (nb % 8 == 0 && reinterpret_cast<uintptr_t>(W.d) % 16 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((k_gemv_batch_xp<1>), dim3((N + gbm_rows(1) - 1) / gbm_rows(1), ks), dim3(GBM_NW * WAVE),
+                       gemv_batch_mfma_lds_bytes(), s, W.d, W.qs, XP, XS, Y, N, nb, T, kch, (size_t)T * N, dvec);
+    return hipGetLastError();
 }
 
 extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_last, qd_stream stream)
@@ -1800,17 +1789,20 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
     const hipStream_t s = (hipStream_t)stream;
     const int H = m->H, hd = m->hd, gq = m->nq / m->nkv;
     const int mbps = (m->max_seq + ATT_BS - 1) / ATT_BS;
+    const int nqd = m->nq * hd, I = m->I;
     int T = 0;
     for (int c0 = 0; c0 < n; c0 += PF_T) {
         T = std::min(PF_T, n - c0);
         const int p0 = pos0 + c0;
+        const size_t slab_h = (size_t)T * H;
         hipLaunchKernelGGL(k_pf_embed, dim3((H + 255) / 256, T), dim3(256), 0, s, m->embed.d, m->embed.qs,
                            H, m->ids, p0, P.X);
+        hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(T), dim3(SB_THREADS), 0, s, P.X, nullptr, 0, (size_t)0,
+                           H, m->layers[0].attn_norm, m->eps, nullptr, P.xp_h, P.xs_h);
         for (int l = 0; l < m->L; ++l) {
             DevLayer& Ly = m->layers[l];
-            hipLaunchKernelGGL(k_pf_rmsnorm_xp, dim3(T), dim3(1024), 0, s, P.X, Ly.attn_norm, H, m->eps, P.XP1,
-                               P.XS1);
-            HIP_TRY(pf_gemm<PG_STORE>(Ly.qkv, P.XP1, P.XS1, T, P.QKV, s));
+            HIP_TRY(pf_gemv(Ly.qkv, P.xp_h, P.xs_h, T, P.QKV, P.ks_qkv, s));
+            const size_t slab_qkv = (size_t)T * m->qkv_rows;
             const float* qn = m->qk_norm ? Ly.q_norm : m->ones_hd;
             const float* kn = m->qk_norm ? Ly.k_norm : m->ones_hd;
             const int32_t* tbl = m->paged ? m->table : nullptr;
@@ -1818,7 +1810,7 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
 #define QD_PFQK(HD_, K8_)                                                                            \
     hipLaunchKernelGGL((k_pf_qk<HD_, K8_>), g, dim3(WAVE), 0, s, P.QKV, m->qkv_rows, m->nq, m->nkv, qn,  \
                        kn, m->qk_norm, m->eps, m->rot, m->rope_cos, m->rope_sin, p0, P.Q, Ly.kc, Ly.vc, \
-                       tbl, m->max_seq, m->k_scale, m->v_scale, P.lens)
+                       tbl, m->max_seq, m->k_scale, m->v_scale, P.lens, P.ks_qkv, slab_qkv)
             if (hd == 128) {
                 if (m->kv_fp8) QD_PFQK(128, true); else QD_PFQK(128, false);
             } else {
@@ -1850,23 +1842,27 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
             } else {
                 pf_attention(m, Ly, p0, T, s);
             }
-            const int kq = m->nq * hd;
             // the gate rows follow q|k|v in the fused product
             const float* gate = m->attn_gate ? P.QKV + (size_t)(m->nq + 2 * m->nkv) * hd : nullptr;
-            hipLaunchKernelGGL(k_pf_xsplit, dim3(T), dim3(1024), 0, s, P.O, kq, gate, m->qkv_rows, P.XP1,
-                               P.XS1);
-            HIP_TRY(pf_gemm<PG_RESID>(Ly.o, P.XP1, P.XS1, T, P.X, s));
-            hipLaunchKernelGGL(k_pf_rmsnorm_xp, dim3(T), dim3(1024), 0, s, P.X, Ly.ffn_norm, H, m->eps, P.XP1,
-                               P.XS1);
-            HIP_TRY(pf_gemm<PG_SWIGLU>(Ly.gu, P.XP1, P.XS1, T, P.A, s));
-            hipLaunchKernelGGL(k_pf_xsplit, dim3(T), dim3(1024), 0, s, P.A, m->I, nullptr, 0, P.XP2, P.XS2);
-            HIP_TRY(pf_gemm<PG_RESID>(Ly.down, P.XP2, P.XS2, T, P.X, s));
+            hipLaunchKernelGGL(k_xsplit_batch, dim3((nqd / 32 + GBM_KC - 1) / GBM_KC, T), dim3(128), 0, s, P.O,
+                               nqd / 32, P.xp_o, P.xs_o, gate, m->qkv_rows, P.ks_qkv, slab_qkv);
+            HIP_TRY(pf_gemv(Ly.o, P.xp_o, P.xs_o, T, P.OD, P.ks_o, s));
+            hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(T), dim3(SB_THREADS), 0, s, P.X, P.OD, P.ks_o, slab_h,
+                               H, Ly.ffn_norm, m->eps, nullptr, P.xp_h, P.xs_h);
+            HIP_TRY(pf_gemv(Ly.gu, P.xp_h, P.xs_h, T, P.GU, P.ks_gu, s));
+            hipLaunchKernelGGL(k_swiglu_xp_batch, dim3((I / 32 + GBM_KC - 1) / GBM_KC, T), dim3(128), 0, s, P.GU,
+                               P.ks_gu, (size_t)T * 2 * I, I, P.xp_i, P.xs_i);
+            HIP_TRY(pf_gemv(Ly.down, P.xp_i, P.xs_i, T, P.OD, P.ks_down, s));
+            // the residual, then the next layer's norm (split for its q|k|v), or
+            // the final norm of every position (f32, the last one feeds the LM head)
+            const bool last = l + 1 == m->L;
+            hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(T), dim3(SB_THREADS), 0, s, P.X, P.OD, P.ks_down,
+                               slab_h, H, last ? m->final_norm : m->layers[l + 1].attn_norm, m->eps,
+                               last ? P.HF : nullptr, last ? nullptr : P.xp_h, P.xs_h);
         }
     }
-    // the last position: final norm, LM head, greedy token as a decode step records it
-    hipLaunchKernelGGL(k_pf_rmsnorm, dim3(1), dim3(256), 0, s, P.X + (size_t)(T - 1) * H, m->final_norm, H,
-                       m->eps, P.hf);
-    HIP_TRY(launch_gemv_plain(m->lm.d, m->lm.qs, P.hf, m->logits, m->V, H, s));
+    // the last position: LM head, greedy token as a decode step records it
+    HIP_TRY(launch_gemv_plain(m->lm.d, m->lm.qs, P.HF + (size_t)(T - 1) * H, m->logits, m->V, H, s));
     hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, s, m->st, m->ids, pos0 + n - 1, -1, -1, 0);
     hipLaunchKernelGGL(k_argmax_advance, dim3(1), dim3(256), 0, s, m->logits, P.iota, m->V, m->V, m->st,
                        m->ids, m->pred, m->max_seq);
