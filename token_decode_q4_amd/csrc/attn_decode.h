@@ -224,7 +224,13 @@ QD_DEV void attn_merge_heads(const AttnParams& p, int b, int g, int nact)
 // agent-scope; each thread waits for its own, the workgroup counts itself once
 // with a relaxed agent-scope add, and the one that completes the count reads
 // all partials with agent-scope loads.  No fence is needed: no plain store is
-// published this way.  The counter is returned to zero for the next launch.
+// published this way.  The order rests on a gfx9 property, not on the memory
+// model's release/acquire: stores count in vmcnt, so after s_waitcnt vmcnt(0)
+// this thread's agent-scope stores are complete at the agent's coherence
+// point, before the add is issued; and the merging workgroup's agent-scope
+// loads are issued after it observed the count.  (A release add would write
+// back the XCD's L2 in every workgroup: ~19 us against ~1.5 us per round trip.)
+// The counter is returned to zero for the next launch.
 template <int HD, int GQ, bool COH>
 QD_DEV void attn_merge_last(const AttnParams& p, int b, int g, int kv_len, int* last)
 {

@@ -15,7 +15,11 @@
 // Coherence inside the launch.  Every value a phase produces for other
 // workgroups is stored agent-scope (write-through to memory) and read
 // agent-scope; each thread waits for its own stores before its workgroup
-// arrives at the barrier.  Every layer has its own activation buffers.
+// arrives at the barrier.  Every layer has its own activation buffers.  The
+// relaxed arrival adds are ordered after those stores by a gfx9 property:
+// stores count in vmcnt, so s_waitcnt vmcnt(0) means they are complete at the
+// agent's coherence point (a release add would write back the XCD's L2 in
+// every workgroup).
 //
 // Barrier: 16 arrival counters 256 B apart (workgroup w adds 1 to counter
 // w % 16, one relaxed agent-scope add per workgroup); a waiter polls all 16
