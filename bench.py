@@ -551,12 +551,14 @@ def cpu_baseline(mi, pos0: int, tokens, seconds: float = 15.0):
 
 def prefill_row(model, s, n: int, reps: int = 3):
     """Prompt positions 0..n-1 of a created model: chunked prefill (qd_prefill,
-    chunks of 16 through the batched GEMV) against prefill as sequential
+    chunks of qd_prefill_chunk() positions through the batched product) against prefill as sequential
     decode steps (qd_generate over the prompt).  The K/V cache is rewritten
     with the same values; each is timed with events around `reps` runs after
     one untimed run.  Weight bytes per chunk give its GB/s."""
     import torch
+    import token_decode_q4_amd as qd
     stream = torch.cuda.current_stream()
+    chunk = qd.prefill_chunk()
 
     def timed(fn):
         fn()
@@ -573,13 +575,13 @@ def prefill_row(model, s, n: int, reps: int = 3):
     ms_c = timed(lambda: model.prefill(0, n))
     ms_s = timed(lambda: model.generate(0, n))
     model.check()
-    chunks = -(-n // 16)
+    chunks = -(-n // chunk)
     H, I = s.hidden, s.intermediate
     qkv = (s.n_heads + 2 * s.n_kv) * s.head_dim
     wbytes = s.layers * (q4_bytes(qkv, H) + q4_bytes(H, s.n_heads * s.head_dim) + q4_bytes(2 * I, H)
                          + q4_bytes(H, I))
     gbs = chunks * wbytes / (ms_c * 1e-3) / 1e9
-    return {"workload": f"{s.name} prompt positions 0..{n - 1}", "positions": n, "chunk": 16,
+    return {"workload": f"{s.name} prompt positions 0..{n - 1}", "positions": n, "chunk": chunk,
             "chunked_ms": round(ms_c, 3), "chunked_tok_s": round(n / (ms_c * 1e-3), 1),
             "sequential_ms": round(ms_s, 3), "sequential_tok_s": round(n / (ms_s * 1e-3), 1),
             "speedup": round(ms_s / ms_c, 2),

@@ -196,6 +196,9 @@ int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* d_tokens,
  * pos0 + n <= max_seq and pos0 is at most one past the written prefix;
  * afterwards the prefix is 0 .. pos0+n-1. */
 int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_last, qd_stream stream);
+/* Prompt positions per qd_prefill chunk (every weight is read once per
+ * chunk); a constant of the library build.  Host only. */
+int32_t qd_prefill_chunk(void);
 
 /* Batched decode (inferencelayer cuda_llm.rs page, step_batch_inner and its
  * batched head-to-head of the q4 GEMV arm at M = 2 .. 16 tokens;

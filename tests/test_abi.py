@@ -36,6 +36,11 @@ def test_header_functions_exported(qd):
         assert re.search(rf"\bT {n}$", syms, re.M), n
 
 
+def test_prefill_chunk(qd):
+    # two groups of 16 positions: the matrix-core product's vectors
+    assert qd.prefill_chunk() == 32
+
+
 def test_gemv_validation(qd):
     L = qd.lib()
     p = C.c_void_p(16)

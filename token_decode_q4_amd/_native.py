@@ -19,7 +19,7 @@ QD_OK, QD_EINVAL, QD_ERANGE, QD_ENOMEM, QD_EUNSUPPORTED, QD_EHIP = 0, -1, -2, -3
 
 # every function declared in include/qd.h
 EXPORTS = ("qd_create", "qd_create_batch", "qd_set_prompt_seq", "qd_generate_batch", "qd_decode_step_batch",
-           "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate", "qd_prefill",
+           "qd_destroy", "qd_decode_step", "qd_set_prompt", "qd_generate", "qd_prefill", "qd_prefill_chunk",
            "qd_gemv_q4_0", "qd_gemv_q4_0_batch", "qd_gemv_q4_0_experts", "qd_rope_inv_freq", "qd_attn_workspace_bytes",
            "qd_attn_decode_kv8", "qd_attn_decode", "qd_attn_noalloc_max_bytes", "qd_attn_decode_noalloc",
            "qd_check",
@@ -92,6 +92,8 @@ def lib():
         L.qd_generate.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                   C.c_void_p]
         L.qd_prefill.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
+        L.qd_prefill_chunk.argtypes = []
+        L.qd_prefill_chunk.restype = C.c_int32
         L.qd_gemv_q4_0.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
                                    C.c_int32, C.c_void_p]
         L.qd_gemv_q4_0_batch.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
@@ -194,6 +196,11 @@ def rope_inv_freq(theta: float, rot_dim: int, scaling: str = "default", factor: 
 
 def stream_read_groups(nbytes: int) -> int:
     return int(lib().qd_stream_read_groups(nbytes))
+
+
+def prefill_chunk() -> int:
+    """Prompt positions per qd_prefill chunk (qd_prefill_chunk)."""
+    return int(lib().qd_prefill_chunk())
 
 
 def stream_read(src, sink, nbytes=None, stream=None) -> int:

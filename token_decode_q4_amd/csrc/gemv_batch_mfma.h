@@ -389,14 +389,19 @@ k_gemv_batch_mfma(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
 }
 
 // ---------------------------------------------------------------------------
-// x split once, outside the product (the batched decode step).  The producer
-// of a product's input writes it already split, in the staged layout, one
-// 64 KB chunk per 32 blocks: XP[chunk][block][lane group][hi, lo][16 vector
-// slots][8 halves], and XS[chunk][16] = 1/s of each vector's chunk.  Slots
-// past the batch and blocks past the end stay zero (the buffers are cleared
-// once when allocated).  The product then copies a chunk into LDS with
-// global-to-LDS loads: no registers, no arithmetic, once per workgroup.
-constexpr int GBM_XP_CHUNK = GBM_KC * 4 * 2 * 16 * 8;   // halves per chunk
+// x split once, outside the product (the batched decode step, prefill).  The
+// producer of a product's input writes it already split, in the staged
+// layout, one 64 KB chunk at a time: with NG groups of 16 vector slots
+// (S = 16 NG slots) a chunk holds KCB = 32 / NG blocks,
+//   XP[chunk][block][lane group][hi, lo][S slots][8 halves],
+// and XS[chunk][S] = 1/s of each vector's chunk.  Slots past the batch and
+// blocks past the end stay zero (the buffers are cleared once when
+// allocated).  The product then copies a chunk into LDS, once per workgroup,
+// with no arithmetic.
+constexpr int GBM_XP_CHUNK = GBM_KC * 4 * 2 * 16 * 8;   // halves per chunk (any NG)
+
+__host__ __device__ constexpr int gbm_kcb(int ng) { return GBM_KC / ng; }          // blocks per chunk
+__host__ __device__ constexpr int gbm_nchunks(int nb, int ng) { return (nb + gbm_kcb(ng) - 1) / gbm_kcb(ng); }
 
 // largest |.| of the 8 elements in slot order (the high four undone)
 QD_DEV float gbm_xp_absmax(const float (&e)[8])
@@ -409,7 +414,8 @@ QD_DEV float gbm_xp_absmax(const float (&e)[8])
 }
 
 // writes the split pair of (chunk c, block bl, lane group kg, slot v), scale s
-QD_DEV void gbm_xp_put(_Float16* __restrict__ XP, int c, int bl, int kg, int v, const float (&e)[8], float s)
+QD_DEV void gbm_xp_put(_Float16* __restrict__ XP, int ng, int c, int bl, int kg, int v, const float (&e)[8],
+                       float s)
 {
     gbm_half8 xh, xl;
 #pragma unroll
@@ -419,12 +425,13 @@ QD_DEV void gbm_xp_put(_Float16* __restrict__ XP, int c, int bl, int kg, int v, 
         xh[k] = t;
         xl[k] = (_Float16)(f - (float)t);
     }
-    _Float16* dst = XP + (size_t)c * GBM_XP_CHUNK + ((size_t)(bl * 4 + kg) * 2 * 16 + v) * 8;
+    const int S = 16 * ng;
+    _Float16* dst = XP + (size_t)c * GBM_XP_CHUNK + ((size_t)(bl * 4 + kg) * 2 * S + v) * 8;
     *reinterpret_cast<gbm_half8*>(dst) = xh;
-    *reinterpret_cast<gbm_half8*>(dst + 16 * 8) = xl;
+    *reinterpret_cast<gbm_half8*>(dst + S * 8) = xl;
 }
 
-// largest value over the 128 threads of a chunk workgroup (2 waves); every
+// largest value over a workgroup of 64 or 128 threads (a chunk's items); every
 // thread gets it; red >= 2 floats
 QD_DEV float gbm_chunk_max(float m, float* red)
 {
@@ -432,20 +439,21 @@ QD_DEV float gbm_chunk_max(float m, float* red)
     if ((threadIdx.x & (WAVE - 1)) == 0)
         red[threadIdx.x / WAVE] = m;
     __syncthreads();
-    return fmaxf(red[0], red[1]);
+    return blockDim.x > WAVE ? fmaxf(red[0], red[1]) : red[0];
 }
 
-// grid (chunks, B), 128 threads: vector b of X [B][nb * 32] into XP / XS.
-// With a gate (vector b's at gate + b * gstride, as ngslab partial products
-// gslab floats apart, added in slab order) x is first multiplied by
-// sigmoid(gate), as the decode step gates the merged attention output.
+// grid (chunks, B), 4 * KCB threads (one per (block, lane group) item):
+// vector b of X [B][nb * 32] into XP / XS with NG = ng slot groups.  With a
+// gate (vector b's at gate + b * gstride, as ngslab partial products gslab
+// floats apart, added in slab order) x is first multiplied by sigmoid(gate),
+// as the decode step gates the merged attention output.
 __global__ void __launch_bounds__(128)
-k_xsplit_batch(const float* __restrict__ X, int nb, _Float16* __restrict__ XP, float* __restrict__ XS,
+k_xsplit_batch(const float* __restrict__ X, int nb, int ng, _Float16* __restrict__ XP, float* __restrict__ XS,
                const float* __restrict__ gate = nullptr, int gstride = 0, int ngslab = 1, size_t gslab = 0)
 {
     __shared__ float red[2];
     const int c = blockIdx.x, b = blockIdx.y;
-    const int bl = threadIdx.x >> 2, kg = threadIdx.x & 3, blk = c * GBM_KC + bl;
+    const int bl = threadIdx.x >> 2, kg = threadIdx.x & 3, blk = c * gbm_kcb(ng) + bl;
     const bool in = blk < nb;
     float e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (in) {
@@ -476,24 +484,31 @@ k_xsplit_batch(const float* __restrict__ X, int nb, _Float16* __restrict__ XP, f
     }
     const float s = gbm_scale_for(gbm_chunk_max(gbm_xp_absmax(e), red));
     if (in)
-        gbm_xp_put(XP, c, bl, kg, b, e, s);
+        gbm_xp_put(XP, ng, c, bl, kg, b, e, s);
     if (threadIdx.x == 0)
-        XS[c * 16 + b] = 1.0f / s;
+        XS[c * 16 * ng + b] = 1.0f / s;
 }
 
-// The product on a split x: grid (row tiles, K slices) as k_gemv_batch_mfma,
-// B vectors at run time (slots past B are zero in XP); Y[b] for b < B.
-template <int RG>
+// The product on a split x: grid (row tiles, K slices) as k_gemv_batch_mfma
+// (K slices in units of KCB-block chunks), B <= 16 NG vectors at run time
+// (slots past B are zero in XP); Y[b] for b < B.  With NG = 2 each block's
+// codes, built once, meet two 16-vector groups: the code-building work per
+// vector halves.
+template <int RG, int NG>
 __global__ void __launch_bounds__(GBM_NW* WAVE)
 k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                 const _Float16* __restrict__ XP, const float* __restrict__ XS, float* __restrict__ Y,
                 int N, int nb, int B, int kch, size_t ystride, int dvec)
 {
+    static_assert(NG == 1 || NG == 2, "slot groups");
+    constexpr int KCB = GBM_KC / NG;      // blocks per chunk
+    constexpr int STEPS = KCB / 4;        // 4-block steps per chunk
+    constexpr int S = 16 * NG;            // vector slots
     extern __shared__ __align__(16) _Float16 xs[];   // one chunk of XP
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
     const int r = lane & 15, kg = lane >> 4;
-    const int nch = (nb + GBM_KC - 1) / GBM_KC;
+    const int nch = (nb + KCB - 1) / KCB;
     const int c0 = (int)blockIdx.y * kch, c1 = min(nch, c0 + kch);
     Y += (size_t)blockIdx.y * ystride;
     const int row0 = (int)blockIdx.x * gbm_rows(RG) + wave * 16 * RG;
@@ -501,13 +516,14 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
 #pragma unroll
     for (int g = 0; g < RG; ++g)
         rb[g] = (size_t)min(row0 + 16 * g + r, N - 1) * (size_t)nb;
-    const int nsteps = (c1 - c0) * GBM_STEPS;
+    const int nsteps = (c1 - c0) * STEPS;
     if (nsteps <= 0) {   // an empty slice (the host never launches one): zeros
         for (int g = 0; g < RG; ++g) {
             const int row = row0 + 16 * g + r;
-            for (int i = 0; i < 4; ++i)
-                if (row < N && 4 * kg + i < B)
-                    Y[(size_t)(4 * kg + i) * N + row] = 0.f;
+            for (int v = 4 * kg; v < S; v += 16)
+                for (int i = 0; i < 4; ++i)
+                    if (row < N && v + i < B)
+                        Y[(size_t)(v + i) * N + row] = 0.f;
         }
         return;
     }
@@ -516,13 +532,15 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
     };
     auto load = [&](Buf& bf, int s) {
         s = min(s, nsteps - 1);
-        const int blk = min((c0 + s / GBM_STEPS) * GBM_KC + (s % GBM_STEPS) * 4 + kg, nb - 1);
+        const int blk = min((c0 + s / STEPS) * KCB + (s % STEPS) * 4 + kg, nb - 1);
 #pragma unroll
         for (int g = 0; g < RG; ++g)
             bf.q[g] = *reinterpret_cast<const uint4*>(Q + (rb[g] + (size_t)blk) * 16u);
     };
+    // scales of chunk c: lane group kg's eighth-of-32 blocks, c*KCB + 8kg .. +7
+    // (with NG = 2 only lane groups 0 and 1 hold scales of the chunk)
     auto load_d = [&](uint4 (&dq)[RG], int c) {
-        const int b0 = c * GBM_KC + 8 * kg;
+        const int b0 = c * KCB + 8 * kg;
         if (dvec) {   // uniform: nb % 8 == 0 and D 16-byte aligned
             const int bq = min(b0, nb - 8);
 #pragma unroll
@@ -548,35 +566,39 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                 (const __attribute__((address_space(1))) void*)(src + q * 512),
                 (__attribute__((address_space(3))) void*)(xs + (wave * 16 + q) * 512), 16, 0, 0);
     };
-    auto load_inv = [&](float (&inv)[4], int c) {
+    auto load_inv = [&](float (&inv)[NG][4], int c) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            inv[i] = XS[c * 16 + 4 * kg + i];
+        for (int h = 0; h < NG; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                inv[h][i] = XS[c * S + 16 * h + 4 * kg + i];
     };
 
-    float acc[RG][4];
+    float acc[NG][RG][4];
 #pragma unroll
-    for (int g = 0; g < RG; ++g)
+    for (int h = 0; h < NG; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc[g][i] = 0.f;
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[h][g][i] = 0.f;
     // x first (loads complete in order), then the scales, then every weight
     // load of the first chunk; the next chunk's weights are issued while the
     // current one is computed, its x and scales right after it
     dma_x(c0);
     uint4 dq[RG];
     load_d(dq, c0);
-    float inv[4];
+    float inv[NG][4];
     load_inv(inv, c0);
-    Buf bufs[GBM_STEPS];
+    Buf bufs[STEPS];
 #pragma unroll
-    for (int u = 0; u < GBM_STEPS; ++u)
+    for (int u = 0; u < STEPS; ++u)
         load(bufs[u], u);
     const gbm_floatx4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int c = c0; c < c1; ++c) {
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this chunk's x (and everything before it) landed
         __syncthreads();
-        uint32_t dg[RG][4][4];
+        uint32_t dg[RG][KCB / 8][4];   // [group][lane group q][dword]: halves = scales of blocks 8q ..
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
             const uint32_t dw[4] = {dq[g].x, dq[g].y, dq[g].z, dq[g].w};
@@ -585,23 +607,27 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                 uint32_t t[4];
                 gbm_allgather4(dw[k], t);
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+                for (int q = 0; q < KCB / 8; ++q)
                     dg[g][q][k] = t[q];
             }
         }
-        float cinv[4];
+        float cinv[NG][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            cinv[i] = inv[i];
-        float cacc[RG][4];
-#pragma unroll
-        for (int g = 0; g < RG; ++g)
+        for (int h = 0; h < NG; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                cacc[g][i] = 0.f;
-        const int sbase = (c - c0) * GBM_STEPS;
+                cinv[h][i] = inv[h][i];
+        float cacc[NG][RG][4];
 #pragma unroll
-        for (int j = 0; j < GBM_STEPS; ++j) {
+        for (int h = 0; h < NG; ++h)
+#pragma unroll
+            for (int g = 0; g < RG; ++g)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    cacc[h][g][i] = 0.f;
+        const int sbase = (c - c0) * STEPS;
+#pragma unroll
+        for (int j = 0; j < STEPS; ++j) {
             uint32_t w[RG][4];
 #pragma unroll
             for (int g = 0; g < RG; ++g) {
@@ -611,39 +637,40 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                 w[g][3] = bufs[j].q[g].w;
                 gbm_transpose4(w[g]);
             }
-            load(bufs[j], sbase + GBM_STEPS + j);   // the same step of the next chunk
-            gbm_half8 xh[4], xl[4];
+            load(bufs[j], sbase + STEPS + j);   // the same step of the next chunk
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const _Float16* src = xs + ((size_t)((4 * j + b) * 4 + kg) * 2 * 16 + r) * 8;
-                xh[b] = *reinterpret_cast<const gbm_half8*>(src);
-                xl[b] = *reinterpret_cast<const gbm_half8*>(src + 16 * 8);
-            }
+                const int bl = 4 * j + b;   // block within the chunk
+                gbm_half8 xh[NG], xl[NG];
 #pragma unroll
-            for (int g = 0; g < RG; ++g) {
-                gbm_floatx4 p[4];
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const gbm_half8 wop = gbm_codes(w[g][b]);
-                    p[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[b], wop, zero, 0, 0, 0);
-                    p[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[b], wop, p[b], 0, 0, 0);
+                for (int h = 0; h < NG; ++h) {
+                    const _Float16* src = xs + ((size_t)(bl * 4 + kg) * 2 * S + 16 * h + r) * 8;
+                    xh[h] = *reinterpret_cast<const gbm_half8*>(src);
+                    xl[h] = *reinterpret_cast<const gbm_half8*>(src + S * 8);
                 }
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int bl = 4 * j + b;
+                for (int g = 0; g < RG; ++g) {
+                    const gbm_half8 wop = gbm_codes(w[g][b]);
                     const uint32_t dd = dg[g][bl >> 3][(bl & 7) >> 1];
                     const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)((bl & 1) ? dd >> 16 : dd));
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        cacc[g][i] = fmaf((float)dh, p[b][i], cacc[g][i]);
+                    for (int h = 0; h < NG; ++h) {
+                        gbm_floatx4 pv = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[h], wop, zero, 0, 0, 0);
+                        pv = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[h], wop, pv, 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            cacc[h][g][i] = fmaf((float)dh, pv[i], cacc[h][g][i]);
+                    }
                 }
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int h = 0; h < NG; ++h)
 #pragma unroll
-            for (int g = 0; g < RG; ++g)
-                acc[g][i] = fmaf(cacc[g][i], cinv[i], acc[g][i]);
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int g = 0; g < RG; ++g)
+                    acc[h][g][i] = fmaf(cacc[h][g][i], cinv[h][i], acc[h][g][i]);
         if (c + 1 < c1) {   // uniform
             __syncthreads();   // every wave is done with this chunk's x
             dma_x(c + 1);
@@ -657,9 +684,11 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
         const int row = row0 + 16 * g + r;
         if (row < N) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (4 * kg + i < B)
-                    Y[(size_t)(4 * kg + i) * N + row] = acc[g][i];
+            for (int h = 0; h < NG; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * h + 4 * kg + i < B)
+                        Y[(size_t)(16 * h + 4 * kg + i) * N + row] = acc[h][g][i];
         }
     }
 }

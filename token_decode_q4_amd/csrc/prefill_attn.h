@@ -1,7 +1,7 @@
 // prefill_attn.h -- causal attention of a prefill chunk with each K/V tile
 // read once for all of the chunk's queries (gfx950 matrix cores).
 //
-// The T <= 16 positions p0 .. p0+T-1 of a chunk attend over one cache: query
+// The T positions p0 .. p0+T-1 of a chunk attend over one cache: query
 // t sees keys 0 .. p0+t (inferencelayer cuda_llm.rs page, fa_prefill: a tile
 // of queries, K and V tiles staged once and shared, the causal mask inside
 // the tile; the online-softmax partials merged as in attn_reduce).
@@ -9,8 +9,8 @@
 // Workgroup (split s, kv head g) owns keys [s*chunk, (s+1)*chunk) of that kv
 // head and every query row of its GQA group: T*GQ rows (t, j), row R = t*GQ
 // + j (head g*GQ + j), 16 rows per wave (wave w: rows 16w .. 16w+15), so
-// GQ waves.  Per 16-key step (one paged block) the K and V tiles are loaded
-// once into LDS and every wave uses them:
+// NWV = GQ * ceil(T / 16) waves.  Per 16-key step (one paged block) the K and
+// V tiles are loaded once into LDS and every wave uses them:
 //   S^T = K Q^T   v_mfma_f32_16x16x32_f16, M = the 16 keys, N = the wave's 16
 //                 query rows, K = 32 dims per instruction; q enters as an f16
 //                 hi + lo pair (about 22 bits), K is f16 already
@@ -49,12 +49,13 @@ struct FaParams {
     float* part;              // [T][nq][nsplit][HD + 2]
 };
 
-template <int HD, int GQ>
-__global__ void __launch_bounds__(GQ* WAVE) k_pf_attn(FaParams p)
+template <int HD, int GQ, int NWV>
+__global__ void __launch_bounds__(NWV* WAVE) k_pf_attn(FaParams p)
 {
+    static_assert(NWV * WAVE <= 1024, "workgroup");
     constexpr int NI = HD / 32;     // 32-dim slices (QK)
     constexpr int NT = HD / 16;     // 16-dim tiles (PV)
-    constexpr int NTH = GQ * WAVE;
+    constexpr int NTH = NWV * WAVE;
     constexpr int KROW = HD + FA_KPAD, VROW = 16 + FA_VPAD;
     __shared__ __align__(16) _Float16 kt[16 * KROW];    // K tile [key][dim]
     __shared__ __align__(16) _Float16 vt[HD * VROW];    // V tile transposed [dim][key]

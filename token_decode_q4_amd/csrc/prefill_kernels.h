@@ -1,5 +1,5 @@
 // prefill_kernels.h -- the kernels of a chunked prefill (gfx950) of its own:
-// T <= 16 prompt positions at a time, every weight read once per chunk by the
+// T <= 32 prompt positions at a time, every weight read once per chunk by the
 // batched GEMV on split inputs (gemv_batch_mfma.h: the positions are its
 // vectors), the norms, SwiGLU and splits of the batched decode step
 // (step_batch.h), the same arithmetic per position as the decode step
@@ -12,7 +12,8 @@
 
 namespace qd {
 
-constexpr int PF_T = 16;   // positions per chunk
+constexpr int PF_NG = 2;          // 16-position groups per chunk
+constexpr int PF_T = 16 * PF_NG;   // positions per chunk
 
 // X[t][i] = dequant(E)[ids[p0 + t]][i]; grid (ceil(H/256), T)
 __global__ void __launch_bounds__(256)

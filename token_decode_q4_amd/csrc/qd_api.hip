@@ -494,10 +494,10 @@ static int enqueue_step_fused(qd_model* m, hipStream_t s)
 // of the matrix-core GEMV alone give too few workgroups for short matrices,
 // so K is cut into slices (whole 32-block chunks) up to about 768 workgroups
 // (measured at the Qwen3-8B shapes: gate|up 2 slices, q|k|v and o 4, down 6)
-static int step_kslices(int N, int nb)
+static int step_kslices(int N, int nb, int ng = 1)
 {
     const int tiles = (N + gbm_rows(1) - 1) / gbm_rows(1);
-    const int nch = (nb + GBM_KC - 1) / GBM_KC;
+    const int nch = gbm_nchunks(nb, ng);
     int ks = std::min({nch, SB_MAXSLAB, std::max(1, (768 + tiles / 2) / tiles)});
     if (ks > 1) {
         const int kch = (nch + ks - 1) / ks;
@@ -514,14 +514,14 @@ static hipError_t step_gemv(const qd_model* m, const DevQ4& W, const _Float16* X
                             int ks, hipStream_t s)
 {
     const int N = W.rows, nb = W.nb;
-    const int nch = (nb + GBM_KC - 1) / GBM_KC;
+    const int nch = gbm_nchunks(nb, 1);
     const int kch = (nch + ks - 1) / ks;
     if (ks < 1 || (int64_t)(ks - 1) * kch >= nch)   // every slice holds at least one chunk
         return hipErrorInvalidValue;
     const int dvec = (nb % 8 == 0 && reinterpret_cast<uintptr_t>(W.d) % 16 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((k_gemv_batch_xp<1>), dim3((N + gbm_rows(1) - 1) / gbm_rows(1), ks), dim3(GBM_NW * WAVE),
-                       gemv_batch_mfma_lds_bytes(), s, W.d, W.qs, XP, XS, Y, N, nb, m->B, kch, (size_t)m->B * N,
-                       dvec);
+    hipLaunchKernelGGL((k_gemv_batch_xp<1, 1>), dim3((N + gbm_rows(1) - 1) / gbm_rows(1), ks),
+                       dim3(GBM_NW * WAVE), gemv_batch_mfma_lds_bytes(), s, W.d, W.qs, XP, XS, Y, N, nb, m->B, kch,
+                       (size_t)m->B * N, dvec);
     return hipGetLastError();
 }
 
@@ -534,7 +534,7 @@ static int enqueue_step_batch(qd_model* m, hipStream_t s)
     const int B = m->B, H = m->H, I = m->I;
     const int nqd = m->nq * m->hd;
     hipLaunchKernelGGL(k_embed_batch, dim3(B), dim3(SB_THREADS), 0, s, m->embed.d, m->embed.qs, H, m->V, m->st,
-                       m->ids, m->max_seq, m->layers[0].attn_norm, m->eps, m->bx, nullptr, m->xp_h, m->xs_h,
+                       m->ids, m->max_seq, m->layers[0].attn_norm, m->eps, m->bx, nullptr, m->xp_h, m->xs_h, 1,
                        m->rope_cos, m->rope_sin, m->rot / 2, m->rope_cur, m->rstride);
     for (int l = 0; l < m->L; ++l) {
         DevLayer& Ly = m->layers[l];
@@ -577,18 +577,18 @@ static int enqueue_step_batch(qd_model* m, hipStream_t s)
         else
             launch_attention<1>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, B, m->nq, s);
         const size_t slab_h = (size_t)B * H;
-        hipLaunchKernelGGL(k_xsplit_batch, dim3((nqd / 32 + GBM_KC - 1) / GBM_KC, B), dim3(128), 0, s, m->battn,
-                           nqd / 32, m->xp_o, m->xs_o);
+        hipLaunchKernelGGL(k_xsplit_batch, dim3(gbm_nchunks(nqd / 32, 1), B), dim3(128), 0, s, m->battn,
+                           nqd / 32, 1, m->xp_o, m->xs_o, nullptr, 0, 1, (size_t)0);
         HIP_TRY(step_gemv(m, Ly.o, m->xp_o, m->xs_o, m->bo, m->ks_o, s));
         hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(B), dim3(SB_THREADS), 0, s, m->bx, m->bo, m->ks_o, slab_h,
-                           H, Ly.ffn_norm, m->eps, nullptr, m->xp_h, m->xs_h);
+                           H, Ly.ffn_norm, m->eps, nullptr, m->xp_h, m->xs_h, 1);
         HIP_TRY(step_gemv(m, Ly.gu, m->xp_h, m->xs_h, m->bgu, m->ks_gu, s));
-        hipLaunchKernelGGL(k_swiglu_xp_batch, dim3((I / 32 + GBM_KC - 1) / GBM_KC, B), dim3(128), 0, s, m->bgu,
-                           m->ks_gu, (size_t)B * 2 * I, I, m->xp_i, m->xs_i);
+        hipLaunchKernelGGL(k_swiglu_xp_batch, dim3(gbm_nchunks(I / 32, 1), B), dim3(128), 0, s, m->bgu,
+                           m->ks_gu, (size_t)B * 2 * I, I, 1, m->xp_i, m->xs_i);
         HIP_TRY(step_gemv(m, Ly.down, m->xp_i, m->xs_i, m->bo, m->ks_down, s));
         const float* wn = (l + 1 < m->L) ? m->layers[l + 1].attn_norm : m->final_norm;
         hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(B), dim3(SB_THREADS), 0, s, m->bx, m->bo, m->ks_down,
-                           slab_h, H, wn, m->eps, nullptr, m->xp_h, m->xs_h);
+                           slab_h, H, wn, m->eps, nullptr, m->xp_h, m->xs_h, 1);
     }
     HIP_TRY(step_gemv(m, m->lm, m->xp_h, m->xs_h, m->blog, 1, s));
     hipLaunchKernelGGL(k_argmax_batch, dim3(m->bG, B), dim3(256), 0, s, m->blog, m->V, m->bchunk, m->bcval,
@@ -954,8 +954,8 @@ static int create_model(const qd_config* cfg, const qd_weights* w, int B, qd_str
             (rc = dev_alloc_t(m, &m->bact, Bz * m->I)) || (rc = dev_alloc_t(m, &m->blog, Bz * m->V)) ||
             (rc = dev_alloc_t(m, &m->bcval, Bz * m->bG)) || (rc = dev_alloc_t(m, &m->bcidx, Bz * m->bG)))
             return bail(rc);
-        const size_t ch_h = (H / 32 + GBM_KC - 1) / GBM_KC, ch_o = (nqd / 32 + GBM_KC - 1) / GBM_KC,
-                     ch_i = (m->I / 32 + GBM_KC - 1) / GBM_KC;
+        const size_t ch_h = gbm_nchunks(H / 32, 1), ch_o = gbm_nchunks(nqd / 32, 1),
+                     ch_i = gbm_nchunks(m->I / 32, 1);
         if ((rc = dev_alloc_t(m, &m->xp_h, ch_h * GBM_XP_CHUNK)) ||
             (rc = dev_alloc_t(m, &m->xp_o, ch_o * GBM_XP_CHUNK)) ||
             (rc = dev_alloc_t(m, &m->xp_i, ch_i * GBM_XP_CHUNK)) || (rc = dev_alloc_t(m, &m->xs_h, ch_h * 16)) ||
@@ -1696,13 +1696,14 @@ static void pf_attention(qd_model* m, DevLayer& Ly, int p0, int T, hipStream_t s
     f.chunk = chunk;
     f.nsplit = nsplit;
     f.part = P.fa;
-    const dim3 grid(nsplit, m->nkv), block(gq * WAVE);
+    // a wave per 16 query rows (position, head) of the kv head's group
+    const dim3 grid(nsplit, m->nkv), block(gq * PF_NG * WAVE);
 #define QD_FA(HD_)                                                                                 \
     switch (gq) {                                                                                  \
-    case 1: hipLaunchKernelGGL((k_pf_attn<HD_, 1>), grid, block, 0, s, f); break;                  \
-    case 2: hipLaunchKernelGGL((k_pf_attn<HD_, 2>), grid, block, 0, s, f); break;                  \
-    case 4: hipLaunchKernelGGL((k_pf_attn<HD_, 4>), grid, block, 0, s, f); break;                  \
-    default: hipLaunchKernelGGL((k_pf_attn<HD_, 8>), grid, block, 0, s, f); break;                 \
+    case 1: hipLaunchKernelGGL((k_pf_attn<HD_, 1, PF_NG>), grid, block, 0, s, f); break;           \
+    case 2: hipLaunchKernelGGL((k_pf_attn<HD_, 2, 2 * PF_NG>), grid, block, 0, s, f); break;       \
+    case 4: hipLaunchKernelGGL((k_pf_attn<HD_, 4, 4 * PF_NG>), grid, block, 0, s, f); break;       \
+    default: hipLaunchKernelGGL((k_pf_attn<HD_, 8, 8 * PF_NG>), grid, block, 0, s, f); break;      \
     }                                                                                              \
     hipLaunchKernelGGL((k_attn_combine<HD_>), dim3(m->nq, T), dim3(ATT_CNT), 0, s, P.fa, nsplit, chunk, \
                        P.lens, (const int32_t*)nullptr, m->max_seq, m->nq, P.O);
@@ -1723,12 +1724,12 @@ static int pf_setup(qd_model* m)
     const size_t ws = attn_ws_layout(PF_T, m->nq, m->nkv, m->hd, m->max_seq, &P.geo);
     if (m->H > 16384)   // the batched RMSNorm splits at most 2 items per thread
         return fail(QD_EUNSUPPORTED, "qd_prefill supports hidden <= 16384 (got %d)", m->H);
-    P.ks_qkv = step_kslices(m->qkv_rows, m->H / 32);
-    P.ks_o = step_kslices(m->H, (int)nqd / 32);
-    P.ks_gu = step_kslices(2 * m->I, m->H / 32);
-    P.ks_down = step_kslices(m->H, m->I / 32);
-    const size_t ch_h = (H / 32 + GBM_KC - 1) / GBM_KC, ch_o = (nqd / 32 + GBM_KC - 1) / GBM_KC,
-                 ch_i = (I / 32 + GBM_KC - 1) / GBM_KC;
+    P.ks_qkv = step_kslices(m->qkv_rows, m->H / 32, PF_NG);
+    P.ks_o = step_kslices(m->H, (int)nqd / 32, PF_NG);
+    P.ks_gu = step_kslices(2 * m->I, m->H / 32, PF_NG);
+    P.ks_down = step_kslices(m->H, m->I / 32, PF_NG);
+    const size_t ch_h = gbm_nchunks(m->H / 32, PF_NG), ch_o = gbm_nchunks((int)nqd / 32, PF_NG),
+                 ch_i = gbm_nchunks(m->I / 32, PF_NG), S = 16 * PF_NG;
     int rc;
     if ((rc = dev_alloc_t(m, &P.X, T * H)) || (rc = dev_alloc_t(m, &P.Q, T * nqd)) ||
         (rc = dev_alloc_t(m, &P.O, T * nqd)) || (rc = dev_alloc_t(m, &P.HF, T * H)) ||
@@ -1736,8 +1737,8 @@ static int pf_setup(qd_model* m)
         (rc = dev_alloc_t(m, &P.OD, (size_t)std::max(P.ks_o, P.ks_down) * T * H)) ||
         (rc = dev_alloc_t(m, &P.GU, (size_t)P.ks_gu * T * 2 * I)) ||
         (rc = dev_alloc_t(m, &P.xp_h, ch_h * GBM_XP_CHUNK)) || (rc = dev_alloc_t(m, &P.xp_o, ch_o * GBM_XP_CHUNK)) ||
-        (rc = dev_alloc_t(m, &P.xp_i, ch_i * GBM_XP_CHUNK)) || (rc = dev_alloc_t(m, &P.xs_h, ch_h * 16)) ||
-        (rc = dev_alloc_t(m, &P.xs_o, ch_o * 16)) || (rc = dev_alloc_t(m, &P.xs_i, ch_i * 16)) ||
+        (rc = dev_alloc_t(m, &P.xp_i, ch_i * GBM_XP_CHUNK)) || (rc = dev_alloc_t(m, &P.xs_h, ch_h * S)) ||
+        (rc = dev_alloc_t(m, &P.xs_o, ch_o * S)) || (rc = dev_alloc_t(m, &P.xs_i, ch_i * S)) ||
         (rc = dev_alloc_t(m, &P.fa, T * nqd / m->hd * PF_FA_MAXS * (m->hd + 2))) ||
         (rc = dev_alloc_t(m, &P.lens, T)) || (rc = dev_alloc_t(m, &P.iota, (size_t)m->V)) ||
         (rc = dev_alloc_t(m, &P.ws, ws / sizeof(float) + 1)))
@@ -1748,9 +1749,9 @@ static int pf_setup(qd_model* m)
     if (hipMemset(P.xp_h, 0, ch_h * GBM_XP_CHUNK * sizeof(_Float16)) != hipSuccess ||
         hipMemset(P.xp_o, 0, ch_o * GBM_XP_CHUNK * sizeof(_Float16)) != hipSuccess ||
         hipMemset(P.xp_i, 0, ch_i * GBM_XP_CHUNK * sizeof(_Float16)) != hipSuccess ||
-        hipMemset(P.xs_h, 0, ch_h * 16 * sizeof(float)) != hipSuccess ||
-        hipMemset(P.xs_o, 0, ch_o * 16 * sizeof(float)) != hipSuccess ||
-        hipMemset(P.xs_i, 0, ch_i * 16 * sizeof(float)) != hipSuccess)
+        hipMemset(P.xs_h, 0, ch_h * S * sizeof(float)) != hipSuccess ||
+        hipMemset(P.xs_o, 0, ch_o * S * sizeof(float)) != hipSuccess ||
+        hipMemset(P.xs_i, 0, ch_i * S * sizeof(float)) != hipSuccess)
         return fail(QD_EHIP, "prefill buffer set-up failed");
     if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess)
         return fail(QD_EHIP, "prefill buffer set-up failed");
@@ -1759,20 +1760,24 @@ static int pf_setup(qd_model* m)
 }
 
 // the chunk's product Y = W X on the matrix cores from x split in XP / XS,
-// T positions (vector slots), in ks K slices (partial slabs of T*N floats)
+// T positions (vector slots in PF_NG groups of 16), in ks K slices (partial
+// slabs of T*N floats)
 static hipError_t pf_gemv(const DevQ4& W, const _Float16* XP, const float* XS, int T, float* Y, int ks,
                           hipStream_t s)
 {
     const int N = W.rows, nb = W.nb;
-    const int nch = (nb + GBM_KC - 1) / GBM_KC;
+    const int nch = gbm_nchunks(nb, PF_NG);
     const int kch = (nch + ks - 1) / ks;
     if (ks < 1 || (int64_t)(ks - 1) * kch >= nch)
         return hipErrorInvalidValue;
     const int dvec = (nb % 8 == 0 && reinterpret_cast<uintptr_t>(W.d) % 16 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((k_gemv_batch_xp<1>), dim3((N + gbm_rows(1) - 1) / gbm_rows(1), ks), dim3(GBM_NW * WAVE),
-                       gemv_batch_mfma_lds_bytes(), s, W.d, W.qs, XP, XS, Y, N, nb, T, kch, (size_t)T * N, dvec);
+    hipLaunchKernelGGL((k_gemv_batch_xp<1, PF_NG>), dim3((N + gbm_rows(1) - 1) / gbm_rows(1), ks),
+                       dim3(GBM_NW * WAVE), gemv_batch_mfma_lds_bytes(), s, W.d, W.qs, XP, XS, Y, N, nb, T, kch,
+                       (size_t)T * N, dvec);
     return hipGetLastError();
 }
+
+extern "C" int32_t qd_prefill_chunk(void) { return PF_T; }
 
 extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_last, qd_stream stream)
 {
@@ -1798,7 +1803,7 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
         hipLaunchKernelGGL(k_pf_embed, dim3((H + 255) / 256, T), dim3(256), 0, s, m->embed.d, m->embed.qs,
                            H, m->ids, p0, P.X);
         hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(T), dim3(SB_THREADS), 0, s, P.X, nullptr, 0, (size_t)0,
-                           H, m->layers[0].attn_norm, m->eps, nullptr, P.xp_h, P.xs_h);
+                           H, m->layers[0].attn_norm, m->eps, nullptr, P.xp_h, P.xs_h, PF_NG);
         for (int l = 0; l < m->L; ++l) {
             DevLayer& Ly = m->layers[l];
             HIP_TRY(pf_gemv(Ly.qkv, P.xp_h, P.xs_h, T, P.QKV, P.ks_qkv, s));
@@ -1844,21 +1849,21 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
             }
             // the gate rows follow q|k|v in the fused product
             const float* gate = m->attn_gate ? P.QKV + (size_t)(m->nq + 2 * m->nkv) * hd : nullptr;
-            hipLaunchKernelGGL(k_xsplit_batch, dim3((nqd / 32 + GBM_KC - 1) / GBM_KC, T), dim3(128), 0, s, P.O,
-                               nqd / 32, P.xp_o, P.xs_o, gate, m->qkv_rows, P.ks_qkv, slab_qkv);
+            hipLaunchKernelGGL(k_xsplit_batch, dim3(gbm_nchunks(nqd / 32, PF_NG), T), dim3(4 * gbm_kcb(PF_NG)), 0,
+                               s, P.O, nqd / 32, PF_NG, P.xp_o, P.xs_o, gate, m->qkv_rows, P.ks_qkv, slab_qkv);
             HIP_TRY(pf_gemv(Ly.o, P.xp_o, P.xs_o, T, P.OD, P.ks_o, s));
             hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(T), dim3(SB_THREADS), 0, s, P.X, P.OD, P.ks_o, slab_h,
-                               H, Ly.ffn_norm, m->eps, nullptr, P.xp_h, P.xs_h);
+                               H, Ly.ffn_norm, m->eps, nullptr, P.xp_h, P.xs_h, PF_NG);
             HIP_TRY(pf_gemv(Ly.gu, P.xp_h, P.xs_h, T, P.GU, P.ks_gu, s));
-            hipLaunchKernelGGL(k_swiglu_xp_batch, dim3((I / 32 + GBM_KC - 1) / GBM_KC, T), dim3(128), 0, s, P.GU,
-                               P.ks_gu, (size_t)T * 2 * I, I, P.xp_i, P.xs_i);
+            hipLaunchKernelGGL(k_swiglu_xp_batch, dim3(gbm_nchunks(I / 32, PF_NG), T), dim3(4 * gbm_kcb(PF_NG)), 0,
+                               s, P.GU, P.ks_gu, (size_t)T * 2 * I, I, PF_NG, P.xp_i, P.xs_i);
             HIP_TRY(pf_gemv(Ly.down, P.xp_i, P.xs_i, T, P.OD, P.ks_down, s));
             // the residual, then the next layer's norm (split for its q|k|v), or
             // the final norm of every position (f32, the last one feeds the LM head)
             const bool last = l + 1 == m->L;
             hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(T), dim3(SB_THREADS), 0, s, P.X, P.OD, P.ks_down,
                                slab_h, H, last ? m->final_norm : m->layers[l + 1].attn_norm, m->eps,
-                               last ? P.HF : nullptr, last ? nullptr : P.xp_h, P.xs_h);
+                               last ? P.HF : nullptr, last ? nullptr : P.xp_h, P.xs_h, PF_NG);
         }
     }
     // the last position: LM head, greedy token as a decode step records it

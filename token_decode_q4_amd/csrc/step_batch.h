@@ -50,20 +50,23 @@ QD_DEV float sb_block_sum(float v, float* red)
 
 // The batched RMSNorm works on items (chunk, block, lane group) of 8
 // elements: 4kg .. 4kg+3 and 16+4kg .. 16+4kg+3 of the block, as the split
-// for the product groups them.  A thread holds at most SB_ITEMS items (item
+// for the product groups them (chunks of 32 / ng blocks for ng slot groups).  A thread holds at most SB_ITEMS items (item
 // it = thread + u * SB_THREADS), so every load of a row is issued in one
 // round and the values stay in registers between the two passes.
 constexpr int SB_ITEMS = 2;   // H <= 16384
 
-QD_DEV int sb_nitems(int H) { return ((H / 32 + GBM_KC - 1) / GBM_KC) * 128; }
+// items of a row with NG = ng slot groups: chunks of KCB = 32 / ng blocks,
+// 4 KCB items each (a multiple of a wave)
+QD_DEV int sb_nitems(int H, int ng) { return gbm_nchunks(H / 32, ng) * 4 * gbm_kcb(ng); }
 
 // item it of a row: its chunk, block within the chunk, lane group, block
-QD_DEV void sb_item(int it, int& c, int& bl, int& kg, int& blk)
+QD_DEV void sb_item(int it, int ng, int& c, int& bl, int& kg, int& blk)
 {
-    c = it >> 7;
-    bl = (it >> 2) & 31;
+    const int kcb = gbm_kcb(ng);
+    c = it / (4 * kcb);
+    bl = (it >> 2) % kcb;
     kg = it & 3;
-    blk = c * GBM_KC + bl;
+    blk = c * kcb + bl;
 }
 
 // the second pass: v[u] (element order 4kg.., 16+4kg..) / rms * w of the
@@ -71,16 +74,16 @@ QD_DEV void sb_item(int it, int& c, int& bl, int& kg, int& blk)
 // (if not null) for the product; cmax >= 32 floats
 QD_DEV void sb_norm_items(const float (&v)[SB_ITEMS][8], const float (&wv)[SB_ITEMS][8], float inv, int H,
                           int b, float* __restrict__ h, _Float16* __restrict__ XP, float* __restrict__ XS,
-                          float* cmax)
+                          int ng, float* cmax)
 {
-    const int nb = H / 32, nit = sb_nitems(H);
+    const int nb = H / 32, nit = sb_nitems(H, ng), wpc = gbm_kcb(ng) * 4 / WAVE;   // waves per chunk
     float e[SB_ITEMS][8];
 #pragma unroll
     for (int u = 0; u < SB_ITEMS; ++u) {
         const int it = (int)threadIdx.x + u * SB_THREADS;
-        if (it < nit) {   // uniform per wave (nit is a multiple of 128)
+        if (it < nit) {   // uniform per wave (nit is a multiple of 64)
             int c, bl, kg, blk;
-            sb_item(it, c, bl, kg, blk);
+            sb_item(it, ng, c, bl, kg, blk);
             float hv[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k)
@@ -110,12 +113,15 @@ QD_DEV void sb_norm_items(const float (&v)[SB_ITEMS][8], const float (&wv)[SB_IT
         const int it = (int)threadIdx.x + u * SB_THREADS;
         if (it < nit) {
             int c, bl, kg, blk;
-            sb_item(it, c, bl, kg, blk);
-            const float s = gbm_scale_for(fmaxf(cmax[2 * c], cmax[2 * c + 1]));
+            sb_item(it, ng, c, bl, kg, blk);
+            float cm = cmax[c * wpc];
+            for (int q = 1; q < wpc; ++q)
+                cm = fmaxf(cm, cmax[c * wpc + q]);
+            const float s = gbm_scale_for(cm);
             if (blk < nb)
-                gbm_xp_put(XP, c, bl, kg, b, e[u], s);
-            if ((it & 127) == 0)
-                XS[c * 16 + b] = 1.0f / s;
+                gbm_xp_put(XP, ng, c, bl, kg, b, e[u], s);
+            if (bl == 0 && kg == 0)
+                XS[c * 16 * ng + b] = 1.0f / s;
         }
     }
 }
@@ -129,7 +135,7 @@ __global__ void __launch_bounds__(SB_THREADS)
 k_embed_batch(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, int H, int vocab,
               StepState* __restrict__ st, const int32_t* __restrict__ ids, int max_seq,
               const float* __restrict__ w, float eps, float* __restrict__ x, float* __restrict__ h,
-              _Float16* __restrict__ XP, float* __restrict__ XS,
+              _Float16* __restrict__ XP, float* __restrict__ XS, int ng,
               const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int half,
               float* __restrict__ rope_cur, int rstride)
 {
@@ -151,7 +157,7 @@ k_embed_batch(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, i
         rope_cur[(size_t)b * rstride + k] = rope_cos[(size_t)pos * half + k];
         rope_cur[(size_t)b * rstride + half + k] = rope_sin[(size_t)pos * half + k];
     }
-    const int nb = H / 32, nit = sb_nitems(H);
+    const int nb = H / 32, nit = sb_nitems(H, ng);
     float* xb = x + (size_t)b * H;
     float v[SB_ITEMS][8], wv[SB_ITEMS][8];
     float ss = 0.f;
@@ -159,7 +165,7 @@ k_embed_batch(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, i
     for (int u = 0; u < SB_ITEMS; ++u) {
         const int it = (int)threadIdx.x + u * SB_THREADS;
         int c, bl, kg, blk;
-        sb_item(it, c, bl, kg, blk);
+        sb_item(it, ng, c, bl, kg, blk);
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             v[u][k] = wv[u][k] = 0.f;
@@ -187,7 +193,7 @@ k_embed_batch(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, i
         }
     }
     const float inv = 1.0f / sqrtf(sb_block_sum(ss, red) / (float)H + eps);
-    sb_norm_items(v, wv, inv, H, b, h, XP, XS, cmax);
+    sb_norm_items(v, wv, inv, H, b, h, XP, XS, ng, cmax);
 }
 
 // grid B: x[b] += y[b] (y may be null: no residual; y may come as nslab <=
@@ -196,12 +202,12 @@ k_embed_batch(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, i
 __global__ void __launch_bounds__(SB_THREADS)
 k_resid_rmsnorm_batch(float* __restrict__ x, const float* __restrict__ y, int nslab, size_t slab, int H,
                       const float* __restrict__ w, float eps, float* __restrict__ h,
-                      _Float16* __restrict__ XP, float* __restrict__ XS)
+                      _Float16* __restrict__ XP, float* __restrict__ XS, int ng)
 {
     __shared__ float red[16];
     __shared__ float cmax[32];
     const int b = blockIdx.x;
-    const int nb = H / 32, nit = sb_nitems(H);
+    const int nb = H / 32, nit = sb_nitems(H, ng);
     float* xb = x + (size_t)b * H;
     float v[SB_ITEMS][8], wv[SB_ITEMS][8];
     float ss = 0.f;
@@ -209,7 +215,7 @@ k_resid_rmsnorm_batch(float* __restrict__ x, const float* __restrict__ y, int ns
     for (int u = 0; u < SB_ITEMS; ++u) {
         const int it = (int)threadIdx.x + u * SB_THREADS;
         int c, bl, kg, blk;
-        sb_item(it, c, bl, kg, blk);
+        sb_item(it, ng, c, bl, kg, blk);
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             v[u][k] = wv[u][k] = 0.f;
@@ -248,20 +254,21 @@ k_resid_rmsnorm_batch(float* __restrict__ x, const float* __restrict__ y, int ns
         }
     }
     const float inv = 1.0f / sqrtf(sb_block_sum(ss, red) / (float)H + eps);
-    sb_norm_items(v, wv, inv, H, b, h, XP, XS, cmax);
+    sb_norm_items(v, wv, inv, H, b, h, XP, XS, ng, cmax);
 }
 
-// grid (chunks of I, B), 128 threads: a = silu(g) * up of sequence b, chunk
-// by chunk, split for the down product into XP / XS (gate and up rows
+// grid (chunks of I, B), 4 KCB threads (KCB = 32 / ng): a = silu(g) * up of
+// sequence b, chunk by chunk, split for the down product into XP / XS with
+// ng slot groups (gate and up rows
 // interleaved; gu as nslab partial products slab floats apart, added in slab
 // order)
 __global__ void __launch_bounds__(128)
-k_swiglu_xp_batch(const float* __restrict__ gu, int nslab, size_t slab, int I, _Float16* __restrict__ XP,
+k_swiglu_xp_batch(const float* __restrict__ gu, int nslab, size_t slab, int I, int ng, _Float16* __restrict__ XP,
                   float* __restrict__ XS)
 {
     __shared__ float red[2];
     const int c = blockIdx.x, b = blockIdx.y;
-    const int bl = threadIdx.x >> 2, kg = threadIdx.x & 3, blk = c * GBM_KC + bl;
+    const int bl = threadIdx.x >> 2, kg = threadIdx.x & 3, blk = c * gbm_kcb(ng) + bl;
     const bool in = blk < I / 32;
     float e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (in) {
@@ -289,9 +296,9 @@ k_swiglu_xp_batch(const float* __restrict__ gu, int nslab, size_t slab, int I, _
     }
     const float s = gbm_scale_for(gbm_chunk_max(gbm_xp_absmax(e), red));
     if (in)
-        gbm_xp_put(XP, c, bl, kg, b, e, s);
+        gbm_xp_put(XP, ng, c, bl, kg, b, e, s);
     if (threadIdx.x == 0)
-        XS[c * 16 + b] = 1.0f / s;
+        XS[c * 16 * ng + b] = 1.0f / s;
 }
 
 // (value, index) better than (bv, bi): larger value, lowest index among equals
