@@ -364,8 +364,8 @@ def test_tiny_attn_out_gate_vs_oracle(paged):
 
 @pytest.mark.parametrize("paged,kv_fp8", [(False, False), (True, False), (False, True), (True, True)])
 def test_tiny_prefill_vs_oracle(tiny, paged, kv_fp8):
-    """qd_prefill of the 16-token prompt (one full chunk: the matrix-core
-    GEMV), then qd_generate from position 16: logits at the last prompt
+    """qd_prefill of the 16-token prompt (one chunk, half of its vector slots
+    in use), then qd_generate from position 16: logits at the last prompt
     position against the oracle's, and the free-running greedy tokens."""
     import torch
     import token_decode_q4_amd as qd
@@ -399,22 +399,25 @@ def test_tiny_prefill_vs_oracle(tiny, paged, kv_fp8):
 
 
 def test_tiny_prefill_ragged_chunks_vs_oracle(tiny, tiny_ref):
-    """40 teacher-forced positions prefilled as 21 + 19 (chunks of 16, 5, 16
-    and 3 positions: both batched GEMV kernels), logits at positions 20 and
-    39 against the oracle's, then generation of the remaining greedy tokens."""
+    """40 teacher-forced positions prefilled as C + 5 and 35 - C positions
+    (C = qd.prefill_chunk(): a full chunk, a ragged one, then a short call
+    continuing the cache), logits at the last position of each call against
+    the oracle's, then generation of the remaining greedy tokens."""
     import torch
     import token_decode_q4_amd as qd
     toks, margins, seq, ref = tiny_ref
     s = tiny.shape
     P = s.prompt_len
     n = 40
+    n1 = qd.prefill_chunk() + 5
+    assert n1 < n <= s.max_seq - 1
     say("tiny prefill ragged chunks")
     m = qd.Model(tiny, use_graph=True)
     m.set_prompt(seq[:n])
     lg = torch.empty(s.vocab, dtype=torch.float32, device="cuda")
-    m.prefill(0, 21, logits_last=lg)
-    e1 = float(np.max(np.abs(host(lg) - ref[20])))
-    m.prefill(21, n - 21, logits_last=lg)
+    m.prefill(0, n1, logits_last=lg)
+    e1 = float(np.max(np.abs(host(lg) - ref[n1 - 1])))
+    m.prefill(n1, n - n1, logits_last=lg)
     e2 = float(np.max(np.abs(host(lg) - ref[n - 1])))
     say(f"tiny ragged prefill logits max abs err {e1:.3e} {e2:.3e}")
     assert max(e1, e2) <= 1e-4
@@ -518,7 +521,7 @@ def test_tiny_variant_decode_vs_oracle(name, paged):
 @pytest.mark.parametrize("name,paged", [("tiny-rot32", False), ("tiny-rot32", True),
                                         ("tiny-untied", False)])
 def test_tiny_variant_prefill_vs_oracle(name, paged):
-    """qd_prefill (matrix-core chunk of 16 positions) of the variant's prompt:
+    """qd_prefill (one chunk on the matrix-core products) of the variant's prompt:
     logits at the last prompt position (<= 1e-4), then greedy generation
     against the oracle's tokens."""
     import torch
