@@ -15,6 +15,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # no packed fp32 instructions: the compiler would otherwise form them from plain float code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results straight into VGPRs: the batched products read each
+    # block's result once, and the AGPR form adds a copy per value
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
 ]
 

@@ -493,30 +493,45 @@ k_xsplit_batch(const float* __restrict__ X, int nb, int ng, _Float16* __restrict
 // (K slices in units of KCB-block chunks), B <= 16 NG vectors at run time
 // (slots past B are zero in XP); Y[b] for b < B.  With NG = 2 each block's
 // codes, built once, meet two 16-vector groups: the code-building work per
-// vector halves.
-template <int RG, int NG>
+// vector halves.  A chunk enters LDS in SUB stages of KCB / SUB blocks (32 KB
+// each with SUB = 2), so that four workgroups fit a compute unit's LDS; each
+// block's scaled products are folded into the stage's sums as soon as they
+// are made (held otherwise, the 16 blocks' products would take 64 more
+// registers per lane and halve the waves a SIMD holds).
+constexpr int GBM_XP_SUB = 2;   // stages per chunk
+
+__host__ __device__ constexpr size_t gbm_xp_lds_bytes(int sub = GBM_XP_SUB)
+{
+    return (size_t)GBM_XP_CHUNK * sizeof(_Float16) / sub;
+}
+
+template <int RG, int NG, int DV, int SUB = GBM_XP_SUB>
 __global__ void __launch_bounds__(GBM_NW* WAVE)
 k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                 const _Float16* __restrict__ XP, const float* __restrict__ XS, float* __restrict__ Y,
-                int N, int nb, int B, int kch, size_t ystride, int dvec)
+                int N, int nb, int B, int kch, size_t ystride)
 {
     static_assert(NG == 1 || NG == 2, "slot groups");
     constexpr int KCB = GBM_KC / NG;      // blocks per chunk
-    constexpr int STEPS = KCB / 4;        // 4-block steps per chunk
+    constexpr int KS = KCB / SUB;         // blocks per stage
+    static_assert(KS % 8 == 0 && KS * SUB == KCB, "a stage holds whole eighths of a chunk");
+    constexpr int STEPS = KS / 4;         // 4-block steps per stage
     constexpr int S = 16 * NG;            // vector slots
-    extern __shared__ __align__(16) _Float16 xs[];   // one chunk of XP
+    constexpr int QW = 16 / SUB;          // 1 KB copies per wave and stage
+    extern __shared__ __align__(16) _Float16 xs[];   // one stage of XP
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
     const int r = lane & 15, kg = lane >> 4;
-    const int nch = (nb + KCB - 1) / KCB;
+    const int nch = (nb + KCB - 1) / KCB, nst = (nb + KS - 1) / KS;
     const int c0 = (int)blockIdx.y * kch, c1 = min(nch, c0 + kch);
+    const int s0 = c0 * SUB, s1 = min(nst, c1 * SUB);   // this slice's stages
     Y += (size_t)blockIdx.y * ystride;
     const int row0 = (int)blockIdx.x * gbm_rows(RG) + wave * 16 * RG;
     size_t rb[RG];
 #pragma unroll
     for (int g = 0; g < RG; ++g)
         rb[g] = (size_t)min(row0 + 16 * g + r, N - 1) * (size_t)nb;
-    const int nsteps = (c1 - c0) * STEPS;
+    const int nsteps = (s1 - s0) * STEPS;
     if (nsteps <= 0) {   // an empty slice (the host never launches one): zeros
         for (int g = 0; g < RG; ++g) {
             const int row = row0 + 16 * g + r;
@@ -532,16 +547,16 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
     };
     auto load = [&](Buf& bf, int s) {
         s = min(s, nsteps - 1);
-        const int blk = min((c0 + s / STEPS) * KCB + (s % STEPS) * 4 + kg, nb - 1);
+        const int blk = min((s0 + s / STEPS) * KS + (s % STEPS) * 4 + kg, nb - 1);
 #pragma unroll
         for (int g = 0; g < RG; ++g)
             bf.q[g] = *reinterpret_cast<const uint4*>(Q + (rb[g] + (size_t)blk) * 16u);
     };
-    // scales of chunk c: lane group kg's eighth-of-32 blocks, c*KCB + 8kg .. +7
-    // (with NG = 2 only lane groups 0 and 1 hold scales of the chunk)
-    auto load_d = [&](uint4 (&dq)[RG], int c) {
-        const int b0 = c * KCB + 8 * kg;
-        if (dvec) {   // uniform: nb % 8 == 0 and D 16-byte aligned
+    // scales of stage st: lane group kg's eighth-of-32 blocks, st*KS + 8kg .. +7
+    // (the lane groups past KS / 8 load scales no block of the stage uses)
+    auto load_d = [&](uint4 (&dq)[RG], int st) {
+        const int b0 = st * KS + 8 * kg;
+        if constexpr (DV) {   // nb % 8 == 0 and D 16-byte aligned
             const int bq = min(b0, nb - 8);
 #pragma unroll
             for (int g = 0; g < RG; ++g)
@@ -557,21 +572,21 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
             }
         }
     };
-    // chunk c of XP into LDS: wave w copies 16 KB, 1 KB per instruction
-    auto dma_x = [&](int c) {
-        const _Float16* src = XP + (size_t)c * GBM_XP_CHUNK + (size_t)wave * 16 * 512 + lane * 8;
+    // stage st of XP into LDS (its blocks are contiguous in the chunk): wave w
+    // copies QW KB, 1 KB per instruction
+    auto dma_x = [&](int st) {
+        const _Float16* src = XP + (size_t)(st / SUB) * GBM_XP_CHUNK + (size_t)(st % SUB) * (GBM_XP_CHUNK / SUB) +
+                              (size_t)wave * QW * 512 + lane * 8;
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
+        for (int q = 0; q < QW; ++q)
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void*)(src + q * 512),
-                (__attribute__((address_space(3))) void*)(xs + (wave * 16 + q) * 512), 16, 0, 0);
+                (__attribute__((address_space(3))) void*)(xs + (wave * QW + q) * 512), 16, 0, 0);
     };
-    auto load_inv = [&](float (&inv)[NG][4], int c) {
+    auto load_inv = [&](float4 (&inv)[NG], int st) {
 #pragma unroll
         for (int h = 0; h < NG; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                inv[h][i] = XS[c * S + 16 * h + 4 * kg + i];
+            inv[h] = *reinterpret_cast<const float4*>(XS + (st / SUB) * S + 16 * h + 4 * kg);
     };
 
     float acc[NG][RG][4];
@@ -583,22 +598,22 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
             for (int i = 0; i < 4; ++i)
                 acc[h][g][i] = 0.f;
     // x first (loads complete in order), then the scales, then every weight
-    // load of the first chunk; the next chunk's weights are issued while the
+    // load of the first stage; the next stage's weights are issued while the
     // current one is computed, its x and scales right after it
-    dma_x(c0);
+    dma_x(s0);
     uint4 dq[RG];
-    load_d(dq, c0);
-    float inv[NG][4];
-    load_inv(inv, c0);
+    load_d(dq, s0);
+    float4 inv[NG];
+    load_inv(inv, s0);
     Buf bufs[STEPS];
 #pragma unroll
     for (int u = 0; u < STEPS; ++u)
         load(bufs[u], u);
     const gbm_floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-    for (int c = c0; c < c1; ++c) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this chunk's x (and everything before it) landed
+    for (int st = s0; st < s1; ++st) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this stage's x (and everything before it) landed
         __syncthreads();
-        uint32_t dg[RG][KCB / 8][4];   // [group][lane group q][dword]: halves = scales of blocks 8q ..
+        uint32_t dg[RG][KS / 8][4];   // [group][lane group q][dword]: halves = scales of blocks 8q ..
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
             const uint32_t dw[4] = {dq[g].x, dq[g].y, dq[g].z, dq[g].w};
@@ -607,16 +622,10 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                 uint32_t t[4];
                 gbm_allgather4(dw[k], t);
 #pragma unroll
-                for (int q = 0; q < KCB / 8; ++q)
+                for (int q = 0; q < KS / 8; ++q)
                     dg[g][q][k] = t[q];
             }
         }
-        float cinv[NG][4];
-#pragma unroll
-        for (int h = 0; h < NG; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                cinv[h][i] = inv[h][i];
         float cacc[NG][RG][4];
 #pragma unroll
         for (int h = 0; h < NG; ++h)
@@ -625,7 +634,18 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     cacc[h][g][i] = 0.f;
-        const int sbase = (c - c0) * STEPS;
+        const int sbase = (st - s0) * STEPS;
+        // x of block bl of the stage; each block's pair is read one block ahead
+        auto read_x = [&](gbm_half8 (&xh)[NG], gbm_half8 (&xl)[NG], int bl) {
+#pragma unroll
+            for (int h = 0; h < NG; ++h) {
+                const _Float16* src = xs + ((size_t)(bl * 4 + kg) * 2 * S + 16 * h + r) * 8;
+                xh[h] = *reinterpret_cast<const gbm_half8*>(src);
+                xl[h] = *reinterpret_cast<const gbm_half8*>(src + S * 8);
+            }
+        };
+        gbm_half8 nxh[NG], nxl[NG];
+        read_x(nxh, nxl, 0);
 #pragma unroll
         for (int j = 0; j < STEPS; ++j) {
             uint32_t w[RG][4];
@@ -637,17 +657,18 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                 w[g][3] = bufs[j].q[g].w;
                 gbm_transpose4(w[g]);
             }
-            load(bufs[j], sbase + STEPS + j);   // the same step of the next chunk
+            load(bufs[j], sbase + STEPS + j);   // the same step of the next stage
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const int bl = 4 * j + b;   // block within the chunk
+                const int bl = 4 * j + b;   // block within the stage
                 gbm_half8 xh[NG], xl[NG];
 #pragma unroll
                 for (int h = 0; h < NG; ++h) {
-                    const _Float16* src = xs + ((size_t)(bl * 4 + kg) * 2 * S + 16 * h + r) * 8;
-                    xh[h] = *reinterpret_cast<const gbm_half8*>(src);
-                    xl[h] = *reinterpret_cast<const gbm_half8*>(src + S * 8);
+                    xh[h] = nxh[h];
+                    xl[h] = nxl[h];
                 }
+                if (bl + 1 < KS)   // compile-time
+                    read_x(nxh, nxl, bl + 1);
 #pragma unroll
                 for (int g = 0; g < RG; ++g) {
                     const gbm_half8 wop = gbm_codes(w[g][b]);
@@ -662,22 +683,32 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                             cacc[h][g][i] = fmaf((float)dh, pv[i], cacc[h][g][i]);
                     }
                 }
+                // the block's sums are made here: its products die at once
+#pragma unroll
+                for (int h = 0; h < NG; ++h)
+#pragma unroll
+                    for (int g = 0; g < RG; ++g)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            asm volatile("" : "+v"(cacc[h][g][i]));
             }
         }
 #pragma unroll
-        for (int h = 0; h < NG; ++h)
+        for (int h = 0; h < NG; ++h) {
+            const float ci[4] = {inv[h].x, inv[h].y, inv[h].z, inv[h].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int g = 0; g < RG; ++g)
-                    acc[h][g][i] = fmaf(cacc[h][g][i], cinv[h][i], acc[h][g][i]);
-        if (c + 1 < c1) {   // uniform
-            __syncthreads();   // every wave is done with this chunk's x
-            dma_x(c + 1);
-            load_d(dq, c + 1);
-            load_inv(inv, c + 1);
+                    acc[h][g][i] = fmaf(cacc[h][g][i], ci[i], acc[h][g][i]);
         }
-        asm volatile("" ::: "memory");   // keeps the next chunk's loads where they are issued
+        if (st + 1 < s1) {   // uniform
+            __syncthreads();   // every wave is done with this stage's x
+            dma_x(st + 1);
+            load_d(dq, st + 1);
+            load_inv(inv, st + 1);
+        }
+        asm volatile("" ::: "memory");   // keeps the next stage's loads where they are issued   // keeps the next stage's loads where they are issued
     }
 #pragma unroll
     for (int g = 0; g < RG; ++g) {

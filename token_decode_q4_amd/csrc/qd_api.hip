@@ -494,9 +494,17 @@ static int enqueue_step_fused(qd_model* m, hipStream_t s)
 // of the matrix-core GEMV alone give too few workgroups for short matrices,
 // so K is cut into slices (whole 32-block chunks) up to about 768 workgroups
 // (measured at the Qwen3-8B shapes: gate|up 2 slices, q|k|v and o 4, down 6)
-static int step_kslices(int N, int nb, int ng = 1)
+// Row groups per wave of each split-input product (measured best at the
+// Qwen3-8B shape: with 16 vectors one row group except the LM head, whose
+// grid is large anyway; with the prefill's 32 two, except o)
+constexpr int STEP_RG_QKV = 1, STEP_RG_O = 1, STEP_RG_GU = 1, STEP_RG_DOWN = 1, STEP_RG_LM = 2;
+constexpr int PF_RG_QKV = 2, PF_RG_O = 1, PF_RG_GU = 2, PF_RG_DOWN = 2;
+
+// K slices of a split-input product: about 768 workgroups, at most one per
+// chunk and SB_MAXSLAB in all
+static int step_kslices(int N, int nb, int ng, int rg)
 {
-    const int tiles = (N + gbm_rows(1) - 1) / gbm_rows(1);
+    const int tiles = (N + gbm_rows(rg) - 1) / gbm_rows(rg);
     const int nch = gbm_nchunks(nb, ng);
     int ks = std::min({nch, SB_MAXSLAB, std::max(1, (768 + tiles / 2) / tiles)});
     if (ks > 1) {
@@ -506,23 +514,37 @@ static int step_kslices(int N, int nb, int ng = 1)
     return ks;
 }
 
-// the batched step's product Y = W X on the matrix cores from x split in
-// XP / XS, in ks K slices (partial slabs of B*N floats, summed by the
-// consumer); one row group per wave (two need more registers than a wave
-// has and spill: measured 2-3x slower at every shape of the step)
-static hipError_t step_gemv(const qd_model* m, const DevQ4& W, const _Float16* XP, const float* XS, float* Y,
-                            int ks, hipStream_t s)
+// Y = W X on the matrix cores from x split in XP / XS with NG slot groups
+// (nv <= 16 NG vectors), rg row groups per wave, in ks K slices (partial
+// slabs of nv*N floats, summed by the consumer)
+template <int NG>
+static hipError_t xp_gemv(const DevQ4& W, const _Float16* XP, const float* XS, float* Y, int nv, int ks, int rg,
+                          hipStream_t s)
 {
     const int N = W.rows, nb = W.nb;
-    const int nch = gbm_nchunks(nb, 1);
+    const int nch = gbm_nchunks(nb, NG);
     const int kch = (nch + ks - 1) / ks;
-    if (ks < 1 || (int64_t)(ks - 1) * kch >= nch)   // every slice holds at least one chunk
+    if (ks < 1 || (int64_t)(ks - 1) * kch >= nch || (rg != 1 && rg != 2))   // every slice holds a chunk
         return hipErrorInvalidValue;
-    const int dvec = (nb % 8 == 0 && reinterpret_cast<uintptr_t>(W.d) % 16 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((k_gemv_batch_xp<1, 1>), dim3((N + gbm_rows(1) - 1) / gbm_rows(1), ks),
-                       dim3(GBM_NW * WAVE), gemv_batch_mfma_lds_bytes(), s, W.d, W.qs, XP, XS, Y, N, nb, m->B, kch,
-                       (size_t)m->B * N, dvec);
+    const bool dvec = nb % 8 == 0 && reinterpret_cast<uintptr_t>(W.d) % 16 == 0;
+    const dim3 grid((N + gbm_rows(rg) - 1) / gbm_rows(rg), ks), block(GBM_NW * WAVE);
+    const size_t lds = gbm_xp_lds_bytes(), ys = (size_t)nv * N;
+    if (rg == 1 && dvec)
+        hipLaunchKernelGGL((k_gemv_batch_xp<1, NG, 1>), grid, block, lds, s, W.d, W.qs, XP, XS, Y, N, nb, nv, kch, ys);
+    else if (rg == 1)
+        hipLaunchKernelGGL((k_gemv_batch_xp<1, NG, 0>), grid, block, lds, s, W.d, W.qs, XP, XS, Y, N, nb, nv, kch, ys);
+    else if (dvec)
+        hipLaunchKernelGGL((k_gemv_batch_xp<2, NG, 1>), grid, block, lds, s, W.d, W.qs, XP, XS, Y, N, nb, nv, kch, ys);
+    else
+        hipLaunchKernelGGL((k_gemv_batch_xp<2, NG, 0>), grid, block, lds, s, W.d, W.qs, XP, XS, Y, N, nb, nv, kch, ys);
     return hipGetLastError();
+}
+
+// the batched step's product over its B sequences
+static hipError_t step_gemv(const qd_model* m, const DevQ4& W, const _Float16* XP, const float* XS, float* Y,
+                            int ks, int rg, hipStream_t s)
+{
+    return xp_gemv<1>(W, XP, XS, Y, m->B, ks, rg, s);
 }
 
 // One step of the B sequences of a batched model: every weight read once for
@@ -538,7 +560,7 @@ static int enqueue_step_batch(qd_model* m, hipStream_t s)
                        m->rope_cos, m->rope_sin, m->rot / 2, m->rope_cur, m->rstride);
     for (int l = 0; l < m->L; ++l) {
         DevLayer& Ly = m->layers[l];
-        HIP_TRY(step_gemv(m, Ly.qkv, m->xp_h, m->xs_h, m->bqkv, m->ks_qkv, s));
+        HIP_TRY(step_gemv(m, Ly.qkv, m->xp_h, m->xs_h, m->bqkv, m->ks_qkv, STEP_RG_QKV, s));
         AttnParams p;
         memset(&p, 0, sizeof p);
         p.q = m->bqkv;
@@ -579,18 +601,18 @@ static int enqueue_step_batch(qd_model* m, hipStream_t s)
         const size_t slab_h = (size_t)B * H;
         hipLaunchKernelGGL(k_xsplit_batch, dim3(gbm_nchunks(nqd / 32, 1), B), dim3(128), 0, s, m->battn,
                            nqd / 32, 1, m->xp_o, m->xs_o, nullptr, 0, 1, (size_t)0);
-        HIP_TRY(step_gemv(m, Ly.o, m->xp_o, m->xs_o, m->bo, m->ks_o, s));
+        HIP_TRY(step_gemv(m, Ly.o, m->xp_o, m->xs_o, m->bo, m->ks_o, STEP_RG_O, s));
         hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(B), dim3(SB_THREADS), 0, s, m->bx, m->bo, m->ks_o, slab_h,
                            H, Ly.ffn_norm, m->eps, nullptr, m->xp_h, m->xs_h, 1);
-        HIP_TRY(step_gemv(m, Ly.gu, m->xp_h, m->xs_h, m->bgu, m->ks_gu, s));
+        HIP_TRY(step_gemv(m, Ly.gu, m->xp_h, m->xs_h, m->bgu, m->ks_gu, STEP_RG_GU, s));
         hipLaunchKernelGGL(k_swiglu_xp_batch, dim3(gbm_nchunks(I / 32, 1), B), dim3(128), 0, s, m->bgu,
                            m->ks_gu, (size_t)B * 2 * I, I, 1, m->xp_i, m->xs_i);
-        HIP_TRY(step_gemv(m, Ly.down, m->xp_i, m->xs_i, m->bo, m->ks_down, s));
+        HIP_TRY(step_gemv(m, Ly.down, m->xp_i, m->xs_i, m->bo, m->ks_down, STEP_RG_DOWN, s));
         const float* wn = (l + 1 < m->L) ? m->layers[l + 1].attn_norm : m->final_norm;
         hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(B), dim3(SB_THREADS), 0, s, m->bx, m->bo, m->ks_down,
                            slab_h, H, wn, m->eps, nullptr, m->xp_h, m->xs_h, 1);
     }
-    HIP_TRY(step_gemv(m, m->lm, m->xp_h, m->xs_h, m->blog, 1, s));
+    HIP_TRY(step_gemv(m, m->lm, m->xp_h, m->xs_h, m->blog, 1, STEP_RG_LM, s));
     hipLaunchKernelGGL(k_argmax_batch, dim3(m->bG, B), dim3(256), 0, s, m->blog, m->V, m->bchunk, m->bcval,
                        m->bcidx);
     hipLaunchKernelGGL(k_argmax_advance_batch, dim3(B), dim3(256), 0, s, m->bcval, m->bcidx, m->bG, m->V, m->st,
@@ -941,10 +963,10 @@ static int create_model(const qd_config* cfg, const qd_weights* w, int B, qd_str
     if (B > 1) {
         m->bchunk = 4096;
         m->bG = (m->V + m->bchunk - 1) / m->bchunk;
-        m->ks_qkv = step_kslices(m->qkv_rows, H / 32);
-        m->ks_o = step_kslices(H, nqd / 32);
-        m->ks_gu = step_kslices(2 * m->I, H / 32);
-        m->ks_down = step_kslices(H, m->I / 32);
+        m->ks_qkv = step_kslices(m->qkv_rows, H / 32, 1, STEP_RG_QKV);
+        m->ks_o = step_kslices(H, nqd / 32, 1, STEP_RG_O);
+        m->ks_gu = step_kslices(2 * m->I, H / 32, 1, STEP_RG_GU);
+        m->ks_down = step_kslices(H, m->I / 32, 1, STEP_RG_DOWN);
         const size_t Bz = B;
         if ((rc = dev_alloc_t(m, &m->bx, Bz * H)) || (rc = dev_alloc_t(m, &m->bh, Bz * H)) ||
             (rc = dev_alloc_t(m, &m->bqkv, Bz * m->ks_qkv * m->qkv_rows)) ||
@@ -1724,10 +1746,10 @@ static int pf_setup(qd_model* m)
     const size_t ws = attn_ws_layout(PF_T, m->nq, m->nkv, m->hd, m->max_seq, &P.geo);
     if (m->H > 16384)   // the batched RMSNorm splits at most 2 items per thread
         return fail(QD_EUNSUPPORTED, "qd_prefill supports hidden <= 16384 (got %d)", m->H);
-    P.ks_qkv = step_kslices(m->qkv_rows, m->H / 32, PF_NG);
-    P.ks_o = step_kslices(m->H, (int)nqd / 32, PF_NG);
-    P.ks_gu = step_kslices(2 * m->I, m->H / 32, PF_NG);
-    P.ks_down = step_kslices(m->H, m->I / 32, PF_NG);
+    P.ks_qkv = step_kslices(m->qkv_rows, m->H / 32, PF_NG, PF_RG_QKV);
+    P.ks_o = step_kslices(m->H, (int)nqd / 32, PF_NG, PF_RG_O);
+    P.ks_gu = step_kslices(2 * m->I, m->H / 32, PF_NG, PF_RG_GU);
+    P.ks_down = step_kslices(m->H, m->I / 32, PF_NG, PF_RG_DOWN);
     const size_t ch_h = gbm_nchunks(m->H / 32, PF_NG), ch_o = gbm_nchunks((int)nqd / 32, PF_NG),
                  ch_i = gbm_nchunks(m->I / 32, PF_NG), S = 16 * PF_NG;
     int rc;
@@ -1759,22 +1781,11 @@ static int pf_setup(qd_model* m)
     return QD_OK;
 }
 
-// the chunk's product Y = W X on the matrix cores from x split in XP / XS,
-// T positions (vector slots in PF_NG groups of 16), in ks K slices (partial
-// slabs of T*N floats)
-static hipError_t pf_gemv(const DevQ4& W, const _Float16* XP, const float* XS, int T, float* Y, int ks,
+// the chunk's product over its T positions (vector slots in PF_NG groups of 16)
+static hipError_t pf_gemv(const DevQ4& W, const _Float16* XP, const float* XS, int T, float* Y, int ks, int rg,
                           hipStream_t s)
 {
-    const int N = W.rows, nb = W.nb;
-    const int nch = gbm_nchunks(nb, PF_NG);
-    const int kch = (nch + ks - 1) / ks;
-    if (ks < 1 || (int64_t)(ks - 1) * kch >= nch)
-        return hipErrorInvalidValue;
-    const int dvec = (nb % 8 == 0 && reinterpret_cast<uintptr_t>(W.d) % 16 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((k_gemv_batch_xp<1, PF_NG>), dim3((N + gbm_rows(1) - 1) / gbm_rows(1), ks),
-                       dim3(GBM_NW * WAVE), gemv_batch_mfma_lds_bytes(), s, W.d, W.qs, XP, XS, Y, N, nb, T, kch,
-                       (size_t)T * N, dvec);
-    return hipGetLastError();
+    return xp_gemv<PF_NG>(W, XP, XS, Y, T, ks, rg, s);
 }
 
 extern "C" int32_t qd_prefill_chunk(void) { return PF_T; }
@@ -1806,7 +1817,7 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
                            H, m->layers[0].attn_norm, m->eps, nullptr, P.xp_h, P.xs_h, PF_NG);
         for (int l = 0; l < m->L; ++l) {
             DevLayer& Ly = m->layers[l];
-            HIP_TRY(pf_gemv(Ly.qkv, P.xp_h, P.xs_h, T, P.QKV, P.ks_qkv, s));
+            HIP_TRY(pf_gemv(Ly.qkv, P.xp_h, P.xs_h, T, P.QKV, P.ks_qkv, PF_RG_QKV, s));
             const size_t slab_qkv = (size_t)T * m->qkv_rows;
             const float* qn = m->qk_norm ? Ly.q_norm : m->ones_hd;
             const float* kn = m->qk_norm ? Ly.k_norm : m->ones_hd;
@@ -1851,13 +1862,13 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
             const float* gate = m->attn_gate ? P.QKV + (size_t)(m->nq + 2 * m->nkv) * hd : nullptr;
             hipLaunchKernelGGL(k_xsplit_batch, dim3(gbm_nchunks(nqd / 32, PF_NG), T), dim3(4 * gbm_kcb(PF_NG)), 0,
                                s, P.O, nqd / 32, PF_NG, P.xp_o, P.xs_o, gate, m->qkv_rows, P.ks_qkv, slab_qkv);
-            HIP_TRY(pf_gemv(Ly.o, P.xp_o, P.xs_o, T, P.OD, P.ks_o, s));
+            HIP_TRY(pf_gemv(Ly.o, P.xp_o, P.xs_o, T, P.OD, P.ks_o, PF_RG_O, s));
             hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(T), dim3(SB_THREADS), 0, s, P.X, P.OD, P.ks_o, slab_h,
                                H, Ly.ffn_norm, m->eps, nullptr, P.xp_h, P.xs_h, PF_NG);
-            HIP_TRY(pf_gemv(Ly.gu, P.xp_h, P.xs_h, T, P.GU, P.ks_gu, s));
+            HIP_TRY(pf_gemv(Ly.gu, P.xp_h, P.xs_h, T, P.GU, P.ks_gu, PF_RG_GU, s));
             hipLaunchKernelGGL(k_swiglu_xp_batch, dim3(gbm_nchunks(I / 32, PF_NG), T), dim3(4 * gbm_kcb(PF_NG)), 0,
                                s, P.GU, P.ks_gu, (size_t)T * 2 * I, I, PF_NG, P.xp_i, P.xs_i);
-            HIP_TRY(pf_gemv(Ly.down, P.xp_i, P.xs_i, T, P.OD, P.ks_down, s));
+            HIP_TRY(pf_gemv(Ly.down, P.xp_i, P.xs_i, T, P.OD, P.ks_down, PF_RG_DOWN, s));
             // the residual, then the next layer's norm (split for its q|k|v), or
             // the final norm of every position (f32, the last one feeds the LM head)
             const bool last = l + 1 == m->L;

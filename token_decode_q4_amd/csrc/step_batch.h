@@ -30,7 +30,7 @@ namespace qd {
 
 constexpr int SB_MAXB = 16;    // sequences of a batched model
 constexpr int SB_THREADS = 1024;
-constexpr int SB_MAXSLAB = 8;  // K slices of a batched step's product
+constexpr int SB_MAXSLAB = 12;  // K slices of a batched step's product
 
 // sum over a workgroup of SB_THREADS threads in a fixed order (every thread
 // gets it); red >= 16 floats
