@@ -76,6 +76,11 @@ MODELS = {
     # q/k head turn (inv_freq = 1e6^(-2i/32), 16 frequencies), the rest pass
     "tiny-rot32": ModelShape("tiny-rot32", 1, 2, 256, 4, 2, 64, 768, 1024, True, True, 1e6,
                              32, 1e-6, False, 48, 16, 32),
+    # the tiny decoder at sizes that are not multiples of 256: hidden 288 and
+    # SwiGLU 800 (9 and 25 q4_0 blocks per row, a ragged last chunk), vocab
+    # 1000 (a ragged last row tile)
+    "tiny-odd": ModelShape("tiny-odd", 7, 2, 288, 4, 2, 64, 800, 1000, True, True, 1e6, 64, 1e-6,
+                           False, 48, 16, 32),
     # Qwen3-0.6B shape, contiguous KV; 512 prompt tokens + 256 greedy tokens
     "qwen3-0.6b": ModelShape("qwen3-0.6b", 4, 28, 1024, 16, 8, 128, 3072, 151936, True,
                              True, 1e6, 128, 1e-6, False, 768, 512, 256),

@@ -147,6 +147,29 @@ def test_tiny_batch_teacher_forced_logits(tiny, tiny_runs, B):
     assert worst <= 1e-3
 
 
+@pytest.mark.parametrize("B,paged", [(4, False), (16, True)])
+def test_tiny_odd_batch_vs_oracle(B, paged):
+    """A model at sizes that are not multiples of 256 (hidden 288, SwiGLU 800,
+    vocab 1000): the products' rows hold 9 and 25 q4_0 blocks (scales loaded
+    one by one, a ragged last chunk) and the LM head ends in a partial row
+    tile.  Teacher-forced logits of every sequence within 1e-3 of the oracle,
+    then each sequence's greedy tokens."""
+    mi = synth.make_model("tiny-odd")
+    prompts = _prompts(mi, B, 8, 16, seed=79)
+    runs = _oracle_runs(mi, prompts, TINY_S)
+    say(f"tiny-odd batch B={B} paged={paged}")
+    m = _batch_model(mi, B, paged)
+    lg = _teacher_forced_batch(m, runs, TINY_S, mi.shape.vocab)
+    m.close()
+    worst = max(float(np.max(np.abs(lg[b] - runs[b][3]))) for b in range(B))
+    record(f"tiny-odd batch B={B}: teacher-forced logits max abs err {worst:.3e}")
+    assert worst <= 1e-3
+    m = _batch_model(mi, B, paged)
+    got = _run_lockstep(m, prompts, TINY_S)
+    m.close()
+    _compare(got, prompts, runs, f"tiny-odd B={B} paged={paged}", lg)
+
+
 def test_tiny_batch_kv_fp8_vs_oracle(tiny):
     """fp8 e4m3 K/V caches in the batched step (k_scale 0.5, v_scale 0.125)."""
     B = 4

@@ -472,6 +472,15 @@ def test_tiny_gated_prefill_vs_oracle(paged):
     _greedy_gate(got, toks, margins, "tiny gated prefill")
 
 
+# Regression guards on the variants' teacher-forced logits (max abs), far
+# inside the c14 parity bar of 2e-2 and a few times above each model's
+# measured f32 error: the tiny family's is 2.5e-5 .. 5e-5; tiny-odd, another
+# random draw, sits at 1.4e-4 on both the decode and the batched paths (the
+# tiny weights with only the vocabulary cut to 1000 show the same level, so
+# it is the draw's conditioning, not its sizes).
+_VARIANT_GUARD = {"tiny-odd": 5e-4}
+
+
 def _variant_ref(name):
     mi = synth.make_model(name)
     om = oracle.Model(mi)
@@ -491,9 +500,11 @@ def _paged_inputs(mi, nblocks=8):
 
 
 @pytest.mark.parametrize("name,paged", [("tiny-rot32", False), ("tiny-rot32", True),
-                                        ("tiny-untied", False), ("tiny-untied", True)])
+                                        ("tiny-untied", False), ("tiny-untied", True),
+                                        ("tiny-odd", False), ("tiny-odd", True)])
 def test_tiny_variant_decode_vs_oracle(name, paged):
-    """Partial rotary (rot_dim 32 of head_dim 64) and an untied LM head through
+    """Partial rotary (rot_dim 32 of head_dim 64), an untied LM head and sizes
+    that are not multiples of 256 (hidden 288, SwiGLU 800, vocab 1000) through
     the decode step: teacher-forced logits of every position (<= 1e-4 abs) and
     the teacher-forced argmax, free-running greedy tokens, graph == eager."""
     import token_decode_q4_amd as qd
@@ -507,7 +518,7 @@ def test_tiny_variant_decode_vs_oracle(name, paged):
     lg, nxt = _teacher_forced_logits(m, seq, s.vocab)
     err = float(np.max(np.abs(lg - ref)))
     say(f"{name} paged={paged}: logits max abs err {err:.3e} over {len(seq)} positions")
-    assert err <= 1e-4
+    assert err <= _VARIANT_GUARD.get(name, 1e-4)
     assert np.array_equal(nxt[P - 1:], np.argmax(ref.astype(np.float32), axis=1)[P - 1:])
     got = _gen(m, mi.prompt, s.gen)[P - 1:]
     m.close()
@@ -519,7 +530,7 @@ def test_tiny_variant_decode_vs_oracle(name, paged):
 
 
 @pytest.mark.parametrize("name,paged", [("tiny-rot32", False), ("tiny-rot32", True),
-                                        ("tiny-untied", False)])
+                                        ("tiny-untied", False), ("tiny-odd", False), ("tiny-odd", True)])
 def test_tiny_variant_prefill_vs_oracle(name, paged):
     """qd_prefill (one chunk on the matrix-core products) of the variant's prompt:
     logits at the last prompt position (<= 1e-4), then greedy generation
@@ -538,7 +549,7 @@ def test_tiny_variant_prefill_vs_oracle(name, paged):
     m.prefill(0, P, logits_last=lg)
     err = float(np.max(np.abs(host(lg) - ref[P - 1])))
     say(f"{name} prefill paged={paged}: logits max abs err {err:.3e}")
-    assert err <= 1e-4
+    assert err <= _VARIANT_GUARD.get(name, 1e-4)
     out = torch.full((G - 1,), -1, dtype=torch.int32, device="cuda")
     m.generate(P, G - 1, tokens=out)
     m.check()
