@@ -509,7 +509,8 @@ template <int RG, int NG, int DV, int SUB = GBM_XP_SUB>
 __global__ void __launch_bounds__(GBM_NW* WAVE)
 k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                 const _Float16* __restrict__ XP, const float* __restrict__ XS, float* __restrict__ Y,
-                int N, int nb, int B, int kch, size_t ystride)
+                int N, int nb, int B, int kch, size_t ystride, const float* __restrict__ SQ = nullptr,
+                int nsq = 0, float hn = 1.f, float eps = 0.f)
 {
     static_assert(NG == 1 || NG == 2, "slot groups");
     constexpr int KCB = GBM_KC / NG;      // blocks per chunk
@@ -597,6 +598,23 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 acc[h][g][i] = 0.f;
+    // an input split without its RMSNorm (SQ: the chunk sums of x^2, nsq <= 32
+    // chunks, hn = the row length): 1/rms of each of this lane's vectors
+    // multiplies its sums at the end.  Lane r of a lane group loads chunks r
+    // and r + 16 (clamped, zero past nsq) first; the 16 lanes' values are
+    // added, in a fixed order, once the first stage's wait has seen them land.
+    const bool norm = SQ != nullptr;
+    const int nq = norm ? nsq : 0;
+    float4 sa[NG], sb[NG];
+    {
+        const float* sqp = norm ? SQ : XS;
+        const int last = max(nq - 1, 0);
+#pragma unroll
+        for (int h = 0; h < NG; ++h) {
+            sa[h] = *reinterpret_cast<const float4*>(sqp + (size_t)min(r, last) * S + 16 * h + 4 * kg);
+            sb[h] = *reinterpret_cast<const float4*>(sqp + (size_t)min(r + 16, last) * S + 16 * h + 4 * kg);
+        }
+    }
     // x first (loads complete in order), then the scales, then every weight
     // load of the first stage; the next stage's weights are issued while the
     // current one is computed, its x and scales right after it
@@ -610,9 +628,21 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
     for (int u = 0; u < STEPS; ++u)
         load(bufs[u], u);
     const gbm_floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+    float rinv[NG][4];
     for (int st = s0; st < s1; ++st) {
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this stage's x (and everything before it) landed
         __syncthreads();
+        if (st == s0) {   // uniform
+#pragma unroll
+            for (int h = 0; h < NG; ++h) {
+                const float ua = r < nq ? 1.f : 0.f, ub = r + 16 < nq ? 1.f : 0.f;
+                const float v[4] = {sa[h].x * ua + sb[h].x * ub, sa[h].y * ua + sb[h].y * ub,
+                                    sa[h].z * ua + sb[h].z * ub, sa[h].w * ua + sb[h].w * ub};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    rinv[h][i] = norm ? 1.0f / sqrtf(group_sum<16>(v[i]) / hn + eps) : 1.0f;
+            }
+        }
         uint32_t dg[RG][KS / 8][4];   // [group][lane group q][dword]: halves = scales of blocks 8q ..
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
@@ -708,7 +738,7 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
             load_d(dq, st + 1);
             load_inv(inv, st + 1);
         }
-        asm volatile("" ::: "memory");   // keeps the next stage's loads where they are issued   // keeps the next stage's loads where they are issued
+        asm volatile("" ::: "memory");   // keeps the next stage's loads where they are issued
     }
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
@@ -719,7 +749,7 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (16 * h + 4 * kg + i < B)
-                        Y[(size_t)(16 * h + 4 * kg + i) * N + row] = acc[h][g][i];
+                        Y[(size_t)(16 * h + 4 * kg + i) * N + row] = acc[h][g][i] * rinv[h][i];
         }
     }
 }

@@ -130,6 +130,7 @@ struct qd_model {
     // (q|k|v, gate|up, LM head), attention output (o), SwiGLU output (down)
     _Float16 *xp_h = nullptr, *xp_o = nullptr, *xp_i = nullptr;
     float *xs_h = nullptr, *xs_o = nullptr, *xs_i = nullptr;
+    float* sq_h = nullptr;   // chunk sums of x^2 of the hidden-sized split (its norm's 1/rms)
     int32_t* bcidx = nullptr;
     int bG = 1, bchunk = 1;
     int ks_qkv = 1, ks_o = 1, ks_gu = 1, ks_down = 1;   // K slices of the batched products
@@ -147,6 +148,7 @@ struct qd_model {
         // position: hidden-sized, attention output, SwiGLU output
         _Float16 *xp_h = nullptr, *xp_o = nullptr, *xp_i = nullptr;
         float *xs_h = nullptr, *xs_o = nullptr, *xs_i = nullptr;
+        float* sq_h = nullptr;   // chunk sums of x^2 of the hidden-sized split
         float* fa = nullptr;                       // k_pf_attn partials [T][nq][FA_MAXS][hd + 2]
         int32_t *lens = nullptr, *iota = nullptr;
         float* ws = nullptr;
@@ -516,34 +518,43 @@ static int step_kslices(int N, int nb, int ng, int rg)
 
 // Y = W X on the matrix cores from x split in XP / XS with NG slot groups
 // (nv <= 16 NG vectors), rg row groups per wave, in ks K slices (partial
-// slabs of nv*N floats, summed by the consumer)
+// slabs of nv*N floats, summed by the consumer).  With SQ (the chunk sums of
+// x^2 of a split written without its RMSNorm, nsq chunks) the product applies
+// 1/rms = 1/sqrt(sum / hn + eps) of each vector itself.
 template <int NG>
 static hipError_t xp_gemv(const DevQ4& W, const _Float16* XP, const float* XS, float* Y, int nv, int ks, int rg,
-                          hipStream_t s)
+                          hipStream_t s, const float* SQ = nullptr, int nsq = 0, float hn = 1.f, float eps = 0.f)
 {
     const int N = W.rows, nb = W.nb;
     const int nch = gbm_nchunks(nb, NG);
     const int kch = (nch + ks - 1) / ks;
-    if (ks < 1 || (int64_t)(ks - 1) * kch >= nch || (rg != 1 && rg != 2))   // every slice holds a chunk
-        return hipErrorInvalidValue;
+    if (ks < 1 || (int64_t)(ks - 1) * kch >= nch || (rg != 1 && rg != 2) || nsq < 0 || nsq > 32)
+        return hipErrorInvalidValue;   // every slice holds a chunk; at most 32 chunk sums
     const bool dvec = nb % 8 == 0 && reinterpret_cast<uintptr_t>(W.d) % 16 == 0;
     const dim3 grid((N + gbm_rows(rg) - 1) / gbm_rows(rg), ks), block(GBM_NW * WAVE);
     const size_t lds = gbm_xp_lds_bytes(), ys = (size_t)nv * N;
     if (rg == 1 && dvec)
-        hipLaunchKernelGGL((k_gemv_batch_xp<1, NG, 1>), grid, block, lds, s, W.d, W.qs, XP, XS, Y, N, nb, nv, kch, ys);
+        hipLaunchKernelGGL((k_gemv_batch_xp<1, NG, 1>), grid, block, lds, s, W.d, W.qs, XP, XS, Y, N, nb, nv, kch, ys, SQ, nsq,
+                           hn, eps);
     else if (rg == 1)
-        hipLaunchKernelGGL((k_gemv_batch_xp<1, NG, 0>), grid, block, lds, s, W.d, W.qs, XP, XS, Y, N, nb, nv, kch, ys);
+        hipLaunchKernelGGL((k_gemv_batch_xp<1, NG, 0>), grid, block, lds, s, W.d, W.qs, XP, XS, Y, N, nb, nv, kch, ys, SQ, nsq,
+                           hn, eps);
     else if (dvec)
-        hipLaunchKernelGGL((k_gemv_batch_xp<2, NG, 1>), grid, block, lds, s, W.d, W.qs, XP, XS, Y, N, nb, nv, kch, ys);
+        hipLaunchKernelGGL((k_gemv_batch_xp<2, NG, 1>), grid, block, lds, s, W.d, W.qs, XP, XS, Y, N, nb, nv, kch, ys, SQ, nsq,
+                           hn, eps);
     else
-        hipLaunchKernelGGL((k_gemv_batch_xp<2, NG, 0>), grid, block, lds, s, W.d, W.qs, XP, XS, Y, N, nb, nv, kch, ys);
+        hipLaunchKernelGGL((k_gemv_batch_xp<2, NG, 0>), grid, block, lds, s, W.d, W.qs, XP, XS, Y, N, nb, nv, kch, ys, SQ, nsq,
+                           hn, eps);
     return hipGetLastError();
 }
 
-// the batched step's product over its B sequences
+// the batched step's product over its B sequences; normed: the input is the
+// hidden-sized split written by a norm (k_resid_norm_xp_batch, k_embed_xp_batch)
 static hipError_t step_gemv(const qd_model* m, const DevQ4& W, const _Float16* XP, const float* XS, float* Y,
-                            int ks, int rg, hipStream_t s)
+                            int ks, int rg, hipStream_t s, bool normed = false)
 {
+    if (normed)
+        return xp_gemv<1>(W, XP, XS, Y, m->B, ks, rg, s, m->sq_h, gbm_nchunks(m->H / 32, 1), (float)m->H, m->eps);
     return xp_gemv<1>(W, XP, XS, Y, m->B, ks, rg, s);
 }
 
@@ -555,12 +566,13 @@ static int enqueue_step_batch(qd_model* m, hipStream_t s)
 {
     const int B = m->B, H = m->H, I = m->I;
     const int nqd = m->nq * m->hd;
-    hipLaunchKernelGGL(k_embed_batch, dim3(B), dim3(SB_THREADS), 0, s, m->embed.d, m->embed.qs, H, m->V, m->st,
-                       m->ids, m->max_seq, m->layers[0].attn_norm, m->eps, m->bx, nullptr, m->xp_h, m->xs_h, 1,
-                       m->rope_cos, m->rope_sin, m->rot / 2, m->rope_cur, m->rstride);
+    const dim3 ngrid(gbm_nchunks(H / 32, 1), B), nblock(4 * gbm_kcb(1));
+    hipLaunchKernelGGL(k_embed_xp_batch, ngrid, nblock, 0, s, m->embed.d, m->embed.qs, H, m->V, m->st, m->ids,
+                       m->max_seq, m->layers[0].attn_norm, m->bx, 1, m->xp_h, m->xs_h, m->sq_h, m->rope_cos,
+                       m->rope_sin, m->rot / 2, m->rope_cur, m->rstride);
     for (int l = 0; l < m->L; ++l) {
         DevLayer& Ly = m->layers[l];
-        HIP_TRY(step_gemv(m, Ly.qkv, m->xp_h, m->xs_h, m->bqkv, m->ks_qkv, STEP_RG_QKV, s));
+        HIP_TRY(step_gemv(m, Ly.qkv, m->xp_h, m->xs_h, m->bqkv, m->ks_qkv, STEP_RG_QKV, s, true));
         AttnParams p;
         memset(&p, 0, sizeof p);
         p.q = m->bqkv;
@@ -602,17 +614,17 @@ static int enqueue_step_batch(qd_model* m, hipStream_t s)
         hipLaunchKernelGGL(k_xsplit_batch, dim3(gbm_nchunks(nqd / 32, 1), B), dim3(128), 0, s, m->battn,
                            nqd / 32, 1, m->xp_o, m->xs_o, nullptr, 0, 1, (size_t)0);
         HIP_TRY(step_gemv(m, Ly.o, m->xp_o, m->xs_o, m->bo, m->ks_o, STEP_RG_O, s));
-        hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(B), dim3(SB_THREADS), 0, s, m->bx, m->bo, m->ks_o, slab_h,
-                           H, Ly.ffn_norm, m->eps, nullptr, m->xp_h, m->xs_h, 1);
-        HIP_TRY(step_gemv(m, Ly.gu, m->xp_h, m->xs_h, m->bgu, m->ks_gu, STEP_RG_GU, s));
+        hipLaunchKernelGGL(k_resid_norm_xp_batch, ngrid, nblock, 0, s, m->bx, m->bo, m->ks_o, slab_h, H,
+                           Ly.ffn_norm, 1, m->xp_h, m->xs_h, m->sq_h);
+        HIP_TRY(step_gemv(m, Ly.gu, m->xp_h, m->xs_h, m->bgu, m->ks_gu, STEP_RG_GU, s, true));
         hipLaunchKernelGGL(k_swiglu_xp_batch, dim3(gbm_nchunks(I / 32, 1), B), dim3(128), 0, s, m->bgu,
                            m->ks_gu, (size_t)B * 2 * I, I, 1, m->xp_i, m->xs_i);
         HIP_TRY(step_gemv(m, Ly.down, m->xp_i, m->xs_i, m->bo, m->ks_down, STEP_RG_DOWN, s));
         const float* wn = (l + 1 < m->L) ? m->layers[l + 1].attn_norm : m->final_norm;
-        hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(B), dim3(SB_THREADS), 0, s, m->bx, m->bo, m->ks_down,
-                           slab_h, H, wn, m->eps, nullptr, m->xp_h, m->xs_h, 1);
+        hipLaunchKernelGGL(k_resid_norm_xp_batch, ngrid, nblock, 0, s, m->bx, m->bo, m->ks_down, slab_h, H, wn,
+                           1, m->xp_h, m->xs_h, m->sq_h);
     }
-    HIP_TRY(step_gemv(m, m->lm, m->xp_h, m->xs_h, m->blog, 1, STEP_RG_LM, s));
+    HIP_TRY(step_gemv(m, m->lm, m->xp_h, m->xs_h, m->blog, 1, STEP_RG_LM, s, true));
     hipLaunchKernelGGL(k_argmax_batch, dim3(m->bG, B), dim3(256), 0, s, m->blog, m->V, m->bchunk, m->bcval,
                        m->bcidx);
     hipLaunchKernelGGL(k_argmax_advance_batch, dim3(B), dim3(256), 0, s, m->bcval, m->bcidx, m->bG, m->V, m->st,
@@ -981,7 +993,8 @@ static int create_model(const qd_config* cfg, const qd_weights* w, int B, qd_str
         if ((rc = dev_alloc_t(m, &m->xp_h, ch_h * GBM_XP_CHUNK)) ||
             (rc = dev_alloc_t(m, &m->xp_o, ch_o * GBM_XP_CHUNK)) ||
             (rc = dev_alloc_t(m, &m->xp_i, ch_i * GBM_XP_CHUNK)) || (rc = dev_alloc_t(m, &m->xs_h, ch_h * 16)) ||
-            (rc = dev_alloc_t(m, &m->xs_o, ch_o * 16)) || (rc = dev_alloc_t(m, &m->xs_i, ch_i * 16)))
+            (rc = dev_alloc_t(m, &m->xs_o, ch_o * 16)) || (rc = dev_alloc_t(m, &m->xs_i, ch_i * 16)) ||
+            (rc = dev_alloc_t(m, &m->sq_h, ch_h * 16)))
             return bail(rc);
         // slots past the batch and blocks past the end are read as zeros forever
         if (hipMemsetAsync(m->xp_h, 0, ch_h * GBM_XP_CHUNK * sizeof(_Float16), s) != hipSuccess ||
@@ -989,7 +1002,8 @@ static int create_model(const qd_config* cfg, const qd_weights* w, int B, qd_str
             hipMemsetAsync(m->xp_i, 0, ch_i * GBM_XP_CHUNK * sizeof(_Float16), s) != hipSuccess ||
             hipMemsetAsync(m->xs_h, 0, ch_h * 16 * sizeof(float), s) != hipSuccess ||
             hipMemsetAsync(m->xs_o, 0, ch_o * 16 * sizeof(float), s) != hipSuccess ||
-            hipMemsetAsync(m->xs_i, 0, ch_i * 16 * sizeof(float), s) != hipSuccess)
+            hipMemsetAsync(m->xs_i, 0, ch_i * 16 * sizeof(float), s) != hipSuccess ||
+            hipMemsetAsync(m->sq_h, 0, ch_h * 16 * sizeof(float), s) != hipSuccess)
             return bail(fail(QD_EHIP, "batch buffer clear failed"));
     }
     if (hipMemsetAsync(m->st, 0, sizeof(StepState) * B, s) != hipSuccess ||
@@ -1761,6 +1775,7 @@ static int pf_setup(qd_model* m)
         (rc = dev_alloc_t(m, &P.xp_h, ch_h * GBM_XP_CHUNK)) || (rc = dev_alloc_t(m, &P.xp_o, ch_o * GBM_XP_CHUNK)) ||
         (rc = dev_alloc_t(m, &P.xp_i, ch_i * GBM_XP_CHUNK)) || (rc = dev_alloc_t(m, &P.xs_h, ch_h * S)) ||
         (rc = dev_alloc_t(m, &P.xs_o, ch_o * S)) || (rc = dev_alloc_t(m, &P.xs_i, ch_i * S)) ||
+        (rc = dev_alloc_t(m, &P.sq_h, ch_h * S)) ||
         (rc = dev_alloc_t(m, &P.fa, T * nqd / m->hd * PF_FA_MAXS * (m->hd + 2))) ||
         (rc = dev_alloc_t(m, &P.lens, T)) || (rc = dev_alloc_t(m, &P.iota, (size_t)m->V)) ||
         (rc = dev_alloc_t(m, &P.ws, ws / sizeof(float) + 1)))
@@ -1773,7 +1788,8 @@ static int pf_setup(qd_model* m)
         hipMemset(P.xp_i, 0, ch_i * GBM_XP_CHUNK * sizeof(_Float16)) != hipSuccess ||
         hipMemset(P.xs_h, 0, ch_h * S * sizeof(float)) != hipSuccess ||
         hipMemset(P.xs_o, 0, ch_o * S * sizeof(float)) != hipSuccess ||
-        hipMemset(P.xs_i, 0, ch_i * S * sizeof(float)) != hipSuccess)
+        hipMemset(P.xs_i, 0, ch_i * S * sizeof(float)) != hipSuccess ||
+        hipMemset(P.sq_h, 0, ch_h * S * sizeof(float)) != hipSuccess)
         return fail(QD_EHIP, "prefill buffer set-up failed");
     if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess)
         return fail(QD_EHIP, "prefill buffer set-up failed");
@@ -1781,10 +1797,13 @@ static int pf_setup(qd_model* m)
     return QD_OK;
 }
 
-// the chunk's product over its T positions (vector slots in PF_NG groups of 16)
-static hipError_t pf_gemv(const DevQ4& W, const _Float16* XP, const float* XS, int T, float* Y, int ks, int rg,
-                          hipStream_t s)
+// the chunk's product over its T positions (vector slots in PF_NG groups of
+// 16); SQ: the input is a hidden-sized split written by k_resid_norm_xp_batch
+static hipError_t pf_gemv(const qd_model* m, const DevQ4& W, const _Float16* XP, const float* XS, int T, float* Y,
+                          int ks, int rg, hipStream_t s, const float* SQ = nullptr)
 {
+    if (SQ)
+        return xp_gemv<PF_NG>(W, XP, XS, Y, T, ks, rg, s, SQ, gbm_nchunks(m->H / 32, PF_NG), (float)m->H, m->eps);
     return xp_gemv<PF_NG>(W, XP, XS, Y, T, ks, rg, s);
 }
 
@@ -1813,11 +1832,12 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
         const size_t slab_h = (size_t)T * H;
         hipLaunchKernelGGL(k_pf_embed, dim3((H + 255) / 256, T), dim3(256), 0, s, m->embed.d, m->embed.qs,
                            H, m->ids, p0, P.X);
-        hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(T), dim3(SB_THREADS), 0, s, P.X, nullptr, 0, (size_t)0,
-                           H, m->layers[0].attn_norm, m->eps, nullptr, P.xp_h, P.xs_h, PF_NG);
+        const dim3 ngrid(gbm_nchunks(H / 32, PF_NG), T), nblock(4 * gbm_kcb(PF_NG));
+        hipLaunchKernelGGL(k_resid_norm_xp_batch, ngrid, nblock, 0, s, P.X, nullptr, 0, (size_t)0, H,
+                           m->layers[0].attn_norm, PF_NG, P.xp_h, P.xs_h, P.sq_h);
         for (int l = 0; l < m->L; ++l) {
             DevLayer& Ly = m->layers[l];
-            HIP_TRY(pf_gemv(Ly.qkv, P.xp_h, P.xs_h, T, P.QKV, P.ks_qkv, PF_RG_QKV, s));
+            HIP_TRY(pf_gemv(m, Ly.qkv, P.xp_h, P.xs_h, T, P.QKV, P.ks_qkv, PF_RG_QKV, s, P.sq_h));
             const size_t slab_qkv = (size_t)T * m->qkv_rows;
             const float* qn = m->qk_norm ? Ly.q_norm : m->ones_hd;
             const float* kn = m->qk_norm ? Ly.k_norm : m->ones_hd;
@@ -1862,19 +1882,21 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
             const float* gate = m->attn_gate ? P.QKV + (size_t)(m->nq + 2 * m->nkv) * hd : nullptr;
             hipLaunchKernelGGL(k_xsplit_batch, dim3(gbm_nchunks(nqd / 32, PF_NG), T), dim3(4 * gbm_kcb(PF_NG)), 0,
                                s, P.O, nqd / 32, PF_NG, P.xp_o, P.xs_o, gate, m->qkv_rows, P.ks_qkv, slab_qkv);
-            HIP_TRY(pf_gemv(Ly.o, P.xp_o, P.xs_o, T, P.OD, P.ks_o, PF_RG_O, s));
-            hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(T), dim3(SB_THREADS), 0, s, P.X, P.OD, P.ks_o, slab_h,
-                               H, Ly.ffn_norm, m->eps, nullptr, P.xp_h, P.xs_h, PF_NG);
-            HIP_TRY(pf_gemv(Ly.gu, P.xp_h, P.xs_h, T, P.GU, P.ks_gu, PF_RG_GU, s));
+            HIP_TRY(pf_gemv(m, Ly.o, P.xp_o, P.xs_o, T, P.OD, P.ks_o, PF_RG_O, s));
+            hipLaunchKernelGGL(k_resid_norm_xp_batch, ngrid, nblock, 0, s, P.X, P.OD, P.ks_o, slab_h, H,
+                               Ly.ffn_norm, PF_NG, P.xp_h, P.xs_h, P.sq_h);
+            HIP_TRY(pf_gemv(m, Ly.gu, P.xp_h, P.xs_h, T, P.GU, P.ks_gu, PF_RG_GU, s, P.sq_h));
             hipLaunchKernelGGL(k_swiglu_xp_batch, dim3(gbm_nchunks(I / 32, PF_NG), T), dim3(4 * gbm_kcb(PF_NG)), 0,
                                s, P.GU, P.ks_gu, (size_t)T * 2 * I, I, PF_NG, P.xp_i, P.xs_i);
-            HIP_TRY(pf_gemv(Ly.down, P.xp_i, P.xs_i, T, P.OD, P.ks_down, PF_RG_DOWN, s));
+            HIP_TRY(pf_gemv(m, Ly.down, P.xp_i, P.xs_i, T, P.OD, P.ks_down, PF_RG_DOWN, s));
             // the residual, then the next layer's norm (split for its q|k|v), or
             // the final norm of every position (f32, the last one feeds the LM head)
-            const bool last = l + 1 == m->L;
-            hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(T), dim3(SB_THREADS), 0, s, P.X, P.OD, P.ks_down,
-                               slab_h, H, last ? m->final_norm : m->layers[l + 1].attn_norm, m->eps,
-                               last ? P.HF : nullptr, last ? nullptr : P.xp_h, P.xs_h, PF_NG);
+            if (l + 1 < m->L)
+                hipLaunchKernelGGL(k_resid_norm_xp_batch, ngrid, nblock, 0, s, P.X, P.OD, P.ks_down, slab_h, H,
+                                   m->layers[l + 1].attn_norm, PF_NG, P.xp_h, P.xs_h, P.sq_h);
+            else
+                hipLaunchKernelGGL(k_resid_rmsnorm_batch, dim3(T), dim3(SB_THREADS), 0, s, P.X, P.OD, P.ks_down,
+                                   slab_h, H, m->final_norm, m->eps, P.HF, nullptr, P.xs_h, PF_NG);
         }
     }
     // the last position: LM head, greedy token as a decode step records it

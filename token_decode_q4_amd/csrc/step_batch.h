@@ -6,21 +6,19 @@
 //
 // Each of the B sequences has its own position, stored tokens, K/V cache and
 // greedy prediction; every weight is read once per step for all of them by
-// the batched GEMVs (gemv_batch.h, gemv_batch_mfma.h), which take the
-// normalised activations whole.  So here, unlike the one-sequence step, the
-// RMSNorm is applied before the product: one workgroup per sequence adds the
-// residual, takes the mean square of the row in a fixed order and writes the
-// normalised row for the next product.
-//   k_embed_batch           x[b] = E[token_b]; h[b] = rms(x[b]) * w; rotary factors
+// the batched GEMVs (gemv_batch_mfma.h), which take their input already split
+// (XP / XS).  So here, unlike the one-sequence step, the RMSNorm's weights are
+// applied before the product, by one workgroup per (chunk, sequence); each
+// chunk's sum of x^2 goes beside the split and the product applies 1/rms.
+//   k_embed_xp_batch        x[b] = E[token_b]; split of x[b] * w; rotary factors
 //   (batched q|k|v GEMV; split-KV attention over the B caches; k_xsplit_batch;
 //    batched o GEMV)
-//   k_resid_rmsnorm_batch   x[b] += y[b]; h[b] = rms(x[b]) * w
+//   k_resid_norm_xp_batch   x[b] += y[b]; split of x[b] * w
 //   (batched gate|up GEMV)  k_swiglu_xp_batch: a[b][i] = silu(g) * up
-//   (batched down GEMV)     k_resid_rmsnorm_batch (next layer's or the final norm)
-// The products take their input already split (XP / XS, gemv_batch_mfma.h):
-// the normalised rows, the SwiGLU output and the attention output are written
-// in that form by their producers.
+//   (batched down GEMV)     k_resid_norm_xp_batch (next layer's or the final norm)
 //   (batched LM head)       k_argmax_batch, k_argmax_advance_batch
+// k_resid_rmsnorm_batch, one workgroup per row, writes a normalised row in
+// f32 (the prefill's final norm, whose last row feeds the one-vector LM head).
 #pragma once
 
 #include "gemv_batch_mfma.h"
@@ -126,76 +124,6 @@ QD_DEV void sb_norm_items(const float (&v)[SB_ITEMS][8], const float (&wv)[SB_IT
     }
 }
 
-// grid B: sequence b at its position st[b].pos reads its stored token, writes
-// x[b] (the embedding row) and x[b] / rms * w (to h and/or XP / XS, as
-// sb_norm_items), and the rotary factors of its position (cos [half] then sin
-// [half]) at rope_cur + b * rstride.  A position or token out of range is
-// recorded in st[b].error and replaced by 0 (reported by qd_check).
-__global__ void __launch_bounds__(SB_THREADS)
-k_embed_batch(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, int H, int vocab,
-              StepState* __restrict__ st, const int32_t* __restrict__ ids, int max_seq,
-              const float* __restrict__ w, float eps, float* __restrict__ x, float* __restrict__ h,
-              _Float16* __restrict__ XP, float* __restrict__ XS, int ng,
-              const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int half,
-              float* __restrict__ rope_cur, int rstride)
-{
-    __shared__ float red[16];
-    __shared__ float cmax[32];
-    const int b = blockIdx.x;
-    StepState* sb = st + b;
-    int pos = sb->pos;
-    if (pos < 0 || pos >= max_seq) {
-        if (threadIdx.x == 0) sb->error |= 2;
-        pos = 0;
-    }
-    int tok = ids[(size_t)b * max_seq + pos];
-    if (tok < 0 || tok >= vocab) {
-        if (threadIdx.x == 0) sb->error |= 1;
-        tok = 0;
-    }
-    for (int k = threadIdx.x; k < half; k += blockDim.x) {
-        rope_cur[(size_t)b * rstride + k] = rope_cos[(size_t)pos * half + k];
-        rope_cur[(size_t)b * rstride + half + k] = rope_sin[(size_t)pos * half + k];
-    }
-    const int nb = H / 32, nit = sb_nitems(H, ng);
-    float* xb = x + (size_t)b * H;
-    float v[SB_ITEMS][8], wv[SB_ITEMS][8];
-    float ss = 0.f;
-#pragma unroll
-    for (int u = 0; u < SB_ITEMS; ++u) {
-        const int it = (int)threadIdx.x + u * SB_THREADS;
-        int c, bl, kg, blk;
-        sb_item(it, ng, c, bl, kg, blk);
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            v[u][k] = wv[u][k] = 0.f;
-        if (it < nit && blk < nb) {
-            // word kg of the token's block: codes of elements 4kg.. (low nibbles) and 16+4kg.. (high)
-            const size_t blkg = (size_t)tok * nb + blk;
-            const uint32_t wd = *reinterpret_cast<const uint32_t*>(Eq + blkg * 16 + 4 * kg);
-            const float d = f16_to_f32(Ed[blkg]);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                v[u][k] = (float)((int)((wd >> (8 * k)) & 15u) - 8) * d;
-                v[u][4 + k] = (float)((int)((wd >> (8 * k + 4)) & 15u) - 8) * d;
-            }
-            float* xp = xb + (size_t)blk * 32 + 4 * kg;
-            *reinterpret_cast<float4*>(xp) = make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
-            *reinterpret_cast<float4*>(xp + 16) = make_float4(v[u][4], v[u][5], v[u][6], v[u][7]);
-            const float4 wa = *reinterpret_cast<const float4*>(w + (size_t)blk * 32 + 4 * kg);
-            const float4 wh = *reinterpret_cast<const float4*>(w + (size_t)blk * 32 + 16 + 4 * kg);
-            const float wl[8] = {wa.x, wa.y, wa.z, wa.w, wh.x, wh.y, wh.z, wh.w};
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                wv[u][k] = wl[k];
-                ss = fmaf(v[u][k], v[u][k], ss);
-            }
-        }
-    }
-    const float inv = 1.0f / sqrtf(sb_block_sum(ss, red) / (float)H + eps);
-    sb_norm_items(v, wv, inv, H, b, h, XP, XS, ng, cmax);
-}
-
 // grid B: x[b] += y[b] (y may be null: no residual; y may come as nslab <=
 // SB_MAXSLAB partial products slab floats apart, added in slab order);
 // x[b] / rms * w to h and/or XP / XS (as sb_norm_items)
@@ -255,6 +183,154 @@ k_resid_rmsnorm_batch(float* __restrict__ x, const float* __restrict__ y, int ns
     }
     const float inv = 1.0f / sqrtf(sb_block_sum(ss, red) / (float)H + eps);
     sb_norm_items(v, wv, inv, H, b, h, XP, XS, ng, cmax);
+}
+
+// sum over a workgroup of 64 or 128 threads (a chunk's items) in a fixed
+// order; every thread gets it; red >= 2 floats
+QD_DEV float sb_chunk_sum(float v, float* red)
+{
+    v = group_sum<WAVE>(v);
+    if ((threadIdx.x & (WAVE - 1)) == 0)
+        red[threadIdx.x / WAVE] = v;
+    __syncthreads();
+    return blockDim.x > WAVE ? red[0] + red[1] : red[0];
+}
+
+// The chunk-parallel form of the norm before a product: one workgroup per
+// (chunk, sequence) holds v (elements 4kg.., 16+4kg.. of its item, zero past
+// the row) and the norm weights wv, and writes v * w split (XP / XS with a
+// scale of its own) and the chunk's sum of v^2 to SQ[c][slot].  The 1/rms
+// factor is left to the product, which sums SQ over the chunks of its
+// vectors (k_gemv_batch_xp): a row's norm needs no workgroup to wait for
+// another.
+QD_DEV void sb_norm_chunk(const float (&v)[8], const float (&wv)[8], int c, int bl, int kg, int b, bool in,
+                          int ng, _Float16* __restrict__ XP, float* __restrict__ XS, float* __restrict__ SQ,
+                          float* red_m, float* red_s)
+{
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        ss = fmaf(v[k], v[k], ss);
+    const float q = 0.0625f;   // the split order (high four divided by 16)
+    const float e[8] = {v[0] * wv[0], v[2] * wv[2], v[1] * wv[1], v[3] * wv[3],
+                        v[4] * wv[4] * q, v[6] * wv[6] * q, v[5] * wv[5] * q, v[7] * wv[7] * q};
+    const float s = gbm_scale_for(gbm_chunk_max(gbm_xp_absmax(e), red_m));
+    const float sq = sb_chunk_sum(ss, red_s);
+    if (in)
+        gbm_xp_put(XP, ng, c, bl, kg, b, e, s);
+    if (threadIdx.x == 0) {
+        XS[c * 16 * ng + b] = 1.0f / s;
+        SQ[c * 16 * ng + b] = sq;
+    }
+}
+
+// grid (chunks of H, B), 4 KCB threads (KCB = 32 / ng): x[b] += y[b] (y may
+// be null: no residual; y may come as nslab partial products slab floats
+// apart, added in slab order), then x[b] * w split for the product with the
+// chunk sums of x[b]^2 (sb_norm_chunk)
+__global__ void __launch_bounds__(128)
+k_resid_norm_xp_batch(float* __restrict__ x, const float* __restrict__ y, int nslab, size_t slab, int H,
+                      const float* __restrict__ w, int ng, _Float16* __restrict__ XP, float* __restrict__ XS,
+                      float* __restrict__ SQ)
+{
+    __shared__ float red_m[2], red_s[2];
+    const int c = blockIdx.x, b = blockIdx.y;
+    const int bl = threadIdx.x >> 2, kg = threadIdx.x & 3, blk = c * gbm_kcb(ng) + bl;
+    const bool in = blk < H / 32;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float wv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (in) {
+        const size_t off = (size_t)blk * 32 + 4 * kg;
+        float* xb = x + (size_t)b * H + off;
+        float4 a = *reinterpret_cast<const float4*>(xb);
+        float4 e = *reinterpret_cast<const float4*>(xb + 16);
+        const float4 wa = *reinterpret_cast<const float4*>(w + off);
+        const float4 wh = *reinterpret_cast<const float4*>(w + off + 16);
+        if (y) {   // uniform
+            const float* yb = y + (size_t)b * H + off;
+            float4 ra = *reinterpret_cast<const float4*>(yb);
+            float4 re = *reinterpret_cast<const float4*>(yb + 16);
+            for (int k = 1; k < nslab; ++k) {
+                const float4 pa = *reinterpret_cast<const float4*>(yb + k * slab);
+                const float4 pe = *reinterpret_cast<const float4*>(yb + k * slab + 16);
+                ra = make_float4(ra.x + pa.x, ra.y + pa.y, ra.z + pa.z, ra.w + pa.w);
+                re = make_float4(re.x + pe.x, re.y + pe.y, re.z + pe.z, re.w + pe.w);
+            }
+            a = make_float4(a.x + ra.x, a.y + ra.y, a.z + ra.z, a.w + ra.w);
+            e = make_float4(e.x + re.x, e.y + re.y, e.z + re.z, e.w + re.w);
+            *reinterpret_cast<float4*>(xb) = a;
+            *reinterpret_cast<float4*>(xb + 16) = e;
+        }
+        const float vl[8] = {a.x, a.y, a.z, a.w, e.x, e.y, e.z, e.w};
+        const float wl[8] = {wa.x, wa.y, wa.z, wa.w, wh.x, wh.y, wh.z, wh.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            v[k] = vl[k];
+            wv[k] = wl[k];
+        }
+    }
+    sb_norm_chunk(v, wv, c, bl, kg, b, in, ng, XP, XS, SQ, red_m, red_s);
+}
+
+// grid (chunks of H, B), 4 KCB threads: sequence b at its position
+// st[b].pos reads its stored token and writes x[b] (the embedding row), the
+// split of x[b] * w with the chunk sums of x[b]^2 (as k_resid_norm_xp_batch)
+// and, in the chunk 0 workgroup, the rotary factors of its position (cos
+// [half] then sin [half]) at rope_cur + b * rstride.  A position or token out
+// of range is recorded in st[b].error and replaced by 0 (reported by
+// qd_check).
+__global__ void __launch_bounds__(128)
+k_embed_xp_batch(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq, int H, int vocab,
+                 StepState* __restrict__ st, const int32_t* __restrict__ ids, int max_seq,
+                 const float* __restrict__ w, float* __restrict__ x, int ng, _Float16* __restrict__ XP,
+                 float* __restrict__ XS, float* __restrict__ SQ, const float* __restrict__ rope_cos,
+                 const float* __restrict__ rope_sin, int half, float* __restrict__ rope_cur, int rstride)
+{
+    __shared__ float red_m[2], red_s[2];
+    const int c = blockIdx.x, b = blockIdx.y;
+    StepState* sb = st + b;
+    int pos = sb->pos;
+    const bool pos_bad = pos < 0 || pos >= max_seq;
+    if (pos_bad)
+        pos = 0;
+    int tok = ids[(size_t)b * max_seq + pos];
+    const bool tok_bad = tok < 0 || tok >= vocab;
+    if (tok_bad)
+        tok = 0;
+    if (c == 0) {
+        if (threadIdx.x == 0 && (pos_bad || tok_bad))
+            sb->error |= (pos_bad ? 2 : 0) | (tok_bad ? 1 : 0);
+        for (int k = threadIdx.x; k < half; k += blockDim.x) {
+            rope_cur[(size_t)b * rstride + k] = rope_cos[(size_t)pos * half + k];
+            rope_cur[(size_t)b * rstride + half + k] = rope_sin[(size_t)pos * half + k];
+        }
+    }
+    const int nb = H / 32;
+    const int bl = threadIdx.x >> 2, kg = threadIdx.x & 3, blk = c * gbm_kcb(ng) + bl;
+    const bool in = blk < nb;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float wv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (in) {
+        // word kg of the token's block: codes of elements 4kg.. (low nibbles) and 16+4kg.. (high)
+        const size_t blkg = (size_t)tok * nb + blk;
+        const uint32_t wd = *reinterpret_cast<const uint32_t*>(Eq + blkg * 16 + 4 * kg);
+        const float d = f16_to_f32(Ed[blkg]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[k] = (float)((int)((wd >> (8 * k)) & 15u) - 8) * d;
+            v[4 + k] = (float)((int)((wd >> (8 * k + 4)) & 15u) - 8) * d;
+        }
+        float* xp = x + (size_t)b * H + (size_t)blk * 32 + 4 * kg;
+        *reinterpret_cast<float4*>(xp) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(xp + 16) = make_float4(v[4], v[5], v[6], v[7]);
+        const float4 wa = *reinterpret_cast<const float4*>(w + (size_t)blk * 32 + 4 * kg);
+        const float4 wh = *reinterpret_cast<const float4*>(w + (size_t)blk * 32 + 16 + 4 * kg);
+        const float wl[8] = {wa.x, wa.y, wa.z, wa.w, wh.x, wh.y, wh.z, wh.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            wv[k] = wl[k];
+    }
+    sb_norm_chunk(v, wv, c, bl, kg, b, in, ng, XP, XS, SQ, red_m, red_s);
 }
 
 // grid (chunks of I, B), 4 KCB threads (KCB = 32 / ng): a = silu(g) * up of
