@@ -1706,14 +1706,18 @@ extern "C" int qd_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink,
 // ------------------------------------------------------------------ chunked prefill
 
 // Chunk attention with each K/V tile read once for the chunk's queries
-// (k_pf_attn, f16 caches): about 256 workgroups over the keys 0 .. p0+T-1,
-// at most PF_FA_MAXS splits of a multiple of 16 keys, then the combine.
+// (k_pf_attn, f16 caches): about QD_PF_ATT_WGS workgroups over the keys
+// 0 .. p0+T-1, at most PF_FA_MAXS splits of a multiple of 16 keys, then the
+// combine.
+#ifndef QD_PF_ATT_WGS
+#define QD_PF_ATT_WGS 256
+#endif
 constexpr int PF_FA_MAXS = 64;
 static void pf_attention(qd_model* m, DevLayer& Ly, int p0, int T, hipStream_t s)
 {
     auto& P = m->pf;
     const int kv_total = p0 + T, gq = m->nq / m->nkv;
-    const int target = std::max(1, 256 / m->nkv);
+    const int target = std::max(1, QD_PF_ATT_WGS / m->nkv);
     int chunk = (kv_total + target - 1) / target;
     chunk = std::max(chunk, (kv_total + PF_FA_MAXS - 1) / PF_FA_MAXS);
     chunk = std::max(16, (chunk + 15) / 16 * 16);
