@@ -174,23 +174,24 @@ int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* d_tokens,
 
 /* Chunked prompt prefill (inferencelayer cuda_llm.rs page: prefill as the
  * many-token form of the decode step, its q4 GEMV arm at M > 1): runs the
- * positions pos0 .. pos0+n-1 in chunks of up to 16, each chunk one batched
- * GEMV per matrix (every weight read once per chunk), with the tokens
+ * positions pos0 .. pos0+n-1 in chunks of up to qd_prefill_chunk() (32),
+ * each chunk one batched product per matrix (every weight read once per
+ * chunk), with the tokens
  * stored by qd_set_prompt (or an earlier step).  It writes the K/V cache of
  * every position as n decode steps would, and at the last position p =
  * pos0+n-1 it records what a decode step at p records: the argmax of its
  * logits as the prediction at p and, if p+1 is not forced, the token at
  * p+1.  d_logits_last (device f32 [vocab] or NULL) receives the logits at p.
  * Each position's values equal the decode step's up to f32 rounding order.
- * Continue with qd_generate(pos0 + n, ...).  Buffers (about 16 positions of
+ * Continue with qd_generate(pos0 + n, ...).  Buffers (about 32 positions of
  * activations plus an attention workspace) are allocated by the first call,
  * which synchronises; later calls allocate nothing.  The matrix products
  * are those of the batched decode step with the chunk's positions as its
  * vectors: each position's activations enter as an f16 pair (hi + lo, about
- * 22 significant bits) after scaling each 1024-element chunk of the position's
+ * 22 significant bits) after scaling each 512-element chunk of the position's
  * vector by a power of two that puts its largest magnitude in [2^13, 2^14),
  * undone exactly in f32, so any finite activation scale is handled; the block
- * scales d are applied in f32.  A model with attn_out_gate gates each
+ * scales d and each position's 1/rms are applied in f32.  A model with attn_out_gate gates each
  * position's attention output as the decode step does.  hidden <= 16384
  * (QD_EUNSUPPORTED otherwise).  QD_ERANGE unless 0 <= pos0, n >= 1,
  * pos0 + n <= max_seq and pos0 is at most one past the written prefix;
