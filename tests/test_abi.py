@@ -37,8 +37,8 @@ def test_header_functions_exported(qd):
 
 
 def test_prefill_chunk(qd):
-    # two groups of 16 positions: the matrix-core product's vectors
-    assert qd.prefill_chunk() == 32
+    # four groups of 16 positions: the matrix-core product's vectors
+    assert qd.prefill_chunk() == 64
 
 
 def test_gemv_validation(qd):

@@ -364,9 +364,9 @@ def test_tiny_attn_out_gate_vs_oracle(paged):
 
 @pytest.mark.parametrize("paged,kv_fp8", [(False, False), (True, False), (False, True), (True, True)])
 def test_tiny_prefill_vs_oracle(tiny, paged, kv_fp8):
-    """qd_prefill of the 16-token prompt (one chunk, half of its vector slots
-    in use), then qd_generate from position 16: logits at the last prompt
-    position against the oracle's, and the free-running greedy tokens."""
+    """qd_prefill of the 16-token prompt (one chunk, a quarter of its vector
+    slots in use), then qd_generate from position 16: logits at the last
+    prompt position against the oracle's, and the free-running greedy tokens."""
     import torch
     import token_decode_q4_amd as qd
     s = tiny.shape
@@ -398,30 +398,36 @@ def test_tiny_prefill_vs_oracle(tiny, paged, kv_fp8):
     _greedy_gate(got, toks, margins, "tiny prefill")
 
 
-def test_tiny_prefill_ragged_chunks_vs_oracle(tiny, tiny_ref):
-    """40 teacher-forced positions prefilled as C + 5 and 35 - C positions
-    (C = qd.prefill_chunk(): a full chunk, a ragged one, then a short call
-    continuing the cache), logits at the last position of each call against
-    the oracle's, then generation of the remaining greedy tokens."""
+def test_tiny_prefill_ragged_chunks_vs_oracle():
+    """The tiny decoder with a 160-position cache: 100 teacher-forced
+    positions prefilled as C + 5 and 95 - C positions (C = qd.prefill_chunk():
+    a full chunk, a ragged one, then a call continuing the cache in a ragged
+    chunk), logits at the last position of each call against the oracle's,
+    then generation of the remaining greedy tokens."""
+    import dataclasses
     import torch
     import token_decode_q4_amd as qd
-    toks, margins, seq, ref = tiny_ref
-    s = tiny.shape
-    P = s.prompt_len
-    n = 40
+    shape = dataclasses.replace(synth.MODELS["tiny"], name="tiny-long", max_seq=160, gen=145)
+    mi = synth.make_model(shape)
+    P, G = shape.prompt_len, shape.gen
+    toks, margins, _ = oracle.generate(oracle.Model(mi), mi.prompt, G)
+    seq = list(mi.prompt) + list(toks[:-1])
+    om = oracle.Model(mi)
+    ref = np.stack([om.step(int(t), p) for p, t in enumerate(seq)])
+    n = 100
     n1 = qd.prefill_chunk() + 5
-    assert n1 < n <= s.max_seq - 1
+    assert n1 < n <= shape.max_seq - 1
     say("tiny prefill ragged chunks")
-    m = qd.Model(tiny, use_graph=True)
+    m = qd.Model(mi, use_graph=True)
     m.set_prompt(seq[:n])
-    lg = torch.empty(s.vocab, dtype=torch.float32, device="cuda")
+    lg = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
     m.prefill(0, n1, logits_last=lg)
     e1 = float(np.max(np.abs(host(lg) - ref[n1 - 1])))
     m.prefill(n1, n - n1, logits_last=lg)
     e2 = float(np.max(np.abs(host(lg) - ref[n - 1])))
     say(f"tiny ragged prefill logits max abs err {e1:.3e} {e2:.3e}")
     assert max(e1, e2) <= 1e-4
-    rest = s.max_seq - 1 - n
+    rest = shape.max_seq - 1 - n
     out = torch.full((rest,), -1, dtype=torch.int32, device="cuda")
     m.generate(n, rest, tokens=out)
     m.check()

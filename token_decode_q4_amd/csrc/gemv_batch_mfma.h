@@ -402,6 +402,9 @@ constexpr int GBM_XP_CHUNK = GBM_KC * 4 * 2 * 16 * 8;   // halves per chunk (any
 
 __host__ __device__ constexpr int gbm_kcb(int ng) { return GBM_KC / ng; }          // blocks per chunk
 __host__ __device__ constexpr int gbm_nchunks(int nb, int ng) { return (nb + gbm_kcb(ng) - 1) / gbm_kcb(ng); }
+// threads of a producer workgroup of one chunk (4 per block; at least a wave,
+// the items past the chunk's blocks idle)
+__host__ __device__ constexpr int gbm_chunk_threads(int ng) { return 4 * gbm_kcb(ng) > 64 ? 4 * gbm_kcb(ng) : 64; }
 
 // largest |.| of the 8 elements in slot order (the high four undone)
 QD_DEV float gbm_xp_absmax(const float (&e)[8])
@@ -442,7 +445,7 @@ QD_DEV float gbm_chunk_max(float m, float* red)
     return blockDim.x > WAVE ? fmaxf(red[0], red[1]) : red[0];
 }
 
-// grid (chunks, B), 4 * KCB threads (one per (block, lane group) item):
+// grid (chunks, B), gbm_chunk_threads(ng) threads (one per (block, lane group) item):
 // vector b of X [B][nb * 32] into XP / XS with NG = ng slot groups.  With a
 // gate (vector b's at gate + b * gstride, as ngslab partial products gslab
 // floats apart, added in slab order) x is first multiplied by sigmoid(gate),
@@ -454,7 +457,7 @@ k_xsplit_batch(const float* __restrict__ X, int nb, int ng, _Float16* __restrict
     __shared__ float red[2];
     const int c = blockIdx.x, b = blockIdx.y;
     const int bl = threadIdx.x >> 2, kg = threadIdx.x & 3, blk = c * gbm_kcb(ng) + bl;
-    const bool in = blk < nb;
+    const bool in = bl < gbm_kcb(ng) && blk < nb;
     float e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (in) {
         const size_t off = (size_t)blk * 32 + 4 * kg;
@@ -498,21 +501,23 @@ k_xsplit_batch(const float* __restrict__ X, int nb, int ng, _Float16* __restrict
 // block's scaled products are folded into the stage's sums as soon as they
 // are made (held otherwise, the 16 blocks' products would take 64 more
 // registers per lane and halve the waves a SIMD holds).
-constexpr int GBM_XP_SUB = 2;   // stages per chunk
+constexpr int GBM_XP_SUB = 2;   // stages per chunk (one with NG = 4: 8 blocks)
+
+__host__ __device__ constexpr int gbm_xp_sub(int ng) { return ng == 4 ? 1 : GBM_XP_SUB; }
 
 __host__ __device__ constexpr size_t gbm_xp_lds_bytes(int sub = GBM_XP_SUB)
 {
     return (size_t)GBM_XP_CHUNK * sizeof(_Float16) / sub;
 }
 
-template <int RG, int NG, int DV, int SUB = GBM_XP_SUB>
+template <int RG, int NG, int DV, int SUB = gbm_xp_sub(NG)>
 __global__ void __launch_bounds__(GBM_NW* WAVE)
 k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
                 const _Float16* __restrict__ XP, const float* __restrict__ XS, float* __restrict__ Y,
                 int N, int nb, int B, int kch, size_t ystride, const float* __restrict__ SQ = nullptr,
                 int nsq = 0, float hn = 1.f, float eps = 0.f)
 {
-    static_assert(NG == 1 || NG == 2, "slot groups");
+    static_assert(NG == 1 || NG == 2 || NG == 4, "slot groups");
     constexpr int KCB = GBM_KC / NG;      // blocks per chunk
     constexpr int KS = KCB / SUB;         // blocks per stage
     static_assert(KS % 8 == 0 && KS * SUB == KCB, "a stage holds whole eighths of a chunk");
@@ -598,22 +603,24 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 acc[h][g][i] = 0.f;
-    // an input split without its RMSNorm (SQ: the chunk sums of x^2, nsq <= 32
-    // chunks, hn = the row length): 1/rms of each of this lane's vectors
-    // multiplies its sums at the end.  Lane r of a lane group loads chunks r
-    // and r + 16 (clamped, zero past nsq) first; the 16 lanes' values are
-    // added, in a fixed order, once the first stage's wait has seen them land.
+    // an input split without its RMSNorm (SQ: the chunk sums of x^2, nsq <=
+    // 16 NQR chunks, hn = the row length): 1/rms of each of this lane's
+    // vectors multiplies its sums at the end.  Lane r of a lane group loads
+    // chunks r, r + 16, .. (clamped, zero past nsq) first; the 16 lanes'
+    // values are added, in a fixed order, once the first stage's wait has
+    // seen them land.
+    constexpr int NQR = NG == 4 ? 4 : 2;
     const bool norm = SQ != nullptr;
     const int nq = norm ? nsq : 0;
-    float4 sa[NG], sb[NG];
+    float4 sq4[NQR][NG];
     {
         const float* sqp = norm ? SQ : XS;
         const int last = max(nq - 1, 0);
 #pragma unroll
-        for (int h = 0; h < NG; ++h) {
-            sa[h] = *reinterpret_cast<const float4*>(sqp + (size_t)min(r, last) * S + 16 * h + 4 * kg);
-            sb[h] = *reinterpret_cast<const float4*>(sqp + (size_t)min(r + 16, last) * S + 16 * h + 4 * kg);
-        }
+        for (int u = 0; u < NQR; ++u)
+#pragma unroll
+            for (int h = 0; h < NG; ++h)
+                sq4[u][h] = *reinterpret_cast<const float4*>(sqp + (size_t)min(r + 16 * u, last) * S + 16 * h + 4 * kg);
     }
     // x first (loads complete in order), then the scales, then every weight
     // load of the first stage; the next stage's weights are issued while the
@@ -635,9 +642,15 @@ k_gemv_batch_xp(const uint16_t* __restrict__ D, const uint8_t* __restrict__ Q,
         if (st == s0) {   // uniform
 #pragma unroll
             for (int h = 0; h < NG; ++h) {
-                const float ua = r < nq ? 1.f : 0.f, ub = r + 16 < nq ? 1.f : 0.f;
-                const float v[4] = {sa[h].x * ua + sb[h].x * ub, sa[h].y * ua + sb[h].y * ub,
-                                    sa[h].z * ua + sb[h].z * ub, sa[h].w * ua + sb[h].w * ub};
+                float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < NQR; ++u) {
+                    const float on = r + 16 * u < nq ? 1.f : 0.f;
+                    v[0] += sq4[u][h].x * on;
+                    v[1] += sq4[u][h].y * on;
+                    v[2] += sq4[u][h].z * on;
+                    v[3] += sq4[u][h].w * on;
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     rinv[h][i] = norm ? 1.0f / sqrtf(group_sum<16>(v[i]) / hn + eps) : 1.0f;

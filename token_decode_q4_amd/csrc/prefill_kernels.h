@@ -12,7 +12,7 @@
 
 namespace qd {
 
-constexpr int PF_NG = 2;          // 16-position groups per chunk
+constexpr int PF_NG = 4;          // 16-position groups per chunk
 constexpr int PF_T = 16 * PF_NG;   // positions per chunk
 
 // X[t][i] = dequant(E)[ids[p0 + t]][i]; grid (ceil(H/256), T)

@@ -528,11 +528,11 @@ static hipError_t xp_gemv(const DevQ4& W, const _Float16* XP, const float* XS, f
     const int N = W.rows, nb = W.nb;
     const int nch = gbm_nchunks(nb, NG);
     const int kch = (nch + ks - 1) / ks;
-    if (ks < 1 || (int64_t)(ks - 1) * kch >= nch || (rg != 1 && rg != 2) || nsq < 0 || nsq > 32)
-        return hipErrorInvalidValue;   // every slice holds a chunk; at most 32 chunk sums
+    if (ks < 1 || (int64_t)(ks - 1) * kch >= nch || (rg != 1 && rg != 2) || nsq < 0 || nsq > (NG == 4 ? 64 : 32))
+        return hipErrorInvalidValue;   // every slice holds a chunk; the chunk sums the product reads
     const bool dvec = nb % 8 == 0 && reinterpret_cast<uintptr_t>(W.d) % 16 == 0;
     const dim3 grid((N + gbm_rows(rg) - 1) / gbm_rows(rg), ks), block(GBM_NW * WAVE);
-    const size_t lds = gbm_xp_lds_bytes(), ys = (size_t)nv * N;
+    const size_t lds = gbm_xp_lds_bytes(gbm_xp_sub(NG)), ys = (size_t)nv * N;
     if (rg == 1 && dvec)
         hipLaunchKernelGGL((k_gemv_batch_xp<1, NG, 1>), grid, block, lds, s, W.d, W.qs, XP, XS, Y, N, nb, nv, kch, ys, SQ, nsq,
                            hn, eps);
@@ -566,7 +566,7 @@ static int enqueue_step_batch(qd_model* m, hipStream_t s)
 {
     const int B = m->B, H = m->H, I = m->I;
     const int nqd = m->nq * m->hd;
-    const dim3 ngrid(gbm_nchunks(H / 32, 1), B), nblock(4 * gbm_kcb(1));
+    const dim3 ngrid(gbm_nchunks(H / 32, 1), B), nblock(gbm_chunk_threads(1));
     hipLaunchKernelGGL(k_embed_xp_batch, ngrid, nblock, 0, s, m->embed.d, m->embed.qs, H, m->V, m->st, m->ids,
                        m->max_seq, m->layers[0].attn_norm, m->bx, 1, m->xp_h, m->xs_h, m->sq_h, m->rope_cos,
                        m->rope_sin, m->rot / 2, m->rope_cur, m->rstride);
@@ -1736,14 +1736,29 @@ static void pf_attention(qd_model* m, DevLayer& Ly, int p0, int T, hipStream_t s
     f.chunk = chunk;
     f.nsplit = nsplit;
     f.part = P.fa;
-    // a wave per 16 query rows (position, head) of the kv head's group
-    const dim3 grid(nsplit, m->nkv), block(gq * PF_NG * WAVE);
+    // a wave per 16 query rows (position, head) of the kv head's group, at
+    // most 16 waves: the chunk's positions in pieces of 256 / gq (a piece's
+    // splits past its last key return at once; every piece writes the
+    // partials of its own positions, under the one split geometry above)
+    const int tp = std::min(PF_T, 256 / gq);
+    const dim3 grid(nsplit, m->nkv);
+    const float* q0 = f.q;
+    float* part0 = f.part;
+#define QD_FA_GQ(HD_, GQ_)                                                                          \
+    hipLaunchKernelGGL((k_pf_attn<HD_, GQ_, GQ_ * (PF_T < 256 / GQ_ ? PF_T : 256 / GQ_) / 16>), grid, \
+                       dim3(GQ_ * (PF_T < 256 / GQ_ ? PF_T : 256 / GQ_) / 16 * WAVE), 0, s, f)
 #define QD_FA(HD_)                                                                                 \
-    switch (gq) {                                                                                  \
-    case 1: hipLaunchKernelGGL((k_pf_attn<HD_, 1, PF_NG>), grid, block, 0, s, f); break;           \
-    case 2: hipLaunchKernelGGL((k_pf_attn<HD_, 2, 2 * PF_NG>), grid, block, 0, s, f); break;       \
-    case 4: hipLaunchKernelGGL((k_pf_attn<HD_, 4, 4 * PF_NG>), grid, block, 0, s, f); break;       \
-    default: hipLaunchKernelGGL((k_pf_attn<HD_, 8, 8 * PF_NG>), grid, block, 0, s, f); break;      \
+    for (int t0 = 0; t0 < T; t0 += tp) {                                                           \
+        f.T = std::min(tp, T - t0);                                                                \
+        f.p0 = p0 + t0;                                                                            \
+        f.q = q0 + (size_t)t0 * m->nq * HD_;                                                       \
+        f.part = part0 + (size_t)t0 * m->nq * nsplit * (HD_ + 2);                                   \
+        switch (gq) {                                                                              \
+        case 1: QD_FA_GQ(HD_, 1); break;                                                           \
+        case 2: QD_FA_GQ(HD_, 2); break;                                                           \
+        case 4: QD_FA_GQ(HD_, 4); break;                                                           \
+        default: QD_FA_GQ(HD_, 8); break;                                                          \
+        }                                                                                          \
     }                                                                                              \
     hipLaunchKernelGGL((k_attn_combine<HD_>), dim3(m->nq, T), dim3(ATT_CNT), 0, s, P.fa, nsplit, chunk, \
                        P.lens, (const int32_t*)nullptr, m->max_seq, m->nq, P.O);
@@ -1753,6 +1768,7 @@ static void pf_attention(qd_model* m, DevLayer& Ly, int p0, int T, hipStream_t s
         QD_FA(64)
     }
 #undef QD_FA
+#undef QD_FA_GQ
 }
 
 static int pf_setup(qd_model* m)
@@ -1836,7 +1852,7 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
         const size_t slab_h = (size_t)T * H;
         hipLaunchKernelGGL(k_pf_embed, dim3((H + 255) / 256, T), dim3(256), 0, s, m->embed.d, m->embed.qs,
                            H, m->ids, p0, P.X);
-        const dim3 ngrid(gbm_nchunks(H / 32, PF_NG), T), nblock(4 * gbm_kcb(PF_NG));
+        const dim3 ngrid(gbm_nchunks(H / 32, PF_NG), T), nblock(gbm_chunk_threads(PF_NG));
         hipLaunchKernelGGL(k_resid_norm_xp_batch, ngrid, nblock, 0, s, P.X, nullptr, 0, (size_t)0, H,
                            m->layers[0].attn_norm, PF_NG, P.xp_h, P.xs_h, P.sq_h);
         for (int l = 0; l < m->L; ++l) {
@@ -1884,13 +1900,13 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
             }
             // the gate rows follow q|k|v in the fused product
             const float* gate = m->attn_gate ? P.QKV + (size_t)(m->nq + 2 * m->nkv) * hd : nullptr;
-            hipLaunchKernelGGL(k_xsplit_batch, dim3(gbm_nchunks(nqd / 32, PF_NG), T), dim3(4 * gbm_kcb(PF_NG)), 0,
+            hipLaunchKernelGGL(k_xsplit_batch, dim3(gbm_nchunks(nqd / 32, PF_NG), T), dim3(gbm_chunk_threads(PF_NG)), 0,
                                s, P.O, nqd / 32, PF_NG, P.xp_o, P.xs_o, gate, m->qkv_rows, P.ks_qkv, slab_qkv);
             HIP_TRY(pf_gemv(m, Ly.o, P.xp_o, P.xs_o, T, P.OD, P.ks_o, PF_RG_O, s));
             hipLaunchKernelGGL(k_resid_norm_xp_batch, ngrid, nblock, 0, s, P.X, P.OD, P.ks_o, slab_h, H,
                                Ly.ffn_norm, PF_NG, P.xp_h, P.xs_h, P.sq_h);
             HIP_TRY(pf_gemv(m, Ly.gu, P.xp_h, P.xs_h, T, P.GU, P.ks_gu, PF_RG_GU, s, P.sq_h));
-            hipLaunchKernelGGL(k_swiglu_xp_batch, dim3(gbm_nchunks(I / 32, PF_NG), T), dim3(4 * gbm_kcb(PF_NG)), 0,
+            hipLaunchKernelGGL(k_swiglu_xp_batch, dim3(gbm_nchunks(I / 32, PF_NG), T), dim3(gbm_chunk_threads(PF_NG)), 0,
                                s, P.GU, P.ks_gu, (size_t)T * 2 * I, I, PF_NG, P.xp_i, P.xs_i);
             HIP_TRY(pf_gemv(m, Ly.down, P.xp_i, P.xs_i, T, P.OD, P.ks_down, PF_RG_DOWN, s));
             // the residual, then the next layer's norm (split for its q|k|v), or

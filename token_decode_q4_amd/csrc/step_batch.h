@@ -224,7 +224,7 @@ QD_DEV void sb_norm_chunk(const float (&v)[8], const float (&wv)[8], int c, int 
     }
 }
 
-// grid (chunks of H, B), 4 KCB threads (KCB = 32 / ng): x[b] += y[b] (y may
+// grid (chunks of H, B), gbm_chunk_threads(ng) threads: x[b] += y[b] (y may
 // be null: no residual; y may come as nslab partial products slab floats
 // apart, added in slab order), then x[b] * w split for the product with the
 // chunk sums of x[b]^2 (sb_norm_chunk)
@@ -236,7 +236,7 @@ k_resid_norm_xp_batch(float* __restrict__ x, const float* __restrict__ y, int ns
     __shared__ float red_m[2], red_s[2];
     const int c = blockIdx.x, b = blockIdx.y;
     const int bl = threadIdx.x >> 2, kg = threadIdx.x & 3, blk = c * gbm_kcb(ng) + bl;
-    const bool in = blk < H / 32;
+    const bool in = bl < gbm_kcb(ng) && blk < H / 32;
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float wv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (in) {
@@ -272,7 +272,7 @@ k_resid_norm_xp_batch(float* __restrict__ x, const float* __restrict__ y, int ns
     sb_norm_chunk(v, wv, c, bl, kg, b, in, ng, XP, XS, SQ, red_m, red_s);
 }
 
-// grid (chunks of H, B), 4 KCB threads: sequence b at its position
+// grid (chunks of H, B), gbm_chunk_threads(ng) threads: sequence b at its position
 // st[b].pos reads its stored token and writes x[b] (the embedding row), the
 // split of x[b] * w with the chunk sums of x[b]^2 (as k_resid_norm_xp_batch)
 // and, in the chunk 0 workgroup, the rotary factors of its position (cos
@@ -307,7 +307,7 @@ k_embed_xp_batch(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq
     }
     const int nb = H / 32;
     const int bl = threadIdx.x >> 2, kg = threadIdx.x & 3, blk = c * gbm_kcb(ng) + bl;
-    const bool in = blk < nb;
+    const bool in = bl < gbm_kcb(ng) && blk < nb;
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float wv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (in) {
@@ -333,7 +333,8 @@ k_embed_xp_batch(const uint16_t* __restrict__ Ed, const uint8_t* __restrict__ Eq
     sb_norm_chunk(v, wv, c, bl, kg, b, in, ng, XP, XS, SQ, red_m, red_s);
 }
 
-// grid (chunks of I, B), 4 KCB threads (KCB = 32 / ng): a = silu(g) * up of
+// grid (chunks of I, B), gbm_chunk_threads(ng) threads (KCB = 32 / ng blocks
+// per chunk): a = silu(g) * up of
 // sequence b, chunk by chunk, split for the down product into XP / XS with
 // ng slot groups (gate and up rows
 // interleaved; gu as nslab partial products slab floats apart, added in slab
@@ -345,7 +346,7 @@ k_swiglu_xp_batch(const float* __restrict__ gu, int nslab, size_t slab, int I, i
     __shared__ float red[2];
     const int c = blockIdx.x, b = blockIdx.y;
     const int bl = threadIdx.x >> 2, kg = threadIdx.x & 3, blk = c * gbm_kcb(ng) + bl;
-    const bool in = blk < I / 32;
+    const bool in = bl < gbm_kcb(ng) && blk < I / 32;
     float e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (in) {
         const float2* g2 = reinterpret_cast<const float2*>(gu + (size_t)b * 2 * I);
