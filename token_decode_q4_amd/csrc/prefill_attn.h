@@ -6,10 +6,11 @@
 // of queries, K and V tiles staged once and shared, the causal mask inside
 // the tile; the online-softmax partials merged as in attn_reduce).
 //
-// Workgroup (split s, kv head g) owns keys [s*chunk, (s+1)*chunk) of that kv
-// head and every query row of its GQA group: T*GQ rows (t, j), row R = t*GQ
-// + j (head g*GQ + j), 16 rows per wave (wave w: rows 16w .. 16w+15), so
-// NWV = GQ * ceil(T / 16) waves.  Per 16-key step (one paged block) the K and
+// Workgroup (split s, kv head g, piece z) owns keys [s*chunk, (s+1)*chunk)
+// of that kv head and every query row of its GQA group for the piece's tp
+// positions: tp*GQ rows (t, j), row R = t*GQ + j (head g*GQ + j), 16 rows per
+// wave (wave w: rows 16w .. 16w+15), so NWV = GQ * tp / 16 waves.  A piece's
+// splits past its last key return at once.  Per 16-key step (one paged block) the K and
 // V tiles are loaded once into LDS and every wave uses them:
 //   S^T = K Q^T   v_mfma_f32_16x16x32_f16, M = the 16 keys, N = the wave's 16
 //                 query rows, K = 32 dims per instruction; q enters as an f16
@@ -47,11 +48,19 @@ struct FaParams {
     float scale;
     int chunk, nsplit;        // keys per split (a multiple of 16), splits
     float* part;              // [T][nq][nsplit][HD + 2]
+    int tp;                   // positions per workgroup (blockIdx.z: the piece)
 };
 
 template <int HD, int GQ, int NWV>
 __global__ void __launch_bounds__(NWV* WAVE) k_pf_attn(FaParams p)
 {
+    {   // this workgroup's piece of the chunk: positions z*tp .. z*tp+tp-1
+        const int z = blockIdx.z, t0 = z * p.tp;
+        p.p0 += t0;
+        p.q += (size_t)t0 * p.nq * HD;
+        p.part += (size_t)t0 * p.nq * p.nsplit * (HD + 2);
+        p.T = min(p.tp, p.T - t0);
+    }
     static_assert(NWV * WAVE <= 1024, "workgroup");
     constexpr int NI = HD / 32;     // 32-dim slices (QK)
     constexpr int NT = HD / 16;     // 16-dim tiles (PV)

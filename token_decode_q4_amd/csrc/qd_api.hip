@@ -1706,18 +1706,25 @@ extern "C" int qd_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink,
 // ------------------------------------------------------------------ chunked prefill
 
 // Chunk attention with each K/V tile read once for the chunk's queries
-// (k_pf_attn, f16 caches): about QD_PF_ATT_WGS workgroups over the keys
-// 0 .. p0+T-1, at most PF_FA_MAXS splits of a multiple of 16 keys, then the
-// combine.
+// (k_pf_attn, f16 caches): the chunk's positions in pieces of tp (a
+// workgroup's query rows, tp * gq <= QD_PF_ATT_ROWS), about QD_PF_ATT_WGS
+// workgroups over (key split, kv head, piece), at most PF_FA_MAXS splits of a
+// multiple of 16 keys, then the combine.
 #ifndef QD_PF_ATT_WGS
 #define QD_PF_ATT_WGS 256
 #endif
+#ifndef QD_PF_ATT_ROWS
+#define QD_PF_ATT_ROWS 128
+#endif
 constexpr int PF_FA_MAXS = 64;
+template <int GQ>
+constexpr int pf_att_tp() { return PF_T < QD_PF_ATT_ROWS / GQ ? PF_T : QD_PF_ATT_ROWS / GQ; }
 static void pf_attention(qd_model* m, DevLayer& Ly, int p0, int T, hipStream_t s)
 {
     auto& P = m->pf;
     const int kv_total = p0 + T, gq = m->nq / m->nkv;
-    const int target = std::max(1, QD_PF_ATT_WGS / m->nkv);
+    const int tp = std::min(PF_T, QD_PF_ATT_ROWS / gq), npiece = (T + tp - 1) / tp;
+    const int target = std::max(1, QD_PF_ATT_WGS / (m->nkv * npiece));
     int chunk = (kv_total + target - 1) / target;
     chunk = std::max(chunk, (kv_total + PF_FA_MAXS - 1) / PF_FA_MAXS);
     chunk = std::max(16, (chunk + 15) / 16 * 16);
@@ -1736,29 +1743,17 @@ static void pf_attention(qd_model* m, DevLayer& Ly, int p0, int T, hipStream_t s
     f.chunk = chunk;
     f.nsplit = nsplit;
     f.part = P.fa;
-    // a wave per 16 query rows (position, head) of the kv head's group, at
-    // most 16 waves: the chunk's positions in pieces of 256 / gq (a piece's
-    // splits past its last key return at once; every piece writes the
-    // partials of its own positions, under the one split geometry above)
-    const int tp = std::min(PF_T, 256 / gq);
-    const dim3 grid(nsplit, m->nkv);
-    const float* q0 = f.q;
-    float* part0 = f.part;
+    f.tp = tp;
+    const dim3 grid(nsplit, m->nkv, npiece);
 #define QD_FA_GQ(HD_, GQ_)                                                                          \
-    hipLaunchKernelGGL((k_pf_attn<HD_, GQ_, GQ_ * (PF_T < 256 / GQ_ ? PF_T : 256 / GQ_) / 16>), grid, \
-                       dim3(GQ_ * (PF_T < 256 / GQ_ ? PF_T : 256 / GQ_) / 16 * WAVE), 0, s, f)
+    hipLaunchKernelGGL((k_pf_attn<HD_, GQ_, GQ_ * pf_att_tp<GQ_>() / 16>), grid,                    \
+                       dim3(GQ_ * pf_att_tp<GQ_>() / 16 * WAVE), 0, s, f)
 #define QD_FA(HD_)                                                                                 \
-    for (int t0 = 0; t0 < T; t0 += tp) {                                                           \
-        f.T = std::min(tp, T - t0);                                                                \
-        f.p0 = p0 + t0;                                                                            \
-        f.q = q0 + (size_t)t0 * m->nq * HD_;                                                       \
-        f.part = part0 + (size_t)t0 * m->nq * nsplit * (HD_ + 2);                                   \
-        switch (gq) {                                                                              \
-        case 1: QD_FA_GQ(HD_, 1); break;                                                           \
-        case 2: QD_FA_GQ(HD_, 2); break;                                                           \
-        case 4: QD_FA_GQ(HD_, 4); break;                                                           \
-        default: QD_FA_GQ(HD_, 8); break;                                                          \
-        }                                                                                          \
+    switch (gq) {                                                                                  \
+    case 1: QD_FA_GQ(HD_, 1); break;                                                               \
+    case 2: QD_FA_GQ(HD_, 2); break;                                                               \
+    case 4: QD_FA_GQ(HD_, 4); break;                                                               \
+    default: QD_FA_GQ(HD_, 8); break;                                                              \
     }                                                                                              \
     hipLaunchKernelGGL((k_attn_combine<HD_>), dim3(m->nq, T), dim3(ATT_CNT), 0, s, P.fa, nsplit, chunk, \
                        P.lens, (const int32_t*)nullptr, m->max_seq, m->nq, P.O);
