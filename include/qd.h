@@ -174,7 +174,7 @@ int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* d_tokens,
 
 /* Chunked prompt prefill (inferencelayer cuda_llm.rs page: prefill as the
  * many-token form of the decode step, its q4 GEMV arm at M > 1): runs the
- * positions pos0 .. pos0+n-1 in chunks of up to qd_prefill_chunk() (32),
+ * positions pos0 .. pos0+n-1 in chunks of up to qd_prefill_chunk() (64),
  * each chunk one batched product per matrix (every weight read once per
  * chunk), with the tokens
  * stored by qd_set_prompt (or an earlier step).  It writes the K/V cache of
@@ -183,12 +183,12 @@ int qd_generate(qd_model* m, int32_t pos0, int32_t n_steps, int32_t* d_tokens,
  * logits as the prediction at p and, if p+1 is not forced, the token at
  * p+1.  d_logits_last (device f32 [vocab] or NULL) receives the logits at p.
  * Each position's values equal the decode step's up to f32 rounding order.
- * Continue with qd_generate(pos0 + n, ...).  Buffers (about 32 positions of
+ * Continue with qd_generate(pos0 + n, ...).  Buffers (about 64 positions of
  * activations plus an attention workspace) are allocated by the first call,
  * which synchronises; later calls allocate nothing.  The matrix products
  * are those of the batched decode step with the chunk's positions as its
  * vectors: each position's activations enter as an f16 pair (hi + lo, about
- * 22 significant bits) after scaling each 512-element chunk of the position's
+ * 22 significant bits) after scaling each 256-element chunk of the position's
  * vector by a power of two that puts its largest magnitude in [2^13, 2^14),
  * undone exactly in f32, so any finite activation scale is handled; the block
  * scales d and each position's 1/rms are applied in f32.  A model with attn_out_gate gates each
