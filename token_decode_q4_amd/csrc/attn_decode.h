@@ -22,7 +22,8 @@
 // workgroup's partial.  k_attn_combine (grid (nq, B)) merges a head's partials:
 //   M = max_s m_s,  out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s.
 //
-// In the decode step (QMODE 1) the split kernel also finishes the projection:
+// In the decode step (QMODE 1; QMODE 2 for B sequences whose raw q|k|v come
+// as K-slice partial products) the split kernel also finishes the projection:
 // from the raw q|k|v of the token it applies the per-head q/k RMSNorm and the
 // NeoX rotary at the position (ferrum-kernels cuda_decode.rs page, the q/k
 // norm then rope order of decode_step), and the wave whose keys hold the
@@ -53,7 +54,7 @@ struct AttnParams {
     float* out;                // [B][nq][HD] (combine)
     unsigned* counters;        // [B][nkv], zero between launches: when given, the last
                                // workgroup of each (b, g) merges the partials itself
-    // decode-step prologue (QMODE 1)
+    // decode-step prologue (QMODE 1 and 2)
     int qk_norm;               // 1: per-head RMSNorm of q and k
     const float* q_norm;       // [HD] (valid even when qk_norm is 0)
     const float* k_norm;
@@ -70,11 +71,11 @@ struct AttnParams {
     // 1: every sequence b reads the cache of sequence 0 (the B queries of a
     // prefill chunk over one cache, each with its own kv_len)
     int shared_kv;
-    // decode step of B sequences (QMODE 1): sequence b's raw q|k|v at
+    // decode step of B sequences (QMODE 1 and 2): sequence b's raw q|k|v at
     // q + b * q_stride, its position at pos[b * pos_stride], its rotary
-    // factors at rope_cur + b * rope_stride (all 0 for one sequence); the raw
-    // q|k|v may come as q_slabs partial products q_slab_stride floats apart,
-    // summed here in slab order (0 or 1: one)
+    // factors at rope_cur + b * rope_stride (all 0 for one sequence); with
+    // QMODE 2 the raw q|k|v come as q_slabs partial products q_slab_stride
+    // floats apart, summed here in slab order (QMODE 1: one, q_slabs unused)
     int q_stride, pos_stride, rope_stride;
     int q_slabs;
     size_t q_slab_stride;
@@ -258,7 +259,8 @@ QD_DEV void attn_merge_last(const AttnParams& p, int b, int g, int kv_len, int* 
 }
 
 // The work of one split workgroup: (split s, kv head g, sequence b).
-// QMODE 0: q given (standalone); QMODE 1: decode-step prologue from raw q|k|v.
+// QMODE 0: q given (standalone); QMODE 1: decode-step prologue from raw q|k|v;
+// QMODE 2: the same with q|k|v summed from q_slabs partial products.
 // FUSED: inside the persistent layer kernel.  wait() runs after the first
 // step's K/V loads are issued (they need nothing of this step) and before
 // anything of this step's q|k|v is read; q|k|v are read and the merged output
@@ -269,6 +271,8 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
     static_assert(HD == 64 || HD == 128, "head_dim");
     static_assert(!KV8 || !FUSED, "fp8 K/V: not in the persistent layer kernel");
     static_assert(GQ == 1 || GQ == 2 || GQ == 4 || GQ == 8, "group");
+    static_assert(QMODE >= 0 && QMODE <= 2, "query mode");
+    static_assert(QMODE != 2 || !FUSED, "q|k|v slabs: not in the persistent layer kernel");
     using Step = AttnStep<HD>;
     constexpr int NI = Step::NI, DPL = Step::DPL;
 
@@ -356,30 +360,71 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
     const int kv_raw = *kvp;
 
     // ---- loads that do not need kv_len: the token's q|k|v, norm weights,
-    // rotary factors, and (decode step) the first step's K/V
-    const float* qb = p.q + (size_t)b * p.q_stride;              // QMODE 1: this sequence's q|k|v
-    auto qkv_at = [&](size_t off) {                               // QMODE 1: summed over the slabs
-        float v = ld_f32<FUSED>(qb + off);
-        for (int sl = 1; sl < p.q_slabs; ++sl)
-            v += ld_f32<FUSED>(qb + sl * p.q_slab_stride + off);
-        return v;
+    // rotary factors, and (decode step) the first step's K/V.  Lane values
+    // raw[i][e] at dim lane*DPL + e: query heads h0 .. h0+GQ-1, then the kv
+    // head's k and v (QMODE >= 1).
+    constexpr int NE = GQ + 2;
+    const float* qb = p.q + (size_t)b * p.q_stride;              // QMODE >= 1: this sequence's q|k|v
+    auto qkv_off = [&](int i, int e) -> size_t {
+        const int row = i < GQ ? h0 + i : (i == GQ ? p.nq + g : p.nq + p.nkv + g);
+        return (size_t)row * HD + lane * DPL + e;
     };
-    const float* rc = p.rope_cur + (size_t)b * p.rope_stride;    // QMODE 1: its rotary factors
+    float raw[NE][DPL];
+    if (QMODE == 2) {
+        // q|k|v as q_slabs partial products, added in slab order.  Every load
+        // of a group of QSG slabs is issued before any is used (slab indexes
+        // clamped, never a branch): adding each slab as its load arrived would
+        // wait out one memory latency per slab.
+        constexpr int QSG = 4;
+        const int nsl = max(1, p.q_slabs);
+#pragma unroll
+        for (int i = 0; i < NE; ++i)
+#pragma unroll
+            for (int e = 0; e < DPL; ++e)
+                raw[i][e] = 0.f;
+        for (int s0 = 0; s0 < nsl; s0 += QSG) {
+            float t[QSG][NE][DPL];
+#pragma unroll
+            for (int u = 0; u < QSG; ++u) {
+                const float* src = qb + (size_t)min(s0 + u, nsl - 1) * p.q_slab_stride;
+#pragma unroll
+                for (int i = 0; i < NE; ++i)
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e)
+                        t[u][i][e] = ld_f32<FUSED>(src + qkv_off(i, e));
+            }
+#pragma unroll
+            for (int u = 0; u < QSG; ++u) {
+                const bool on = s0 + u < nsl;
+#pragma unroll
+                for (int i = 0; i < NE; ++i)
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e)
+                        raw[i][e] += on ? t[u][i][e] : 0.f;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NE; ++i)
+#pragma unroll
+            for (int e = 0; e < DPL; ++e)
+                raw[i][e] = (QMODE == 0) ? (i < GQ ? ld_f32<FUSED>(p.q + ((size_t)b * p.nq + h0 + i) * HD + lane * DPL + e) : 0.f)
+                                         : ld_f32<FUSED>(qb + qkv_off(i, e));
+    }
+    const float* rc = p.rope_cur + (size_t)b * p.rope_stride;    // QMODE >= 1: its rotary factors
     float qv[GQ][DPL], kv_[DPL], vv[DPL], wq[DPL], wk[DPL], cs[DPL], sn[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) {
         const int d = lane * DPL + e;
 #pragma unroll
         for (int j = 0; j < GQ; ++j)
-            qv[j][e] = (QMODE == 0) ? ld_f32<FUSED>(p.q + ((size_t)b * p.nq + h0 + j) * HD + d)
-                                    : qkv_at((size_t)(h0 + j) * HD + d);
-        kv_[e] = vv[e] = 0.f;
+            qv[j][e] = raw[j][e];
+        kv_[e] = raw[GQ][e];
+        vv[e] = raw[GQ + 1][e];
         wq[e] = wk[e] = cs[e] = 1.f;
         sn[e] = 0.f;
-        if (QMODE == 1) {
+        if (QMODE >= 1) {
             // q_norm / k_norm / rope_cur always point at valid arrays here
-            kv_[e] = qkv_at(((size_t)p.nq + g) * HD + d);
-            vv[e] = qkv_at(((size_t)p.nq + p.nkv + g) * HD + d);
             wq[e] = p.q_norm[d];
             wk[e] = p.k_norm[d];
             const int half = p.rot / 2;
@@ -392,10 +437,10 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
     if (!FUSED)
         load_step(cur_st, tw0);
 
-    // ---- queries (and the token's k): per-head RMSNorm and rotary (QMODE 1),
+    // ---- queries (and the token's k): per-head RMSNorm and rotary (QMODE >= 1),
     // times scale, into this wave's LDS rows.  None of it needs kv_len, so it
     // runs while the position is still in flight.
-    if (QMODE == 1) {
+    if (QMODE >= 1) {
         // no branch around the uses of the norm weights: a load used only in
         // a branch is sunk into it, behind the K/V loads, and then waits for them
         const bool qkn = p.qk_norm != 0;
@@ -471,7 +516,7 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
     const int tcur = kv_len - 1;
     float vnew[DPL];
     const int rel = tcur - t_begin;
-    const bool owner = QMODE == 1 && tcur >= t_begin && tcur < t_end && (rel / ATT_WK) % nw == w;
+    const bool owner = QMODE >= 1 && tcur >= t_begin && tcur < t_end && (rel / ATT_WK) % nw == w;
     const int own_tw = t_begin + (rel / ATT_WK) * ATT_WK;
     const int slot = tcur - own_tw;
     if (owner) {

@@ -53,12 +53,7 @@ k_pf_qk(const float* __restrict__ QKV, int qkv_rows, int nq, int nkv, const floa
     const bool is_q = hh < nq;
     const int g = hh - nq;
     // QKV may come as nslab partial products slab floats apart: added in slab order
-    auto ld = [&](const float* p) {
-        float a = p[0];
-        for (int k = 1; k < nslab; ++k)
-            a += p[k * slab];
-        return a;
-    };
+    auto ld = [&](const float* p) { return slab_sum<8>(p, nslab, slab); };
     const float* src = QKV + (size_t)t * qkv_rows + (size_t)(is_q ? hh : nq + g) * HD;
     const float* w = is_q ? q_norm : k_norm;
     float v[DPL];

@@ -607,9 +607,9 @@ static int enqueue_step_batch(qd_model* m, hipStream_t s)
         p.k_scale = m->k_scale;
         p.v_scale = m->v_scale;
         if (m->kv_fp8)
-            launch_attention<1, true>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, B, m->nq, s);
+            launch_attention<2, true>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, B, m->nq, s);
         else
-            launch_attention<1>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, B, m->nq, s);
+            launch_attention<2>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, B, m->nq, s);
         const size_t slab_h = (size_t)B * H;
         hipLaunchKernelGGL(k_xsplit_batch, dim3(gbm_nchunks(nqd / 32, 1), B), dim3(128), 0, s, m->battn,
                            nqd / 32, 1, m->xp_o, m->xs_o, nullptr, 0, 1, (size_t)0);

@@ -96,6 +96,32 @@ QD_DEV float group_max(float v)
     return v;
 }
 
+QD_DEV float slab_add(float a, float b) { return a + b; }
+QD_DEV float2 slab_add(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+QD_DEV float4 slab_add(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+
+// p[0] + p[stride] + .. + p[(n-1) stride], n >= 1 partial products (K
+// slices) of one value, added in that order.  The loads of each group of G
+// are all issued before any is used (indexes clamped, no branch around a
+// load): adding each term as its load arrived would wait out one memory
+// latency per term.
+template <int G, class T>
+QD_DEV T slab_sum(const T* p, int n, size_t stride)
+{
+    T r{};   // set by the first term
+    for (int k0 = 0; k0 < n; k0 += G) {
+        T t[G];
+#pragma unroll
+        for (int u = 0; u < G; ++u)
+            t[u] = p[(size_t)min(k0 + u, n - 1) * stride];
+#pragma unroll
+        for (int u = 0; u < G; ++u)
+            if (k0 + u < n)
+                r = (k0 + u == 0) ? t[0] : slab_add(r, t[u]);
+    }
+    return r;
+}
+
 // Timeline marks for profiling builds only: with QD_TIMELINE defined, thread 0
 // of every workgroup stores the 100 MHz real-time counter for mark k (0..7) at
 // qd_tl[8 * w + k], w = the linear workgroup index; the profiling host points

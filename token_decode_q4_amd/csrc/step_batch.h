@@ -248,14 +248,8 @@ k_resid_norm_xp_batch(float* __restrict__ x, const float* __restrict__ y, int ns
         const float4 wh = *reinterpret_cast<const float4*>(w + off + 16);
         if (y) {   // uniform
             const float* yb = y + (size_t)b * H + off;
-            float4 ra = *reinterpret_cast<const float4*>(yb);
-            float4 re = *reinterpret_cast<const float4*>(yb + 16);
-            for (int k = 1; k < nslab; ++k) {
-                const float4 pa = *reinterpret_cast<const float4*>(yb + k * slab);
-                const float4 pe = *reinterpret_cast<const float4*>(yb + k * slab + 16);
-                ra = make_float4(ra.x + pa.x, ra.y + pa.y, ra.z + pa.z, ra.w + pa.w);
-                re = make_float4(re.x + pe.x, re.y + pe.y, re.z + pe.z, re.w + pe.w);
-            }
+            const float4 ra = slab_sum<SB_MAXSLAB>(reinterpret_cast<const float4*>(yb), nslab, slab / 4);
+            const float4 re = slab_sum<SB_MAXSLAB>(reinterpret_cast<const float4*>(yb + 16), nslab, slab / 4);
             a = make_float4(a.x + ra.x, a.y + ra.y, a.z + ra.z, a.w + ra.w);
             e = make_float4(e.x + re.x, e.y + re.y, e.z + re.z, e.w + re.w);
             *reinterpret_cast<float4*>(xb) = a;
@@ -354,12 +348,7 @@ k_swiglu_xp_batch(const float* __restrict__ gu, int nslab, size_t slab, int I, i
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int i = blk * 32 + 4 * kg + (q < 4 ? q : 12 + q);
-            float2 v = g2[i];
-            for (int k = 1; k < nslab; ++k) {
-                const float2 u = reinterpret_cast<const float2*>(gu + k * slab + (size_t)b * 2 * I)[i];
-                v.x += u.x;
-                v.y += u.y;
-            }
+            const float2 v = slab_sum<4>(g2 + i, nslab, slab / 2);
             a[q] = v.x * __builtin_amdgcn_rcpf(1.0f + __expf(-v.x)) * v.y;
         }
         e[0] = a[0];
