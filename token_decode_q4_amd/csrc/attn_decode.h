@@ -34,6 +34,7 @@
 #pragma once
 
 #include "qd_common.h"
+#include "gemv_batch_mfma.h"
 
 namespace qd {
 
@@ -79,6 +80,14 @@ struct AttnParams {
     int q_stride, pos_stride, rope_stride;
     int q_slabs;
     size_t q_slab_stride;
+    // QMODE 2 with counters: when xp is given, the merge writes sequence b's
+    // output as the o product's split input instead of out: chunk c of 1024
+    // elements (the kv heads whose query heads it holds) is merged by the
+    // last workgroup of those kv heads to finish, which writes its f16 pairs
+    // to xp and 1/scale to xs[c * 16 + b] (the layout of k_xsplit_batch with
+    // one slot group); counters are then per (b, chunk)
+    _Float16* xp;
+    float* xs;
 };
 
 constexpr int ATT_WK = 16;                 // keys per wave step (one paged block)
@@ -179,7 +188,7 @@ struct AttnStep {
 // of a round are issued before any is used (indexes clamped, never a branch).
 // Agent-scope loads: the partials come from other workgroups of this launch.
 template <int HD, int GQ, int U, bool COH>
-QD_DEV void attn_merge_heads(const AttnParams& p, int b, int g, int nact)
+QD_DEV void attn_merge_heads(const AttnParams& p, int b, int g, int nact, float* lds_out = nullptr)
 {
     static_assert(U <= WAVE, "one split per lane");
     const size_t pstride = HD + 2;
@@ -214,6 +223,10 @@ QD_DEV void attn_merge_heads(const AttnParams& p, int b, int g, int nact)
             mt = rm;
         }
         float o = (den > 0.f) ? num / den : 0.f;
+        if (lds_out) {   // uniform
+            lds_out[i] = o;
+            continue;
+        }
         if (p.gate)   // uniform
             o *= 1.0f / (1.0f + expf(-ld_f32<COH>(p.gate + (size_t)h * HD + d)));
         st_f32<COH>(p.out + ((size_t)b * p.nq + h) * HD + d, o);
@@ -256,6 +269,160 @@ QD_DEV void attn_merge_last(const AttnParams& p, int b, int g, int kv_len, int* 
         attn_merge_heads<HD, GQ, 32, COH>(p, b, g, nact);
     if (threadIdx.x == 0)
         __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The merge as attn_merge_last, per chunk c of 1024 output elements of
+// sequence b (KPC = 1024 / (GQ HD) kv heads, fewer in a ragged last chunk):
+// the last of the chunk's workgroups to finish merges every head of the chunk
+// into LDS (buf: 1024 floats) and writes the chunk as the o product's split
+// input, as k_xsplit_batch does: one item (block, lane group) of 8 elements
+// per thread, the power of two that puts the chunk's largest |x| in
+// [2^13, 2^14), the f16 pair of each element, 1/scale in xs.
+// The merge of attn_merge_heads for n consecutive output elements of
+// sequence b starting at kv head g0's first query head, EPT elements per
+// thread (i = threadIdx.x + r * blockDim.x, n <= EPT * blockDim.x), into
+// out[i]: every load of a round of U splits is issued for all of a thread's
+// elements before any is used, so the merge costs one memory latency per
+// round whatever EPT is.  Indexes past n are clamped (their results dropped).
+template <int HD, int GQ, int U, int EPT>
+QD_DEV void attn_merge_rows(const AttnParams& p, int b, int g0, int n, int nact, float* out)
+{
+    static_assert(U <= WAVE, "one split per lane");
+    const size_t pstride = HD + 2;
+    const int lane = threadIdx.x & (WAVE - 1);
+    float mt[EPT], num[EPT], den[EPT];
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) {
+        mt[r] = -INFINITY;
+        num[r] = den[r] = 0.f;
+    }
+    for (int s0 = 0; s0 < nact; s0 += U) {
+        uint64_t ml[EPT];
+        float a[EPT][U];
+#pragma unroll
+        for (int r = 0; r < EPT; ++r) {
+            // a wave's 64 elements lie in one head (HD and blockDim.x multiples of 64)
+            const int i = min((int)threadIdx.x + r * (int)blockDim.x, n - 1);
+            const float* pp = p.part + ((size_t)b * p.nq + g0 * GQ + i / HD) * p.nsplit * pstride;
+            const int sl = min(s0 + lane, nact - 1);
+            ml[r] = __hip_atomic_load(reinterpret_cast<const uint64_t*>(pp + sl * pstride + HD), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                a[r][u] = __hip_atomic_load(pp + (size_t)min(s0 + u, nact - 1) * pstride + i % HD, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int r = 0; r < EPT; ++r) {
+            const bool act = s0 + lane < nact;
+            const float m = act ? __uint_as_float((uint32_t)ml[r]) : -INFINITY;
+            const float l = act ? __uint_as_float((uint32_t)(ml[r] >> 32)) : 0.f;
+            const float rm = fmaxf(mt[r], group_max<WAVE>(m));
+            const float sc = (mt[r] == -INFINITY) ? 0.f : expf(mt[r] - rm);
+            const float f = (m == -INFINITY) ? 0.f : expf(m - rm);
+            den[r] = fmaf(den[r], sc, group_sum<WAVE>(f * l));
+            num[r] *= sc;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (s0 + u < nact)   // uniform
+                    num[r] = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), u)), a[r][u], num[r]);
+            mt[r] = rm;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < EPT; ++r) {
+        const int i = threadIdx.x + r * blockDim.x;
+        if (i < n)
+            out[i] = (den[r] > 0.f) ? num[r] / den[r] : 0.f;
+    }
+}
+
+// the chunk merge needs 1024 floats of LDS, taken from the workgroup's acc
+// rows, and one float per wave (m rows)
+__host__ __device__ constexpr bool attn_split_out_ok(int hd, int gq)
+{
+    return (gq <= 4 ? 8 : 4) * gq * hd >= 1024 && 1024 % (gq * hd) == 0;
+}
+
+template <int HD, int GQ>
+QD_DEV void attn_merge_split(const AttnParams& p, int b, int g, int kv_len, int* last, float* buf, float* red)
+{
+    constexpr int KPC = 1024 / (GQ * HD);
+    static_assert(attn_split_out_ok(HD, GQ) && AttnMaxWaves<GQ>::value == (GQ <= 4 ? 8 : 4),
+                  "a kv head inside one chunk, 1024 floats of acc rows");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's partial stores are done
+    __syncthreads();
+    const int nact = (kv_len + p.chunk - 1) / p.chunk;
+    const int c = g / KPC, g0 = c * KPC, nkc = min(KPC, p.nkv - g0);
+    const int nchunk = (p.nkv + KPC - 1) / KPC;
+    unsigned* cnt = p.counters + (size_t)b * nchunk + c;
+    if (threadIdx.x == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *last = (prev + 1 == (unsigned)(nact * nkc));
+    }
+    __syncthreads();
+    if (!*last)
+        return;
+    const int n = nkc * GQ * HD, ept = (n + (int)blockDim.x - 1) / (int)blockDim.x;
+    if (ept <= 2 && nact <= 8)
+        attn_merge_rows<HD, GQ, 8, 2>(p, b, g0, n, nact, buf);
+    else if (ept <= 2)
+        attn_merge_rows<HD, GQ, 32, 2>(p, b, g0, n, nact, buf);
+    else if (ept <= 4 && nact <= 8)
+        attn_merge_rows<HD, GQ, 8, 4>(p, b, g0, n, nact, buf);
+    else if (ept <= 4)
+        attn_merge_rows<HD, GQ, 32, 4>(p, b, g0, n, nact, buf);
+    else   // small workgroups: kv head by kv head
+        for (int k = 0; k < nkc; ++k) {
+            float* dst = buf + k * GQ * HD;
+            if (nact <= 8)
+                attn_merge_heads<HD, GQ, 8, false>(p, b, g0 + k, nact, dst);
+            else if (nact <= 16)
+                attn_merge_heads<HD, GQ, 16, false>(p, b, g0 + k, nact, dst);
+            else
+                attn_merge_heads<HD, GQ, 32, false>(p, b, g0 + k, nact, dst);
+        }
+    __syncthreads();
+    // the chunk's 128 items (block bl = it / 4, lane group kg = it % 4): item
+    // t and t + blockDim.x of thread t (blockDim.x >= 64)
+    const int nb = p.nq * HD / 32, nw = blockDim.x / WAVE;
+    float e[2][8];
+    float m = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int it = threadIdx.x + u * blockDim.x;
+        const bool in = it < 128 && c * 32 + (it >> 2) < nb;
+        const float* x = buf + min(it >> 2, 31) * 32 + 4 * (it & 3);
+        // slot order of a lane group: 4kg, 4kg+2, 4kg+1, 4kg+3, then the same
+        // four plus 16, divided by 16 (exact)
+        e[u][0] = in ? x[0] : 0.f;
+        e[u][1] = in ? x[2] : 0.f;
+        e[u][2] = in ? x[1] : 0.f;
+        e[u][3] = in ? x[3] : 0.f;
+        e[u][4] = in ? x[16] * 0.0625f : 0.f;
+        e[u][5] = in ? x[18] * 0.0625f : 0.f;
+        e[u][6] = in ? x[17] * 0.0625f : 0.f;
+        e[u][7] = in ? x[19] * 0.0625f : 0.f;
+        m = fmaxf(m, gbm_xp_absmax(e[u]));
+    }
+    m = group_max<WAVE>(m);
+    if ((threadIdx.x & (WAVE - 1)) == 0)
+        red[threadIdx.x / WAVE] = m;
+    __syncthreads();
+    float cm = red[0];
+    for (int u = 1; u < nw; ++u)
+        cm = fmaxf(cm, red[u]);
+    const float sc = gbm_scale_for(cm);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int it = threadIdx.x + u * blockDim.x;
+        if (it < 128 && c * 32 + (it >> 2) < nb)
+            gbm_xp_put(p.xp, 1, c, it >> 2, it & 3, b, e[u], sc);
+    }
+    if (threadIdx.x == 0) {
+        p.xs[c * 16 + b] = 1.0f / sc;
+        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // The work of one split workgroup: (split s, kv head g, sequence b).
@@ -770,6 +937,14 @@ QD_DEV void attn_split_body(const AttnParams& p, int s, int g, int b, AttnSmem<H
                 pp[HD] = M;
                 pp[HD + 1] = L;
             }
+        }
+    }
+    if constexpr (QMODE == 2 && attn_split_out_ok(HD, GQ)) {
+        if (merge_here && p.xp) {   // uniform
+            // the LDS rows of acc and m were all read above, before the partial stores
+            attn_merge_split<HD, GQ>(p, b, g, kv_len, &sm.last, &sm.acc[0][0][0], &sm.m[0][0]);
+            QD_MARK(3);
+            return;
         }
     }
     if (merge_here)

@@ -100,6 +100,10 @@ static hipError_t launch_gemv_batch_mfma(const uint16_t* d, const uint8_t* q, co
 #ifndef QD_ATT_BATCH_WGS
 #define QD_ATT_BATCH_WGS 256
 #endif
+// sequences from which a batched step's attention writes the o product's split
+// input itself (Qwen3-8B shape, one box: 2.94 -> 2.88 ms per step at 8, 3.10
+// -> 3.06 at 16, 2.797 -> 2.813 at 4)
+static constexpr int ATT_SPLIT_OUT_MIN_B = 8;
 
 // ------------------------------------------------------------------ model
 
@@ -606,13 +610,21 @@ static int enqueue_step_batch(qd_model* m, hipStream_t s)
         p.vc = Ly.vc;
         p.k_scale = m->k_scale;
         p.v_scale = m->v_scale;
+        // from 8 sequences the attention's merge writes the o product's split
+        // input itself (per 1024-element chunk; where its LDS allows): one
+        // launch less per layer.  With fewer sequences each chunk's merge
+        // waits for more split workgroups than the separate split costs.
+        const bool split_out = B >= ATT_SPLIT_OUT_MIN_B && attn_split_out_ok(m->hd, m->nq / m->nkv);
+        p.xp = split_out ? m->xp_o : nullptr;
+        p.xs = split_out ? m->xs_o : nullptr;
         if (m->kv_fp8)
             launch_attention<2, true>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, B, m->nq, s);
         else
             launch_attention<2>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, B, m->nq, s);
         const size_t slab_h = (size_t)B * H;
-        hipLaunchKernelGGL(k_xsplit_batch, dim3(gbm_nchunks(nqd / 32, 1), B), dim3(128), 0, s, m->battn,
-                           nqd / 32, 1, m->xp_o, m->xs_o, nullptr, 0, 1, (size_t)0);
+        if (!split_out)
+            hipLaunchKernelGGL(k_xsplit_batch, dim3(gbm_nchunks(nqd / 32, 1), B), dim3(128), 0, s, m->battn,
+                               nqd / 32, 1, m->xp_o, m->xs_o, nullptr, 0, 1, (size_t)0);
         HIP_TRY(step_gemv(m, Ly.o, m->xp_o, m->xs_o, m->bo, m->ks_o, STEP_RG_O, s));
         hipLaunchKernelGGL(k_resid_norm_xp_batch, ngrid, nblock, 0, s, m->bx, m->bo, m->ks_o, slab_h, H,
                            Ly.ffn_norm, 1, m->xp_h, m->xs_h, m->sq_h);
