@@ -228,4 +228,115 @@ __global__ void __launch_bounds__(NWV* WAVE) k_pf_attn(FaParams p)
     }
 }
 
+// The split merge of a prefill chunk written straight as the o product's
+// input: grid (chunks of 256 output elements, T positions), 512 threads
+// (element i = tid % 256 of the chunk, split group tid / 256).  Each group
+// merges splits sg, sg + 2, .. with every load of a round of U issued first
+// (U * 2 >= nsplit on the host, so one round); the two groups are merged in
+// LDS (M = max m_s, out = sum e^(m_s - M) acc_s / sum e^(m_s - M) l_s, as
+// k_attn_combine), the output multiplied by sigmoid(gate) for a model with
+// the attention output gate (gate rows of position t at gate + t * gstride,
+// as ngslab partial products gslab floats apart), then split as
+// k_xsplit_batch does with four slot groups: the chunk's largest |x| sets its
+// power of two, position t is slot t.
+constexpr int FA_CMB_THREADS = 512;
+template <int HD, int U>
+__global__ void __launch_bounds__(FA_CMB_THREADS)
+k_attn_combine_xp(const float* __restrict__ part, int nsplit, int chunk, const int32_t* __restrict__ kv_lens,
+                  int max_kv, int nq, _Float16* __restrict__ XP, float* __restrict__ XS,
+                  const float* __restrict__ gate, int gstride, int ngslab, size_t gslab)
+{
+    constexpr int NG = 4, CE = 32 * gbm_kcb(NG), SG = FA_CMB_THREADS / CE;   // 256 elements, 2 groups
+    __shared__ float gm[SG][CE], gn[SG][CE], gd[SG][CE];
+    const int c = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+    const int i = tid % CE, sg = tid / CE;
+    const int n = nq * HD, e = min(c * CE + i, n - 1);   // clamped: the results past n are dropped
+    const int h = e / HD, d = e % HD;
+    const size_t pstride = HD + 2;
+    const float* pp = part + ((size_t)t * nq + h) * nsplit * pstride;
+    int kv_len = kv_lens[t];
+    kv_len = max(0, min(kv_len, max_kv));
+    const int nact = min(nsplit, (kv_len + chunk - 1) / chunk);
+    float mt = -INFINITY, num = 0.f, den = 0.f;
+    for (int s0 = sg; s0 < nsplit; s0 += U * SG) {
+        float a[U], mm[U], ll[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t sp = (size_t)min(s0 + u * SG, nsplit - 1) * pstride;   // never a branch
+            a[u] = pp[sp + d];
+            mm[u] = pp[sp + HD];
+            ll[u] = pp[sp + HD + 1];
+        }
+        float rm = mt;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (s0 + u * SG < nact)
+                rm = fmaxf(rm, mm[u]);
+        if (rm == -INFINITY)
+            continue;
+        const float sc = (mt == -INFINITY) ? 0.f : expf(mt - rm);
+        num *= sc;
+        den *= sc;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (s0 + u * SG < nact) {
+                const float f = expf(mm[u] - rm);
+                num = fmaf(f, a[u], num);
+                den = fmaf(f, ll[u], den);
+            }
+        }
+        mt = rm;
+    }
+    gm[sg][i] = mt;
+    gn[sg][i] = num;
+    gd[sg][i] = den;
+    __syncthreads();
+    if (sg == 0) {
+        float M = gm[0][i];
+#pragma unroll
+        for (int k = 1; k < SG; ++k)
+            M = fmaxf(M, gm[k][i]);
+        float N = 0.f, D = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int k = 0; k < SG; ++k) {
+                const float f = (gm[k][i] == -INFINITY) ? 0.f : expf(gm[k][i] - M);
+                N = fmaf(f, gn[k][i], N);
+                D = fmaf(f, gd[k][i], D);
+            }
+        }
+        float o = (D > 0.f) ? N / D : 0.f;
+        if (gate) {   // uniform
+            const float g = slab_sum<4>(gate + (size_t)t * gstride + e, ngslab, gslab);
+            o *= 1.0f / (1.0f + expf(-g));
+        }
+        gm[1][i] = o;   // the merged chunk, read below by the split items
+    }
+    __syncthreads();
+    // the chunk's 32 items (block bl = tid / 4, lane group kg = tid % 4): wave 0
+    if (tid < WAVE) {
+        const int bl = tid >> 2, kg = tid & 3;
+        const bool in = tid < 4 * gbm_kcb(NG) && (c * CE + bl * 32) < n;
+        float ev[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (in) {
+            const float* x = &gm[1][bl * 32 + 4 * kg];
+            // slot order of a lane group: 4kg, 4kg+2, 4kg+1, 4kg+3, then the
+            // same four plus 16, divided by 16 (exact)
+            ev[0] = x[0];
+            ev[1] = x[2];
+            ev[2] = x[1];
+            ev[3] = x[3];
+            ev[4] = x[16] * 0.0625f;
+            ev[5] = x[18] * 0.0625f;
+            ev[6] = x[17] * 0.0625f;
+            ev[7] = x[19] * 0.0625f;
+        }
+        const float sc = gbm_scale_for(group_max<WAVE>(gbm_xp_absmax(ev)));
+        if (in)
+            gbm_xp_put(XP, NG, c, bl, kg, t, ev, sc);
+        if (tid == 0)
+            XS[c * 16 * NG + t] = 1.0f / sc;
+    }
+}
+
 }  // namespace qd

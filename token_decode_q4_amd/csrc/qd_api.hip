@@ -1731,7 +1731,34 @@ extern "C" int qd_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink,
 constexpr int PF_FA_MAXS = 64;
 template <int GQ>
 constexpr int pf_att_tp() { return PF_T < QD_PF_ATT_ROWS / GQ ? PF_T : QD_PF_ATT_ROWS / GQ; }
-static void pf_attention(qd_model* m, DevLayer& Ly, int p0, int T, hipStream_t s)
+// the split merge of the prefill's chunk attention, one round of loads per
+// split group (U * 2 >= nsplit splits)
+template <int HD>
+static void pf_combine_xp(qd_model* m, int nsplit, int chunk, int T, const float* gate, size_t gslab,
+                          hipStream_t s)
+{
+    auto& P = m->pf;
+    const dim3 grid(gbm_nchunks(m->nq * HD / 32, PF_NG), T), block(FA_CMB_THREADS);
+    const int half = (nsplit + 1) / 2;
+#define QD_CMB(U_)                                                                                  \
+    hipLaunchKernelGGL((k_attn_combine_xp<HD, U_>), grid, block, 0, s, P.fa, nsplit, chunk, P.lens,  \
+                       m->max_seq, m->nq, P.xp_o, P.xs_o, gate, m->qkv_rows, P.ks_qkv, gslab)
+    if (half <= 2)
+        QD_CMB(2);
+    else if (half <= 4)
+        QD_CMB(4);
+    else if (half <= 8)
+        QD_CMB(8);
+    else if (half <= 16)
+        QD_CMB(16);
+    else
+        QD_CMB(32);
+#undef QD_CMB
+}
+
+// the prefill's chunk attention (f16 cache), its split merge writing the o
+// product's input (P.xp_o, P.xs_o; times sigmoid(gate) when gate is given)
+static void pf_attention(qd_model* m, DevLayer& Ly, int p0, int T, const float* gate, size_t gslab, hipStream_t s)
 {
     auto& P = m->pf;
     const int kv_total = p0 + T, gq = m->nq / m->nkv;
@@ -1767,8 +1794,7 @@ static void pf_attention(qd_model* m, DevLayer& Ly, int p0, int T, hipStream_t s
     case 4: QD_FA_GQ(HD_, 4); break;                                                               \
     default: QD_FA_GQ(HD_, 8); break;                                                              \
     }                                                                                              \
-    hipLaunchKernelGGL((k_attn_combine<HD_>), dim3(m->nq, T), dim3(ATT_CNT), 0, s, P.fa, nsplit, chunk, \
-                       P.lens, (const int32_t*)nullptr, m->max_seq, m->nq, P.O);
+    pf_combine_xp<HD_>(m, nsplit, chunk, T, gate, gslab, s);
     if (m->hd == 128) {
         QD_FA(128)
     } else {
@@ -1902,13 +1928,15 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
                 p.v_scale = m->v_scale;
                 p.shared_kv = 1;
                 launch_attention<0, true>(p, P.geo.waves, hd, gq, m->paged, T, m->nq, s);
-            } else {
-                pf_attention(m, Ly, p0, T, s);
             }
             // the gate rows follow q|k|v in the fused product
             const float* gate = m->attn_gate ? P.QKV + (size_t)(m->nq + 2 * m->nkv) * hd : nullptr;
-            hipLaunchKernelGGL(k_xsplit_batch, dim3(gbm_nchunks(nqd / 32, PF_NG), T), dim3(gbm_chunk_threads(PF_NG)), 0,
-                               s, P.O, nqd / 32, PF_NG, P.xp_o, P.xs_o, gate, m->qkv_rows, P.ks_qkv, slab_qkv);
+            if (m->kv_fp8)
+                hipLaunchKernelGGL(k_xsplit_batch, dim3(gbm_nchunks(nqd / 32, PF_NG), T),
+                                   dim3(gbm_chunk_threads(PF_NG)), 0, s, P.O, nqd / 32, PF_NG, P.xp_o, P.xs_o, gate,
+                                   m->qkv_rows, P.ks_qkv, slab_qkv);
+            else
+                pf_attention(m, Ly, p0, T, gate, slab_qkv, s);   // writes the split itself
             HIP_TRY(pf_gemv(m, Ly.o, P.xp_o, P.xs_o, T, P.OD, P.ks_o, PF_RG_O, s));
             hipLaunchKernelGGL(k_resid_norm_xp_batch, ngrid, nblock, 0, s, P.X, P.OD, P.ks_o, slab_h, H,
                                Ly.ffn_norm, PF_NG, P.xp_h, P.xs_h, P.sq_h);
