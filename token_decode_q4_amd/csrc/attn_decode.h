@@ -964,10 +964,11 @@ constexpr int ATT_CNT = 512;   // combine threads per head
 
 // Merge the partials of one (sequence, head): grid (nq, B), 512 threads in
 // groups of HD; group sg takes splits sg, sg + SG, ...  Each round issues all
-// of its loads (acc, m, l of up to 16 splits) before using them; only splits
-// holding keys below kv_len count.  The groups' (max, numerator, denominator)
+// of its loads (acc, m, l of U splits, U * SG >= the split count on the host
+// so that one round does, and no more loads than the splits need) before
+// using them; only splits holding keys below kv_len count.  The groups' (max, numerator, denominator)
 // are merged through LDS in a fixed order.
-template <int HD>
+template <int HD, int U = 16>
 __global__ void __launch_bounds__(ATT_CNT) k_attn_combine(const float* __restrict__ part,
                                                           int nsplit_all, int chunk,
                                                           const int32_t* __restrict__ kv_lens,
@@ -975,7 +976,6 @@ __global__ void __launch_bounds__(ATT_CNT) k_attn_combine(const float* __restric
                                                           int max_kv, int nq, float* __restrict__ out)
 {
     constexpr int SG = ATT_CNT / HD;
-    constexpr int U = 16;
     __shared__ float gm[SG][HD], gn[SG][HD], gd[SG][HD];
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int d = tid % HD, sg = tid / HD;

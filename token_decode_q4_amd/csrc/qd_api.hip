@@ -439,12 +439,19 @@ static void launch_attention(const AttnParams& p, int waves, int hd, int gq, boo
 #undef QD_ATT
     if (p.counters)
         return;   // the split kernel merged the partials itself
-    if (hd == 128)
-        hipLaunchKernelGGL((k_attn_combine<128>), dim3(nq, B), dim3(ATT_CNT), 0, s, p.part,
-                           p.nsplit, p.chunk, p.kv_lens, p.pos, p.max_kv, nq, p.out);
-    else
-        hipLaunchKernelGGL((k_attn_combine<64>), dim3(nq, B), dim3(ATT_CNT), 0, s, p.part,
-                           p.nsplit, p.chunk, p.kv_lens, p.pos, p.max_kv, nq, p.out);
+    // one round of loads: U splits per group of HD threads, U * (ATT_CNT / HD) >= nsplit
+    const int per = (p.nsplit + ATT_CNT / hd - 1) / (ATT_CNT / hd);
+#define QD_CMB(HD_, U_)                                                                             \
+    hipLaunchKernelGGL((k_attn_combine<HD_, U_>), dim3(nq, B), dim3(ATT_CNT), 0, s, p.part, p.nsplit, \
+                       p.chunk, p.kv_lens, p.pos, p.max_kv, nq, p.out)
+    if (hd == 128) {
+        if (per <= 2) QD_CMB(128, 2); else if (per <= 4) QD_CMB(128, 4); else if (per <= 8) QD_CMB(128, 8);
+        else QD_CMB(128, 16);
+    } else {
+        if (per <= 2) QD_CMB(64, 2); else if (per <= 4) QD_CMB(64, 4); else if (per <= 8) QD_CMB(64, 8);
+        else QD_CMB(64, 16);
+    }
+#undef QD_CMB
 }
 
 // Enqueue one decode step (position and token come from the device state).
