@@ -514,12 +514,21 @@ constexpr int STEP_RG_QKV = 1, STEP_RG_O = 1, STEP_RG_GU = 1, STEP_RG_DOWN = 1, 
 constexpr int PF_RG_QKV = 2, PF_RG_O = 1, PF_RG_GU = 2, PF_RG_DOWN = 2;
 
 // K slices of a split-input product: about 768 workgroups, at most one per
-// chunk and SB_MAXSLAB in all
-static int step_kslices(int N, int nb, int ng, int rg)
+// chunk and SB_MAXSLAB in all (Qwen3-8B shape, one box: prefill 11 988
+// positions/s against 11 659 and 11 414 with 384 and 512 (gate|up in 2 and 3
+// slices instead of 4); the 16-sequence step 3.08 ms against 3.30 with 512
+// (gate|up 1 slice, down 6))
+#ifndef QD_STEP_KS_WGS
+#define QD_STEP_KS_WGS 768
+#endif
+#ifndef QD_PF_KS_WGS
+#define QD_PF_KS_WGS 768
+#endif
+static int step_kslices(int N, int nb, int ng, int rg, int target = 768)
 {
     const int tiles = (N + gbm_rows(rg) - 1) / gbm_rows(rg);
     const int nch = gbm_nchunks(nb, ng);
-    int ks = std::min({nch, SB_MAXSLAB, std::max(1, (768 + tiles / 2) / tiles)});
+    int ks = std::min({nch, SB_MAXSLAB, std::max(1, (target + tiles / 2) / tiles)});
     if (ks > 1) {
         const int kch = (nch + ks - 1) / ks;
         ks = (nch + kch - 1) / kch;
@@ -994,10 +1003,10 @@ static int create_model(const qd_config* cfg, const qd_weights* w, int B, qd_str
     if (B > 1) {
         m->bchunk = 4096;
         m->bG = (m->V + m->bchunk - 1) / m->bchunk;
-        m->ks_qkv = step_kslices(m->qkv_rows, H / 32, 1, STEP_RG_QKV);
-        m->ks_o = step_kslices(H, nqd / 32, 1, STEP_RG_O);
-        m->ks_gu = step_kslices(2 * m->I, H / 32, 1, STEP_RG_GU);
-        m->ks_down = step_kslices(H, m->I / 32, 1, STEP_RG_DOWN);
+        m->ks_qkv = step_kslices(m->qkv_rows, H / 32, 1, STEP_RG_QKV, QD_STEP_KS_WGS);
+        m->ks_o = step_kslices(H, nqd / 32, 1, STEP_RG_O, QD_STEP_KS_WGS);
+        m->ks_gu = step_kslices(2 * m->I, H / 32, 1, STEP_RG_GU, QD_STEP_KS_WGS);
+        m->ks_down = step_kslices(H, m->I / 32, 1, STEP_RG_DOWN, QD_STEP_KS_WGS);
         const size_t Bz = B;
         if ((rc = dev_alloc_t(m, &m->bx, Bz * H)) || (rc = dev_alloc_t(m, &m->bh, Bz * H)) ||
             (rc = dev_alloc_t(m, &m->bqkv, Bz * m->ks_qkv * m->qkv_rows)) ||
@@ -1820,10 +1829,10 @@ static int pf_setup(qd_model* m)
     const size_t ws = attn_ws_layout(PF_T, m->nq, m->nkv, m->hd, m->max_seq, &P.geo);
     if (m->H > 16384)   // the batched RMSNorm splits at most 2 items per thread
         return fail(QD_EUNSUPPORTED, "qd_prefill supports hidden <= 16384 (got %d)", m->H);
-    P.ks_qkv = step_kslices(m->qkv_rows, m->H / 32, PF_NG, PF_RG_QKV);
-    P.ks_o = step_kslices(m->H, (int)nqd / 32, PF_NG, PF_RG_O);
-    P.ks_gu = step_kslices(2 * m->I, m->H / 32, PF_NG, PF_RG_GU);
-    P.ks_down = step_kslices(m->H, m->I / 32, PF_NG, PF_RG_DOWN);
+    P.ks_qkv = step_kslices(m->qkv_rows, m->H / 32, PF_NG, PF_RG_QKV, QD_PF_KS_WGS);
+    P.ks_o = step_kslices(m->H, (int)nqd / 32, PF_NG, PF_RG_O, QD_PF_KS_WGS);
+    P.ks_gu = step_kslices(2 * m->I, m->H / 32, PF_NG, PF_RG_GU, QD_PF_KS_WGS);
+    P.ks_down = step_kslices(m->H, m->I / 32, PF_NG, PF_RG_DOWN, QD_PF_KS_WGS);
     const size_t ch_h = gbm_nchunks(m->H / 32, PF_NG), ch_o = gbm_nchunks((int)nqd / 32, PF_NG),
                  ch_i = gbm_nchunks(m->I / 32, PF_NG), S = 16 * PF_NG;
     int rc;
