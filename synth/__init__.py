@@ -84,6 +84,9 @@ MODELS = {
     # the tiny decoder with all 8 query heads on one kv head (GQA group 8)
     "tiny-gq8": ModelShape("tiny-gq8", 8, 2, 256, 8, 1, 64, 768, 1024, True, True, 1e6, 64, 1e-6,
                            False, 48, 16, 32),
+    # the tiny decoder with a kv head per query head (GQA group 1)
+    "tiny-mha": ModelShape("tiny-mha", 9, 2, 256, 4, 4, 64, 768, 1024, True, True, 1e6, 64, 1e-6,
+                           False, 48, 16, 32),
     # Qwen3-0.6B shape, contiguous KV; 512 prompt tokens + 256 greedy tokens
     "qwen3-0.6b": ModelShape("qwen3-0.6b", 4, 28, 1024, 16, 8, 128, 3072, 151936, True,
                              True, 1e6, 128, 1e-6, False, 768, 512, 256),

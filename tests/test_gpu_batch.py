@@ -170,6 +170,28 @@ def test_tiny_odd_batch_vs_oracle(B, paged):
     _compare(got, prompts, runs, f"tiny-odd B={B} paged={paged}", lg)
 
 
+@pytest.mark.parametrize("name,B,paged", [("tiny-gq8", 16, True), ("tiny-mha", 16, False), ("tiny-mha", 4, True)])
+def test_tiny_group_batch_vs_oracle(name, B, paged):
+    """GQA groups of 8 (the attention's chunk merge writing the o product's
+    input for one kv head) and 1 (head_dim 64: the separate split, whatever
+    B) in the batched step: teacher-forced logits of every sequence within
+    1e-3 of the oracle, then each sequence's greedy tokens."""
+    mi = synth.make_model(name)
+    prompts = _prompts(mi, B, 8, 16, seed=83)
+    runs = _oracle_runs(mi, prompts, TINY_S)
+    say(f"{name} batch B={B} paged={paged}")
+    m = _batch_model(mi, B, paged)
+    lg = _teacher_forced_batch(m, runs, TINY_S, mi.shape.vocab)
+    m.close()
+    worst = max(float(np.max(np.abs(lg[b] - runs[b][3]))) for b in range(B))
+    record(f"{name} batch B={B}: teacher-forced logits max abs err {worst:.3e}")
+    assert worst <= 1e-3
+    m = _batch_model(mi, B, paged)
+    got = _run_lockstep(m, prompts, TINY_S)
+    m.close()
+    _compare(got, prompts, runs, f"{name} B={B} paged={paged}", lg)
+
+
 def test_tiny_batch_kv_fp8_vs_oracle(tiny):
     """fp8 e4m3 K/V caches in the batched step (k_scale 0.5, v_scale 0.125)."""
     B = 4

@@ -507,11 +507,12 @@ def _paged_inputs(mi, nblocks=8):
 
 @pytest.mark.parametrize("name,paged", [("tiny-rot32", False), ("tiny-rot32", True),
                                         ("tiny-untied", False), ("tiny-untied", True),
-                                        ("tiny-odd", False), ("tiny-odd", True), ("tiny-gq8", True)])
+                                        ("tiny-odd", False), ("tiny-odd", True), ("tiny-gq8", True),
+                                        ("tiny-mha", False)])
 def test_tiny_variant_decode_vs_oracle(name, paged):
     """Partial rotary (rot_dim 32 of head_dim 64), an untied LM head, sizes
-    that are not multiples of 256 (hidden 288, SwiGLU 800, vocab 1000) and a
-    GQA group of 8 through the decode step: teacher-forced logits of every position (<= 1e-4 abs) and
+    that are not multiples of 256 (hidden 288, SwiGLU 800, vocab 1000) and
+    GQA groups of 8 and 1 through the decode step: teacher-forced logits of every position (<= 1e-4 abs) and
     the teacher-forced argmax, free-running greedy tokens, graph == eager."""
     import token_decode_q4_amd as qd
     mi, toks, margins, seq, ref = _variant_ref(name)
@@ -537,7 +538,8 @@ def test_tiny_variant_decode_vs_oracle(name, paged):
 
 @pytest.mark.parametrize("name,paged", [("tiny-rot32", False), ("tiny-rot32", True),
                                         ("tiny-untied", False), ("tiny-odd", False), ("tiny-odd", True),
-                                        ("tiny-gq8", False), ("tiny-gq8", True)])
+                                        ("tiny-gq8", False), ("tiny-gq8", True), ("tiny-mha", False),
+                                        ("tiny-mha", True)])
 def test_tiny_variant_prefill_vs_oracle(name, paged):
     """qd_prefill (one chunk on the matrix-core products) of the variant's prompt:
     logits at the last prompt position (<= 1e-4), then greedy generation
