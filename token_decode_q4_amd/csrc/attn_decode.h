@@ -7,20 +7,26 @@
 // whole query group; ferrum-kernels cuda_decode.rs page, flash_decode_attention
 // phase 1/2, paged_decode_attention, batched_decode_attention).
 //
-// k_attn_split: grid (nsplit, nkv, B), 4 waves.  A workgroup owns one
-// (sequence, kv head, key range) and serves all GQ query heads of that kv
-// head.  Each wave works on its own 16-key steps (one paged block) with no
+// k_attn_split: grid (nsplit, nkv, B), up to 8 waves (4 with GQA 8).  A
+// workgroup owns one (sequence, kv head, key range) and serves all GQ query
+// heads of that kv head.  Each wave works on its own 16-key steps (one paged
+// block), the next step's K/V in flight while it computes one, with no
 // workgroup barrier until the end:
-//   QK   lane (key k = lane/4, quarter c = lane%4) holds 8 dims of K[k] in each
-//        32-dim slice (dims 32i + 8c .. +7), reads the matching query dims from
-//        LDS and reduces the 4 quarters with two shuffles;
-//   softmax  per head over the 16 keys (shuffles across the key lanes), online
-//        across the wave's steps (running max m, sum l, rescale of acc);
+//   QK   v_mfma_f32_16x16x32_f16 with M = the step's 16 keys (straight from
+//        the K loads), N = the query heads (columns past GQ zero), K = 32 dims
+//        per instruction; q enters as an f16 hi + lo pair (about 22 bits);
+//   softmax  per head over the 16 keys (4 accumulator registers, then shuffles
+//        across the 4 lane groups), online across the wave's steps (running
+//        max m, sum l, rescale of acc);
 //   PV   lane owns HD/64 output dims; the step's probabilities go through a
 //        small per-wave LDS table [key][head]; V is loaded in that layout.
-// The four waves' (m, l, acc) are merged once through LDS and written as the
-// workgroup's partial.  k_attn_combine (grid (nq, B)) merges a head's partials:
-//   M = max_s m_s,  out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s.
+// The waves' (m, l, acc) are merged once through LDS and written as the
+// workgroup's partial.  The partials of a head are merged as
+//   M = max_s m_s,  out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s
+// by one of: k_attn_combine (grid (nq, B), a launch of its own); the last
+// split workgroup of each (sequence, kv head) to finish (counters given); or,
+// in the batched decode step, the last of each (sequence, 1024-element chunk
+// of the output), which writes the chunk as the o product's split input.
 //
 // In the decode step (QMODE 1; QMODE 2 for B sequences whose raw q|k|v come
 // as K-slice partial products) the split kernel also finishes the projection:
@@ -271,13 +277,6 @@ QD_DEV void attn_merge_last(const AttnParams& p, int b, int g, int kv_len, int* 
         __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The merge as attn_merge_last, per chunk c of 1024 output elements of
-// sequence b (KPC = 1024 / (GQ HD) kv heads, fewer in a ragged last chunk):
-// the last of the chunk's workgroups to finish merges every head of the chunk
-// into LDS (buf: 1024 floats) and writes the chunk as the o product's split
-// input, as k_xsplit_batch does: one item (block, lane group) of 8 elements
-// per thread, the power of two that puts the chunk's largest |x| in
-// [2^13, 2^14), the f16 pair of each element, 1/scale in xs.
 // The merge of attn_merge_heads for n consecutive output elements of
 // sequence b starting at kv head g0's first query head, EPT elements per
 // thread (i = threadIdx.x + r * blockDim.x, n <= EPT * blockDim.x), into
@@ -344,6 +343,14 @@ __host__ __device__ constexpr bool attn_split_out_ok(int hd, int gq)
     return (gq <= 4 ? 8 : 4) * gq * hd >= 1024 && 1024 % (gq * hd) == 0;
 }
 
+// The merge as attn_merge_last, per chunk c of 1024 output elements of
+// sequence b (KPC = 1024 / (GQ HD) kv heads, fewer in a ragged last chunk):
+// the last of the chunk's workgroups to finish merges every head of the chunk
+// into LDS (buf: 1024 floats; one round of loads with attn_merge_rows when a
+// thread holds at most 4 elements, else kv head by kv head) and writes the
+// chunk as the o product's split input, as k_xsplit_batch does: items
+// (block, lane group) of 8 elements, the power of two that puts the chunk's
+// largest |x| in [2^13, 2^14), the f16 pair of each element, 1/scale in xs.
 template <int HD, int GQ>
 QD_DEV void attn_merge_split(const AttnParams& p, int b, int g, int kv_len, int* last, float* buf, float* red)
 {

@@ -11,8 +11,9 @@
 // applied before the product, by one workgroup per (chunk, sequence); each
 // chunk's sum of x^2 goes beside the split and the product applies 1/rms.
 //   k_embed_xp_batch        x[b] = E[token_b]; split of x[b] * w; rotary factors
-//   (batched q|k|v GEMV; split-KV attention over the B caches; k_xsplit_batch;
-//    batched o GEMV)
+//   (batched q|k|v GEMV; split-KV attention over the B caches, whose merge
+//    writes the o product's split input from 8 sequences, k_xsplit_batch
+//    below that; batched o GEMV)
 //   k_resid_norm_xp_batch   x[b] += y[b]; split of x[b] * w
 //   (batched gate|up GEMV)  k_swiglu_xp_batch: a[b][i] = silu(g) * up
 //   (batched down GEMV)     k_resid_norm_xp_batch (next layer's or the final norm)
