@@ -608,6 +608,8 @@ def main():
     ap.add_argument("--batch-only", action="store_true",
                     help="print only the batched decode rows of --config")
     ap.add_argument("--batch-sizes", default="4,8,16", help="sequences of the batched decode rows")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="print only the standalone attention rows (f16 and fp8 caches)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): batch-1 decode of one "
@@ -629,6 +631,12 @@ def main():
         sys.exit(f"warmup + steps must be <= {s.max_seq - P + 1}")
     if args.batch_only:
         print(json.dumps(batch_decode_rows(mi, tuple(int(b) for b in args.batch_sizes.split(",")))), flush=True)
+        return
+    if args.attention_only:
+        a_rows = attention_rows() + attention_rows(kv8=True)
+        for r in a_rows:
+            log(f"attention {r['case']} {r['kv']}: {r['mean_us']} us, {r['achieved']} GB/s ({r['frac']:.3f})")
+        print(json.dumps(a_rows), flush=True)
         return
     t0 = time.time()
     model = qd.Model(mi, use_graph=True, layer_kernel=bool(args.layer_kernel), kv_fp8=args.kv_fp8,

@@ -418,9 +418,12 @@ static int validate_config(const qd_config* c, const qd_weights* w, int B)
 
 // Launch the split-KV attention (split + combine).
 template <int QMODE, bool KV8 = false>
-static void launch_attention(const AttnParams& p, int waves, int hd, int gq, bool paged, int B,
-                             int nq, hipStream_t s)
+static hipError_t launch_attention(const AttnParams& p, int waves, int hd, int gq, bool paged, int B,
+                                   int nq, hipStream_t s)
 {
+    // the split kernel's LDS rows and launch bound hold AttnMaxWaves<GQ> waves
+    if (waves < 1 || waves > (gq <= 4 ? 8 : 4))
+        return hipErrorInvalidConfiguration;
     const dim3 grid(p.nsplit, p.nkv, B), block(waves * WAVE);
     // with max_kv == 0 every kv_len is 0: no split runs and the combine writes zeros
 #define QD_ATT(HD_, GQ_)                                                                          \
@@ -438,7 +441,7 @@ static void launch_attention(const AttnParams& p, int waves, int hd, int gq, boo
     }
 #undef QD_ATT
     if (p.counters)
-        return;   // the split kernel merged the partials itself
+        return hipGetLastError();   // the split kernel merged the partials itself
     // one round of loads: U splits per group of HD threads, U * (ATT_CNT / HD) >= nsplit
     const int per = (p.nsplit + ATT_CNT / hd - 1) / (ATT_CNT / hd);
 #define QD_CMB(HD_, U_)                                                                             \
@@ -452,6 +455,7 @@ static void launch_attention(const AttnParams& p, int waves, int hd, int gq, boo
         else QD_CMB(64, 16);
     }
 #undef QD_CMB
+    return hipGetLastError();
 }
 
 // Enqueue one decode step (position and token come from the device state).
@@ -634,9 +638,9 @@ static int enqueue_step_batch(qd_model* m, hipStream_t s)
         p.xp = split_out ? m->xp_o : nullptr;
         p.xs = split_out ? m->xs_o : nullptr;
         if (m->kv_fp8)
-            launch_attention<2, true>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, B, m->nq, s);
+            HIP_TRY((launch_attention<2, true>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, B, m->nq, s)));
         else
-            launch_attention<2>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, B, m->nq, s);
+            HIP_TRY((launch_attention<2>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, B, m->nq, s)));
         const size_t slab_h = (size_t)B * H;
         if (!split_out)
             hipLaunchKernelGGL(k_xsplit_batch, dim3(gbm_nchunks(nqd / 32, 1), B), dim3(128), 0, s, m->battn,
@@ -711,9 +715,9 @@ static int enqueue_step(qd_model* m, hipStream_t s)
             p.v_scale = m->v_scale;
             p.gate = m->attn_gate ? m->qkv_raw + (size_t)(m->nq + 2 * m->nkv) * m->hd : nullptr;
             if (m->kv_fp8)
-                launch_attention<1, true>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, 1, m->nq, s);
+                HIP_TRY((launch_attention<1, true>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, 1, m->nq, s)));
             else
-                launch_attention<1>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, 1, m->nq, s);
+                HIP_TRY((launch_attention<1>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, 1, m->nq, s)));
         }
         // o-proj + residual, u = x * ffn_norm
         QD_GEMV(k_gemv_residual, (QD_CFG_O), m->lpr_o, m->grid_o, gemv_lds_bytes(Ly.o.nb), s,
@@ -1535,15 +1539,34 @@ extern "C" int qd_gemv_q4_0_experts(const uint16_t* d_scales, const uint8_t* d_q
     return QD_OK;
 }
 
-static AttnGeom standalone_geom(int32_t B, int32_t nkv, int32_t max_kv)
+// Grid of qd_attn_decode.  The split kernel holds 212 VGPRs, so a compute
+// unit runs 8 of its waves.  One sequence: 256 workgroups of 8 waves, one
+// resident round.  Several: 2048 workgroups of 4 waves, so that the longest
+// sequences' splits hold fewer keys (a split past a sequence's kv_len returns
+// at once).  Measured (graph of 100 launches over rotated pools, f16 / fp8):
+// one sequence at kv_len 32768 32.4 / 24.0 us against 40.1 / 29.4 with 1024
+// x 4 waves for every B, 4096 11.2 / 10.6 against 12.7 / 12.1, 512 8.7 / 8.5
+// against 8.1 / 8.1; 8 sequences of mixed lengths up to 16384 70.4 / 49.0
+// against 89.1 / 65.1.
+#ifndef QD_ATT_SA1_WGS
+#define QD_ATT_SA1_WGS 256
+#endif
+#ifndef QD_ATT_SA_WGS
+#define QD_ATT_SA_WGS 2048
+#endif
+static AttnGeom standalone_geom(int32_t B, int32_t nq, int32_t nkv, int32_t max_kv)
 {
-    return attn_geom(B, nkv, max_kv, 1024, 4, 4);
+    // the kernel's LDS rows and launch bound hold 8 waves up to GQA 4, 4 beyond
+    const int wmax = nq / nkv <= 4 ? 8 : 4;
+    if (B == 1)
+        return attn_geom(B, nkv, max_kv, QD_ATT_SA1_WGS * 8 / wmax, wmax, wmax);
+    return attn_geom(B, nkv, max_kv, QD_ATT_SA_WGS, 4, 4);
 }
 
 static size_t attn_ws_layout(int32_t B, int32_t nq, int32_t nkv, int32_t hd, int32_t max_kv,
                              AttnGeom* g)
 {
-    *g = standalone_geom(B, nkv, max_kv);
+    *g = standalone_geom(B, nq, nkv, max_kv);
     return (size_t)B * nq * g->nsplit * (hd + 2) * sizeof(float);
 }
 
@@ -1620,8 +1643,8 @@ static int attn_decode_impl(const qd_attn_args* a, float k_scale, float v_scale,
     p.out = a->out;
     p.k_scale = k_scale;
     p.v_scale = v_scale;
-    launch_attention<0, KV8>(p, geo.waves, a->head_dim, a->nq / a->nkv, a->block_tables != nullptr, a->B, a->nq,
-                             (hipStream_t)stream);
+    HIP_TRY((launch_attention<0, KV8>(p, geo.waves, a->head_dim, a->nq / a->nkv, a->block_tables != nullptr, a->B, a->nq,
+                             (hipStream_t)stream)));
     HIP_TRY(hipGetLastError());
     return QD_OK;
 }
@@ -1943,7 +1966,7 @@ extern "C" int qd_prefill(qd_model* m, int32_t pos0, int32_t n, float* d_logits_
                 p.k_scale = m->k_scale;
                 p.v_scale = m->v_scale;
                 p.shared_kv = 1;
-                launch_attention<0, true>(p, P.geo.waves, hd, gq, m->paged, T, m->nq, s);
+                HIP_TRY((launch_attention<0, true>(p, P.geo.waves, hd, gq, m->paged, T, m->nq, s)));
             }
             // the gate rows follow q|k|v in the fused product
             const float* gate = m->attn_gate ? P.QKV + (size_t)(m->nq + 2 * m->nkv) * hd : nullptr;
