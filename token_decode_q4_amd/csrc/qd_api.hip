@@ -421,9 +421,13 @@ template <int QMODE, bool KV8 = false>
 static hipError_t launch_attention(const AttnParams& p, int waves, int hd, int gq, bool paged, int B,
                                    int nq, hipStream_t s)
 {
-    // the split kernel's LDS rows and launch bound hold AttnMaxWaves<GQ> waves
+    // the split kernel's LDS rows and launch bound hold AttnMaxWaves<GQ> waves;
+    // the split output (xp) is written by the counted merge of the batched
+    // step's query mode only
     if (waves < 1 || waves > (gq <= 4 ? 8 : 4))
         return hipErrorInvalidConfiguration;
+    if (p.xp && (QMODE != 2 || !p.counters || !p.xs || !attn_split_out_ok(hd, gq)))
+        return hipErrorInvalidValue;
     const dim3 grid(p.nsplit, p.nkv, B), block(waves * WAVE);
     // with max_kv == 0 every kv_len is 0: no split runs and the combine writes zeros
 #define QD_ATT(HD_, GQ_)                                                                          \
