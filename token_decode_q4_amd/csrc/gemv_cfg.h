@@ -18,11 +18,24 @@ struct GemvCfg {
 #define QD_CFG_QKV 3, 8, 1, 2, 4, false    // q|k|v
 #define QD_CFG_GU 2, 4, 2, 2, 8, false     // gate|up (16 lanes per row)
 #define QD_CFG_HEAD 4, 4, 1, 2, 10, true   // LM head (streamed once)
+// one row per slot: for matrices whose row tiles at the sizes above give too
+// few workgroups to fill the chip (small models; the same waves, so the x
+// staging registers do not grow)
+#define QD_CFG_O_S 1, 8, 1, 2, 4, false
+#define QD_CFG_DOWN_S 1, 8, 1, 3, 6, false
+#define QD_CFG_QKV_S 1, 8, 1, 2, 4, false
 static constexpr GemvCfg CFG_O = {QD_CFG_O, 1 << 30, 64};
 static constexpr GemvCfg CFG_DOWN = {QD_CFG_DOWN, 1 << 30, 64};
 static constexpr GemvCfg CFG_QKV = {QD_CFG_QKV, 1 << 30, 64};
 static constexpr GemvCfg CFG_GU = {QD_CFG_GU, 512, 16};
 static constexpr GemvCfg CFG_HEAD = {QD_CFG_HEAD, 2048, 64};
+static constexpr GemvCfg CFG_O_S = {QD_CFG_O_S, 1 << 30, 64};
+static constexpr GemvCfg CFG_DOWN_S = {QD_CFG_DOWN_S, 1 << 30, 64};
+static constexpr GemvCfg CFG_QKV_S = {QD_CFG_QKV_S, 1 << 30, 64};
+// a call site takes its one-row configuration below this many workgroups
+#ifndef QD_GEMV_SMALL_GRID
+#define QD_GEMV_SMALL_GRID 128
+#endif
 static constexpr int GEMV_MAX_LDS = 64 * 1024;
 
 // lanes per row: the largest of 64/32/16/8, at most the configuration's

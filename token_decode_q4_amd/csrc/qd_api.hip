@@ -180,6 +180,7 @@ struct qd_model {
     int32_t *ids = nullptr, *pred = nullptr;
     // launch geometry
     int lpr_qkv, grid_qkv, lpr_o, grid_o, lpr_gu, grid_gu, lpr_down, grid_down;
+    bool small_qkv = false, small_o = false, small_down = false;   // one-row configurations
     int lpr_lm, grid_lm, grid_embed;
     // graph
     int use_graph = 0;
@@ -684,9 +685,15 @@ static int enqueue_step(qd_model* m, hipStream_t s)
     for (int l = 0; l < m->L; ++l) {
         DevLayer& Ly = m->layers[l];
         // q | k | v (raw, before the per-head norm and rotary)
-        QD_GEMV(k_gemv_scaled, (QD_CFG_QKV), m->lpr_qkv, m->grid_qkv, gemv_lds_bytes(Ly.qkv.nb), s,
-                       Ly.qkv.d, Ly.qkv.qs, m->u, Ly.qkv.rows, Ly.qkv.nb, m->ss_part, n_part, H,
-                       m->eps, m->qkv_raw);
+        if (m->small_qkv) {
+            QD_GEMV(k_gemv_scaled, (QD_CFG_QKV_S), m->lpr_qkv, m->grid_qkv, gemv_lds_bytes(Ly.qkv.nb), s,
+                    Ly.qkv.d, Ly.qkv.qs, m->u, Ly.qkv.rows, Ly.qkv.nb, m->ss_part, n_part, H, m->eps,
+                    m->qkv_raw);
+        } else {
+            QD_GEMV(k_gemv_scaled, (QD_CFG_QKV), m->lpr_qkv, m->grid_qkv, gemv_lds_bytes(Ly.qkv.nb), s,
+                    Ly.qkv.d, Ly.qkv.qs, m->u, Ly.qkv.rows, Ly.qkv.nb, m->ss_part, n_part, H, m->eps,
+                    m->qkv_raw);
+        }
         // per-head norm + rotary, K/V write, split-KV attention, combine
         {
             AttnParams p;
@@ -724,9 +731,13 @@ static int enqueue_step(qd_model* m, hipStream_t s)
                 HIP_TRY((launch_attention<1>(p, m->attn_waves, m->hd, m->nq / m->nkv, m->paged, 1, m->nq, s)));
         }
         // o-proj + residual, u = x * ffn_norm
-        QD_GEMV(k_gemv_residual, (QD_CFG_O), m->lpr_o, m->grid_o, gemv_lds_bytes(Ly.o.nb), s,
-                       Ly.o.d, Ly.o.qs, m->attn, Ly.o.rows, Ly.o.nb, m->x, m->u, Ly.ffn_norm,
-                       m->ss_part);
+        if (m->small_o) {
+            QD_GEMV(k_gemv_residual, (QD_CFG_O_S), m->lpr_o, m->grid_o, gemv_lds_bytes(Ly.o.nb), s,
+                    Ly.o.d, Ly.o.qs, m->attn, Ly.o.rows, Ly.o.nb, m->x, m->u, Ly.ffn_norm, m->ss_part);
+        } else {
+            QD_GEMV(k_gemv_residual, (QD_CFG_O), m->lpr_o, m->grid_o, gemv_lds_bytes(Ly.o.nb), s,
+                    Ly.o.d, Ly.o.qs, m->attn, Ly.o.rows, Ly.o.nb, m->x, m->u, Ly.ffn_norm, m->ss_part);
+        }
         n_part = m->grid_o;
         // gate|up + SwiGLU
         QD_GEMV(k_gemv_swiglu, (QD_CFG_GU), m->lpr_gu, m->grid_gu, gemv_lds_bytes(Ly.gu.nb), s,
@@ -734,9 +745,13 @@ static int enqueue_step(qd_model* m, hipStream_t s)
                        m->act);
         // down + residual, u = x * (next attn_norm | final_norm)
         const float* wn = (l + 1 < m->L) ? m->layers[l + 1].attn_norm : m->final_norm;
-        QD_GEMV(k_gemv_residual, (QD_CFG_DOWN), m->lpr_down, m->grid_down,
-                       gemv_lds_bytes(Ly.down.nb), s, Ly.down.d, Ly.down.qs, m->act, Ly.down.rows,
-                       Ly.down.nb, m->x, m->u, wn, m->ss_part);
+        if (m->small_down) {
+            QD_GEMV(k_gemv_residual, (QD_CFG_DOWN_S), m->lpr_down, m->grid_down, gemv_lds_bytes(Ly.down.nb), s,
+                    Ly.down.d, Ly.down.qs, m->act, Ly.down.rows, Ly.down.nb, m->x, m->u, wn, m->ss_part);
+        } else {
+            QD_GEMV(k_gemv_residual, (QD_CFG_DOWN), m->lpr_down, m->grid_down, gemv_lds_bytes(Ly.down.nb), s,
+                    Ly.down.d, Ly.down.qs, m->act, Ly.down.rows, Ly.down.nb, m->x, m->u, wn, m->ss_part);
+        }
         n_part = m->grid_down;
     }
     QD_GEMV(k_gemv_lmhead, (QD_CFG_HEAD), m->lpr_lm, m->grid_lm, gemv_lds_bytes(m->lm.nb), s,
@@ -979,12 +994,18 @@ static int create_model(const qd_config* cfg, const qd_weights* w, int B, qd_str
         m->grid_embed = (H + 255) / 256;
         m->lpr_qkv = pick_lpr(nbH);
         m->grid_qkv = gemv_grid(CFG_QKV, m->lpr_qkv, m->qkv_rows);
+        if ((m->small_qkv = m->grid_qkv < QD_GEMV_SMALL_GRID))
+            m->grid_qkv = gemv_grid(CFG_QKV_S, m->lpr_qkv, m->qkv_rows);
         m->lpr_o = pick_lpr(nqd / 32);
         m->grid_o = gemv_grid(CFG_O, m->lpr_o, H);   // one tile per workgroup (residual epilogue)
+        if ((m->small_o = m->grid_o < QD_GEMV_SMALL_GRID))
+            m->grid_o = gemv_grid(CFG_O_S, m->lpr_o, H);
         m->lpr_gu = pick_lpr(nbH, CFG_GU.lpr_max);
         m->grid_gu = gemv_grid(CFG_GU, m->lpr_gu, 2 * m->I);
         m->lpr_down = pick_lpr(m->I / 32);
         m->grid_down = gemv_grid(CFG_DOWN, m->lpr_down, H);   // one tile per workgroup
+        if ((m->small_down = m->grid_down < QD_GEMV_SMALL_GRID))
+            m->grid_down = gemv_grid(CFG_DOWN_S, m->lpr_down, H);
         m->lpr_lm = pick_lpr(nbH);
         m->grid_lm = gemv_grid(CFG_HEAD, m->lpr_lm, m->V);
         // attention: splits over max_seq (the grid does not depend on the position),
