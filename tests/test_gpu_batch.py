@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_helpers import check_greedy, host, record, say
+from gpu_helpers import LOGITS_BAR, check_greedy, host, load_golden, record, say
 
 pytestmark = pytest.mark.gpu
 
@@ -266,3 +266,65 @@ def test_qwen3_06b_shape_batch_vs_oracle(small, small_runs, B):
     record(f"qwen3-0.6b B={B}: teacher-forced logits of {B} x {SMALL_S} steps, max abs err {worst:.3e}")
     assert worst <= 2e-2
     _compare(got, prompts[:B], runs[:B], f"qwen3-0.6b B={B}", lg)
+
+
+def test_qwen3_8b_shape_batch_vs_golden():
+    """The batched step at the benchmarked size: 16 sequences of the Qwen3-8B
+    shape, each on its own paged cache (a shuffled table per sequence) and
+    holding the 8B golden file's prompt and greedy tokens as forced tokens,
+    stepped together through positions 0 .. P+G-2.  The contexts are then the
+    oracle's, so at every greedy position every sequence's argmax must be the
+    oracle's greedy token, and at the golden file's sampled positions every
+    sequence's logits must be within the logits bar of the oracle's."""
+    import torch
+    import token_decode_q4_amd as qd
+    g = load_golden("qwen3-8b")
+    if g is None:
+        pytest.skip("tests/golden/greedy_qwen3-8b.json not generated")
+    say("qwen3-8b batch: generating inputs")
+    mi = synth.make_model("qwen3-8b")
+    assert mi.digest == g["digest"], "inputs differ from the ones the golden file was made from"
+    s = mi.shape
+    P, G, V, B = s.prompt_len, s.gen, s.vocab, 16
+    stream = np.concatenate([mi.prompt, np.asarray(g["tokens"][:G - 1], dtype=np.int32)]).astype(np.int32)
+    tbl, nblk = _paged_table(B, s.max_seq, seed=11)
+    say("qwen3-8b batch: qd_create_batch")
+    m = qd.Model(mi, batch=B, paged=True, block_table=tbl, num_kv_blocks=nblk)
+    for b in range(B):
+        m.set_prompt_seq(b, stream)
+    points = {}
+    for tag in g["samples"]:
+        kind, k = tag.split(":")
+        points[int(k) if kind == "prefill" else P - 1 + int(k)] = tag
+    last = P + G - 2
+    preds = np.full((B, last + 1), -1, np.int32)
+    lg = torch.empty((B, V), dtype=torch.float32, device="cuda")
+    got = {}
+    pos = 0
+    for stop in sorted(set(points) | {last}):
+        n = stop + 1 - pos
+        seg = torch.full((B, n), -1, dtype=torch.int32, device="cuda")
+        m.generate_batch([pos] * B, n, tokens=seg, logits_last=lg)
+        preds[:, pos:stop + 1] = host(seg)
+        if stop in points:
+            got[points[stop]] = host(lg).copy()
+        pos = stop + 1
+        say(f"qwen3-8b batch: reached position {pos}")
+    m.check()
+    m.close()
+    ref = np.asarray(g["tokens"], dtype=np.int32)
+    worst = 0.0
+    for b in range(B):
+        gr = preds[b, P - 1:P - 1 + G]
+        bad = np.nonzero(gr != ref)[0]
+        record(f"qwen3-8b batch B={B} seq {b}: {G - len(bad)}/{G} teacher-forced greedy tokens equal"
+               + (f" (first difference at step {int(bad[0])}, oracle margin {float(g['margins'][bad[0]]):.3e})"
+                  if len(bad) else ""))
+        assert len(bad) == 0
+        for tag, lv in got.items():
+            smp = g["samples"][tag]
+            err = float(np.max(np.abs(lv[b][np.array(smp["idx"])] - np.array(smp["val"]))))
+            err = max(err, float(np.max(np.abs(lv[b][np.array(smp["top_idx"])] - np.array(smp["top_val"])))))
+            worst = max(worst, err)
+    record(f"qwen3-8b batch B={B}: {len(got)} sampled positions x {B} sequences, worst logit error {worst:.3e}")
+    assert worst <= LOGITS_BAR
