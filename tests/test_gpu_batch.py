@@ -268,9 +268,11 @@ def test_qwen3_06b_shape_batch_vs_oracle(small, small_runs, B):
     _compare(got, prompts[:B], runs[:B], f"qwen3-0.6b B={B}", lg)
 
 
-def test_qwen3_8b_shape_batch_vs_golden():
-    """The batched step at the benchmarked size: 16 sequences of the Qwen3-8B
-    shape, each on its own paged cache (a shuffled table per sequence) and
+@pytest.mark.parametrize("B", [4, 16])
+def test_qwen3_8b_shape_batch_vs_golden(B):
+    """The batched step at the benchmarked size: 4 and 16 sequences of the
+    Qwen3-8B shape (the attention output split by its own kernel, and by the
+    attention's chunk merge), each on its own paged cache (a shuffled table per sequence) and
     holding the 8B golden file's prompt and greedy tokens as forced tokens,
     stepped together through positions 0 .. P+G-2.  The contexts are then the
     oracle's, so at every greedy position every sequence's argmax must be the
@@ -285,7 +287,7 @@ def test_qwen3_8b_shape_batch_vs_golden():
     mi = synth.make_model("qwen3-8b")
     assert mi.digest == g["digest"], "inputs differ from the ones the golden file was made from"
     s = mi.shape
-    P, G, V, B = s.prompt_len, s.gen, s.vocab, 16
+    P, G, V = s.prompt_len, s.gen, s.vocab
     stream = np.concatenate([mi.prompt, np.asarray(g["tokens"][:G - 1], dtype=np.int32)]).astype(np.int32)
     tbl, nblk = _paged_table(B, s.max_seq, seed=11)
     say("qwen3-8b batch: qd_create_batch")
