@@ -439,6 +439,47 @@ def test_tiny_prefill_ragged_chunks_vs_oracle():
     _greedy_gate(got, toks[i0:i0 + len(got)], margins[i0:i0 + len(got)], "tiny ragged prefill")
 
 
+def test_tiny_long_prefill_vs_oracle():
+    """qd_prefill over 4096 positions of the tiny decoder on a paged cache, in
+    two calls (0 .. 2047, 2048 .. 4095): the chunk attention's splits grow with
+    the context (up to 64 per chunk), so the split merge takes every one of
+    its round sizes (U = 2 .. 32 splits per thread group); logits at the last
+    position of each call against the oracle's teacher-forced ones (<= 1e-4),
+    and the prediction at 4095."""
+    import dataclasses
+    import torch
+    import token_decode_q4_amd as qd
+    shape = dataclasses.replace(synth.MODELS["tiny"], name="tiny-4k", max_seq=4160, prompt_len=4096, gen=8)
+    mi = synth.make_model(shape)
+    n, half = 4096, 2048
+    om = oracle.Model(mi)
+    ref = {}
+    for p in range(n):
+        lg_o = om.step(int(mi.prompt[p]), p)
+        if p in (half - 1, n - 1):
+            ref[p] = lg_o
+    say("tiny long prefill")
+    nblk = (shape.max_seq + 15) // 16 + 3
+    tbl = np.random.default_rng(17).permutation(nblk).astype(np.int32)
+    src = synth.ModelInputs(mi.shape, mi.embed, mi.layers, mi.final_norm, mi.lm_head, mi.inv_freq,
+                            mi.prompt, tbl, mi.digest)
+    m = qd.Model(src, use_graph=True, paged=True, num_kv_blocks=nblk)
+    m.set_prompt(mi.prompt)
+    lg = torch.empty(shape.vocab, dtype=torch.float32, device="cuda")
+    m.prefill(0, half, logits_last=lg)
+    e1 = float(np.max(np.abs(host(lg) - ref[half - 1])))
+    m.prefill(half, n - half, logits_last=lg)
+    got = host(lg)
+    e2 = float(np.max(np.abs(got - ref[n - 1])))
+    m.check()
+    m.close()
+    say(f"tiny long prefill logits max abs err {e1:.3e} (position {half - 1}), {e2:.3e} (position {n - 1})")
+    assert max(e1, e2) <= 1e-4
+    r = ref[n - 1].astype(np.float32)
+    top2 = np.sort(r)[-2:]
+    assert int(np.argmax(got)) == int(np.argmax(r)) or top2[1] - top2[0] < e2
+
+
 def test_tiny_prefill_rejects(tiny):
     import token_decode_q4_amd as qd
     m = qd.Model(tiny)
