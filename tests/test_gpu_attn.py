@@ -54,6 +54,19 @@ def test_attention_ragged_lengths(hd, nq, nkv):
     assert normwise(got, ref) <= ATTN_TOL
 
 
+def test_attention_two_long_sequences():
+    """Two sequences of 20 001 and 32 768 keys (32 q / 8 kv heads of 128): with
+    several sequences the grid holds 2048 workgroups, 128 key splits per head,
+    so the merge takes 16 splits per thread group in each of two load rounds."""
+    lens = [20001, 32768]
+    a = synth.random_attn(97, len(lens), lens, nq=32, nkv=8, hd=128)
+    ref = oracle.attn_inputs(a)
+    got, _ = _run(a)
+    err = normwise(got, ref)
+    say(f"attention two long sequences: normwise err {err:.3e}")
+    assert err <= ATTN_TOL
+
+
 def test_attention_paged_equals_contiguous_bitwise():
     a = synth.random_attn(41, 3, [5, 130, 777], nq=32, nkv=8, hd=128)
     p, _ = _run(a, paged=True)
