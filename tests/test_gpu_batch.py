@@ -192,6 +192,31 @@ def test_tiny_group_batch_vs_oracle(name, B, paged):
     _compare(got, prompts, runs, f"{name} B={B} paged={paged}", lg)
 
 
+def test_tiny_gq8_long_batch_vs_oracle():
+    """8 sequences of the GQA-8 tiny model (one kv head) with a 640-position
+    cache and prompts of 560 .. 600 tokens: the attention takes ~20 key splits
+    per sequence, so the chunk merge that writes the o product's input runs
+    its 32-split load round.  Teacher-forced logits of every step and sequence
+    within 1e-3 of the oracle, then each sequence's greedy tokens."""
+    import dataclasses
+    shape = dataclasses.replace(synth.MODELS["tiny-gq8"], name="tiny-gq8-640", max_seq=640)
+    mi = synth.make_model(shape)
+    B, S = 8, 620
+    prompts = _prompts(mi, B, 560, 600, seed=89)
+    runs = _oracle_runs(mi, prompts, S)
+    say(f"tiny-gq8 long batch B={B}")
+    m = _batch_model(mi, B, True)
+    lg = _teacher_forced_batch(m, runs, S, mi.shape.vocab)
+    m.close()
+    worst = max(float(np.max(np.abs(lg[b] - runs[b][3]))) for b in range(B))
+    record(f"tiny-gq8 long batch B={B}: teacher-forced logits of {B} x {S} steps, max abs err {worst:.3e}")
+    assert worst <= 1e-3
+    m = _batch_model(mi, B, True)
+    got = _run_lockstep(m, prompts, S)
+    m.close()
+    _compare(got, prompts, runs, f"tiny-gq8 long B={B}", lg)
+
+
 def test_tiny_batch_kv_fp8_vs_oracle(tiny):
     """fp8 e4m3 K/V caches in the batched step (k_scale 0.5, v_scale 0.125)."""
     B = 4
