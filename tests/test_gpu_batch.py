@@ -95,11 +95,13 @@ def tiny_runs(tiny):
     return prompts, _oracle_runs(tiny, prompts, TINY_S)
 
 
-@pytest.mark.parametrize("B", [2, 4, 8, 16])
+@pytest.mark.parametrize("B", [2, 3, 4, 6, 8, 11, 16])
 @pytest.mark.parametrize("paged", [False, True])
 def test_tiny_batch_greedy_vs_oracle(tiny, tiny_runs, B, paged):
     """Each of B sequences (ragged prompts of 8 .. 16 tokens, the rest greedy)
-    generates the oracle's greedy tokens."""
+    generates the oracle's greedy tokens.  The widths include ones that fill
+    no 4-vector slot group (3, 11) and both sides of the attention's chunk
+    merge (from 8)."""
     prompts, runs = tiny_runs
     say(f"tiny batch B={B} paged={paged}")
     m = _batch_model(tiny, B, paged)
@@ -108,7 +110,7 @@ def test_tiny_batch_greedy_vs_oracle(tiny, tiny_runs, B, paged):
     _compare(got, prompts[:B], runs[:B], f"tiny B={B} paged={paged}")
 
 
-@pytest.mark.parametrize("B", [4, 16])
+@pytest.mark.parametrize("B", [4, 11, 16])
 def test_tiny_batch_teacher_forced_logits(tiny, tiny_runs, B):
     """qd_decode_step_batch along each oracle sequence: every position's logits
     of every sequence within 1e-3 of the oracle's, and the step's argmax equal
@@ -273,7 +275,7 @@ def small_runs(small):
     return prompts, _oracle_runs(small, prompts, SMALL_S)
 
 
-@pytest.mark.parametrize("B", [2, 4, 8, 16])
+@pytest.mark.parametrize("B", [2, 4, 8, 11, 16])
 def test_qwen3_06b_shape_batch_vs_oracle(small, small_runs, B):
     """The Qwen3-0.6B shape (28 layers, vocabulary 151936) in batches of 2 to
     16 sequences with ragged prompts of 16 .. 24 tokens: every sequence's greedy
